@@ -1,0 +1,230 @@
+"""Literal fp64 oracle of the Interdomain Attention token-mixer forward pass.
+
+TEST INFRASTRUCTURE.  Plain NumPy, float64 / complex128, a Python loop over
+time with each step vectorised over (batch, head, mode, channel).  Slow and
+meant to be read against the pages by eye.
+
+Pages cited (all about arXiv 2605.24330, "Interdomain Attention: Beyond
+Token-Level Key-Value Memory"):
+  p1  "Interdomain Attention: 超越令牌级键值记忆" - Chinese rendering of the
+      arXiv HTML (bittide.aicompass.dev).  Sections 2 (attention as kernel
+      regression, eq. 1; SSMs and HiPPO), 3 (Fig. 1), 3.1 (eqs. 3-6).
+  p2  gist.science German summary, "Technische Zusammenfassung":
+      "Theoretische Herleitung" and "Skalierbare Implementierung".
+  p3  gist.science Dutch summary, "Technische Samenvatting":
+      "Schaalbare Implementatie" (same content as p2).
+
+What the scalable layer computes, per batch row b, head h and position i
+(p2 "Skalierbare Implementierung", all four bullets; p3 the same bullets):
+  1. c = SC(x): causal depthwise short convolution of q and of k.
+  2. xi = SiLU(c) / ||SiLU(c)||^2 over the R = d channels of the head.
+  3. z_k = RMSNorm(xi_k) and z_v = RMSNorm(v), each half with its own
+     per-head gain and bias, before the SSM.
+  4. One complex-diagonal S4D system per head, ZOH-discretised:
+     abar = exp(Delta*lambda), bbar = (abar - 1)/lambda * B.
+  5. Driven by the concatenation [z_k, z_v]:
+     U_m(i) = abar_m U_m(i-1) + bbar_m z_k(i)          (M x R)
+     Gamma_m(i) = abar_m Gamma_m(i-1) + bbar_m z_v(i)  (M x d)
+  6. Mode scores s_m(i) = xi_q(i) . U_m(i)  (F_q U^T, N_q x M; p1 Fig. 1).
+  7. Denominator-free readout o_i = Re sum_m s_m(i) Gamma_m(i)
+     (F_q U^T Gamma; p2 last implementation bullet; eta is dropped).
+
+Readings where the pages are silent (each also listed in the design notes):
+  - the norm in xi is squared as printed on p2/p3, with eps_feat added;
+  - RMSNorm is g * x / sqrt(mean(x^2) + eps_norm) + b, per half;
+  - product convention: plain bilinear, no conjugation anywhere;
+  - tap W-1 of the conv multiplies the current token; no conv bias;
+    history before the first token is zero unless a tail is given;
+  - o_i uses the state after token i; zero initial state unless given.
+
+Parity pins (tests/test_oracle_pins.py):
+  short_conv   pinned: per-channel numpy.convolve (textbook FIR).
+  silu         pinned: scipy.special.expit.
+  feature_map  pinned: ||xi|| * ||y|| = 1 at eps_feat = 0; direction of y.
+  rms_norm     pinned: mean(((z - b)/g)^2) = m/(m + eps) identity.
+  zoh          pinned: quadrature of exp(lambda*tau) and scipy.linalg.expm.
+  forward      pinned: O(N^2) closed form of U, O(N^3) state-free kernel form
+               of o, M=1 real-EMA limit via scipy.signal.lfilter, Delta -> 0
+               limit, causality, row/head independence, split-sequence resume.
+  decode_step  pinned: equals the next position of a longer forward.
+  Parity unpinned (fixed by reading only, no printed value exists): the
+  complex-product convention, eps_feat and eps_norm values, the conv tap
+  order, and the gain/bias shapes.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+C128 = np.complex128
+
+
+def _complex(pair: np.ndarray) -> np.ndarray:
+    """[..., 2] (re, im) float array -> complex128 array."""
+    pair = np.asarray(pair, dtype=F64)
+    return pair[..., 0] + 1j * pair[..., 1]
+
+
+def zoh(log_dt, A, Bc):
+    """Zero-order-hold discretisation of the per-head diagonal S4D system.
+
+    The continuous system u'(t) = lambda u(t) + B z(t) (p1 section 2, "SSMs
+    and HiPPO", with a diagonal complex A as in the S4D core of p2
+    "Skalierbare Implementierung") held constant over a step of length
+    Delta = exp(log_dt) gives abar = exp(Delta*lambda) and
+    bbar = (exp(Delta*lambda) - 1)/lambda * B.
+
+    log_dt [H]; A, Bc [H, M, 2] (re, im).  Returns abar, bbar complex128 [H, M].
+    """
+    dt = np.exp(np.asarray(log_dt, dtype=F64))[:, None]
+    lam = _complex(A)
+    b = _complex(Bc)
+    abar = np.exp(dt * lam)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        bbar = np.where(lam != 0, (abar - 1.0) / lam, dt) * b
+    return abar, bbar
+
+
+def short_conv(x, w, hist):
+    """Causal depthwise short convolution SC (p2 "Skalierbare Implementierung",
+    feature-map bullet: SC is a causal depthwise convolution).
+
+    c(i)_r = sum_{j=0}^{W-1} w[h, r, j] * x(i - W + 1 + j)_r, so tap W-1 is the
+    current token.  Tokens before position 0 come from hist (oldest first).
+
+    x [B, N, H, d]; w [H, d, W]; hist [B, H, W-1, d].  Returns [B, N, H, d].
+    """
+    x = np.asarray(x, dtype=F64)
+    w = np.asarray(w, dtype=F64)
+    B, N, H, d = x.shape
+    W = w.shape[-1]
+    hist = np.asarray(hist, dtype=F64).reshape(B, H, W - 1, d)
+    xp = np.concatenate([hist.transpose(0, 2, 1, 3), x], axis=1)  # [B, N+W-1, H, d]
+    c = np.zeros_like(x)
+    for j in range(W):
+        c += xp[:, j:j + N] * w[None, None, :, :, j]
+    return c
+
+
+def silu(c):
+    """SiLU(c) = c * sigmoid(c) = c / (1 + exp(-c))."""
+    c = np.asarray(c, dtype=F64)
+    with np.errstate(over="ignore"):
+        return c / (1.0 + np.exp(-c))
+
+
+def feature_map(c, eps_feat):
+    """xi = y / (||y||^2 + eps_feat), y = SiLU(c), norm over the last axis
+    (the R channels of one head).  p2/p3 implementation bullets print the
+    squared norm; eps_feat is this build's guard against an all-zero y."""
+    y = silu(c)
+    return y / ((y * y).sum(axis=-1, keepdims=True) + eps_feat)
+
+
+def rms_norm(x, gain, bias, eps_norm):
+    """Input RMSNorm with learnable per-head gain and bias (p2 normalisation
+    bullet): z = g * x / sqrt(mean(x^2) + eps_norm) + b over the last axis.
+
+    x [B, N, H, m]; gain, bias [H, m]."""
+    x = np.asarray(x, dtype=F64)
+    g = np.asarray(gain, dtype=F64)[None, None]
+    b = np.asarray(bias, dtype=F64)[None, None]
+    return g * x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps_norm) + b
+
+
+def ssm_step(U, Gamma, xi_q_i, z_k_i, z_v_i, abar, bbar):
+    """One position of the shared S4D recurrence and its readout.
+
+    The SSM input is the concatenation [z_k, z_v] (p2 recurrent-core bullet);
+    both halves see the same abar, bbar.  Mode scores are the row of F_q U^T
+    for this query (p1 Fig. 1 caption) and the output is the denominator-free
+    readout Re(F_q U^T Gamma) (p2 last implementation bullet), read as a plain
+    bilinear product without conjugation.
+
+    U [B, H, M, R], Gamma [B, H, M, d] complex; xi_q_i, z_k_i [B, H, R];
+    z_v_i [B, H, d]; abar, bbar broadcastable to [B, H, M, 1].
+    Returns (U, Gamma, s [B, H, M], o_i [B, H, d]).
+    """
+    U = abar * U + bbar * z_k_i[:, :, None, :]
+    Gamma = abar * Gamma + bbar * z_v_i[:, :, None, :]
+    s = np.einsum("bhr,bhmr->bhm", xi_q_i, U)
+    o_i = np.einsum("bhm,bhmc->bhc", s, Gamma).real
+    return U, Gamma, s, o_i
+
+
+def forward(q, k, v, params, eps_feat=1e-6, eps_norm=1e-6,
+            state_in=None, tail_in=None, intermediates=False):
+    """Forward pass of the mixer over a block of N tokens.
+
+    q, k, v    [B, N, H, d] (any real dtype; upcast to float64)
+    params     dict: conv_q, conv_k [H, d, W]; gain, bias [H, 2d] (key half
+               then value half); log_dt [H]; A, Bc [H, M, 2]
+    state_in   complex [B, H, M, 2d] (U then Gamma) or None (zeros)
+    tail_in    [B, H, 2, W-1, d] raw q then k tokens before position 0, or None
+
+    Returns (o [B, N, H, d] float64, state_out complex128 [B, H, M, 2d],
+    tail_out [B, H, 2, W-1, d] float64) and, with intermediates=True, a dict
+    of every stage as a fourth element.
+    """
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    B, N, H, d = q.shape
+    W = params["conv_q"].shape[-1]
+    M = params["A"].shape[1]
+    gain = np.asarray(params["gain"], dtype=F64)
+    bias = np.asarray(params["bias"], dtype=F64)
+
+    if tail_in is None:
+        tail_in = np.zeros((B, H, 2, W - 1, d), dtype=F64)
+    tail_in = np.asarray(tail_in, dtype=F64)
+    if state_in is None:
+        state_in = np.zeros((B, H, M, 2 * d), dtype=C128)
+    state_in = np.asarray(state_in, dtype=C128)
+
+    # 1-2. short conv and feature map on queries and keys
+    c_q = short_conv(q, params["conv_q"], tail_in[:, :, 0])
+    c_k = short_conv(k, params["conv_k"], tail_in[:, :, 1])
+    xi_q = feature_map(c_q, eps_feat)
+    xi_k = feature_map(c_k, eps_feat)
+    # 3. input RMSNorm on the key-feature half and the value half
+    z_k = rms_norm(xi_k, gain[:, :d], bias[:, :d], eps_norm)
+    z_v = rms_norm(v, gain[:, d:], bias[:, d:], eps_norm)
+    # 4. ZOH discretisation, one (Delta, lambda, B) per head and mode
+    abar, bbar = zoh(params["log_dt"], params["A"], params["Bc"])
+    a4 = abar[None, :, :, None]
+    b4 = bbar[None, :, :, None]
+
+    # 5-7. recurrence over time, mode scores, readout
+    U = state_in[..., :d].copy()
+    Gamma = state_in[..., d:].copy()
+    o = np.empty((B, N, H, d), dtype=F64)
+    s_all = np.empty((B, N, H, M), dtype=C128) if intermediates else None
+    for i in range(N):
+        U, Gamma, s, o[:, i] = ssm_step(U, Gamma, xi_q[:, i], z_k[:, i], z_v[:, i], a4, b4)
+        if intermediates:
+            s_all[:, i] = s
+
+    state_out = np.concatenate([U, Gamma], axis=-1)
+    # raw tokens that precede the next block, oldest first
+    qp = np.concatenate([tail_in[:, :, 0], q.transpose(0, 2, 1, 3)], axis=2)
+    kp = np.concatenate([tail_in[:, :, 1], k.transpose(0, 2, 1, 3)], axis=2)
+    tail_out = np.stack([qp[:, :, N:], kp[:, :, N:]], axis=2)
+    if not intermediates:
+        return o, state_out, tail_out
+    inter = dict(c_q=c_q, c_k=c_k, xi_q=xi_q, xi_k=xi_k, z_k=z_k, z_v=z_v,
+                 abar=abar, bbar=bbar, s=s_all)
+    return o, state_out, tail_out, inter
+
+
+def decode_step(q_t, k_t, v_t, state, tail, params, eps_feat=1e-6, eps_norm=1e-6):
+    """One autoregressive step: the forward pass with N = 1 from a carried
+    state and conv tail (fixed-size state, O(1) work per token: p1 section 1).
+
+    q_t, k_t, v_t [B, H, d]; state complex [B, H, M, 2d]; tail [B, H, 2, W-1, d].
+    Returns (o_t [B, H, d], new state, new tail)."""
+    o, st, tl = forward(np.asarray(q_t, dtype=F64)[:, None],
+                        np.asarray(k_t, dtype=F64)[:, None],
+                        np.asarray(v_t, dtype=F64)[:, None],
+                        params, eps_feat, eps_norm, state_in=state, tail_in=tail)
+    return o[:, 0], st, tl

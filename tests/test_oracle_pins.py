@@ -1,0 +1,122 @@
+"""The fp64 oracle against its pins (CPU only), and planted mistakes that the
+pins must catch."""
+import numpy as np
+import pytest
+
+from oracle import idattn_oracle as O
+from tests.oracle_pins import PINS
+
+
+@pytest.mark.parametrize("name", sorted(PINS))
+def test_pin(name):
+    fn, tol = PINS[name]
+    err = fn(O)
+    assert err <= tol, f"pin {name}: error {err:.3e} > {tol:.1e}"
+
+
+# ---------------------------------------------------------------- mutations
+def _conv_reversed(x, w, hist):
+    return _orig["short_conv"](x, np.asarray(w)[..., ::-1], hist)
+
+
+def _conv_shift(x, w, hist):
+    # uses x(i - W + j): every tap one token too far in the past
+    x = np.asarray(x, float)
+    hist = np.asarray(hist, float)                       # [B, H, W-1, d]
+    Wm1 = hist.shape[2]
+    full = np.concatenate([hist.transpose(0, 2, 1, 3), x], axis=1)
+    full = np.concatenate([np.zeros_like(full[:, :1]), full[:, :-1]], axis=1)
+    return _orig["short_conv"](full[:, Wm1:], w, full[:, :Wm1].transpose(0, 2, 1, 3))
+
+
+def _silu_sign(c):
+    c = np.asarray(c, float)
+    with np.errstate(over="ignore"):
+        return c / (1.0 + np.exp(c))
+
+
+def _featmap_unsquared(c, eps):
+    y = O.silu(c)
+    return y / (np.sqrt((y * y).sum(-1, keepdims=True)) + eps)
+
+
+def _rms_sum(x, g, b, eps):
+    x = np.asarray(x, float)
+    return np.asarray(g)[None, None] * x / np.sqrt((x * x).sum(-1, keepdims=True) + eps) + np.asarray(b)[None, None]
+
+
+def _rms_no_bias(x, g, b, eps):
+    return _orig["rms_norm"](x, g, np.zeros_like(np.asarray(b, float)), eps)
+
+
+def _zoh_euler(log_dt, A, Bc):
+    abar, _ = _orig["zoh"](log_dt, A, Bc)
+    dt = np.exp(np.asarray(log_dt, float))[:, None]
+    return abar, dt * (np.asarray(Bc, float)[..., 0] + 1j * np.asarray(Bc, float)[..., 1])
+
+
+def _zoh_no_dt(log_dt, A, Bc):
+    return _orig["zoh"](np.zeros_like(np.asarray(log_dt, float)), A, Bc)
+
+
+def _step_read_before_update(U, G, xq, zk, zv, a, b):
+    s = np.einsum("bhr,bhmr->bhm", xq, U)
+    o = np.einsum("bhm,bhmc->bhc", s, G).real
+    U = a * U + b * zk[:, :, None, :]
+    G = a * G + b * zv[:, :, None, :]
+    return U, G, s, o
+
+
+def _step_conj(U, G, xq, zk, zv, a, b):
+    U, G, s, _ = _orig["ssm_step"](U, G, xq, zk, zv, a, b)
+    return U, G, s, np.einsum("bhm,bhmc->bhc", np.conj(s), G).real
+
+
+def _step_swapped_inputs(U, G, xq, zk, zv, a, b):
+    return _orig["ssm_step"](U, G, xq, zv, zk, a, b)
+
+
+def _step_no_bbar_value(U, G, xq, zk, zv, a, b):
+    U = a * U + b * zk[:, :, None, :]
+    G = a * G + zv[:, :, None, :]
+    s = np.einsum("bhr,bhmr->bhm", xq, U)
+    return U, G, s, np.einsum("bhm,bhmc->bhc", s, G).real
+
+
+def _step_imag_dropped(U, G, xq, zk, zv, a, b):
+    U, G, s, _ = _orig["ssm_step"](U, G, xq, zk, zv, a, b)
+    return U, G, s, np.einsum("bhm,bhmc->bhc", s.real, G.real)
+
+
+_orig = {name: getattr(O, name) for name in ("short_conv", "silu", "feature_map", "rms_norm", "zoh", "ssm_step")}
+
+MUTANTS = {
+    "conv_reversed_taps": ("short_conv", _conv_reversed),
+    "conv_off_by_one": ("short_conv", _conv_shift),
+    "silu_wrong_sign": ("silu", _silu_sign),
+    "featmap_unsquared_norm": ("feature_map", _featmap_unsquared),
+    "rms_sum_not_mean": ("rms_norm", _rms_sum),
+    "rms_dropped_bias": ("rms_norm", _rms_no_bias),
+    "zoh_euler_bbar": ("zoh", _zoh_euler),
+    "zoh_missing_delta": ("zoh", _zoh_no_dt),
+    "readout_before_update": ("ssm_step", _step_read_before_update),
+    "conjugated_readout": ("ssm_step", _step_conj),
+    "key_value_inputs_swapped": ("ssm_step", _step_swapped_inputs),
+    "value_bbar_dropped": ("ssm_step", _step_no_bbar_value),
+    "imaginary_parts_dropped": ("ssm_step", _step_imag_dropped),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_planted_mistake_is_caught(mutant, monkeypatch):
+    attr, fn = MUTANTS[mutant]
+    monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for name, (pin, tol) in PINS.items():
+        try:
+            err = pin(O)
+        except Exception:  # a crash also counts as caught
+            err = np.inf
+        if not err <= max(tol, 1e-300) * 10:
+            caught.append(name)
+    assert caught, f"no pin catches mutant {mutant}"
