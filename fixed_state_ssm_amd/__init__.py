@@ -1,0 +1,78 @@
+"""Interdomain Attention token mixer on AMD MI355X (gfx950).
+
+The work runs in libidattn.so (HIP kernels behind a C ABI, include/idattn.h).
+This package holds the ctypes binding (functions named like the C entry
+points) and two conveniences, forward() and decode_step(), that allocate
+outputs and workspace with PyTorch and call the binding on the current
+stream.
+"""
+from __future__ import annotations
+
+from .binding import (ALGO, EXPORTS, IO, LIB_PATH, STATUS, IdattnDims, IdattnError, IdattnParams,
+                      idattn_decode_step, idattn_forward, idattn_forward_workspace_size,
+                      idattn_last_error, idattn_status_string, idattn_version, load_library,
+                      make_dims, make_params)
+
+__all__ = ["ALGO", "EXPORTS", "IO", "LIB_PATH", "STATUS", "IdattnDims", "IdattnError", "IdattnParams",
+           "idattn_decode_step", "idattn_forward", "idattn_forward_workspace_size",
+           "idattn_last_error", "idattn_status_string", "idattn_version", "load_library",
+           "make_dims", "make_params", "forward", "decode_step", "params_to_device"]
+
+PARAM_KEYS = ("conv_q", "conv_k", "gain", "bias", "log_dt", "A", "Bc")
+
+
+def params_to_device(p: dict, device="cuda"):
+    """Copy a dict of float32 arrays/tensors (the idattn_params layout) to the device."""
+    import torch
+    return {k: torch.as_tensor(p[k], dtype=torch.float32).contiguous().to(device) for k in PARAM_KEYS}
+
+
+def _io_name(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    if t.dtype == torch.float32:
+        return "f32"
+    raise TypeError(f"q, k, v must be bfloat16 or float32, got {t.dtype}")
+
+
+def forward(q, k, v, params: dict, *, state_in=None, tail_in=None, return_state=False,
+            algo="auto", eps_feat=1e-6, eps_norm=1e-6, stream=None):
+    """o = mixer(q, k, v) for q, k, v of shape [B, N, H, d] on the GPU.
+
+    params: device tensors (see params_to_device).  state_in: float32
+    [B, H, M, 2d, 2] or None; tail_in: [B, H, 2, W-1, d] in q's dtype or None.
+    With return_state=True returns (o, state_out, tail_out)."""
+    import torch
+    B, N, H, d = q.shape
+    M = params["A"].shape[1]
+    W = params["conv_q"].shape[-1]
+    io = _io_name(q)
+    for t in (k, v):
+        if t.dtype != q.dtype or t.shape != q.shape:
+            raise ValueError("q, k, v must share shape and dtype")
+    dims = make_dims(B, N, H, d, M, W, io, algo, eps_feat, eps_norm)
+    nbytes = idattn_forward_workspace_size(dims)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    state_out = tail_out = None
+    if return_state:
+        state_out = torch.empty((B, H, M, 2 * d, 2), dtype=torch.float32, device=q.device)
+        tail_out = torch.empty((B, H, 2, W - 1, d), dtype=q.dtype, device=q.device)
+    idattn_forward(dims, make_params(params), q, k, v, o, state_in, tail_in, state_out, tail_out,
+                   ws, nbytes, stream)
+    return (o, state_out, tail_out) if return_state else o
+
+
+def decode_step(q_t, k_t, v_t, params: dict, state, tail, *, eps_feat=1e-6, eps_norm=1e-6, stream=None):
+    """One token per sequence: q_t, k_t, v_t [B, H, d]; state float32
+    [B, H, M, 2d, 2] and tail [B, H, 2, W-1, d] are updated in place.
+    Returns o_t [B, H, d]."""
+    import torch
+    B, H, d = q_t.shape
+    M = params["A"].shape[1]
+    W = params["conv_q"].shape[-1]
+    dims = make_dims(B, 1, H, d, M, W, _io_name(q_t), "auto", eps_feat, eps_norm)
+    o_t = torch.empty_like(q_t)
+    idattn_decode_step(dims, make_params(params), q_t, k_t, v_t, o_t, state, tail, stream)
+    return o_t

@@ -1,0 +1,293 @@
+// C-ABI layer of libidattn: argument validation (entirely before any HIP
+// call), workspace sizing, dispatch to the kernels, error text.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/idattn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+idattn_status fail(idattn_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+idattn_status hip_fail(hipError_t e, const char* what) {
+    return fail(IDATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct Range {
+    const char* name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range(const char* name, const void* ptr, size_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
+    return Range{name, lo, ptr ? lo + bytes : lo};
+}
+
+bool overlap(const Range& a, const Range& b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
+
+bool supported_d(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool supported_m(int64_t m) { return m == 16 || m == 32 || m == 64; }
+
+idattn_status check_dims(const idattn_dims* dims, bool decode) {
+    if (dims == nullptr) return fail(IDATTN_ERR_NULL, "dims is NULL");
+    const idattn_dims& D = *dims;
+    if (D.B < 1 || D.H < 1 || D.d < 1 || D.M < 1 || D.W < 1 || D.N < 0)
+        return fail(IDATTN_ERR_SHAPE, "sizes must be positive (N >= 0): B=%lld N=%lld H=%lld d=%lld M=%lld W=%lld",
+                    (long long)D.B, (long long)D.N, (long long)D.H, (long long)D.d, (long long)D.M,
+                    (long long)D.W);
+    if (decode && D.N != 1) return fail(IDATTN_ERR_SHAPE, "decode step needs N == 1, got %lld", (long long)D.N);
+    if (D.io_dtype != IDATTN_IO_F32 && D.io_dtype != IDATTN_IO_BF16)
+        return fail(IDATTN_ERR_ARG, "io_dtype %d is not IDATTN_IO_F32 or IDATTN_IO_BF16", D.io_dtype);
+    if (D.algo != IDATTN_ALGO_AUTO && D.algo != IDATTN_ALGO_SEQUENTIAL && D.algo != IDATTN_ALGO_CHUNKED)
+        return fail(IDATTN_ERR_ARG, "algo %d is not a known idattn_algo", D.algo);
+    if (!(D.eps_feat >= 0.f) || !std::isfinite(D.eps_feat))
+        return fail(IDATTN_ERR_ARG, "eps_feat must be finite and >= 0");
+    if (!(D.eps_norm >= 0.f) || !std::isfinite(D.eps_norm))
+        return fail(IDATTN_ERR_ARG, "eps_norm must be finite and >= 0");
+    // element counts must stay far from int64 overflow
+    const double elems = static_cast<double>(D.B) * D.N * D.H * D.d;
+    const double state = static_cast<double>(D.B) * D.H * D.M * D.d * 4.0;
+    if (elems > 4.0e15 || state > 4.0e15 || D.H > (1 << 24) || D.B > (1LL << 31) || D.N > (1LL << 40))
+        return fail(IDATTN_ERR_SHAPE, "sizes too large");
+    if (!supported_d(D.d))
+        return fail(IDATTN_ERR_UNSUPPORTED, "d=%lld: supported d (= R) are 16, 32, 64, 128", (long long)D.d);
+    if (!supported_m(D.M))
+        return fail(IDATTN_ERR_UNSUPPORTED, "M=%lld: supported M are 16, 32, 64", (long long)D.M);
+    if (D.W > 8) return fail(IDATTN_ERR_UNSUPPORTED, "W=%lld: supported W are 1..8", (long long)D.W);
+    if (D.B * D.H > 0x7fffffffLL)
+        return fail(IDATTN_ERR_UNSUPPORTED, "B*H=%lld exceeds one grid dimension", (long long)(D.B * D.H));
+    return IDATTN_OK;
+}
+
+idattn_status check_params(const idattn_params* prm) {
+    if (prm == nullptr) return fail(IDATTN_ERR_NULL, "params is NULL");
+    if (!prm->conv_q || !prm->conv_k || !prm->gain || !prm->bias || !prm->log_dt || !prm->A || !prm->Bc)
+        return fail(IDATTN_ERR_NULL, "a parameter pointer is NULL");
+    return IDATTN_OK;
+}
+
+idattn::Problem problem(const idattn_dims& D) {
+    idattn::Problem p;
+    p.B = D.B;
+    p.N = D.N;
+    p.H = D.H;
+    p.d = D.d;
+    p.M = D.M;
+    p.W = D.W;
+    p.bf16 = D.io_dtype == IDATTN_IO_BF16;
+    p.eps_feat = D.eps_feat;
+    p.eps_norm = D.eps_norm;
+    return p;
+}
+
+int resolve_algo(const idattn_dims& D) {
+    if (D.algo != IDATTN_ALGO_AUTO) return D.algo;
+    return D.io_dtype == IDATTN_IO_BF16 && idattn::chunked_supported(problem(D)) ? IDATTN_ALGO_CHUNKED
+                                                                                 : IDATTN_ALGO_SEQUENTIAL;
+}
+
+size_t seq_workspace_bytes(const idattn_dims& D) {
+    // xi_q, z_k, z_v: float [B][H][N][d]; s: complex float [B][H][N][M]
+    const size_t tok = static_cast<size_t>(D.B) * D.H * D.N;
+    const size_t a = 3 * tok * D.d * sizeof(float);
+    const size_t s = tok * D.M * 2 * sizeof(float);
+    return ((a + 255) / 256) * 256 + s;
+}
+
+idattn_status workspace_bytes(const idattn_dims& D, int algo, size_t* bytes) {
+    if (D.N == 0) {
+        *bytes = 0;
+        return IDATTN_OK;
+    }
+    if (algo == IDATTN_ALGO_CHUNKED) {
+        const idattn::Problem p = problem(D);
+        if (D.io_dtype != IDATTN_IO_BF16)
+            return fail(IDATTN_ERR_UNSUPPORTED, "the chunked algorithm needs bf16 I/O");
+        if (!idattn::chunked_supported(p))
+            return fail(IDATTN_ERR_UNSUPPORTED, "the chunked algorithm has no kernel for d=%lld M=%lld",
+                        (long long)D.d, (long long)D.M);
+        *bytes = idattn::chunked_workspace_bytes(p);
+    } else {
+        *bytes = seq_workspace_bytes(D);
+    }
+    return IDATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int idattn_version(void) { return 100; }
+
+const char* idattn_status_string(idattn_status st) {
+    switch (st) {
+        case IDATTN_OK: return "IDATTN_OK";
+        case IDATTN_ERR_NULL: return "IDATTN_ERR_NULL";
+        case IDATTN_ERR_SHAPE: return "IDATTN_ERR_SHAPE";
+        case IDATTN_ERR_UNSUPPORTED: return "IDATTN_ERR_UNSUPPORTED";
+        case IDATTN_ERR_WORKSPACE: return "IDATTN_ERR_WORKSPACE";
+        case IDATTN_ERR_ALIAS: return "IDATTN_ERR_ALIAS";
+        case IDATTN_ERR_ARG: return "IDATTN_ERR_ARG";
+        case IDATTN_ERR_HIP: return "IDATTN_ERR_HIP";
+    }
+    return "IDATTN_ERR_UNKNOWN";
+}
+
+const char* idattn_last_error(void) { return g_last_error; }
+
+idattn_status idattn_forward_workspace_size(const idattn_dims* dims, size_t* bytes) {
+    if (bytes == nullptr) return fail(IDATTN_ERR_NULL, "bytes is NULL");
+    idattn_status st = check_dims(dims, false);
+    if (st != IDATTN_OK) return st;
+    return workspace_bytes(*dims, resolve_algo(*dims), bytes);
+}
+
+idattn_status idattn_forward(const idattn_dims* dims, const idattn_params* params, const void* q,
+                             const void* k, const void* v, void* o, const float* state_in,
+                             const void* tail_in, float* state_out, void* tail_out, void* workspace,
+                             size_t workspace_bytes_given, void* stream) {
+    idattn_status st = check_dims(dims, false);
+    if (st != IDATTN_OK) return st;
+    st = check_params(params);
+    if (st != IDATTN_OK) return st;
+    const idattn_dims& D = *dims;
+    const int algo = resolve_algo(D);
+    if (D.N > 0 && (!q || !k || !v || !o)) return fail(IDATTN_ERR_NULL, "q, k, v and o must be non-NULL");
+    size_t need = 0;
+    st = workspace_bytes(D, algo, &need);
+    if (st != IDATTN_OK) return st;
+    if (need > 0 && workspace == nullptr) return fail(IDATTN_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+    if (workspace_bytes_given < need)
+        return fail(IDATTN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_given, need);
+
+    {
+        const void* ptrs[] = {q, k, v, o, state_in, tail_in, state_out, tail_out, workspace};
+        for (const void* ptr : ptrs)
+            if (misaligned(ptr)) return fail(IDATTN_ERR_ARG, "device buffers must be 16-byte aligned");
+    }
+    const size_t io = D.io_dtype == IDATTN_IO_BF16 ? 2 : 4;
+    const size_t act = static_cast<size_t>(D.B) * D.N * D.H * D.d * io;
+    const size_t stb = static_cast<size_t>(D.B) * D.H * D.M * 2 * D.d * 2 * sizeof(float);
+    const size_t tlb = static_cast<size_t>(D.B) * D.H * 2 * (D.W - 1) * D.d * io;
+    const Range rq = range("q", q, act), rk = range("k", k, act), rv = range("v", v, act);
+    const Range ro = range("o", o, act);
+    const Range rsi = range("state_in", state_in, stb), rso = range("state_out", state_out, stb);
+    const Range rti = range("tail_in", tail_in, tlb), rto = range("tail_out", tail_out, tlb);
+    const Range rws = range("workspace", workspace, need);
+    const Range outs[] = {ro, rso, rto, rws};
+    const Range all[] = {rq, rk, rv, ro, rsi, rso, rti, rto, rws};
+    for (const Range& a : outs)
+        for (const Range& b : all) {
+            if (&a == &b || a.name == b.name) continue;
+            if (!overlap(a, b)) continue;
+            // exact in-place pairs are allowed
+            if ((a.name == rso.name && b.name == rsi.name) || (a.name == rto.name && b.name == rti.name)) {
+                if (a.lo == b.lo) continue;
+            }
+            return fail(IDATTN_ERR_ALIAS, "%s overlaps %s", a.name, b.name);
+        }
+    {
+        const size_t conv = static_cast<size_t>(D.H * D.d * D.W) * 4, gb = static_cast<size_t>(D.H * 2 * D.d) * 4;
+        const size_t mb = static_cast<size_t>(D.H * D.M * 2) * 4;
+        const Range prm[] = {range("conv_q", params->conv_q, conv), range("conv_k", params->conv_k, conv),
+                             range("gain", params->gain, gb),        range("bias", params->bias, gb),
+                             range("log_dt", params->log_dt, D.H * 4), range("A", params->A, mb),
+                             range("Bc", params->Bc, mb)};
+        for (const Range& a : outs)
+            for (const Range& b : prm)
+                if (overlap(a, b)) return fail(IDATTN_ERR_ALIAS, "%s overlaps parameter %s", a.name, b.name);
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const idattn::Problem p = problem(D);
+    hipError_t e;
+    if (D.N == 0) {
+        if (state_out) {
+            e = idattn::launch_copy_or_zero(state_in, state_out, static_cast<int64_t>(stb / 4), s);
+            if (e != hipSuccess) return hip_fail(e, "state copy");
+        }
+        if (tail_out && tlb > 0) {
+            e = idattn::launch_copy_or_zero(tail_in, tail_out, static_cast<int64_t>(tlb / 4), s);
+            if (e != hipSuccess) return hip_fail(e, "tail copy");
+        }
+        return IDATTN_OK;
+    }
+
+    if (algo == IDATTN_ALGO_CHUNKED) {
+        e = idattn::launch_forward_chunked(p, *params, q, k, v, o, state_in, tail_in, state_out, workspace, s);
+        if (e != hipSuccess) return hip_fail(e, "chunked forward");
+    } else {
+        const size_t tok = static_cast<size_t>(D.B) * D.H * D.N;
+        float* ws = static_cast<float*>(workspace);
+        float* xi_q = ws;
+        float* z_k = xi_q + tok * D.d;
+        float* z_v = z_k + tok * D.d;
+        float* sbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                               ((3 * tok * D.d * sizeof(float) + 255) / 256) * 256);
+        e = idattn::launch_featmap_conv_norm(p, *params, q, k, v, tail_in, xi_q, z_k, z_v, s);
+        if (e != hipSuccess) return hip_fail(e, "featmap_conv_norm");
+        e = idattn::launch_ssm_key_scan_seq(p, *params, xi_q, z_k, state_in, sbuf, state_out, s);
+        if (e != hipSuccess) return hip_fail(e, "ssm_key_scan");
+        e = idattn::launch_ssm_value_scan_readout_seq(p, *params, sbuf, z_v, state_in, o, state_out, s);
+        if (e != hipSuccess) return hip_fail(e, "ssm_value_scan_readout");
+    }
+    if (tail_out) {
+        e = idattn::launch_tail_update(p, q, k, tail_in, tail_out, s);
+        if (e != hipSuccess) return hip_fail(e, "tail update");
+    }
+    return IDATTN_OK;
+}
+
+idattn_status idattn_decode_step(const idattn_dims* dims, const idattn_params* params, const void* q_t,
+                                 const void* k_t, const void* v_t, void* o_t, float* state, void* tail,
+                                 void* stream) {
+    idattn_status st = check_dims(dims, true);
+    if (st != IDATTN_OK) return st;
+    st = check_params(params);
+    if (st != IDATTN_OK) return st;
+    const idattn_dims& D = *dims;
+    if (!q_t || !k_t || !v_t || !o_t || !state) return fail(IDATTN_ERR_NULL, "q_t, k_t, v_t, o_t and state must be non-NULL");
+    if (D.W > 1 && !tail) return fail(IDATTN_ERR_NULL, "tail must be non-NULL when W > 1");
+    {
+        const void* ptrs[] = {q_t, k_t, v_t, o_t, state, tail};
+        for (const void* ptr : ptrs)
+            if (misaligned(ptr)) return fail(IDATTN_ERR_ARG, "device buffers must be 16-byte aligned");
+    }
+    const size_t io = D.io_dtype == IDATTN_IO_BF16 ? 2 : 4;
+    const size_t tokb = static_cast<size_t>(D.B) * D.H * D.d * io;
+    const size_t stb = static_cast<size_t>(D.B) * D.H * D.M * 2 * D.d * 2 * sizeof(float);
+    const size_t tlb = static_cast<size_t>(D.B) * D.H * 2 * (D.W - 1) * D.d * io;
+    const Range rq = range("q_t", q_t, tokb), rk = range("k_t", k_t, tokb), rv = range("v_t", v_t, tokb);
+    const Range ro = range("o_t", o_t, tokb), rs = range("state", state, stb), rt = range("tail", tail, tlb);
+    const Range outs[] = {ro, rs, rt};
+    const Range all[] = {rq, rk, rv, ro, rs, rt};
+    for (const Range& a : outs)
+        for (const Range& b : all) {
+            if (a.name == b.name) continue;
+            if (overlap(a, b)) return fail(IDATTN_ERR_ALIAS, "%s overlaps %s", a.name, b.name);
+        }
+    const hipError_t e = idattn::launch_decode_step(problem(D), *params, q_t, k_t, v_t, o_t, state, tail,
+                                                    static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode_step");
+    return IDATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,211 @@
+// decode_step: one token per sequence against a carried state held in HBM.
+//
+// One block of 4 waves per (b, h).  Wave 0 first builds the token's features
+// (conv over the tail and the new token, SiLU feature map, per-half RMSNorm)
+// into LDS, shifts the conv tail, and evaluates the ZOH coefficients of all M
+// modes in fp64 (one mode per lane).  Then every wave streams its quarter of
+// the M rows of the complex state [M][2d]: a row is read once as float4s,
+// updated, reduced to s_m over the key half with a wave butterfly, read out
+// into per-lane partial sums of Re(s_m Gamma_m), and written back in place.
+// The state sweep (2 x 128 KiB per (b, h) at d = 128, M = 64) is the whole
+// cost; all loads of a wave's rows are issued before any of them is used.
+#include "common.h"
+#include "launch.h"
+
+namespace idattn {
+
+namespace {
+
+template <bool BF16, int FJ, int RPW>
+__global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_params prm,
+                                                          const void* __restrict__ q_t,
+                                                          const void* __restrict__ k_t,
+                                                          const void* __restrict__ v_t,
+                                                          void* __restrict__ o_t, float* state,
+                                                          void* tail) {
+    // FJ = float4 chunks of a state row per lane (d / 64, at least 1);
+    // RPW = rows per wave (M / 4).
+    __shared__ float xq_s[128], zk_s[128], zv_s[128];
+    __shared__ float4 coef_s[64];
+    __shared__ float part_s[4][128];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x >> 6;
+    const int64_t bh = blockIdx.x;
+    const int64_t h = bh % p.H;
+    const int d = static_cast<int>(p.d), W = static_cast<int>(p.W);
+    const int64_t M = p.M;
+
+    // ---- load this wave's state rows first: the long-latency part
+    const int nf = d;  // float4 chunks per row (4d floats)
+    float4 row[RPW][FJ];
+    float4* st4 = reinterpret_cast<float4*>(state) + bh * M * nf;
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+            const int f = lane + kWave * j;
+            row[rr][j] = f < nf ? st4[(w * RPW + rr) * nf + f] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+
+    if (w == 0) {
+        // features of the new token; lane owns channels lane and lane + 64
+        float yq[2], yk[2], vv[2];
+        float sq = 0.f, sk = 0.f, sv = 0.f;
+        const int64_t tok = bh * d;  // [B][H][d]
+        const int64_t E = 2 * static_cast<int64_t>(W - 1) * d;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int c = lane + kWave * j;
+            float cq = 0.f, ck = 0.f;
+            yq[j] = yk[j] = vv[j] = 0.f;
+            if (c < d) {
+                const float* wq = prm.conv_q + (h * d + c) * W;
+                const float* wk = prm.conv_k + (h * d + c) * W;
+                float hq[8], hk[8];
+                for (int t = 0; t < W - 1; ++t) {
+                    hq[t] = load_io<BF16>(tail, bh * E + static_cast<int64_t>(t) * d + c);
+                    hk[t] = load_io<BF16>(tail, bh * E + static_cast<int64_t>(W - 1 + t) * d + c);
+                }
+                const float xq = load_io<BF16>(q_t, tok + c);
+                const float xk = load_io<BF16>(k_t, tok + c);
+                for (int t = 0; t < W - 1; ++t) {
+                    cq = fmaf(wq[t], hq[t], cq);
+                    ck = fmaf(wk[t], hk[t], ck);
+                }
+                cq = fmaf(wq[W - 1], xq, cq);
+                ck = fmaf(wk[W - 1], xk, ck);
+                // shift the tail by one token (this lane owns channel c)
+                for (int t = 0; t + 1 < W - 1; ++t) {
+                    store_io<BF16>(tail, bh * E + static_cast<int64_t>(t) * d + c, hq[t + 1]);
+                    store_io<BF16>(tail, bh * E + static_cast<int64_t>(W - 1 + t) * d + c, hk[t + 1]);
+                }
+                if (W > 1) {
+                    store_io<BF16>(tail, bh * E + static_cast<int64_t>(W - 2) * d + c, xq);
+                    store_io<BF16>(tail, bh * E + static_cast<int64_t>(2 * W - 3) * d + c, xk);
+                }
+                vv[j] = load_io<BF16>(v_t, tok + c);
+                yq[j] = cq / (1.f + expf(-cq));
+                yk[j] = ck / (1.f + expf(-ck));
+            }
+            sq = fmaf(yq[j], yq[j], sq);
+            sk = fmaf(yk[j], yk[j], sk);
+            sv = fmaf(vv[j], vv[j], sv);
+        }
+        sq = wave_sum(sq);
+        sk = wave_sum(sk);
+        sv = wave_sum(sv);
+        const float inv_q = 1.f / (sq + p.eps_feat);
+        const float inv_k = 1.f / (sk + p.eps_feat);
+        float xk2 = 0.f, xik[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            xik[j] = yk[j] * inv_k;
+            xk2 = fmaf(xik[j], xik[j], xk2);
+        }
+        xk2 = wave_sum(xk2);
+        const float rk = 1.f / sqrtf(xk2 / d + p.eps_norm);
+        const float rv = 1.f / sqrtf(sv / d + p.eps_norm);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int c = lane + kWave * j;
+            if (c < d) {
+                xq_s[c] = yq[j] * inv_q;
+                zk_s[c] = fmaf(prm.gain[h * 2 * d + c] * xik[j], rk, prm.bias[h * 2 * d + c]);
+                zv_s[c] = fmaf(prm.gain[h * 2 * d + d + c] * vv[j], rv, prm.bias[h * 2 * d + d + c]);
+            }
+        }
+        if (lane < M) {
+            const Zoh z = zoh_mode(prm.log_dt[h], prm.A[(h * M + lane) * 2], prm.A[(h * M + lane) * 2 + 1],
+                                   prm.Bc[(h * M + lane) * 2], prm.Bc[(h * M + lane) * 2 + 1]);
+            coef_s[lane] = make_float4(static_cast<float>(z.ar), static_cast<float>(z.ai),
+                                       static_cast<float>(z.br), static_cast<float>(z.bi));
+        }
+    }
+    __syncthreads();
+
+    // ---- state sweep
+    float acc[FJ][2];
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) acc[j][0] = acc[j][1] = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+        const int m = w * RPW + rr;
+        const float4 cf = coef_s[m];
+        float pr = 0.f, pi = 0.f;
+        // complex columns 2f and 2f+1; columns < d belong to U, the rest to Gamma
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+            const int f = lane + kWave * j;
+            if (f < nf) {
+                const int col = 2 * f;
+                const bool key = col < d;
+                const float in0 = key ? zk_s[col] : zv_s[col - d];
+                const float in1 = key ? zk_s[col + 1] : zv_s[col + 1 - d];
+                float4 x = row[rr][j];
+                const float r0 = fmaf(cf.x, x.x, fmaf(-cf.y, x.y, cf.z * in0));
+                const float i0 = fmaf(cf.x, x.y, fmaf(cf.y, x.x, cf.w * in0));
+                const float r1 = fmaf(cf.x, x.z, fmaf(-cf.y, x.w, cf.z * in1));
+                const float i1 = fmaf(cf.x, x.w, fmaf(cf.y, x.z, cf.w * in1));
+                x = make_float4(r0, i0, r1, i1);
+                row[rr][j] = x;
+                if (key) {
+                    pr = fmaf(xq_s[col], r0, fmaf(xq_s[col + 1], r1, pr));
+                    pi = fmaf(xq_s[col], i0, fmaf(xq_s[col + 1], i1, pi));
+                }
+            }
+        }
+        pr = wave_sum(pr);
+        pi = wave_sum(pi);
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+            const int f = lane + kWave * j;
+            if (f < nf && 2 * f >= d) {
+                const float4 x = row[rr][j];
+                acc[j][0] = fmaf(pr, x.x, fmaf(-pi, x.y, acc[j][0]));
+                acc[j][1] = fmaf(pr, x.z, fmaf(-pi, x.w, acc[j][1]));
+            }
+            if (f < nf) st4[m * nf + f] = row[rr][j];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) {
+        const int f = lane + kWave * j;
+        if (f < nf && 2 * f >= d) {
+            part_s[w][2 * f - d] = acc[j][0];
+            part_s[w][2 * f + 1 - d] = acc[j][1];
+        }
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < d; c += 256) {
+        const float sum = (part_s[0][c] + part_s[1][c]) + (part_s[2][c] + part_s[3][c]);
+        store_io<BF16>(o_t, bh * d + c, sum);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_step(const Problem& p, const idattn_params& prm, const void* q_t,
+                              const void* k_t, const void* v_t, void* o_t, float* state,
+                              void* tail, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(p.B * p.H));
+#define IDATTN_DEC(FJ, RPW)                                                                      \
+    do {                                                                                         \
+        if (p.bf16)                                                                              \
+            decode_step_kernel<true, FJ, RPW><<<grid, 256, 0, stream>>>(p, prm, q_t, k_t, v_t, o_t, state, tail); \
+        else                                                                                     \
+            decode_step_kernel<false, FJ, RPW><<<grid, 256, 0, stream>>>(p, prm, q_t, k_t, v_t, o_t, state, tail); \
+    } while (0)
+    const int fj = p.d > 64 ? 2 : 1;
+    const int rpw = static_cast<int>(p.M / 4);
+    if (fj == 2 && rpw == 16) IDATTN_DEC(2, 16);
+    else if (fj == 2 && rpw == 8) IDATTN_DEC(2, 8);
+    else if (fj == 2 && rpw == 4) IDATTN_DEC(2, 4);
+    else if (fj == 1 && rpw == 16) IDATTN_DEC(1, 16);
+    else if (fj == 1 && rpw == 8) IDATTN_DEC(1, 8);
+    else if (fj == 1 && rpw == 4) IDATTN_DEC(1, 4);
+    else return hipErrorInvalidValue;
+#undef IDATTN_DEC
+    return hipGetLastError();
+}
+
+}  // namespace idattn

@@ -1,0 +1,179 @@
+// featmap_conv_norm: causal depthwise short conv of q and k, the SiLU feature
+// map with squared-norm normalisation, and the per-half input RMSNorm
+// (gist.science German summary, "Skalierbare Implementierung": feature-map
+// and normalisation bullets).  Also the conv-tail update and a copy kernel.
+//
+// One wave per token-head; lane l owns channels l and l + 64.  Token-heads are
+// numbered in [B][N][H] order so that neighbouring waves read neighbouring
+// rows of q, k, v.  Outputs go to the workspace in [B][H][N][d] float32 order,
+// which the sequential scans read one (b, h) sequence at a time.
+#include "common.h"
+#include "launch.h"
+
+namespace idattn {
+
+namespace {
+
+template <bool BF16, int DJ>
+__global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
+    Problem p, idattn_params prm, const void* __restrict__ q, const void* __restrict__ k,
+    const void* __restrict__ v, const void* __restrict__ tail_in, float* __restrict__ xi_q,
+    float* __restrict__ z_k, float* __restrict__ z_v) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t th = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t H = p.H, N = p.N;
+    const int d = static_cast<int>(p.d), W = static_cast<int>(p.W);
+    if (th >= p.B * N * H) return;  // whole wave exits; no barriers below
+    const int64_t h = th % H;
+    const int64_t n = (th / H) % N;
+    const int64_t b = th / (H * N);
+
+    float yq[DJ], yk[DJ], xv[DJ];
+    float sq = 0.f, sk = 0.f, sv = 0.f;
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+        const int c = lane + kWave * j;
+        float cq = 0.f, ck = 0.f, vv = 0.f;
+        if (c < d) {
+            const float* wq = prm.conv_q + (h * d + c) * W;
+            const float* wk = prm.conv_k + (h * d + c) * W;
+            for (int t = 0; t < W; ++t) {
+                const int64_t pos = n - (W - 1) + t;
+                float xq = 0.f, xk = 0.f;
+                if (pos >= 0) {
+                    const int64_t idx = ((b * N + pos) * H + h) * d + c;
+                    xq = load_io<BF16>(q, idx);
+                    xk = load_io<BF16>(k, idx);
+                } else if (tail_in != nullptr) {
+                    const int64_t tq = ((b * H + h) * 2 * (W - 1) + (W - 1 + pos)) * d + c;
+                    xq = load_io<BF16>(tail_in, tq);
+                    xk = load_io<BF16>(tail_in, tq + static_cast<int64_t>(W - 1) * d);
+                }
+                cq = fmaf(wq[t], xq, cq);
+                ck = fmaf(wk[t], xk, ck);
+            }
+            vv = load_io<BF16>(v, ((b * N + n) * H + h) * d + c);
+        }
+        // SiLU(c) = c / (1 + exp(-c)); lanes past d hold c = 0 -> y = 0.
+        yq[j] = cq / (1.f + expf(-cq));
+        yk[j] = ck / (1.f + expf(-ck));
+        xv[j] = vv;
+        sq = fmaf(yq[j], yq[j], sq);
+        sk = fmaf(yk[j], yk[j], sk);
+        sv = fmaf(vv, vv, sv);
+    }
+    sq = wave_sum(sq);
+    sk = wave_sum(sk);
+    sv = wave_sum(sv);
+    const float inv_q = 1.f / (sq + p.eps_feat);
+    const float inv_k = 1.f / (sk + p.eps_feat);
+    float xk2 = 0.f;
+    float xik[DJ];
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+        xik[j] = yk[j] * inv_k;
+        xk2 = fmaf(xik[j], xik[j], xk2);
+    }
+    xk2 = wave_sum(xk2);
+    const float rk = 1.f / sqrtf(xk2 / d + p.eps_norm);
+    const float rv = 1.f / sqrtf(sv / d + p.eps_norm);
+    const int64_t orow = ((b * H + h) * N + n) * d;
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+        const int c = lane + kWave * j;
+        if (c < d) {
+            xi_q[orow + c] = yq[j] * inv_q;
+            z_k[orow + c] = fmaf(prm.gain[h * 2 * d + c] * xik[j], rk, prm.bias[h * 2 * d + c]);
+            z_v[orow + c] = fmaf(prm.gain[h * 2 * d + d + c] * xv[j], rv, prm.bias[h * 2 * d + d + c]);
+        }
+    }
+}
+
+// One block per (b, h): read every tail element first, then write, so that
+// tail_out may be tail_in.
+template <bool BF16>
+__global__ __launch_bounds__(256) void tail_update_kernel(Problem p, const void* __restrict__ q,
+                                                          const void* __restrict__ k,
+                                                          const void* tail_in, void* tail_out) {
+    constexpr int kMaxPer = 8;  // 2 * (W-1) * d <= 2 * 7 * 128 = 1792 <= 8 * 256
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / p.H, h = bh % p.H;
+    const int Wm1 = static_cast<int>(p.W) - 1;
+    const int d = static_cast<int>(p.d);
+    const int E = 2 * Wm1 * d;
+    float val[kMaxPer];
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+        const int e = threadIdx.x + 256 * j;
+        val[j] = 0.f;
+        if (e < E) {
+            const int sel = e / (Wm1 * d);          // 0 = q, 1 = k
+            const int t = (e / d) % Wm1;            // slot in the new tail
+            const int c = e % d;
+            const int64_t src = p.N + t;            // index in [tail_in ; x]
+            if (src < Wm1) {
+                if (tail_in != nullptr)
+                    val[j] = load_io<BF16>(tail_in, bh * E + (static_cast<int64_t>(sel) * Wm1 + src) * d + c);
+            } else {
+                const int64_t pos = src - Wm1;
+                val[j] = load_io<BF16>(sel == 0 ? q : k, ((b * p.N + pos) * p.H + h) * d + c);
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+        const int e = threadIdx.x + 256 * j;
+        if (e < E) store_io<BF16>(tail_out, bh * E + e, val[j]);
+    }
+}
+
+__global__ __launch_bounds__(256) void copy_or_zero_kernel(const uint32_t* __restrict__ src,
+                                                           uint32_t* __restrict__ dst, int64_t n) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+        dst[i] = src != nullptr ? src[i] : 0u;
+}
+
+}  // namespace
+
+hipError_t launch_featmap_conv_norm(const Problem& p, const idattn_params& prm, const void* q,
+                                    const void* k, const void* v, const void* tail_in,
+                                    float* xi_q, float* z_k, float* z_v, hipStream_t stream) {
+    const int64_t th = p.B * p.N * p.H;
+    const dim3 grid(static_cast<unsigned>((th + 3) / 4));
+    if (p.d > 64) {
+        if (p.bf16)
+            featmap_conv_norm_kernel<true, 2><<<grid, 256, 0, stream>>>(p, prm, q, k, v, tail_in, xi_q, z_k, z_v);
+        else
+            featmap_conv_norm_kernel<false, 2><<<grid, 256, 0, stream>>>(p, prm, q, k, v, tail_in, xi_q, z_k, z_v);
+    } else {
+        if (p.bf16)
+            featmap_conv_norm_kernel<true, 1><<<grid, 256, 0, stream>>>(p, prm, q, k, v, tail_in, xi_q, z_k, z_v);
+        else
+            featmap_conv_norm_kernel<false, 1><<<grid, 256, 0, stream>>>(p, prm, q, k, v, tail_in, xi_q, z_k, z_v);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_tail_update(const Problem& p, const void* q, const void* k, const void* tail_in,
+                              void* tail_out, hipStream_t stream) {
+    if (p.W <= 1) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(p.B * p.H));
+    if (p.bf16)
+        tail_update_kernel<true><<<grid, 256, 0, stream>>>(p, q, k, tail_in, tail_out);
+    else
+        tail_update_kernel<false><<<grid, 256, 0, stream>>>(p, q, k, tail_in, tail_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_or_zero(const void* src, void* dst, int64_t n_words, hipStream_t stream) {
+    if (n_words <= 0 || src == dst) return hipSuccess;
+    int64_t blocks = (n_words + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    copy_or_zero_kernel<<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(
+        static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst), n_words);
+    return hipGetLastError();
+}
+
+}  // namespace idattn

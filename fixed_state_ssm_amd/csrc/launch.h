@@ -1,0 +1,54 @@
+// Internal launchers of libidattn.  Every launcher enqueues on `stream` and
+// returns hipGetLastError() of its launch; arguments are validated by the
+// C-ABI layer before any launcher is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/idattn.h"
+
+namespace idattn {
+
+struct Problem {
+    int64_t B, N, H, d, M, W;
+    bool bf16;
+    float eps_feat, eps_norm;
+};
+
+// ---- stage kernels of the sequential (fp32) path; workspace layout [B][H][N][*]
+hipError_t launch_featmap_conv_norm(const Problem& p, const idattn_params& prm,
+                                    const void* q, const void* k, const void* v,
+                                    const void* tail_in, float* xi_q, float* z_k,
+                                    float* z_v, hipStream_t stream);
+
+hipError_t launch_ssm_key_scan_seq(const Problem& p, const idattn_params& prm,
+                                   const float* xi_q, const float* z_k,
+                                   const float* state_in, float* s, float* state_out,
+                                   hipStream_t stream);
+
+hipError_t launch_ssm_value_scan_readout_seq(const Problem& p, const idattn_params& prm,
+                                             const float* s, const float* z_v,
+                                             const float* state_in, void* o,
+                                             float* state_out, hipStream_t stream);
+
+// ---- chunked MFMA path (bf16 I/O)
+size_t chunked_workspace_bytes(const Problem& p);
+bool chunked_supported(const Problem& p);
+hipError_t launch_forward_chunked(const Problem& p, const idattn_params& prm,
+                                  const void* q, const void* k, const void* v, void* o,
+                                  const float* state_in, const void* tail_in,
+                                  float* state_out, void* workspace, hipStream_t stream);
+
+// ---- state and tail plumbing
+// tail_out = last W-1 raw tokens of [tail_in (or zeros) ; x]; safe in place.
+hipError_t launch_tail_update(const Problem& p, const void* q, const void* k,
+                              const void* tail_in, void* tail_out, hipStream_t stream);
+// dst = src (or zeros when src is NULL); n_elems 32-bit words.
+hipError_t launch_copy_or_zero(const void* src, void* dst, int64_t n_words, hipStream_t stream);
+
+// ---- decode
+hipError_t launch_decode_step(const Problem& p, const idattn_params& prm,
+                              const void* q_t, const void* k_t, const void* v_t, void* o_t,
+                              float* state, void* tail, hipStream_t stream);
+
+}  // namespace idattn

@@ -1,0 +1,213 @@
+// Sequential fp32 scans: the literal recurrence, one time step after another.
+// This is the all-fp32 path (it keeps the per-step rounding of a plain fp32
+// recurrence) and the reference the chunked path is compared with.
+//
+// ssm_key_scan_seq: one wave per (b, h, mode m); lane l owns channels l, l+64
+// of U_m.  Each step updates U_m(i) = abar U_m(i-1) + bbar z_k(i) and reduces
+// s_m(i) = xi_q(i) . U_m(i) over the R channels with a wave butterfly.
+//
+// ssm_value_scan_readout_seq: one block per (b, h, 64-channel group); wave w
+// owns a contiguous quarter of the modes, lane l one channel, so Gamma_{m,c}
+// stays in registers and o_i,c = Re sum_m s_m(i) Gamma_{m,c}(i) needs only a
+// 4-way cross-wave sum through LDS, done once per block of 16 tokens.
+#include "common.h"
+#include "launch.h"
+
+namespace idattn {
+
+namespace {
+
+constexpr int kTok = 8;  // tokens whose inputs are loaded ahead of the key recurrence
+
+template <int RJ>
+__global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_params prm,
+                                                           const float* __restrict__ xi_q,
+                                                           const float* __restrict__ z_k,
+                                                           const float* state_in,
+                                                           float2* __restrict__ s, float* state_out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t bh = blockIdx.x;
+    const int64_t m = static_cast<int64_t>(blockIdx.y) * 4 + (threadIdx.x >> 6);
+    const int64_t M = p.M, N = p.N;
+    const int d = static_cast<int>(p.d);
+    if (m >= M) return;  // whole wave; no barriers in this kernel
+    const int64_t h = bh % p.H;
+    const Zoh z = zoh_mode(prm.log_dt[h], prm.A[(h * M + m) * 2], prm.A[(h * M + m) * 2 + 1],
+                           prm.Bc[(h * M + m) * 2], prm.Bc[(h * M + m) * 2 + 1]);
+    const float ar = static_cast<float>(z.ar), ai = static_cast<float>(z.ai);
+    const float br = static_cast<float>(z.br), bi = static_cast<float>(z.bi);
+
+    float ur[RJ], ui[RJ];
+    const int64_t st_row = ((bh * M + m) * 2 * d) * 2;  // complex row m of [M][2d], U half first
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+        const int r = lane + kWave * j;
+        ur[j] = ui[j] = 0.f;
+        if (state_in != nullptr && r < d) {
+            ur[j] = state_in[st_row + 2 * r];
+            ui[j] = state_in[st_row + 2 * r + 1];
+        }
+    }
+    const float* xq = xi_q + bh * N * d;
+    const float* zk = z_k + bh * N * d;
+    float2* srow = s + bh * N * M + m;
+    for (int64_t i0 = 0; i0 < N; i0 += kTok) {
+        float xv[kTok][RJ], zv[kTok][RJ];
+#pragma unroll
+        for (int t = 0; t < kTok; ++t)
+#pragma unroll
+            for (int j = 0; j < RJ; ++j) {
+                const int r = lane + kWave * j;
+                const bool ok = (i0 + t < N) && (r < d);
+                xv[t][j] = ok ? xq[(i0 + t) * d + r] : 0.f;
+                zv[t][j] = ok ? zk[(i0 + t) * d + r] : 0.f;
+            }
+#pragma unroll
+        for (int t = 0; t < kTok; ++t) {
+            if (i0 + t >= N) break;
+            float pr = 0.f, pi = 0.f;
+#pragma unroll
+            for (int j = 0; j < RJ; ++j) {
+                const float nr = fmaf(ar, ur[j], fmaf(-ai, ui[j], br * zv[t][j]));
+                const float ni = fmaf(ar, ui[j], fmaf(ai, ur[j], bi * zv[t][j]));
+                ur[j] = nr;
+                ui[j] = ni;
+                pr = fmaf(xv[t][j], nr, pr);
+                pi = fmaf(xv[t][j], ni, pi);
+            }
+            pr = wave_sum(pr);
+            pi = wave_sum(pi);
+            if (lane == 0) srow[(i0 + t) * M] = make_float2(pr, pi);
+        }
+    }
+    if (state_out != nullptr) {
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) {
+            const int r = lane + kWave * j;
+            if (r < d) {
+                state_out[st_row + 2 * r] = ur[j];
+                state_out[st_row + 2 * r + 1] = ui[j];
+            }
+        }
+    }
+}
+
+constexpr int kBlk = 16;  // tokens per LDS round of the value scan
+
+template <bool BF16, int MW>
+__global__ __launch_bounds__(256) void value_scan_seq_kernel(Problem p, idattn_params prm,
+                                                             const float2* __restrict__ s,
+                                                             const float* __restrict__ z_v,
+                                                             const float* state_in, void* __restrict__ o,
+                                                             float* state_out) {
+    __shared__ float2 s_blk[kBlk * 64];
+    __shared__ float red[4][kBlk][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x >> 6;
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / p.H, h = bh % p.H;
+    const int64_t M = p.M, N = p.N, H = p.H;
+    const int d = static_cast<int>(p.d);
+    const int c = static_cast<int>(blockIdx.y) * kWave + lane;
+    const bool cok = c < d;
+
+    float ar[MW], ai[MW], br[MW], bi[MW], gr[MW], gi[MW];
+#pragma unroll
+    for (int mm = 0; mm < MW; ++mm) {
+        const int64_t m = w * MW + mm;
+        const Zoh z = zoh_mode(prm.log_dt[h], prm.A[(h * M + m) * 2], prm.A[(h * M + m) * 2 + 1],
+                               prm.Bc[(h * M + m) * 2], prm.Bc[(h * M + m) * 2 + 1]);
+        ar[mm] = static_cast<float>(z.ar);
+        ai[mm] = static_cast<float>(z.ai);
+        br[mm] = static_cast<float>(z.br);
+        bi[mm] = static_cast<float>(z.bi);
+        gr[mm] = gi[mm] = 0.f;
+        if (state_in != nullptr && cok) {
+            const int64_t idx = ((bh * M + m) * 2 * d + d + c) * 2;
+            gr[mm] = state_in[idx];
+            gi[mm] = state_in[idx + 1];
+        }
+    }
+    const float* zv = z_v + bh * N * d;
+    for (int64_t i0 = 0; i0 < N; i0 += kBlk) {
+        const int nt = static_cast<int>(N - i0 < kBlk ? N - i0 : kBlk);
+        for (int e = threadIdx.x; e < nt * M; e += 256) s_blk[e] = s[(bh * N + i0) * M + e];
+        float zz[kBlk];
+#pragma unroll
+        for (int t = 0; t < kBlk; ++t) zz[t] = (t < nt && cok) ? zv[(i0 + t) * d + c] : 0.f;
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < kBlk; ++t) {
+            if (t < nt) {
+                float acc = 0.f;
+#pragma unroll
+                for (int mm = 0; mm < MW; ++mm) {
+                    const float2 sv = s_blk[t * M + w * MW + mm];
+                    const float nr = fmaf(ar[mm], gr[mm], fmaf(-ai[mm], gi[mm], br[mm] * zz[t]));
+                    const float ni = fmaf(ar[mm], gi[mm], fmaf(ai[mm], gr[mm], bi[mm] * zz[t]));
+                    gr[mm] = nr;
+                    gi[mm] = ni;
+                    acc = fmaf(sv.x, nr, fmaf(-sv.y, ni, acc));
+                }
+                red[w][t][lane] = acc;
+            }
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < nt * kWave; e += 256) {
+            const int t = e / kWave, l = e % kWave;
+            const int cc = static_cast<int>(blockIdx.y) * kWave + l;
+            if (cc < d) {
+                const float sum = (red[0][t][l] + red[1][t][l]) + (red[2][t][l] + red[3][t][l]);
+                store_io<BF16>(o, ((b * N + i0 + t) * H + h) * d + cc, sum);
+            }
+        }
+        __syncthreads();
+    }
+    if (state_out != nullptr && cok) {
+#pragma unroll
+        for (int mm = 0; mm < MW; ++mm) {
+            const int64_t idx = ((bh * M + w * MW + mm) * 2 * d + d + c) * 2;
+            state_out[idx] = gr[mm];
+            state_out[idx + 1] = gi[mm];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_ssm_key_scan_seq(const Problem& p, const idattn_params& prm, const float* xi_q,
+                                   const float* z_k, const float* state_in, float* s,
+                                   float* state_out, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(p.B * p.H), static_cast<unsigned>((p.M + 3) / 4));
+    float2* s2 = reinterpret_cast<float2*>(s);
+    if (p.d > 64)
+        key_scan_seq_kernel<2><<<grid, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, s2, state_out);
+    else
+        key_scan_seq_kernel<1><<<grid, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, s2, state_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_ssm_value_scan_readout_seq(const Problem& p, const idattn_params& prm,
+                                             const float* s, const float* z_v,
+                                             const float* state_in, void* o, float* state_out,
+                                             hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(p.B * p.H), static_cast<unsigned>((p.d + kWave - 1) / kWave));
+    const float2* s2 = reinterpret_cast<const float2*>(s);
+#define IDATTN_VSCAN(MW)                                                                         \
+    do {                                                                                         \
+        if (p.bf16)                                                                              \
+            value_scan_seq_kernel<true, MW><<<grid, 256, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out); \
+        else                                                                                     \
+            value_scan_seq_kernel<false, MW><<<grid, 256, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out); \
+    } while (0)
+    switch (p.M / 4) {
+        case 4: IDATTN_VSCAN(4); break;
+        case 8: IDATTN_VSCAN(8); break;
+        case 16: IDATTN_VSCAN(16); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef IDATTN_VSCAN
+    return hipGetLastError();
+}
+
+}  // namespace idattn

@@ -1,0 +1,165 @@
+/*
+ * idattn.h - C ABI of the Interdomain Attention token mixer on AMD MI355X
+ * (gfx950).  One shared library, libidattn.so; every entry point is plain C
+ * with plain pointers and sizes.
+ *
+ * The method (arXiv 2605.24330, "Interdomain Attention: Beyond Token-Level
+ * Key-Value Memory"; gist.science German summary, "Skalierbare
+ * Implementierung", all four bullets; Chinese rendering of the paper, Fig. 1
+ * caption for the state shapes):
+ *   per batch row b, head h, position i, with R = d channels per head,
+ *   c   = SC(x), a causal depthwise conv of width W, on q and on k
+ *   xi  = SiLU(c) / (||SiLU(c)||^2 + eps_feat)             (norm over R)
+ *   z_k = g_k * xi_k / sqrt(mean(xi_k^2) + eps_norm) + b_k  (RMSNorm, key half)
+ *   z_v = g_v * v    / sqrt(mean(v^2)    + eps_norm) + b_v  (RMSNorm, value half)
+ *   abar_m = exp(Delta lambda_m), bbar_m = (abar_m - 1)/lambda_m * B_m,
+ *   Delta = exp(log_dt_h)                                   (ZOH of S4D)
+ *   U_m(i)     = abar_m U_m(i-1)     + bbar_m z_k(i)         (M x R complex)
+ *   Gamma_m(i) = abar_m Gamma_m(i-1) + bbar_m z_v(i)         (M x d complex)
+ *   s_m(i) = xi_q(i) . U_m(i)                                (row of F_q U^T)
+ *   o_i    = Re sum_m s_m(i) Gamma_m(i)                      (F_q U^T Gamma,
+ *                                                             no denominator)
+ * Products are plain bilinear (no conjugation).  Tap W-1 of the conv
+ * multiplies the current token; history before the first token is zero or
+ * the caller's tail.
+ *
+ * Common rules for every entry point:
+ *  - Ownership: every buffer is owned by the caller.  Device pointers must be
+ *    device memory of the current HIP device, 16-byte aligned (else
+ *    IDATTN_ERR_ARG).  The library never allocates, frees, synchronises, or
+ *    changes the current device.
+ *  - Streams: all device work is enqueued on `stream` (a hipStream_t passed as
+ *    void*; NULL = the null stream).  Calls return after enqueueing.
+ *  - Errors: every argument error is detected and returned before any HIP
+ *    call is made, so validation works on a host without a GPU.  A failed
+ *    kernel launch returns IDATTN_ERR_HIP.  Device faults surface at the
+ *    caller's next synchronisation.  No C++ exception crosses the ABI.
+ *    idattn_last_error() gives a thread-local text for the last failure.
+ *  - NaN and Inf in the inputs propagate; they are not checked.
+ *  - lambda must have a negative real part for a bounded state; this is not
+ *    checked (the values live in device memory).
+ *  - Results are bitwise reproducible for equal inputs and dims: no float
+ *    atomics.
+ */
+#ifndef IDATTN_H
+#define IDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum idattn_status {
+    IDATTN_OK = 0,
+    IDATTN_ERR_NULL = 1,         /* a required pointer is NULL                  */
+    IDATTN_ERR_SHAPE = 2,        /* a size is out of range or inconsistent      */
+    IDATTN_ERR_UNSUPPORTED = 3,  /* a valid size this library has no kernel for */
+    IDATTN_ERR_WORKSPACE = 4,    /* workspace missing or too small              */
+    IDATTN_ERR_ALIAS = 5,        /* buffers overlap in a way that is not allowed */
+    IDATTN_ERR_ARG = 6,          /* an enum or epsilon value is invalid          */
+    IDATTN_ERR_HIP = 7           /* the HIP runtime reported an error            */
+} idattn_status;
+
+typedef enum idattn_io_dtype {
+    IDATTN_IO_F32 = 0,   /* q, k, v, o and tails in float32  */
+    IDATTN_IO_BF16 = 1   /* q, k, v, o and tails in bfloat16 */
+} idattn_io_dtype;
+
+typedef enum idattn_algo {
+    IDATTN_ALGO_AUTO = 0,        /* CHUNKED for bf16 I/O, SEQUENTIAL for f32 I/O          */
+    IDATTN_ALGO_SEQUENTIAL = 1,  /* fp32 recurrence, one time step after another         */
+    IDATTN_ALGO_CHUNKED = 2      /* chunked parallel-in-time scan, fp16 MFMA operands,
+                                    fp32 accumulation and state; bf16 I/O only            */
+} idattn_algo;
+
+/* Sizes.  R == d.  Layout of q, k, v, o: contiguous [B][N][H][d]. */
+typedef struct idattn_dims {
+    int64_t B;        /* batch rows, >= 1                                     */
+    int64_t N;        /* tokens in this call, >= 0 (forward) or == 1 (decode) */
+    int64_t H;        /* heads, >= 1                                          */
+    int64_t d;        /* channels per head (= R); supported 16, 32, 64, 128   */
+    int64_t M;        /* complex modes per head; supported 16, 32, 64         */
+    int64_t W;        /* short-conv width; supported 1..8                     */
+    int32_t io_dtype; /* idattn_io_dtype                                      */
+    int32_t algo;     /* idattn_algo                                          */
+    float eps_feat;   /* >= 0: xi = y / (||y||^2 + eps_feat)                   */
+    float eps_norm;   /* >= 0: RMSNorm sqrt(mean(x^2) + eps_norm)              */
+} idattn_dims;
+
+/* Per-head parameters, all float32 device buffers, read only. */
+typedef struct idattn_params {
+    const float *conv_q;  /* [H][d][W]; tap W-1 multiplies the current token */
+    const float *conv_k;  /* [H][d][W]                                        */
+    const float *gain;    /* [H][2d]: key-feature half, then value half       */
+    const float *bias;    /* [H][2d]: key-feature half, then value half       */
+    const float *log_dt;  /* [H]: Delta_h = exp(log_dt[h])                    */
+    const float *A;       /* [H][M][2]: lambda (re, im), Re < 0               */
+    const float *Bc;      /* [H][M][2]: B (re, im)                            */
+} idattn_params;
+
+/*
+ * Carried state (the method's fixed-size memory; the Chinese rendering, Fig. 1
+ * caption, gives U as M x R and Gamma as M x d):
+ *   state: float32 [B][H][M][2d][2] = complex64 [B][H][M][2d] interleaved
+ *          (re, im); columns 0..d-1 hold U_m, columns d..2d-1 hold Gamma_m.
+ *   tail:  io dtype [B][H][2][W-1][d]: the last W-1 raw (pre-conv) q tokens,
+ *          then the last W-1 raw k tokens, oldest first.
+ */
+
+/* Bytes of device workspace idattn_forward needs for these dims (0 is
+ * possible).  Returns IDATTN_OK and sets *bytes, or an argument error. */
+idattn_status idattn_forward_workspace_size(const idattn_dims *dims, size_t *bytes);
+
+/*
+ * Forward pass over N tokens of every batch row (the scalable layer of the
+ * gist.science summaries, "Skalierbare Implementierung": feature map, input
+ * RMSNorm, S4D recurrence on [xi(k), v], denominator-free readout).
+ *
+ *  q, k, v   in   [B][N][H][d] io dtype
+ *  o         out  [B][N][H][d] io dtype; must not overlap q, k, v
+ *  state_in  in   NULL (zero state) or state layout above
+ *  tail_in   in   NULL (zero conv history) or tail layout above
+ *  state_out out  NULL or state layout; may equal state_in exactly (in place)
+ *  tail_out  out  NULL or tail layout; may equal tail_in exactly (in place)
+ *  workspace      device memory of at least idattn_forward_workspace_size bytes
+ *  stream         hipStream_t as void*
+ * N == 0 is allowed: o is not touched; state_out/tail_out receive state_in/
+ * tail_in (or zeros).  Any partial overlap among the buffers is rejected.
+ */
+idattn_status idattn_forward(const idattn_dims *dims, const idattn_params *params,
+                             const void *q, const void *k, const void *v, void *o,
+                             const float *state_in, const void *tail_in,
+                             float *state_out, void *tail_out,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One autoregressive step for every batch row (O(1) work and a fixed-size
+ * state per token: Chinese rendering, section 1; German summary,
+ * "Problemstellung").  dims->N must be 1.
+ *
+ *  q_t, k_t, v_t in  [B][H][d] io dtype
+ *  o_t          out  [B][H][d] io dtype
+ *  state     in/out  state layout, updated in place
+ *  tail      in/out  tail layout, shifted in place by one token
+ * No workspace.  o_t must not overlap any other buffer.
+ */
+idattn_status idattn_decode_step(const idattn_dims *dims, const idattn_params *params,
+                                 const void *q_t, const void *k_t, const void *v_t, void *o_t,
+                                 float *state, void *tail, void *stream);
+
+/* Static text for a status code ("IDATTN_OK", ...). */
+const char *idattn_status_string(idattn_status status);
+
+/* Thread-local detail of the last non-OK status returned on this thread. */
+const char *idattn_last_error(void);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int idattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IDATTN_H */

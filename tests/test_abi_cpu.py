@@ -1,0 +1,166 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+the header declares, and rejects bad arguments before making any HIP call
+(all failing calls below return from validation; no kernel is launched)."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import fixed_state_ssm_amd as fs
+from fixed_state_ssm_amd.binding import IdattnDims, IdattnParams
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "idattn.h")
+
+FAKE = 0x10000000  # an address that validation never dereferences
+
+
+def header_entry_points():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(idattn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_entry_point():
+    lib = fs.load_library()
+    names = header_entry_points()
+    assert set(names) == set(fs.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fs.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (idattn_\w+)$", out, re.M))
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_header():
+    src = r"""
+    #include <stdio.h>
+    #include <stddef.h>
+    #include "idattn.h"
+    int main(void) {
+      printf("%zu %zu %zu %zu %zu %zu\n", sizeof(idattn_dims), offsetof(idattn_dims, io_dtype),
+             offsetof(idattn_dims, eps_norm), sizeof(idattn_params), offsetof(idattn_params, log_dt),
+             offsetof(idattn_params, Bc));
+      return 0;
+    }"""
+    with tempfile.TemporaryDirectory() as td:
+        c = os.path.join(td, "t.c")
+        exe = os.path.join(td, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        got = list(map(int, subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()))
+    want = [ctypes.sizeof(IdattnDims), IdattnDims.io_dtype.offset, IdattnDims.eps_norm.offset,
+            ctypes.sizeof(IdattnParams), IdattnParams.log_dt.offset, IdattnParams.Bc.offset]
+    assert got == want
+
+
+def test_status_strings_and_version():
+    for code, name in fs.STATUS.items():
+        assert fs.idattn_status_string(code) == name
+    assert fs.idattn_status_string(99) == "IDATTN_ERR_UNKNOWN"
+    assert fs.idattn_version() >= 100
+
+
+def dims(**kw):
+    base = dict(B=2, N=64, H=3, d=64, M=32, W=4, io="bf16", algo="auto")
+    base.update(kw)
+    return fs.make_dims(**base)
+
+
+def params(**kw):
+    vals = {k: FAKE + 0x1000000 * (i + 1) for i, k in enumerate(("conv_q", "conv_k", "gain", "bias", "log_dt", "A", "Bc"))}
+    vals.update(kw)
+    return IdattnParams(*(vals[k] for k in ("conv_q", "conv_k", "gain", "bias", "log_dt", "A", "Bc")))
+
+
+QB = 0x200000000  # q, k, v, o, ... spaced far apart
+ADDR = dict(q=QB, k=2 * QB, v=3 * QB, o=4 * QB, si=5 * QB, ti=6 * QB, so=7 * QB, to=8 * QB, ws=9 * QB)
+
+
+def call_forward(d, p, ws_bytes=None, **over):
+    a = dict(ADDR)
+    a.update(over)
+    if ws_bytes is None:
+        try:
+            ws_bytes = fs.idattn_forward_workspace_size(d)
+        except fs.IdattnError:
+            ws_bytes = 0
+    lib = fs.load_library()
+    return lib.idattn_forward(ctypes.byref(d), ctypes.byref(p), a["q"], a["k"], a["v"], a["o"], a["si"], a["ti"],
+                              a["so"], a["to"], a["ws"], ws_bytes, None)
+
+
+def expect(status, name):
+    assert fs.STATUS[status] == name, (fs.STATUS[status], fs.idattn_last_error())
+
+
+@pytest.mark.parametrize("field,value,name", [
+    ("B", 0, "IDATTN_ERR_SHAPE"), ("H", -1, "IDATTN_ERR_SHAPE"), ("N", -5, "IDATTN_ERR_SHAPE"),
+    ("W", 0, "IDATTN_ERR_SHAPE"), ("d", 48, "IDATTN_ERR_UNSUPPORTED"), ("d", 256, "IDATTN_ERR_UNSUPPORTED"),
+    ("M", 8, "IDATTN_ERR_UNSUPPORTED"), ("M", 128, "IDATTN_ERR_UNSUPPORTED"), ("W", 9, "IDATTN_ERR_UNSUPPORTED"),
+    ("io", 7, "IDATTN_ERR_ARG"), ("algo", 9, "IDATTN_ERR_ARG"), ("eps_feat", -1.0, "IDATTN_ERR_ARG"),
+    ("eps_norm", float("nan"), "IDATTN_ERR_ARG"), ("eps_norm", float("inf"), "IDATTN_ERR_ARG"),
+])
+def test_forward_rejects_bad_dims(field, value, name):
+    d = dims(**{field: value})
+    expect(call_forward(d, params(), ws_bytes=1 << 40), name)
+    assert fs.idattn_last_error()
+
+
+def test_forward_rejects_null_pointers():
+    lib = fs.load_library()
+    d = dims()
+    assert fs.STATUS[lib.idattn_forward(None, ctypes.byref(params()), *([None] * 9), 0, None)] == "IDATTN_ERR_NULL"
+    expect(call_forward(d, params(A=0)), "IDATTN_ERR_NULL")
+    expect(call_forward(d, params(), q=0), "IDATTN_ERR_NULL")
+    expect(call_forward(d, params(), o=0), "IDATTN_ERR_NULL")
+    expect(call_forward(d, params(), ws=0), "IDATTN_ERR_WORKSPACE")
+
+
+def test_forward_rejects_small_workspace():
+    d = dims()
+    need = fs.idattn_forward_workspace_size(d)
+    assert need > 0
+    expect(call_forward(d, params(), ws_bytes=need - 1), "IDATTN_ERR_WORKSPACE")
+
+
+def test_chunked_needs_bf16():
+    with pytest.raises(fs.IdattnError) as e:
+        fs.idattn_forward_workspace_size(dims(io="f32", algo="chunked"))
+    assert e.value.status_name == "IDATTN_ERR_UNSUPPORTED"
+
+
+def test_workspace_size_zero_tokens():
+    assert fs.idattn_forward_workspace_size(dims(N=0)) == 0
+
+
+@pytest.mark.parametrize("over,name", [
+    (dict(o=ADDR["q"] + 64), "IDATTN_ERR_ALIAS"),               # o overlaps q
+    (dict(so=ADDR["si"] + 16), "IDATTN_ERR_ALIAS"),              # partial state overlap
+    (dict(to=ADDR["ti"] + 16), "IDATTN_ERR_ALIAS"),              # partial tail overlap
+    (dict(ws=ADDR["v"]), "IDATTN_ERR_ALIAS"),                   # workspace over v
+    (dict(so=ADDR["o"]), "IDATTN_ERR_ALIAS"),                   # state_out over o
+    (dict(o=FAKE + 0x3000000), "IDATTN_ERR_ALIAS"),             # o over a parameter
+    (dict(q=ADDR["q"] + 2), "IDATTN_ERR_ARG"),                  # misaligned
+])
+def test_forward_rejects_aliasing(over, name):
+    expect(call_forward(dims(), params(), **over), name)
+
+
+def test_decode_validation():
+    lib = fs.load_library()
+    p = params()
+
+    def dec(d, **over):
+        a = dict(q=QB, k=2 * QB, v=3 * QB, o=4 * QB, s=5 * QB, t=6 * QB)
+        a.update(over)
+        return lib.idattn_decode_step(ctypes.byref(d), ctypes.byref(p), a["q"], a["k"], a["v"], a["o"], a["s"], a["t"], None)
+
+    expect(dec(dims(N=2)), "IDATTN_ERR_SHAPE")
+    expect(dec(dims(N=1), s=0), "IDATTN_ERR_NULL")
+    expect(dec(dims(N=1), t=0), "IDATTN_ERR_NULL")
+    expect(dec(dims(N=1), o=QB + 16), "IDATTN_ERR_ALIAS")
+    expect(dec(dims(N=1), s=5 * QB + 4), "IDATTN_ERR_ARG")
+    expect(dec(dims(N=1, d=100)), "IDATTN_ERR_UNSUPPORTED")

@@ -22,8 +22,10 @@ bf16_bits() gives the 16-bit patterns that a device buffer holds.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 
 import numpy as np
 
@@ -65,9 +67,9 @@ def _rng(seed: int, tag: int, kind: int, row: int = 0) -> np.random.Generator:
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> bfloat16 bit patterns (uint16), round to nearest even."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+    u = x.view(np.uint32)
+    # for every non-NaN pattern u + 0x7FFF + 1 stays below 2**32
+    r = ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         r[nan] = np.uint16(0x7FC0)
@@ -85,9 +87,28 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return bf16_from_bits(bf16_bits(x))
 
 
+def _round_bf16_inplace(x: np.ndarray, block: int = 1 << 18) -> None:
+    """Round a contiguous float32 array to bfloat16 values in place, in
+    cache-sized blocks (same rounding as bf16_bits)."""
+    flat = x.reshape(-1)
+    u_all = flat.view(np.uint32)
+    nan = np.isnan(flat)
+    for i in range(0, u_all.size, block):
+        u = u_all[i:i + block]
+        t = u >> np.uint32(16)
+        t &= np.uint32(1)
+        t += np.uint32(0x7FFF)
+        u += t
+        u &= np.uint32(0xFFFF0000)
+    if nan.any():
+        u_all[nan] = np.uint32(0x7FC00000)
+
+
 def _store(x: np.ndarray, io: str) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
-    return bf16_round(x) if io == "bf16" else x
+    if io == "bf16":
+        _round_bf16_inplace(x)
+    return x
 
 
 # ---------------------------------------------------------------- parameters
@@ -129,11 +150,23 @@ def make_rows(s: dict, rows=None, seed: int = 0, N: int | None = None):
     q = np.empty((len(rows), n, H, d), dtype=np.float32)
     k = np.empty_like(q)
     v = np.empty_like(q)
-    for i, b in enumerate(rows):
+
+    def one(i_b):
+        i, b = i_b
         g = _rng(seed, s["tag"], KIND_ROW, b)
-        q[i] = _store(g.standard_normal((n, H, d), dtype=np.float32), s["io"])
-        k[i] = _store(g.standard_normal((n, H, d), dtype=np.float32), s["io"])
-        v[i] = _store(g.standard_normal((n, H, d), dtype=np.float32), s["io"])
+        for arr in (q, k, v):
+            g.standard_normal(out=arr[i], dtype=np.float32)
+            if s["io"] == "bf16":
+                _round_bf16_inplace(arr[i])
+
+    # rows are independent streams; numpy releases the GIL while drawing
+    workers = min(len(rows), os.cpu_count() or 1, 16)
+    if workers > 1:
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one, enumerate(rows)))
+    else:
+        for item in enumerate(rows):
+            one(item)
     return q, k, v
 
 
