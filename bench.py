@@ -1,0 +1,257 @@
+"""Benchmark of the Interdomain Attention mixer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1p3b]
+
+A step is one idattn_forward over the whole workload batch (short conv,
+feature map, RMSNorm, ZOH tables, key scan, value scan + readout, state and
+tail emission), inputs already resident in HBM.  Three copies of the inputs
+are rotated so that consecutive steps do not re-read the previous step's
+bytes from the 256 MB last-level cache.  Prints one JSON line.
+
+The roofline object covers the forward launch: algorithmic bytes (read q, k,
+v once, write o once: 8 d bytes per token-head in bf16) divided by the mean
+duration of the forward measured with HIP events on the launch stream.
+Traffic (bytes actually moved, from rocprofv3 FETCH_SIZE / WRITE_SIZE) comes
+from the committed profile summary when it was taken on the current kernel
+source, else null.
+
+The CPU baseline is the fp64 oracle, single-threaded, on a bounded sample of
+the same workload (batch row 0, every head, a prefix of the sequence).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "mixer tokens/sec fwd (1.3B shape, N=4096) + % of HBM roofline, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+FP32_PEAK_TFLOPS = 157.3
+FP16_MFMA_PEAK_TFLOPS = 2500.0
+KERNEL_SOURCES = ["fixed_state_ssm_amd/csrc/chunked.hip", "fixed_state_ssm_amd/csrc/featmap.hip",
+                  "fixed_state_ssm_amd/csrc/scan_seq.hip", "fixed_state_ssm_amd/csrc/common.h",
+                  "fixed_state_ssm_amd/csrc/api.cpp"]
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(config: str, algo: str):
+    """Bytes per launch from profiles/forward_<algo>__<config>_traffic.md if
+    its recorded source hash matches the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"forward_{algo}__{config}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"^source_sha:\s*(\w+)", text, re.M)
+    m_b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_sha or not m_b or m_sha.group(1) != source_sha():
+        return None
+    return float(m_b.group(1))
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="1p3b", choices=["125m", "1p3b", "14k"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "sequential", "chunked"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(s, q, k, v, params, target_s: float):
+    """The oracle as it stands, one thread, on row 0 / all heads / a prefix."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    with threadpool_limits(limits=1):
+        n0 = 32
+        t = time.perf_counter()
+        oracle.forward(q[:1, :n0], k[:1, :n0], v[:1, :n0], params)
+        per_tok = (time.perf_counter() - t) / n0
+        n = int(max(n0, min(s["N"], target_s / max(per_tok, 1e-9))))
+        t = time.perf_counter()
+        o, _, _ = oracle.forward(q[:1, :n], k[:1, :n], v[:1, :n], params)
+        dt = time.perf_counter() - t
+    assert np.isfinite(o).all()
+    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"batch row 0, all {s['H']} heads, first {n} of {s['N']} tokens "
+                      f"({dt:.1f} s, fp64 NumPy, 1 thread)"}
+
+
+def measure_copy_gbps(torch, nbytes=2 << 30):
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    del a, b
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def decode_bench(torch, fs, steps, warmup):
+    """Decode workload: 256 sequences x 16 heads, d = R = 128, M = 64, prefilled
+    by a 2048-token forward on N(0,1) inputs drawn on the device, then one
+    token per sequence per step (state updated in place)."""
+    import workloads as WL
+    s = WL.spec("decode")
+    B, N, H, d, M, W = s["B"], s["N"], s["H"], s["d"], s["M"], s["W"]
+    p = fs.params_to_device(WL.make_params(s))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    x = [torch.randn((B, N, H, d), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3)]
+    _, state, tail = fs.forward(x[0], x[1], x[2], p, return_state=True)
+    del x
+    tok = [torch.randn((B, H, d), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3)]
+    o_t = torch.empty_like(tok[0])
+    dims = fs.make_dims(B, 1, H, d, M, W, "bf16")
+    prm = fs.make_params(p)
+    for _ in range(warmup):
+        fs.idattn_decode_step(dims, prm, tok[0], tok[1], tok[2], o_t, state, tail)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record()
+        fs.idattn_decode_step(dims, prm, tok[0], tok[1], tok[2], o_t, state, tail)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    med = ms[len(ms) // 2]
+    nbytes = 2 * B * H * M * 2 * d * 8 + 4 * B * H * d * 2 + 2 * B * H * 2 * (W - 1) * d * 2
+    return {"workload": "decode: 256 sequences x 16 heads, d=R=128, M=64, W=4, bf16 I/O, fp32 state "
+                        "prefilled by a 2048-token forward",
+            "tokens_per_s": B / (med * 1e-3), "ms_per_step_median": med,
+            "roofline": {"bound": "hbm", "achieved": nbytes / (med * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                         "algorithmic_bytes": nbytes}}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the mixer forward needs no "
+              f"collective and this build runs on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import fixed_state_ssm_amd as fs
+    import workloads as WL
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fs.load_library()
+    s = WL.spec(args.config)
+    B, N, H, d, M, W = s["B"], s["N"], s["H"], s["d"], s["M"], s["W"]
+    q, k, v = WL.make_rows(s)
+    params = WL.make_params(s)
+    p = fs.params_to_device(params)
+    prm = fs.make_params(p)
+
+    def up(x):
+        return torch.from_numpy(WL.bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    sets = []
+    base = [up(q), up(k), up(v)]
+    for r in range(3):
+        sets.append([t.clone() for t in base] + [torch.empty_like(base[0])])
+    del base
+    state_out = torch.empty((B, H, M, 2 * d, 2), dtype=torch.float32, device="cuda")
+    tail_out = torch.empty((B, H, 2, W - 1, d), dtype=torch.bfloat16, device="cuda")
+    dims = fs.make_dims(B, N, H, d, M, W, "bf16", args.algo)
+    nbytes = fs.idattn_forward_workspace_size(dims)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    algo = args.algo
+    if algo == "auto":
+        try:
+            fs.idattn_forward_workspace_size(fs.make_dims(B, N, H, d, M, W, "bf16", "chunked"))
+            algo = "chunked"
+        except fs.IdattnError:
+            algo = "sequential"
+
+    def step(i):
+        qq, kk, vv, oo = sets[i % len(sets)]
+        fs.idattn_forward(dims, prm, qq, kk, vv, oo, None, None, state_out, tail_out, ws, nbytes)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i, (e0, e1) in enumerate(ev):
+        e0.record()
+        step(i)
+        e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    mean_launch_ms = sum(launch_ms) / len(launch_ms)
+    wall = t1 - t0
+    tokens = B * N * args.steps
+    alg_bytes = B * N * H * d * 2 * 4
+    achieved = alg_bytes / (mean_launch_ms * 1e-3) / 1e9
+    flops_literal = 14.0 * M * 2 * d * B * N * H
+
+    out = {
+        "metric": METRIC,
+        "value": tokens / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if algo == "sequential" else "f16-mfma/f32",
+        "data": "synthetic (seeded N(0,1) bf16 q,k,v; S4D-Lin init)",
+        "config": {"workload": f"{args.config}: B={B} H={H} N={N} d=R={d} M={M} W={W}, bf16 I/O, fp32 state",
+                   "B": B, "N": N, "H": H, "d": d, "M": M, "W": W, "io": "bf16", "algo": algo},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": committed_traffic(args.config, algo),
+                     "kernel": "idattn_forward launch (all kernels of one forward, HIP events on the launch stream)",
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "launch_ms_mean": mean_launch_ms, "launch_ms_min": min(launch_ms)},
+        "flops": {"literal_per_launch": flops_literal,
+                  "literal_tflops": flops_literal / (mean_launch_ms * 1e-3) / 1e12,
+                  "frac_fp32_peak": flops_literal / (mean_launch_ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS},
+        "source_sha": source_sha(),
+    }
+    out["measured_copy_gbps"] = measure_copy_gbps(torch)
+    if not args.no_decode:
+        out["decode"] = decode_bench(torch, fs, steps=20, warmup=3)
+    del sets, ws
+    torch.cuda.empty_cache()
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(s, q, k, v, params, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
