@@ -77,7 +77,9 @@ def parse():
 
 
 def cpu_baseline(s, q, k, v, params, target_s: float):
-    """The oracle as it stands, one thread, on row 0 / all heads / a prefix."""
+    """The oracle as it stands, one thread, on a bounded sample: the first
+    batch rows (every head), whole sequences when they fit the time target,
+    else a prefix of row 0."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -86,14 +88,16 @@ def cpu_baseline(s, q, k, v, params, target_s: float):
         n0 = 32
         t = time.perf_counter()
         oracle.forward(q[:1, :n0], k[:1, :n0], v[:1, :n0], params)
-        per_tok = (time.perf_counter() - t) / n0
-        n = int(max(n0, min(s["N"], target_s / max(per_tok, 1e-9))))
+        per_tok = (time.perf_counter() - t) / n0  # one row, every head
+        budget_tok = target_s / max(per_tok, 1e-9)
+        rows = int(max(1, min(s["B"], budget_tok // s["N"])))
+        n = int(max(n0, min(s["N"], budget_tok)))
         t = time.perf_counter()
-        o, _, _ = oracle.forward(q[:1, :n], k[:1, :n], v[:1, :n], params)
+        o, _, _ = oracle.forward(q[:rows, :n], k[:rows, :n], v[:rows, :n], params)
         dt = time.perf_counter() - t
     assert np.isfinite(o).all()
-    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"batch row 0, all {s['H']} heads, first {n} of {s['N']} tokens "
+    return {"value": rows * n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"batch rows 0..{rows - 1}, all {s['H']} heads, first {n} of {s['N']} tokens "
                       f"({dt:.1f} s, fp64 NumPy, 1 thread)"}
 
 

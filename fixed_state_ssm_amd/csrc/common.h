@@ -33,6 +33,19 @@ __device__ __forceinline__ void store_io(void* base, int64_t idx, float x) {
     else static_cast<float*>(base)[idx] = x;
 }
 
+// ------------------------------------------------------------------ barriers
+// Workgroup barrier that waits only for this wave's LDS operations.  Unlike
+// __syncthreads() it does not wait for outstanding global loads, so loads
+// issued ahead of time (prefetch) stay in flight across it.  Use it only
+// where no other wave reads global memory this wave wrote before it.
+// It is also a scheduling fence: the compiler keeps every instruction on its
+// side, which bounds how many registers one phase of a kernel can hold.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // ------------------------------------------------------------------ reductions
 // Butterfly sum over the 64 lanes of a wave; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float x) {
