@@ -16,7 +16,8 @@ from the committed profile summary when it was taken on the current kernel
 source, else null.
 
 The CPU baseline is the fp64 oracle, single-threaded, on a bounded sample of
-the same workload (batch row 0, every head, a prefix of the sequence).
+the same workload (the first batch rows with every head and whole sequences,
+or a prefix of row 0 when one row exceeds the time target).
 """
 from __future__ import annotations
 
