@@ -11,7 +11,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libidattn.so")
-SOURCES = ["api.cpp", "featmap.hip", "scan_seq.hip", "chunked.hip", "chunked_d128.hip", "decode.hip"]
+SOURCES = ["api.cpp", "featmap.hip", "scan_seq.hip", "chunked.hip", "chunked_ws.hip", "decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

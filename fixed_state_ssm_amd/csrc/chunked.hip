@@ -953,14 +953,14 @@ void plan_segments(const Problem& p, int& S, int64_t& Lseg) {
 
 bool chunked_supported(const Problem& p) {
     if (!(p.bf16 && p.M == MM && (p.d == 64 || p.d == 128) && p.W >= 1 && p.W <= kMaxW)) return false;
-    // the d = 128 kernels address one (b, h) sequence with 32-bit byte offsets
-    return p.d != 128 || p.N * p.H * p.d * 2 < (int64_t{1} << 31);
+    // the kernels address one (b, h) sequence with 32-bit byte offsets
+    return p.N * p.H * p.d * 2 < (int64_t{1} << 31);
 }
 
 static size_t tables_bytes(const Problem& p) { return static_cast<size_t>(p.H) * kTabBytes; }
 
 size_t chunked_workspace_bytes(const Problem& p) {
-    if (p.d == 128) return chunked_d128_workspace_bytes(p);
+    return chunked_ws_workspace_bytes(p);
     int S;
     int64_t Lseg;
     plan_segments(p, S, Lseg);
@@ -970,8 +970,7 @@ size_t chunked_workspace_bytes(const Problem& p) {
 hipError_t launch_forward_chunked(const Problem& p, const idattn_params& prm, const void* q, const void* k,
                                   const void* v, void* o, const float* state_in, const void* tail_in,
                                   float* state_out, void* workspace, hipStream_t stream) {
-    if (p.d == 128)
-        return launch_forward_chunked_d128(p, prm, q, k, v, o, state_in, tail_in, state_out, workspace, stream);
+    return launch_forward_chunked_ws(p, prm, q, k, v, o, state_in, tail_in, state_out, workspace, stream);
     int S;
     int64_t Lseg;
     plan_segments(p, S, Lseg);

@@ -39,12 +39,12 @@ hipError_t launch_forward_chunked(const Problem& p, const idattn_params& prm,
                                   const float* state_in, const void* tail_in,
                                   float* state_out, void* workspace, hipStream_t stream);
 
-// eight-wave kernels for d = R = 128, M = 64 (called by the two above)
-size_t chunked_d128_workspace_bytes(const Problem& p);
-hipError_t launch_forward_chunked_d128(const Problem& p, const idattn_params& prm,
-                                       const void* q, const void* k, const void* v, void* o,
-                                       const float* state_in, const void* tail_in,
-                                       float* state_out, void* workspace, hipStream_t stream);
+// wave-specialised kernels for d = R in {64, 128}, M = 64 (called by the two above)
+size_t chunked_ws_workspace_bytes(const Problem& p);
+hipError_t launch_forward_chunked_ws(const Problem& p, const idattn_params& prm,
+                                     const void* q, const void* k, const void* v, void* o,
+                                     const float* state_in, const void* tail_in,
+                                     float* state_out, void* workspace, hipStream_t stream);
 
 // ---- state and tail plumbing
 // tail_out = last W-1 raw tokens of [tail_in (or zeros) ; x]; safe in place.
