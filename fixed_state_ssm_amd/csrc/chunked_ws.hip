@@ -25,21 +25,20 @@
 //    add up coherently; it is carried as a pair of fp16 values (about 22
 //    bits) and every product with T is two MFMAs.
 //
-// A workgroup is eight waves, two per SIMD.  Waves 0-3 (one per SIMD) own the
-// state and run every MFMA phase of chunk c; waves 4-7 build the features of
-// chunk c+1 meanwhile (short conv, SiLU, norms), keep them in registers and
-// write them to shared memory once the MFMA waves no longer read the previous
-// chunk's tiles.  Each SIMD thus runs one MFMA-bound and one VALU-bound wave.
-// All eight waves meet at the same four barriers per chunk:
-//   G   (MFMA: G tiles -> G')                       | features: -
-//   S   (MFMA: y_q.U, G'T, s~, X; U update; Z_v frag)| features: keys of c+1
-//   P   (MFMA: P~ tiles)                             | features: write z_k; values of c+1
-//   O   (MFMA: output; Gamma update)                 | features: queries of c+1
+// A workgroup is sixteen waves, four per SIMD, two roles of eight waves:
+// key waves own the key state U and run the products that make s~ and X
+// (G, y_q . U, G'T, P~) and the U update; value waves own the value state
+// Gamma and run the readout (X Gamma, P~ Z_v) and the Gamma update.  The
+// features of chunk c+1 (short conv, SiLU, norms) are built while chunk c
+// runs: queries and keys by the value waves in the two phases where they have
+// no MFMA work, values by the key waves in the phase where they have none.
+// Every SIMD thus holds two MFMA-issuing and two VALU-heavy waves per phase.
 //
 // Index m' = 2 m + part (part 0 = real, 1 = imaginary) runs over the 2M = 128
-// real rows of a complex mode set.  MFMA wave w (0..3) keeps
-//   U     : rows r (all D), columns m' in [32w, 32w+32)       -> 2 x D/16 tiles
-//   Gamma : rows m' (all 128), columns c in [w D/4, (w+1) D/4) -> 8 x D/64 tiles
+// real rows of a complex mode set.  Key wave kw (0..7) keeps U's rows r (all
+// D) of columns m' in [16kw, 16kw+16) (D/16 MFMA tiles); value wave vw keeps
+// Gamma's rows m' (all 128) of columns c in [16vw, 16vw+16) (8 tiles; value
+// waves vw >= D/16 own none).
 // An accumulator tile [X][Y] doubles as an operand with K = X once two of
 // them are concatenated (lane (g, i) then supplies K rows 4g..4g+3 and
 // 16+4g..16+4g+3 of a 32-row block), so U feeds y_q . U and Gamma feeds the
@@ -55,10 +54,11 @@ namespace {
 constexpr int L = 64;        // chunk length
 constexpr int MM = 64;       // complex modes
 constexpr int M2 = 2 * MM;   // m' rows
-constexpr int NTH = 512;     // eight waves
+constexpr int NTH = 1024;    // sixteen waves
 constexpr int kMaxW = 4;     // conv widths 1..4
 constexpr int RS = M2 + 8;   // padded row length (halfs) of [t][m'] tiles
-constexpr int RP = L + 8;    // padded row length of [t][64] tiles
+constexpr int RP = L + 16;   // padded row length of [t][64] tiles
+constexpr int PWS = MM + 4;  // padded row length (float2) of the abar^{k+1} rows
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLn2Sq = 0.4804530139182014f;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -67,8 +67,8 @@ template <int D>
 struct Cfg {
     static constexpr int RT = D / 16;   // 16-row tiles over R
     static constexpr int KB = D / 32;   // 32-wide K steps over R
-    static constexpr int CW = D / 64;   // 16-column Gamma tiles per MFMA wave
-    static constexpr int CPT = D / 32;  // feature channels per thread
+    static constexpr int CP = D / 2;    // channel pairs = lanes that share a feature token block
+    static constexpr int NF = 8 * CP;   // feature threads per role (8 token blocks)
     static constexpr int RY = D + 8;    // padded row length of the y' tile
 };
 
@@ -115,6 +115,10 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
     asm volatile("" : "+v"(x));
     return x;
 }
+// The thread index passed through an empty asm: what is derived from it is
+// recomputed at each use instead of being hoisted out of the chunk loop and
+// held in registers beside the state.
+__device__ __forceinline__ int tid_now() { return static_cast<int>(opaque(threadIdx.x)); }
 __device__ __forceinline__ half8 rd8(uint32_t a) { return *(lds_h8*)(uintptr_t)a; }
 __device__ __forceinline__ half4 rd4(uint32_t a) { return *(lds_h4*)(uintptr_t)a; }
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
@@ -132,28 +136,62 @@ __device__ __forceinline__ void wr2(uint32_t a, float x0, float x1) {
 }
 __device__ __forceinline__ void wr1(uint32_t a, float x) { *(lds_h1*)(uintptr_t)a = static_cast<_Float16>(x); }
 
+// DPP lane move (every pattern used here has a valid source for every lane);
+// written as an update of 0 with bound_ctrl so that the compiler folds it
+// into the consuming VALU instruction.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
 }
-// Sums over the 32 lanes of a half-wave for N values at once; every lane gets the totals.
-template <int N>
-__device__ __forceinline__ void sum32(float (&x)[N]) {
+// Reduce-scatter of 8 per-token partial sums over an aligned group of NL
+// lanes (32 or 64): on return lane l holds the group total of token
+// tau(l) = 4 b0 + 2 b1 + b2 (b_k bit k of l), so that the 8 lanes l % NL < 8
+// hold all 8 tokens.  Each of the first three steps pairs lanes that differ in
+// one of bits 0..2, keeps the half of the tokens that the lane's bit selects
+// and adds what the partner sends of that half; the last steps add the one
+// remaining value across bit 3 (rotate by 8 within a row), across rows
+// (v_permlane16_swap) and across halves (v_permlane32_swap).  For bit 2 the
+// partner is the lane 4 apart in rotation within its row of 16, which has the
+// other bit 2 and the same bits 0..1; together with the rotation by 8 every
+// lane of the group of 4 sharing bits 0..1 contributes once.
+template <int NL>
+__device__ __forceinline__ float reduce_scatter8(const float (&v)[8]) {
+    const int l = tid_now();
+    const bool b0 = l & 1, b1 = l & 2, b2 = l & 4;
+    float u[4], w[2];
 #pragma unroll
-    for (int s = 0; s < N; ++s) x[s] += dpp_mov<0xB1>(x[s]);   // quad_perm [1,0,3,2]
+    for (int k = 0; k < 4; ++k) {
+        const float send = b0 ? v[k] : v[k + 4], keep = b0 ? v[k + 4] : v[k];
+        u[k] = keep + dpp_mov<0xB1>(send);  // quad_perm [1,0,3,2]
+    }
 #pragma unroll
-    for (int s = 0; s < N; ++s) x[s] += dpp_mov<0x4E>(x[s]);   // quad_perm [2,3,0,1]
-#pragma unroll
-    for (int s = 0; s < N; ++s) x[s] += dpp_mov<0x141>(x[s]);  // row_half_mirror
-#pragma unroll
-    for (int s = 0; s < N; ++s) x[s] += dpp_mov<0x140>(x[s]);  // row_mirror
-#pragma unroll
-    for (int s = 0; s < N; ++s) x[s] += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x[s]), 0x401F));
+    for (int k = 0; k < 2; ++k) {
+        const float send = b1 ? u[k] : u[k + 2], keep = b1 ? u[k + 2] : u[k];
+        w[k] = keep + dpp_mov<0x4E>(send);  // quad_perm [2,3,0,1]
+    }
+    float x = (b2 ? w[1] : w[0]) + dpp_mov<0x124>(b2 ? w[0] : w[1]);  // row_ror:4
+    x += dpp_mov<0x128>(x);                                           // row_ror:8
+    {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    if constexpr (NL == 64) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    return x;
 }
+__device__ __forceinline__ int scatter_token(int l) { return 4 * (l & 1) + 2 * ((l >> 1) & 1) + ((l >> 2) & 1); }
 
 // Keeps the compiler from hoisting the next step's operand loads above this
 // point: one K-step of fragments is live at a time.
 __device__ __forceinline__ void step_fence() { __builtin_amdgcn_sched_barrier(0); }
+// s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima).  Loads and
+// stores share this counter and may complete out of order with respect to
+// each other, so once a store is in flight every wait for a load waits for
+// the store as well; a wave that stores collects its prefetched loads with
+// this wait before it issues the stores.
+__device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ uint16_t to_bf16(float x) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); }
 
@@ -239,12 +277,13 @@ struct SmemFwd {
     // window C
     _Float16 gp[L * RP];          // G' (zero above the causal band, never rewritten there)
     _Float16 pp[L * RP];          // P~ [t][l] (likewise)
-    float sig[L];                 // sigma~_t
+    float sig[2][L];              // sigma~_t, by chunk parity
     float2 aL[MM];                // abar^L
-    float2 pw[17][MM];            // abar^{k+1}, k = 0..16
+    float2 pw[16][PWS];           // abar^{k+1}, k = 0..15
     float gain[2 * D], bias[2 * D];
-    float wq[D * kMaxW], wk[D * kMaxW];  // conv weights times -log2(e), right-aligned taps
+    float wq[D * kMaxW], wk[D * kMaxW];  // conv weights times -log2(e), right-aligned taps (layout: wt_index)
     uint16_t halo[2][3][D];              // raw q, k at positions -3..-1 of the sequence
+    float fac[16][2][8];                 // per-token feature factors, by wave and token block
 };
 
 template <int D>
@@ -257,6 +296,7 @@ struct SmemSeg {
     float gain[2 * D], bias[2 * D];
     float wk[D * kMaxW];
     uint16_t halo[2][3][D];
+    float fac[16][2][8];
 };
 
 // byte distances inside window B (identical in both layouts)
@@ -265,217 +305,193 @@ struct WinOff {
     static constexpr uint32_t zv = D * L * 2, ft = 2 * D * L * 2, ftl = 2 * D * L * 2 + M2 * L * 2;
 };
 
-// ------------------------------------------------------------------ feature waves
-// Thread f = tid - 256 (cgi = f % 32, tb = f / 32) owns channels CPT cgi .. +CPT-1
-// of tokens 8tb..8tb+7 of a chunk; the short conv needs the three tokens
-// before, which the thread loads itself (positions < 0 read zeros, replaced
-// by the stored tail for the first chunk of a sequence).
+// ------------------------------------------------------------------ features
+// Within a role (512 threads), feature thread fi < NF owns channels 2 cgi and
+// 2 cgi + 1 (cgi = fi % CP) of tokens 8 tb .. 8 tb + 7 (tb = fi / CP) of a
+// chunk, so that the CP lanes of a token block hold all D channels of its
+// tokens and the channel norms are lane sums.  The short conv needs the three
+// tokens before, which the thread loads itself (positions < 0 read zeros,
+// replaced by the stored tail for the first chunk of a sequence).  With
+// D = 64 the feature threads are the upper half of the role.
 template <int D>
-struct FmT;
-template <>
-struct FmT<128> {
-    typedef u2 T;
-};
-template <>
-struct FmT<64> {
-    typedef uint32_t T;
-};
+__device__ __forceinline__ int feat_index() {
+    return (tid_now() & 511) ^ (Cfg<D>::NF < 512 ? 256 : 0);
+}
 
 // Buffer resources over one (b, h) sequence up to the end of the segment:
 // token t, channel c sits at byte 2 (t H D + c) from the sequence's first
 // token.  Offsets are whole VGPR operands, which the hardware range-checks;
 // loads past the end of a resource return zeros.
-struct SeqBuf {
-    __amdgpu_buffer_rsrc_t q, k, v;
-};
 template <int D>
-__device__ __forceinline__ SeqBuf seq_buf(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t b,
-                                          int64_t h, int64_t N, int64_t H, int64_t t_end) {
-    const int64_t first = b * N * H * D + h * D;
-    const int nrec = static_cast<int>(t_end * H * D * 2);
-    SeqBuf r;
-    r.q = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>((q ? q : k) + first), 0, nrec, 0x00020000);
-    r.k = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(k + first), 0, nrec, 0x00020000);
-    r.v = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(v + first), 0, nrec, 0x00020000);
-    return r;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const uint16_t* x, int64_t b, int64_t h, int64_t N,
+                                                           int64_t H, int64_t t_end) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x + b * N * H * D + h * D), 0,
+                                             static_cast<int>(t_end * H * D * 2), 0x00020000);
 }
-template <int D>
-__device__ __forceinline__ typename FmT<D>::T bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    if constexpr (D == 128) return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-    else return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-template <int D>
-__device__ __forceinline__ void unpack(const typename FmT<D>::T& u, float* x) {
-    if constexpr (D == 128) {
-        x[0] = __uint_as_float(u[0] << 16);
-        x[1] = __uint_as_float(u[0] & 0xffff0000u);
-        x[2] = __uint_as_float(u[1] << 16);
-        x[3] = __uint_as_float(u[1] & 0xffff0000u);
-    } else {
-        x[0] = __uint_as_float(u << 16);
-        x[1] = __uint_as_float(u & 0xffff0000u);
-    }
-}
-
-// Raw inputs of one chunk for one thread: 8 tokens and the 3 before (q, k).
-template <int D, bool WITH_Q>
-struct FmRaw {
-    typedef typename FmT<D>::T T;
-    T q[WITH_Q ? 11 : 1];
-    T k[11];
-    T v[8];
-};
-
-// tok0 = first token of the chunk; lane_b = 2 (8 tb H D + CPT cgi) bytes, rsb = 2 H D.
-template <int D, bool WITH_Q>
-__device__ __forceinline__ void load_qk(FmRaw<D, WITH_Q>& r, const SeqBuf& sb, int64_t tok0, int rsb, int lane_b,
-                                        bool want_q) {
+// The thread's channel pair of 8 tokens at tok0 + 8tb .. (+7) and, with HALO,
+// of the 3 before (slots 0..2); rsb = 2 H D is the byte stride of a token.
+template <int D, bool HALO>
+__device__ __forceinline__ void fm_load(uint32_t (&r)[HALO ? 11 : 8], __amdgpu_buffer_rsrc_t rs, int rsb,
+                                        int64_t tok0) {
+    const int fi = feat_index<D>();
+    if (fi >= Cfg<D>::NF) return;
+    const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
+    const uint32_t lane_b = static_cast<uint32_t>(8 * tb * rsb + 4 * cgi);
 #pragma unroll
-    for (int s = 0; s < 11; ++s) {
-        const uint32_t off = static_cast<uint32_t>(lane_b + (tok0 - 3 + s) * rsb);
-        if constexpr (WITH_Q)
-            if (want_q) r.q[s] = bload<D>(sb.q, off);
-        if (!want_q) r.k[s] = bload<D>(sb.k, off);
-    }
+    for (int s = 0; s < (HALO ? 11 : 8); ++s)
+        r[s] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane_b + static_cast<uint32_t>((tok0 + s - (HALO ? 3 : 0)) * rsb),
+                                                    0, 0);
 }
-template <int D, bool WITH_Q>
-__device__ __forceinline__ void load_v(FmRaw<D, WITH_Q>& r, const SeqBuf& sb, int64_t tok0, int rsb, int lane_b) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) r.v[s] = bload<D>(sb.v, static_cast<uint32_t>(lane_b + (tok0 + s) * rsb));
-}
-
 // The stored tail replaces the three positions before the sequence start.
-template <int D, class SM, class T>
-__device__ __forceinline__ void halo_fix(T (&x)[11], const SM& sm, int sel, int64_t tok0) {
-    const int cgi = (threadIdx.x - 256) & 31;
-    if (tok0 == 0) {
-#pragma unroll
-        for (int j = 0; j < 3; ++j) x[j] = *reinterpret_cast<const T*>(&sm.halo[sel][j][Cfg<D>::CPT * cgi]);
-    }
-}
-
-// y' = c' / (1 + 2^c') for 8 tokens x CPT channels; ss = partial ||y'||^2.
-template <int D>
-__device__ __forceinline__ void conv_silu(const typename FmT<D>::T (&raw)[11], const float* wl, float (&y)[8][Cfg<D>::CPT],
-                                          float (&ss)[8]) {
-    constexpr int CPT = Cfg<D>::CPT;
-    float x[11][CPT];
-#pragma unroll
-    for (int s = 0; s < 11; ++s) unpack<D>(raw[s], x[s]);
-    float w[CPT][kMaxW];
-#pragma unroll
-    for (int c = 0; c < CPT; ++c)
-#pragma unroll
-        for (int j = 0; j < kMaxW; ++j) w[c][j] = wl[c * kMaxW + j];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        ss[s] = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            float acc = w[c][0] * x[s][c];
-#pragma unroll
-            for (int j = 1; j < kMaxW; ++j) acc = fmaf(w[c][j], x[s + j][c], acc);
-            y[s][c] = acc * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(acc));
-            ss[s] = fmaf(y[s][c], y[s][c], ss[s]);
-        }
-    }
-}
-
-// z_k of the thread's 8 tokens, packed per channel (z masked to 0 at t >= n).
-template <int D, bool WITH_Q, class SM>
-__device__ __forceinline__ void fm_keys(half8 (&zk)[Cfg<D>::CPT], FmRaw<D, WITH_Q>& r, const SM& sm, int64_t tok0,
-                                        int n, float eps_feat, float eps_norm) {
-    constexpr int CPT = Cfg<D>::CPT;
-    const int f = threadIdx.x - 256, cgi = f & 31, tb = f >> 5, c0 = CPT * cgi;
-    if (tb == 0) halo_fix<D>(r.k, sm, 1, tok0);
-    float y[8][CPT], ss[8];
-    conv_silu<D>(r.k, &sm.wk[c0 * kMaxW], y, ss);
-    sum32<8>(ss);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        // xi = -ln2 inv y',  mean xi^2 = ln^2 2 inv^2 ||y'||^2 / D
-        const float inv = __builtin_amdgcn_rcpf(fmaf(kLn2Sq, ss[s], eps_feat));
-        const float rs = __builtin_amdgcn_rsqf(fmaf(kLn2Sq * (1.f / D) * inv * inv, ss[s], eps_norm));
-        ss[s] = (8 * tb + s < n) ? -kLn2 * inv * rs : 0.f;  // rho, 0 past the valid tokens
-    }
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-        const float g = sm.gain[c0 + c], bb = sm.bias[c0 + c];
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-            zk[c][s] = static_cast<_Float16>(8 * tb + s < n ? fmaf(g * ss[s], y[s][c], bb) : 0.f);
-    }
-}
-
-// z_v of the thread's 8 tokens, written to z_v^T at column 8tb.
-template <int D>
-struct FmAddr;
-template <int D, bool WITH_Q, class SM>
-__device__ __forceinline__ void fm_values(const FmRaw<D, WITH_Q>& r, const SM& sm, const FmAddr<D>& fa, int n,
-                                          float eps_norm) {
-    constexpr int CPT = Cfg<D>::CPT;
-    const int f = threadIdx.x - 256, cgi = f & 31, tb = f >> 5, c0 = CPT * cgi;
-    float xv[8][CPT], ss[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        unpack<D>(r.v[s], xv[s]);
-        ss[s] = xv[s][0] * xv[s][0];
-#pragma unroll
-        for (int c = 1; c < CPT; ++c) ss[s] = fmaf(xv[s][c], xv[s][c], ss[s]);
-    }
-    sum32<8>(ss);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) ss[s] = __builtin_amdgcn_rsqf(fmaf(1.f / D, ss[s], eps_norm));
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-        const float g = sm.gain[D + c0 + c], bb = sm.bias[D + c0 + c];
-        half8 z;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) z[s] = static_cast<_Float16>(8 * tb + s < n ? fmaf(g * ss[s], xv[s][c], bb) : 0.f);
-        wr8(fa.z[c] + WinOff<D>::zv, z);
-    }
-}
-
-// y' of the thread's 8 tokens into rows 8tb.. of yq, and sigma~.
 template <int D, class SM>
-__device__ __forceinline__ void fm_queries(FmRaw<D, true>& r, SM& sm, uint32_t yst, int64_t tok0, float eps_feat,
-                                           float inv_dt) {
-    constexpr int CPT = Cfg<D>::CPT;
-    const int f = threadIdx.x - 256, cgi = f & 31, tb = f >> 5, c0 = CPT * cgi;
-    if (tb == 0) halo_fix<D>(r.q, sm, 0, tok0);
-    float y[8][CPT], ss[8];
-    conv_silu<D>(r.q, &sm.wq[c0 * kMaxW], y, ss);
+__device__ __forceinline__ void halo_fix(uint32_t (&r)[11], const SM& sm, int sel, int64_t tok0) {
+    const int fi = feat_index<D>();
+    if (tok0 == 0 && fi < Cfg<D>::CP) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) r[j] = *reinterpret_cast<const uint32_t*>(&sm.halo[sel][j][2 * fi]);
+    }
+}
+// Conv weight of channel c, tap j (0..3, right-aligned) in shared memory:
+// the thread of channel pair cgi reads taps {0,1} and {2,3} of both channels
+// as two 16-byte words at consecutive addresses across the lanes.
+template <int D>
+__host__ __device__ constexpr int wt_index(int c, int j) {
+    return (((j >> 1) * Cfg<D>::CP + (c >> 1)) * 2 + (c & 1)) * 2 + (j & 1);
+}
+
+// y'[e][s] = c' / (1 + 2^c') for channel 2 cgi + e and token 8 tb + s;
+// ss[s] = partial ||y'||^2 over the thread's two channels.
+template <int D>
+__device__ __forceinline__ void conv_silu(const uint32_t (&r)[11], const float* w, int cgi, float (&y)[2][8],
+                                          float (&ss)[8]) {
+    const float4 wa = *reinterpret_cast<const float4*>(w + 4 * cgi);                 // taps 0, 1
+    const float4 wb = *reinterpret_cast<const float4*>(w + 4 * (Cfg<D>::CP + cgi));  // taps 2, 3
+    const float w0[4] = {wa.x, wa.y, wb.x, wb.y}, w1[4] = {wa.z, wa.w, wb.z, wb.w};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        if constexpr (CPT == 4) wr4(yst + 2 * s * Cfg<D>::RY, y[s][0], y[s][1], y[s][2], y[s][3]);
-        else wr2(yst + 2 * s * Cfg<D>::RY, y[s][0], y[s][1]);
-    }
-    sum32<8>(ss);
-    if (cgi == 0) {
+        float a0 = w0[0] * lo_bf16(r[s]), a1 = w1[0] * hi_bf16(r[s]);
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-            sm.sig[8 * tb + s] = -kLn2 * inv_dt * __builtin_amdgcn_rcpf(fmaf(kLn2Sq, ss[s], eps_feat));
+        for (int j = 1; j < 4; ++j) {
+            a0 = fmaf(w0[j], lo_bf16(r[s + j]), a0);
+            a1 = fmaf(w1[j], hi_bf16(r[s + j]), a1);
+        }
+        y[0][s] = a0 * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(a0));
+        y[1][s] = a1 * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(a1));
+        ss[s] = fmaf(y[1][s], y[1][s], y[0][s] * y[0][s]);
+    }
+}
+// Zeroes the features of tokens 8 tb + s >= n (the end of a ragged last chunk).
+__device__ __forceinline__ void mask_tokens(float (&z)[2][8], int tb, int n) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const bool ok = 8 * tb + s < n;
+        z[0][s] = ok ? z[0][s] : 0.f;
+        z[1][s] = ok ? z[1][s] : 0.f;
+    }
+}
+// z^T rows 2 cgi + e, columns 8 tb .. 8 tb + 7: one 16-byte store per channel.
+__device__ __forceinline__ void write_zt(const void* zT, int cgi, int tb, const float (&z)[2][8]) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        half8 hv;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) hv[s] = static_cast<_Float16>(z[e][s]);
+        wr8(lds_addr(zT) + 2 * o128(2 * cgi + e, 8 * tb), hv);
     }
 }
 
-// Per-thread store addresses of the feature waves: z_k^T row CPT cgi + c at
-// column 8tb (each row has its own swizzle; z_v^T at + WinOff::zv), and y'
-// row 8tb at column CPT cgi.
-template <int D>
-struct FmAddr {
-    uint32_t z[Cfg<D>::CPT];
-    uint32_t y;
-};
-template <int D>
-__device__ __forceinline__ FmAddr<D> fm_addr(const void* zkT, const void* yq) {
-    constexpr int CPT = Cfg<D>::CPT;
-    const int f = threadIdx.x - 256, cgi = f & 31, tb = f >> 5;
-    FmAddr<D> a;
+// Per-token factors through shared memory: the lanes l % NL < 8 of each token
+// block hold token tau(l); every lane of the block then reads all 8 (the
+// accesses of one wave execute in order, so no barrier is needed).
+template <int D, class SM>
+__device__ __forceinline__ void share_factor(SM& sm, float f, float (&out)[8]) {
+    constexpr int NL = Cfg<D>::CP;
+    const int l = tid_now(), w = (l >> 6) & 15, blk = NL == 32 ? (l >> 5) & 1 : 0;
+    float* slot = const_cast<float*>(&sm.fac[w][blk][0]);
+    if ((l & (NL - 1)) < 8) slot[scatter_token(l)] = f;
+    const float4 a = *reinterpret_cast<const float4*>(slot), b = *reinterpret_cast<const float4*>(slot + 4);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+// z_k of the thread's 8 tokens to z_k^T (zero past n valid tokens).
+template <int D, class SM>
+__device__ __forceinline__ void fm_keys(const uint32_t (&r)[11], const SM& sm, int n, float eps_feat, float eps_norm) {
+    const int fi = feat_index<D>();
+    if (fi >= Cfg<D>::NF) return;
+    const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
+    float y[2][8], ss[8], rho[8];
+    conv_silu<D>(r, sm.wk, cgi, y, ss);
+    {
+        // xi = -ln2 inv y',  mean xi^2 = ln^2 2 inv^2 ||y'||^2 / D
+        const float tot = reduce_scatter8<Cfg<D>::CP>(ss);
+        const float inv = __builtin_amdgcn_rcpf(fmaf(kLn2Sq, tot, eps_feat));
+        const float rs = __builtin_amdgcn_rsqf(fmaf(kLn2Sq * (1.f / D) * inv * inv, tot, eps_norm));
+        share_factor<D>(const_cast<SM&>(sm), -kLn2 * inv * rs, rho);
+    }
+    const float g0 = sm.gain[2 * cgi], g1 = sm.gain[2 * cgi + 1], b0 = sm.bias[2 * cgi], b1 = sm.bias[2 * cgi + 1];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) a.z[c] = opaque(lds_addr(zkT) + 2 * o128(CPT * cgi + c, 8 * tb));
-    a.y = yq ? opaque(lds_addr(yq) + 2 * (8 * tb * Cfg<D>::RY + CPT * cgi)) : 0u;
-    return a;
+    for (int s = 0; s < 8; ++s) {
+        y[0][s] = fmaf(g0 * rho[s], y[0][s], b0);
+        y[1][s] = fmaf(g1 * rho[s], y[1][s], b1);
+    }
+    if (n < L) mask_tokens(y, tb, n);
+    write_zt(sm.zkT, cgi, tb, y);
+}
+
+// z_v of the thread's 8 tokens to z_v^T (zero past n valid tokens).
+template <int D, class SM>
+__device__ __forceinline__ void fm_values(const uint32_t (&r)[8], const SM& sm, int n, float eps_norm) {
+    const int fi = feat_index<D>();
+    if (fi >= Cfg<D>::NF) return;
+    const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
+    float x[2][8], ss[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        x[0][s] = lo_bf16(r[s]);
+        x[1][s] = hi_bf16(r[s]);
+        ss[s] = fmaf(x[1][s], x[1][s], x[0][s] * x[0][s]);
+    }
+    float rs[8];
+    share_factor<D>(const_cast<SM&>(sm), __builtin_amdgcn_rsqf(fmaf(1.f / D, reduce_scatter8<Cfg<D>::CP>(ss), eps_norm)),
+                    rs);
+    const float g0 = sm.gain[D + 2 * cgi], g1 = sm.gain[D + 2 * cgi + 1];
+    const float b0 = sm.bias[D + 2 * cgi], b1 = sm.bias[D + 2 * cgi + 1];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        x[0][s] = fmaf(g0 * rs[s], x[0][s], b0);
+        x[1][s] = fmaf(g1 * rs[s], x[1][s], b1);
+    }
+    if (n < L) mask_tokens(x, tb, n);
+    write_zt(sm.zvT, cgi, tb, x);
+}
+
+// y' of the thread's 8 tokens (kept in registers as fp16 pairs until written
+// by fm_write_q) and sigma~ to sig.
+template <int D, class SM>
+__device__ __forceinline__ void fm_queries(half2v (&yo)[8], const uint32_t (&r)[11], SM& sm, float* sig,
+                                           float eps_feat, float inv_dt) {
+    const int fi = feat_index<D>();
+    if (fi >= Cfg<D>::NF) return;
+    const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
+    float y[2][8], ss[8];
+    conv_silu<D>(r, sm.wq, cgi, y, ss);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) yo[s] = half2v{static_cast<_Float16>(y[0][s]), static_cast<_Float16>(y[1][s])};
+    const float tot = reduce_scatter8<Cfg<D>::CP>(ss);
+    if (cgi < 8) sig[8 * tb + scatter_token(cgi)] = -kLn2 * inv_dt * __builtin_amdgcn_rcpf(fmaf(kLn2Sq, tot, eps_feat));
+}
+template <int D>
+__device__ __forceinline__ void fm_write_q(const half2v (&yo)[8], const void* yq) {
+    const int fi = feat_index<D>();
+    if (fi >= Cfg<D>::NF) return;
+    const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
+    const uint32_t yst = opaque(lds_addr(yq) + 2 * (8 * tb * Cfg<D>::RY + 2 * cgi));
+#pragma unroll
+    for (int s = 0; s < 8; ++s) *(lds_h2*)(uintptr_t)(yst + 2 * s * Cfg<D>::RY) = yo[s];
 }
 
 // Conv weights (times -log2 e, taps right-aligned into 4 slots), gain, bias,
@@ -490,8 +506,8 @@ __device__ __forceinline__ void load_prologue(SM& sm, const idattn_params& prm, 
     for (int e = threadIdx.x; e < D * kMaxW; e += NTH) {
         const int c = e / kMaxW, j = e % kMaxW;
         const int tap = j - (kMaxW - W);
-        if constexpr (WITH_Q) sm.wq[e] = tap >= 0 ? -kLog2e * prm.conv_q[(h * D + c) * W + tap] : 0.f;
-        sm.wk[e] = tap >= 0 ? -kLog2e * prm.conv_k[(h * D + c) * W + tap] : 0.f;
+        if constexpr (WITH_Q) sm.wq[wt_index<D>(c, j)] = tap >= 0 ? -kLog2e * prm.conv_q[(h * D + c) * W + tap] : 0.f;
+        sm.wk[wt_index<D>(c, j)] = tap >= 0 ? -kLog2e * prm.conv_k[(h * D + c) * W + tap] : 0.f;
     }
     for (int e = threadIdx.x; e < 2 * 3 * D; e += NTH) {
         const int sel = e / (3 * D), row = (e / D) % 3, c = e % D;
@@ -510,185 +526,135 @@ __device__ __forceinline__ void copy16(void* dst, const void* src, int bytes) {
         reinterpret_cast<u4*>(dst)[e] = reinterpret_cast<const u4*>(src)[e];
 }
 
-// ------------------------------------------------------------------ MFMA-wave state
-// Lane (g, i) of MFMA wave w:
-//   U[mu][rt][jj]  = U_m[r],     r = 16rt + 4g + jj,  m' = 32w + 16mu + i
-//   Gm[mt][ct][jj] = Gamma_m[c], m' = 16mt + 4g + jj, c = 16(CW w + ct) + i
+// ------------------------------------------------------------------ state
+// Key wave kw (0..7), lane (g, i):  U[rt][jj] = U_m[r],  r = 16rt + 4g + jj, m' = 16kw + i
+// Value wave vw (0..D/16-1):        G[mt][jj] = Gamma_m[c], m' = 16mt + 4g + jj, c = 16vw + i
 // Memory layout: float [M][2D][2] (complex), columns 0..D-1 hold U, D..2D-1 Gamma.
 template <int D>
-struct State {
-    f4 U[2][Cfg<D>::RT];
-    f4 Gm[8][Cfg<D>::CW];
-};
-
-template <int D>
-__device__ __forceinline__ void state_load(State<D>& st, const float* src) {
-    constexpr int RT = Cfg<D>::RT, CW = Cfg<D>::CW;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, i = lane & 15;
+__device__ __forceinline__ void u_load(f4 (&U)[Cfg<D>::RT], const float* src, int kw) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15, mp = 16 * kw + i;
 #pragma unroll
-    for (int mu = 0; mu < 2; ++mu)
+    for (int rt = 0; rt < Cfg<D>::RT; ++rt)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int r = 16 * rt + 4 * g + jj, mp = 32 * w + 16 * mu + i;
-                st.U[mu][rt][jj] = src ? src[((mp >> 1) * 2 * D + r) * 2 + (mp & 1)] : 0.f;
-            }
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int ct = 0; ct < CW; ++ct)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int mp = 16 * mt + 4 * g + jj, c = 16 * (CW * w + ct) + i;
-                st.Gm[mt][ct][jj] = src ? src[((mp >> 1) * 2 * D + D + c) * 2 + (mp & 1)] : 0.f;
-            }
+        for (int jj = 0; jj < 4; ++jj)
+            U[rt][jj] = src ? src[((mp >> 1) * 2 * D + 16 * rt + 4 * g + jj) * 2 + (mp & 1)] : 0.f;
 }
-
-// Stores the state, first multiplying every mode by corr[m] when corr is not NULL.
 template <int D>
-__device__ __forceinline__ void state_store(const State<D>& st, float* dst, const float2* corr) {
-    constexpr int RT = Cfg<D>::RT, CW = Cfg<D>::CW;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, i = lane & 15;
-#pragma unroll
-    for (int mu = 0; mu < 2; ++mu) {
-        const int mp = 32 * w + 16 * mu + i;
-        const float2 c = corr ? corr[mp >> 1] : make_float2(1.f, 0.f);
-        const float sc = (mp & 1) ? c.y : -c.y;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int r = 16 * rt + 4 * g + jj;
-                const float u = st.U[mu][rt][jj];
-                const float pu = dpp_mov<0xB1>(u);  // other part of the same mode (lane i ^ 1)
-                dst[((mp >> 1) * 2 * D + r) * 2 + (mp & 1)] = fmaf(sc, pu, c.x * u);
-            }
-    }
+__device__ __forceinline__ void g_load(f4 (&G)[8], const float* src, int vw) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15, c = 16 * vw + i;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-        for (int ct = 0; ct < CW; ++ct)
+        for (int jj = 0; jj < 4; ++jj) {
+            const int mp = 16 * mt + 4 * g + jj;
+            G[mt][jj] = src ? src[((mp >> 1) * 2 * D + D + c) * 2 + (mp & 1)] : 0.f;
+        }
+}
+// Stores, first multiplying every mode by corr[m] when corr is not NULL.
+template <int D>
+__device__ __forceinline__ void u_store(const f4 (&U)[Cfg<D>::RT], float* dst, const float2* corr, int kw) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15, mp = 16 * kw + i;
+    const float2 c = corr ? corr[mp >> 1] : make_float2(1.f, 0.f);
+    const float sc = (mp & 1) ? c.y : -c.y;
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int m = 8 * mt + 2 * g + q, c = 16 * (CW * w + ct) + i;
-                const float2 a = corr ? corr[m] : make_float2(1.f, 0.f);
-                const float gr = st.Gm[mt][ct][2 * q], gi = st.Gm[mt][ct][2 * q + 1];
-                *reinterpret_cast<float2*>(dst + (static_cast<int64_t>(m) * 2 * D + D + c) * 2) =
-                    make_float2(a.x * gr - a.y * gi, a.x * gi + a.y * gr);
-            }
+    for (int rt = 0; rt < Cfg<D>::RT; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const float u = U[rt][jj];
+            const float pu = dpp_mov<0xB1>(u);  // other part of the same mode (lane i ^ 1)
+            dst[((mp >> 1) * 2 * D + 16 * rt + 4 * g + jj) * 2 + (mp & 1)] = fmaf(sc, pu, c.x * u);
+        }
+}
+template <int D>
+__device__ __forceinline__ void g_store(const f4 (&G)[8], float* dst, const float2* corr, int vw) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15, c = 16 * vw + i;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int m = 8 * mt + 2 * g + q;
+            const float2 a = corr ? corr[m] : make_float2(1.f, 0.f);
+            const float gr = G[mt][2 * q], gi = G[mt][2 * q + 1];
+            *reinterpret_cast<float2*>(dst + (static_cast<int64_t>(m) * 2 * D + D + c) * 2) =
+                make_float2(a.x * gr - a.y * gi, a.x * gi + a.y * gr);
+        }
 }
 
 // Window-B lane base (byte address from z_k^T) for fragment reads of rows
-// R0 + i at column chunk 4kb + g, R0 = 16 x any tile index of any of the four
-// tiles; the wave-uniform offsets of the F^T rows of U's m' block and of the
-// z_v^T rows of the wave's Gamma columns are added at use.
-template <int D>
-struct WinB {
-    uint32_t all[2];
-    __device__ __forceinline__ uint32_t ownU(int mu, int kb) const {
-        return all[kb] + WinOff<D>::ft + 2 * 64 * (32 * (threadIdx.x >> 6) + 16 * mu);
-    }
-    __device__ __forceinline__ uint32_t ownC(int kb) const {
-        return all[kb] + WinOff<D>::zv + 2 * 64 * 16 * Cfg<D>::CW * (threadIdx.x >> 6);
-    }
-};
-template <int D>
-__device__ __forceinline__ WinB<D> win_b(const void* zkT) {
-    const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15;
-    WinB<D> b;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) b.all[kb] = opaque(lds_addr(zkT) + 2 * o128(i, 32 * kb + 8 * g));
-    return b;
+// R0 + i at column chunk 4kb + g (R0 = 16 x any tile index of any of the four tiles).
+__device__ __forceinline__ uint32_t win_b(const void* zkT, int kb) {
+    const int lane = tid_now() & 63, g = lane >> 4, i = lane & 15;
+    return opaque(lds_addr(zkT) + 2 * o128(i, 32 * kb + 8 * g));
 }
 
 // U <- abar^L U + Z_k^T F  (the real and imaginary rows of a mode sit in lanes i, i ^ 1)
 template <int D>
-__device__ __forceinline__ void key_update(State<D>& st, const WinB<D>& wb, const float (&aLr)[2],
-                                           const float (&aLs)[2]) {
+__device__ __forceinline__ void key_update(f4 (&U)[Cfg<D>::RT], const float2* aL, int kw, const void* zkT) {
     constexpr int RT = Cfg<D>::RT;
     constexpr uint32_t dl = WinOff<D>::ftl - WinOff<D>::ft;
+    const int i = tid_now() & 15;
+    const float2 a = aL[(16 * kw + i) >> 1];
+    const float aLs = (i & 1) ? a.y : -a.y;
 #pragma unroll
-    for (int mu = 0; mu < 2; ++mu)
+    for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const float u = st.U[mu][rt][jj];
-                st.U[mu][rt][jj] = fmaf(aLs[mu], dpp_mov<0xB1>(u), aLr[mu] * u);
-            }
-            if (rt % 2 == 1) step_fence();  // bounds the partner values held at once
+        for (int jj = 0; jj < 4; ++jj) {
+            const float u = U[rt][jj];
+            U[rt][jj] = fmaf(a.x, u, dpp_mov<0xB1>(u) * aLs);
         }
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-        half8 bF[2], bFl[2];
-#pragma unroll
-        for (int mu = 0; mu < 2; ++mu) {
-            bF[mu] = rd8(wb.ownU(mu, kb));  // F[j][m'], j = 32kb + 8g + jj
-            bFl[mu] = rd8(wb.ownU(mu, kb) + dl);
-        }
+        const uint32_t wb = win_b(zkT, kb);
+        const uint32_t fo = wb + WinOff<D>::ft + 2 * 64 * 16 * kw;  // F^T rows 16kw + i
+        const half8 bF = rd8(fo), bFl = rd8(fo + dl);                // F[j][m'], j = 32kb + 8g + jj
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const half8 a = rd8(wb.all[kb] + 2048 * rt);  // z_k[j][r = 16rt + i]
-#pragma unroll
-            for (int mu = 0; mu < 2; ++mu) {
-                st.U[mu][rt] = mfma(a, bF[mu], st.U[mu][rt]);
-                st.U[mu][rt] = mfma(a, bFl[mu], st.U[mu][rt]);
-            }
-            if (rt % 4 == 3) step_fence();
+            const half8 a8 = rd8(wb + 2048 * rt);  // z_k[j][r = 16rt + i]
+            U[rt] = mfma(a8, bF, U[rt]);
+            U[rt] = mfma(a8, bFl, U[rt]);
         }
     }
 }
 
-// Gamma <- abar^L Gamma + F^T Z_v, with bZ[ct][kb] = Z_v[32kb + 8g + jj][16(CW w + ct) + i]
+// Gamma <- abar^L Gamma + F^T Z_v, with bZ[kb] = Z_v[32kb + 8g + jj][16vw + i]
 template <int D>
-__device__ __forceinline__ void value_update(State<D>& st, const float2* aL, const WinB<D>& wb,
-                                             const half8 (&bZ)[Cfg<D>::CW][2]) {
-    constexpr int CW = Cfg<D>::CW;
-    const int g = (threadIdx.x & 63) >> 4;
+__device__ __forceinline__ void value_update(f4 (&G)[8], const float2* aL, const half8 (&bZ)[2], const void* zkT) {
+    const int g = (tid_now() & 63) >> 4;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
         const float4 a = *reinterpret_cast<const float4*>(&aL[8 * mt + 2 * g]);
-#pragma unroll
-        for (int ct = 0; ct < CW; ++ct) {
-            const float r0 = st.Gm[mt][ct][0], i0 = st.Gm[mt][ct][1], r1 = st.Gm[mt][ct][2], i1 = st.Gm[mt][ct][3];
-            st.Gm[mt][ct][0] = a.x * r0 - a.y * i0;
-            st.Gm[mt][ct][1] = a.x * i0 + a.y * r0;
-            st.Gm[mt][ct][2] = a.z * r1 - a.w * i1;
-            st.Gm[mt][ct][3] = a.z * i1 + a.w * r1;
-        }
-        if (mt % 2 == 1) step_fence();
+        const float r0 = G[mt][0], i0 = G[mt][1], r1 = G[mt][2], i1 = G[mt][3];
+        G[mt][0] = a.x * r0 - a.y * i0;
+        G[mt][1] = a.x * i0 + a.y * r0;
+        G[mt][2] = a.z * r1 - a.w * i1;
+        G[mt][3] = a.z * i1 + a.w * r1;
     }
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t wb = win_b(zkT, kb);
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-            const half8 a = rd8(wb.all[kb] + WinOff<D>::ft + 2048 * mt);
-            const half8 al = rd8(wb.all[kb] + WinOff<D>::ftl + 2048 * mt);
-#pragma unroll
-            for (int ct = 0; ct < CW; ++ct) {
-                st.Gm[mt][ct] = mfma(a, bZ[ct][kb], st.Gm[mt][ct]);
-                st.Gm[mt][ct] = mfma(al, bZ[ct][kb], st.Gm[mt][ct]);
-            }
-            if (mt % 4 == 3) step_fence();
+            G[mt] = mfma(rd8(wb + WinOff<D>::ft + 2048 * mt), bZ[kb], G[mt]);
+            G[mt] = mfma(rd8(wb + WinOff<D>::ftl + 2048 * mt), bZ[kb], G[mt]);
         }
+    }
 }
 
 template <int D>
-__device__ __forceinline__ void load_bz(half8 (&bZ)[Cfg<D>::CW][2], const WinB<D>& wb) {
+__device__ __forceinline__ void load_bz(half8 (&bZ)[2], int vw, const void* zkT) {
 #pragma unroll
-    for (int ct = 0; ct < Cfg<D>::CW; ++ct)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) bZ[ct][kb] = rd8(wb.ownC(kb) + 2048 * ct);
+    for (int kb = 0; kb < 2; ++kb) bZ[kb] = rd8(win_b(zkT, kb) + WinOff<D>::zv + 2048 * vw);
 }
 
-// Causal 16 x 16 tiles (tt, kt), kt <= tt, of the G and P~ products, split
-// over the four MFMA waves: wave w takes tiles w, w + 4, w + 8 of the list.
+// Causal 16 x 16 tiles (tt, kt), kt <= tt, of the G and P~ products: key wave
+// kw takes tile kw of the list, and kw + 8 when that exists.
 __device__ __forceinline__ int tile_tt(int q) { return q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3; }
 __device__ __forceinline__ int tile_kt(int q) { return q - (tile_tt(q) * (tile_tt(q) + 1)) / 2; }
 
 // ------------------------------------------------------------------ kernels
 // Segment end states from a zero start: grid B*H*(S-1), block (bh, seg).
+// Per chunk:  A (key: U update | value: Gamma update)  B (key: keys of c+1 | value: values of c+1).
 template <int D>
 __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_params prm,
                                                             const uint16_t* __restrict__ k,
@@ -696,10 +662,9 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
                                                             const uint16_t* __restrict__ tail_in,
                                                             const uint8_t* __restrict__ tab, float* __restrict__ ws,
                                                             int64_t Lseg, int S) {
-    constexpr int CPT = Cfg<D>::CPT, CW = Cfg<D>::CW;
     __shared__ SmemSeg<D> sm;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15;
-    const bool mw = w < 4;  // MFMA wave
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool key = w < 8;
     const int64_t bh = blockIdx.x / (S - 1);
     const int seg = static_cast<int>(blockIdx.x % (S - 1));
     const int64_t b = bh / p.H, h = bh % p.H;
@@ -711,62 +676,61 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
     copy16(sm.ftl, th + kTabFTL, M2 * L * 2);
     if (tid < MM) sm.aL[tid] = reinterpret_cast<const float2*>(th + kTabPw)[(L - 1) * MM + tid];
     __syncthreads();
-    if (mw) {
-        State<D> st;
-        state_load<D>(st, nullptr);
-        lds_barrier();  // features of chunk 0 are in shared memory
-        for (int c = 0; c < nch; ++c) {
-            const WinB<D> wb = win_b<D>(sm.zkT);
-            float aLr[2], aLs[2];
-#pragma unroll
-            for (int mu = 0; mu < 2; ++mu) {
-                const float2 a = sm.aL[(32 * w + 16 * mu + i) >> 1];
-                aLr[mu] = a.x;
-                aLs[mu] = (i & 1) ? a.y : -a.y;
-            }
-            half8 bZ[CW][2];
-            key_update<D>(st, wb, aLr, aLs);
-            load_bz<D>(bZ, wb);
-            lds_barrier();
-            value_update<D>(st, sm.aL, wb, bZ);
-            lds_barrier();
-        }
-        state_store<D>(st, ws + (static_cast<int64_t>(seg) * p.B * p.H + bh) * MM * 2 * D * 2, nullptr);
-    } else {
-        FmRaw<D, false> rr;
-        const int rsb = static_cast<int>(p.H * D * 2);
-        const int f = tid - 256;
-        const int lane_b = 2 * (8 * (f >> 5) * static_cast<int>(p.H * D) + CPT * (f & 31));
-        const SeqBuf sq = seq_buf<D>(nullptr, k, v, b, h, p.N, p.H, t_end);
-        const FmAddr<D> fa = fm_addr<D>(sm.zkT, nullptr);
-        load_qk<D, false>(rr, sq, t_begin, rsb, lane_b, false);
-        load_v<D, false>(rr, sq, t_begin, rsb, lane_b);
-        {
-            half8 zk[CPT];
-            fm_keys<D, false>(zk, rr, sm, t_begin, L, p.eps_feat, p.eps_norm);
-#pragma unroll
-            for (int c = 0; c < CPT; ++c) wr8(fa.z[c], zk[c]);
-            fm_values<D, false>(rr, sm, fa, L, p.eps_norm);
-            if (nch > 1) {
-                load_qk<D, false>(rr, sq, t_begin + L, rsb, lane_b, false);
-                load_v<D, false>(rr, sq, t_begin + L, rsb, lane_b);
-            }
-        }
-        lds_barrier();  // features of chunk 0 are in shared memory
+    float* dst = ws + (static_cast<int64_t>(seg) * p.B * p.H + bh) * MM * 2 * D * 2;
+    const int rsb = static_cast<int>(p.H * D * 2);  // token stride, bytes
+    if (key) {
+        const int kw = w;
+        f4 U[Cfg<D>::RT];
+        u_load<D>(U, nullptr, kw);
+        const __amdgpu_buffer_rsrc_t rk = seq_rsrc<D>(k, b, h, p.N, p.H, t_end);
+        uint32_t rkk[11];
+        fm_load<D, true>(rkk, rk, rsb, t_begin);
+        halo_fix<D>(rkk, sm, 1, t_begin);
+        fm_keys<D>(rkk, sm, L, p.eps_feat, p.eps_norm);
+        if (nch > 1) fm_load<D, true>(rkk, rk, rsb, t_begin + L);
+        lds_barrier();  // chunk 0 features
         for (int c = 0; c < nch; ++c) {
             const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
-            half8 zk[CPT];
-            if (c + 1 < nch) fm_keys<D, false>(zk, rr, sm, t0 + L, L, p.eps_feat, p.eps_norm);
+            key_update<D>(U, sm.aL, kw, sm.zkT);
             lds_barrier();
             if (c + 1 < nch) {
-#pragma unroll
-                for (int cc = 0; cc < CPT; ++cc) wr8(fa.z[cc], zk[cc]);
-                if (c + 2 < nch) load_qk<D, false>(rr, sq, t0 + 2 * L, rsb, lane_b, false);
-                fm_values<D, false>(rr, sm, fa, L, p.eps_norm);
-                if (c + 2 < nch) load_v<D, false>(rr, sq, t0 + 2 * L, rsb, lane_b);
+                fm_keys<D>(rkk, sm, L, p.eps_feat, p.eps_norm);
+                if (c + 2 < nch) {
+                    step_fence();
+                    fm_load<D, true>(rkk, rk, rsb, t0 + 2 * L);
+                }
             }
             lds_barrier();
         }
+        u_store<D>(U, dst, nullptr, kw);
+    } else {
+        const int vw = w - 8;
+        f4 G[8];
+        if (vw < D / 16) g_load<D>(G, nullptr, vw);
+        const __amdgpu_buffer_rsrc_t rv = seq_rsrc<D>(v, b, h, p.N, p.H, t_end);
+        uint32_t rvv[8];
+        fm_load<D, false>(rvv, rv, rsb, t_begin);
+        fm_values<D>(rvv, sm, L, p.eps_norm);
+        if (nch > 1) fm_load<D, false>(rvv, rv, rsb, t_begin + L);
+        lds_barrier();  // chunk 0 features
+        for (int c = 0; c < nch; ++c) {
+            const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
+            if (vw < D / 16) {
+                half8 bZ[2];
+                load_bz<D>(bZ, vw, sm.zkT);
+                value_update<D>(G, sm.aL, bZ, sm.zkT);
+            }
+            lds_barrier();
+            if (c + 1 < nch) {
+                fm_values<D>(rvv, sm, L, p.eps_norm);
+                if (c + 2 < nch) {
+                    step_fence();
+                    fm_load<D, false>(rvv, rv, rsb, t0 + 2 * L);
+                }
+            }
+            lds_barrier();
+        }
+        if (vw < D / 16) g_store<D>(G, dst, nullptr, vw);
     }
 }
 
@@ -791,7 +755,11 @@ __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, const flo
     }
 }
 
-// Full chunk loop of one segment: grid B*H*S, block (bh, seg).
+// Full chunk loop of one segment: grid B*H*S, block (bh, seg).  Per chunk c:
+//   A  key: G tiles, Q^T = U Y^T, U update        | value: queries of c+1; token loads
+//   B  key: S^T = T^T G'^T, s~, X                  | value: write y'; values of c
+//   C  key: P~ tiles                               | value: X Gamma, Z_v fragments
+//   D  key: keys of c+1                            | value: P~ Z_v, output, Gamma update
 template <int D>
 __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_params prm,
                                                               const uint16_t* __restrict__ q,
@@ -801,12 +769,12 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                                                               const uint16_t* __restrict__ tail_in, float* state_out,
                                                               const uint8_t* __restrict__ tab,
                                                               const float* __restrict__ carry, int64_t Lseg, int S) {
-    constexpr int RT = Cfg<D>::RT, KB = Cfg<D>::KB, CW = Cfg<D>::CW, CPT = Cfg<D>::CPT, RY = Cfg<D>::RY;
+    constexpr int RT = Cfg<D>::RT, KB = Cfg<D>::KB, RY = Cfg<D>::RY;
     constexpr uint32_t dl = WinOff<D>::ftl - WinOff<D>::ft;
     __shared__ SmemFwd<D> sm;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6, g = lane >> 4, i = lane & 15;
-    const bool mw = w < 4;  // MFMA wave
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool key = w < 8;
     const int64_t bh = blockIdx.x / S;
     const int seg = static_cast<int>(blockIdx.x % S);
     const int64_t b = bh / p.H, h = bh % p.H;
@@ -821,52 +789,39 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
     copy16(sm.ft, th + kTabFT, M2 * L * 2);
     copy16(sm.ftl, th + kTabFTL, M2 * L * 2);
     if (tid < MM) sm.aL[tid] = reinterpret_cast<const float2*>(th + kTabPw)[(L - 1) * MM + tid];
-    copy16(sm.pw, th + kTabPw, 16 * MM * 8);
+    for (int e = tid; e < 16 * MM; e += NTH) sm.pw[e / MM][e % MM] = reinterpret_cast<const float2*>(th + kTabPw)[e];
     for (int e = tid; e < L * RP * 2 / 16; e += NTH)
         reinterpret_cast<u4*>(sm.gp)[e] = reinterpret_cast<u4*>(sm.pp)[e] = u4{0u, 0u, 0u, 0u};
     const float2 hc = reinterpret_cast<const float2*>(th + kTabHc)[0];
     const float dt = hc.x, inv_dt = hc.y;
-
-    constexpr uint32_t xc_sc = L * RS * 2;  // xc - sc
+    const int rsb = static_cast<int>(H * D * 2);  // token stride, bytes
+    const float* src = seg == 0 ? (state_in ? state_in + bh * MM * 2 * D * 2 : nullptr)
+                                : carry + (static_cast<int64_t>(seg - 1) * p.B * p.H + bh) * MM * 2 * D * 2;
     __syncthreads();
-    if (mw) {
-        // ---------------- MFMA waves: chunk c
-        State<D> st;
-        state_load<D>(st, seg == 0 ? (state_in ? state_in + bh * MM * 2 * D * 2 : nullptr)
-                                   : carry + (static_cast<int64_t>(seg - 1) * p.B * p.H + bh) * MM * 2 * D * 2);
-        WinB<D> wb;
-        float aLr[2], aLs[2];
-        uint32_t a_perm, a_px, c_gp, c_pp, a_st;
-        // output: one (b, h) sequence up to the segment end; stores past it are dropped
-        const __amdgpu_buffer_rsrc_t ob = __builtin_amdgcn_make_buffer_rsrc(
-            o + b * N * H * D + h * D, 0, static_cast<int>(t_end * H * D * 2), 0x00020000);
-        const int orsb = static_cast<int>(H * D * 2);
-        lds_barrier();  // features of chunk 0 are in shared memory
+    
+    if (key) {
+        // ---------------- key waves
+        const int kw = w;
+        f4 U[RT];
+        u_load<D>(U, src, kw);  // before the token loads, which are waited for first
+        const __amdgpu_buffer_rsrc_t rk = seq_rsrc<D>(k, b, h, N, H, t_end);
+        uint32_t rkk[11];
+        fm_load<D, true>(rkk, rk, rsb, t_begin);
+        halo_fix<D>(rkk, sm, 1, t_begin);
+        fm_keys<D>(rkk, sm, nch > 1 ? L : n_last, p.eps_feat, p.eps_norm);
+        if (nch > 1) fm_load<D, true>(rkk, rk, rsb, t_begin + L);
+        lds_barrier();  // chunk 0 features
         for (int c = 0; c < nch; ++c) {
             const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
-            half8 bZ[CW][2];
-            // lane bases and per-lane constants, recomputed every chunk (cheaper
-            // than holding them in registers across the loop next to the state)
-            wb = win_b<D>(sm.zkT);
+            const int n1 = c + 2 < nch ? L : n_last;  // valid tokens of chunk c + 1
+            const float* sig = sm.sig[c & 1];
+            // ---- A: G tiles -> G'; Q^T = U Y^T (rows m' = 16kw + 4g + jj, columns t); U update
+            int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
 #pragma unroll
-            for (int mu = 0; mu < 2; ++mu) {
-                const float2 a = sm.aL[(32 * w + 16 * mu + i) >> 1];
-                aLr[mu] = a.x;
-                aLs[mu] = (i & 1) ? a.y : -a.y;
-            }
-            a_perm = opaque(lds_addr(sm.yq) + 2 * (i * RY + 4 * g));  // y' 8-byte halves of rows 16tt + i
-            a_px = opaque(lds_addr(sm.xc) + 2 * (i * RS + 4 * g));    // X, likewise
-            a_st = opaque(lds_addr(sm.sc) + 2 * (i * RS + 32 * w + 4 * g));
-            c_gp = opaque(lds_addr(sm.gp) + 2 * (i * RP + 24 - 8 * g));  // G' fragments at column 56 - 32kb - 8g
-            c_pp = opaque(lds_addr(sm.pp) + 2 * (i * RP + 8 * g));
-
-            // ---- G phase: G = Y Z_k^T tiles, stored skewed as G'
-#pragma unroll
-            for (int slot = 0; slot < 3; ++slot) {
-                const int qt = w + 4 * slot;
+            for (int slot = 0; slot < 2; ++slot) {
+                const int qt = kw + 8 * slot;
                 if (qt < 10) {
                     const int tt = tile_tt(qt), jt = tile_kt(qt);
-                    // (recomputed every chunk: kept out of the registers held across the loop)
                     const uint32_t ar = opaque(lds_addr(sm.yq) + 2 * ((16 * tt + i) * RY + 8 * g));
                     const uint32_t br0 = opaque(lds_addr(sm.zkT) + 2 * o128(8 * g + (i >> 2), 16 * jt + 4 * (i & 3)));
                     const uint32_t br1 = opaque(lds_addr(sm.zkT) + 2 * o128(8 * g + (i >> 2) + 4, 16 * jt + 4 * (i & 3)));
@@ -880,78 +835,76 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                         if (16 * jt + i <= 16 * tt + 4 * g + jj) wr1(gs + 2 * (RP - 1) * jj, accG[jj]);
                 }
             }
-            lds_barrier();
-
-            // ---- S phase: per U block mu: Q^T = U Y^T, S^T = T^T G'^T (K order reversed:
-            // element jj <-> k = 32kb + 8g + 7 - jj), s~ = sigma~ (S + abar^{t+1} Q),
-            // X = s~ abar^{t+1}; then the U update and the Z_v fragments
+            f4 accQ[4];
 #pragma unroll
-            for (int mu = 0; mu < 2; ++mu) {
-                // abar^{i+1} and abar^16 of modes 16w + 8mu + 2g + qq
-                const float4 e0 = *reinterpret_cast<const float4*>(&sm.pw[i][16 * w + 8 * mu + 2 * g]);
-                const float4 e16 = *reinterpret_cast<const float4*>(&sm.pw[15][16 * w + 8 * mu + 2 * g]);
-                float er[2] = {e0.x, e0.z}, ei[2] = {e0.y, e0.w};
-                const float e16r[2] = {e16.x, e16.z}, e16i[2] = {e16.y, e16.w};
+            for (int tt = 0; tt < 4; ++tt) accQ[tt] = f4{0.f, 0.f, 0.f, 0.f};
+            {
+                const uint32_t a_perm = opaque(lds_addr(sm.yq) + 2 * (i * RY + 4 * g));
 #pragma unroll
-                for (int th2 = 0; th2 < 2; ++th2) {  // t-tiles 2 th2, 2 th2 + 1
-                    f4 accQ[2], accS[2];
+                for (int kb = 0; kb < KB; ++kb) {
+                    const half8 aU = to_half8(U[2 * kb], U[2 * kb + 1]);
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) accQ[u] = accS[u] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) {
-                        const half8 aU = to_half8(st.U[mu][2 * kb], st.U[mu][2 * kb + 1]);
-#pragma unroll
-                        for (int u = 0; u < 2; ++u) {
-                            const uint32_t row = a_perm + 2 * (16 * (2 * th2 + u) * RY + 32 * kb);
-                            accQ[u] = mfma(aU, cat(rd4(row), rd4(row + 32)), accQ[u]);
-                        }
-                        step_fence();
-                    }
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
-                        const uint32_t ta =
-                            opaque(lds_addr(sm.ft) + 2 * (o128(i, L - 8 - 32 * kb - 8 * g) + 64 * (32 * w + 16 * mu)));
-                        const half8 aT = rd8(ta), aTl = rd8(ta + dl);
-#pragma unroll
-                        for (int u = 0; u < 2; ++u) {
-                            const half8 bg = rd8(c_gp + 2 * (16 * (2 * th2 + u) * RP + 32 * (1 - kb)));
-                            accS[u] = mfma(aT, bg, accS[u]);
-                            accS[u] = mfma(aTl, bg, accS[u]);
-                        }
-                        step_fence();
-                    }
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int tt = 2 * th2 + u;
-                        const float sg = sm.sig[16 * tt + i];
-                        float sv[4], xv[4];
-#pragma unroll
-                        for (int qq = 0; qq < 2; ++qq) {
-                            const float qr = accQ[u][2 * qq], qi = accQ[u][2 * qq + 1];
-                            const float sr = sg * (accS[u][2 * qq] + er[qq] * qr - ei[qq] * qi);
-                            const float si = sg * (accS[u][2 * qq + 1] + er[qq] * qi + ei[qq] * qr);
-                            sv[2 * qq] = sr;
-                            sv[2 * qq + 1] = -si;
-                            xv[2 * qq] = sr * er[qq] - si * ei[qq];
-                            xv[2 * qq + 1] = -(sr * ei[qq] + si * er[qq]);
-                            const float nr = er[qq] * e16r[qq] - ei[qq] * e16i[qq];
-                            ei[qq] = er[qq] * e16i[qq] + ei[qq] * e16r[qq];
-                            er[qq] = nr;
-                        }
-                        wr4(a_st + 2 * (16 * tt * RS + 16 * mu), sv[0], sv[1], sv[2], sv[3]);
-                        wr4(a_st + 2 * (16 * tt * RS + 16 * mu) + xc_sc, xv[0], xv[1], xv[2], xv[3]);
+                    for (int tt = 0; tt < 4; ++tt) {
+                        const uint32_t row = a_perm + 2 * (16 * tt * RY + 32 * kb);
+                        accQ[tt] = mfma(aU, cat(rd4(row), rd4(row + 32)), accQ[tt]);
                     }
                 }
             }
-            key_update<D>(st, wb, aLr, aLs);
-            load_bz<D>(bZ, wb);
+            key_update<D>(U, sm.aL, kw, sm.zkT);
             lds_barrier();
-
-            // ---- P phase: P~'[t][k] = sum_m' sc[t][m'] T[k][m'] tiles (lane (g, i) of the T
-            // operand holds k = 16 kt + 15 - i), un-skewed into P~[t][t - k]
+            ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
+            // ---- B: S^T = T^T G'^T (K order reversed: element jj <-> k = 32kb + 8g + 7 - jj),
+            // s~ = sigma~ (S + abar^{t+1} Q), X = s~ abar^{t+1}
+            {
+                f4 accS[4];
 #pragma unroll
-            for (int slot = 0; slot < 3; ++slot) {
-                const int qt = w + 4 * slot;
+                for (int tt = 0; tt < 4; ++tt) accS[tt] = f4{0.f, 0.f, 0.f, 0.f};
+                const uint32_t c_gp = opaque(lds_addr(sm.gp) + 2 * (i * RP + 24 - 8 * g));
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const uint32_t ta = opaque(lds_addr(sm.ft) + 2 * (o128(i, L - 8 - 32 * kb - 8 * g) + 64 * 16 * kw));
+                    const half8 aT = rd8(ta), aTl = rd8(ta + dl);
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) {
+                        const half8 bg = rd8(c_gp + 2 * (16 * tt * RP + 32 * (1 - kb)));
+                        accS[tt] = mfma(aT, bg, accS[tt]);
+                        accS[tt] = mfma(aTl, bg, accS[tt]);
+                    }
+                }
+                // abar^{i+1} and abar^16 of modes 8kw + 2g + qq
+                const float4 e0 = *reinterpret_cast<const float4*>(&sm.pw[i][8 * kw + 2 * g]);
+                const float4 e16 = *reinterpret_cast<const float4*>(&sm.pw[15][8 * kw + 2 * g]);
+                float er[2] = {e0.x, e0.z}, ei[2] = {e0.y, e0.w};
+                const float e16r[2] = {e16.x, e16.z}, e16i[2] = {e16.y, e16.w};
+                const uint32_t a_st = opaque(lds_addr(sm.sc) + 2 * (i * RS + 16 * kw + 4 * g));
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const float sg = sig[16 * tt + i];
+                    float sv[4], xv[4];
+#pragma unroll
+                    for (int qq = 0; qq < 2; ++qq) {
+                        const float qr = accQ[tt][2 * qq], qi = accQ[tt][2 * qq + 1];
+                        const float sr = sg * (accS[tt][2 * qq] + er[qq] * qr - ei[qq] * qi);
+                        const float si = sg * (accS[tt][2 * qq + 1] + er[qq] * qi + ei[qq] * qr);
+                        sv[2 * qq] = sr;
+                        sv[2 * qq + 1] = -si;
+                        xv[2 * qq] = sr * er[qq] - si * ei[qq];
+                        xv[2 * qq + 1] = -(sr * ei[qq] + si * er[qq]);
+                        const float nr = er[qq] * e16r[qq] - ei[qq] * e16i[qq];
+                        ei[qq] = er[qq] * e16i[qq] + ei[qq] * e16r[qq];
+                        er[qq] = nr;
+                    }
+                    wr4(a_st + 2 * 16 * tt * RS, sv[0], sv[1], sv[2], sv[3]);
+                    wr4(a_st + 2 * 16 * tt * RS + L * RS * 2, xv[0], xv[1], xv[2], xv[3]);
+                }
+            }
+            lds_barrier();
+            ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
+            // ---- C: P~'[t][k] = sum_m' sc[t][m'] T[k][m'] tiles (lane (g, i) of the T operand
+            // holds k = 16 kt + 15 - i), un-skewed into P~[t][t - k]
+#pragma unroll
+            for (int slot = 0; slot < 2; ++slot) {
+                const int qt = kw + 8 * slot;
                 if (qt < 10) {
                     const int tt = tile_tt(qt), kt = tile_kt(qt);
                     const uint32_t ar = opaque(lds_addr(sm.sc) + 2 * ((16 * tt + i) * RS + 8 * g));
@@ -971,95 +924,104 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                 }
             }
             lds_barrier();
-
-            // ---- O phase: o = Delta (X Gamma_prev + P~ Z_v); Gamma update
-#pragma unroll
-            for (int ct = 0; ct < CW; ++ct) {
-                half8 bG[4];
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) bG[kb] = to_half8(st.Gm[2 * kb][ct], st.Gm[2 * kb + 1][ct]);
-                const uint32_t olane = static_cast<uint32_t>(4 * g * orsb + 2 * (16 * (CW * w + ct) + i));
-#pragma unroll
-                for (int th2 = 0; th2 < 2; ++th2) {  // t-tiles 2 th2, 2 th2 + 1
-                    f4 accO[2] = {};
-#pragma unroll
-                    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-                        for (int u = 0; u < 2; ++u) {
-                            const uint32_t row = a_px + 2 * (16 * (2 * th2 + u) * RS + 32 * kb);
-                            accO[u] = mfma(cat(rd4(row), rd4(row + 32)), bG[kb], accO[u]);
-                        }
-                        step_fence();
-                    }
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                        for (int u = 0; u < 2; ++u)
-                            accO[u] = mfma(rd8(c_pp + 2 * (16 * (2 * th2 + u) * RP + 32 * kb)), bZ[ct][kb], accO[u]);
-                        step_fence();
-                    }
-#pragma unroll
-                    for (int u = 0; u < 2; ++u)
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) {
-                            const uint32_t toff = static_cast<uint32_t>((t0 + 16 * (2 * th2 + u) + jj) * orsb);
-                            __builtin_amdgcn_raw_buffer_store_b16(to_bf16(accO[u][jj] * dt), ob, olane + toff, 0, 0);
-                        }
+            // ---- D: keys of chunk c + 1
+            if (c + 1 < nch) {
+                fm_keys<D>(rkk, sm, n1, p.eps_feat, p.eps_norm);
+                if (c + 2 < nch) {
+                    step_fence();
+                    fm_load<D, true>(rkk, rk, rsb, t0 + 2 * L);
                 }
             }
-            value_update<D>(st, sm.aL, wb, bZ);
             lds_barrier();
         }
         if (seg == S - 1 && state_out != nullptr)
-            state_store<D>(st, state_out + bh * MM * 2 * D * 2,
-                           n_last < L ? reinterpret_cast<const float2*>(th + kTabPwBack) : nullptr);
+            u_store<D>(U, state_out + bh * MM * 2 * D * 2,
+                       n_last < L ? reinterpret_cast<const float2*>(th + kTabPwBack) : nullptr, kw);
     } else {
-        // ---------------- feature waves: chunk c + 1 while the MFMA waves run chunk c
-        FmRaw<D, true> rr;
-        const int rsb = static_cast<int>(H * D * 2);
-        const int f = tid - 256;
-        const int lane_b = 2 * (8 * (f >> 5) * static_cast<int>(H * D) + CPT * (f & 31));
-        const SeqBuf sq = seq_buf<D>(q, k, v, b, h, N, H, t_end);
-        const FmAddr<D> fa = fm_addr<D>(sm.zkT, sm.yq);
-        load_qk<D, true>(rr, sq, t_begin, rsb, lane_b, true);
-        load_qk<D, true>(rr, sq, t_begin, rsb, lane_b, false);
-        load_v<D, true>(rr, sq, t_begin, rsb, lane_b);
+        // ---------------- value waves
+        const int vw = w - 8;
+        const bool own = vw < D / 16;  // owns a 16-column block of Gamma
+        f4 G[8];
+        if (own) g_load<D>(G, src, vw);  // before the token loads, which are waited for first
+        const __amdgpu_buffer_rsrc_t rq = seq_rsrc<D>(q, b, h, N, H, t_end);
+        const __amdgpu_buffer_rsrc_t rv = seq_rsrc<D>(v, b, h, N, H, t_end);
+        const __amdgpu_buffer_rsrc_t ob = seq_rsrc<D>(o, b, h, N, H, t_end);
+        uint32_t rqq[11], rvv[8];
+        fm_load<D, true>(rqq, rq, rsb, t_begin);
+        halo_fix<D>(rqq, sm, 0, t_begin);
         {
-            const int n0 = nch > 1 ? L : n_last;
-            half8 zk[CPT];
-            fm_keys<D, true>(zk, rr, sm, t_begin, n0, p.eps_feat, p.eps_norm);
-#pragma unroll
-            for (int c = 0; c < CPT; ++c) wr8(fa.z[c], zk[c]);
-            fm_values<D, true>(rr, sm, fa, n0, p.eps_norm);
-            fm_queries<D>(rr, sm, fa.y, t_begin, p.eps_feat, inv_dt);
-            if (nch > 1) {
-                load_qk<D, true>(rr, sq, t_begin + L, rsb, lane_b, true);
-                load_qk<D, true>(rr, sq, t_begin + L, rsb, lane_b, false);
-                load_v<D, true>(rr, sq, t_begin + L, rsb, lane_b);
-            }
+            half2v yo[8];
+            fm_queries<D>(yo, rqq, sm, sm.sig[0], p.eps_feat, inv_dt);
+            fm_write_q<D>(yo, sm.yq);
         }
-        lds_barrier();  // features of chunk 0 are in shared memory
+        fm_load<D, false>(rvv, rv, rsb, t_begin);
+        if (nch > 1) fm_load<D, true>(rqq, rq, rsb, t_begin + L);
+        vm_wait_all();  // the loop then enters with no load in flight, as it does from its own end
+        lds_barrier();  // chunk 0 features
         for (int c = 0; c < nch; ++c) {
             const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
-            const int n1 = c + 2 < nch ? L : (c + 1 < nch ? n_last : 0);  // valid tokens of chunk c + 1
-            half8 zk[CPT];
-            lds_barrier();  // G phase
-            if (c + 1 < nch) fm_keys<D, true>(zk, rr, sm, t0 + L, n1, p.eps_feat, p.eps_norm);
-            lds_barrier();  // S phase
-            if (c + 1 < nch) {
+            half2v yo[8];
+            uint32_t rvn[8];
+            // ---- A: queries of chunk c + 1 (held until B); token loads for the chunks ahead
+            if (c + 1 < nch) fm_queries<D>(yo, rqq, sm, sm.sig[(c + 1) & 1], p.eps_feat, inv_dt);
+            step_fence();
+            if (c + 2 < nch) fm_load<D, true>(rqq, rq, rsb, t0 + 2 * L);
+            if (c + 1 < nch) fm_load<D, false>(rvn, rv, rsb, t0 + L);
+            lds_barrier();
+            // ---- B: write y' of chunk c + 1; values of chunk c
+            if (c + 1 < nch) fm_write_q<D>(yo, sm.yq);
+            fm_values<D>(rvv, sm, c + 1 < nch ? L : n_last, p.eps_norm);
 #pragma unroll
-                for (int cc = 0; cc < CPT; ++cc) wr8(fa.z[cc], zk[cc]);
-                if (c + 2 < nch) load_qk<D, true>(rr, sq, t0 + 2 * L, rsb, lane_b, false);
-                fm_values<D, true>(rr, sm, fa, n1, p.eps_norm);
-                if (c + 2 < nch) load_v<D, true>(rr, sq, t0 + 2 * L, rsb, lane_b);
+            for (int s2 = 0; s2 < 8; ++s2) rvv[s2] = rvn[s2];
+            lds_barrier();
+            // ---- C: o^T = Gamma_prev^T X^T (c-block vw: lane (g, i) of tile tt holds
+            // o[16tt + i][16vw + 4g + jj], four consecutive channels of one token); Z_v fragments
+            f4 accO[4];
+            half8 bZ[2];
+            if (own) {
+                const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) accO[tt] = f4{0.f, 0.f, 0.f, 0.f};
+                const uint32_t a_px = opaque(lds_addr(sm.xc) + 2 * (i * RS + 4 * g));
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const half8 bG = to_half8(G[2 * kb], G[2 * kb + 1]);
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) {
+                        const uint32_t row = a_px + 2 * (16 * tt * RS + 32 * kb);
+                        accO[tt] = mfma(bG, cat(rd4(row), rd4(row + 32)), accO[tt]);
+                    }
+                }
+                load_bz<D>(bZ, vw, sm.zkT);
             }
-            lds_barrier();  // P phase
-            if (c + 1 < nch) {
-                fm_queries<D>(rr, sm, fa.y, t0 + L, p.eps_feat, inv_dt);
-                if (c + 2 < nch) load_qk<D, true>(rr, sq, t0 + 2 * L, rsb, lane_b, true);
+            lds_barrier();
+            // ---- D: o^T += Z_v^T P~^T; store Delta o; Gamma update
+            vm_wait_all();  // token loads of A, before any store joins the counter
+            if (own) {
+                const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
+                const uint32_t c_pp = opaque(lds_addr(sm.pp) + 2 * (i * RP + 8 * g));
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt)
+                        accO[tt] = mfma(bZ[kb], rd8(c_pp + 2 * (16 * tt * RP + 32 * kb)), accO[tt]);
+                const uint32_t olane = static_cast<uint32_t>(i * rsb + 2 * (16 * vw + 4 * g));
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const uint32_t toff = static_cast<uint32_t>((t0 + 16 * tt) * rsb);
+                    const u2 pk = {static_cast<uint32_t>(to_bf16(accO[tt][0] * dt)) |
+                                       (static_cast<uint32_t>(to_bf16(accO[tt][1] * dt)) << 16),
+                                   static_cast<uint32_t>(to_bf16(accO[tt][2] * dt)) |
+                                       (static_cast<uint32_t>(to_bf16(accO[tt][3] * dt)) << 16)};
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, pk), ob, olane + toff, 0, 0);
+                }
+                value_update<D>(G, sm.aL, bZ, sm.zkT);
             }
-            lds_barrier();  // O phase
+            lds_barrier();
         }
+        if (own && seg == S - 1 && state_out != nullptr)
+            g_store<D>(G, state_out + bh * MM * 2 * D * 2,
+                       n_last < L ? reinterpret_cast<const float2*>(th + kTabPwBack) : nullptr, vw);
     }
 }
 
