@@ -755,11 +755,18 @@ __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, const flo
     }
 }
 
-// Full chunk loop of one segment: grid B*H*S, block (bh, seg).  Per chunk c:
-//   A  key: G tiles, Q^T = U Y^T, U update        | value: queries of c+1; token loads
-//   B  key: S^T = T^T G'^T, s~, X                  | value: write y'; values of c
-//   C  key: P~ tiles                               | value: X Gamma, Z_v fragments
-//   D  key: keys of c+1                            | value: P~ Z_v, output, Gamma update
+// Full chunk loop of one segment: grid B*H*S, block (bh, seg).  The readout of
+// a chunk runs one step behind its s~ and X, so that a step c = 0..nch needs
+// two barriers:
+//   1  key: G tiles, Q^T = U Y^T, U update (chunk c); P~ tiles (c-1)
+//      value: values (c); queries (c+1, held); X Gamma (c-1); token loads
+//   2  key: S^T = T^T G'^T, s~, X (c); keys (c+1)
+//      value: write y' (c+1); P~ Z_v, output, Gamma update (c-1); Z_v fragments (c)
+// Every shared tile is written in one phase and read in the next: y', z_k (c)
+// in 1 of step c, rewritten in 2; G' (c) written in 1, read in 2; s~, X (c)
+// written in 2 of step c, read in 1 of step c+1; P~ (c-1) written in 1, read
+// in 2 of step c; z_v (c) written in 1 and read in 2 of step c into
+// registers that the readout of step c+1 uses.
 template <int D>
 __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_params prm,
                                                               const uint16_t* __restrict__ q,
@@ -811,122 +818,126 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         fm_keys<D>(rkk, sm, nch > 1 ? L : n_last, p.eps_feat, p.eps_norm);
         if (nch > 1) fm_load<D, true>(rkk, rk, rsb, t_begin + L);
         lds_barrier();  // chunk 0 features
-        for (int c = 0; c < nch; ++c) {
+        for (int c = 0; c <= nch; ++c) {
             const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
-            const int n1 = c + 2 < nch ? L : n_last;  // valid tokens of chunk c + 1
-            const float* sig = sm.sig[c & 1];
-            // ---- A: G tiles -> G'; Q^T = U Y^T (rows m' = 16kw + 4g + jj, columns t); U update
-            int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
-#pragma unroll
-            for (int slot = 0; slot < 2; ++slot) {
-                const int qt = kw + 8 * slot;
-                if (qt < 10) {
-                    const int tt = tile_tt(qt), jt = tile_kt(qt);
-                    const uint32_t ar = opaque(lds_addr(sm.yq) + 2 * ((16 * tt + i) * RY + 8 * g));
-                    const uint32_t br0 = opaque(lds_addr(sm.zkT) + 2 * o128(8 * g + (i >> 2), 16 * jt + 4 * (i & 3)));
-                    const uint32_t br1 = opaque(lds_addr(sm.zkT) + 2 * o128(8 * g + (i >> 2) + 4, 16 * jt + 4 * (i & 3)));
-                    f4 accG = {};
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb)
-                        accG = mfma(rd8(ar + 64 * kb), cat(rd4t(br0 + 4096 * kb), rd4t(br1 + 4096 * kb)), accG);
-                    const uint32_t gs = opaque(lds_addr(sm.gp) + 2 * ((16 * tt + 4 * g) * (RP - 1) + L - 1 + 16 * jt + i));
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        if (16 * jt + i <= 16 * tt + 4 * g + jj) wr1(gs + 2 * (RP - 1) * jj, accG[jj]);
-                }
-            }
+            // ---- phase 1
             f4 accQ[4];
+            if (c < nch) {
+                // G tiles -> G'; Q^T = U Y^T (rows m' = 16kw + 4g + jj, columns t); U update
+                const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) accQ[tt] = f4{0.f, 0.f, 0.f, 0.f};
-            {
-                const uint32_t a_perm = opaque(lds_addr(sm.yq) + 2 * (i * RY + 4 * g));
+                for (int slot = 0; slot < 2; ++slot) {
+                    const int qt = kw + 8 * slot;
+                    if (qt < 10) {
+                        const int tt = tile_tt(qt), jt = tile_kt(qt);
+                        const uint32_t ar = opaque(lds_addr(sm.yq) + 2 * ((16 * tt + i) * RY + 8 * g));
+                        const uint32_t br0 = opaque(lds_addr(sm.zkT) + 2 * o128(8 * g + (i >> 2), 16 * jt + 4 * (i & 3)));
+                        const uint32_t br1 = opaque(lds_addr(sm.zkT) + 2 * o128(8 * g + (i >> 2) + 4, 16 * jt + 4 * (i & 3)));
+                        f4 accG = {};
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const half8 aU = to_half8(U[2 * kb], U[2 * kb + 1]);
+                        for (int kb = 0; kb < KB; ++kb)
+                            accG = mfma(rd8(ar + 64 * kb), cat(rd4t(br0 + 4096 * kb), rd4t(br1 + 4096 * kb)), accG);
+                        const uint32_t gs = opaque(lds_addr(sm.gp) + 2 * ((16 * tt + 4 * g) * (RP - 1) + L - 1 + 16 * jt + i));
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+                            if (16 * jt + i <= 16 * tt + 4 * g + jj) wr1(gs + 2 * (RP - 1) * jj, accG[jj]);
+                    }
+                }
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) accQ[tt] = f4{0.f, 0.f, 0.f, 0.f};
+                {
+                    const uint32_t a_perm = opaque(lds_addr(sm.yq) + 2 * (i * RY + 4 * g));
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        const half8 aU = to_half8(U[2 * kb], U[2 * kb + 1]);
+#pragma unroll
+                        for (int tt = 0; tt < 4; ++tt) {
+                            const uint32_t row = a_perm + 2 * (16 * tt * RY + 32 * kb);
+                            accQ[tt] = mfma(aU, cat(rd4(row), rd4(row + 32)), accQ[tt]);
+                        }
+                    }
+                }
+                key_update<D>(U, sm.aL, kw, sm.zkT);
+            }
+            if (c >= 1) {
+                const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
+                // P~'[t][k] = sum_m' sc[t][m'] T[k][m'] tiles (lane (g, i) of the T operand
+                // holds k = 16 kt + 15 - i), un-skewed into P~[t][t - k]
+#pragma unroll
+                for (int slot = 0; slot < 2; ++slot) {
+                    const int qt = kw + 8 * slot;
+                    if (qt < 10) {
+                        const int tt = tile_tt(qt), kt = tile_kt(qt);
+                        const uint32_t ar = opaque(lds_addr(sm.sc) + 2 * ((16 * tt + i) * RS + 8 * g));
+                        const uint32_t br0 = opaque(lds_addr(sm.ft) + 2 * o128(8 * g + (i >> 2), L - 16 - 16 * kt + 4 * (i & 3)));
+                        const uint32_t br1 = opaque(lds_addr(sm.ft) + 2 * o128(8 * g + (i >> 2) + 4, L - 16 - 16 * kt + 4 * (i & 3)));
+                        f4 accP = {};
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb) {
+                            const half8 a = rd8(ar + 64 * kb);
+                            accP = mfma(a, cat(rd4t(br0 + 4096 * kb), rd4t(br1 + 4096 * kb)), accP);
+                            accP = mfma(a, cat(rd4t(br0 + 4096 * kb + dl), rd4t(br1 + 4096 * kb + dl)), accP);
+                        }
+                        const uint32_t ps = opaque(lds_addr(sm.pp) + 2 * ((16 * tt + 4 * g) * (RP + 1) - 16 * kt - 15 + i));
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+                            if (16 * kt + 15 - i <= 16 * tt + 4 * g + jj) wr1(ps + 2 * (RP + 1) * jj, accP[jj]);
+                    }
+                }
+            }
+            lds_barrier();
+            // ---- phase 2
+            if (c < nch) {
+                const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
+                const float* sig = sm.sig[c & 1];
+                // S^T = T^T G'^T (K order reversed: element jj <-> k = 32kb + 8g + 7 - jj),
+                // s~ = sigma~ (S + abar^{t+1} Q), X = s~ abar^{t+1}
+                {
+                    f4 accS[4];
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) accS[tt] = f4{0.f, 0.f, 0.f, 0.f};
+                    const uint32_t c_gp = opaque(lds_addr(sm.gp) + 2 * (i * RP + 24 - 8 * g));
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        const uint32_t ta = opaque(lds_addr(sm.ft) + 2 * (o128(i, L - 8 - 32 * kb - 8 * g) + 64 * 16 * kw));
+                        const half8 aT = rd8(ta), aTl = rd8(ta + dl);
+#pragma unroll
+                        for (int tt = 0; tt < 4; ++tt) {
+                            const half8 bg = rd8(c_gp + 2 * (16 * tt * RP + 32 * (1 - kb)));
+                            accS[tt] = mfma(aT, bg, accS[tt]);
+                            accS[tt] = mfma(aTl, bg, accS[tt]);
+                        }
+                    }
+                    // abar^{i+1} and abar^16 of modes 8kw + 2g + qq
+                    const float4 e0 = *reinterpret_cast<const float4*>(&sm.pw[i][8 * kw + 2 * g]);
+                    const float4 e16 = *reinterpret_cast<const float4*>(&sm.pw[15][8 * kw + 2 * g]);
+                    float er[2] = {e0.x, e0.z}, ei[2] = {e0.y, e0.w};
+                    const float e16r[2] = {e16.x, e16.z}, e16i[2] = {e16.y, e16.w};
+                    const uint32_t a_st = opaque(lds_addr(sm.sc) + 2 * (i * RS + 16 * kw + 4 * g));
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) {
-                        const uint32_t row = a_perm + 2 * (16 * tt * RY + 32 * kb);
-                        accQ[tt] = mfma(aU, cat(rd4(row), rd4(row + 32)), accQ[tt]);
+                        const float sg = sig[16 * tt + i];
+                        float sv[4], xv[4];
+#pragma unroll
+                        for (int qq = 0; qq < 2; ++qq) {
+                            const float qr = accQ[tt][2 * qq], qi = accQ[tt][2 * qq + 1];
+                            const float sr = sg * (accS[tt][2 * qq] + er[qq] * qr - ei[qq] * qi);
+                            const float si = sg * (accS[tt][2 * qq + 1] + er[qq] * qi + ei[qq] * qr);
+                            sv[2 * qq] = sr;
+                            sv[2 * qq + 1] = -si;
+                            xv[2 * qq] = sr * er[qq] - si * ei[qq];
+                            xv[2 * qq + 1] = -(sr * ei[qq] + si * er[qq]);
+                            const float nr = er[qq] * e16r[qq] - ei[qq] * e16i[qq];
+                            ei[qq] = er[qq] * e16i[qq] + ei[qq] * e16r[qq];
+                            er[qq] = nr;
+                        }
+                        wr4(a_st + 2 * 16 * tt * RS, sv[0], sv[1], sv[2], sv[3]);
+                        wr4(a_st + 2 * 16 * tt * RS + L * RS * 2, xv[0], xv[1], xv[2], xv[3]);
                     }
                 }
             }
-            key_update<D>(U, sm.aL, kw, sm.zkT);
-            lds_barrier();
-            ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
-            // ---- B: S^T = T^T G'^T (K order reversed: element jj <-> k = 32kb + 8g + 7 - jj),
-            // s~ = sigma~ (S + abar^{t+1} Q), X = s~ abar^{t+1}
-            {
-                f4 accS[4];
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) accS[tt] = f4{0.f, 0.f, 0.f, 0.f};
-                const uint32_t c_gp = opaque(lds_addr(sm.gp) + 2 * (i * RP + 24 - 8 * g));
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const uint32_t ta = opaque(lds_addr(sm.ft) + 2 * (o128(i, L - 8 - 32 * kb - 8 * g) + 64 * 16 * kw));
-                    const half8 aT = rd8(ta), aTl = rd8(ta + dl);
-#pragma unroll
-                    for (int tt = 0; tt < 4; ++tt) {
-                        const half8 bg = rd8(c_gp + 2 * (16 * tt * RP + 32 * (1 - kb)));
-                        accS[tt] = mfma(aT, bg, accS[tt]);
-                        accS[tt] = mfma(aTl, bg, accS[tt]);
-                    }
-                }
-                // abar^{i+1} and abar^16 of modes 8kw + 2g + qq
-                const float4 e0 = *reinterpret_cast<const float4*>(&sm.pw[i][8 * kw + 2 * g]);
-                const float4 e16 = *reinterpret_cast<const float4*>(&sm.pw[15][8 * kw + 2 * g]);
-                float er[2] = {e0.x, e0.z}, ei[2] = {e0.y, e0.w};
-                const float e16r[2] = {e16.x, e16.z}, e16i[2] = {e16.y, e16.w};
-                const uint32_t a_st = opaque(lds_addr(sm.sc) + 2 * (i * RS + 16 * kw + 4 * g));
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) {
-                    const float sg = sig[16 * tt + i];
-                    float sv[4], xv[4];
-#pragma unroll
-                    for (int qq = 0; qq < 2; ++qq) {
-                        const float qr = accQ[tt][2 * qq], qi = accQ[tt][2 * qq + 1];
-                        const float sr = sg * (accS[tt][2 * qq] + er[qq] * qr - ei[qq] * qi);
-                        const float si = sg * (accS[tt][2 * qq + 1] + er[qq] * qi + ei[qq] * qr);
-                        sv[2 * qq] = sr;
-                        sv[2 * qq + 1] = -si;
-                        xv[2 * qq] = sr * er[qq] - si * ei[qq];
-                        xv[2 * qq + 1] = -(sr * ei[qq] + si * er[qq]);
-                        const float nr = er[qq] * e16r[qq] - ei[qq] * e16i[qq];
-                        ei[qq] = er[qq] * e16i[qq] + ei[qq] * e16r[qq];
-                        er[qq] = nr;
-                    }
-                    wr4(a_st + 2 * 16 * tt * RS, sv[0], sv[1], sv[2], sv[3]);
-                    wr4(a_st + 2 * 16 * tt * RS + L * RS * 2, xv[0], xv[1], xv[2], xv[3]);
-                }
-            }
-            lds_barrier();
-            ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
-            // ---- C: P~'[t][k] = sum_m' sc[t][m'] T[k][m'] tiles (lane (g, i) of the T operand
-            // holds k = 16 kt + 15 - i), un-skewed into P~[t][t - k]
-#pragma unroll
-            for (int slot = 0; slot < 2; ++slot) {
-                const int qt = kw + 8 * slot;
-                if (qt < 10) {
-                    const int tt = tile_tt(qt), kt = tile_kt(qt);
-                    const uint32_t ar = opaque(lds_addr(sm.sc) + 2 * ((16 * tt + i) * RS + 8 * g));
-                    const uint32_t br0 = opaque(lds_addr(sm.ft) + 2 * o128(8 * g + (i >> 2), L - 16 - 16 * kt + 4 * (i & 3)));
-                    const uint32_t br1 = opaque(lds_addr(sm.ft) + 2 * o128(8 * g + (i >> 2) + 4, L - 16 - 16 * kt + 4 * (i & 3)));
-                    f4 accP = {};
-#pragma unroll
-                    for (int kb = 0; kb < 4; ++kb) {
-                        const half8 a = rd8(ar + 64 * kb);
-                        accP = mfma(a, cat(rd4t(br0 + 4096 * kb), rd4t(br1 + 4096 * kb)), accP);
-                        accP = mfma(a, cat(rd4t(br0 + 4096 * kb + dl), rd4t(br1 + 4096 * kb + dl)), accP);
-                    }
-                    const uint32_t ps = opaque(lds_addr(sm.pp) + 2 * ((16 * tt + 4 * g) * (RP + 1) - 16 * kt - 15 + i));
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        if (16 * kt + 15 - i <= 16 * tt + 4 * g + jj) wr1(ps + 2 * (RP + 1) * jj, accP[jj]);
-                }
-            }
-            lds_barrier();
-            // ---- D: keys of chunk c + 1
             if (c + 1 < nch) {
-                fm_keys<D>(rkk, sm, n1, p.eps_feat, p.eps_norm);
+                fm_keys<D>(rkk, sm, c + 2 < nch ? L : n_last, p.eps_feat, p.eps_norm);
                 if (c + 2 < nch) {
                     step_fence();
                     fm_load<D, true>(rkk, rk, rsb, t0 + 2 * L);
@@ -958,27 +969,29 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         if (nch > 1) fm_load<D, true>(rqq, rq, rsb, t_begin + L);
         vm_wait_all();  // the loop then enters with no load in flight, as it does from its own end
         lds_barrier();  // chunk 0 features
-        for (int c = 0; c < nch; ++c) {
+        half8 bZ[2];    // Z_v fragments of the chunk whose readout comes next
+        for (int c = 0; c <= nch; ++c) {
             const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
             half2v yo[8];
-            uint32_t rvn[8];
-            // ---- A: queries of chunk c + 1 (held until B); token loads for the chunks ahead
-            if (c + 1 < nch) fm_queries<D>(yo, rqq, sm, sm.sig[(c + 1) & 1], p.eps_feat, inv_dt);
-            step_fence();
-            if (c + 2 < nch) fm_load<D, true>(rqq, rq, rsb, t0 + 2 * L);
-            if (c + 1 < nch) fm_load<D, false>(rvn, rv, rsb, t0 + L);
-            lds_barrier();
-            // ---- B: write y' of chunk c + 1; values of chunk c
-            if (c + 1 < nch) fm_write_q<D>(yo, sm.yq);
-            fm_values<D>(rvv, sm, c + 1 < nch ? L : n_last, p.eps_norm);
-#pragma unroll
-            for (int s2 = 0; s2 < 8; ++s2) rvv[s2] = rvn[s2];
-            lds_barrier();
-            // ---- C: o^T = Gamma_prev^T X^T (c-block vw: lane (g, i) of tile tt holds
-            // o[16tt + i][16vw + 4g + jj], four consecutive channels of one token); Z_v fragments
             f4 accO[4];
-            half8 bZ[2];
-            if (own) {
+            // ---- phase 1: values (c); queries (c+1), held until phase 2; token loads; X Gamma (c-1)
+            if (c < nch) {
+                fm_values<D>(rvv, sm, c + 1 < nch ? L : n_last, p.eps_norm);
+                if (c + 1 < nch) {
+                    step_fence();
+                    fm_load<D, false>(rvv, rv, rsb, t0 + L);
+                }
+            }
+            if (c + 1 < nch) {
+                fm_queries<D>(yo, rqq, sm, sm.sig[(c + 1) & 1], p.eps_feat, inv_dt);
+                if (c + 2 < nch) {
+                    step_fence();
+                    fm_load<D, true>(rqq, rq, rsb, t0 + 2 * L);
+                }
+            }
+            if (c >= 1 && own) {
+                // o^T = Gamma_prev^T X^T (c-block vw: lane (g, i) of tile tt holds
+                // o[16tt + i][16vw + 4g + jj], four consecutive channels of one token)
                 const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) accO[tt] = f4{0.f, 0.f, 0.f, 0.f};
@@ -992,12 +1005,13 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                         accO[tt] = mfma(bG, cat(rd4(row), rd4(row + 32)), accO[tt]);
                     }
                 }
-                load_bz<D>(bZ, vw, sm.zkT);
             }
             lds_barrier();
-            // ---- D: o^T += Z_v^T P~^T; store Delta o; Gamma update
-            vm_wait_all();  // token loads of A, before any store joins the counter
-            if (own) {
+            // ---- phase 2: y' (c+1); o^T += Z_v^T P~^T, Delta o, Gamma update (c-1); Z_v fragments (c)
+            vm_wait_all();  // token loads of phase 1, before any store joins the counter
+            if (c + 1 < nch) fm_write_q<D>(yo, sm.yq);
+            if (c >= 1 && own) {
+                const int64_t tp = t0 - L;  // first token of chunk c-1
                 const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
                 const uint32_t c_pp = opaque(lds_addr(sm.pp) + 2 * (i * RP + 8 * g));
 #pragma unroll
@@ -1008,7 +1022,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                 const uint32_t olane = static_cast<uint32_t>(i * rsb + 2 * (16 * vw + 4 * g));
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
-                    const uint32_t toff = static_cast<uint32_t>((t0 + 16 * tt) * rsb);
+                    const uint32_t toff = static_cast<uint32_t>((tp + 16 * tt) * rsb);
                     const u2 pk = {static_cast<uint32_t>(to_bf16(accO[tt][0] * dt)) |
                                        (static_cast<uint32_t>(to_bf16(accO[tt][1] * dt)) << 16),
                                    static_cast<uint32_t>(to_bf16(accO[tt][2] * dt)) |
@@ -1017,6 +1031,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                 }
                 value_update<D>(G, sm.aL, bZ, sm.zkT);
             }
+            if (c < nch && own) load_bz<D>(bZ, vw, sm.zkT);
             lds_barrier();
         }
         if (own && seg == S - 1 && state_out != nullptr)
