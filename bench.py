@@ -37,9 +37,10 @@ METRIC = "mixer tokens/sec fwd (1.3B shape, N=4096) + % of HBM roofline, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 FP32_PEAK_TFLOPS = 157.3
 FP16_MFMA_PEAK_TFLOPS = 2500.0
-KERNEL_SOURCES = ["fixed_state_ssm_amd/csrc/chunked.hip", "fixed_state_ssm_amd/csrc/featmap.hip",
-                  "fixed_state_ssm_amd/csrc/scan_seq.hip", "fixed_state_ssm_amd/csrc/common.h",
-                  "fixed_state_ssm_amd/csrc/api.cpp"]
+KERNEL_SOURCES = ["fixed_state_ssm_amd/csrc/chunked.hip", "fixed_state_ssm_amd/csrc/chunked_ws.hip",
+                  "fixed_state_ssm_amd/csrc/featmap.hip", "fixed_state_ssm_amd/csrc/scan_seq.hip",
+                  "fixed_state_ssm_amd/csrc/decode.hip", "fixed_state_ssm_amd/csrc/common.h",
+                  "fixed_state_ssm_amd/csrc/launch.h", "fixed_state_ssm_amd/csrc/api.cpp"]
 
 
 def source_sha() -> str:
