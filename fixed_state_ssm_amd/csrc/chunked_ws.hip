@@ -288,8 +288,8 @@ struct SmemFwd {
 
 template <int D>
 struct SmemSeg {
-    _Float16 zkT[D * L];
-    _Float16 zvT[D * L];
+    _Float16 zkT[2][D * L];  // by chunk parity
+    _Float16 zvT[2][D * L];
     _Float16 ft[M2 * L];
     _Float16 ftl[M2 * L];
     float2 aL[MM];
@@ -335,8 +335,7 @@ __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w 
 // of the 3 before (slots 0..2); rsb = 2 H D is the byte stride of a token.
 template <int D, bool HALO>
 __device__ __forceinline__ void fm_load(uint32_t (&r)[HALO ? 11 : 8], __amdgpu_buffer_rsrc_t rs, int rsb,
-                                        int64_t tok0) {
-    const int fi = feat_index<D>();
+                                        int64_t tok0, int fi = feat_index<D>()) {
     if (fi >= Cfg<D>::NF) return;
     const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
     const uint32_t lane_b = static_cast<uint32_t>(8 * tb * rsb + 4 * cgi);
@@ -347,8 +346,8 @@ __device__ __forceinline__ void fm_load(uint32_t (&r)[HALO ? 11 : 8], __amdgpu_b
 }
 // The stored tail replaces the three positions before the sequence start.
 template <int D, class SM>
-__device__ __forceinline__ void halo_fix(uint32_t (&r)[11], const SM& sm, int sel, int64_t tok0) {
-    const int fi = feat_index<D>();
+__device__ __forceinline__ void halo_fix(uint32_t (&r)[11], const SM& sm, int sel, int64_t tok0,
+                                         int fi = feat_index<D>()) {
     if (tok0 == 0 && fi < Cfg<D>::CP) {
 #pragma unroll
         for (int j = 0; j < 3; ++j) r[j] = *reinterpret_cast<const uint32_t*>(&sm.halo[sel][j][2 * fi]);
@@ -419,8 +418,8 @@ __device__ __forceinline__ void share_factor(SM& sm, float f, float (&out)[8]) {
 
 // z_k of the thread's 8 tokens to z_k^T (zero past n valid tokens).
 template <int D, class SM>
-__device__ __forceinline__ void fm_keys(const uint32_t (&r)[11], const SM& sm, int n, float eps_feat, float eps_norm) {
-    const int fi = feat_index<D>();
+__device__ __forceinline__ void fm_keys(const uint32_t (&r)[11], const SM& sm, const void* zT, int n, float eps_feat,
+                                        float eps_norm, int fi = feat_index<D>()) {
     if (fi >= Cfg<D>::NF) return;
     const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
     float y[2][8], ss[8], rho[8];
@@ -439,13 +438,13 @@ __device__ __forceinline__ void fm_keys(const uint32_t (&r)[11], const SM& sm, i
         y[1][s] = fmaf(g1 * rho[s], y[1][s], b1);
     }
     if (n < L) mask_tokens(y, tb, n);
-    write_zt(sm.zkT, cgi, tb, y);
+    write_zt(zT, cgi, tb, y);
 }
 
 // z_v of the thread's 8 tokens to z_v^T (zero past n valid tokens).
 template <int D, class SM>
-__device__ __forceinline__ void fm_values(const uint32_t (&r)[8], const SM& sm, int n, float eps_norm) {
-    const int fi = feat_index<D>();
+__device__ __forceinline__ void fm_values(const uint32_t (&r)[8], const SM& sm, const void* zT, int n, float eps_norm,
+                                          int fi = feat_index<D>()) {
     if (fi >= Cfg<D>::NF) return;
     const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
     float x[2][8], ss[8];
@@ -466,15 +465,14 @@ __device__ __forceinline__ void fm_values(const uint32_t (&r)[8], const SM& sm, 
         x[1][s] = fmaf(g1 * rs[s], x[1][s], b1);
     }
     if (n < L) mask_tokens(x, tb, n);
-    write_zt(sm.zvT, cgi, tb, x);
+    write_zt(zT, cgi, tb, x);
 }
 
 // y' of the thread's 8 tokens (kept in registers as fp16 pairs until written
 // by fm_write_q) and sigma~ to sig.
 template <int D, class SM>
 __device__ __forceinline__ void fm_queries(half2v (&yo)[8], const uint32_t (&r)[11], SM& sm, float* sig,
-                                           float eps_feat, float inv_dt) {
-    const int fi = feat_index<D>();
+                                           float eps_feat, float inv_dt, int fi = feat_index<D>()) {
     if (fi >= Cfg<D>::NF) return;
     const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
     float y[2][8], ss[8];
@@ -485,8 +483,7 @@ __device__ __forceinline__ void fm_queries(half2v (&yo)[8], const uint32_t (&r)[
     if (cgi < 8) sig[8 * tb + scatter_token(cgi)] = -kLn2 * inv_dt * __builtin_amdgcn_rcpf(fmaf(kLn2Sq, tot, eps_feat));
 }
 template <int D>
-__device__ __forceinline__ void fm_write_q(const half2v (&yo)[8], const void* yq) {
-    const int fi = feat_index<D>();
+__device__ __forceinline__ void fm_write_q(const half2v (&yo)[8], const void* yq, int fi = feat_index<D>()) {
     if (fi >= Cfg<D>::NF) return;
     const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
     const uint32_t yst = opaque(lds_addr(yq) + 2 * (8 * tb * Cfg<D>::RY + 2 * cgi));
@@ -496,20 +493,20 @@ __device__ __forceinline__ void fm_write_q(const half2v (&yo)[8], const void* yq
 
 // Conv weights (times -log2 e, taps right-aligned into 4 slots), gain, bias,
 // and the stored tail of the sequence (positions -3..-1; zeros when absent).
-template <int D, bool WITH_Q, class SM>
+template <int D, bool WITH_Q, int NT = NTH, class SM>
 __device__ __forceinline__ void load_prologue(SM& sm, const idattn_params& prm, const uint16_t* tail_in, int64_t b,
                                               int64_t h, int64_t H, int W) {
-    for (int e = threadIdx.x; e < 2 * D; e += NTH) {
+    for (int e = threadIdx.x; e < 2 * D; e += NT) {
         sm.gain[e] = prm.gain[h * 2 * D + e];
         sm.bias[e] = prm.bias[h * 2 * D + e];
     }
-    for (int e = threadIdx.x; e < D * kMaxW; e += NTH) {
+    for (int e = threadIdx.x; e < D * kMaxW; e += NT) {
         const int c = e / kMaxW, j = e % kMaxW;
         const int tap = j - (kMaxW - W);
         if constexpr (WITH_Q) sm.wq[wt_index<D>(c, j)] = tap >= 0 ? -kLog2e * prm.conv_q[(h * D + c) * W + tap] : 0.f;
         sm.wk[wt_index<D>(c, j)] = tap >= 0 ? -kLog2e * prm.conv_k[(h * D + c) * W + tap] : 0.f;
     }
-    for (int e = threadIdx.x; e < 2 * 3 * D; e += NTH) {
+    for (int e = threadIdx.x; e < 2 * 3 * D; e += NT) {
         const int sel = e / (3 * D), row = (e / D) % 3, c = e % D;
         const int pos = row - 3;
         uint16_t val = 0;
@@ -521,8 +518,9 @@ __device__ __forceinline__ void load_prologue(SM& sm, const idattn_params& prm, 
     }
 }
 
+template <int NT = NTH>
 __device__ __forceinline__ void copy16(void* dst, const void* src, int bytes) {
-    for (int e = threadIdx.x; e < bytes / 16; e += NTH)
+    for (int e = threadIdx.x; e < bytes / 16; e += NT)
         reinterpret_cast<u4*>(dst)[e] = reinterpret_cast<const u4*>(src)[e];
 }
 
@@ -587,11 +585,13 @@ __device__ __forceinline__ uint32_t win_b(const void* zkT, int kb) {
     return opaque(lds_addr(zkT) + 2 * o128(i, 32 * kb + 8 * g));
 }
 
-// U <- abar^L U + Z_k^T F  (the real and imaginary rows of a mode sit in lanes i, i ^ 1)
+// U <- abar^L U + Z_k^T F  (the real and imaginary rows of a mode sit in lanes i, i ^ 1);
+// the low parts of F^T follow the high parts at M2 L halfs.
 template <int D>
-__device__ __forceinline__ void key_update(f4 (&U)[Cfg<D>::RT], const float2* aL, int kw, const void* zkT) {
+__device__ __forceinline__ void key_update(f4 (&U)[Cfg<D>::RT], const float2* aL, int kw, const void* zkT,
+                                           const void* ft) {
     constexpr int RT = Cfg<D>::RT;
-    constexpr uint32_t dl = WinOff<D>::ftl - WinOff<D>::ft;
+    constexpr uint32_t dl = M2 * L * 2;
     const int i = tid_now() & 15;
     const float2 a = aL[(16 * kw + i) >> 1];
     const float aLs = (i & 1) ? a.y : -a.y;
@@ -606,7 +606,7 @@ __device__ __forceinline__ void key_update(f4 (&U)[Cfg<D>::RT], const float2* aL
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         const uint32_t wb = win_b(zkT, kb);
-        const uint32_t fo = wb + WinOff<D>::ft + 2 * 64 * 16 * kw;  // F^T rows 16kw + i
+        const uint32_t fo = win_b(ft, kb) + 2 * 64 * 16 * kw;  // F^T rows 16kw + i
         const half8 bF = rd8(fo), bFl = rd8(fo + dl);                // F[j][m'], j = 32kb + 8g + jj
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -619,7 +619,7 @@ __device__ __forceinline__ void key_update(f4 (&U)[Cfg<D>::RT], const float2* aL
 
 // Gamma <- abar^L Gamma + F^T Z_v, with bZ[kb] = Z_v[32kb + 8g + jj][16vw + i]
 template <int D>
-__device__ __forceinline__ void value_update(f4 (&G)[8], const float2* aL, const half8 (&bZ)[2], const void* zkT) {
+__device__ __forceinline__ void value_update(f4 (&G)[8], const float2* aL, const half8 (&bZ)[2], const void* ft) {
     const int g = (tid_now() & 63) >> 4;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
@@ -632,19 +632,18 @@ __device__ __forceinline__ void value_update(f4 (&G)[8], const float2* aL, const
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t wb = win_b(zkT, kb);
+        const uint32_t wb = win_b(ft, kb);
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-            G[mt] = mfma(rd8(wb + WinOff<D>::ft + 2048 * mt), bZ[kb], G[mt]);
-            G[mt] = mfma(rd8(wb + WinOff<D>::ftl + 2048 * mt), bZ[kb], G[mt]);
+            G[mt] = mfma(rd8(wb + 2048 * mt), bZ[kb], G[mt]);
+            G[mt] = mfma(rd8(wb + M2 * L * 2 + 2048 * mt), bZ[kb], G[mt]);
         }
     }
 }
 
-template <int D>
-__device__ __forceinline__ void load_bz(half8 (&bZ)[2], int vw, const void* zkT) {
+__device__ __forceinline__ void load_bz(half8 (&bZ)[2], int vw, const void* zvT) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) bZ[kb] = rd8(win_b(zkT, kb) + WinOff<D>::zv + 2048 * vw);
+    for (int kb = 0; kb < 2; ++kb) bZ[kb] = rd8(win_b(zvT, kb) + 2048 * vw);
 }
 
 // Causal 16 x 16 tiles (tt, kt), kt <= tt, of the G and P~ products: key wave
@@ -654,7 +653,10 @@ __device__ __forceinline__ int tile_kt(int q) { return q - (tile_tt(q) * (tile_t
 
 // ------------------------------------------------------------------ kernels
 // Segment end states from a zero start: grid B*H*(S-1), block (bh, seg).
-// Per chunk:  A (key: U update | value: Gamma update)  B (key: keys of c+1 | value: values of c+1).
+// z_k and z_v are double-buffered by chunk parity, so a chunk needs one
+// barrier: at step c the key waves update U with the keys of chunk c and build
+// those of c+1 into the other buffer, the value waves do the same for Gamma
+// and the values.
 template <int D>
 __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_params prm,
                                                             const uint16_t* __restrict__ k,
@@ -686,15 +688,14 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
         uint32_t rkk[11];
         fm_load<D, true>(rkk, rk, rsb, t_begin);
         halo_fix<D>(rkk, sm, 1, t_begin);
-        fm_keys<D>(rkk, sm, L, p.eps_feat, p.eps_norm);
+        fm_keys<D>(rkk, sm, sm.zkT[0], L, p.eps_feat, p.eps_norm);
         if (nch > 1) fm_load<D, true>(rkk, rk, rsb, t_begin + L);
         lds_barrier();  // chunk 0 features
         for (int c = 0; c < nch; ++c) {
             const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
-            key_update<D>(U, sm.aL, kw, sm.zkT);
-            lds_barrier();
+            key_update<D>(U, sm.aL, kw, sm.zkT[c & 1], sm.ft);
             if (c + 1 < nch) {
-                fm_keys<D>(rkk, sm, L, p.eps_feat, p.eps_norm);
+                fm_keys<D>(rkk, sm, sm.zkT[(c + 1) & 1], L, p.eps_feat, p.eps_norm);
                 if (c + 2 < nch) {
                     step_fence();
                     fm_load<D, true>(rkk, rk, rsb, t0 + 2 * L);
@@ -710,19 +711,18 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
         const __amdgpu_buffer_rsrc_t rv = seq_rsrc<D>(v, b, h, p.N, p.H, t_end);
         uint32_t rvv[8];
         fm_load<D, false>(rvv, rv, rsb, t_begin);
-        fm_values<D>(rvv, sm, L, p.eps_norm);
+        fm_values<D>(rvv, sm, sm.zvT[0], L, p.eps_norm);
         if (nch > 1) fm_load<D, false>(rvv, rv, rsb, t_begin + L);
         lds_barrier();  // chunk 0 features
         for (int c = 0; c < nch; ++c) {
             const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
             if (vw < D / 16) {
                 half8 bZ[2];
-                load_bz<D>(bZ, vw, sm.zkT);
-                value_update<D>(G, sm.aL, bZ, sm.zkT);
+                load_bz(bZ, vw, sm.zvT[c & 1]);
+                value_update<D>(G, sm.aL, bZ, sm.ft);
             }
-            lds_barrier();
             if (c + 1 < nch) {
-                fm_values<D>(rvv, sm, L, p.eps_norm);
+                fm_values<D>(rvv, sm, sm.zvT[(c + 1) & 1], L, p.eps_norm);
                 if (c + 2 < nch) {
                     step_fence();
                     fm_load<D, false>(rvv, rv, rsb, t0 + 2 * L);
@@ -815,7 +815,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         uint32_t rkk[11];
         fm_load<D, true>(rkk, rk, rsb, t_begin);
         halo_fix<D>(rkk, sm, 1, t_begin);
-        fm_keys<D>(rkk, sm, nch > 1 ? L : n_last, p.eps_feat, p.eps_norm);
+        fm_keys<D>(rkk, sm, sm.zkT, nch > 1 ? L : n_last, p.eps_feat, p.eps_norm);
         if (nch > 1) fm_load<D, true>(rkk, rk, rsb, t_begin + L);
         lds_barrier();  // chunk 0 features
         for (int c = 0; c <= nch; ++c) {
@@ -857,7 +857,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                         }
                     }
                 }
-                key_update<D>(U, sm.aL, kw, sm.zkT);
+                key_update<D>(U, sm.aL, kw, sm.zkT, sm.ft);
             }
             if (c >= 1) {
                 const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
@@ -937,7 +937,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                 }
             }
             if (c + 1 < nch) {
-                fm_keys<D>(rkk, sm, c + 2 < nch ? L : n_last, p.eps_feat, p.eps_norm);
+                fm_keys<D>(rkk, sm, sm.zkT, c + 2 < nch ? L : n_last, p.eps_feat, p.eps_norm);
                 if (c + 2 < nch) {
                     step_fence();
                     fm_load<D, true>(rkk, rk, rsb, t0 + 2 * L);
@@ -976,7 +976,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             f4 accO[4];
             // ---- phase 1: values (c); queries (c+1), held until phase 2; token loads; X Gamma (c-1)
             if (c < nch) {
-                fm_values<D>(rvv, sm, c + 1 < nch ? L : n_last, p.eps_norm);
+                fm_values<D>(rvv, sm, sm.zvT, c + 1 < nch ? L : n_last, p.eps_norm);
                 if (c + 1 < nch) {
                     step_fence();
                     fm_load<D, false>(rvv, rv, rsb, t0 + L);
@@ -1029,9 +1029,9 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                                        (static_cast<uint32_t>(to_bf16(accO[tt][3] * dt)) << 16)};
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, pk), ob, olane + toff, 0, 0);
                 }
-                value_update<D>(G, sm.aL, bZ, sm.zkT);
+                value_update<D>(G, sm.aL, bZ, sm.ft);
             }
-            if (c < nch && own) load_bz<D>(bZ, vw, sm.zkT);
+            if (c < nch && own) load_bz(bZ, vw, sm.zvT);
             lds_barrier();
         }
         if (own && seg == S - 1 && state_out != nullptr)
