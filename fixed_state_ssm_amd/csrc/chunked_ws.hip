@@ -56,7 +56,6 @@ constexpr int MM = 64;       // complex modes
 constexpr int M2 = 2 * MM;   // m' rows
 constexpr int NTH = 1024;    // sixteen waves
 constexpr int kMaxW = 4;     // conv widths 1..4
-constexpr int RS = M2 + 8;   // padded row length (halfs) of [t][m'] tiles
 constexpr int RP = L + 16;   // padded row length of [t][64] tiles
 constexpr int PWS = MM + 4;  // padded row length (float2) of the abar^{k+1} rows
 constexpr float kLn2 = 0.6931471805599453f;
@@ -69,7 +68,7 @@ struct Cfg {
     static constexpr int KB = D / 32;   // 32-wide K steps over R
     static constexpr int CP = D / 2;    // channel pairs = lanes that share a feature token block
     static constexpr int NF = 8 * CP;   // feature threads per role (8 token blocks)
-    static constexpr int RY = D + 8;    // padded row length of the y' tile
+    static constexpr int YR = D;        // row length (halfs) of the y' tile
 };
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -91,6 +90,18 @@ __device__ __forceinline__ f4 mfma(const half8& a, const half8& b, const f4& c) 
 // halves use padded rows instead.
 __host__ __device__ constexpr int sw128(int r) { return 2 * (((r >> 1) & 3) ^ (2 * ((r >> 3) & 1))) + ((r >> 3) & 1); }
 __host__ __device__ constexpr int o128(int r, int col) { return r * 64 + ((((col >> 3) ^ sw128(r)) & 7) << 3) + (col & 7); }
+// [rows][128] fp16 tiles: 256-byte rows with the 16-byte chunk index XOR-ed by row % 16.
+__host__ __device__ constexpr int x256(int r, int col) { return r * 128 + ((((col >> 3) ^ r) & 15) << 3) + (col & 7); }
+// The K-ordered [t][*] tiles (y', X) store their columns in the order in which
+// a lane supplies them as an MFMA operand: within each block of 32, column
+// 4g + e (e < 4) goes to 8g + e and column 16 + 4g + e to 8g + 4 + e, so that
+// lane group g reads its eight K values with one 16-byte access.
+__host__ __device__ constexpr int perm32(int c) {
+    return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
+}
+// y' [t][r]: 256-byte rows (D = 128) or swizzled 128-byte rows (D = 64), columns in perm32 order.
+template <int D>
+__host__ __device__ constexpr int yq_off(int t, int c) { return D == 128 ? x256(t, perm32(c)) : o128(t, perm32(c)); }
 
 __device__ __forceinline__ half8 cat(const half4& a, const half4& b) {
     half8 r;
@@ -266,9 +277,9 @@ __global__ __launch_bounds__(256) void zoh_tables_kernel(Problem p, idattn_param
 template <int D>
 struct SmemFwd {
     // window A: [t][*] tiles
-    _Float16 yq[L * Cfg<D>::RY];  // y' of the queries [t][r]
-    _Float16 sc[L * RS];          // [t][m'] (Re s~, -Im s~)
-    _Float16 xc[L * RS];          // [t][m'] (Re X, -Im X)
+    _Float16 yq[L * D];           // y' of the queries [t][r] (yq_off)
+    _Float16 sc[L * M2];          // [t][m'] (Re s~, -Im s~) (x256)
+    _Float16 xc[L * M2];          // [t][m'] (Re X, -Im X) (x256 of perm32)
     // window B: swizzled [rows][64] tiles
     _Float16 zkT[D * L];          // z_k^T [r][j]
     _Float16 zvT[D * L];          // z_v^T [c][l]
@@ -486,9 +497,8 @@ template <int D>
 __device__ __forceinline__ void fm_write_q(const half2v (&yo)[8], const void* yq, int fi = feat_index<D>()) {
     if (fi >= Cfg<D>::NF) return;
     const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
-    const uint32_t yst = opaque(lds_addr(yq) + 2 * (8 * tb * Cfg<D>::RY + 2 * cgi));
 #pragma unroll
-    for (int s = 0; s < 8; ++s) *(lds_h2*)(uintptr_t)(yst + 2 * s * Cfg<D>::RY) = yo[s];
+    for (int s = 0; s < 8; ++s) *(lds_h2*)(uintptr_t)(lds_addr(yq) + 2 * yq_off<D>(8 * tb + s, 2 * cgi)) = yo[s];
 }
 
 // Conv weights (times -log2 e, taps right-aligned into 4 slots), gain, bias,
@@ -776,7 +786,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                                                               const uint16_t* __restrict__ tail_in, float* state_out,
                                                               const uint8_t* __restrict__ tab,
                                                               const float* __restrict__ carry, int64_t Lseg, int S) {
-    constexpr int RT = Cfg<D>::RT, KB = Cfg<D>::KB, RY = Cfg<D>::RY;
+    constexpr int RT = Cfg<D>::RT, KB = Cfg<D>::KB, YR = Cfg<D>::YR;
     constexpr uint32_t dl = WinOff<D>::ftl - WinOff<D>::ft;
     __shared__ SmemFwd<D> sm;
     const int tid = threadIdx.x;
@@ -830,13 +840,16 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                     const int qt = kw + 8 * slot;
                     if (qt < 10) {
                         const int tt = tile_tt(qt), jt = tile_kt(qt);
-                        const uint32_t ar = opaque(lds_addr(sm.yq) + 2 * ((16 * tt + i) * RY + 8 * g));
-                        const uint32_t br0 = opaque(lds_addr(sm.zkT) + 2 * o128(8 * g + (i >> 2), 16 * jt + 4 * (i & 3)));
-                        const uint32_t br1 = opaque(lds_addr(sm.zkT) + 2 * o128(8 * g + (i >> 2) + 4, 16 * jt + 4 * (i & 3)));
+                        // K in perm32 order on both sides: y' fragments as stored, z_k^T rows
+                        // 32kb + 4g + e and 32kb + 16 + 4g + e through the transposing reads
+                        const uint32_t br0 = opaque(lds_addr(sm.zkT) + 2 * o128(4 * g + (i >> 2), 16 * jt + 4 * (i & 3)));
+                        const uint32_t br1 = opaque(lds_addr(sm.zkT) + 2 * o128(16 + 4 * g + (i >> 2), 16 * jt + 4 * (i & 3)));
                         f4 accG = {};
 #pragma unroll
-                        for (int kb = 0; kb < KB; ++kb)
-                            accG = mfma(rd8(ar + 64 * kb), cat(rd4t(br0 + 4096 * kb), rd4t(br1 + 4096 * kb)), accG);
+                        for (int kb = 0; kb < KB; ++kb) {
+                            const uint32_t ar = opaque(lds_addr(sm.yq) + 2 * yq_off<D>(16 * tt + i, 32 * kb + 4 * g));
+                            accG = mfma(rd8(ar), cat(rd4t(br0 + 4096 * kb), rd4t(br1 + 4096 * kb)), accG);
+                        }
                         const uint32_t gs = opaque(lds_addr(sm.gp) + 2 * ((16 * tt + 4 * g) * (RP - 1) + L - 1 + 16 * jt + i));
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj)
@@ -845,17 +858,12 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                 }
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) accQ[tt] = f4{0.f, 0.f, 0.f, 0.f};
-                {
-                    const uint32_t a_perm = opaque(lds_addr(sm.yq) + 2 * (i * RY + 4 * g));
 #pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) {
-                        const half8 aU = to_half8(U[2 * kb], U[2 * kb + 1]);
+                for (int kb = 0; kb < KB; ++kb) {
+                    const half8 aU = to_half8(U[2 * kb], U[2 * kb + 1]);
+                    const uint32_t yb = opaque(lds_addr(sm.yq) + 2 * yq_off<D>(i, 32 * kb + 4 * g));
 #pragma unroll
-                        for (int tt = 0; tt < 4; ++tt) {
-                            const uint32_t row = a_perm + 2 * (16 * tt * RY + 32 * kb);
-                            accQ[tt] = mfma(aU, cat(rd4(row), rd4(row + 32)), accQ[tt]);
-                        }
-                    }
+                    for (int tt = 0; tt < 4; ++tt) accQ[tt] = mfma(aU, rd8(yb + 2 * 16 * tt * YR), accQ[tt]);
                 }
                 key_update<D>(U, sm.aL, kw, sm.zkT, sm.ft);
             }
@@ -868,13 +876,12 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                     const int qt = kw + 8 * slot;
                     if (qt < 10) {
                         const int tt = tile_tt(qt), kt = tile_kt(qt);
-                        const uint32_t ar = opaque(lds_addr(sm.sc) + 2 * ((16 * tt + i) * RS + 8 * g));
                         const uint32_t br0 = opaque(lds_addr(sm.ft) + 2 * o128(8 * g + (i >> 2), L - 16 - 16 * kt + 4 * (i & 3)));
                         const uint32_t br1 = opaque(lds_addr(sm.ft) + 2 * o128(8 * g + (i >> 2) + 4, L - 16 - 16 * kt + 4 * (i & 3)));
                         f4 accP = {};
 #pragma unroll
                         for (int kb = 0; kb < 4; ++kb) {
-                            const half8 a = rd8(ar + 64 * kb);
+                            const half8 a = rd8(opaque(lds_addr(sm.sc) + 2 * x256(16 * tt + i, 32 * kb + 8 * g)));
                             accP = mfma(a, cat(rd4t(br0 + 4096 * kb), rd4t(br1 + 4096 * kb)), accP);
                             accP = mfma(a, cat(rd4t(br0 + 4096 * kb + dl), rd4t(br1 + 4096 * kb + dl)), accP);
                         }
@@ -913,7 +920,11 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                     const float4 e16 = *reinterpret_cast<const float4*>(&sm.pw[15][8 * kw + 2 * g]);
                     float er[2] = {e0.x, e0.z}, ei[2] = {e0.y, e0.w};
                     const float e16r[2] = {e16.x, e16.z}, e16i[2] = {e16.y, e16.w};
-                    const uint32_t a_st = opaque(lds_addr(sm.sc) + 2 * (i * RS + 16 * kw + 4 * g));
+                    // X: 8-byte stores at the perm32 position of m' = 16kw + 4g; s~: lanes of
+                    // groups g and g ^ 1 exchange their halves so that group g (even) stores
+                    // tiles 0 and 2 and group g + 1 tiles 1 and 3, eight m' per 16-byte store
+                    const uint32_t x_st = opaque(lds_addr(sm.xc) + 2 * x256(i, perm32(16 * kw + 4 * g)));
+                    u2 spk[4];
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) {
                         const float sg = sig[16 * tt + i];
@@ -931,8 +942,21 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                             ei[qq] = er[qq] * e16i[qq] + ei[qq] * e16r[qq];
                             er[qq] = nr;
                         }
-                        wr4(a_st + 2 * 16 * tt * RS, sv[0], sv[1], sv[2], sv[3]);
-                        wr4(a_st + 2 * 16 * tt * RS + L * RS * 2, xv[0], xv[1], xv[2], xv[3]);
+                        wr4(x_st + 2 * 16 * tt * M2, xv[0], xv[1], xv[2], xv[3]);
+                        spk[tt] = u2{__builtin_bit_cast(uint32_t, half2v{static_cast<_Float16>(sv[0]), static_cast<_Float16>(sv[1])}),
+                                     __builtin_bit_cast(uint32_t, half2v{static_cast<_Float16>(sv[2]), static_cast<_Float16>(sv[3])})};
+                    }
+                    const bool godd = g & 1;
+                    const uint32_t s_st = opaque(lds_addr(sm.sc) + 2 * x256(16 * godd + i, 16 * kw + 8 * (g >> 1)));
+#pragma unroll
+                    for (int pq = 0; pq < 2; ++pq) {
+                        const u2 own = godd ? spk[2 * pq + 1] : spk[2 * pq];
+                        const u2 send = godd ? spk[2 * pq] : spk[2 * pq + 1];
+                        const auto r0 = __builtin_amdgcn_permlane16_swap(send[0], send[0], false, false);
+                        const auto r1 = __builtin_amdgcn_permlane16_swap(send[1], send[1], false, false);
+                        const u2 recv = {godd ? r0[0] : r0[1], godd ? r1[0] : r1[1]};
+                        const u4 v8 = godd ? u4{recv[0], recv[1], own[0], own[1]} : u4{own[0], own[1], recv[0], recv[1]};
+                        *(__attribute__((address_space(3))) u4*)(uintptr_t)(s_st + 2 * 32 * pq * M2) = v8;
                     }
                 }
             }
@@ -995,15 +1019,12 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                 const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) accO[tt] = f4{0.f, 0.f, 0.f, 0.f};
-                const uint32_t a_px = opaque(lds_addr(sm.xc) + 2 * (i * RS + 4 * g));
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
                     const half8 bG = to_half8(G[2 * kb], G[2 * kb + 1]);
+                    const uint32_t xb = opaque(lds_addr(sm.xc) + 2 * x256(i, 32 * kb + 8 * g));  // perm32 positions
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt) {
-                        const uint32_t row = a_px + 2 * (16 * tt * RS + 32 * kb);
-                        accO[tt] = mfma(bG, cat(rd4(row), rd4(row + 32)), accO[tt]);
-                    }
+                    for (int tt = 0; tt < 4; ++tt) accO[tt] = mfma(bG, rd8(xb + 2 * 16 * tt * M2), accO[tt]);
                 }
             }
             lds_barrier();
