@@ -25,14 +25,16 @@
 //    add up coherently; it is carried as a pair of fp16 values (about 22
 //    bits) and every product with T is two MFMAs.
 //
+// Two kernels run per segment of the sequence.  The feature pass builds z_k
+// and z_v of every chunk once (short conv, SiLU, norms), stores them as fp16
+// tiles for the forward, and runs the state updates from a zero start to get
+// each segment's end state; a carry chain turns those into the state entering
+// each segment; the forward then runs the full chunk loop of its segment.
 // A workgroup is sixteen waves, four per SIMD, two roles of eight waves:
 // key waves own the key state U and run the products that make s~ and X
-// (G, y_q . U, G'T, P~) and the U update; value waves own the value state
-// Gamma and run the readout (X Gamma, P~ Z_v) and the Gamma update.  The
-// features of chunk c+1 (short conv, SiLU, norms) are built while chunk c
-// runs: queries and keys by the value waves in the two phases where they have
-// no MFMA work, values by the key waves in the phase where they have none.
-// Every SIMD thus holds two MFMA-issuing and two VALU-heavy waves per phase.
+// (G, y_q . U, G'T) and the U update, and build the queries' features of the
+// next chunk; value waves own the value state Gamma and run the P~ tiles, the
+// readout (X Gamma, P~ Z_v) and the Gamma update.
 //
 // Index m' = 2 m + part (part 0 = real, 1 = imaginary) runs over the 2M = 128
 // real rows of a complex mode set.  Key wave kw (0..7) keeps U's rows r (all
@@ -479,26 +481,20 @@ __device__ __forceinline__ void fm_values(const uint32_t (&r)[8], const SM& sm, 
     write_zt(zT, cgi, tb, x);
 }
 
-// y' of the thread's 8 tokens (kept in registers as fp16 pairs until written
-// by fm_write_q) and sigma~ to sig.
+// y' of the thread's 8 tokens to the shared tile yq, and sigma~ to sig.
 template <int D, class SM>
-__device__ __forceinline__ void fm_queries(half2v (&yo)[8], const uint32_t (&r)[11], SM& sm, float* sig,
-                                           float eps_feat, float inv_dt, int fi = feat_index<D>()) {
+__device__ __forceinline__ void fm_queries(const uint32_t (&r)[11], SM& sm, const void* yq, float* sig, float eps_feat,
+                                           float inv_dt, int fi = feat_index<D>()) {
     if (fi >= Cfg<D>::NF) return;
     const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
     float y[2][8], ss[8];
     conv_silu<D>(r, sm.wq, cgi, y, ss);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) yo[s] = half2v{static_cast<_Float16>(y[0][s]), static_cast<_Float16>(y[1][s])};
+    for (int s = 0; s < 8; ++s)
+        *(lds_h2*)(uintptr_t)(lds_addr(yq) + 2 * yq_off<D>(8 * tb + s, 2 * cgi)) =
+            half2v{static_cast<_Float16>(y[0][s]), static_cast<_Float16>(y[1][s])};
     const float tot = reduce_scatter8<Cfg<D>::CP>(ss);
     if (cgi < 8) sig[8 * tb + scatter_token(cgi)] = -kLn2 * inv_dt * __builtin_amdgcn_rcpf(fmaf(kLn2Sq, tot, eps_feat));
-}
-template <int D>
-__device__ __forceinline__ void fm_write_q(const half2v (&yo)[8], const void* yq, int fi = feat_index<D>()) {
-    if (fi >= Cfg<D>::NF) return;
-    const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) *(lds_h2*)(uintptr_t)(lds_addr(yq) + 2 * yq_off<D>(8 * tb + s, 2 * cgi)) = yo[s];
 }
 
 // Conv weights (times -log2 e, taps right-aligned into 4 slots), gain, bias,
@@ -532,6 +528,35 @@ template <int NT = NTH>
 __device__ __forceinline__ void copy16(void* dst, const void* src, int bytes) {
     for (int e = threadIdx.x; e < bytes / 16; e += NT)
         reinterpret_cast<u4*>(dst)[e] = reinterpret_cast<const u4*>(src)[e];
+}
+
+// A [D][L] feature tile, global to registers to shared memory: thread x of a
+// role (512 threads) moves the 16-byte pieces x, x + 512, ...
+template <int D>
+constexpr int kTilePieces = D * L * 2 / 16 / 512;
+template <int D>
+__device__ __forceinline__ void tile_load(u4 (&r)[kTilePieces<D>], const _Float16* src) {
+    const int x = tid_now() & 511;
+#pragma unroll
+    for (int j = 0; j < kTilePieces<D>; ++j) r[j] = reinterpret_cast<const u4*>(src)[512 * j + x];
+}
+template <int D>
+__device__ __forceinline__ void tile_store(const void* dst, const u4 (&r)[kTilePieces<D>]) {
+    const int x = tid_now() & 511;
+#pragma unroll
+    for (int j = 0; j < kTilePieces<D>; ++j)
+        *(__attribute__((address_space(3))) u4*)(uintptr_t)(lds_addr(dst) + 16 * (512 * j + x)) = r[j];
+}
+// ... and shared memory to global, with the same piece mapping.
+template <int D>
+__device__ __forceinline__ void tile_copy_out(const void* src, _Float16* dst) {
+    const int x = tid_now() & 511;
+    u4 r[kTilePieces<D>];
+#pragma unroll
+    for (int j = 0; j < kTilePieces<D>; ++j)
+        r[j] = *(__attribute__((address_space(3))) u4*)(uintptr_t)(lds_addr(src) + 16 * (512 * j + x));
+#pragma unroll
+    for (int j = 0; j < kTilePieces<D>; ++j) reinterpret_cast<u4*>(dst)[512 * j + x] = r[j];
 }
 
 // ------------------------------------------------------------------ state
@@ -662,26 +687,33 @@ __device__ __forceinline__ int tile_tt(int q) { return q < 1 ? 0 : q < 3 ? 1 : q
 __device__ __forceinline__ int tile_kt(int q) { return q - (tile_tt(q) * (tile_tt(q) + 1)) / 2; }
 
 // ------------------------------------------------------------------ kernels
-// Segment end states from a zero start: grid B*H*(S-1), block (bh, seg).
-// z_k and z_v are double-buffered by chunk parity, so a chunk needs one
-// barrier: at step c the key waves update U with the keys of chunk c and build
-// those of c+1 into the other buffer, the value waves do the same for Gamma
-// and the values.
+// Features of every chunk and segment end states from a zero start: grid
+// B*H*S, block (bh, seg).  z_k^T and z_v^T of each chunk go to its tile in
+// global memory (zt, two [D][L] fp16 tiles per chunk in the shared-memory
+// layout, chunks numbered from the sequence start), from which the forward
+// copies them; blocks of segments 0..S-2 also run the state updates, the last
+// segment's blocks only build features.  z_k and z_v are double-buffered by
+// chunk parity, so a chunk needs one barrier: at step c the key waves update U
+// with the keys of chunk c and build those of c+1 into the other buffer, the
+// value waves do the same for Gamma and the values.
 template <int D>
 __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_params prm,
                                                             const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ v,
                                                             const uint16_t* __restrict__ tail_in,
                                                             const uint8_t* __restrict__ tab, float* __restrict__ ws,
-                                                            int64_t Lseg, int S) {
+                                                            _Float16* __restrict__ zt, int64_t Lseg, int S) {
     __shared__ SmemSeg<D> sm;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool key = w < 8;
-    const int64_t bh = blockIdx.x / (S - 1);
-    const int seg = static_cast<int>(blockIdx.x % (S - 1));
+    const int64_t bh = blockIdx.x / S;
+    const int seg = static_cast<int>(blockIdx.x % S);
+    const bool upd = seg + 1 < S;  // this segment's end state is needed
     const int64_t b = bh / p.H, h = bh % p.H;
-    const int64_t t_begin = seg * Lseg, t_end = t_begin + Lseg;  // segments 0..S-2 are full
-    const int nch = static_cast<int>(Lseg / L);
+    const int64_t t_begin = seg * Lseg;
+    const int64_t t_end = t_begin + Lseg < p.N ? t_begin + Lseg : p.N;
+    const int nch = static_cast<int>((t_end - t_begin + L - 1) / L);
+    const int n_last = static_cast<int>(t_end - t_begin - static_cast<int64_t>(nch - 1) * L);
     const uint8_t* th = tab + h * kTabBytes;
     load_prologue<D, false>(sm, prm, tail_in, b, h, p.H, static_cast<int>(p.W));
     copy16(sm.ft, th + kTabFT, M2 * L * 2);
@@ -690,6 +722,8 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
     __syncthreads();
     float* dst = ws + (static_cast<int64_t>(seg) * p.B * p.H + bh) * MM * 2 * D * 2;
     const int rsb = static_cast<int>(p.H * D * 2);  // token stride, bytes
+    // tile of chunk c of this segment: z_k^T, then z_v^T
+    _Float16* zseg = zt + ((bh * S + seg) * (Lseg / L)) * 2 * D * L;
     if (key) {
         const int kw = w;
         f4 U[Cfg<D>::RT];
@@ -698,14 +732,15 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
         uint32_t rkk[11];
         fm_load<D, true>(rkk, rk, rsb, t_begin);
         halo_fix<D>(rkk, sm, 1, t_begin);
-        fm_keys<D>(rkk, sm, sm.zkT[0], L, p.eps_feat, p.eps_norm);
+        fm_keys<D>(rkk, sm, sm.zkT[0], nch > 1 ? L : n_last, p.eps_feat, p.eps_norm);
         if (nch > 1) fm_load<D, true>(rkk, rk, rsb, t_begin + L);
         lds_barrier();  // chunk 0 features
         for (int c = 0; c < nch; ++c) {
             const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
-            key_update<D>(U, sm.aL, kw, sm.zkT[c & 1], sm.ft);
+            tile_copy_out<D>(sm.zkT[c & 1], zseg + c * 2 * D * L);
+            if (upd) key_update<D>(U, sm.aL, kw, sm.zkT[c & 1], sm.ft);
             if (c + 1 < nch) {
-                fm_keys<D>(rkk, sm, sm.zkT[(c + 1) & 1], L, p.eps_feat, p.eps_norm);
+                fm_keys<D>(rkk, sm, sm.zkT[(c + 1) & 1], c + 2 < nch ? L : n_last, p.eps_feat, p.eps_norm);
                 if (c + 2 < nch) {
                     step_fence();
                     fm_load<D, true>(rkk, rk, rsb, t0 + 2 * L);
@@ -713,26 +748,28 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
             }
             lds_barrier();
         }
-        u_store<D>(U, dst, nullptr, kw);
+        if (upd) u_store<D>(U, dst, nullptr, kw);
     } else {
         const int vw = w - 8;
+        const bool own = upd && vw < D / 16;
         f4 G[8];
-        if (vw < D / 16) g_load<D>(G, nullptr, vw);
+        if (own) g_load<D>(G, nullptr, vw);
         const __amdgpu_buffer_rsrc_t rv = seq_rsrc<D>(v, b, h, p.N, p.H, t_end);
         uint32_t rvv[8];
         fm_load<D, false>(rvv, rv, rsb, t_begin);
-        fm_values<D>(rvv, sm, sm.zvT[0], L, p.eps_norm);
+        fm_values<D>(rvv, sm, sm.zvT[0], nch > 1 ? L : n_last, p.eps_norm);
         if (nch > 1) fm_load<D, false>(rvv, rv, rsb, t_begin + L);
         lds_barrier();  // chunk 0 features
         for (int c = 0; c < nch; ++c) {
             const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
-            if (vw < D / 16) {
+            tile_copy_out<D>(sm.zvT[c & 1], zseg + c * 2 * D * L + D * L);
+            if (own) {
                 half8 bZ[2];
                 load_bz(bZ, vw, sm.zvT[c & 1]);
                 value_update<D>(G, sm.aL, bZ, sm.ft);
             }
             if (c + 1 < nch) {
-                fm_values<D>(rvv, sm, sm.zvT[(c + 1) & 1], L, p.eps_norm);
+                fm_values<D>(rvv, sm, sm.zvT[(c + 1) & 1], c + 2 < nch ? L : n_last, p.eps_norm);
                 if (c + 2 < nch) {
                     step_fence();
                     fm_load<D, false>(rvv, rv, rsb, t0 + 2 * L);
@@ -740,7 +777,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
             }
             lds_barrier();
         }
-        if (vw < D / 16) g_store<D>(G, dst, nullptr, vw);
+        if (own) g_store<D>(G, dst, nullptr, vw);
     }
 }
 
@@ -765,23 +802,23 @@ __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, const flo
     }
 }
 
-// Full chunk loop of one segment: grid B*H*S, block (bh, seg).  The readout of
-// a chunk runs one step behind its s~ and X, so that a step c = 0..nch needs
-// two barriers:
-//   1  key: G tiles, Q^T = U Y^T, U update (chunk c); P~ tiles (c-1)
-//      value: values (c); queries (c+1, held); X Gamma (c-1); token loads
-//   2  key: S^T = T^T G'^T, s~, X (c); keys (c+1)
-//      value: write y' (c+1); P~ Z_v, output, Gamma update (c-1); Z_v fragments (c)
+// Full chunk loop of one segment: grid B*H*S, block (bh, seg).  z_k^T and
+// z_v^T of every chunk come ready from the feature pass; the queries' features
+// are built here.  The readout of a chunk runs one step behind its s~ and X,
+// so that a step c = 0..nch needs two barriers:
+//   1  key: G tiles, Q^T = U Y^T, U update (chunk c)
+//      value: z_v^T (c) to shared memory; P~ tiles, X Gamma (c-1)
+//   2  key: S^T = T^T G'^T, s~, X (c); z_k^T (c+1) to shared memory; queries (c+1)
+//      value: P~ Z_v, output, Gamma update (c-1); Z_v fragments (c)
 // Every shared tile is written in one phase and read in the next: y', z_k (c)
-// in 1 of step c, rewritten in 2; G' (c) written in 1, read in 2; s~, X (c)
-// written in 2 of step c, read in 1 of step c+1; P~ (c-1) written in 1, read
-// in 2 of step c; z_v (c) written in 1 and read in 2 of step c into
+// read in 1 of step c, rewritten in 2; G' (c) written in 1, read in 2; s~, X
+// (c) written in 2 of step c, read in 1 of step c+1; P~ (c-1) written in 1,
+// read in 2 of step c; z_v (c) written in 1 and read in 2 of step c into
 // registers that the readout of step c+1 uses.
 template <int D>
 __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_params prm,
                                                               const uint16_t* __restrict__ q,
-                                                              const uint16_t* __restrict__ k,
-                                                              const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
+                                                              const _Float16* __restrict__ zt, uint16_t* __restrict__ o,
                                                               const float* state_in,
                                                               const uint16_t* __restrict__ tail_in, float* state_out,
                                                               const uint8_t* __restrict__ tab,
@@ -814,22 +851,29 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
     const int rsb = static_cast<int>(H * D * 2);  // token stride, bytes
     const float* src = seg == 0 ? (state_in ? state_in + bh * MM * 2 * D * 2 : nullptr)
                                 : carry + (static_cast<int64_t>(seg - 1) * p.B * p.H + bh) * MM * 2 * D * 2;
+    constexpr int64_t tile2 = 2 * D * L;  // halfs per chunk: z_k^T, z_v^T
+    const _Float16* zseg = zt + (bh * S + seg) * (Lseg / L) * tile2;
     __syncthreads();
-    
+
     if (key) {
         // ---------------- key waves
         const int kw = w;
         f4 U[RT];
-        u_load<D>(U, src, kw);  // before the token loads, which are waited for first
-        const __amdgpu_buffer_rsrc_t rk = seq_rsrc<D>(k, b, h, N, H, t_end);
-        uint32_t rkk[11];
-        fm_load<D, true>(rkk, rk, rsb, t_begin);
-        halo_fix<D>(rkk, sm, 1, t_begin);
-        fm_keys<D>(rkk, sm, sm.zkT, nch > 1 ? L : n_last, p.eps_feat, p.eps_norm);
-        if (nch > 1) fm_load<D, true>(rkk, rk, rsb, t_begin + L);
+        u_load<D>(U, src, kw);  // before the tile and token loads, which are waited for first
+        const __amdgpu_buffer_rsrc_t rq = seq_rsrc<D>(q, b, h, N, H, t_end);
+        u4 zr[kTilePieces<D>];  // z_k^T of the chunk after the current one
+        uint32_t rqq[11];       // raw queries of the chunk after that
+        tile_load<D>(zr, zseg);
+        fm_load<D, true>(rqq, rq, rsb, t_begin);
+        halo_fix<D>(rqq, sm, 0, t_begin);
+        tile_store<D>(sm.zkT, zr);
+        fm_queries<D>(rqq, sm, sm.yq, sm.sig[0], p.eps_feat, inv_dt);
+        if (nch > 1) {
+            tile_load<D>(zr, zseg + tile2);
+            fm_load<D, true>(rqq, rq, rsb, t_begin + L);
+        }
         lds_barrier();  // chunk 0 features
         for (int c = 0; c <= nch; ++c) {
-            const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
             // ---- phase 1
             f4 accQ[4];
             if (c < nch) {
@@ -867,13 +911,110 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                 }
                 key_update<D>(U, sm.aL, kw, sm.zkT, sm.ft);
             }
+            lds_barrier();
+            // ---- phase 2
+            if (c < nch) {
+                const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
+                const float* sig = sm.sig[c & 1];
+                // S^T = T^T G'^T (K order reversed: element jj <-> k = 32kb + 8g + 7 - jj),
+                // s~ = sigma~ (S + abar^{t+1} Q), X = s~ abar^{t+1}
+                f4 accS[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) accS[tt] = f4{0.f, 0.f, 0.f, 0.f};
+                const uint32_t c_gp = opaque(lds_addr(sm.gp) + 2 * (i * RP + 24 - 8 * g));
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const uint32_t ta = opaque(lds_addr(sm.ft) + 2 * (o128(i, L - 8 - 32 * kb - 8 * g) + 64 * 16 * kw));
+                    const half8 aT = rd8(ta), aTl = rd8(ta + dl);
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) {
+                        const half8 bg = rd8(c_gp + 2 * (16 * tt * RP + 32 * (1 - kb)));
+                        accS[tt] = mfma(aT, bg, accS[tt]);
+                        accS[tt] = mfma(aTl, bg, accS[tt]);
+                    }
+                }
+                // abar^{i+1} and abar^16 of modes 8kw + 2g + qq
+                const float4 e0 = *reinterpret_cast<const float4*>(&sm.pw[i][8 * kw + 2 * g]);
+                const float4 e16 = *reinterpret_cast<const float4*>(&sm.pw[15][8 * kw + 2 * g]);
+                float er[2] = {e0.x, e0.z}, ei[2] = {e0.y, e0.w};
+                const float e16r[2] = {e16.x, e16.z}, e16i[2] = {e16.y, e16.w};
+                // X: 8-byte stores at the perm32 position of m' = 16kw + 4g; s~: lanes of
+                // groups g and g ^ 1 exchange their halves so that group g (even) stores
+                // tiles 0 and 2 and group g + 1 tiles 1 and 3, eight m' per 16-byte store
+                const uint32_t x_st = opaque(lds_addr(sm.xc) + 2 * x256(i, perm32(16 * kw + 4 * g)));
+                u2 spk[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const float sg = sig[16 * tt + i];
+                    float sv[4], xv[4];
+#pragma unroll
+                    for (int qq = 0; qq < 2; ++qq) {
+                        const float qr = accQ[tt][2 * qq], qi = accQ[tt][2 * qq + 1];
+                        const float sr = sg * (accS[tt][2 * qq] + er[qq] * qr - ei[qq] * qi);
+                        const float si = sg * (accS[tt][2 * qq + 1] + er[qq] * qi + ei[qq] * qr);
+                        sv[2 * qq] = sr;
+                        sv[2 * qq + 1] = -si;
+                        xv[2 * qq] = sr * er[qq] - si * ei[qq];
+                        xv[2 * qq + 1] = -(sr * ei[qq] + si * er[qq]);
+                        const float nr = er[qq] * e16r[qq] - ei[qq] * e16i[qq];
+                        ei[qq] = er[qq] * e16i[qq] + ei[qq] * e16r[qq];
+                        er[qq] = nr;
+                    }
+                    wr4(x_st + 2 * 16 * tt * M2, xv[0], xv[1], xv[2], xv[3]);
+                    spk[tt] = u2{__builtin_bit_cast(uint32_t, half2v{static_cast<_Float16>(sv[0]), static_cast<_Float16>(sv[1])}),
+                                 __builtin_bit_cast(uint32_t, half2v{static_cast<_Float16>(sv[2]), static_cast<_Float16>(sv[3])})};
+                }
+                const bool godd = g & 1;
+                const uint32_t s_st = opaque(lds_addr(sm.sc) + 2 * x256(16 * godd + i, 16 * kw + 8 * (g >> 1)));
+#pragma unroll
+                for (int pq = 0; pq < 2; ++pq) {
+                    const u2 own = godd ? spk[2 * pq + 1] : spk[2 * pq];
+                    const u2 send = godd ? spk[2 * pq] : spk[2 * pq + 1];
+                    const auto r0 = __builtin_amdgcn_permlane16_swap(send[0], send[0], false, false);
+                    const auto r1 = __builtin_amdgcn_permlane16_swap(send[1], send[1], false, false);
+                    const u2 recv = {godd ? r0[0] : r0[1], godd ? r1[0] : r1[1]};
+                    const u4 v8 = godd ? u4{recv[0], recv[1], own[0], own[1]} : u4{own[0], own[1], recv[0], recv[1]};
+                    *(__attribute__((address_space(3))) u4*)(uintptr_t)(s_st + 2 * 32 * pq * M2) = v8;
+                }
+            }
+            if (c + 1 < nch) {
+                // features of chunk c+1: z_k^T from the feature pass, y' and sigma~ built here
+                tile_store<D>(sm.zkT, zr);
+                fm_queries<D>(rqq, sm, sm.yq, sm.sig[(c + 1) & 1], p.eps_feat, inv_dt);
+                if (c + 2 < nch) {
+                    step_fence();
+                    tile_load<D>(zr, zseg + (c + 2) * tile2);
+                    fm_load<D, true>(rqq, rq, rsb, t_begin + static_cast<int64_t>(c + 2) * L);
+                }
+            }
+            lds_barrier();
+        }
+        if (seg == S - 1 && state_out != nullptr)
+            u_store<D>(U, state_out + bh * MM * 2 * D * 2,
+                       n_last < L ? reinterpret_cast<const float2*>(th + kTabPwBack) : nullptr, kw);
+    } else {
+        // ---------------- value waves
+        const int vw = w - 8;
+        const bool own = vw < D / 16;  // owns a 16-column block of Gamma
+        f4 G[8];
+        if (own) g_load<D>(G, src, vw);  // before the tile loads, which are waited for first
+        const __amdgpu_buffer_rsrc_t ob = seq_rsrc<D>(o, b, h, N, H, t_end);
+        u4 zr[kTilePieces<D>];  // z_v^T of the next chunk to enter
+        tile_load<D>(zr, zseg + D * L);
+        lds_barrier();  // chunk 0 features
+        half8 bZ[2];    // Z_v fragments of the chunk whose readout comes next
+        for (int c = 0; c <= nch; ++c) {
+            const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
+            f4 accO[4];
+            // ---- phase 1: z_v^T (c); P~ tiles, X Gamma (c-1)
+            if (c < nch) tile_store<D>(sm.zvT, zr);
             if (c >= 1) {
                 const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
                 // P~'[t][k] = sum_m' sc[t][m'] T[k][m'] tiles (lane (g, i) of the T operand
                 // holds k = 16 kt + 15 - i), un-skewed into P~[t][t - k]
 #pragma unroll
                 for (int slot = 0; slot < 2; ++slot) {
-                    const int qt = kw + 8 * slot;
+                    const int qt = vw + 8 * slot;
                     if (qt < 10) {
                         const int tt = tile_tt(qt), kt = tile_kt(qt);
                         const uint32_t br0 = opaque(lds_addr(sm.ft) + 2 * o128(8 * g + (i >> 2), L - 16 - 16 * kt + 4 * (i & 3)));
@@ -892,127 +1033,6 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                     }
                 }
             }
-            lds_barrier();
-            // ---- phase 2
-            if (c < nch) {
-                const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
-                const float* sig = sm.sig[c & 1];
-                // S^T = T^T G'^T (K order reversed: element jj <-> k = 32kb + 8g + 7 - jj),
-                // s~ = sigma~ (S + abar^{t+1} Q), X = s~ abar^{t+1}
-                {
-                    f4 accS[4];
-#pragma unroll
-                    for (int tt = 0; tt < 4; ++tt) accS[tt] = f4{0.f, 0.f, 0.f, 0.f};
-                    const uint32_t c_gp = opaque(lds_addr(sm.gp) + 2 * (i * RP + 24 - 8 * g));
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
-                        const uint32_t ta = opaque(lds_addr(sm.ft) + 2 * (o128(i, L - 8 - 32 * kb - 8 * g) + 64 * 16 * kw));
-                        const half8 aT = rd8(ta), aTl = rd8(ta + dl);
-#pragma unroll
-                        for (int tt = 0; tt < 4; ++tt) {
-                            const half8 bg = rd8(c_gp + 2 * (16 * tt * RP + 32 * (1 - kb)));
-                            accS[tt] = mfma(aT, bg, accS[tt]);
-                            accS[tt] = mfma(aTl, bg, accS[tt]);
-                        }
-                    }
-                    // abar^{i+1} and abar^16 of modes 8kw + 2g + qq
-                    const float4 e0 = *reinterpret_cast<const float4*>(&sm.pw[i][8 * kw + 2 * g]);
-                    const float4 e16 = *reinterpret_cast<const float4*>(&sm.pw[15][8 * kw + 2 * g]);
-                    float er[2] = {e0.x, e0.z}, ei[2] = {e0.y, e0.w};
-                    const float e16r[2] = {e16.x, e16.z}, e16i[2] = {e16.y, e16.w};
-                    // X: 8-byte stores at the perm32 position of m' = 16kw + 4g; s~: lanes of
-                    // groups g and g ^ 1 exchange their halves so that group g (even) stores
-                    // tiles 0 and 2 and group g + 1 tiles 1 and 3, eight m' per 16-byte store
-                    const uint32_t x_st = opaque(lds_addr(sm.xc) + 2 * x256(i, perm32(16 * kw + 4 * g)));
-                    u2 spk[4];
-#pragma unroll
-                    for (int tt = 0; tt < 4; ++tt) {
-                        const float sg = sig[16 * tt + i];
-                        float sv[4], xv[4];
-#pragma unroll
-                        for (int qq = 0; qq < 2; ++qq) {
-                            const float qr = accQ[tt][2 * qq], qi = accQ[tt][2 * qq + 1];
-                            const float sr = sg * (accS[tt][2 * qq] + er[qq] * qr - ei[qq] * qi);
-                            const float si = sg * (accS[tt][2 * qq + 1] + er[qq] * qi + ei[qq] * qr);
-                            sv[2 * qq] = sr;
-                            sv[2 * qq + 1] = -si;
-                            xv[2 * qq] = sr * er[qq] - si * ei[qq];
-                            xv[2 * qq + 1] = -(sr * ei[qq] + si * er[qq]);
-                            const float nr = er[qq] * e16r[qq] - ei[qq] * e16i[qq];
-                            ei[qq] = er[qq] * e16i[qq] + ei[qq] * e16r[qq];
-                            er[qq] = nr;
-                        }
-                        wr4(x_st + 2 * 16 * tt * M2, xv[0], xv[1], xv[2], xv[3]);
-                        spk[tt] = u2{__builtin_bit_cast(uint32_t, half2v{static_cast<_Float16>(sv[0]), static_cast<_Float16>(sv[1])}),
-                                     __builtin_bit_cast(uint32_t, half2v{static_cast<_Float16>(sv[2]), static_cast<_Float16>(sv[3])})};
-                    }
-                    const bool godd = g & 1;
-                    const uint32_t s_st = opaque(lds_addr(sm.sc) + 2 * x256(16 * godd + i, 16 * kw + 8 * (g >> 1)));
-#pragma unroll
-                    for (int pq = 0; pq < 2; ++pq) {
-                        const u2 own = godd ? spk[2 * pq + 1] : spk[2 * pq];
-                        const u2 send = godd ? spk[2 * pq] : spk[2 * pq + 1];
-                        const auto r0 = __builtin_amdgcn_permlane16_swap(send[0], send[0], false, false);
-                        const auto r1 = __builtin_amdgcn_permlane16_swap(send[1], send[1], false, false);
-                        const u2 recv = {godd ? r0[0] : r0[1], godd ? r1[0] : r1[1]};
-                        const u4 v8 = godd ? u4{recv[0], recv[1], own[0], own[1]} : u4{own[0], own[1], recv[0], recv[1]};
-                        *(__attribute__((address_space(3))) u4*)(uintptr_t)(s_st + 2 * 32 * pq * M2) = v8;
-                    }
-                }
-            }
-            if (c + 1 < nch) {
-                fm_keys<D>(rkk, sm, sm.zkT, c + 2 < nch ? L : n_last, p.eps_feat, p.eps_norm);
-                if (c + 2 < nch) {
-                    step_fence();
-                    fm_load<D, true>(rkk, rk, rsb, t0 + 2 * L);
-                }
-            }
-            lds_barrier();
-        }
-        if (seg == S - 1 && state_out != nullptr)
-            u_store<D>(U, state_out + bh * MM * 2 * D * 2,
-                       n_last < L ? reinterpret_cast<const float2*>(th + kTabPwBack) : nullptr, kw);
-    } else {
-        // ---------------- value waves
-        const int vw = w - 8;
-        const bool own = vw < D / 16;  // owns a 16-column block of Gamma
-        f4 G[8];
-        if (own) g_load<D>(G, src, vw);  // before the token loads, which are waited for first
-        const __amdgpu_buffer_rsrc_t rq = seq_rsrc<D>(q, b, h, N, H, t_end);
-        const __amdgpu_buffer_rsrc_t rv = seq_rsrc<D>(v, b, h, N, H, t_end);
-        const __amdgpu_buffer_rsrc_t ob = seq_rsrc<D>(o, b, h, N, H, t_end);
-        uint32_t rqq[11], rvv[8];
-        fm_load<D, true>(rqq, rq, rsb, t_begin);
-        halo_fix<D>(rqq, sm, 0, t_begin);
-        {
-            half2v yo[8];
-            fm_queries<D>(yo, rqq, sm, sm.sig[0], p.eps_feat, inv_dt);
-            fm_write_q<D>(yo, sm.yq);
-        }
-        fm_load<D, false>(rvv, rv, rsb, t_begin);
-        if (nch > 1) fm_load<D, true>(rqq, rq, rsb, t_begin + L);
-        vm_wait_all();  // the loop then enters with no load in flight, as it does from its own end
-        lds_barrier();  // chunk 0 features
-        half8 bZ[2];    // Z_v fragments of the chunk whose readout comes next
-        for (int c = 0; c <= nch; ++c) {
-            const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
-            half2v yo[8];
-            f4 accO[4];
-            // ---- phase 1: values (c); queries (c+1), held until phase 2; token loads; X Gamma (c-1)
-            if (c < nch) {
-                fm_values<D>(rvv, sm, sm.zvT, c + 1 < nch ? L : n_last, p.eps_norm);
-                if (c + 1 < nch) {
-                    step_fence();
-                    fm_load<D, false>(rvv, rv, rsb, t0 + L);
-                }
-            }
-            if (c + 1 < nch) {
-                fm_queries<D>(yo, rqq, sm, sm.sig[(c + 1) & 1], p.eps_feat, inv_dt);
-                if (c + 2 < nch) {
-                    step_fence();
-                    fm_load<D, true>(rqq, rq, rsb, t0 + 2 * L);
-                }
-            }
             if (c >= 1 && own) {
                 // o^T = Gamma_prev^T X^T (c-block vw: lane (g, i) of tile tt holds
                 // o[16tt + i][16vw + 4g + jj], four consecutive channels of one token)
@@ -1028,9 +1048,8 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                 }
             }
             lds_barrier();
-            // ---- phase 2: y' (c+1); o^T += Z_v^T P~^T, Delta o, Gamma update (c-1); Z_v fragments (c)
-            vm_wait_all();  // token loads of phase 1, before any store joins the counter
-            if (c + 1 < nch) fm_write_q<D>(yo, sm.yq);
+            // ---- phase 2: o^T += Z_v^T P~^T, Delta o, Gamma update (c-1); Z_v fragments (c)
+            if (c + 1 < nch) tile_load<D>(zr, zseg + (c + 1) * tile2 + D * L);
             if (c >= 1 && own) {
                 const int64_t tp = t0 - L;  // first token of chunk c-1
                 const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
@@ -1086,16 +1105,17 @@ hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, con
     uint8_t* tab = static_cast<uint8_t*>(workspace);
     float* ws = reinterpret_cast<float*>(tab + static_cast<size_t>(p.H) * kTabBytes);
     const int64_t pairs = p.B * p.H;
+    _Float16* zt = reinterpret_cast<_Float16*>(ws + static_cast<size_t>(S - 1) * pairs * MM * 2 * D * 2);
     const int64_t last_len = p.N - (S - 1) * Lseg;
     const int back = static_cast<int>((L - last_len % L) % L);
     zoh_tables_kernel<<<dim3(static_cast<unsigned>(p.H), 16), 256, 0, stream>>>(p, prm, Lseg, back, tab);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    segment_state_kernel<D><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(p, prm, k16, v16, t16, tab, ws,
+                                                                                      zt, Lseg, S);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     if (S > 1) {
-        segment_state_kernel<D><<<dim3(static_cast<unsigned>(pairs * (S - 1))), NTH, 0, stream>>>(p, prm, k16, v16,
-                                                                                                 t16, tab, ws, Lseg, S);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
         const int64_t total = pairs * MM * 2 * p.d;
         segment_carry_kernel<<<dim3(static_cast<unsigned>((total + 255) / 256)), 256, 0, stream>>>(p, state_in, tab,
                                                                                                   ws, S);
@@ -1103,7 +1123,7 @@ hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, con
         if (e != hipSuccess) return e;
     }
     chunked_forward_kernel<D><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(
-        p, prm, q16, k16, v16, static_cast<uint16_t*>(o), state_in, t16, state_out, tab, ws, Lseg, S);
+        p, prm, q16, zt, static_cast<uint16_t*>(o), state_in, t16, state_out, tab, ws, Lseg, S);
     return hipGetLastError();
 }
 
@@ -1114,8 +1134,10 @@ size_t chunked_ws_workspace_bytes(const Problem& p) {
     int S;
     int64_t Lseg;
     cws::plan_segments(p, S, Lseg);
+    // tables, segment states, and one z_k^T, z_v^T tile pair per chunk slot
     return static_cast<size_t>(p.H) * cws::kTabBytes +
-           static_cast<size_t>(S - 1) * p.B * p.H * p.M * 2 * p.d * 2 * sizeof(float);
+           static_cast<size_t>(S - 1) * p.B * p.H * p.M * 2 * p.d * 2 * sizeof(float) +
+           static_cast<size_t>(p.B * p.H) * S * static_cast<size_t>(Lseg) * 2 * p.d * sizeof(_Float16);
 }
 
 hipError_t launch_forward_chunked_ws(const Problem& p, const idattn_params& prm, const void* q, const void* k,
