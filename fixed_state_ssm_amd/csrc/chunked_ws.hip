@@ -104,6 +104,23 @@ __host__ __device__ constexpr int perm32(int c) {
 // y' [t][r]: 256-byte rows (D = 128) or swizzled 128-byte rows (D = 64), columns in perm32 order.
 template <int D>
 __host__ __device__ constexpr int yq_off(int t, int c) { return D == 128 ? x256(t, perm32(c)) : o128(t, perm32(c)); }
+// Byte offset of y'(8tb + s, c) from y'(8tb, c): s rows on, with the row swizzle
+// of token s folded into an XOR of the 16-byte chunk bits only.
+template <int D>
+__host__ __device__ constexpr uint32_t yq_sx(int s) { return D == 128 ? 16u * s : 32u * (s >> 1); }
+template <int D>
+constexpr uint32_t kYqRow = 2 * D;
+template <int D>
+constexpr bool yq_xor_ok() {
+    for (int tb = 0; tb < L / 8; ++tb)
+        for (int c = 0; c < D; c += 2)
+            for (int s = 0; s < 8; ++s) {
+                const uint32_t b0 = 2u * yq_off<D>(8 * tb, c);
+                if (2u * yq_off<D>(8 * tb + s, c) != (b0 ^ yq_sx<D>(s)) + s * kYqRow<D>) return false;
+            }
+    return true;
+}
+static_assert(yq_xor_ok<64>() && yq_xor_ok<128>(), "y' row swizzle must reduce to an XOR of chunk bits");
 
 __device__ __forceinline__ half8 cat(const half4& a, const half4& b) {
     half8 r;
@@ -206,7 +223,12 @@ __device__ __forceinline__ void step_fence() { __builtin_amdgcn_sched_barrier(0)
 // this wait before it issues the stores.
 __device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-__device__ __forceinline__ uint16_t to_bf16(float x) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+// Two floats to a packed bf16 pair (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{lo, hi}, bf16x2));
+}
 
 __device__ __forceinline__ half8 to_half8(const f4& a, const f4& b) {
     half8 r;
@@ -280,7 +302,7 @@ template <int D>
 struct SmemFwd {
     // window A: [t][*] tiles
     _Float16 yq[L * D];           // y' of the queries [t][r] (yq_off)
-    _Float16 sc[L * M2];          // [t][m'] (Re s~, -Im s~) (x256)
+    _Float16 sc[L * M2];          // [t][m'] (Re s~, -Im s~) (x256 of perm32)
     _Float16 xc[L * M2];          // [t][m'] (Re X, -Im X) (x256 of perm32)
     // window B: swizzled [rows][64] tiles
     _Float16 zkT[D * L];          // z_k^T [r][j]
@@ -489,9 +511,10 @@ __device__ __forceinline__ void fm_queries(const uint32_t (&r)[11], SM& sm, cons
     const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
     float y[2][8], ss[8];
     conv_silu<D>(r, sm.wq, cgi, y, ss);
+    const uint32_t y0 = 2u * yq_off<D>(8 * tb, 2 * cgi);
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-        *(lds_h2*)(uintptr_t)(lds_addr(yq) + 2 * yq_off<D>(8 * tb + s, 2 * cgi)) =
+        *(lds_h2*)(uintptr_t)(lds_addr(yq) + (y0 ^ yq_sx<D>(s)) + s * kYqRow<D>) =
             half2v{static_cast<_Float16>(y[0][s]), static_cast<_Float16>(y[1][s])};
     const float tot = reduce_scatter8<Cfg<D>::CP>(ss);
     if (cgi < 8) sig[8 * tb + scatter_token(cgi)] = -kLn2 * inv_dt * __builtin_amdgcn_rcpf(fmaf(kLn2Sq, tot, eps_feat));
@@ -613,21 +636,35 @@ __device__ __forceinline__ void g_store(const f4 (&G)[8], float* dst, const floa
         }
 }
 
-// Window-B lane base (byte address from z_k^T) for fragment reads of rows
-// R0 + i at column chunk 4kb + g (R0 = 16 x any tile index of any of the four tiles).
-__device__ __forceinline__ uint32_t win_b(const void* zkT, int kb) {
-    const int lane = tid_now() & 63, g = lane >> 4, i = lane & 15;
-    return opaque(lds_addr(zkT) + 2 * o128(i, 32 * kb + 8 * g));
+// Lane byte offset, within a swizzled [rows][64] tile, of the fragment read of
+// row R0 + i at column chunk g (R0 any multiple of 16).  Column chunk 4kb + g
+// is the same offset with bit 6 flipped: the swizzle XORs the low three chunk
+// bits with a function of the row, which leaves bit 2 of the chunk alone.
+__device__ __forceinline__ uint32_t frag_off(int ln) { return opaque(2u * o128(ln & 15, 8 * (ln >> 4))); }
+__device__ __forceinline__ uint32_t frag_kb(uint32_t off, int kb) { return off ^ (64u * kb); }
+// The same holds for the 256-byte rows of x256 (chunk 4kb + g XOR row % 16, kb < 4).
+__device__ __forceinline__ uint32_t frag256_off(int ln) { return opaque(2u * x256(ln & 15, 8 * (ln >> 4))); }
+constexpr bool frag_xor_ok() {
+    for (int r = 0; r < 128; ++r)
+        for (int g = 0; g < 4; ++g) {
+            for (int kb = 0; kb < 2; ++kb)
+                if (o128(r, 32 * kb + 8 * g) != (o128(r % 16, 8 * g) ^ (32 * kb)) + 64 * (r - r % 16)) return false;
+            for (int kb = 0; kb < 4; ++kb)
+                if (r < 64 && x256(r, 32 * kb + 8 * g) != (x256(r % 16, 8 * g) ^ (32 * kb)) + 128 * (r - r % 16))
+                    return false;
+        }
+    return true;
 }
+static_assert(frag_xor_ok(), "fragment offsets of K block kb must be an XOR of bit 5 (in halfs)");
 
 // U <- abar^L U + Z_k^T F  (the real and imaginary rows of a mode sit in lanes i, i ^ 1);
 // the low parts of F^T follow the high parts at M2 L halfs.
 template <int D>
 __device__ __forceinline__ void key_update(f4 (&U)[Cfg<D>::RT], const float2* aL, int kw, const void* zkT,
-                                           const void* ft) {
+                                           const void* ft, int ln) {
     constexpr int RT = Cfg<D>::RT;
     constexpr uint32_t dl = M2 * L * 2;
-    const int i = tid_now() & 15;
+    const int i = ln & 15;
     const float2 a = aL[(16 * kw + i) >> 1];
     const float aLs = (i & 1) ? a.y : -a.y;
 #pragma unroll
@@ -638,10 +675,11 @@ __device__ __forceinline__ void key_update(f4 (&U)[Cfg<D>::RT], const float2* aL
             U[rt][jj] = fmaf(a.x, u, dpp_mov<0xB1>(u) * aLs);
         }
     }
+    const uint32_t off = frag_off(ln);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t wb = win_b(zkT, kb);
-        const uint32_t fo = win_b(ft, kb) + 2 * 64 * 16 * kw;  // F^T rows 16kw + i
+        const uint32_t wb = lds_addr(zkT) + frag_kb(off, kb);
+        const uint32_t fo = lds_addr(ft) + frag_kb(off, kb) + 2 * 64 * 16 * kw;  // F^T rows 16kw + i
         const half8 bF = rd8(fo), bFl = rd8(fo + dl);                // F[j][m'], j = 32kb + 8g + jj
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -654,8 +692,9 @@ __device__ __forceinline__ void key_update(f4 (&U)[Cfg<D>::RT], const float2* aL
 
 // Gamma <- abar^L Gamma + F^T Z_v, with bZ[kb] = Z_v[32kb + 8g + jj][16vw + i]
 template <int D>
-__device__ __forceinline__ void value_update(f4 (&G)[8], const float2* aL, const half8 (&bZ)[2], const void* ft) {
-    const int g = (tid_now() & 63) >> 4;
+__device__ __forceinline__ void value_update(f4 (&G)[8], const float2* aL, const half8 (&bZ)[2], const void* ft,
+                                             int ln) {
+    const int g = ln >> 4;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
         const float4 a = *reinterpret_cast<const float4*>(&aL[8 * mt + 2 * g]);
@@ -665,9 +704,10 @@ __device__ __forceinline__ void value_update(f4 (&G)[8], const float2* aL, const
         G[mt][2] = a.z * r1 - a.w * i1;
         G[mt][3] = a.z * i1 + a.w * r1;
     }
+    const uint32_t off = frag_off(ln);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t wb = win_b(ft, kb);
+        const uint32_t wb = lds_addr(ft) + frag_kb(off, kb);
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             G[mt] = mfma(rd8(wb + 2048 * mt), bZ[kb], G[mt]);
@@ -676,9 +716,10 @@ __device__ __forceinline__ void value_update(f4 (&G)[8], const float2* aL, const
     }
 }
 
-__device__ __forceinline__ void load_bz(half8 (&bZ)[2], int vw, const void* zvT) {
+__device__ __forceinline__ void load_bz(half8 (&bZ)[2], int vw, const void* zvT, int ln) {
+    const uint32_t off = frag_off(ln);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) bZ[kb] = rd8(win_b(zvT, kb) + 2048 * vw);
+    for (int kb = 0; kb < 2; ++kb) bZ[kb] = rd8(lds_addr(zvT) + frag_kb(off, kb) + 2048 * vw);
 }
 
 // Causal 16 x 16 tiles (tt, kt), kt <= tt, of the G and P~ products: key wave
@@ -738,7 +779,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
         for (int c = 0; c < nch; ++c) {
             const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
             tile_copy_out<D>(sm.zkT[c & 1], zseg + c * 2 * D * L);
-            if (upd) key_update<D>(U, sm.aL, kw, sm.zkT[c & 1], sm.ft);
+            if (upd) key_update<D>(U, sm.aL, kw, sm.zkT[c & 1], sm.ft, tid_now() & 63);
             if (c + 1 < nch) {
                 fm_keys<D>(rkk, sm, sm.zkT[(c + 1) & 1], c + 2 < nch ? L : n_last, p.eps_feat, p.eps_norm);
                 if (c + 2 < nch) {
@@ -764,9 +805,10 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
             const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
             tile_copy_out<D>(sm.zvT[c & 1], zseg + c * 2 * D * L + D * L);
             if (own) {
+                const int ln = tid_now() & 63;
                 half8 bZ[2];
-                load_bz(bZ, vw, sm.zvT[c & 1]);
-                value_update<D>(G, sm.aL, bZ, sm.ft);
+                load_bz(bZ, vw, sm.zvT[c & 1], ln);
+                value_update<D>(G, sm.aL, bZ, sm.ft, ln);
             }
             if (c + 1 < nch) {
                 fm_values<D>(rvv, sm, sm.zvT[(c + 1) & 1], c + 2 < nch ? L : n_last, p.eps_norm);
@@ -879,6 +921,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             if (c < nch) {
                 // G tiles -> G'; Q^T = U Y^T (rows m' = 16kw + 4g + jj, columns t); U update
                 const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
+                const uint32_t yoff = opaque(2u * yq_off<D>(i, 4 * g));  // y' row i, K block 0
 #pragma unroll
                 for (int slot = 0; slot < 2; ++slot) {
                     const int qt = kw + 8 * slot;
@@ -891,7 +934,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                         f4 accG = {};
 #pragma unroll
                         for (int kb = 0; kb < KB; ++kb) {
-                            const uint32_t ar = opaque(lds_addr(sm.yq) + 2 * yq_off<D>(16 * tt + i, 32 * kb + 4 * g));
+                            const uint32_t ar = lds_addr(sm.yq) + frag_kb(yoff, kb) + 2 * 16 * tt * YR;
                             accG = mfma(rd8(ar), cat(rd4t(br0 + 4096 * kb), rd4t(br1 + 4096 * kb)), accG);
                         }
                         const uint32_t gs = opaque(lds_addr(sm.gp) + 2 * ((16 * tt + 4 * g) * (RP - 1) + L - 1 + 16 * jt + i));
@@ -905,11 +948,11 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
                     const half8 aU = to_half8(U[2 * kb], U[2 * kb + 1]);
-                    const uint32_t yb = opaque(lds_addr(sm.yq) + 2 * yq_off<D>(i, 32 * kb + 4 * g));
+                    const uint32_t yb = lds_addr(sm.yq) + frag_kb(yoff, kb);
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) accQ[tt] = mfma(aU, rd8(yb + 2 * 16 * tt * YR), accQ[tt]);
                 }
-                key_update<D>(U, sm.aL, kw, sm.zkT, sm.ft);
+                key_update<D>(U, sm.aL, kw, sm.zkT, sm.ft, ln);
             }
             lds_barrier();
             // ---- phase 2
@@ -922,9 +965,10 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) accS[tt] = f4{0.f, 0.f, 0.f, 0.f};
                 const uint32_t c_gp = opaque(lds_addr(sm.gp) + 2 * (i * RP + 24 - 8 * g));
+                const uint32_t toff = opaque(2u * (o128(i, L - 8 - 8 * g) + 64 * 16 * kw));
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const uint32_t ta = opaque(lds_addr(sm.ft) + 2 * (o128(i, L - 8 - 32 * kb - 8 * g) + 64 * 16 * kw));
+                    const uint32_t ta = lds_addr(sm.ft) + frag_kb(toff, kb);
                     const half8 aT = rd8(ta), aTl = rd8(ta + dl);
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) {
@@ -938,11 +982,9 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                 const float4 e16 = *reinterpret_cast<const float4*>(&sm.pw[15][8 * kw + 2 * g]);
                 float er[2] = {e0.x, e0.z}, ei[2] = {e0.y, e0.w};
                 const float e16r[2] = {e16.x, e16.z}, e16i[2] = {e16.y, e16.w};
-                // X: 8-byte stores at the perm32 position of m' = 16kw + 4g; s~: lanes of
-                // groups g and g ^ 1 exchange their halves so that group g (even) stores
-                // tiles 0 and 2 and group g + 1 tiles 1 and 3, eight m' per 16-byte store
-                const uint32_t x_st = opaque(lds_addr(sm.xc) + 2 * x256(i, perm32(16 * kw + 4 * g)));
-                u2 spk[4];
+                // s~ and X: 8-byte stores at the perm32 position of m' = 16kw + 4g
+                const uint32_t pst = opaque(2 * x256(i, perm32(16 * kw + 4 * g)));
+                const uint32_t x_st = lds_addr(sm.xc) + pst, s_st = lds_addr(sm.sc) + pst;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     const float sg = sig[16 * tt + i];
@@ -961,20 +1003,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                         er[qq] = nr;
                     }
                     wr4(x_st + 2 * 16 * tt * M2, xv[0], xv[1], xv[2], xv[3]);
-                    spk[tt] = u2{__builtin_bit_cast(uint32_t, half2v{static_cast<_Float16>(sv[0]), static_cast<_Float16>(sv[1])}),
-                                 __builtin_bit_cast(uint32_t, half2v{static_cast<_Float16>(sv[2]), static_cast<_Float16>(sv[3])})};
-                }
-                const bool godd = g & 1;
-                const uint32_t s_st = opaque(lds_addr(sm.sc) + 2 * x256(16 * godd + i, 16 * kw + 8 * (g >> 1)));
-#pragma unroll
-                for (int pq = 0; pq < 2; ++pq) {
-                    const u2 own = godd ? spk[2 * pq + 1] : spk[2 * pq];
-                    const u2 send = godd ? spk[2 * pq] : spk[2 * pq + 1];
-                    const auto r0 = __builtin_amdgcn_permlane16_swap(send[0], send[0], false, false);
-                    const auto r1 = __builtin_amdgcn_permlane16_swap(send[1], send[1], false, false);
-                    const u2 recv = {godd ? r0[0] : r0[1], godd ? r1[0] : r1[1]};
-                    const u4 v8 = godd ? u4{recv[0], recv[1], own[0], own[1]} : u4{own[0], own[1], recv[0], recv[1]};
-                    *(__attribute__((address_space(3))) u4*)(uintptr_t)(s_st + 2 * 32 * pq * M2) = v8;
+                    wr4(s_st + 2 * 16 * tt * M2, sv[0], sv[1], sv[2], sv[3]);
                 }
             }
             if (c + 1 < nch) {
@@ -1008,21 +1037,24 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             f4 accO[4];
             // ---- phase 1: z_v^T (c); P~ tiles, X Gamma (c-1)
             if (c < nch) tile_store<D>(sm.zvT, zr);
+            const int ln = tid_now() & 63;
+            const uint32_t xoff = frag256_off(ln);  // s~ and X rows i, K block 0
             if (c >= 1) {
-                const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
+                const int g = ln >> 4, i = ln & 15;
                 // P~'[t][k] = sum_m' sc[t][m'] T[k][m'] tiles (lane (g, i) of the T operand
-                // holds k = 16 kt + 15 - i), un-skewed into P~[t][t - k]
+                // holds k = 16 kt + 15 - i), un-skewed into P~[t][t - k]; K = m' in perm32
+                // order on both sides: s~ as stored, F^T rows 32kb + 4g + e and 32kb + 16 + 4g + e
 #pragma unroll
                 for (int slot = 0; slot < 2; ++slot) {
                     const int qt = vw + 8 * slot;
                     if (qt < 10) {
                         const int tt = tile_tt(qt), kt = tile_kt(qt);
-                        const uint32_t br0 = opaque(lds_addr(sm.ft) + 2 * o128(8 * g + (i >> 2), L - 16 - 16 * kt + 4 * (i & 3)));
-                        const uint32_t br1 = opaque(lds_addr(sm.ft) + 2 * o128(8 * g + (i >> 2) + 4, L - 16 - 16 * kt + 4 * (i & 3)));
+                        const uint32_t br0 = opaque(lds_addr(sm.ft) + 2 * o128(4 * g + (i >> 2), L - 16 - 16 * kt + 4 * (i & 3)));
+                        const uint32_t br1 = opaque(lds_addr(sm.ft) + 2 * o128(16 + 4 * g + (i >> 2), L - 16 - 16 * kt + 4 * (i & 3)));
                         f4 accP = {};
 #pragma unroll
                         for (int kb = 0; kb < 4; ++kb) {
-                            const half8 a = rd8(opaque(lds_addr(sm.sc) + 2 * x256(16 * tt + i, 32 * kb + 8 * g)));
+                            const half8 a = rd8(lds_addr(sm.sc) + frag_kb(xoff, kb) + 2 * 16 * tt * M2);
                             accP = mfma(a, cat(rd4t(br0 + 4096 * kb), rd4t(br1 + 4096 * kb)), accP);
                             accP = mfma(a, cat(rd4t(br0 + 4096 * kb + dl), rd4t(br1 + 4096 * kb + dl)), accP);
                         }
@@ -1036,13 +1068,12 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             if (c >= 1 && own) {
                 // o^T = Gamma_prev^T X^T (c-block vw: lane (g, i) of tile tt holds
                 // o[16tt + i][16vw + 4g + jj], four consecutive channels of one token)
-                const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) accO[tt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
                     const half8 bG = to_half8(G[2 * kb], G[2 * kb + 1]);
-                    const uint32_t xb = opaque(lds_addr(sm.xc) + 2 * x256(i, 32 * kb + 8 * g));  // perm32 positions
+                    const uint32_t xb = lds_addr(sm.xc) + frag_kb(xoff, kb);  // perm32 positions
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) accO[tt] = mfma(bG, rd8(xb + 2 * 16 * tt * M2), accO[tt]);
                 }
@@ -1050,9 +1081,10 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             lds_barrier();
             // ---- phase 2: o^T += Z_v^T P~^T, Delta o, Gamma update (c-1); Z_v fragments (c)
             if (c + 1 < nch) tile_load<D>(zr, zseg + (c + 1) * tile2 + D * L);
+            const int ln2 = tid_now() & 63;
             if (c >= 1 && own) {
                 const int64_t tp = t0 - L;  // first token of chunk c-1
-                const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
+                const int g = ln2 >> 4, i = ln2 & 15;
                 const uint32_t c_pp = opaque(lds_addr(sm.pp) + 2 * (i * RP + 8 * g));
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
@@ -1063,15 +1095,12 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     const uint32_t toff = static_cast<uint32_t>((tp + 16 * tt) * rsb);
-                    const u2 pk = {static_cast<uint32_t>(to_bf16(accO[tt][0] * dt)) |
-                                       (static_cast<uint32_t>(to_bf16(accO[tt][1] * dt)) << 16),
-                                   static_cast<uint32_t>(to_bf16(accO[tt][2] * dt)) |
-                                       (static_cast<uint32_t>(to_bf16(accO[tt][3] * dt)) << 16)};
+                    const u2 pk = {pack_bf16(accO[tt][0] * dt, accO[tt][1] * dt), pack_bf16(accO[tt][2] * dt, accO[tt][3] * dt)};
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, pk), ob, olane + toff, 0, 0);
                 }
-                value_update<D>(G, sm.aL, bZ, sm.ft);
+                value_update<D>(G, sm.aL, bZ, sm.ft, ln2);
             }
-            if (c < nch && own) load_bz(bZ, vw, sm.zvT);
+            if (c < nch && own) load_bz(bZ, vw, sm.zvT, ln2);
             lds_barrier();
         }
         if (own && seg == S - 1 && state_out != nullptr)
