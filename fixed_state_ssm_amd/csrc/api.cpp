@@ -232,8 +232,10 @@ idattn_status idattn_forward(const idattn_dims* dims, const idattn_params* param
     }
 
     if (algo == IDATTN_ALGO_CHUNKED) {
-        e = idattn::launch_forward_chunked(p, *params, q, k, v, o, state_in, tail_in, state_out, workspace, s);
+        e = idattn::launch_forward_chunked(p, *params, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace,
+                                           s);
         if (e != hipSuccess) return hip_fail(e, "chunked forward");
+        return IDATTN_OK;  // the chunked forward writes tail_out itself
     } else {
         const size_t tok = static_cast<size_t>(D.B) * D.H * D.N;
         float* ws = static_cast<float*>(workspace);

@@ -18,8 +18,8 @@ size_t chunked_workspace_bytes(const Problem& p) { return chunked_ws_workspace_b
 
 hipError_t launch_forward_chunked(const Problem& p, const idattn_params& prm, const void* q, const void* k,
                                   const void* v, void* o, const float* state_in, const void* tail_in,
-                                  float* state_out, void* workspace, hipStream_t stream) {
-    return launch_forward_chunked_ws(p, prm, q, k, v, o, state_in, tail_in, state_out, workspace, stream);
+                                  float* state_out, void* tail_out, void* workspace, hipStream_t stream) {
+    return launch_forward_chunked_ws(p, prm, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, stream);
 }
 
 }  // namespace idattn

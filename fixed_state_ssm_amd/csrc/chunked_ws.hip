@@ -860,9 +860,10 @@ __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, const flo
 template <int D>
 __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_params prm,
                                                               const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ k,
                                                               const _Float16* __restrict__ zt, uint16_t* __restrict__ o,
-                                                              const float* state_in,
-                                                              const uint16_t* __restrict__ tail_in, float* state_out,
+                                                              const float* state_in, const uint16_t* tail_in,
+                                                              float* state_out, uint16_t* tail_out,
                                                               const uint8_t* __restrict__ tab,
                                                               const float* __restrict__ carry, int64_t Lseg, int S) {
     constexpr int RT = Cfg<D>::RT, KB = Cfg<D>::KB, YR = Cfg<D>::YR;
@@ -881,7 +882,8 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
     const int n_last = static_cast<int>(t_end - t_begin - static_cast<int64_t>(nch - 1) * L);
     const uint8_t* th = tab + h * kTabBytes;
 
-    load_prologue<D, true>(sm, prm, tail_in, b, h, H, static_cast<int>(p.W));
+    // only the first segment reads the stored tail (and writes the new one at its end)
+    load_prologue<D, true>(sm, prm, seg == 0 ? tail_in : nullptr, b, h, H, static_cast<int>(p.W));
     copy16(sm.ft, th + kTabFT, M2 * L * 2);
     copy16(sm.ftl, th + kTabFTL, M2 * L * 2);
     if (tid < MM) sm.aL[tid] = reinterpret_cast<const float2*>(th + kTabPw)[(L - 1) * MM + tid];
@@ -1107,6 +1109,18 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             g_store<D>(G, state_out + bh * MM * 2 * D * 2,
                        n_last < L ? reinterpret_cast<const float2*>(th + kTabPwBack) : nullptr, vw);
     }
+    if (seg == 0 && tail_out != nullptr) {
+        // New conv tail: positions N-W+1 .. N-1 of q and k, where negative positions
+        // come from the stored tail kept in shared memory since the prologue; tail_in
+        // is not read again, so tail_out may be the same buffer.
+        const int Wm1 = static_cast<int>(p.W) - 1, E = 2 * Wm1 * D;
+        for (int e = tid; e < E; e += NTH) {
+            const int sel = e / (Wm1 * D), t = (e / D) % Wm1, c = e % D;
+            const int64_t pos = N - Wm1 + t;
+            tail_out[bh * E + e] = pos < 0 ? sm.halo[sel][3 + pos][c]
+                                           : (sel == 0 ? q : k)[((b * N + pos) * H + h) * D + c];
+        }
+    }
 }
 
 void plan_segments(const Problem& p, int& S, int64_t& Lseg) {
@@ -1123,7 +1137,8 @@ void plan_segments(const Problem& p, int& S, int64_t& Lseg) {
 
 template <int D>
 hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, const void* k, const void* v, void* o,
-                  const float* state_in, const void* tail_in, float* state_out, void* workspace, hipStream_t stream) {
+                  const float* state_in, const void* tail_in, float* state_out, void* tail_out, void* workspace,
+                  hipStream_t stream) {
     int S;
     int64_t Lseg;
     plan_segments(p, S, Lseg);
@@ -1152,7 +1167,8 @@ hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, con
         if (e != hipSuccess) return e;
     }
     chunked_forward_kernel<D><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(
-        p, prm, q16, zt, static_cast<uint16_t*>(o), state_in, t16, state_out, tab, ws, Lseg, S);
+        p, prm, q16, k16, zt, static_cast<uint16_t*>(o), state_in, t16, state_out, static_cast<uint16_t*>(tail_out),
+        tab, ws, Lseg, S);
     return hipGetLastError();
 }
 
@@ -1171,9 +1187,10 @@ size_t chunked_ws_workspace_bytes(const Problem& p) {
 
 hipError_t launch_forward_chunked_ws(const Problem& p, const idattn_params& prm, const void* q, const void* k,
                                      const void* v, void* o, const float* state_in, const void* tail_in,
-                                     float* state_out, void* workspace, hipStream_t stream) {
-    if (p.d == 128) return cws::launch<128>(p, prm, q, k, v, o, state_in, tail_in, state_out, workspace, stream);
-    return cws::launch<64>(p, prm, q, k, v, o, state_in, tail_in, state_out, workspace, stream);
+                                     float* state_out, void* tail_out, void* workspace, hipStream_t stream) {
+    if (p.d == 128)
+        return cws::launch<128>(p, prm, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, stream);
+    return cws::launch<64>(p, prm, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, stream);
 }
 
 }  // namespace idattn

@@ -266,3 +266,31 @@ def test_in_place_state_and_zero_tokens(fs):
     fs.idattn_forward(d0, fs.make_params(p), None, None, None, None, None, None, st2, tl2, None, 0)
     _sync()
     assert not st2.any() and not tl2.any()
+
+
+@pytest.mark.parametrize("N", [2, 50, 1000])
+def test_in_place_state_and_tail_chunked(fs, N):
+    """The chunked path with state_out = state_in and tail_out = tail_in (the
+    same buffers): short sequences whose new tail still holds stored tail
+    positions, one segment, and many segments."""
+    import torch
+    s = WL.spec("1p3b", B=1, H=2, N=N)
+    if not _chunked_available(fs, s):
+        pytest.skip("chunked path not built")
+    q, k, v = WL.make_rows(s, seed=7)
+    params = WL.make_params(s)
+    p = fs.params_to_device(params)
+    st0, tl0 = WL.make_decode_state(s, seed=7)
+    st = state_dev(st0)
+    tl = up(tl0, "bf16")
+    dims = fs.make_dims(1, N, 2, 128, 64, 4, "bf16", "chunked")
+    nb = fs.idattn_forward_workspace_size(dims)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    o = torch.empty((1, N, 2, 128), dtype=torch.bfloat16, device="cuda")
+    print(f"in-place chunked N={N}", flush=True)
+    fs.idattn_forward(dims, fs.make_params(p), up(q, "bf16"), up(k, "bf16"), up(v, "bf16"), o, st, tl, st, tl, ws, nb)
+    _sync()
+    o_ref, st_ref, tl_ref = oracle.forward(q, k, v, params, state_in=st0, tail_in=tl0)  # bf16-exact inputs
+    assert rel_l2(down(o), o_ref) <= GATE_BF16
+    assert rel_l2(state_np(st), st_ref) <= GATE_BF16
+    assert np.array_equal(down(tl), tl_ref.astype(np.float32))
