@@ -503,21 +503,26 @@ __device__ __forceinline__ void fm_values(const uint32_t (&r)[8], const SM& sm, 
     write_zt(zT, cgi, tb, x);
 }
 
-// y' of the thread's 8 tokens to the shared tile yq, and sigma~ to sig.
+// y' of the thread's 8 tokens, kept as fp16 pairs until fm_write_q, and sigma~ to sig.
 template <int D, class SM>
-__device__ __forceinline__ void fm_queries(const uint32_t (&r)[11], SM& sm, const void* yq, float* sig, float eps_feat,
-                                           float inv_dt, int fi = feat_index<D>()) {
+__device__ __forceinline__ void fm_queries(half2v (&yo)[8], const uint32_t (&r)[11], SM& sm, float* sig,
+                                           float eps_feat, float inv_dt, int fi = feat_index<D>()) {
     if (fi >= Cfg<D>::NF) return;
     const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
     float y[2][8], ss[8];
     conv_silu<D>(r, sm.wq, cgi, y, ss);
-    const uint32_t y0 = 2u * yq_off<D>(8 * tb, 2 * cgi);
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-        *(lds_h2*)(uintptr_t)(lds_addr(yq) + (y0 ^ yq_sx<D>(s)) + s * kYqRow<D>) =
-            half2v{static_cast<_Float16>(y[0][s]), static_cast<_Float16>(y[1][s])};
+    for (int s = 0; s < 8; ++s) yo[s] = half2v{static_cast<_Float16>(y[0][s]), static_cast<_Float16>(y[1][s])};
     const float tot = reduce_scatter8<Cfg<D>::CP>(ss);
     if (cgi < 8) sig[8 * tb + scatter_token(cgi)] = -kLn2 * inv_dt * __builtin_amdgcn_rcpf(fmaf(kLn2Sq, tot, eps_feat));
+}
+template <int D>
+__device__ __forceinline__ void fm_write_q(const half2v (&yo)[8], const void* yq, int fi = feat_index<D>()) {
+    if (fi >= Cfg<D>::NF) return;
+    const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
+    const uint32_t y0 = 2u * yq_off<D>(8 * tb, 2 * cgi);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) *(lds_h2*)(uintptr_t)(lds_addr(yq) + (y0 ^ yq_sx<D>(s)) + s * kYqRow<D>) = yo[s];
 }
 
 // Conv weights (times -log2 e, taps right-aligned into 4 slots), gain, bias,
@@ -848,9 +853,9 @@ __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, const flo
 // z_v^T of every chunk come ready from the feature pass; the queries' features
 // are built here.  The readout of a chunk runs one step behind its s~ and X,
 // so that a step c = 0..nch needs two barriers:
-//   1  key: G tiles, Q^T = U Y^T, U update (chunk c)
+//   1  key: queries' features (c+1, held); G tiles, Q^T = U Y^T, U update (c)
 //      value: z_v^T (c) to shared memory; P~ tiles, X Gamma (c-1)
-//   2  key: S^T = T^T G'^T, s~, X (c); z_k^T (c+1) to shared memory; queries (c+1)
+//   2  key: S^T = T^T G'^T, s~, X (c); z_k^T, y' (c+1) to shared memory
 //      value: P~ Z_v, output, Gamma update (c-1); Z_v fragments (c)
 // Every shared tile is written in one phase and read in the next: y', z_k (c)
 // read in 1 of step c, rewritten in 2; G' (c) written in 1, read in 2; s~, X
@@ -911,7 +916,11 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         fm_load<D, true>(rqq, rq, rsb, t_begin);
         halo_fix<D>(rqq, sm, 0, t_begin);
         tile_store<D>(sm.zkT, zr);
-        fm_queries<D>(rqq, sm, sm.yq, sm.sig[0], p.eps_feat, inv_dt);
+        {
+            half2v yo[8];
+            fm_queries<D>(yo, rqq, sm, sm.sig[0], p.eps_feat, inv_dt);
+            fm_write_q<D>(yo, sm.yq);
+        }
         if (nch > 1) {
             tile_load<D>(zr, zseg + tile2);
             fm_load<D, true>(rqq, rq, rsb, t_begin + L);
@@ -920,6 +929,16 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         for (int c = 0; c <= nch; ++c) {
             // ---- phase 1
             f4 accQ[4];
+            half2v yo[8];  // y' of chunk c+1, written to the tile in phase 2
+            if (c + 1 < nch) {
+                // queries' features of chunk c+1 (sigma~ goes to the buffer of parity c+1,
+                // last read in phase 2 of the previous step); the raw tokens of c+2 follow
+                fm_queries<D>(yo, rqq, sm, sm.sig[(c + 1) & 1], p.eps_feat, inv_dt);
+                if (c + 2 < nch) {
+                    step_fence();
+                    fm_load<D, true>(rqq, rq, rsb, t_begin + static_cast<int64_t>(c + 2) * L);
+                }
+            }
             if (c < nch) {
                 // G tiles -> G'; Q^T = U Y^T (rows m' = 16kw + 4g + jj, columns t); U update
                 const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
@@ -1009,13 +1028,12 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                 }
             }
             if (c + 1 < nch) {
-                // features of chunk c+1: z_k^T from the feature pass, y' and sigma~ built here
+                // features of chunk c+1: z_k^T from the feature pass, y' from phase 1
                 tile_store<D>(sm.zkT, zr);
-                fm_queries<D>(rqq, sm, sm.yq, sm.sig[(c + 1) & 1], p.eps_feat, inv_dt);
+                fm_write_q<D>(yo, sm.yq);
                 if (c + 2 < nch) {
                     step_fence();
                     tile_load<D>(zr, zseg + (c + 2) * tile2);
-                    fm_load<D, true>(rqq, rq, rsb, t_begin + static_cast<int64_t>(c + 2) * L);
                 }
             }
             lds_barrier();
