@@ -314,6 +314,7 @@ struct SmemFwd {
     _Float16 pp[L * RP];          // P~ [t][l] (likewise)
     float sig[2][L];              // sigma~_t, by chunk parity
     float2 aL[MM];                // abar^L
+    float2 aH[MM];                // abar^(L/2)
     float2 pw[16][PWS];           // abar^{k+1}, k = 0..15
     float gain[2 * D], bias[2 * D];
     float wq[D * kMaxW], wk[D * kMaxW];  // conv weights times -log2(e), right-aligned taps (layout: wt_index)
@@ -328,6 +329,7 @@ struct SmemSeg {
     _Float16 ft[M2 * L];
     _Float16 ftl[M2 * L];
     float2 aL[MM];
+    float2 aH[MM];
     float gain[2 * D], bias[2 * D];
     float wk[D * kMaxW];
     uint16_t halo[2][3][D];
@@ -695,29 +697,41 @@ __device__ __forceinline__ void key_update(f4 (&U)[Cfg<D>::RT], const float2* aL
     }
 }
 
-// Gamma <- abar^L Gamma + F^T Z_v, with bZ[kb] = Z_v[32kb + 8g + jj][16vw + i]
-template <int D>
-__device__ __forceinline__ void value_update(f4 (&G)[8], const float2* aL, const half8 (&bZ)[2], const void* ft,
+// Gamma <- abar^L Gamma + F^T Z_v, with bZ[kb] = Z_v[32kb + 8g + jj][16vw + i].
+// The first half of F is abar^(L/2) times the second (F[j] = bbar abar^{L-1-j}),
+// so with F1 = F[L/2 .. L-1]:  Gamma <- abar^(L/2) (abar^(L/2) Gamma + F1^T Z_v0) + F1^T Z_v1,
+// and each fragment of F1 (high and low parts) is read once for both halves:
+// half the shared-memory reads of the plain update for one more complex scaling.
+__device__ __forceinline__ void cscale(f4& x, const float4& a) {
+    const float r0 = x[0], i0 = x[1], r1 = x[2], i1 = x[3];
+    x[0] = a.x * r0 - a.y * i0;
+    x[1] = a.x * i0 + a.y * r0;
+    x[2] = a.z * r1 - a.w * i1;
+    x[3] = a.z * i1 + a.w * r1;
+}
+template <int D, int GRP = 2>
+__device__ __forceinline__ void value_update(f4 (&G)[8], const float2* aH, const half8 (&bZ)[2], const void* ft,
                                              int ln) {
     const int g = ln >> 4;
+    const uint32_t wb = lds_addr(ft) + frag_kb(frag_off(ln), 1);
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-        const float4 a = *reinterpret_cast<const float4*>(&aL[8 * mt + 2 * g]);
-        const float r0 = G[mt][0], i0 = G[mt][1], r1 = G[mt][2], i1 = G[mt][3];
-        G[mt][0] = a.x * r0 - a.y * i0;
-        G[mt][1] = a.x * i0 + a.y * r0;
-        G[mt][2] = a.z * r1 - a.w * i1;
-        G[mt][3] = a.z * i1 + a.w * r1;
-    }
-    const uint32_t off = frag_off(ln);
+    for (int m0 = 0; m0 < 8; m0 += GRP) {
+        half8 fh[GRP], fl[GRP];
+        float4 a[GRP];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t wb = lds_addr(ft) + frag_kb(off, kb);
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            G[mt] = mfma(rd8(wb + 2048 * mt), bZ[kb], G[mt]);
-            G[mt] = mfma(rd8(wb + M2 * L * 2 + 2048 * mt), bZ[kb], G[mt]);
+        for (int u = 0; u < GRP; ++u) {
+            fh[u] = rd8(wb + 2048 * (m0 + u));
+            fl[u] = rd8(wb + M2 * L * 2 + 2048 * (m0 + u));
+            a[u] = *reinterpret_cast<const float4*>(&aH[8 * (m0 + u) + 2 * g]);
         }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int u = 0; u < GRP; ++u) {
+                cscale(G[m0 + u], a[u]);
+                G[m0 + u] = mfma(fh[u], bZ[kb], G[m0 + u]);
+                G[m0 + u] = mfma(fl[u], bZ[kb], G[m0 + u]);
+            }
     }
 }
 
@@ -765,6 +779,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
     copy16(sm.ft, th + kTabFT, M2 * L * 2);
     copy16(sm.ftl, th + kTabFTL, M2 * L * 2);
     if (tid < MM) sm.aL[tid] = reinterpret_cast<const float2*>(th + kTabPw)[(L - 1) * MM + tid];
+    if (tid < MM) sm.aH[tid] = reinterpret_cast<const float2*>(th + kTabPw)[(L / 2 - 1) * MM + tid];
     __syncthreads();
     float* dst = ws + (static_cast<int64_t>(seg) * p.B * p.H + bh) * MM * 2 * D * 2;
     const int rsb = static_cast<int>(p.H * D * 2);  // token stride, bytes
@@ -813,7 +828,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
                 const int ln = tid_now() & 63;
                 half8 bZ[2];
                 load_bz(bZ, vw, sm.zvT[c & 1], ln);
-                value_update<D>(G, sm.aL, bZ, sm.ft, ln);
+                value_update<D>(G, sm.aH, bZ, sm.ft, ln);
             }
             if (c + 1 < nch) {
                 fm_values<D>(rvv, sm, sm.zvT[(c + 1) & 1], c + 2 < nch ? L : n_last, p.eps_norm);
@@ -892,6 +907,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
     copy16(sm.ft, th + kTabFT, M2 * L * 2);
     copy16(sm.ftl, th + kTabFTL, M2 * L * 2);
     if (tid < MM) sm.aL[tid] = reinterpret_cast<const float2*>(th + kTabPw)[(L - 1) * MM + tid];
+    if (tid < MM) sm.aH[tid] = reinterpret_cast<const float2*>(th + kTabPw)[(L / 2 - 1) * MM + tid];
     for (int e = tid; e < 16 * MM; e += NTH) sm.pw[e / MM][e % MM] = reinterpret_cast<const float2*>(th + kTabPw)[e];
     for (int e = tid; e < L * RP * 2 / 16; e += NTH)
         reinterpret_cast<u4*>(sm.gp)[e] = reinterpret_cast<u4*>(sm.pp)[e] = u4{0u, 0u, 0u, 0u};
@@ -1118,7 +1134,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                     const u2 pk = {pack_bf16(accO[tt][0] * dt, accO[tt][1] * dt), pack_bf16(accO[tt][2] * dt, accO[tt][3] * dt)};
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, pk), ob, olane + toff, 0, 0);
                 }
-                value_update<D>(G, sm.aL, bZ, sm.ft, ln2);
+                value_update<D>(G, sm.aH, bZ, sm.ft, ln2);
             }
             if (c < nch && own) load_bz(bZ, vw, sm.zvT, ln2);
             lds_barrier();
