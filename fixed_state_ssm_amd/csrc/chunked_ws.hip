@@ -329,7 +329,6 @@ struct SmemSeg {
     _Float16 ft[M2 * L];
     _Float16 ftl[M2 * L];
     float2 aL[MM];
-    float2 aH[MM];
     float gain[2 * D], bias[2 * D];
     float wk[D * kMaxW];
     uint16_t halo[2][3][D];
@@ -697,11 +696,7 @@ __device__ __forceinline__ void key_update(f4 (&U)[Cfg<D>::RT], const float2* aL
     }
 }
 
-// Gamma <- abar^L Gamma + F^T Z_v, with bZ[kb] = Z_v[32kb + 8g + jj][16vw + i].
-// The first half of F is abar^(L/2) times the second (F[j] = bbar abar^{L-1-j}),
-// so with F1 = F[L/2 .. L-1]:  Gamma <- abar^(L/2) (abar^(L/2) Gamma + F1^T Z_v0) + F1^T Z_v1,
-// and each fragment of F1 (high and low parts) is read once for both halves:
-// half the shared-memory reads of the plain update for one more complex scaling.
+// Complex scaling of the two modes (real, imaginary rows) of an accumulator tile.
 __device__ __forceinline__ void cscale(f4& x, const float4& a) {
     const float r0 = x[0], i0 = x[1], r1 = x[2], i1 = x[3];
     x[0] = a.x * r0 - a.y * i0;
@@ -709,6 +704,30 @@ __device__ __forceinline__ void cscale(f4& x, const float4& a) {
     x[2] = a.z * r1 - a.w * i1;
     x[3] = a.z * i1 + a.w * r1;
 }
+
+// Gamma <- abar^L Gamma + F^T Z_v, with bZ[kb] = Z_v[32kb + 8g + jj][16vw + i]: one
+// complex scaling and every fragment of F (for the feature pass, bound by VALU issue).
+template <int D>
+__device__ __forceinline__ void value_update_plain(f4 (&G)[8], const float2* aL, const half8 (&bZ)[2],
+                                                   const void* ft, int ln) {
+    const int g = ln >> 4;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) cscale(G[mt], *reinterpret_cast<const float4*>(&aL[8 * mt + 2 * g]));
+    const uint32_t off = frag_off(ln);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t wb = lds_addr(ft) + frag_kb(off, kb);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            G[mt] = mfma(rd8(wb + 2048 * mt), bZ[kb], G[mt]);
+            G[mt] = mfma(rd8(wb + M2 * L * 2 + 2048 * mt), bZ[kb], G[mt]);
+        }
+    }
+}
+// The same for the forward, bound by shared-memory bandwidth there.  The first half of F is abar^(L/2) times the second (F[j] = bbar abar^{L-1-j}),
+// so with F1 = F[L/2 .. L-1]:  Gamma <- abar^(L/2) (abar^(L/2) Gamma + F1^T Z_v0) + F1^T Z_v1,
+// and each fragment of F1 (high and low parts) is read once for both halves:
+// half the shared-memory reads of the plain update for one more complex scaling.
 template <int D, int GRP = 2>
 __device__ __forceinline__ void value_update(f4 (&G)[8], const float2* aH, const half8 (&bZ)[2], const void* ft,
                                              int ln) {
@@ -779,7 +798,6 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
     copy16(sm.ft, th + kTabFT, M2 * L * 2);
     copy16(sm.ftl, th + kTabFTL, M2 * L * 2);
     if (tid < MM) sm.aL[tid] = reinterpret_cast<const float2*>(th + kTabPw)[(L - 1) * MM + tid];
-    if (tid < MM) sm.aH[tid] = reinterpret_cast<const float2*>(th + kTabPw)[(L / 2 - 1) * MM + tid];
     __syncthreads();
     float* dst = ws + (static_cast<int64_t>(seg) * p.B * p.H + bh) * MM * 2 * D * 2;
     const int rsb = static_cast<int>(p.H * D * 2);  // token stride, bytes
@@ -828,7 +846,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
                 const int ln = tid_now() & 63;
                 half8 bZ[2];
                 load_bz(bZ, vw, sm.zvT[c & 1], ln);
-                value_update<D>(G, sm.aH, bZ, sm.ft, ln);
+                value_update_plain<D>(G, sm.aL, bZ, sm.ft, ln);
             }
             if (c + 1 < nch) {
                 fm_values<D>(rvv, sm, sm.zvT[(c + 1) & 1], c + 2 < nch ? L : n_last, p.eps_norm);
