@@ -2,13 +2,16 @@
 //
 // One block of 4 waves per (b, h).  Wave 0 first builds the token's features
 // (conv over the tail and the new token, SiLU feature map, per-half RMSNorm)
-// into LDS, shifts the conv tail, and evaluates the ZOH coefficients of all M
-// modes in fp64 (one mode per lane).  Then every wave streams its quarter of
+// into LDS and shifts the conv tail; wave 1 evaluates the ZOH coefficients of
+// all M modes (one mode per lane).  Then every wave streams its quarter of
 // the M rows of the complex state [M][2d]: a row is read once as float4s,
-// updated, reduced to s_m over the key half with a wave butterfly, read out
+// updated, reduced to s_m over the key half with a lane reduction, read out
 // into per-lane partial sums of Re(s_m Gamma_m), and written back in place.
 // The state sweep (2 x 128 KiB per (b, h) at d = 128, M = 64) is the whole
-// cost; all loads of a wave's rows are issued before any of them is used.
+// cost: each wave streams its rows one at a time with few live registers, so
+// that many workgroups share a CU and hide each other's memory latency, and
+// the ZOH coefficients (wave 1, fp32 with the phase reduced in fp64) are built
+// while wave 0 builds the features.
 #include "common.h"
 #include "launch.h"
 
@@ -16,6 +19,53 @@ namespace idattn {
 
 namespace {
 
+// ZOH coefficients of one mode, abar = exp(Delta lambda) and
+// bbar = (exp(Delta lambda) - 1) / lambda * B (Delta B when lambda = 0), with
+// Delta and the phase Delta Im(lambda) formed and reduced modulo 2 pi in fp64 and
+// the rest in fp32 (about 1e-7 relative).
+__device__ __forceinline__ float4 zoh_coef(double dt, float lre, float lim, float bre, float bim) {
+    const double y64 = dt * static_cast<double>(lim);
+    const double turns = rint(y64 * 0.15915494309189535);  // 1 / (2 pi)
+    const float y = static_cast<float>(fma(-turns, 6.283185307179586, y64));
+    const float x = static_cast<float>(dt * static_cast<double>(lre));
+    float sy, cy;
+    sincosf(y, &sy, &cy);
+    const float ex = expf(x);
+    const float sh = sinf(0.5f * y);
+    const float em1_re = expm1f(x) * cy - 2.f * sh * sh;  // Re(exp(z) - 1) without cancellation
+    const float em1_im = ex * sy;
+    const float l2 = lre * lre + lim * lim;
+    float qr, qi;  // (exp(z) - 1) / lambda
+    if (l2 == 0.f) {
+        qr = static_cast<float>(dt);
+        qi = 0.f;
+    } else {
+        qr = (em1_re * lre + em1_im * lim) / l2;
+        qi = (em1_im * lre - em1_re * lim) / l2;
+    }
+    return make_float4(ex * cy, ex * sy, qr * bre - qi * bim, qr * bim + qi * bre);
+}
+
+// Sum over the 64 lanes of a wave, every lane receiving the total: lane swaps by
+// DPP within rows of 16 (xor 1, xor 2, rotate by 4 and 8), then across rows with
+// v_permlane16_swap and v_permlane32_swap.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float wave_total(float x) {
+    x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_f<0x124>(x);  // row_ror:4
+    x += dpp_f<0x128>(x);  // row_ror:8
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// FJ = float4 chunks of a state row per lane (d / 64, at least 1); RPW = rows per
+// wave (M / 4).
 template <bool BF16, int FJ, int RPW>
 __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_params prm,
                                                           const void* __restrict__ q_t,
@@ -23,8 +73,6 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
                                                           const void* __restrict__ v_t,
                                                           void* __restrict__ o_t, float* state,
                                                           void* tail) {
-    // FJ = float4 chunks of a state row per lane (d / 64, at least 1);
-    // RPW = rows per wave (M / 4).
     __shared__ float xq_s[128], zk_s[128], zv_s[128];
     __shared__ float4 coef_s[64];
     __shared__ float part_s[4][128];
@@ -34,18 +82,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
     const int64_t h = bh % p.H;
     const int d = static_cast<int>(p.d), W = static_cast<int>(p.W);
     const int64_t M = p.M;
-
-    // ---- load this wave's state rows first: the long-latency part
     const int nf = d;  // float4 chunks per row (4d floats)
-    float4 row[RPW][FJ];
     float4* st4 = reinterpret_cast<float4*>(state) + bh * M * nf;
-#pragma unroll
-    for (int rr = 0; rr < RPW; ++rr)
-#pragma unroll
-        for (int j = 0; j < FJ; ++j) {
-            const int f = lane + kWave * j;
-            row[rr][j] = f < nf ? st4[(w * RPW + rr) * nf + f] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
 
     if (w == 0) {
         // features of the new token; lane owns channels lane and lane + 64
@@ -114,22 +152,28 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
                 zv_s[c] = fmaf(prm.gain[h * 2 * d + d + c] * vv[j], rv, prm.bias[h * 2 * d + d + c]);
             }
         }
-        if (lane < M) {
-            const Zoh z = zoh_mode(prm.log_dt[h], prm.A[(h * M + lane) * 2], prm.A[(h * M + lane) * 2 + 1],
-                                   prm.Bc[(h * M + lane) * 2], prm.Bc[(h * M + lane) * 2 + 1]);
-            coef_s[lane] = make_float4(static_cast<float>(z.ar), static_cast<float>(z.ai),
-                                       static_cast<float>(z.br), static_cast<float>(z.bi));
-        }
+    } else if (w == 1 && lane < M) {
+        // ZOH coefficients of mode lane, while wave 0 builds the features
+        const double dt = exp(static_cast<double>(prm.log_dt[h]));
+        coef_s[lane] = zoh_coef(dt, prm.A[(h * M + lane) * 2], prm.A[(h * M + lane) * 2 + 1],
+                                prm.Bc[(h * M + lane) * 2], prm.Bc[(h * M + lane) * 2 + 1]);
     }
     __syncthreads();
 
-    // ---- state sweep
+    // ---- state sweep: one row at a time per wave, so that few registers are live
+    // and many workgroups share a CU; they hide each other's memory latency
     float acc[FJ][2];
 #pragma unroll
     for (int j = 0; j < FJ; ++j) acc[j][0] = acc[j][1] = 0.f;
-#pragma unroll
+#pragma unroll 1
     for (int rr = 0; rr < RPW; ++rr) {
         const int m = w * RPW + rr;
+        float4 row[FJ];
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+            const int f = lane + kWave * j;
+            row[j] = f < nf ? st4[m * nf + f] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
         const float4 cf = coef_s[m];
         float pr = 0.f, pi = 0.f;
         // complex columns 2f and 2f+1; columns < d belong to U, the rest to Gamma
@@ -141,30 +185,29 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
                 const bool key = col < d;
                 const float in0 = key ? zk_s[col] : zv_s[col - d];
                 const float in1 = key ? zk_s[col + 1] : zv_s[col + 1 - d];
-                float4 x = row[rr][j];
+                const float4 x = row[j];
                 const float r0 = fmaf(cf.x, x.x, fmaf(-cf.y, x.y, cf.z * in0));
                 const float i0 = fmaf(cf.x, x.y, fmaf(cf.y, x.x, cf.w * in0));
                 const float r1 = fmaf(cf.x, x.z, fmaf(-cf.y, x.w, cf.z * in1));
                 const float i1 = fmaf(cf.x, x.w, fmaf(cf.y, x.z, cf.w * in1));
-                x = make_float4(r0, i0, r1, i1);
-                row[rr][j] = x;
+                row[j] = make_float4(r0, i0, r1, i1);
                 if (key) {
                     pr = fmaf(xq_s[col], r0, fmaf(xq_s[col + 1], r1, pr));
                     pi = fmaf(xq_s[col], i0, fmaf(xq_s[col + 1], i1, pi));
                 }
             }
         }
-        pr = wave_sum(pr);
-        pi = wave_sum(pi);
+        pr = wave_total(pr);
+        pi = wave_total(pi);
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
             const int f = lane + kWave * j;
             if (f < nf && 2 * f >= d) {
-                const float4 x = row[rr][j];
+                const float4 x = row[j];
                 acc[j][0] = fmaf(pr, x.x, fmaf(-pi, x.y, acc[j][0]));
                 acc[j][1] = fmaf(pr, x.z, fmaf(-pi, x.w, acc[j][1]));
             }
-            if (f < nf) st4[m * nf + f] = row[rr][j];
+            if (f < nf) st4[m * nf + f] = row[j];
         }
     }
 #pragma unroll
