@@ -887,9 +887,9 @@ __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, const flo
 // are built here.  The readout of a chunk runs one step behind its s~ and X,
 // so that a step c = 0..nch needs two barriers:
 //   1  key: queries' features (c+1, held); G tiles, Q^T = U Y^T, U update (c)
-//      value: z_v^T (c) to shared memory; P~ tiles, X Gamma (c-1)
+//      value: z_v^T (c) to shared memory; P~ tiles, X Gamma, Gamma update (c-1)
 //   2  key: S^T = T^T G'^T, s~, X (c); z_k^T, y' (c+1) to shared memory
-//      value: P~ Z_v, output, Gamma update (c-1); Z_v fragments (c)
+//      value: P~ Z_v, output (c-1); Z_v fragments (c)
 // Every shared tile is written in one phase and read in the next: y', z_k (c)
 // read in 1 of step c, rewritten in 2; G' (c) written in 1, read in 2; s~, X
 // (c) written in 2 of step c, read in 1 of step c+1; P~ (c-1) written in 1,
@@ -1089,7 +1089,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         for (int c = 0; c <= nch; ++c) {
             const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
             f4 accO[4];
-            // ---- phase 1: z_v^T (c); P~ tiles, X Gamma (c-1)
+            // ---- phase 1: z_v^T (c); P~ tiles, X Gamma, Gamma update (c-1)
             if (c < nch) tile_store<D>(sm.zvT, zr);
             const int ln = tid_now() & 63;
             const uint32_t xoff = frag256_off(ln);  // s~ and X rows i, K block 0
@@ -1131,9 +1131,11 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) accO[tt] = mfma(bG, rd8(xb + 2 * 16 * tt * M2), accO[tt]);
                 }
+                // Gamma update with chunk c-1, once X Gamma has read the state before it
+                value_update<D>(G, sm.aH, bZ, sm.ft, ln);
             }
             lds_barrier();
-            // ---- phase 2: o^T += Z_v^T P~^T, Delta o, Gamma update (c-1); Z_v fragments (c)
+            // ---- phase 2: o^T += Z_v^T P~^T, Delta o (c-1); Z_v fragments (c)
             if (c + 1 < nch) tile_load<D>(zr, zseg + (c + 1) * tile2 + D * L);
             const int ln2 = tid_now() & 63;
             if (c >= 1 && own) {
@@ -1152,7 +1154,6 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                     const u2 pk = {pack_bf16(accO[tt][0] * dt, accO[tt][1] * dt), pack_bf16(accO[tt][2] * dt, accO[tt][3] * dt)};
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, pk), ob, olane + toff, 0, 0);
                 }
-                value_update<D>(G, sm.aH, bZ, sm.ft, ln2);
             }
             if (c < nch && own) load_bz(bZ, vw, sm.zvT, ln2);
             lds_barrier();
