@@ -882,12 +882,36 @@ __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, const flo
     }
 }
 
+// One causal tile (tt, kt) of P~'[t][k] = sum_m' s~[t][m'] T[k][m'] (lane (g, i) of the
+// T operand holds k = 16 kt + 15 - i), un-skewed into P~[t][t - k].  K = m' in perm32
+// order on both sides: s~ as stored, F^T rows 32kb + 4g + e and 32kb + 16 + 4g + e.
+template <class SM>
+__device__ __forceinline__ void p_tile(const SM& sm, int qt, int ln, uint32_t xoff) {
+    constexpr uint32_t dl = M2 * L * 2;
+    const int g = ln >> 4, i = ln & 15;
+    const int tt = tile_tt(qt), kt = tile_kt(qt);
+    const uint32_t br0 = opaque(lds_addr(sm.ft) + 2 * o128(4 * g + (i >> 2), L - 16 - 16 * kt + 4 * (i & 3)));
+    const uint32_t br1 = opaque(lds_addr(sm.ft) + 2 * o128(16 + 4 * g + (i >> 2), L - 16 - 16 * kt + 4 * (i & 3)));
+    f4 accP = {};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const half8 a = rd8(lds_addr(sm.sc) + frag_kb(xoff, kb) + 2 * 16 * tt * M2);
+        accP = mfma(a, cat(rd4t(br0 + 4096 * kb), rd4t(br1 + 4096 * kb)), accP);
+        accP = mfma(a, cat(rd4t(br0 + 4096 * kb + dl), rd4t(br1 + 4096 * kb + dl)), accP);
+    }
+    const uint32_t ps = opaque(lds_addr(sm.pp) + 2 * ((16 * tt + 4 * g) * (RP + 1) - 16 * kt - 15 + i));
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+        if (16 * kt + 15 - i <= 16 * tt + 4 * g + jj) wr1(ps + 2 * (RP + 1) * jj, accP[jj]);
+}
+
 // Full chunk loop of one segment: grid B*H*S, block (bh, seg).  z_k^T and
 // z_v^T of every chunk come ready from the feature pass; the queries' features
 // are built here.  The readout of a chunk runs one step behind its s~ and X,
 // so that a step c = 0..nch needs two barriers:
-//   1  key: queries' features (c+1, held); G tiles, Q^T = U Y^T, U update (c)
-//      value: z_v^T (c) to shared memory; P~ tiles, X Gamma, Gamma update (c-1)
+//   1  key: queries' features (c+1, held); G tiles, Q^T = U Y^T, U update (c);
+//           two P~ tiles (c-1)
+//      value: z_v^T (c) to shared memory; the other P~ tiles, X Gamma, Gamma update (c-1)
 //   2  key: S^T = T^T G'^T, s~, X (c); z_k^T, y' (c+1) to shared memory
 //      value: P~ Z_v, output (c-1); Z_v fragments (c)
 // Every shared tile is written in one phase and read in the next: y', z_k (c)
@@ -1009,6 +1033,10 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                 }
                 key_update<D>(U, sm.aL, kw, sm.zkT, sm.ft, ln);
             }
+            if (c >= 1 && (kw == 2 || kw == 3)) {
+                const int ln = tid_now() & 63;
+                p_tile(sm, kw + 6, ln, frag256_off(ln));  // P~ tiles 8, 9 of chunk c-1
+            }
             lds_barrier();
             // ---- phase 2
             if (c < nch) {
@@ -1093,32 +1121,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             if (c < nch) tile_store<D>(sm.zvT, zr);
             const int ln = tid_now() & 63;
             const uint32_t xoff = frag256_off(ln);  // s~ and X rows i, K block 0
-            if (c >= 1) {
-                const int g = ln >> 4, i = ln & 15;
-                // P~'[t][k] = sum_m' sc[t][m'] T[k][m'] tiles (lane (g, i) of the T operand
-                // holds k = 16 kt + 15 - i), un-skewed into P~[t][t - k]; K = m' in perm32
-                // order on both sides: s~ as stored, F^T rows 32kb + 4g + e and 32kb + 16 + 4g + e
-#pragma unroll
-                for (int slot = 0; slot < 2; ++slot) {
-                    const int qt = vw + 8 * slot;
-                    if (qt < 10) {
-                        const int tt = tile_tt(qt), kt = tile_kt(qt);
-                        const uint32_t br0 = opaque(lds_addr(sm.ft) + 2 * o128(4 * g + (i >> 2), L - 16 - 16 * kt + 4 * (i & 3)));
-                        const uint32_t br1 = opaque(lds_addr(sm.ft) + 2 * o128(16 + 4 * g + (i >> 2), L - 16 - 16 * kt + 4 * (i & 3)));
-                        f4 accP = {};
-#pragma unroll
-                        for (int kb = 0; kb < 4; ++kb) {
-                            const half8 a = rd8(lds_addr(sm.sc) + frag_kb(xoff, kb) + 2 * 16 * tt * M2);
-                            accP = mfma(a, cat(rd4t(br0 + 4096 * kb), rd4t(br1 + 4096 * kb)), accP);
-                            accP = mfma(a, cat(rd4t(br0 + 4096 * kb + dl), rd4t(br1 + 4096 * kb + dl)), accP);
-                        }
-                        const uint32_t ps = opaque(lds_addr(sm.pp) + 2 * ((16 * tt + 4 * g) * (RP + 1) - 16 * kt - 15 + i));
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj)
-                            if (16 * kt + 15 - i <= 16 * tt + 4 * g + jj) wr1(ps + 2 * (RP + 1) * jj, accP[jj]);
-                    }
-                }
-            }
+            if (c >= 1) p_tile(sm, vw, ln, xoff);  // P~ tiles 0..7 of chunk c-1 (8, 9: key waves 2, 3)
             if (c >= 1 && own) {
                 // o^T = Gamma_prev^T X^T (c-block vw: lane (g, i) of tile tt holds
                 // o[16tt + i][16vw + 4g + jj], four consecutive channels of one token)
