@@ -912,8 +912,8 @@ __device__ __forceinline__ void p_tile(const SM& sm, int qt, int ln, uint32_t xo
 //   1  key: queries' features (c+1, held); G tiles, Q^T = U Y^T, U update (c);
 //           two P~ tiles (c-1)
 //      value: z_v^T (c) to shared memory; the other P~ tiles, X Gamma, Gamma update (c-1)
-//   2  key: S^T = T^T G'^T, s~, X (c); z_k^T, y' (c+1) to shared memory
-//      value: P~ Z_v, output (c-1); Z_v fragments (c)
+//   2  key: S^T = T^T G'^T, s~, X (c); y' (c+1) to shared memory
+//      value: z_k^T (c+1) to shared memory; P~ Z_v, output (c-1); Z_v fragments (c)
 // Every shared tile is written in one phase and read in the next: y', z_k (c)
 // read in 1 of step c, rewritten in 2; G' (c) written in 1, read in 2; s~, X
 // (c) written in 2 of step c, read in 1 of step c+1; P~ (c-1) written in 1,
@@ -966,23 +966,17 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         // ---------------- key waves
         const int kw = w;
         f4 U[RT];
-        u_load<D>(U, src, kw);  // before the tile and token loads, which are waited for first
+        u_load<D>(U, src, kw);  // before the token loads, which are waited for first
         const __amdgpu_buffer_rsrc_t rq = seq_rsrc<D>(q, b, h, N, H, t_end);
-        u4 zr[kTilePieces<D>];  // z_k^T of the chunk after the current one
-        uint32_t rqq[11];       // raw queries of the chunk after that
-        tile_load<D>(zr, zseg);
+        uint32_t rqq[11];  // raw queries of the chunk after the next
         fm_load<D, true>(rqq, rq, rsb, t_begin);
         halo_fix<D>(rqq, sm, 0, t_begin);
-        tile_store<D>(sm.zkT, zr);
         {
             half2v yo[8];
             fm_queries<D>(yo, rqq, sm, sm.sig[0], p.eps_feat, inv_dt);
             fm_write_q<D>(yo, sm.yq);
         }
-        if (nch > 1) {
-            tile_load<D>(zr, zseg + tile2);
-            fm_load<D, true>(rqq, rq, rsb, t_begin + L);
-        }
+        if (nch > 1) fm_load<D, true>(rqq, rq, rsb, t_begin + L);
         lds_barrier();  // chunk 0 features
         for (int c = 0; c <= nch; ++c) {
             // ---- phase 1
@@ -1089,15 +1083,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                     wr4(s_st + 2 * 16 * tt * M2, sv[0], sv[1], sv[2], sv[3]);
                 }
             }
-            if (c + 1 < nch) {
-                // features of chunk c+1: z_k^T from the feature pass, y' from phase 1
-                tile_store<D>(sm.zkT, zr);
-                fm_write_q<D>(yo, sm.yq);
-                if (c + 2 < nch) {
-                    step_fence();
-                    tile_load<D>(zr, zseg + (c + 2) * tile2);
-                }
-            }
+            if (c + 1 < nch) fm_write_q<D>(yo, sm.yq);  // y' of chunk c+1, built in phase 1
             lds_barrier();
         }
         if (seg == S - 1 && state_out != nullptr)
@@ -1111,7 +1097,11 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         if (own) g_load<D>(G, src, vw);  // before the tile loads, which are waited for first
         const __amdgpu_buffer_rsrc_t ob = seq_rsrc<D>(o, b, h, N, H, t_end);
         u4 zr[kTilePieces<D>];  // z_v^T of the next chunk to enter
+        u4 kr[kTilePieces<D>];  // z_k^T of the chunk after it
+        tile_load<D>(kr, zseg);
         tile_load<D>(zr, zseg + D * L);
+        tile_store<D>(sm.zkT, kr);
+        if (nch > 1) tile_load<D>(kr, zseg + tile2);
         lds_barrier();  // chunk 0 features
         half8 bZ[2];    // Z_v fragments of the chunk whose readout comes next
         for (int c = 0; c <= nch; ++c) {
@@ -1138,8 +1128,12 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                 value_update<D>(G, sm.aH, bZ, sm.ft, ln);
             }
             lds_barrier();
-            // ---- phase 2: o^T += Z_v^T P~^T, Delta o (c-1); Z_v fragments (c)
-            if (c + 1 < nch) tile_load<D>(zr, zseg + (c + 1) * tile2 + D * L);
+            // ---- phase 2: z_k^T (c+1); o^T += Z_v^T P~^T, Delta o (c-1); Z_v fragments (c)
+            if (c + 1 < nch) {
+                tile_store<D>(sm.zkT, kr);  // read by the key waves in phase 1 of step c+1
+                tile_load<D>(zr, zseg + (c + 1) * tile2 + D * L);
+                if (c + 2 < nch) tile_load<D>(kr, zseg + (c + 2) * tile2);
+            }
             const int ln2 = tid_now() & 63;
             if (c >= 1 && own) {
                 const int64_t tp = t0 - L;  // first token of chunk c-1
