@@ -68,8 +68,11 @@ def committed_traffic(config: str, algo: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    # the GPU's clocks take several dozen back-to-back launches to settle; a short
+    # warmup times that ramp (about 15 % slower at the 1.3B shape) instead of the
+    # steady state
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="1p3b", choices=["125m", "1p3b", "14k"])
     ap.add_argument("--algo", default="auto", choices=["auto", "sequential", "chunked"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
