@@ -817,6 +817,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
         for (int c = 0; c < nch; ++c) {
             const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
             tile_copy_out<D>(sm.zkT[c & 1], zseg + c * 2 * D * L);
+            tile_copy_out<D>(sm.zvT[c & 1], zseg + c * 2 * D * L + D * L);  // both tiles: the value waves are the longer role
             if (upd) key_update<D>(U, sm.aL, kw, sm.zkT[c & 1], sm.ft, tid_now() & 63);
             if (c + 1 < nch) {
                 fm_keys<D>(rkk, sm, sm.zkT[(c + 1) & 1], c + 2 < nch ? L : n_last, p.eps_feat, p.eps_norm);
@@ -841,7 +842,6 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
         lds_barrier();  // chunk 0 features
         for (int c = 0; c < nch; ++c) {
             const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
-            tile_copy_out<D>(sm.zvT[c & 1], zseg + c * 2 * D * L + D * L);
             if (own) {
                 const int ln = tid_now() & 63;
                 half8 bZ[2];
