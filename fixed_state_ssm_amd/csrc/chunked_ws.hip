@@ -263,18 +263,31 @@ __device__ __forceinline__ void cpow(double dt, float lre, float lim, double n, 
     pi = e * sy;
 }
 
-// grid (H, 16), 256 threads: one (k, m) per thread.
+// grid (H, 17), 256 threads.  Blocks y < 16: one (k, m) per thread, with
+// abar^{k+1} = abar^k abar; block y = 16: abar^Lseg (threads 0..63) and
+// abar^-back (64..127), so that no thread evaluates more than one power
+// besides the ZOH step.
 __global__ __launch_bounds__(256) void zoh_tables_kernel(Problem p, idattn_params prm, int64_t Lseg, int back,
                                                          uint8_t* __restrict__ tab) {
     const int64_t h = blockIdx.x;
     uint8_t* th = tab + h * kTabBytes;
     const int m = threadIdx.x & (MM - 1);
-    const int k = 4 * static_cast<int>(blockIdx.y) + (threadIdx.x >> 6);
     const float log_dt = prm.log_dt[h];
     const float lre = prm.A[(h * MM + m) * 2], lim = prm.A[(h * MM + m) * 2 + 1];
-    const Zoh z = zoh_mode(log_dt, lre, lim, prm.Bc[(h * MM + m) * 2], prm.Bc[(h * MM + m) * 2 + 1]);
     const double dt = exp(static_cast<double>(log_dt));
     double pr, pi;
+    if (blockIdx.y == 16) {
+        const int which = threadIdx.x >> 6;
+        if (which >= 2) return;
+        cpow(dt, lre, lim, which == 0 ? static_cast<double>(Lseg) : -static_cast<double>(back), pr, pi);
+        reinterpret_cast<float2*>(th + (which == 0 ? kTabPwSeg : kTabPwBack))[m] =
+            make_float2(static_cast<float>(pr), static_cast<float>(pi));
+        if (threadIdx.x == 0)
+            reinterpret_cast<float2*>(th + kTabHc)[0] = make_float2(static_cast<float>(dt), static_cast<float>(1.0 / dt));
+        return;
+    }
+    const int k = 4 * static_cast<int>(blockIdx.y) + (threadIdx.x >> 6);
+    const Zoh z = zoh_mode(log_dt, lre, lim, prm.Bc[(h * MM + m) * 2], prm.Bc[(h * MM + m) * 2 + 1]);
     cpow(dt, lre, lim, static_cast<double>(k), pr, pi);  // abar^k
     const double tv[2] = {z.br * pr - z.bi * pi, z.br * pi + z.bi * pr};
     _Float16* ft = reinterpret_cast<_Float16*>(th + kTabFT);
@@ -285,16 +298,8 @@ __global__ __launch_bounds__(256) void zoh_tables_kernel(Problem p, idattn_param
         ft[o128(2 * m + part, L - 1 - k)] = hi;
         ftl[o128(2 * m + part, L - 1 - k)] = static_cast<_Float16>(static_cast<float>(tv[part] - static_cast<double>(hi)));
     }
-    cpow(dt, lre, lim, static_cast<double>(k + 1), pr, pi);
-    reinterpret_cast<float2*>(th + kTabPw)[k * MM + m] = make_float2(static_cast<float>(pr), static_cast<float>(pi));
-    if (blockIdx.y == 0 && threadIdx.x < MM) {
-        cpow(dt, lre, lim, static_cast<double>(Lseg), pr, pi);
-        reinterpret_cast<float2*>(th + kTabPwSeg)[m] = make_float2(static_cast<float>(pr), static_cast<float>(pi));
-        cpow(dt, lre, lim, -static_cast<double>(back), pr, pi);
-        reinterpret_cast<float2*>(th + kTabPwBack)[m] = make_float2(static_cast<float>(pr), static_cast<float>(pi));
-        if (threadIdx.x == 0)
-            reinterpret_cast<float2*>(th + kTabHc)[0] = make_float2(static_cast<float>(dt), static_cast<float>(1.0 / dt));
-    }
+    reinterpret_cast<float2*>(th + kTabPw)[k * MM + m] =
+        make_float2(static_cast<float>(pr * z.ar - pi * z.ai), static_cast<float>(pr * z.ai + pi * z.ar));
 }
 
 // ------------------------------------------------------------------ shared memory
@@ -642,6 +647,101 @@ __device__ __forceinline__ void g_store(const f4 (&G)[8], float* dst, const floa
         }
 }
 
+// Segment end states and carries in the workspace are kept in lane order:
+// each lane's accumulator tiles as consecutive float4s, [key wave][tile][lane]
+// for U (D/16 tiles per wave, 128 D floats) followed by [value wave][tile][lane]
+// for Gamma (8 tiles per value wave 0..D/16-1, 128 D floats), so that they are
+// stored and loaded with coalesced 16-byte accesses.
+template <int D>
+__device__ __forceinline__ void u_load_lane(f4 (&U)[Cfg<D>::RT], const float* src, int kw) {
+    const f4* s4 = reinterpret_cast<const f4*>(src) + (kw * Cfg<D>::RT) * 64 + (threadIdx.x & 63);
+#pragma unroll
+    for (int rt = 0; rt < Cfg<D>::RT; ++rt) U[rt] = s4[64 * rt];
+}
+template <int D>
+__device__ __forceinline__ void u_store_lane(const f4 (&U)[Cfg<D>::RT], float* dst, int kw) {
+    f4* d4 = reinterpret_cast<f4*>(dst) + (kw * Cfg<D>::RT) * 64 + (threadIdx.x & 63);
+#pragma unroll
+    for (int rt = 0; rt < Cfg<D>::RT; ++rt) d4[64 * rt] = U[rt];
+}
+template <int D>
+__device__ __forceinline__ void g_load_lane(f4 (&G)[8], const float* src, int vw) {
+    const f4* s4 = reinterpret_cast<const f4*>(src + 128 * D) + (vw * 8) * 64 + (threadIdx.x & 63);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) G[mt] = s4[64 * mt];
+}
+template <int D>
+__device__ __forceinline__ void g_store_lane(const f4 (&G)[8], float* dst, int vw) {
+    f4* d4 = reinterpret_cast<f4*>(dst + 128 * D) + (vw * 8) * 64 + (threadIdx.x & 63);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) d4[64 * mt] = G[mt];
+}
+
+// Carry chain folded into the forward (few segments): the state entering
+// segment seg is C <- abar^Lseg C + E_j over the end states E_0..E_{seg-1} of
+// the segments before it (each from a zero start, in lane order), C =
+// state_in (or zero) at first.  A few tiles at a time, every E_j is loaded (address clamped to E_0
+// past seg) before any is combined, so that the loads overlap; the combine of
+// a j >= seg is discarded.  U: the real and imaginary rows of a mode sit in
+// lanes i, i ^ 1; Gamma: in elements 2q, 2q + 1 of a lane.
+constexpr int kFoldMax = 4;  // largest segment count folded into the forward
+template <int D, int TG>
+__device__ __forceinline__ void u_fold(f4 (&U)[Cfg<D>::RT], const float* e0, int64_t estride, int seg,
+                                       const float2* aseg, int kw) {
+    constexpr int RT = Cfg<D>::RT;
+    const int i = threadIdx.x & 15;
+    const float2 a = aseg[(16 * kw + i) >> 1];
+    const float as = (i & 1) ? a.y : -a.y;
+#pragma unroll
+    for (int rt = 0; rt < RT; rt += TG) {
+        f4 E[kFoldMax - 1][TG];
+#pragma unroll
+        for (int j = 0; j < kFoldMax - 1; ++j)
+#pragma unroll
+            for (int r = 0; r < TG; ++r)
+                E[j][r] = reinterpret_cast<const f4*>(e0 + (j < seg ? j : 0) * estride)[(kw * RT + rt + r) * 64 +
+                                                                                        (threadIdx.x & 63)];
+#pragma unroll
+        for (int j = 0; j < kFoldMax - 1; ++j)
+#pragma unroll
+            for (int r = 0; r < TG; ++r)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float u = U[rt + r][jj];
+                    const float n = fmaf(a.x, u, fmaf(dpp_mov<0xB1>(u), as, E[j][r][jj]));
+                    U[rt + r][jj] = j < seg ? n : u;
+                }
+    }
+}
+template <int D, int TG>
+__device__ __forceinline__ void g_fold(f4 (&G)[8], const float* e0, int64_t estride, int seg, const float2* aseg,
+                                       int vw) {
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int mt = 0; mt < 8; mt += TG) {
+        f4 E[kFoldMax - 1][TG];
+#pragma unroll
+        for (int j = 0; j < kFoldMax - 1; ++j)
+#pragma unroll
+            for (int r = 0; r < TG; ++r)
+                E[j][r] = reinterpret_cast<const f4*>(e0 + (j < seg ? j : 0) * estride +
+                                                      128 * D)[(vw * 8 + mt + r) * 64 + (threadIdx.x & 63)];
+#pragma unroll
+        for (int j = 0; j < kFoldMax - 1; ++j)
+#pragma unroll
+            for (int r = 0; r < TG; ++r)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const float2 av = aseg[8 * (mt + r) + 2 * g + q];
+                    const float gr = G[mt + r][2 * q], gi = G[mt + r][2 * q + 1];
+                    const float nr = fmaf(av.x, gr, fmaf(-av.y, gi, E[j][r][2 * q]));
+                    const float ni = fmaf(av.x, gi, fmaf(av.y, gr, E[j][r][2 * q + 1]));
+                    G[mt + r][2 * q] = j < seg ? nr : gr;
+                    G[mt + r][2 * q + 1] = j < seg ? ni : gi;
+                }
+    }
+}
+
 // Lane byte offset, within a swizzled [rows][64] tile, of the fragment read of
 // row R0 + i at column chunk g (R0 any multiple of 16).  Column chunk 4kb + g
 // is the same offset with bit 6 flipped: the swizzle XORs the low three chunk
@@ -828,7 +928,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
             }
             lds_barrier();
         }
-        if (upd) u_store<D>(U, dst, nullptr, kw);
+        if (upd) u_store_lane<D>(U, dst, kw);
     } else {
         const int vw = w - 8;
         const bool own = upd && vw < D / 16;
@@ -857,28 +957,83 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
             }
             lds_barrier();
         }
-        if (own) g_store<D>(G, dst, nullptr, vw);
+        if (own) g_store_lane<D>(G, dst, vw);
     }
 }
 
-// Carry chain over segments, one thread per complex state element:
-// ws[seg] <- state entering segment seg+1.
+// Carry chain over segments (states in lane order), four complex state
+// elements (eight floats, two lanes' float4) per thread: ws[seg] <- state
+// entering segment seg+1.  The end states of up to eight segments are loaded
+// before any of them is combined, so that the loads overlap instead of forming
+// a chain of dependent round trips.  state_in is read in its own layout.
 __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, const float* __restrict__ state_in,
                                                             const uint8_t* __restrict__ tab,
                                                             float* __restrict__ ws, int S) {
-    const int64_t D2 = 2 * p.d;
-    const int64_t total = p.B * p.H * MM * D2;
+    constexpr int kBatch = 8;
+    const int D = static_cast<int>(p.d);
+    const int64_t per = 32 * D;  // threads per (b, h)
     const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (e >= total) return;
-    const int64_t m = (e / D2) % MM;
-    const int64_t h = (e / (D2 * MM)) % p.H;
-    const float2 a = reinterpret_cast<const float2*>(tab + h * kTabBytes + kTabPwSeg)[m];
-    float2 c = state_in ? reinterpret_cast<const float2*>(state_in)[e] : make_float2(0.f, 0.f);
-    float2* w2 = reinterpret_cast<float2*>(ws);
-    for (int seg = 0; seg + 1 < S; ++seg) {
-        const float2 loc = w2[seg * total + e];
-        c = make_float2(a.x * c.x - a.y * c.y + loc.x, a.x * c.y + a.y * c.x + loc.y);
-        w2[seg * total + e] = c;
+    if (e >= p.B * p.H * per) return;
+    const int64_t bh = e / per, h = bh % p.H;
+    const int o = static_cast<int>(e % per) * 8;  // float offset in the (b, h) state, an even lane's float4
+    int mode[4], pre[4], pim[4], abi[4];           // mode, positions of re / im in the 8 floats, re in state_in
+    if (o < 128 * D) {  // U: [kw][rt][lane][jj], re in lane i, im in lane i + 1
+        const int kw = o / (16 * D), rem = o % (16 * D), rt = rem / 256, ln = (rem % 256) / 4;
+        const int g = ln >> 4, i = ln & 15;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            mode[k] = 8 * kw + i / 2;
+            pre[k] = k;
+            pim[k] = 4 + k;
+            abi[k] = (mode[k] * 2 * D + 16 * rt + 4 * g + k) * 2;
+        }
+    } else {  // Gamma: [vw][mt][lane][jj], (re, im) of modes m0, m0 + 1 in jj, channel 16 vw + i of the lane
+        const int o2 = o - 128 * D, vw = o2 / 2048, mt = (o2 % 2048) / 256, ln = (o2 % 256) / 4;
+        const int g = ln >> 4, i = ln & 15;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            mode[k] = 8 * mt + 2 * g + (k & 1);
+            pre[k] = 2 * k;
+            pim[k] = 2 * k + 1;
+            abi[k] = (mode[k] * 2 * D + D + 16 * vw + i + (k >> 1)) * 2;
+        }
+    }
+    const float2* aseg = reinterpret_cast<const float2*>(tab + h * kTabBytes + kTabPwSeg);
+    float2 a[4], c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        a[k] = aseg[mode[k]];
+        c[k] = state_in ? make_float2(state_in[bh * 256 * D + abi[k]], state_in[bh * 256 * D + abi[k] + 1])
+                        : make_float2(0.f, 0.f);
+    }
+    const int64_t sst = p.B * p.H * 256 * D;  // floats per segment
+    float* base = ws + bh * 256 * D + o;
+    for (int s0 = 0; s0 + 1 < S; s0 += kBatch) {
+        const int n = S - 1 - s0 < kBatch ? S - 1 - s0 : kBatch;
+        float loc[kBatch][8];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+            if (j < n) {
+                const float4* l4 = reinterpret_cast<const float4*>(base + (s0 + j) * sst);
+                const float4 x0 = l4[0], x1 = l4[1];
+                loc[j][0] = x0.x; loc[j][1] = x0.y; loc[j][2] = x0.z; loc[j][3] = x0.w;
+                loc[j][4] = x1.x; loc[j][5] = x1.y; loc[j][6] = x1.z; loc[j][7] = x1.w;
+            }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+            if (j < n) {
+                float out[8];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    c[k] = make_float2(a[k].x * c[k].x - a[k].y * c[k].y + loc[j][pre[k]],
+                                       a[k].x * c[k].y + a[k].y * c[k].x + loc[j][pim[k]]);
+                    out[pre[k]] = c[k].x;
+                    out[pim[k]] = c[k].y;
+                }
+                float4* d4 = reinterpret_cast<float4*>(base + (s0 + j) * sst);
+                d4[0] = make_float4(out[0], out[1], out[2], out[3]);
+                d4[1] = make_float4(out[4], out[5], out[6], out[7]);
+            }
     }
 }
 
@@ -927,7 +1082,8 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                                                               const float* state_in, const uint16_t* tail_in,
                                                               float* state_out, uint16_t* tail_out,
                                                               const uint8_t* __restrict__ tab,
-                                                              const float* __restrict__ carry, int64_t Lseg, int S) {
+                                                              const float* __restrict__ carry, int64_t Lseg, int S,
+                                                              int fold) {
     constexpr int RT = Cfg<D>::RT, KB = Cfg<D>::KB, YR = Cfg<D>::YR;
     constexpr uint32_t dl = WinOff<D>::ftl - WinOff<D>::ft;
     __shared__ SmemFwd<D> sm;
@@ -956,8 +1112,16 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
     const float2 hc = reinterpret_cast<const float2*>(th + kTabHc)[0];
     const float dt = hc.x, inv_dt = hc.y;
     const int rsb = static_cast<int>(H * D * 2);  // token stride, bytes
-    const float* src = seg == 0 ? (state_in ? state_in + bh * MM * 2 * D * 2 : nullptr)
-                                : carry + (static_cast<int64_t>(seg - 1) * p.B * p.H + bh) * MM * 2 * D * 2;
+    // state entering the segment: state_in, the carry chain's output, or (fold)
+    // state_in followed by the end states of the segments before this one
+    const int64_t sstride = MM * 2 * D * 2;  // floats per (b, h) state
+    const float* sin = state_in ? state_in + bh * sstride : nullptr;
+    const float* src = carry + (static_cast<int64_t>(seg > 0 ? seg - 1 : 0) * p.B * p.H + bh) * sstride;
+    const float* e0 = carry + bh * sstride;
+    const int64_t estride = p.B * p.H * sstride;
+    const int nfold = fold ? seg : 0;
+    constexpr int kFoldTiles = D == 128 ? 4 : 2;  // tiles per round trip of the fold (register bound)
+    const float2* aseg = reinterpret_cast<const float2*>(th + kTabPwSeg);
     constexpr int64_t tile2 = 2 * D * L;  // halfs per chunk: z_k^T, z_v^T
     const _Float16* zseg = zt + (bh * S + seg) * (Lseg / L) * tile2;
     __syncthreads();
@@ -966,7 +1130,13 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         // ---------------- key waves
         const int kw = w;
         f4 U[RT];
-        u_load<D>(U, src, kw);  // before the token loads, which are waited for first
+        // before the token loads, which are waited for first
+        if (seg > 0 && !fold) {
+            u_load_lane<D>(U, src, kw);
+        } else {
+            u_load<D>(U, sin, kw);
+            if (nfold > 0) u_fold<D, kFoldTiles>(U, e0, estride, nfold, aseg, kw);
+        }
         const __amdgpu_buffer_rsrc_t rq = seq_rsrc<D>(q, b, h, N, H, t_end);
         uint32_t rqq[11];  // raw queries of the chunk after the next
         fm_load<D, true>(rqq, rq, rsb, t_begin);
@@ -1094,7 +1264,14 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         const int vw = w - 8;
         const bool own = vw < D / 16;  // owns a 16-column block of Gamma
         f4 G[8];
-        if (own) g_load<D>(G, src, vw);  // before the tile loads, which are waited for first
+        if (own) {  // before the tile loads, which are waited for first
+            if (seg > 0 && !fold) {
+                g_load_lane<D>(G, src, vw);
+            } else {
+                g_load<D>(G, sin, vw);
+                if (nfold > 0) g_fold<D, kFoldTiles>(G, e0, estride, nfold, aseg, vw);
+            }
+        }
         const __amdgpu_buffer_rsrc_t ob = seq_rsrc<D>(o, b, h, N, H, t_end);
         u4 zr[kTilePieces<D>];  // z_v^T of the next chunk to enter
         u4 kr[kTilePieces<D>];  // z_k^T of the chunk after it
@@ -1202,23 +1379,24 @@ hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, con
     _Float16* zt = reinterpret_cast<_Float16*>(ws + static_cast<size_t>(S - 1) * pairs * MM * 2 * D * 2);
     const int64_t last_len = p.N - (S - 1) * Lseg;
     const int back = static_cast<int>((L - last_len % L) % L);
-    zoh_tables_kernel<<<dim3(static_cast<unsigned>(p.H), 16), 256, 0, stream>>>(p, prm, Lseg, back, tab);
+    zoh_tables_kernel<<<dim3(static_cast<unsigned>(p.H), 17), 256, 0, stream>>>(p, prm, Lseg, back, tab);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     segment_state_kernel<D><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(p, prm, k16, v16, t16, tab, ws,
                                                                                       zt, Lseg, S);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (S > 1) {
-        const int64_t total = pairs * MM * 2 * p.d;
-        segment_carry_kernel<<<dim3(static_cast<unsigned>((total + 255) / 256)), 256, 0, stream>>>(p, state_in, tab,
+    const int fold = S <= kFoldMax ? 1 : 0;
+    if (S > 1 && !fold) {
+        const int64_t threads = pairs * 32 * p.d;  // eight floats each
+        segment_carry_kernel<<<dim3(static_cast<unsigned>((threads + 255) / 256)), 256, 0, stream>>>(p, state_in, tab,
                                                                                                   ws, S);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     chunked_forward_kernel<D><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(
         p, prm, q16, k16, zt, static_cast<uint16_t*>(o), state_in, t16, state_out, static_cast<uint16_t*>(tail_out),
-        tab, ws, Lseg, S);
+        tab, ws, Lseg, S, fold);
     return hipGetLastError();
 }
 
