@@ -263,19 +263,22 @@ __device__ __forceinline__ void cpow(double dt, float lre, float lim, double n, 
     pi = e * sy;
 }
 
-// grid (H, 17), 256 threads.  Blocks y < 16: one (k, m) per thread, with
-// abar^{k+1} = abar^k abar; block y = 16: abar^Lseg (threads 0..63) and
-// abar^-back (64..127), so that no thread evaluates more than one power
-// besides the ZOH step.
-__global__ __launch_bounds__(256) void zoh_tables_kernel(Problem p, idattn_params prm, int64_t Lseg, int back,
-                                                         uint8_t* __restrict__ tab) {
+// grid (H, 17), 320 threads.  Blocks y < 16: threads 0..255 take one (k, m)
+// each and evaluate abar^k while threads 256..319 run the ZOH step of mode m
+// into shared memory, then T = bbar abar^k and abar^{k+1} = abar^k abar;
+// block y = 16: abar^Lseg (threads 0..63) and abar^-back (64..127).  No
+// thread runs more than one fp64 power or ZOH step before the combine.
+constexpr int kTabThreads = 320;
+__global__ __launch_bounds__(kTabThreads) void zoh_tables_kernel(Problem p, idattn_params prm, int64_t Lseg,
+                                                                 int back, uint8_t* __restrict__ tab) {
+    __shared__ Zoh zs[MM];
     const int64_t h = blockIdx.x;
     uint8_t* th = tab + h * kTabBytes;
     const int m = threadIdx.x & (MM - 1);
     const float log_dt = prm.log_dt[h];
     const float lre = prm.A[(h * MM + m) * 2], lim = prm.A[(h * MM + m) * 2 + 1];
     const double dt = exp(static_cast<double>(log_dt));
-    double pr, pi;
+    double pr = 0.0, pi = 0.0;
     if (blockIdx.y == 16) {
         const int which = threadIdx.x >> 6;
         if (which >= 2) return;
@@ -287,8 +290,13 @@ __global__ __launch_bounds__(256) void zoh_tables_kernel(Problem p, idattn_param
         return;
     }
     const int k = 4 * static_cast<int>(blockIdx.y) + (threadIdx.x >> 6);
-    const Zoh z = zoh_mode(log_dt, lre, lim, prm.Bc[(h * MM + m) * 2], prm.Bc[(h * MM + m) * 2 + 1]);
-    cpow(dt, lre, lim, static_cast<double>(k), pr, pi);  // abar^k
+    if (threadIdx.x >= 256)
+        zs[m] = zoh_mode(log_dt, lre, lim, prm.Bc[(h * MM + m) * 2], prm.Bc[(h * MM + m) * 2 + 1]);
+    else
+        cpow(dt, lre, lim, static_cast<double>(k), pr, pi);  // abar^k
+    __syncthreads();
+    if (threadIdx.x >= 256) return;
+    const Zoh z = zs[m];
     const double tv[2] = {z.br * pr - z.bi * pi, z.br * pi + z.bi * pr};
     _Float16* ft = reinterpret_cast<_Float16*>(th + kTabFT);
     _Float16* ftl = reinterpret_cast<_Float16*>(th + kTabFTL);
@@ -961,78 +969,56 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
     }
 }
 
-// Carry chain over segments (states in lane order), four complex state
-// elements (eight floats, two lanes' float4) per thread: ws[seg] <- state
-// entering segment seg+1.  The end states of up to eight segments are loaded
-// before any of them is combined, so that the loads overlap instead of forming
-// a chain of dependent round trips.  state_in is read in its own layout.
+// Carry chain over segments (states in lane order), one complex state element
+// per thread (four threads share the eight floats of an even lane's float4
+// and the next lane's): ws[seg] <- state entering segment seg+1.  The end
+// states of up to eight segments are loaded before any of them is combined,
+// so that the loads overlap instead of forming a chain of dependent round
+// trips.  state_in is read in its own layout.
 __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, const float* __restrict__ state_in,
                                                             const uint8_t* __restrict__ tab,
                                                             float* __restrict__ ws, int S) {
     constexpr int kBatch = 8;
     const int D = static_cast<int>(p.d);
-    const int64_t per = 32 * D;  // threads per (b, h)
+    const int64_t per = 128 * D;  // threads per (b, h)
     const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (e >= p.B * p.H * per) return;
     const int64_t bh = e / per, h = bh % p.H;
-    const int o = static_cast<int>(e % per) * 8;  // float offset in the (b, h) state, an even lane's float4
-    int mode[4], pre[4], pim[4], abi[4];           // mode, positions of re / im in the 8 floats, re in state_in
-    if (o < 128 * D) {  // U: [kw][rt][lane][jj], re in lane i, im in lane i + 1
+    const int o = static_cast<int>((e % per) >> 2) * 8;  // float offset of the group of eight
+    const int k = static_cast<int>(e & 3);
+    int mode, pre, pim, abi;  // mode, positions of re / im in the eight floats, re in state_in
+    if (o < 128 * D) {        // U: [kw][rt][lane][jj], re in lane i, im in lane i + 1
         const int kw = o / (16 * D), rem = o % (16 * D), rt = rem / 256, ln = (rem % 256) / 4;
         const int g = ln >> 4, i = ln & 15;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            mode[k] = 8 * kw + i / 2;
-            pre[k] = k;
-            pim[k] = 4 + k;
-            abi[k] = (mode[k] * 2 * D + 16 * rt + 4 * g + k) * 2;
-        }
+        mode = 8 * kw + i / 2;
+        pre = k;
+        pim = 4 + k;
+        abi = (mode * 2 * D + 16 * rt + 4 * g + k) * 2;
     } else {  // Gamma: [vw][mt][lane][jj], (re, im) of modes m0, m0 + 1 in jj, channel 16 vw + i of the lane
         const int o2 = o - 128 * D, vw = o2 / 2048, mt = (o2 % 2048) / 256, ln = (o2 % 256) / 4;
         const int g = ln >> 4, i = ln & 15;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            mode[k] = 8 * mt + 2 * g + (k & 1);
-            pre[k] = 2 * k;
-            pim[k] = 2 * k + 1;
-            abi[k] = (mode[k] * 2 * D + D + 16 * vw + i + (k >> 1)) * 2;
-        }
+        mode = 8 * mt + 2 * g + (k & 1);
+        pre = 2 * k;
+        pim = 2 * k + 1;
+        abi = (mode * 2 * D + D + 16 * vw + i + (k >> 1)) * 2;
     }
-    const float2* aseg = reinterpret_cast<const float2*>(tab + h * kTabBytes + kTabPwSeg);
-    float2 a[4], c[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        a[k] = aseg[mode[k]];
-        c[k] = state_in ? make_float2(state_in[bh * 256 * D + abi[k]], state_in[bh * 256 * D + abi[k] + 1])
+    const float2 a = reinterpret_cast<const float2*>(tab + h * kTabBytes + kTabPwSeg)[mode];
+    float2 c = state_in ? make_float2(state_in[bh * 256 * D + abi], state_in[bh * 256 * D + abi + 1])
                         : make_float2(0.f, 0.f);
-    }
     const int64_t sst = p.B * p.H * 256 * D;  // floats per segment
     float* base = ws + bh * 256 * D + o;
     for (int s0 = 0; s0 + 1 < S; s0 += kBatch) {
         const int n = S - 1 - s0 < kBatch ? S - 1 - s0 : kBatch;
-        float loc[kBatch][8];
+        float2 loc[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+            if (j < n) loc[j] = make_float2(base[(s0 + j) * sst + pre], base[(s0 + j) * sst + pim]);
 #pragma unroll
         for (int j = 0; j < kBatch; ++j)
             if (j < n) {
-                const float4* l4 = reinterpret_cast<const float4*>(base + (s0 + j) * sst);
-                const float4 x0 = l4[0], x1 = l4[1];
-                loc[j][0] = x0.x; loc[j][1] = x0.y; loc[j][2] = x0.z; loc[j][3] = x0.w;
-                loc[j][4] = x1.x; loc[j][5] = x1.y; loc[j][6] = x1.z; loc[j][7] = x1.w;
-            }
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j)
-            if (j < n) {
-                float out[8];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    c[k] = make_float2(a[k].x * c[k].x - a[k].y * c[k].y + loc[j][pre[k]],
-                                       a[k].x * c[k].y + a[k].y * c[k].x + loc[j][pim[k]]);
-                    out[pre[k]] = c[k].x;
-                    out[pim[k]] = c[k].y;
-                }
-                float4* d4 = reinterpret_cast<float4*>(base + (s0 + j) * sst);
-                d4[0] = make_float4(out[0], out[1], out[2], out[3]);
-                d4[1] = make_float4(out[4], out[5], out[6], out[7]);
+                c = make_float2(a.x * c.x - a.y * c.y + loc[j].x, a.x * c.y + a.y * c.x + loc[j].y);
+                base[(s0 + j) * sst + pre] = c.x;
+                base[(s0 + j) * sst + pim] = c.y;
             }
     }
 }
@@ -1379,7 +1365,7 @@ hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, con
     _Float16* zt = reinterpret_cast<_Float16*>(ws + static_cast<size_t>(S - 1) * pairs * MM * 2 * D * 2);
     const int64_t last_len = p.N - (S - 1) * Lseg;
     const int back = static_cast<int>((L - last_len % L) % L);
-    zoh_tables_kernel<<<dim3(static_cast<unsigned>(p.H), 17), 256, 0, stream>>>(p, prm, Lseg, back, tab);
+    zoh_tables_kernel<<<dim3(static_cast<unsigned>(p.H), 17), kTabThreads, 0, stream>>>(p, prm, Lseg, back, tab);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     segment_state_kernel<D><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(p, prm, k16, v16, t16, tab, ws,
@@ -1388,7 +1374,7 @@ hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, con
     if (e != hipSuccess) return e;
     const int fold = S <= kFoldMax ? 1 : 0;
     if (S > 1 && !fold) {
-        const int64_t threads = pairs * 32 * p.d;  // eight floats each
+        const int64_t threads = pairs * 128 * p.d;  // one complex element each
         segment_carry_kernel<<<dim3(static_cast<unsigned>((threads + 255) / 256)), 256, 0, stream>>>(p, state_in, tab,
                                                                                                   ws, S);
         e = hipGetLastError();
