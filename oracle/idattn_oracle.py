@@ -41,6 +41,9 @@ Parity pins (tests/test_oracle_pins.py):
   short_conv   pinned: per-channel numpy.convolve (textbook FIR).
   silu         pinned: scipy.special.expit.
   feature_map  pinned: ||xi|| * ||y|| = 1 at eps_feat = 0; direction of y.
+  feature_map_unit  pinned: ||xi|| = 1 and xi . y = ||y|| at eps_feat = 0;
+               with both eps = 0 the unit-norm forward equals ||y_q|| times the
+               squared one, token by token (RMSNorm removes the key-side scale).
   rms_norm     pinned: mean(((z - b)/g)^2) = m/(m + eps) identity.
   zoh          pinned: quadrature of exp(lambda*tau) and scipy.linalg.expm.
   forward      pinned: O(N^2) closed form of U, O(N^3) state-free kernel form
@@ -121,6 +124,17 @@ def feature_map(c, eps_feat):
     return y / ((y * y).sum(axis=-1, keepdims=True) + eps_feat)
 
 
+def feature_map_unit(c, eps_feat):
+    """Unit-norm variant xi = y / sqrt(||y||^2 + eps_feat), y = SiLU(c): the
+    feature map that p1 section 1 names "SiLU/l_2", read as division by the
+    plain l2 norm (the other reading of the printed squared norm)."""
+    y = silu(c)
+    return y / np.sqrt((y * y).sum(axis=-1, keepdims=True) + eps_feat)
+
+
+FEATURE_NORMS = ("squared", "unit")
+
+
 def rms_norm(x, gain, bias, eps_norm):
     """Input RMSNorm with learnable per-head gain and bias (p2 normalisation
     bullet): z = g * x / sqrt(mean(x^2) + eps_norm) + b over the last axis.
@@ -153,7 +167,7 @@ def ssm_step(U, Gamma, xi_q_i, z_k_i, z_v_i, abar, bbar):
 
 
 def forward(q, k, v, params, eps_feat=1e-6, eps_norm=1e-6,
-            state_in=None, tail_in=None, intermediates=False):
+            state_in=None, tail_in=None, intermediates=False, feature_norm="squared"):
     """Forward pass of the mixer over a block of N tokens.
 
     q, k, v    [B, N, H, d] (any real dtype; upcast to float64)
@@ -161,6 +175,8 @@ def forward(q, k, v, params, eps_feat=1e-6, eps_norm=1e-6,
                then value half); log_dt [H]; A, Bc [H, M, 2]
     state_in   complex [B, H, M, 2d] (U then Gamma) or None (zeros)
     tail_in    [B, H, 2, W-1, d] raw q then k tokens before position 0, or None
+    feature_norm  "squared" (xi = y / (||y||^2 + eps), the printed form) or
+               "unit" (xi = y / sqrt(||y||^2 + eps))
 
     Returns (o [B, N, H, d] float64, state_out complex128 [B, H, M, 2d],
     tail_out [B, H, 2, W-1, d] float64) and, with intermediates=True, a dict
@@ -185,8 +201,11 @@ def forward(q, k, v, params, eps_feat=1e-6, eps_norm=1e-6,
     # 1-2. short conv and feature map on queries and keys
     c_q = short_conv(q, params["conv_q"], tail_in[:, :, 0])
     c_k = short_conv(k, params["conv_k"], tail_in[:, :, 1])
-    xi_q = feature_map(c_q, eps_feat)
-    xi_k = feature_map(c_k, eps_feat)
+    if feature_norm not in FEATURE_NORMS:
+        raise ValueError(f"feature_norm must be one of {FEATURE_NORMS}")
+    fmap = feature_map if feature_norm == "squared" else feature_map_unit
+    xi_q = fmap(c_q, eps_feat)
+    xi_k = fmap(c_k, eps_feat)
     # 3. input RMSNorm on the key-feature half and the value half
     z_k = rms_norm(xi_k, gain[:, :d], bias[:, :d], eps_norm)
     z_v = rms_norm(v, gain[:, d:], bias[:, d:], eps_norm)
@@ -217,7 +236,7 @@ def forward(q, k, v, params, eps_feat=1e-6, eps_norm=1e-6,
     return o, state_out, tail_out, inter
 
 
-def decode_step(q_t, k_t, v_t, state, tail, params, eps_feat=1e-6, eps_norm=1e-6):
+def decode_step(q_t, k_t, v_t, state, tail, params, eps_feat=1e-6, eps_norm=1e-6, feature_norm="squared"):
     """One autoregressive step: the forward pass with N = 1 from a carried
     state and conv tail (fixed-size state, O(1) work per token: p1 section 1).
 
@@ -226,5 +245,6 @@ def decode_step(q_t, k_t, v_t, state, tail, params, eps_feat=1e-6, eps_norm=1e-6
     o, st, tl = forward(np.asarray(q_t, dtype=F64)[:, None],
                         np.asarray(k_t, dtype=F64)[:, None],
                         np.asarray(v_t, dtype=F64)[:, None],
-                        params, eps_feat, eps_norm, state_in=state, tail_in=tail)
+                        params, eps_feat, eps_norm, state_in=state, tail_in=tail,
+                        feature_norm=feature_norm)
     return o[:, 0], st, tl

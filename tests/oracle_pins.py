@@ -86,6 +86,34 @@ def pin_feature_map(O) -> float:
     return max(float(np.abs(dot - 1).max()), float(np.abs(nn - 1).max()))
 
 
+def pin_feature_map_unit(O) -> float:
+    """With eps_feat = 0: ||xi|| = 1 and xi . y = ||y||, which together force
+    xi = y / ||y|| (Cauchy-Schwarz equality)."""
+    r = np.random.default_rng(16)
+    c = r.normal(size=(3, 7, 2, 16)) * 2.0
+    y = c * scipy.special.expit(c)
+    xi = O.feature_map_unit(c, 0.0)
+    ny = np.linalg.norm(y, axis=-1)
+    e1 = np.abs(np.linalg.norm(xi, axis=-1) - 1).max()
+    e2 = np.abs((xi * y).sum(-1) - ny).max() / ny.max()
+    return max(float(e1), float(e2))
+
+
+def pin_unit_scaling(O) -> float:
+    """With eps_feat = eps_norm = 0 the key features enter only through RMSNorm,
+    which is blind to a per-token scale, and the query features scale s (hence
+    o) by ||y_q||: o_unit(i) = ||SiLU(SC(q))(i)|| o_squared(i), per token and
+    head.  The norm comes from scipy.special.expit and the oracle's conv, which
+    the conv pin ties to numpy.convolve."""
+    c = pin_case(with_state=True)
+    q, k, v, p = c["q"], c["k"], c["v"], c["p"]
+    o_sq = O.forward(q, k, v, p, 0.0, 0.0, c["state"], c["tail"])[0]
+    o_un = O.forward(q, k, v, p, 0.0, 0.0, c["state"], c["tail"], feature_norm="unit")[0]
+    cq = O.short_conv(q, p["conv_q"], np.asarray(c["tail"])[:, :, 0])
+    ny = np.linalg.norm(cq * scipy.special.expit(cq), axis=-1, keepdims=True)
+    return rel(o_un, ny * o_sq)
+
+
 def pin_rms_norm(O) -> float:
     """((z - b)/g) is parallel to x with mean square m/(m + eps)."""
     r = np.random.default_rng(7)
@@ -309,6 +337,8 @@ PINS = {
     "conv": (pin_conv, 1e-13),
     "silu": (pin_silu, 1e-14),
     "feature_map": (pin_feature_map, 1e-12),
+    "feature_map_unit": (pin_feature_map_unit, 1e-12),
+    "unit_scaling": (pin_unit_scaling, 1e-11),
     "rms_norm": (pin_rms_norm, 1e-12),
     "zoh": (pin_zoh, 1e-10),
     "wiring": (pin_wiring, 1e-10),

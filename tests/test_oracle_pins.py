@@ -40,6 +40,11 @@ def _featmap_unsquared(c, eps):
     return y / (np.sqrt((y * y).sum(-1, keepdims=True)) + eps)
 
 
+def _featmap_unit_no_sqrt(c, eps):
+    y = O.silu(c)
+    return y / ((y * y).sum(-1, keepdims=True) + eps)
+
+
 def _rms_sum(x, g, b, eps):
     x = np.asarray(x, float)
     return np.asarray(g)[None, None] * x / np.sqrt((x * x).sum(-1, keepdims=True) + eps) + np.asarray(b)[None, None]
@@ -88,13 +93,15 @@ def _step_imag_dropped(U, G, xq, zk, zv, a, b):
     return U, G, s, np.einsum("bhm,bhmc->bhc", s.real, G.real)
 
 
-_orig = {name: getattr(O, name) for name in ("short_conv", "silu", "feature_map", "rms_norm", "zoh", "ssm_step")}
+_orig = {name: getattr(O, name) for name in ("short_conv", "silu", "feature_map", "feature_map_unit", "rms_norm",
+                                             "zoh", "ssm_step")}
 
 MUTANTS = {
     "conv_reversed_taps": ("short_conv", _conv_reversed),
     "conv_off_by_one": ("short_conv", _conv_shift),
     "silu_wrong_sign": ("silu", _silu_sign),
     "featmap_unsquared_norm": ("feature_map", _featmap_unsquared),
+    "featmap_unit_without_sqrt": ("feature_map_unit", _featmap_unit_no_sqrt),
     "rms_sum_not_mean": ("rms_norm", _rms_sum),
     "rms_dropped_bias": ("rms_norm", _rms_no_bias),
     "zoh_euler_bbar": ("zoh", _zoh_euler),
