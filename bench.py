@@ -75,6 +75,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="1p3b", choices=["125m", "1p3b", "14k"])
     ap.add_argument("--algo", default="auto", choices=["auto", "sequential", "chunked"])
+    ap.add_argument("--feature-norm", default="squared", choices=["squared", "unit"],
+                    help="feature map xi = y / (||y||^2 + eps) (squared) or y / sqrt(||y||^2 + eps) (unit)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU sample")
@@ -193,7 +195,7 @@ def main():
     del base
     state_out = torch.empty((B, H, M, 2 * d, 2), dtype=torch.float32, device="cuda")
     tail_out = torch.empty((B, H, 2, W - 1, d), dtype=torch.bfloat16, device="cuda")
-    dims = fs.make_dims(B, N, H, d, M, W, "bf16", args.algo)
+    dims = fs.make_dims(B, N, H, d, M, W, "bf16", args.algo, feature_norm=args.feature_norm)
     nbytes = fs.idattn_forward_workspace_size(dims)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
     algo = args.algo
@@ -240,8 +242,10 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if algo == "sequential" else "f16-mfma/f32",
         "data": "synthetic (seeded N(0,1) bf16 q,k,v; S4D-Lin init)",
-        "config": {"workload": f"{args.config}: B={B} H={H} N={N} d=R={d} M={M} W={W}, bf16 I/O, fp32 state",
-                   "B": B, "N": N, "H": H, "d": d, "M": M, "W": W, "io": "bf16", "algo": algo},
+        "config": {"workload": f"{args.config}: B={B} H={H} N={N} d=R={d} M={M} W={W}, bf16 I/O, fp32 state"
+                               + ("" if args.feature_norm == "squared" else ", unit-norm feature map"),
+                   "B": B, "N": N, "H": H, "d": d, "M": M, "W": W, "io": "bf16", "algo": algo,
+                   "feature_norm": args.feature_norm},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": committed_traffic(args.config, algo),
                      "kernel": "idattn_forward launch (all kernels of one forward, HIP events on the launch stream)",

@@ -8,12 +8,12 @@ stream.
 """
 from __future__ import annotations
 
-from .binding import (ALGO, EXPORTS, IO, LIB_PATH, STATUS, IdattnDims, IdattnError, IdattnParams,
+from .binding import (ALGO, EXPORTS, FEATURE_NORM, IO, LIB_PATH, STATUS, IdattnDims, IdattnError, IdattnParams,
                       idattn_decode_step, idattn_forward, idattn_forward_workspace_size,
                       idattn_last_error, idattn_status_string, idattn_version, load_library,
                       make_dims, make_params)
 
-__all__ = ["ALGO", "EXPORTS", "IO", "LIB_PATH", "STATUS", "IdattnDims", "IdattnError", "IdattnParams",
+__all__ = ["ALGO", "EXPORTS", "FEATURE_NORM", "IO", "LIB_PATH", "STATUS", "IdattnDims", "IdattnError", "IdattnParams",
            "idattn_decode_step", "idattn_forward", "idattn_forward_workspace_size",
            "idattn_last_error", "idattn_status_string", "idattn_version", "load_library",
            "make_dims", "make_params", "forward", "decode_step", "params_to_device"]
@@ -37,7 +37,7 @@ def _io_name(t):
 
 
 def forward(q, k, v, params: dict, *, state_in=None, tail_in=None, return_state=False,
-            algo="auto", eps_feat=1e-6, eps_norm=1e-6, stream=None):
+            algo="auto", eps_feat=1e-6, eps_norm=1e-6, feature_norm="squared", stream=None):
     """o = mixer(q, k, v) for q, k, v of shape [B, N, H, d] on the GPU.
 
     params: device tensors (see params_to_device).  state_in: float32
@@ -51,7 +51,7 @@ def forward(q, k, v, params: dict, *, state_in=None, tail_in=None, return_state=
     for t in (k, v):
         if t.dtype != q.dtype or t.shape != q.shape:
             raise ValueError("q, k, v must share shape and dtype")
-    dims = make_dims(B, N, H, d, M, W, io, algo, eps_feat, eps_norm)
+    dims = make_dims(B, N, H, d, M, W, io, algo, eps_feat, eps_norm, feature_norm)
     nbytes = idattn_forward_workspace_size(dims)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     o = torch.empty_like(q)
@@ -64,7 +64,8 @@ def forward(q, k, v, params: dict, *, state_in=None, tail_in=None, return_state=
     return (o, state_out, tail_out) if return_state else o
 
 
-def decode_step(q_t, k_t, v_t, params: dict, state, tail, *, eps_feat=1e-6, eps_norm=1e-6, stream=None):
+def decode_step(q_t, k_t, v_t, params: dict, state, tail, *, eps_feat=1e-6, eps_norm=1e-6, feature_norm="squared",
+                stream=None):
     """One token per sequence: q_t, k_t, v_t [B, H, d]; state float32
     [B, H, M, 2d, 2] and tail [B, H, 2, W-1, d] are updated in place.
     Returns o_t [B, H, d]."""
@@ -72,7 +73,7 @@ def decode_step(q_t, k_t, v_t, params: dict, state, tail, *, eps_feat=1e-6, eps_
     B, H, d = q_t.shape
     M = params["A"].shape[1]
     W = params["conv_q"].shape[-1]
-    dims = make_dims(B, 1, H, d, M, W, _io_name(q_t), "auto", eps_feat, eps_norm)
+    dims = make_dims(B, 1, H, d, M, W, _io_name(q_t), "auto", eps_feat, eps_norm, feature_norm)
     o_t = torch.empty_like(q_t)
     idattn_decode_step(dims, make_params(params), q_t, k_t, v_t, o_t, state, tail, stream)
     return o_t

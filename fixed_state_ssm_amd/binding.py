@@ -18,6 +18,7 @@ STATUS = {0: "IDATTN_OK", 1: "IDATTN_ERR_NULL", 2: "IDATTN_ERR_SHAPE", 3: "IDATT
           4: "IDATTN_ERR_WORKSPACE", 5: "IDATTN_ERR_ALIAS", 6: "IDATTN_ERR_ARG", 7: "IDATTN_ERR_HIP"}
 IO = {"f32": 0, "bf16": 1}
 ALGO = {"auto": 0, "sequential": 1, "chunked": 2}
+FEATURE_NORM = {"squared": 0, "unit": 1}
 
 EXPORTS = ("idattn_forward_workspace_size", "idattn_forward", "idattn_decode_step",
            "idattn_status_string", "idattn_last_error", "idattn_version")
@@ -26,7 +27,7 @@ EXPORTS = ("idattn_forward_workspace_size", "idattn_forward", "idattn_decode_ste
 class IdattnDims(ctypes.Structure):
     _fields_ = [("B", c_int64), ("N", c_int64), ("H", c_int64), ("d", c_int64), ("M", c_int64),
                 ("W", c_int64), ("io_dtype", c_int32), ("algo", c_int32),
-                ("eps_feat", c_float), ("eps_norm", c_float)]
+                ("eps_feat", c_float), ("eps_norm", c_float), ("feature_norm", c_int32)]
 
 
 class IdattnParams(ctypes.Structure):
@@ -99,9 +100,11 @@ def _check(status: int):
         raise IdattnError(status, detail)
 
 
-def make_dims(B, N, H, d, M, W=4, io="bf16", algo="auto", eps_feat=1e-6, eps_norm=1e-6) -> IdattnDims:
+def make_dims(B, N, H, d, M, W=4, io="bf16", algo="auto", eps_feat=1e-6, eps_norm=1e-6,
+              feature_norm="squared") -> IdattnDims:
     return IdattnDims(int(B), int(N), int(H), int(d), int(M), int(W), IO[io] if isinstance(io, str) else int(io),
-                      ALGO[algo] if isinstance(algo, str) else int(algo), float(eps_feat), float(eps_norm))
+                      ALGO[algo] if isinstance(algo, str) else int(algo), float(eps_feat), float(eps_norm),
+                      FEATURE_NORM[feature_norm] if isinstance(feature_norm, str) else int(feature_norm))
 
 
 def make_params(p: dict) -> IdattnParams:

@@ -62,6 +62,8 @@ idattn_status check_dims(const idattn_dims* dims, bool decode) {
         return fail(IDATTN_ERR_ARG, "eps_feat must be finite and >= 0");
     if (!(D.eps_norm >= 0.f) || !std::isfinite(D.eps_norm))
         return fail(IDATTN_ERR_ARG, "eps_norm must be finite and >= 0");
+    if (D.feature_norm != IDATTN_FEATURE_SQUARED && D.feature_norm != IDATTN_FEATURE_UNIT)
+        return fail(IDATTN_ERR_ARG, "feature_norm %d is not a known idattn_feature_norm", D.feature_norm);
     // element counts must stay far from int64 overflow
     const double elems = static_cast<double>(D.B) * D.N * D.H * D.d;
     const double state = static_cast<double>(D.B) * D.H * D.M * D.d * 4.0;
@@ -95,6 +97,7 @@ idattn::Problem problem(const idattn_dims& D) {
     p.bf16 = D.io_dtype == IDATTN_IO_BF16;
     p.eps_feat = D.eps_feat;
     p.eps_norm = D.eps_norm;
+    p.unit_feat = D.feature_norm == IDATTN_FEATURE_UNIT;
     return p;
 }
 

@@ -468,15 +468,17 @@ __device__ __forceinline__ void share_factor(SM& sm, float f, float (&out)[8]) {
 // z_k of the thread's 8 tokens to z_k^T (zero past n valid tokens).
 template <int D, class SM>
 __device__ __forceinline__ void fm_keys(const uint32_t (&r)[11], const SM& sm, const void* zT, int n, float eps_feat,
-                                        float eps_norm, int fi = feat_index<D>()) {
+                                        float eps_norm, bool unit, int fi = feat_index<D>()) {
     if (fi >= Cfg<D>::NF) return;
     const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
     float y[2][8], ss[8], rho[8];
     conv_silu<D>(r, sm.wk, cgi, y, ss);
     {
-        // xi = -ln2 inv y',  mean xi^2 = ln^2 2 inv^2 ||y'||^2 / D
+        // xi = -ln2 inv y',  mean xi^2 = ln^2 2 inv^2 ||y'||^2 / D, with inv the
+        // reciprocal of ||y||^2 + eps (or of its square root for the unit-norm map)
         const float tot = reduce_scatter8<Cfg<D>::CP>(ss);
-        const float inv = __builtin_amdgcn_rcpf(fmaf(kLn2Sq, tot, eps_feat));
+        const float den = fmaf(kLn2Sq, tot, eps_feat);
+        const float inv = unit ? __builtin_amdgcn_rsqf(den) : __builtin_amdgcn_rcpf(den);
         const float rs = __builtin_amdgcn_rsqf(fmaf(kLn2Sq * (1.f / D) * inv * inv, tot, eps_norm));
         share_factor<D>(const_cast<SM&>(sm), -kLn2 * inv * rs, rho);
     }
@@ -520,7 +522,7 @@ __device__ __forceinline__ void fm_values(const uint32_t (&r)[8], const SM& sm, 
 // y' of the thread's 8 tokens, kept as fp16 pairs until fm_write_q, and sigma~ to sig.
 template <int D, class SM>
 __device__ __forceinline__ void fm_queries(half2v (&yo)[8], const uint32_t (&r)[11], SM& sm, float* sig,
-                                           float eps_feat, float inv_dt, int fi = feat_index<D>()) {
+                                           float eps_feat, float inv_dt, bool unit, int fi = feat_index<D>()) {
     if (fi >= Cfg<D>::NF) return;
     const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
     float y[2][8], ss[8];
@@ -528,7 +530,11 @@ __device__ __forceinline__ void fm_queries(half2v (&yo)[8], const uint32_t (&r)[
 #pragma unroll
     for (int s = 0; s < 8; ++s) yo[s] = half2v{static_cast<_Float16>(y[0][s]), static_cast<_Float16>(y[1][s])};
     const float tot = reduce_scatter8<Cfg<D>::CP>(ss);
-    if (cgi < 8) sig[8 * tb + scatter_token(cgi)] = -kLn2 * inv_dt * __builtin_amdgcn_rcpf(fmaf(kLn2Sq, tot, eps_feat));
+    if (cgi < 8) {
+        const float den = fmaf(kLn2Sq, tot, eps_feat);
+        sig[8 * tb + scatter_token(cgi)] =
+            -kLn2 * inv_dt * (unit ? __builtin_amdgcn_rsqf(den) : __builtin_amdgcn_rcpf(den));
+    }
 }
 template <int D>
 __device__ __forceinline__ void fm_write_q(const half2v (&yo)[8], const void* yq, int fi = feat_index<D>()) {
@@ -919,7 +925,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
         uint32_t rkk[11];
         fm_load<D, true>(rkk, rk, rsb, t_begin);
         halo_fix<D>(rkk, sm, 1, t_begin);
-        fm_keys<D>(rkk, sm, sm.zkT[0], nch > 1 ? L : n_last, p.eps_feat, p.eps_norm);
+        fm_keys<D>(rkk, sm, sm.zkT[0], nch > 1 ? L : n_last, p.eps_feat, p.eps_norm, p.unit_feat);
         if (nch > 1) fm_load<D, true>(rkk, rk, rsb, t_begin + L);
         lds_barrier();  // chunk 0 features
         for (int c = 0; c < nch; ++c) {
@@ -928,7 +934,8 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
             tile_copy_out<D>(sm.zvT[c & 1], zseg + c * 2 * D * L + D * L);  // both tiles: the value waves are the longer role
             if (upd) key_update<D>(U, sm.aL, kw, sm.zkT[c & 1], sm.ft, tid_now() & 63);
             if (c + 1 < nch) {
-                fm_keys<D>(rkk, sm, sm.zkT[(c + 1) & 1], c + 2 < nch ? L : n_last, p.eps_feat, p.eps_norm);
+                fm_keys<D>(rkk, sm, sm.zkT[(c + 1) & 1], c + 2 < nch ? L : n_last, p.eps_feat, p.eps_norm,
+                           p.unit_feat);
                 if (c + 2 < nch) {
                     step_fence();
                     fm_load<D, true>(rkk, rk, rsb, t0 + 2 * L);
@@ -1129,7 +1136,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         halo_fix<D>(rqq, sm, 0, t_begin);
         {
             half2v yo[8];
-            fm_queries<D>(yo, rqq, sm, sm.sig[0], p.eps_feat, inv_dt);
+            fm_queries<D>(yo, rqq, sm, sm.sig[0], p.eps_feat, inv_dt, p.unit_feat);
             fm_write_q<D>(yo, sm.yq);
         }
         if (nch > 1) fm_load<D, true>(rqq, rq, rsb, t_begin + L);
@@ -1141,7 +1148,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             if (c + 1 < nch) {
                 // queries' features of chunk c+1 (sigma~ goes to the buffer of parity c+1,
                 // last read in phase 2 of the previous step); the raw tokens of c+2 follow
-                fm_queries<D>(yo, rqq, sm, sm.sig[(c + 1) & 1], p.eps_feat, inv_dt);
+                fm_queries<D>(yo, rqq, sm, sm.sig[(c + 1) & 1], p.eps_feat, inv_dt, p.unit_feat);
                 if (c + 2 < nch) {
                     step_fence();
                     fm_load<D, true>(rqq, rq, rsb, t_begin + static_cast<int64_t>(c + 2) * L);

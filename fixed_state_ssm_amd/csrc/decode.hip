@@ -132,8 +132,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
         sq = wave_sum(sq);
         sk = wave_sum(sk);
         sv = wave_sum(sv);
-        const float inv_q = 1.f / (sq + p.eps_feat);
-        const float inv_k = 1.f / (sk + p.eps_feat);
+        // xi = y * inv: squared norm, or its square root for the unit-norm map
+        const float inv_q = p.unit_feat ? 1.f / sqrtf(sq + p.eps_feat) : 1.f / (sq + p.eps_feat);
+        const float inv_k = p.unit_feat ? 1.f / sqrtf(sk + p.eps_feat) : 1.f / (sk + p.eps_feat);
         float xk2 = 0.f, xik[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {

@@ -13,6 +13,7 @@ struct Problem {
     int64_t B, N, H, d, M, W;
     bool bf16;
     float eps_feat, eps_norm;
+    bool unit_feat;  // xi = y / sqrt(||y||^2 + eps_feat) instead of y / (||y||^2 + eps_feat)
 };
 
 // ---- stage kernels of the sequential (fp32) path; workspace layout [B][H][N][*]

@@ -9,7 +9,8 @@
  * caption for the state shapes):
  *   per batch row b, head h, position i, with R = d channels per head,
  *   c   = SC(x), a causal depthwise conv of width W, on q and on k
- *   xi  = SiLU(c) / (||SiLU(c)||^2 + eps_feat)             (norm over R)
+ *   xi  = SiLU(c) / (||SiLU(c)||^2 + eps_feat)             (norm over R; or,
+ *         with IDATTN_FEATURE_UNIT, SiLU(c) / sqrt(||SiLU(c)||^2 + eps_feat))
  *   z_k = g_k * xi_k / sqrt(mean(xi_k^2) + eps_norm) + b_k  (RMSNorm, key half)
  *   z_v = g_v * v    / sqrt(mean(v^2)    + eps_norm) + b_v  (RMSNorm, value half)
  *   abar_m = exp(Delta lambda_m), bbar_m = (abar_m - 1)/lambda_m * B_m,
@@ -74,6 +75,14 @@ typedef enum idattn_algo {
                                     fp32 accumulation and state; bf16 I/O only            */
 } idattn_algo;
 
+/* Norm of the feature map.  The gist.science summaries print the squared
+ * norm; the Chinese rendering, section 1, names the feature map "SiLU/l_2",
+ * whose plain reading is the unit-norm map. */
+typedef enum idattn_feature_norm {
+    IDATTN_FEATURE_SQUARED = 0,  /* xi = y / (||y||^2 + eps_feat)        (default) */
+    IDATTN_FEATURE_UNIT = 1      /* xi = y / sqrt(||y||^2 + eps_feat)              */
+} idattn_feature_norm;
+
 /* Sizes.  R == d.  Layout of q, k, v, o: contiguous [B][N][H][d]. */
 typedef struct idattn_dims {
     int64_t B;        /* batch rows, >= 1                                     */
@@ -86,6 +95,7 @@ typedef struct idattn_dims {
     int32_t algo;     /* idattn_algo                                          */
     float eps_feat;   /* >= 0: xi = y / (||y||^2 + eps_feat)                   */
     float eps_norm;   /* >= 0: RMSNorm sqrt(mean(x^2) + eps_norm)              */
+    int32_t feature_norm; /* idattn_feature_norm; 0 (zero-initialised) = squared */
 } idattn_dims;
 
 /* Per-head parameters, all float32 device buffers, read only. */

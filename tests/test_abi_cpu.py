@@ -40,9 +40,9 @@ def test_struct_layout_matches_header():
     #include <stddef.h>
     #include "idattn.h"
     int main(void) {
-      printf("%zu %zu %zu %zu %zu %zu\n", sizeof(idattn_dims), offsetof(idattn_dims, io_dtype),
-             offsetof(idattn_dims, eps_norm), sizeof(idattn_params), offsetof(idattn_params, log_dt),
-             offsetof(idattn_params, Bc));
+      printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(idattn_dims), offsetof(idattn_dims, io_dtype),
+             offsetof(idattn_dims, eps_norm), offsetof(idattn_dims, feature_norm), sizeof(idattn_params),
+             offsetof(idattn_params, log_dt), offsetof(idattn_params, Bc));
       return 0;
     }"""
     with tempfile.TemporaryDirectory() as td:
@@ -52,7 +52,8 @@ def test_struct_layout_matches_header():
         subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
         got = list(map(int, subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()))
     want = [ctypes.sizeof(IdattnDims), IdattnDims.io_dtype.offset, IdattnDims.eps_norm.offset,
-            ctypes.sizeof(IdattnParams), IdattnParams.log_dt.offset, IdattnParams.Bc.offset]
+            IdattnDims.feature_norm.offset, ctypes.sizeof(IdattnParams), IdattnParams.log_dt.offset,
+            IdattnParams.Bc.offset]
     assert got == want
 
 
@@ -102,6 +103,7 @@ def expect(status, name):
     ("M", 8, "IDATTN_ERR_UNSUPPORTED"), ("M", 128, "IDATTN_ERR_UNSUPPORTED"), ("W", 9, "IDATTN_ERR_UNSUPPORTED"),
     ("io", 7, "IDATTN_ERR_ARG"), ("algo", 9, "IDATTN_ERR_ARG"), ("eps_feat", -1.0, "IDATTN_ERR_ARG"),
     ("eps_norm", float("nan"), "IDATTN_ERR_ARG"), ("eps_norm", float("inf"), "IDATTN_ERR_ARG"),
+    ("feature_norm", 2, "IDATTN_ERR_ARG"), ("feature_norm", -1, "IDATTN_ERR_ARG"),
 ])
 def test_forward_rejects_bad_dims(field, value, name):
     d = dims(**{field: value})

@@ -94,6 +94,55 @@ def test_small_forward(fs, name, with_state):
         assert np.array_equal(down(tl), tl_ref.astype(np.float32)), algo
 
 
+# The unit-norm feature map (xi = y / sqrt(||y||^2 + eps)) on both paths: the
+# all-fp32 sequential path, the chunked path with one and with four time
+# segments (carry folded into the forward), and d = 64.
+UNIT = ["tiny_f32", "d128_m64_ragged_bf16", "d128_segments_bf16", "d64_m32_ragged_bf16", "d64_w1_bf16"]
+
+
+@pytest.mark.parametrize("name", UNIT)
+def test_small_forward_unit_feature_map(fs, name):
+    base, over, tag = SMALL[name]
+    c = WL.make_case(base, seed=1, tag=tag, **over)
+    s = c.spec
+    io = s["io"]
+    st0, tl0 = WL.make_decode_state(s, seed=2)
+    o_ref, st_ref, _ = oracle.forward(c.q, c.k, c.v, c.params, state_in=st0, tail_in=tl0, feature_norm="unit")
+    p = fs.params_to_device(c.params)
+    for algo in _algos(io):
+        if algo == "chunked" and not _chunked_available(fs, s):
+            continue
+        o, st, _ = fs.forward(up(c.q, io), up(c.k, io), up(c.v, io), p, return_state=True, algo=algo,
+                              state_in=state_dev(st0), tail_in=up(tl0, io), feature_norm="unit")
+        _sync()
+        e_o = rel_l2(down(o), o_ref)
+        e_s = rel_l2(state_np(st), st_ref)
+        print(f"unit {name} {algo}: o relL2 {e_o:.2e}, state relL2 {e_s:.2e}")
+        assert e_o <= gate(io), (algo, e_o)
+        assert e_s <= gate(io), (algo, e_s)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_decode_step_unit_feature_map(fs, io):
+    base, over, tag = SMALL["d128_m64_ragged_bf16"]
+    over = dict(over, io=io)
+    c = WL.make_case(base, seed=3, tag=tag, **over)
+    s = c.spec
+    st0, tl0 = WL.make_decode_state(s, seed=4)
+    qt, kt, vt = WL.make_decode_token(s)
+    ot_ref, st_ref, tl_ref = oracle.decode_step(qt, kt, vt, st0, tl0, c.params, feature_norm="unit")
+    p = fs.params_to_device(c.params)
+    st = state_dev(st0)
+    tl = up(tl0, io)
+    ot = fs.decode_step(up(qt, io), up(kt, io), up(vt, io), p, st, tl, feature_norm="unit")
+    _sync()
+    e_o = rel_l2(down(ot), ot_ref)
+    e_s = rel_l2(state_np(st), st_ref)
+    print(f"unit decode {io}: o relL2 {e_o:.2e}, state relL2 {e_s:.2e}")
+    assert e_o <= gate(io) and e_s <= gate(io), (e_o, e_s)
+    assert np.array_equal(down(tl), tl_ref.astype(np.float32))
+
+
 def _pairs(s, n, seed):
     r = np.random.default_rng(seed)
     idx = r.choice(s["B"] * s["H"], size=min(n, s["B"] * s["H"]), replace=False)
