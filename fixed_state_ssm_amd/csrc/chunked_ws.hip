@@ -244,14 +244,13 @@ __device__ __forceinline__ half8 to_half8(const f4& a, const f4& b) {
 // Per-head tables, one launch per forward (fp64 arithmetic):
 //   ft, ftl [M2][L] fp16, swizzled rows: F^T[m'][j] = T_{m'}[L-1-j] = ft + ftl
 //   pw [L][MM] float2: abar^{k+1}
-//   pwseg[MM], pwback[MM] float2: abar^{Lseg}, abar^{-back};  hc: Delta, 1/Delta
+//   pwseg[MM] float2: abar^{Lseg};  hc: Delta, 1/Delta
 // with T_{m'}[k] the real (m' even) or imaginary (m' odd) part of bbar_m abar_m^k.
 constexpr int kTabFT = 0;
 constexpr int kTabFTL = kTabFT + M2 * L * 2;
 constexpr int kTabPw = kTabFTL + M2 * L * 2;
 constexpr int kTabPwSeg = kTabPw + L * MM * 8;
-constexpr int kTabPwBack = kTabPwSeg + MM * 8;
-constexpr int kTabHc = kTabPwBack + MM * 8;
+constexpr int kTabHc = kTabPwSeg + MM * 8;
 constexpr int kTabBytes = ((kTabHc + 16 + 255) / 256) * 256;
 
 // Complex fp64 power abar^n = exp(n Delta lambda).
@@ -266,11 +265,11 @@ __device__ __forceinline__ void cpow(double dt, float lre, float lim, double n, 
 // grid (H, 17), 320 threads.  Blocks y < 16: threads 0..255 take one (k, m)
 // each and evaluate abar^k while threads 256..319 run the ZOH step of mode m
 // into shared memory, then T = bbar abar^k and abar^{k+1} = abar^k abar;
-// block y = 16: abar^Lseg (threads 0..63) and abar^-back (64..127).  No
+// block y = 16: abar^Lseg (threads 0..63).  No
 // thread runs more than one fp64 power or ZOH step before the combine.
 constexpr int kTabThreads = 320;
 __global__ __launch_bounds__(kTabThreads) void zoh_tables_kernel(Problem p, idattn_params prm, int64_t Lseg,
-                                                                 int back, uint8_t* __restrict__ tab) {
+                                                                 uint8_t* __restrict__ tab) {
     __shared__ Zoh zs[MM];
     const int64_t h = blockIdx.x;
     uint8_t* th = tab + h * kTabBytes;
@@ -280,11 +279,9 @@ __global__ __launch_bounds__(kTabThreads) void zoh_tables_kernel(Problem p, idat
     const double dt = exp(static_cast<double>(log_dt));
     double pr = 0.0, pi = 0.0;
     if (blockIdx.y == 16) {
-        const int which = threadIdx.x >> 6;
-        if (which >= 2) return;
-        cpow(dt, lre, lim, which == 0 ? static_cast<double>(Lseg) : -static_cast<double>(back), pr, pi);
-        reinterpret_cast<float2*>(th + (which == 0 ? kTabPwSeg : kTabPwBack))[m] =
-            make_float2(static_cast<float>(pr), static_cast<float>(pi));
+        if (threadIdx.x >= MM) return;
+        cpow(dt, lre, lim, static_cast<double>(Lseg), pr, pi);
+        reinterpret_cast<float2*>(th + kTabPwSeg)[m] = make_float2(static_cast<float>(pr), static_cast<float>(pi));
         if (threadIdx.x == 0)
             reinterpret_cast<float2*>(th + kTabHc)[0] = make_float2(static_cast<float>(dt), static_cast<float>(1.0 / dt));
         return;
@@ -605,6 +602,19 @@ __device__ __forceinline__ void tile_copy_out(const void* src, _Float16* dst) {
         r[j] = *(__attribute__((address_space(3))) u4*)(uintptr_t)(lds_addr(src) + 16 * (512 * j + x));
 #pragma unroll
     for (int j = 0; j < kTilePieces<D>; ++j) reinterpret_cast<u4*>(dst)[512 * j + x] = r[j];
+}
+
+// The z^T tile of a ragged last chunk with its n = L - back valid tokens moved
+// to columns back .. L-1 (columns 0 .. back-1 zero), from the stored tile in
+// the shared-memory layout, by the 512 threads of one role.
+template <int D>
+__device__ __forceinline__ void shift_tile(const void* dst, const _Float16* src, int back) {
+    const int x = tid_now() & 511;
+    for (int e = x; e < D * L; e += 512) {
+        const int r = e / L, j = e % L;
+        const _Float16 val = j >= back ? src[o128(r, j - back)] : static_cast<_Float16>(0.f);
+        *(__attribute__((address_space(3))) _Float16*)(uintptr_t)(lds_addr(dst) + 2 * o128(r, j)) = val;
+    }
 }
 
 // ------------------------------------------------------------------ state
@@ -1092,6 +1102,13 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
     const int nch = static_cast<int>((t_end - t_begin + L - 1) / L);
     const int n_last = static_cast<int>(t_end - t_begin - static_cast<int64_t>(nch - 1) * L);
     const uint8_t* th = tab + h * kTabBytes;
+    // A ragged last chunk whose end state is stored: the loop skips its state
+    // update and the epilogue runs it with the valid tokens at the end of the
+    // chunk and the decay abar^n, so that every token keeps its own weight T[n-1-t]
+    // (a zero-padded chunk followed by abar^-(L-n) would carry the weights of its
+    // first tokens as tiny fp16 values and then amplify their rounding).
+    const bool tail_fix = seg == S - 1 && n_last < L && state_out != nullptr;
+    const float2* a_n = reinterpret_cast<const float2*>(th + kTabPw) + (n_last - 1) * MM;  // abar^n
 
     // only the first segment reads the stored tail (and writes the new one at its end)
     load_prologue<D, true>(sm, prm, seg == 0 ? tail_in : nullptr, b, h, H, static_cast<int>(p.W));
@@ -1188,7 +1205,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) accQ[tt] = mfma(aU, rd8(yb + 2 * 16 * tt * YR), accQ[tt]);
                 }
-                key_update<D>(U, sm.aL, kw, sm.zkT, sm.ft, ln);
+                if (!(tail_fix && c == nch - 1)) key_update<D>(U, sm.aL, kw, sm.zkT, sm.ft, ln);
             }
             if (c >= 1 && (kw == 2 || kw == 3)) {
                 const int ln = tid_now() & 63;
@@ -1249,9 +1266,13 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             if (c + 1 < nch) fm_write_q<D>(yo, sm.yq);  // y' of chunk c+1, built in phase 1
             lds_barrier();
         }
-        if (seg == S - 1 && state_out != nullptr)
-            u_store<D>(U, state_out + bh * MM * 2 * D * 2,
-                       n_last < L ? reinterpret_cast<const float2*>(th + kTabPwBack) : nullptr, kw);
+        if (tail_fix) {
+            lds_barrier();
+            shift_tile<D>(sm.zkT, zseg + (nch - 1) * tile2, L - n_last);
+            lds_barrier();
+            key_update<D>(U, a_n, kw, sm.zkT, sm.ft, tid_now() & 63);
+        }
+        if (seg == S - 1 && state_out != nullptr) u_store<D>(U, state_out + bh * MM * 2 * D * 2, nullptr, kw);
     } else {
         // ---------------- value waves
         const int vw = w - 8;
@@ -1295,7 +1316,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                     for (int tt = 0; tt < 4; ++tt) accO[tt] = mfma(bG, rd8(xb + 2 * 16 * tt * M2), accO[tt]);
                 }
                 // Gamma update with chunk c-1, once X Gamma has read the state before it
-                value_update<D>(G, sm.aH, bZ, sm.ft, ln);
+                if (!(tail_fix && c == nch)) value_update<D>(G, sm.aH, bZ, sm.ft, ln);
             }
             lds_barrier();
             // ---- phase 2: z_k^T (c+1); o^T += Z_v^T P~^T, Delta o (c-1); Z_v fragments (c)
@@ -1325,9 +1346,18 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             if (c < nch && own) load_bz(bZ, vw, sm.zvT, ln2);
             lds_barrier();
         }
-        if (own && seg == S - 1 && state_out != nullptr)
-            g_store<D>(G, state_out + bh * MM * 2 * D * 2,
-                       n_last < L ? reinterpret_cast<const float2*>(th + kTabPwBack) : nullptr, vw);
+        if (tail_fix) {
+            lds_barrier();
+            shift_tile<D>(sm.zvT, zseg + (nch - 1) * tile2 + D * L, L - n_last);
+            lds_barrier();
+            if (own) {
+                const int ln = tid_now() & 63;
+                half8 bZl[2];
+                load_bz(bZl, vw, sm.zvT, ln);
+                value_update_plain<D>(G, a_n, bZl, sm.ft, ln);
+            }
+        }
+        if (own && seg == S - 1 && state_out != nullptr) g_store<D>(G, state_out + bh * MM * 2 * D * 2, nullptr, vw);
     }
     if (seg == 0 && tail_out != nullptr) {
         // New conv tail: positions N-W+1 .. N-1 of q and k, where negative positions
@@ -1371,8 +1401,7 @@ hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, con
     const int64_t pairs = p.B * p.H;
     _Float16* zt = reinterpret_cast<_Float16*>(ws + static_cast<size_t>(S - 1) * pairs * MM * 2 * D * 2);
     const int64_t last_len = p.N - (S - 1) * Lseg;
-    const int back = static_cast<int>((L - last_len % L) % L);
-    zoh_tables_kernel<<<dim3(static_cast<unsigned>(p.H), 17), kTabThreads, 0, stream>>>(p, prm, Lseg, back, tab);
+    zoh_tables_kernel<<<dim3(static_cast<unsigned>(p.H), 17), kTabThreads, 0, stream>>>(p, prm, Lseg, tab);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     segment_state_kernel<D><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(p, prm, k16, v16, t16, tab, ws,

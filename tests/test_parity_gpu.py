@@ -143,6 +143,34 @@ def test_decode_step_unit_feature_map(fs, io):
     assert np.array_equal(down(tl), tl_ref.astype(np.float32))
 
 
+# Learned decays can be much faster than the S4D-Lin init: Delta |Re lambda| up
+# to 6 per token.  A ragged last chunk must still leave an exact end state
+# (before the fix, a zero-padded chunk corrected by abar^-(L-n) lost the state:
+# relative error 2.5e-2 at Delta = 0.1, Re lambda = -2 and NaN at Delta = 1).
+# Shapes: six one-chunk segments with the carry kernel (B=1, H=2, N=333), and
+# four segments with the carry folded into the forward (B=4, H=16, N=200).
+@pytest.mark.parametrize("dt,re_lam", [(0.1, -2.0), (0.3, -2.0), (1.0, -0.5), (3.0, -2.0)])
+@pytest.mark.parametrize("shape", [dict(B=1, H=2, N=333), dict(B=4, H=16, N=200, d=64)], ids=["carry", "fold"])
+def test_ragged_end_state_fast_decay(fs, dt, re_lam, shape):
+    c = WL.make_case("1p3b", seed=1, tag=71, **shape)
+    s = c.spec
+    p = dict(c.params)
+    p["log_dt"] = np.full_like(p["log_dt"], np.log(dt))
+    A = np.array(p["A"])
+    A[..., 0] = re_lam
+    p["A"] = A.astype(np.float32)
+    st0, tl0 = WL.make_decode_state(s, seed=2)
+    o_ref, st_ref, _ = oracle.forward(c.q, c.k, c.v, p, state_in=st0, tail_in=tl0)
+    pd = fs.params_to_device(p)
+    o, st, _ = fs.forward(up(c.q, "bf16"), up(c.k, "bf16"), up(c.v, "bf16"), pd, return_state=True, algo="chunked",
+                          state_in=state_dev(st0), tail_in=up(tl0, "bf16"))
+    _sync()
+    e_o = rel_l2(down(o), o_ref)
+    e_s = rel_l2(state_np(st), st_ref)
+    print(f"dt={dt} re={re_lam} {shape}: o relL2 {e_o:.2e}, state relL2 {e_s:.2e}")
+    assert e_o <= GATE_BF16 and e_s <= GATE_BF16, (e_o, e_s)
+
+
 def _pairs(s, n, seed):
     r = np.random.default_rng(seed)
     idx = r.choice(s["B"] * s["H"], size=min(n, s["B"] * s["H"]), replace=False)
