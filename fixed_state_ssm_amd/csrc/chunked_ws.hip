@@ -244,7 +244,10 @@ __device__ __forceinline__ half8 to_half8(const f4& a, const f4& b) {
 // Per-head tables, one launch per forward (fp64 arithmetic):
 //   ft, ftl [M2][L] fp16, swizzled rows: F^T[m'][j] = T_{m'}[L-1-j] = ft + ftl
 //   pw [L][MM] float2: abar^{k+1}
-//   pwseg[MM] float2: abar^{Lseg};  hc: Delta, 1/Delta
+//   pwseg[MM] float2: abar^{Lseg};  hc float4: Delta, 1/Delta, kappa, 1/kappa
+// with kappa a power of two per head such that kappa max_m |bbar_m| is in
+// [1/2, 1): F carries kappa (so that a small Delta |B| leaves the fp16 table
+// in the normal range), and so do the states derived from it.
 // with T_{m'}[k] the real (m' even) or imaginary (m' odd) part of bbar_m abar_m^k.
 constexpr int kTabFT = 0;
 constexpr int kTabFTL = kTabFT + M2 * L * 2;
@@ -265,12 +268,14 @@ __device__ __forceinline__ void cpow(double dt, float lre, float lim, double n, 
 // grid (H, 17), 320 threads.  Blocks y < 16: threads 0..255 take one (k, m)
 // each and evaluate abar^k while threads 256..319 run the ZOH step of mode m
 // into shared memory, then T = bbar abar^k and abar^{k+1} = abar^k abar;
-// block y = 16: abar^Lseg (threads 0..63).  No
+// block y = 16: abar^Lseg (threads 0..63).  The ZOH wave of a block y < 16
+// also finds the head's scale kappa.  No
 // thread runs more than one fp64 power or ZOH step before the combine.
 constexpr int kTabThreads = 320;
 __global__ __launch_bounds__(kTabThreads) void zoh_tables_kernel(Problem p, idattn_params prm, int64_t Lseg,
                                                                  uint8_t* __restrict__ tab) {
     __shared__ Zoh zs[MM];
+    __shared__ double kap_s;
     const int64_t h = blockIdx.x;
     uint8_t* th = tab + h * kTabBytes;
     const int m = threadIdx.x & (MM - 1);
@@ -282,19 +287,31 @@ __global__ __launch_bounds__(kTabThreads) void zoh_tables_kernel(Problem p, idat
         if (threadIdx.x >= MM) return;
         cpow(dt, lre, lim, static_cast<double>(Lseg), pr, pi);
         reinterpret_cast<float2*>(th + kTabPwSeg)[m] = make_float2(static_cast<float>(pr), static_cast<float>(pi));
-        if (threadIdx.x == 0)
-            reinterpret_cast<float2*>(th + kTabHc)[0] = make_float2(static_cast<float>(dt), static_cast<float>(1.0 / dt));
         return;
     }
     const int k = 4 * static_cast<int>(blockIdx.y) + (threadIdx.x >> 6);
-    if (threadIdx.x >= 256)
-        zs[m] = zoh_mode(log_dt, lre, lim, prm.Bc[(h * MM + m) * 2], prm.Bc[(h * MM + m) * 2 + 1]);
-    else
+    if (threadIdx.x >= 256) {  // one wave: the ZOH step of mode m, then the head's scale kappa
+        const Zoh z = zoh_mode(log_dt, lre, lim, prm.Bc[(h * MM + m) * 2], prm.Bc[(h * MM + m) * 2 + 1]);
+        zs[m] = z;
+        double b2 = z.br * z.br + z.bi * z.bi;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) b2 = fmax(b2, __shfl_xor(b2, off, kWave));
+        if (m == 0) {
+            int ex = 0;
+            if (b2 > 0.0 && b2 < 1e300) frexp(sqrt(b2), &ex);  // max |bbar| = f 2^ex, f in [1/2, 1)
+            ex = ex < -60 ? -60 : ex > 60 ? 60 : ex;
+            kap_s = ldexp(1.0, -ex);
+        }
+    } else
         cpow(dt, lre, lim, static_cast<double>(k), pr, pi);  // abar^k
     __syncthreads();
     if (threadIdx.x >= 256) return;
+    const double kap = kap_s;
+    if (blockIdx.y == 0 && threadIdx.x == 0)
+        reinterpret_cast<float4*>(th + kTabHc)[0] = make_float4(static_cast<float>(dt), static_cast<float>(1.0 / dt),
+                                                               static_cast<float>(kap), static_cast<float>(1.0 / kap));
     const Zoh z = zs[m];
-    const double tv[2] = {z.br * pr - z.bi * pi, z.br * pi + z.bi * pr};
+    const double tv[2] = {kap * (z.br * pr - z.bi * pi), kap * (z.br * pi + z.bi * pr)};
     _Float16* ft = reinterpret_cast<_Float16*>(th + kTabFT);
     _Float16* ftl = reinterpret_cast<_Float16*>(th + kTabFTL);
 #pragma unroll
@@ -621,53 +638,46 @@ __device__ __forceinline__ void shift_tile(const void* dst, const _Float16* src,
 // Key wave kw (0..7), lane (g, i):  U[rt][jj] = U_m[r],  r = 16rt + 4g + jj, m' = 16kw + i
 // Value wave vw (0..D/16-1):        G[mt][jj] = Gamma_m[c], m' = 16mt + 4g + jj, c = 16vw + i
 // Memory layout: float [M][2D][2] (complex), columns 0..D-1 hold U, D..2D-1 Gamma.
+// Loads multiply by `scale` (zeros when src is NULL); stores multiply by `scale`.
 template <int D>
-__device__ __forceinline__ void u_load(f4 (&U)[Cfg<D>::RT], const float* src, int kw) {
+__device__ __forceinline__ void u_load(f4 (&U)[Cfg<D>::RT], const float* src, int kw, float scale) {
     const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15, mp = 16 * kw + i;
 #pragma unroll
     for (int rt = 0; rt < Cfg<D>::RT; ++rt)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-            U[rt][jj] = src ? src[((mp >> 1) * 2 * D + 16 * rt + 4 * g + jj) * 2 + (mp & 1)] : 0.f;
+            U[rt][jj] = src ? scale * src[((mp >> 1) * 2 * D + 16 * rt + 4 * g + jj) * 2 + (mp & 1)] : 0.f;
 }
 template <int D>
-__device__ __forceinline__ void g_load(f4 (&G)[8], const float* src, int vw) {
+__device__ __forceinline__ void g_load(f4 (&G)[8], const float* src, int vw, float scale) {
     const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15, c = 16 * vw + i;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int mp = 16 * mt + 4 * g + jj;
-            G[mt][jj] = src ? src[((mp >> 1) * 2 * D + D + c) * 2 + (mp & 1)] : 0.f;
+            G[mt][jj] = src ? scale * src[((mp >> 1) * 2 * D + D + c) * 2 + (mp & 1)] : 0.f;
         }
 }
-// Stores, first multiplying every mode by corr[m] when corr is not NULL.
 template <int D>
-__device__ __forceinline__ void u_store(const f4 (&U)[Cfg<D>::RT], float* dst, const float2* corr, int kw) {
+__device__ __forceinline__ void u_store(const f4 (&U)[Cfg<D>::RT], float* dst, int kw, float scale) {
     const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15, mp = 16 * kw + i;
-    const float2 c = corr ? corr[mp >> 1] : make_float2(1.f, 0.f);
-    const float sc = (mp & 1) ? c.y : -c.y;
 #pragma unroll
     for (int rt = 0; rt < Cfg<D>::RT; ++rt)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const float u = U[rt][jj];
-            const float pu = dpp_mov<0xB1>(u);  // other part of the same mode (lane i ^ 1)
-            dst[((mp >> 1) * 2 * D + 16 * rt + 4 * g + jj) * 2 + (mp & 1)] = fmaf(sc, pu, c.x * u);
-        }
+        for (int jj = 0; jj < 4; ++jj)
+            dst[((mp >> 1) * 2 * D + 16 * rt + 4 * g + jj) * 2 + (mp & 1)] = scale * U[rt][jj];
 }
 template <int D>
-__device__ __forceinline__ void g_store(const f4 (&G)[8], float* dst, const float2* corr, int vw) {
+__device__ __forceinline__ void g_store(const f4 (&G)[8], float* dst, int vw, float scale) {
     const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15, c = 16 * vw + i;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int m = 8 * mt + 2 * g + q;
-            const float2 a = corr ? corr[m] : make_float2(1.f, 0.f);
-            const float gr = G[mt][2 * q], gi = G[mt][2 * q + 1];
             *reinterpret_cast<float2*>(dst + (static_cast<int64_t>(m) * 2 * D + D + c) * 2) =
-                make_float2(a.x * gr - a.y * gi, a.x * gi + a.y * gr);
+                make_float2(scale * G[mt][2 * q], scale * G[mt][2 * q + 1]);
         }
 }
 
@@ -930,7 +940,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
     if (key) {
         const int kw = w;
         f4 U[Cfg<D>::RT];
-        u_load<D>(U, nullptr, kw);
+        u_load<D>(U, nullptr, kw, 1.f);
         const __amdgpu_buffer_rsrc_t rk = seq_rsrc<D>(k, b, h, p.N, p.H, t_end);
         uint32_t rkk[11];
         fm_load<D, true>(rkk, rk, rsb, t_begin);
@@ -958,7 +968,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
         const int vw = w - 8;
         const bool own = upd && vw < D / 16;
         f4 G[8];
-        if (own) g_load<D>(G, nullptr, vw);
+        if (own) g_load<D>(G, nullptr, vw, 1.f);
         const __amdgpu_buffer_rsrc_t rv = seq_rsrc<D>(v, b, h, p.N, p.H, t_end);
         uint32_t rvv[8];
         fm_load<D, false>(rvv, rv, rsb, t_begin);
@@ -1020,7 +1030,8 @@ __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, const flo
         abi = (mode * 2 * D + D + 16 * vw + i + (k >> 1)) * 2;
     }
     const float2 a = reinterpret_cast<const float2*>(tab + h * kTabBytes + kTabPwSeg)[mode];
-    float2 c = state_in ? make_float2(state_in[bh * 256 * D + abi], state_in[bh * 256 * D + abi + 1])
+    const float kap = reinterpret_cast<const float4*>(tab + h * kTabBytes + kTabHc)[0].z;  // states carry kappa
+    float2 c = state_in ? make_float2(kap * state_in[bh * 256 * D + abi], kap * state_in[bh * 256 * D + abi + 1])
                         : make_float2(0.f, 0.f);
     const int64_t sst = p.B * p.H * 256 * D;  // floats per segment
     float* base = ws + bh * 256 * D + o;
@@ -1119,8 +1130,11 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
     for (int e = tid; e < 16 * MM; e += NTH) sm.pw[e / MM][e % MM] = reinterpret_cast<const float2*>(th + kTabPw)[e];
     for (int e = tid; e < L * RP * 2 / 16; e += NTH)
         reinterpret_cast<u4*>(sm.gp)[e] = reinterpret_cast<u4*>(sm.pp)[e] = u4{0u, 0u, 0u, 0u};
-    const float2 hc = reinterpret_cast<const float2*>(th + kTabHc)[0];
-    const float dt = hc.x, inv_dt = hc.y;
+    // Delta, 1/Delta and the head's table scale kappa, 1/kappa: F and the states
+    // carry kappa, undone by sigma~ / kappa, by Delta / kappa on the output and on
+    // the state's way in and out
+    const float4 hc = reinterpret_cast<const float4*>(th + kTabHc)[0];
+    const float dt = hc.x * hc.w, inv_dt = hc.y * hc.w, kap = hc.z, inv_kap = hc.w;
     const int rsb = static_cast<int>(H * D * 2);  // token stride, bytes
     // state entering the segment: state_in, the carry chain's output, or (fold)
     // state_in followed by the end states of the segments before this one
@@ -1144,7 +1158,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         if (seg > 0 && !fold) {
             u_load_lane<D>(U, src, kw);
         } else {
-            u_load<D>(U, sin, kw);
+            u_load<D>(U, sin, kw, kap);
             if (nfold > 0) u_fold<D, kFoldTiles>(U, e0, estride, nfold, aseg, kw);
         }
         const __amdgpu_buffer_rsrc_t rq = seq_rsrc<D>(q, b, h, N, H, t_end);
@@ -1272,7 +1286,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             lds_barrier();
             key_update<D>(U, a_n, kw, sm.zkT, sm.ft, tid_now() & 63);
         }
-        if (seg == S - 1 && state_out != nullptr) u_store<D>(U, state_out + bh * MM * 2 * D * 2, nullptr, kw);
+        if (seg == S - 1 && state_out != nullptr) u_store<D>(U, state_out + bh * MM * 2 * D * 2, kw, inv_kap);
     } else {
         // ---------------- value waves
         const int vw = w - 8;
@@ -1282,7 +1296,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             if (seg > 0 && !fold) {
                 g_load_lane<D>(G, src, vw);
             } else {
-                g_load<D>(G, sin, vw);
+                g_load<D>(G, sin, vw, kap);
                 if (nfold > 0) g_fold<D, kFoldTiles>(G, e0, estride, nfold, aseg, vw);
             }
         }
@@ -1357,7 +1371,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                 value_update_plain<D>(G, a_n, bZl, sm.ft, ln);
             }
         }
-        if (own && seg == S - 1 && state_out != nullptr) g_store<D>(G, state_out + bh * MM * 2 * D * 2, nullptr, vw);
+        if (own && seg == S - 1 && state_out != nullptr) g_store<D>(G, state_out + bh * MM * 2 * D * 2, vw, inv_kap);
     }
     if (seg == 0 && tail_out != nullptr) {
         // New conv tail: positions N-W+1 .. N-1 of q and k, where negative positions
