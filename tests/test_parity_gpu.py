@@ -197,6 +197,27 @@ def test_small_step_scaled_tables(fs, dt, b_scale, shape):
     assert e_o <= GATE_BF16 and e_s <= GATE_BF16, (e_o, e_s)
 
 
+# The chunked path holds the queries' SiLU outputs and the scaled mode scores as
+# fp16 operands, so it has an input range: q, k scaled by 2^-8 .. 2^11 (exact
+# powers of two, so the stored inputs stay bf16) pass the gate (2^12 reaches
+# 1.9e-3); at 2^-12 and 2^13 its output overflows (a documented limit; the
+# sequential path has none).
+@pytest.mark.parametrize("e", [-8, -4, 8, 11])
+def test_chunked_query_scale_range(fs, e):
+    c = WL.make_case("1p3b", seed=1, tag=73, B=1, H=2, N=333)
+    sc = 2.0 ** e
+    q, k = np.asarray(c.q) * sc, np.asarray(c.k) * sc
+    o_ref, st_ref, _ = oracle.forward(q, k, c.v, c.params)
+    p = fs.params_to_device(c.params)
+    for algo in ("sequential", "chunked"):
+        o, st, _ = fs.forward(up(q, "bf16"), up(k, "bf16"), up(c.v, "bf16"), p, return_state=True, algo=algo)
+        _sync()
+        e_o = rel_l2(down(o), o_ref)
+        e_s = rel_l2(state_np(st), st_ref)
+        print(f"q, k x 2^{e} {algo}: o relL2 {e_o:.2e}, state relL2 {e_s:.2e}")
+        assert e_o <= GATE_BF16 and e_s <= GATE_BF16, (algo, e_o, e_s)
+
+
 def _pairs(s, n, seed):
     r = np.random.default_rng(seed)
     idx = r.choice(s["B"] * s["H"], size=min(n, s["B"] * s["H"]), replace=False)
