@@ -17,10 +17,13 @@
 // Scalings that keep fp16 operands in range and save arithmetic:
 //  * the conv weights carry a factor -log2(e), so the conv output c' gives
 //    SiLU through y' = c' / (1 + 2^c') = -y / ln 2 with no extra multiply;
-//  * y' is stored unscaled and the per-token factor
-//    sigma~_t = -ln2 / (Delta (ln^2 2 ||y'||^2 + eps)) is applied to s, so
-//    that the s~ = s / Delta kept in shared memory, P~ = P / Delta and
-//    X = s~ abar^{t+1} = s abar^{t+1} / Delta are all O(1);  o = Delta (P~ Z_v + X Gamma).
+//  * y' of each token is scaled by a power of two r_t with (r_t ||y'||)^2 in
+//    [1, 4), and the mode scores are kept as s~_t = K (S + abar^{t+1} Q) with one
+//    constant K = -ln2 / (4 Delta kappa), so that s~, P~ = Re(s~ T^T) and
+//    X = s~ abar^{t+1} kept in fp16 are O(1) for queries of any scale; the
+//    rest of the true scale, sigma_t = -ln2 / (Delta (ln^2 2 ||y'||^2 + eps)),
+//    returns on the output as o_t = omega_t (P~ Z_v + Re X Gamma)_t with
+//    omega_t = 4 Delta / (kappa r_t (ln^2 2 ||y'||^2 + eps)) (kappa below).
 //  * T enters every chunk of every sequence, so its fp16 rounding error would
 //    add up coherently; it is carried as a pair of fp16 values (about 22
 //    bits) and every product with T is two MFMAs.
@@ -339,7 +342,7 @@ struct SmemFwd {
     // window C
     _Float16 gp[L * RP];          // G' (zero above the causal band, never rewritten there)
     _Float16 pp[L * RP];          // P~ [t][l] (likewise)
-    float sig[2][L];              // sigma~_t, by chunk parity
+    float om[3][L];               // omega_t, output factor of each token, by chunk mod 3
     float2 aL[MM];                // abar^L
     float2 aH[MM];                // abar^(L/2)
     float2 pw[16][PWS];           // abar^{k+1}, k = 0..15
@@ -533,21 +536,33 @@ __device__ __forceinline__ void fm_values(const uint32_t (&r)[8], const SM& sm, 
     write_zt(zT, cgi, tb, x);
 }
 
-// y' of the thread's 8 tokens, kept as fp16 pairs until fm_write_q, and sigma~ to sig.
+// y' of the thread's 8 tokens, each token scaled by a power of two r_t with
+// (r_t ||y'||)^2 in [1, 4) (so that the fp16 operand neither overflows nor
+// loses precision, whatever the scale of q), kept as fp16 pairs until
+// fm_write_q; the token's output factor omega_t to om.  With the scaled y'
+// the mode scores are s~_t = K (S + abar^{t+1} Q) for one constant K, and
+//   o_t = omega_t (P~ Z_v + Re X Gamma)_t,
+//   omega_t = 4 Delta / (kappa r_t (ln^2 2 ||y'||^2 + eps))  (the root of the
+// bracket for the unit-norm map); odt = 4 Delta / kappa.
 template <int D, class SM>
-__device__ __forceinline__ void fm_queries(half2v (&yo)[8], const uint32_t (&r)[11], SM& sm, float* sig,
-                                           float eps_feat, float inv_dt, bool unit, int fi = feat_index<D>()) {
+__device__ __forceinline__ void fm_queries(half2v (&yo)[8], const uint32_t (&r)[11], SM& sm, float* om,
+                                           float eps_feat, float odt, bool unit, int fi = feat_index<D>()) {
     if (fi >= Cfg<D>::NF) return;
     const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
-    float y[2][8], ss[8];
+    float y[2][8], ss[8], rs[8];
     conv_silu<D>(r, sm.wq, cgi, y, ss);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) yo[s] = half2v{static_cast<_Float16>(y[0][s]), static_cast<_Float16>(y[1][s])};
     const float tot = reduce_scatter8<Cfg<D>::CP>(ss);
+    // tot in [2^e, 2^(e+1)): r_t = 2^-floor(e/2), 1/r_t = 2^floor(e/2) (tot = 0 gives r_t = 2^64)
+    const int e = static_cast<int>((__float_as_uint(tot) >> 23) & 255u) - 127;
+    const float rt = __uint_as_float(static_cast<uint32_t>(127 - (e >> 1)) << 23);
+    const float inv_rt = __uint_as_float(static_cast<uint32_t>(127 + (e >> 1)) << 23);
+    share_factor<D>(sm, rt, rs);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+        yo[s] = half2v{static_cast<_Float16>(y[0][s] * rs[s]), static_cast<_Float16>(y[1][s] * rs[s])};
     if (cgi < 8) {
         const float den = fmaf(kLn2Sq, tot, eps_feat);
-        sig[8 * tb + scatter_token(cgi)] =
-            -kLn2 * inv_dt * (unit ? __builtin_amdgcn_rsqf(den) : __builtin_amdgcn_rcpf(den));
+        om[8 * tb + scatter_token(cgi)] = odt * inv_rt * (unit ? __builtin_amdgcn_rsqf(den) : __builtin_amdgcn_rcpf(den));
     }
 }
 template <int D>
@@ -1131,10 +1146,12 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
     for (int e = tid; e < L * RP * 2 / 16; e += NTH)
         reinterpret_cast<u4*>(sm.gp)[e] = reinterpret_cast<u4*>(sm.pp)[e] = u4{0u, 0u, 0u, 0u};
     // Delta, 1/Delta and the head's table scale kappa, 1/kappa: F and the states
-    // carry kappa, undone by sigma~ / kappa, by Delta / kappa on the output and on
+    // carry kappa, undone by K and omega (both carry 1 / kappa) and on
     // the state's way in and out
     const float4 hc = reinterpret_cast<const float4*>(th + kTabHc)[0];
-    const float dt = hc.x * hc.w, inv_dt = hc.y * hc.w, kap = hc.z, inv_kap = hc.w;
+    const float kap = hc.z, inv_kap = hc.w;
+    const float odt = 4.f * hc.x * hc.w;        // 4 Delta / kappa, the output factor's constant part
+    const float ks = -0.25f * kLn2 * hc.y * hc.w;  // K = -ln2 / (4 Delta kappa), the mode scores' scale
     const int rsb = static_cast<int>(H * D * 2);  // token stride, bytes
     // state entering the segment: state_in, the carry chain's output, or (fold)
     // state_in followed by the end states of the segments before this one
@@ -1167,7 +1184,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         halo_fix<D>(rqq, sm, 0, t_begin);
         {
             half2v yo[8];
-            fm_queries<D>(yo, rqq, sm, sm.sig[0], p.eps_feat, inv_dt, p.unit_feat);
+            fm_queries<D>(yo, rqq, sm, sm.om[0], p.eps_feat, odt, p.unit_feat);
             fm_write_q<D>(yo, sm.yq);
         }
         if (nch > 1) fm_load<D, true>(rqq, rq, rsb, t_begin + L);
@@ -1177,9 +1194,9 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             f4 accQ[4];
             half2v yo[8];  // y' of chunk c+1, written to the tile in phase 2
             if (c + 1 < nch) {
-                // queries' features of chunk c+1 (sigma~ goes to the buffer of parity c+1,
-                // last read in phase 2 of the previous step); the raw tokens of c+2 follow
-                fm_queries<D>(yo, rqq, sm, sm.sig[(c + 1) & 1], p.eps_feat, inv_dt, p.unit_feat);
+                // queries' features of chunk c+1 (omega goes to buffer (c+1) mod 3, last
+                // read in phase 2 of the previous step); the raw tokens of c+2 follow
+                fm_queries<D>(yo, rqq, sm, sm.om[(c + 1) % 3], p.eps_feat, odt, p.unit_feat);
                 if (c + 2 < nch) {
                     step_fence();
                     fm_load<D, true>(rqq, rq, rsb, t_begin + static_cast<int64_t>(c + 2) * L);
@@ -1229,9 +1246,8 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             // ---- phase 2
             if (c < nch) {
                 const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
-                const float* sig = sm.sig[c & 1];
                 // S^T = T^T G'^T (K order reversed: element jj <-> k = 32kb + 8g + 7 - jj),
-                // s~ = sigma~ (S + abar^{t+1} Q), X = s~ abar^{t+1}
+                // s~ = K (S + abar^{t+1} Q), X = s~ abar^{t+1}
                 f4 accS[4];
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) accS[tt] = f4{0.f, 0.f, 0.f, 0.f};
@@ -1258,7 +1274,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                 const uint32_t x_st = lds_addr(sm.xc) + pst, s_st = lds_addr(sm.sc) + pst;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
-                    const float sg = sig[16 * tt + i];
+                    const float sg = ks;
                     float sv[4], xv[4];
 #pragma unroll
                     for (int qq = 0; qq < 2; ++qq) {
@@ -1350,10 +1366,12 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                     for (int tt = 0; tt < 4; ++tt)
                         accO[tt] = mfma(bZ[kb], rd8(c_pp + 2 * (16 * tt * RP + 32 * kb)), accO[tt]);
                 const uint32_t olane = static_cast<uint32_t>(i * rsb + 2 * (16 * vw + 4 * g));
+                const float* om = sm.om[(c - 1) % 3];  // chunk c-1, written in phase 1 of step c-2
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     const uint32_t toff = static_cast<uint32_t>((tp + 16 * tt) * rsb);
-                    const u2 pk = {pack_bf16(accO[tt][0] * dt, accO[tt][1] * dt), pack_bf16(accO[tt][2] * dt, accO[tt][3] * dt)};
+                    const float w = om[16 * tt + i];
+                    const u2 pk = {pack_bf16(accO[tt][0] * w, accO[tt][1] * w), pack_bf16(accO[tt][2] * w, accO[tt][3] * w)};
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, pk), ob, olane + toff, 0, 0);
                 }
             }

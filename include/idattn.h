@@ -72,10 +72,7 @@ typedef enum idattn_algo {
     IDATTN_ALGO_AUTO = 0,        /* CHUNKED for bf16 I/O, SEQUENTIAL for f32 I/O          */
     IDATTN_ALGO_SEQUENTIAL = 1,  /* fp32 recurrence, one time step after another         */
     IDATTN_ALGO_CHUNKED = 2      /* chunked parallel-in-time scan, fp16 MFMA operands,
-                                    fp32 accumulation and state; bf16 I/O only.  Input
-                                    range: q, k of order 2^-8 .. 2^11 (tested); far
-                                    outside it the fp16 operands overflow and the
-                                    output is not finite - use SEQUENTIAL there          */
+                                    fp32 accumulation and state; bf16 I/O only           */
 } idattn_algo;
 
 /* Norm of the feature map.  The gist.science summaries print the squared

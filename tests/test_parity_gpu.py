@@ -197,12 +197,12 @@ def test_small_step_scaled_tables(fs, dt, b_scale, shape):
     assert e_o <= GATE_BF16 and e_s <= GATE_BF16, (e_o, e_s)
 
 
-# The chunked path holds the queries' SiLU outputs and the scaled mode scores as
-# fp16 operands, so it has an input range: q, k scaled by 2^-8 .. 2^11 (exact
-# powers of two, so the stored inputs stay bf16) pass the gate (2^12 reaches
-# 1.9e-3); at 2^-12 and 2^13 its output overflows (a documented limit; the
-# sequential path has none).
-@pytest.mark.parametrize("e", [-8, -4, 8, 11])
+# The chunked path holds the queries' SiLU outputs and the mode scores as fp16
+# operands; each token's y' is scaled by a power of two and the rest of its
+# scale applied on the output, so queries of any scale keep the gate.  q, k
+# scaled by exact powers of two (the stored inputs stay bf16); before the
+# per-token scaling, 2^-12 and 2^13 gave non-finite outputs.
+@pytest.mark.parametrize("e", [-12, -8, -4, 8, 11, 13])
 def test_chunked_query_scale_range(fs, e):
     c = WL.make_case("1p3b", seed=1, tag=73, B=1, H=2, N=333)
     sc = 2.0 ** e
