@@ -134,6 +134,21 @@ def test_chunked_needs_bf16():
     assert e.value.status_name == "IDATTN_ERR_UNSUPPORTED"
 
 
+def test_chunked_offset_limit():
+    """The chunked kernels address one (b, h) sequence of bf16 [N][H][d] with
+    32-bit byte offsets: N H d 2 < 2^31 is chunked, beyond it only the
+    sequential path (chosen by AUTO) runs."""
+    H, d = 16, 128
+    n_ok = (1 << 31) // (H * d * 2) - 1
+    assert fs.idattn_forward_workspace_size(dims(B=1, N=n_ok, H=H, d=d, M=64, algo="chunked")) > 0
+    with pytest.raises(fs.IdattnError) as e:
+        fs.idattn_forward_workspace_size(dims(B=1, N=n_ok + 1, H=H, d=d, M=64, algo="chunked"))
+    assert e.value.status_name == "IDATTN_ERR_UNSUPPORTED"
+    auto = fs.idattn_forward_workspace_size(dims(B=1, N=n_ok + 1, H=H, d=d, M=64, algo="auto"))
+    seq = fs.idattn_forward_workspace_size(dims(B=1, N=n_ok + 1, H=H, d=d, M=64, algo="sequential"))
+    assert auto == seq
+
+
 def test_workspace_size_zero_tokens():
     assert fs.idattn_forward_workspace_size(dims(N=0)) == 0
 
