@@ -1154,7 +1154,10 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
     const float ks = -0.25f * kLn2 * hc.y * hc.w;  // K = -ln2 / (4 Delta kappa), the mode scores' scale
     const int rsb = static_cast<int>(H * D * 2);  // token stride, bytes
     // state entering the segment: state_in, the carry chain's output, or (fold)
-    // state_in followed by the end states of the segments before this one
+    // state_in followed by the end states of the segments before this one.
+    // state_in is read here, in the prologue; only the last segment's block writes
+    // state_out, after its whole loop, and blocks are dispatched in index order
+    // with that block last, so the state may be updated in place.
     const int64_t sstride = MM * 2 * D * 2;  // floats per (b, h) state
     const float* sin = state_in ? state_in + bh * sstride : nullptr;
     const float* src = carry + (static_cast<int64_t>(seg > 0 ? seg - 1 : 0) * p.B * p.H + bh) * sstride;
