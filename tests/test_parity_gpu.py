@@ -202,19 +202,21 @@ def test_small_step_scaled_tables(fs, dt, b_scale, shape):
 # scale applied on the output, so queries of any scale keep the gate.  q, k
 # scaled by exact powers of two (the stored inputs stay bf16); before the
 # per-token scaling, 2^-12 and 2^13 gave non-finite outputs.
+@pytest.mark.parametrize("feature_norm", ["squared", "unit"])
 @pytest.mark.parametrize("e", [-12, -8, -4, 8, 11, 13])
-def test_chunked_query_scale_range(fs, e):
+def test_chunked_query_scale_range(fs, e, feature_norm):
     c = WL.make_case("1p3b", seed=1, tag=73, B=1, H=2, N=333)
     sc = 2.0 ** e
     q, k = np.asarray(c.q) * sc, np.asarray(c.k) * sc
-    o_ref, st_ref, _ = oracle.forward(q, k, c.v, c.params)
+    o_ref, st_ref, _ = oracle.forward(q, k, c.v, c.params, feature_norm=feature_norm)
     p = fs.params_to_device(c.params)
     for algo in ("sequential", "chunked"):
-        o, st, _ = fs.forward(up(q, "bf16"), up(k, "bf16"), up(c.v, "bf16"), p, return_state=True, algo=algo)
+        o, st, _ = fs.forward(up(q, "bf16"), up(k, "bf16"), up(c.v, "bf16"), p, return_state=True, algo=algo,
+                              feature_norm=feature_norm)
         _sync()
         e_o = rel_l2(down(o), o_ref)
         e_s = rel_l2(state_np(st), st_ref)
-        print(f"q, k x 2^{e} {algo}: o relL2 {e_o:.2e}, state relL2 {e_s:.2e}")
+        print(f"q, k x 2^{e} {feature_norm} {algo}: o relL2 {e_o:.2e}, state relL2 {e_s:.2e}")
         assert e_o <= GATE_BF16 and e_s <= GATE_BF16, (algo, e_o, e_s)
 
 
