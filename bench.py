@@ -154,9 +154,28 @@ def decode_bench(torch, fs, steps, warmup):
     ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
     med = ms[len(ms) // 2]
     nbytes = 2 * B * H * M * 2 * d * 8 + 4 * B * H * d * 2 + 2 * B * H * 2 * (W - 1) * d * 2
+    # several tokens per sequence in one call: the decode step over NT tokens
+    # (one sweep of the state for all of them), state and tail in place
+    multi = {}
+    for NT in (4, 8):
+        tk = [torch.randn((B, NT, H, d), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3)]
+        o_m = torch.empty_like(tk[0])
+        dims_m = fs.make_dims(B, NT, H, d, M, W, "bf16")
+        for _ in range(warmup):
+            fs.idattn_decode_step(dims_m, prm, tk[0], tk[1], tk[2], o_m, state, tail)
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            e0.record()
+            fs.idattn_decode_step(dims_m, prm, tk[0], tk[1], tk[2], o_m, state, tail)
+            e1.record()
+        torch.cuda.synchronize()
+        ms_m = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        med_m = ms_m[len(ms_m) // 2]
+        multi[f"tokens_{NT}"] = {"ms_per_call_median": med_m, "tokens_per_s": B * NT / (med_m * 1e-3)}
     return {"workload": "decode: 256 sequences x 16 heads, d=R=128, M=64, W=4, bf16 I/O, fp32 state "
                         "prefilled by a 2048-token forward",
             "tokens_per_s": B / (med * 1e-3), "ms_per_step_median": med,
+            "multi_token": dict(multi, path="idattn_decode_step with several tokens per sequence, state and tail in place"),
             "roofline": {"bound": "hbm", "achieved": nbytes / (med * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                          "algorithmic_bytes": nbytes}}

@@ -66,14 +66,18 @@ def forward(q, k, v, params: dict, *, state_in=None, tail_in=None, return_state=
 
 def decode_step(q_t, k_t, v_t, params: dict, state, tail, *, eps_feat=1e-6, eps_norm=1e-6, feature_norm="squared",
                 stream=None):
-    """One token per sequence: q_t, k_t, v_t [B, H, d]; state float32
-    [B, H, M, 2d, 2] and tail [B, H, 2, W-1, d] are updated in place.
-    Returns o_t [B, H, d]."""
+    """One token per sequence, q_t, k_t, v_t [B, H, d], or 1..8 tokens,
+    [B, N, H, d]; state float32 [B, H, M, 2d, 2] and tail [B, H, 2, W-1, d]
+    are updated in place.  Returns o_t shaped like q_t."""
     import torch
-    B, H, d = q_t.shape
+    if q_t.dim() == 3:
+        B, H, d = q_t.shape
+        N = 1
+    else:
+        B, N, H, d = q_t.shape
     M = params["A"].shape[1]
     W = params["conv_q"].shape[-1]
-    dims = make_dims(B, 1, H, d, M, W, _io_name(q_t), "auto", eps_feat, eps_norm, feature_norm)
+    dims = make_dims(B, N, H, d, M, W, _io_name(q_t), "auto", eps_feat, eps_norm, feature_norm)
     o_t = torch.empty_like(q_t)
     idattn_decode_step(dims, make_params(params), q_t, k_t, v_t, o_t, state, tail, stream)
     return o_t

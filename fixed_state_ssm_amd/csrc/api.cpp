@@ -53,7 +53,7 @@ idattn_status check_dims(const idattn_dims* dims, bool decode) {
         return fail(IDATTN_ERR_SHAPE, "sizes must be positive (N >= 0): B=%lld N=%lld H=%lld d=%lld M=%lld W=%lld",
                     (long long)D.B, (long long)D.N, (long long)D.H, (long long)D.d, (long long)D.M,
                     (long long)D.W);
-    if (decode && D.N != 1) return fail(IDATTN_ERR_SHAPE, "decode step needs N == 1, got %lld", (long long)D.N);
+    if (decode && D.N < 1) return fail(IDATTN_ERR_SHAPE, "decode step needs N >= 1, got %lld", (long long)D.N);
     if (D.io_dtype != IDATTN_IO_F32 && D.io_dtype != IDATTN_IO_BF16)
         return fail(IDATTN_ERR_ARG, "io_dtype %d is not IDATTN_IO_F32 or IDATTN_IO_BF16", D.io_dtype);
     if (D.algo != IDATTN_ALGO_AUTO && D.algo != IDATTN_ALGO_SEQUENTIAL && D.algo != IDATTN_ALGO_CHUNKED)
@@ -276,8 +276,11 @@ idattn_status idattn_decode_step(const idattn_dims* dims, const idattn_params* p
         for (const void* ptr : ptrs)
             if (misaligned(ptr)) return fail(IDATTN_ERR_ARG, "device buffers must be 16-byte aligned");
     }
+    if (D.N > idattn::kDecodeMaxTokens)
+        return fail(IDATTN_ERR_UNSUPPORTED, "decode step takes 1..%d tokens per sequence, got %lld",
+                    idattn::kDecodeMaxTokens, (long long)D.N);
     const size_t io = D.io_dtype == IDATTN_IO_BF16 ? 2 : 4;
-    const size_t tokb = static_cast<size_t>(D.B) * D.H * D.d * io;
+    const size_t tokb = static_cast<size_t>(D.B) * D.N * D.H * D.d * io;
     const size_t stb = static_cast<size_t>(D.B) * D.H * D.M * 2 * D.d * 2 * sizeof(float);
     const size_t tlb = static_cast<size_t>(D.B) * D.H * 2 * (D.W - 1) * D.d * io;
     const Range rq = range("q_t", q_t, tokb), rk = range("k_t", k_t, tokb), rv = range("v_t", v_t, tokb);

@@ -1,12 +1,14 @@
-// decode_step: one token per sequence against a carried state held in HBM.
+// decode_step: one to eight tokens per sequence against a carried state held
+// in HBM.
 //
-// One block of 4 waves per (b, h).  Wave 0 first builds the token's features
-// (conv over the tail and the new token, SiLU feature map, per-half RMSNorm)
+// One block of 4 waves per (b, h).  Wave 0 first builds the tokens' features
+// (conv over the tail and the new tokens, SiLU feature map, per-half RMSNorm)
 // into LDS and shifts the conv tail; wave 1 evaluates the ZOH coefficients of
 // all M modes (one mode per lane).  Then every wave streams its quarter of
 // the M rows of the complex state [M][2d]: a row is read once as float4s,
-// updated, reduced to s_m over the key half with a lane reduction, read out
-// into per-lane partial sums of Re(s_m Gamma_m), and written back in place.
+// and for each token in turn updated, reduced to s_m over the key half with
+// a lane reduction and read out into per-lane partial sums of
+// Re(s_m Gamma_m); then it is written back in place.
 // The state sweep (2 x 128 KiB per (b, h) at d = 128, M = 64) is the whole
 // cost: each wave streams its rows one at a time with few live registers, so
 // that many workgroups share a CU and hide each other's memory latency, and
@@ -64,93 +66,190 @@ __device__ __forceinline__ float wave_total(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// FJ = float4 chunks of a state row per lane (d / 64, at least 1); RPW = rows per
-// wave (M / 4).
-template <bool BF16, int FJ, int RPW>
+// NT = most tokens of the instance (1, or kDecodeMaxTokens with the call's
+// n = p.N <= NT); FJ = float4 chunks of a state row per lane (d / 64, at least
+// 1); RPW = rows per wave (M / 4).  Tokens are [B][n][H][d].
+template <bool BF16, int NT, int FJ, int RPW>
 __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_params prm,
                                                           const void* __restrict__ q_t,
                                                           const void* __restrict__ k_t,
                                                           const void* __restrict__ v_t,
                                                           void* __restrict__ o_t, float* state,
                                                           void* tail) {
-    __shared__ float xq_s[128], zk_s[128], zv_s[128];
+    __shared__ float xq_s[NT][128], zk_s[NT][128], zv_s[NT][128];
     __shared__ float4 coef_s[64];
-    __shared__ float part_s[4][128];
+    __shared__ float part_s[4][NT][128];
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x >> 6;
     const int64_t bh = blockIdx.x;
-    const int64_t h = bh % p.H;
+    const int64_t h = bh % p.H, b = bh / p.H;
     const int d = static_cast<int>(p.d), W = static_cast<int>(p.W);
+    const int n = NT == 1 ? 1 : static_cast<int>(p.N);
     const int64_t M = p.M;
     const int nf = d;  // float4 chunks per row (4d floats)
     float4* st4 = reinterpret_cast<float4*>(state) + bh * M * nf;
 
     if (w == 0) {
-        // features of the new token; lane owns channels lane and lane + 64
-        float yq[2], yk[2], vv[2];
-        float sq = 0.f, sk = 0.f, sv = 0.f;
-        const int64_t tok = bh * d;  // [B][H][d]
-        const int64_t E = 2 * static_cast<int64_t>(W - 1) * d;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int c = lane + kWave * j;
-            float cq = 0.f, ck = 0.f;
-            yq[j] = yk[j] = vv[j] = 0.f;
-            if (c < d) {
-                const float* wq = prm.conv_q + (h * d + c) * W;
-                const float* wk = prm.conv_k + (h * d + c) * W;
-                float hq[8], hk[8];
-                for (int t = 0; t < W - 1; ++t) {
-                    hq[t] = load_io<BF16>(tail, bh * E + static_cast<int64_t>(t) * d + c);
-                    hk[t] = load_io<BF16>(tail, bh * E + static_cast<int64_t>(W - 1 + t) * d + c);
+        if constexpr (NT == 1) {
+            // features of the new token; lane owns channels lane and lane + 64
+            float yq[2], yk[2], vv[2];
+            float sq = 0.f, sk = 0.f, sv = 0.f;
+            const int64_t tok = bh * d;  // [B][H][d]
+            const int64_t E = 2 * static_cast<int64_t>(W - 1) * d;
+    #pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int c = lane + kWave * j;
+                float cq = 0.f, ck = 0.f;
+                yq[j] = yk[j] = vv[j] = 0.f;
+                if (c < d) {
+                    const float* wq = prm.conv_q + (h * d + c) * W;
+                    const float* wk = prm.conv_k + (h * d + c) * W;
+                    float hq[8], hk[8];
+                    for (int t = 0; t < W - 1; ++t) {
+                        hq[t] = load_io<BF16>(tail, bh * E + static_cast<int64_t>(t) * d + c);
+                        hk[t] = load_io<BF16>(tail, bh * E + static_cast<int64_t>(W - 1 + t) * d + c);
+                    }
+                    const float xq = load_io<BF16>(q_t, tok + c);
+                    const float xk = load_io<BF16>(k_t, tok + c);
+                    for (int t = 0; t < W - 1; ++t) {
+                        cq = fmaf(wq[t], hq[t], cq);
+                        ck = fmaf(wk[t], hk[t], ck);
+                    }
+                    cq = fmaf(wq[W - 1], xq, cq);
+                    ck = fmaf(wk[W - 1], xk, ck);
+                    // shift the tail by one token (this lane owns channel c)
+                    for (int t = 0; t + 1 < W - 1; ++t) {
+                        store_io<BF16>(tail, bh * E + static_cast<int64_t>(t) * d + c, hq[t + 1]);
+                        store_io<BF16>(tail, bh * E + static_cast<int64_t>(W - 1 + t) * d + c, hk[t + 1]);
+                    }
+                    if (W > 1) {
+                        store_io<BF16>(tail, bh * E + static_cast<int64_t>(W - 2) * d + c, xq);
+                        store_io<BF16>(tail, bh * E + static_cast<int64_t>(2 * W - 3) * d + c, xk);
+                    }
+                    vv[j] = load_io<BF16>(v_t, tok + c);
+                    yq[j] = cq / (1.f + expf(-cq));
+                    yk[j] = ck / (1.f + expf(-ck));
                 }
-                const float xq = load_io<BF16>(q_t, tok + c);
-                const float xk = load_io<BF16>(k_t, tok + c);
-                for (int t = 0; t < W - 1; ++t) {
-                    cq = fmaf(wq[t], hq[t], cq);
-                    ck = fmaf(wk[t], hk[t], ck);
-                }
-                cq = fmaf(wq[W - 1], xq, cq);
-                ck = fmaf(wk[W - 1], xk, ck);
-                // shift the tail by one token (this lane owns channel c)
-                for (int t = 0; t + 1 < W - 1; ++t) {
-                    store_io<BF16>(tail, bh * E + static_cast<int64_t>(t) * d + c, hq[t + 1]);
-                    store_io<BF16>(tail, bh * E + static_cast<int64_t>(W - 1 + t) * d + c, hk[t + 1]);
-                }
-                if (W > 1) {
-                    store_io<BF16>(tail, bh * E + static_cast<int64_t>(W - 2) * d + c, xq);
-                    store_io<BF16>(tail, bh * E + static_cast<int64_t>(2 * W - 3) * d + c, xk);
-                }
-                vv[j] = load_io<BF16>(v_t, tok + c);
-                yq[j] = cq / (1.f + expf(-cq));
-                yk[j] = ck / (1.f + expf(-ck));
+                sq = fmaf(yq[j], yq[j], sq);
+                sk = fmaf(yk[j], yk[j], sk);
+                sv = fmaf(vv[j], vv[j], sv);
             }
-            sq = fmaf(yq[j], yq[j], sq);
-            sk = fmaf(yk[j], yk[j], sk);
-            sv = fmaf(vv[j], vv[j], sv);
-        }
-        sq = wave_sum(sq);
-        sk = wave_sum(sk);
-        sv = wave_sum(sv);
-        // xi = y * inv: squared norm, or its square root for the unit-norm map
-        const float inv_q = p.unit_feat ? 1.f / sqrtf(sq + p.eps_feat) : 1.f / (sq + p.eps_feat);
-        const float inv_k = p.unit_feat ? 1.f / sqrtf(sk + p.eps_feat) : 1.f / (sk + p.eps_feat);
-        float xk2 = 0.f, xik[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            xik[j] = yk[j] * inv_k;
-            xk2 = fmaf(xik[j], xik[j], xk2);
-        }
-        xk2 = wave_sum(xk2);
-        const float rk = 1.f / sqrtf(xk2 / d + p.eps_norm);
-        const float rv = 1.f / sqrtf(sv / d + p.eps_norm);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int c = lane + kWave * j;
-            if (c < d) {
-                xq_s[c] = yq[j] * inv_q;
-                zk_s[c] = fmaf(prm.gain[h * 2 * d + c] * xik[j], rk, prm.bias[h * 2 * d + c]);
-                zv_s[c] = fmaf(prm.gain[h * 2 * d + d + c] * vv[j], rv, prm.bias[h * 2 * d + d + c]);
+            sq = wave_sum(sq);
+            sk = wave_sum(sk);
+            sv = wave_sum(sv);
+            // xi = y * inv: squared norm, or its square root for the unit-norm map
+            const float inv_q = p.unit_feat ? 1.f / sqrtf(sq + p.eps_feat) : 1.f / (sq + p.eps_feat);
+            const float inv_k = p.unit_feat ? 1.f / sqrtf(sk + p.eps_feat) : 1.f / (sk + p.eps_feat);
+            float xk2 = 0.f, xik[2];
+    #pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                xik[j] = yk[j] * inv_k;
+                xk2 = fmaf(xik[j], xik[j], xk2);
+            }
+            xk2 = wave_sum(xk2);
+            const float rk = 1.f / sqrtf(xk2 / d + p.eps_norm);
+            const float rv = 1.f / sqrtf(sv / d + p.eps_norm);
+    #pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int c = lane + kWave * j;
+                if (c < d) {
+                    xq_s[0][c] = yq[j] * inv_q;
+                    zk_s[0][c] = fmaf(prm.gain[h * 2 * d + c] * xik[j], rk, prm.bias[h * 2 * d + c]);
+                    zv_s[0][c] = fmaf(prm.gain[h * 2 * d + d + c] * vv[j], rv, prm.bias[h * 2 * d + d + c]);
+                }
+            }
+        } else {
+            // features of the new tokens, one after another; lane owns channels lane and
+            // lane + 64 and slides its own conv window (the last W-1 raw tokens, oldest
+            // first) over the tail and the new tokens
+            const int64_t E = 2 * static_cast<int64_t>(W - 1) * d;
+            float hq[2][7], hk[2][7], wqh[2][7], wkh[2][7], wqc[2], wkc[2];
+    #pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int c = lane + kWave * j;
+                const bool ok = c < d;
+                wqc[j] = ok ? prm.conv_q[(h * d + c) * W + W - 1] : 0.f;
+                wkc[j] = ok ? prm.conv_k[(h * d + c) * W + W - 1] : 0.f;
+    #pragma unroll
+                for (int u = 0; u < 7; ++u) {
+                    const bool in = ok && u < W - 1;
+                    wqh[j][u] = in ? prm.conv_q[(h * d + c) * W + u] : 0.f;
+                    wkh[j][u] = in ? prm.conv_k[(h * d + c) * W + u] : 0.f;
+                    hq[j][u] = in ? load_io<BF16>(tail, bh * E + static_cast<int64_t>(u) * d + c) : 0.f;
+                    hk[j][u] = in ? load_io<BF16>(tail, bh * E + static_cast<int64_t>(W - 1 + u) * d + c) : 0.f;
+                }
+            }
+    #pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (t < n) {
+                    const int64_t tok = ((b * n + t) * p.H + h) * d;  // [B][n][H][d]
+                    float yq[2], yk[2], vv[2];
+                    float sq = 0.f, sk = 0.f, sv = 0.f;
+    #pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int c = lane + kWave * j;
+                        yq[j] = yk[j] = vv[j] = 0.f;
+                        if (c < d) {
+                            const float xq = load_io<BF16>(q_t, tok + c);
+                            const float xk = load_io<BF16>(k_t, tok + c);
+                            float cq = wqc[j] * xq, ck = wkc[j] * xk;
+    #pragma unroll
+                            for (int u = 0; u < 7; ++u) {
+                                cq = fmaf(wqh[j][u], hq[j][u], cq);
+                                ck = fmaf(wkh[j][u], hk[j][u], ck);
+                            }
+                            // slide the window by one token
+    #pragma unroll
+                            for (int u = 0; u < 7; ++u) {
+                                hq[j][u] = u + 1 < W - 1 ? hq[j][u < 6 ? u + 1 : 6] : (u == W - 2 ? xq : hq[j][u]);
+                                hk[j][u] = u + 1 < W - 1 ? hk[j][u < 6 ? u + 1 : 6] : (u == W - 2 ? xk : hk[j][u]);
+                            }
+                            vv[j] = load_io<BF16>(v_t, tok + c);
+                            yq[j] = cq / (1.f + expf(-cq));
+                            yk[j] = ck / (1.f + expf(-ck));
+                        }
+                        sq = fmaf(yq[j], yq[j], sq);
+                        sk = fmaf(yk[j], yk[j], sk);
+                        sv = fmaf(vv[j], vv[j], sv);
+                    }
+                    sq = wave_sum(sq);
+                    sk = wave_sum(sk);
+                    sv = wave_sum(sv);
+                    // xi = y * inv: squared norm, or its square root for the unit-norm map
+                    const float inv_q = p.unit_feat ? 1.f / sqrtf(sq + p.eps_feat) : 1.f / (sq + p.eps_feat);
+                    const float inv_k = p.unit_feat ? 1.f / sqrtf(sk + p.eps_feat) : 1.f / (sk + p.eps_feat);
+                    float xk2 = 0.f, xik[2];
+    #pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        xik[j] = yk[j] * inv_k;
+                        xk2 = fmaf(xik[j], xik[j], xk2);
+                    }
+                    xk2 = wave_sum(xk2);
+                    const float rk = 1.f / sqrtf(xk2 / d + p.eps_norm);
+                    const float rv = 1.f / sqrtf(sv / d + p.eps_norm);
+    #pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int c = lane + kWave * j;
+                        if (c < d) {
+                            xq_s[t][c] = yq[j] * inv_q;
+                            zk_s[t][c] = fmaf(prm.gain[h * 2 * d + c] * xik[j], rk, prm.bias[h * 2 * d + c]);
+                            zv_s[t][c] = fmaf(prm.gain[h * 2 * d + d + c] * vv[j], rv, prm.bias[h * 2 * d + d + c]);
+                        }
+                    }
+                }
+            }
+            // the new tail: the window after the last token (this lane owns channel c)
+    #pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int c = lane + kWave * j;
+                if (c < d) {
+    #pragma unroll
+                    for (int u = 0; u < 7; ++u)
+                        if (u < W - 1) {
+                            store_io<BF16>(tail, bh * E + static_cast<int64_t>(u) * d + c, hq[j][u]);
+                            store_io<BF16>(tail, bh * E + static_cast<int64_t>(W - 1 + u) * d + c, hk[j][u]);
+                        }
+                }
             }
         }
     } else if (w == 1 && lane < M) {
@@ -162,10 +261,14 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
     __syncthreads();
 
     // ---- state sweep: one row at a time per wave, so that few registers are live
-    // and many workgroups share a CU; they hide each other's memory latency
-    float acc[FJ][2];
+    // and many workgroups share a CU; they hide each other's memory latency.  A row
+    // is read once, takes every token's update and readout in turn, and is written
+    // once.
+    float acc[NT][FJ][2];
 #pragma unroll
-    for (int j = 0; j < FJ; ++j) acc[j][0] = acc[j][1] = 0.f;
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) acc[t][j][0] = acc[t][j][1] = 0.f;
 #pragma unroll 1
     for (int rr = 0; rr < RPW; ++rr) {
         const int m = w * RPW + rr;
@@ -176,53 +279,65 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
             row[j] = f < nf ? st4[m * nf + f] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         const float4 cf = coef_s[m];
-        float pr = 0.f, pi = 0.f;
-        // complex columns 2f and 2f+1; columns < d belong to U, the rest to Gamma
 #pragma unroll
-        for (int j = 0; j < FJ; ++j) {
-            const int f = lane + kWave * j;
-            if (f < nf) {
-                const int col = 2 * f;
-                const bool key = col < d;
-                const float in0 = key ? zk_s[col] : zv_s[col - d];
-                const float in1 = key ? zk_s[col + 1] : zv_s[col + 1 - d];
-                const float4 x = row[j];
-                const float r0 = fmaf(cf.x, x.x, fmaf(-cf.y, x.y, cf.z * in0));
-                const float i0 = fmaf(cf.x, x.y, fmaf(cf.y, x.x, cf.w * in0));
-                const float r1 = fmaf(cf.x, x.z, fmaf(-cf.y, x.w, cf.z * in1));
-                const float i1 = fmaf(cf.x, x.w, fmaf(cf.y, x.z, cf.w * in1));
-                row[j] = make_float4(r0, i0, r1, i1);
-                if (key) {
-                    pr = fmaf(xq_s[col], r0, fmaf(xq_s[col + 1], r1, pr));
-                    pi = fmaf(xq_s[col], i0, fmaf(xq_s[col + 1], i1, pi));
+        for (int t = 0; t < NT; ++t) {
+            if (t < n) {
+                float pr = 0.f, pi = 0.f;
+                // complex columns 2f and 2f+1; columns < d belong to U, the rest to Gamma
+#pragma unroll
+                for (int j = 0; j < FJ; ++j) {
+                    const int f = lane + kWave * j;
+                    if (f < nf) {
+                        const int col = 2 * f;
+                        const bool key = col < d;
+                        const float in0 = key ? zk_s[t][col] : zv_s[t][col - d];
+                        const float in1 = key ? zk_s[t][col + 1] : zv_s[t][col + 1 - d];
+                        const float4 x = row[j];
+                        const float r0 = fmaf(cf.x, x.x, fmaf(-cf.y, x.y, cf.z * in0));
+                        const float i0 = fmaf(cf.x, x.y, fmaf(cf.y, x.x, cf.w * in0));
+                        const float r1 = fmaf(cf.x, x.z, fmaf(-cf.y, x.w, cf.z * in1));
+                        const float i1 = fmaf(cf.x, x.w, fmaf(cf.y, x.z, cf.w * in1));
+                        row[j] = make_float4(r0, i0, r1, i1);
+                        if (key) {
+                            pr = fmaf(xq_s[t][col], r0, fmaf(xq_s[t][col + 1], r1, pr));
+                            pi = fmaf(xq_s[t][col], i0, fmaf(xq_s[t][col + 1], i1, pi));
+                        }
+                    }
+                }
+                pr = wave_total(pr);
+                pi = wave_total(pi);
+#pragma unroll
+                for (int j = 0; j < FJ; ++j) {
+                    const int f = lane + kWave * j;
+                    if (f < nf && 2 * f >= d) {
+                        const float4 x = row[j];
+                        acc[t][j][0] = fmaf(pr, x.x, fmaf(-pi, x.y, acc[t][j][0]));
+                        acc[t][j][1] = fmaf(pr, x.z, fmaf(-pi, x.w, acc[t][j][1]));
+                    }
                 }
             }
         }
-        pr = wave_total(pr);
-        pi = wave_total(pi);
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
             const int f = lane + kWave * j;
-            if (f < nf && 2 * f >= d) {
-                const float4 x = row[j];
-                acc[j][0] = fmaf(pr, x.x, fmaf(-pi, x.y, acc[j][0]));
-                acc[j][1] = fmaf(pr, x.z, fmaf(-pi, x.w, acc[j][1]));
-            }
             if (f < nf) st4[m * nf + f] = row[j];
         }
     }
 #pragma unroll
-    for (int j = 0; j < FJ; ++j) {
-        const int f = lane + kWave * j;
-        if (f < nf && 2 * f >= d) {
-            part_s[w][2 * f - d] = acc[j][0];
-            part_s[w][2 * f + 1 - d] = acc[j][1];
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+            const int f = lane + kWave * j;
+            if (t < n && f < nf && 2 * f >= d) {
+                part_s[w][t][2 * f - d] = acc[t][j][0];
+                part_s[w][t][2 * f + 1 - d] = acc[t][j][1];
+            }
         }
-    }
     __syncthreads();
-    for (int c = threadIdx.x; c < d; c += 256) {
-        const float sum = (part_s[0][c] + part_s[1][c]) + (part_s[2][c] + part_s[3][c]);
-        store_io<BF16>(o_t, bh * d + c, sum);
+    for (int e = threadIdx.x; e < n * d; e += 256) {
+        const int t = e / d, c = e % d;
+        const float sum = (part_s[0][t][c] + part_s[1][t][c]) + (part_s[2][t][c] + part_s[3][t][c]);
+        store_io<BF16>(o_t, ((b * n + t) * p.H + h) * d + c, sum);
     }
 }
 
@@ -232,12 +347,17 @@ hipError_t launch_decode_step(const Problem& p, const idattn_params& prm, const 
                               const void* k_t, const void* v_t, void* o_t, float* state,
                               void* tail, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(p.B * p.H));
-#define IDATTN_DEC(FJ, RPW)                                                                      \
-    do {                                                                                         \
-        if (p.bf16)                                                                              \
-            decode_step_kernel<true, FJ, RPW><<<grid, 256, 0, stream>>>(p, prm, q_t, k_t, v_t, o_t, state, tail); \
-        else                                                                                     \
-            decode_step_kernel<false, FJ, RPW><<<grid, 256, 0, stream>>>(p, prm, q_t, k_t, v_t, o_t, state, tail); \
+#define IDATTN_DEC_NT(NT, FJ, RPW)                                                                            \
+    do {                                                                                                      \
+        if (p.bf16)                                                                                           \
+            decode_step_kernel<true, NT, FJ, RPW><<<grid, 256, 0, stream>>>(p, prm, q_t, k_t, v_t, o_t, state, tail); \
+        else                                                                                                  \
+            decode_step_kernel<false, NT, FJ, RPW><<<grid, 256, 0, stream>>>(p, prm, q_t, k_t, v_t, o_t, state, tail); \
+    } while (0)
+#define IDATTN_DEC(FJ, RPW)                                 \
+    do {                                                    \
+        if (p.N == 1) IDATTN_DEC_NT(1, FJ, RPW);            \
+        else IDATTN_DEC_NT(kDecodeMaxTokens, FJ, RPW);      \
     } while (0)
     const int fj = p.d > 64 ? 2 : 1;
     const int rpw = static_cast<int>(p.M / 4);
@@ -249,6 +369,7 @@ hipError_t launch_decode_step(const Problem& p, const idattn_params& prm, const 
     else if (fj == 1 && rpw == 4) IDATTN_DEC(1, 4);
     else return hipErrorInvalidValue;
 #undef IDATTN_DEC
+#undef IDATTN_DEC_NT
     return hipGetLastError();
 }
 

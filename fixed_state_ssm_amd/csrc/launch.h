@@ -55,7 +55,8 @@ hipError_t launch_tail_update(const Problem& p, const void* q, const void* k,
 // dst = src (or zeros when src is NULL); n_elems 32-bit words.
 hipError_t launch_copy_or_zero(const void* src, void* dst, int64_t n_words, hipStream_t stream);
 
-// ---- decode
+// ---- decode (1 .. kDecodeMaxTokens tokens per sequence, [B][N][H][d])
+constexpr int kDecodeMaxTokens = 8;
 hipError_t launch_decode_step(const Problem& p, const idattn_params& prm,
                               const void* q_t, const void* k_t, const void* v_t, void* o_t,
                               float* state, void* tail, hipStream_t stream);

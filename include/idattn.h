@@ -86,7 +86,7 @@ typedef enum idattn_feature_norm {
 /* Sizes.  R == d.  Layout of q, k, v, o: contiguous [B][N][H][d]. */
 typedef struct idattn_dims {
     int64_t B;        /* batch rows, >= 1                                     */
-    int64_t N;        /* tokens in this call, >= 0 (forward) or == 1 (decode) */
+    int64_t N;        /* tokens in this call, >= 0 (forward) or 1..8 (decode) */
     int64_t H;        /* heads, >= 1                                          */
     int64_t d;        /* channels per head (= R); supported 16, 32, 64, 128   */
     int64_t M;        /* complex modes per head; supported 16, 32, 64         */
@@ -145,14 +145,18 @@ idattn_status idattn_forward(const idattn_dims *dims, const idattn_params *param
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * One autoregressive step for every batch row (O(1) work and a fixed-size
+ * Autoregressive steps for every batch row (O(1) work and a fixed-size
  * state per token: Chinese rendering, section 1; German summary,
- * "Problemstellung").  dims->N must be 1.
+ * "Problemstellung"): N = dims->N new tokens per sequence, 1 <= N <= 8
+ * (IDATTN_ERR_UNSUPPORTED above), the same result as idattn_forward over
+ * those N tokens from the carried state and tail.  The state is streamed
+ * through once per call whatever N is, so several tokens per call cost
+ * little more than one.
  *
- *  q_t, k_t, v_t in  [B][H][d] io dtype
- *  o_t          out  [B][H][d] io dtype
+ *  q_t, k_t, v_t in  [B][N][H][d] io dtype ([B][H][d] for N = 1)
+ *  o_t          out  [B][N][H][d] io dtype
  *  state     in/out  state layout, updated in place
- *  tail      in/out  tail layout, shifted in place by one token
+ *  tail      in/out  tail layout, shifted in place by N tokens
  * No workspace.  o_t must not overlap any other buffer.
  */
 idattn_status idattn_decode_step(const idattn_dims *dims, const idattn_params *params,

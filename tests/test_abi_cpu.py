@@ -175,7 +175,9 @@ def test_decode_validation():
         a.update(over)
         return lib.idattn_decode_step(ctypes.byref(d), ctypes.byref(p), a["q"], a["k"], a["v"], a["o"], a["s"], a["t"], None)
 
-    expect(dec(dims(N=2)), "IDATTN_ERR_SHAPE")
+    expect(dec(dims(N=0)), "IDATTN_ERR_SHAPE")
+    expect(dec(dims(N=9)), "IDATTN_ERR_UNSUPPORTED")          # 1..8 tokens per call
+    expect(dec(dims(N=4), o=QB + 4 * 2 * 3 * 64 * 2 - 16), "IDATTN_ERR_ALIAS")  # o_t over the end of q_t
     expect(dec(dims(N=1), s=0), "IDATTN_ERR_NULL")
     expect(dec(dims(N=1), t=0), "IDATTN_ERR_NULL")
     expect(dec(dims(N=1), o=QB + 16), "IDATTN_ERR_ALIAS")

@@ -220,6 +220,32 @@ def test_chunked_query_scale_range(fs, e, feature_norm):
         assert e_o <= GATE_BF16 and e_s <= GATE_BF16, (algo, e_o, e_s)
 
 
+# Several tokens per decode call (one sweep of the state for all of them)
+# against the oracle's forward over the same tokens from the same state and
+# tail: outputs of every token, the new state and the shifted tail.
+@pytest.mark.parametrize("n_tok", [2, 3, 8])
+@pytest.mark.parametrize("case", ["d128_m64_w4", "d64_m32_w8", "d128_m16_w1_unit"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_decode_multi_token(fs, n_tok, case, io):
+    base, over = {"d128_m64_w4": ("1p3b", dict(B=3, H=2)), "d64_m32_w8": ("125m", dict(B=2, H=3, M=32, W=8)),
+                  "d128_m16_w1_unit": ("1p3b", dict(B=2, H=2, M=16, W=1))}[case]
+    fn = "unit" if case.endswith("unit") else "squared"
+    c = WL.make_case(base, seed=5, tag=75, N=n_tok, io=io, **over)
+    s = c.spec
+    st0, tl0 = WL.make_decode_state(s, seed=6)
+    o_ref, st_ref, tl_ref = oracle.forward(c.q, c.k, c.v, c.params, state_in=st0, tail_in=tl0, feature_norm=fn)
+    p = fs.params_to_device(c.params)
+    st = state_dev(st0)
+    tl = up(tl0, io)
+    o = fs.decode_step(up(c.q, io), up(c.k, io), up(c.v, io), p, st, tl, feature_norm=fn)
+    _sync()
+    e_o = rel_l2(down(o), o_ref)
+    e_s = rel_l2(state_np(st), st_ref)
+    print(f"decode x{n_tok} {case} {io}: o relL2 {e_o:.2e}, state relL2 {e_s:.2e}")
+    assert e_o <= gate(io) and e_s <= gate(io), (e_o, e_s)
+    assert np.array_equal(down(tl), tl_ref.astype(np.float32))
+
+
 def _pairs(s, n, seed):
     r = np.random.default_rng(seed)
     idx = r.choice(s["B"] * s["H"], size=min(n, s["B"] * s["H"]), replace=False)
