@@ -340,8 +340,14 @@ struct SmemFwd {
     _Float16 ft[M2 * L];          // F^T, high and low fp16 parts
     _Float16 ftl[M2 * L];
     // window C
-    _Float16 gp[L * RP];          // G' (zero above the causal band, never rewritten there)
-    _Float16 pp[L * RP];          // P~ [t][l] (likewise)
+    // G' and P~ rows of RP = L + 16 halves, read in columns 0..L-1 only.  The
+    // tiles are written whole: the non-causal G'[t][L-1+(j-t)], j > t, land in
+    // row t's padding columns L..L+14, and P~[t][t-k], k > t, in row t-1's
+    // padding columns RP-15..RP-1 (for t = 0, those of G''s last row, which
+    // precedes pp).  The columns below the causal band are zeroed once and
+    // never written.
+    _Float16 gp[L * RP];          // G'
+    _Float16 pp[L * RP];          // P~ [t][l] (must follow gp)
     float om[3][L];               // omega_t, output factor of each token, by chunk mod 3
     float2 aL[MM];                // abar^L
     float2 aH[MM];                // abar^(L/2)
@@ -351,6 +357,9 @@ struct SmemFwd {
     uint16_t halo[2][3][D];              // raw q, k at positions -3..-1 of the sequence
     float fac[16][2][8];                 // per-token feature factors, by wave and token block
 };
+static_assert(offsetof(SmemFwd<128>, pp) == offsetof(SmemFwd<128>, gp) + sizeof(_Float16) * L * RP &&
+                  offsetof(SmemFwd<64>, pp) == offsetof(SmemFwd<64>, gp) + sizeof(_Float16) * L * RP && RP >= L + 15,
+              "the P~ tile must follow G' and rows need 15 halves of padding");
 
 template <int D>
 struct SmemSeg {
@@ -1086,7 +1095,7 @@ __device__ __forceinline__ void p_tile(const SM& sm, int qt, int ln, uint32_t xo
     const uint32_t ps = opaque(lds_addr(sm.pp) + 2 * ((16 * tt + 4 * g) * (RP + 1) - 16 * kt - 15 + i));
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
-        if (16 * kt + 15 - i <= 16 * tt + 4 * g + jj) wr1(ps + 2 * (RP + 1) * jj, accP[jj]);
+        wr1(ps + 2 * (RP + 1) * jj, accP[jj]);  // k > t lands in padding (see SmemFwd)
 }
 
 // Full chunk loop of one segment: grid B*H*S, block (bh, seg).  z_k^T and
@@ -1227,7 +1236,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                         const uint32_t gs = opaque(lds_addr(sm.gp) + 2 * ((16 * tt + 4 * g) * (RP - 1) + L - 1 + 16 * jt + i));
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj)
-                            if (16 * jt + i <= 16 * tt + 4 * g + jj) wr1(gs + 2 * (RP - 1) * jj, accG[jj]);
+                            wr1(gs + 2 * (RP - 1) * jj, accG[jj]);  // j > t lands in padding
                     }
                 }
 #pragma unroll
