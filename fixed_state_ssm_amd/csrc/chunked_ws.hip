@@ -1078,24 +1078,37 @@ __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, const flo
 // One causal tile (tt, kt) of P~'[t][k] = sum_m' s~[t][m'] T[k][m'] (lane (g, i) of the
 // T operand holds k = 16 kt + 15 - i), un-skewed into P~[t][t - k].  K = m' in perm32
 // order on both sides: s~ as stored, F^T rows 32kb + 4g + e and 32kb + 16 + 4g + e.
+// The lane's shared-memory addresses of tile qt: T fragments (br0, br1), the
+// un-skewed P~ row start (ps) and the tile row tt; the same for every chunk.
+struct PTile {
+    uint32_t br0, br1, ps;
+    int tt;
+};
 template <class SM>
-__device__ __forceinline__ void p_tile(const SM& sm, int qt, int ln, uint32_t xoff) {
-    constexpr uint32_t dl = M2 * L * 2;
+__device__ __forceinline__ PTile p_tile_prep(const SM& sm, int qt, int ln) {
     const int g = ln >> 4, i = ln & 15;
     const int tt = tile_tt(qt), kt = tile_kt(qt);
-    const uint32_t br0 = opaque(lds_addr(sm.ft) + 2 * o128(4 * g + (i >> 2), L - 16 - 16 * kt + 4 * (i & 3)));
-    const uint32_t br1 = opaque(lds_addr(sm.ft) + 2 * o128(16 + 4 * g + (i >> 2), L - 16 - 16 * kt + 4 * (i & 3)));
+    return PTile{opaque(lds_addr(sm.ft) + 2 * o128(4 * g + (i >> 2), L - 16 - 16 * kt + 4 * (i & 3))),
+                 opaque(lds_addr(sm.ft) + 2 * o128(16 + 4 * g + (i >> 2), L - 16 - 16 * kt + 4 * (i & 3))),
+                 opaque(lds_addr(sm.pp) + 2 * ((16 * tt + 4 * g) * (RP + 1) - 16 * kt - 15 + i)), tt};
+}
+template <class SM>
+__device__ __forceinline__ void p_tile_run(const SM& sm, const PTile& pt, uint32_t xoff) {
+    constexpr uint32_t dl = M2 * L * 2;
     f4 accP = {};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        const half8 a = rd8(lds_addr(sm.sc) + frag_kb(xoff, kb) + 2 * 16 * tt * M2);
-        accP = mfma(a, cat(rd4t(br0 + 4096 * kb), rd4t(br1 + 4096 * kb)), accP);
-        accP = mfma(a, cat(rd4t(br0 + 4096 * kb + dl), rd4t(br1 + 4096 * kb + dl)), accP);
+        const half8 a = rd8(lds_addr(sm.sc) + frag_kb(xoff, kb) + 2 * 16 * pt.tt * M2);
+        accP = mfma(a, cat(rd4t(pt.br0 + 4096 * kb), rd4t(pt.br1 + 4096 * kb)), accP);
+        accP = mfma(a, cat(rd4t(pt.br0 + 4096 * kb + dl), rd4t(pt.br1 + 4096 * kb + dl)), accP);
     }
-    const uint32_t ps = opaque(lds_addr(sm.pp) + 2 * ((16 * tt + 4 * g) * (RP + 1) - 16 * kt - 15 + i));
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
-        wr1(ps + 2 * (RP + 1) * jj, accP[jj]);  // k > t lands in padding (see SmemFwd)
+        wr1(pt.ps + 2 * (RP + 1) * jj, accP[jj]);  // k > t lands in padding (see SmemFwd)
+}
+template <class SM>
+__device__ __forceinline__ void p_tile(const SM& sm, int qt, int ln, uint32_t xoff) {
+    p_tile_run(sm, p_tile_prep(sm, qt, ln), xoff);
 }
 
 // Full chunk loop of one segment: grid B*H*S, block (bh, seg).  z_k^T and
@@ -1335,6 +1348,10 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         tile_load<D>(zr, zseg + D * L);
         tile_store<D>(sm.zkT, kr);
         if (nch > 1) tile_load<D>(kr, zseg + tile2);
+        // lane addresses of this wave's P~ tile and of the s~, X fragment reads, kept
+        // across the chunk loop
+        const PTile ptv = p_tile_prep(sm, vw, tid_now() & 63);
+        const uint32_t xoff = frag256_off(tid_now() & 63);  // s~ and X rows i, K block 0
         lds_barrier();  // chunk 0 features
         half8 bZ[2];    // Z_v fragments of the chunk whose readout comes next
         for (int c = 0; c <= nch; ++c) {
@@ -1343,8 +1360,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             // ---- phase 1: z_v^T (c); P~ tiles, X Gamma, Gamma update (c-1)
             if (c < nch) tile_store<D>(sm.zvT, zr);
             const int ln = tid_now() & 63;
-            const uint32_t xoff = frag256_off(ln);  // s~ and X rows i, K block 0
-            if (c >= 1) p_tile(sm, vw, ln, xoff);  // P~ tiles 0..7 of chunk c-1 (8, 9: key waves 2, 3)
+            if (c >= 1) p_tile_run(sm, ptv, xoff);  // P~ tiles 0..7 of chunk c-1 (8, 9: key waves 2, 3)
             if (c >= 1 && own) {
                 // o^T = Gamma_prev^T X^T (c-block vw: lane (g, i) of tile tt holds
                 // o[16tt + i][16vw + 4g + jj], four consecutive channels of one token)
