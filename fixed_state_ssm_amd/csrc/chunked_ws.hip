@@ -886,11 +886,11 @@ __device__ __forceinline__ void value_update_plain(f4 (&G)[8], const float2* aL,
 // so with F1 = F[L/2 .. L-1]:  Gamma <- abar^(L/2) (abar^(L/2) Gamma + F1^T Z_v0) + F1^T Z_v1,
 // and each fragment of F1 (high and low parts) is read once for both halves:
 // half the shared-memory reads of the plain update for one more complex scaling.
+// `off` is the lane's fragment offset frag_off(ln), g = ln >> 4.
 template <int D, int GRP = 2>
 __device__ __forceinline__ void value_update(f4 (&G)[8], const float2* aH, const half8 (&bZ)[2], const void* ft,
-                                             int ln) {
-    const int g = ln >> 4;
-    const uint32_t wb = lds_addr(ft) + frag_kb(frag_off(ln), 1);
+                                             int g, uint32_t off) {
+    const uint32_t wb = lds_addr(ft) + frag_kb(off, 1);
 #pragma unroll
     for (int m0 = 0; m0 < 8; m0 += GRP) {
         half8 fh[GRP], fl[GRP];
@@ -912,8 +912,7 @@ __device__ __forceinline__ void value_update(f4 (&G)[8], const float2* aH, const
     }
 }
 
-__device__ __forceinline__ void load_bz(half8 (&bZ)[2], int vw, const void* zvT, int ln) {
-    const uint32_t off = frag_off(ln);
+__device__ __forceinline__ void load_bz(half8 (&bZ)[2], int vw, const void* zvT, uint32_t off) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) bZ[kb] = rd8(lds_addr(zvT) + frag_kb(off, kb) + 2048 * vw);
 }
@@ -1004,7 +1003,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
             if (own) {
                 const int ln = tid_now() & 63;
                 half8 bZ[2];
-                load_bz(bZ, vw, sm.zvT[c & 1], ln);
+                load_bz(bZ, vw, sm.zvT[c & 1], frag_off(ln));
                 value_update_plain<D>(G, sm.aL, bZ, sm.ft, ln);
             }
             if (c + 1 < nch) {
@@ -1352,6 +1351,8 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         // across the chunk loop
         const PTile ptv = p_tile_prep(sm, vw, tid_now() & 63);
         const uint32_t xoff = frag256_off(tid_now() & 63);  // s~ and X rows i, K block 0
+        const uint32_t foff = frag_off(tid_now() & 63);     // [rows][64] tile fragments (Z_v, F)
+        const uint32_t c_pp = opaque(lds_addr(sm.pp) + 2 * ((tid_now() & 15) * RP + 8 * ((tid_now() & 63) >> 4)));
         lds_barrier();  // chunk 0 features
         half8 bZ[2];    // Z_v fragments of the chunk whose readout comes next
         for (int c = 0; c <= nch; ++c) {
@@ -1374,7 +1375,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                     for (int tt = 0; tt < 4; ++tt) accO[tt] = mfma(bG, rd8(xb + 2 * 16 * tt * M2), accO[tt]);
                 }
                 // Gamma update with chunk c-1, once X Gamma has read the state before it
-                if (!(tail_fix && c == nch)) value_update<D>(G, sm.aH, bZ, sm.ft, ln);
+                if (!(tail_fix && c == nch)) value_update<D>(G, sm.aH, bZ, sm.ft, ln >> 4, foff);
             }
             lds_barrier();
             // ---- phase 2: z_k^T (c+1); o^T += Z_v^T P~^T, Delta o (c-1); Z_v fragments (c)
@@ -1387,7 +1388,6 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             if (c >= 1 && own) {
                 const int64_t tp = t0 - L;  // first token of chunk c-1
                 const int g = ln2 >> 4, i = ln2 & 15;
-                const uint32_t c_pp = opaque(lds_addr(sm.pp) + 2 * (i * RP + 8 * g));
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -1403,7 +1403,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, pk), ob, olane + toff, 0, 0);
                 }
             }
-            if (c < nch && own) load_bz(bZ, vw, sm.zvT, ln2);
+            if (c < nch && own) load_bz(bZ, vw, sm.zvT, foff);
             lds_barrier();
         }
         if (tail_fix) {
@@ -1413,7 +1413,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             if (own) {
                 const int ln = tid_now() & 63;
                 half8 bZl[2];
-                load_bz(bZl, vw, sm.zvT, ln);
+                load_bz(bZl, vw, sm.zvT, frag_off(ln));
                 value_update_plain<D>(G, a_n, bZl, sm.ft, ln);
             }
         }
