@@ -317,6 +317,28 @@ def test_decode_step_full_batch(fs):
     assert np.array_equal(down(tl), tl_ref.astype(np.float32))
 
 
+def test_decode_multi_token_full_batch(fs):
+    """Four tokens per decode call at 256 sequences x 16 heads (the call the
+    benchmark times) from a seeded synthetic state and tail: every output,
+    every updated state entry and the tail against the oracle's forward over
+    the same four tokens."""
+    s = WL.spec("decode")
+    st0, tl0 = WL.make_decode_state(s, seed=8)
+    q, k, v = WL.make_rows(s, seed=9, N=4)  # [B, 4, H, d] each
+    params = WL.make_params(s)
+    p = fs.params_to_device(params)
+    st = state_dev(st0)
+    tl = up(tl0, "bf16")
+    o = fs.decode_step(up(q, "bf16"), up(k, "bf16"), up(v, "bf16"), p, st, tl)
+    _sync()
+    o_ref, st_ref, tl_ref = oracle.forward(q, k, v, params, state_in=st0, tail_in=tl0)
+    e_o = rel_l2(down(o), o_ref)
+    e_s = rel_l2(state_np(st), st_ref)
+    print(f"decode x4: o relL2 {e_o:.3e}, state relL2 {e_s:.3e}")
+    assert e_o <= GATE_BF16 and e_s <= GATE_BF16
+    assert np.array_equal(down(tl), tl_ref.astype(np.float32))
+
+
 def test_decode_step_f32_gate(fs):
     s = WL.spec("1p3b", B=4, io="f32")
     st0, tl0 = WL.make_decode_state(s, seed=4)
