@@ -141,7 +141,12 @@ extern "C" {
 int idattn_version(void) { return 100; }
 
 const char* idattn_status_string(idattn_status st) {
-    switch (st) {
+    // A C caller may pass any int; reading it as the C++ enum type would be
+    // undefined outside the enumerators' range, so read its bytes as an int.
+    static_assert(sizeof(idattn_status) == sizeof(int), "idattn_status must be int-sized");
+    int v;
+    std::memcpy(&v, &st, sizeof v);
+    switch (v) {
         case IDATTN_OK: return "IDATTN_OK";
         case IDATTN_ERR_NULL: return "IDATTN_ERR_NULL";
         case IDATTN_ERR_SHAPE: return "IDATTN_ERR_SHAPE";
