@@ -277,7 +277,7 @@ def main():
     }
     out["measured_copy_gbps"] = measure_copy_gbps(torch)
     if not args.no_decode:
-        out["decode"] = decode_bench(torch, fs, steps=20, warmup=3)
+        out["decode"] = decode_bench(torch, fs, steps=20, warmup=20)
     del sets, ws
     torch.cuda.empty_cache()
     if not args.no_cpu:
