@@ -58,6 +58,9 @@ SMALL = {  # name: (base config, overrides, seed tag)
     "d64_w1_hard_bf16": ("125m", dict(B=1, H=2, N=129, W=1), 59),
     "d128_w1_bf16": ("1p3b", dict(B=1, H=2, N=129, W=1), 64),
     "d128_w8_bf16": ("1p3b", dict(B=1, H=1, N=70, W=8), 52),
+    # conv widths 2 and 3 on the chunked path (its halo holds three tokens)
+    "d128_w2_bf16": ("1p3b", dict(B=2, H=2, N=150, W=2), 65),
+    "d64_w3_bf16": ("125m", dict(B=2, H=2, N=170, W=3), 66),
     # 64 (b, h) pairs: four time segments of three chunks, the last one ragged
     "d128_segments_bf16": ("1p3b", dict(B=4, H=16, N=700), 62),
     "d64_segments_bf16": ("125m", dict(B=4, H=16, N=700), 63),
