@@ -44,6 +44,11 @@ Parity pins (tests/test_oracle_pins.py):
   feature_map_unit  pinned: ||xi|| = 1 and xi . y = ||y|| at eps_feat = 0;
                with both eps = 0 the unit-norm forward equals ||y_q|| times the
                squared one, token by token (RMSNorm removes the key-side scale).
+  feature_map_rff  pinned: the values at phases 0, pi/2 and pi (order of the
+               halves, sign of the sine, argument c rather than SiLU(c)),
+               ||xi|| = 1, eq. 5 by Monte Carlo against the Gaussian kernel for
+               Gaussian frequencies, and in the forward the identity
+               xi_q . xi_k = mean_f cos(w_f^T (c_q - c_k)) with the conv outputs.
   rms_norm     pinned: mean(((z - b)/g)^2) = m/(m + eps) identity.
   zoh          pinned: quadrature of exp(lambda*tau) and scipy.linalg.expm.
   forward      pinned: O(N^2) closed form of U, O(N^3) state-free kernel form
@@ -132,7 +137,23 @@ def feature_map_unit(c, eps_feat):
     return y / np.sqrt((y * y).sum(axis=-1, keepdims=True) + eps_feat)
 
 
-FEATURE_NORMS = ("squared", "unit")
+def feature_map_rff(c, omega):
+    """Random Fourier features xi_w(x) = [cos(w^T x), sin(w^T x)] (p1 section
+    3.1, eq. 6) of the conv output x = c, with the cosine half first.  Each
+    head has its own D = R/2 frequencies, the columns of omega[h] (d x D),
+    drawn by the caller from the spectral density p(w) of the stationary kernel.  The
+    1/sqrt(D) factor makes xi(x) . xi(x') the Monte-Carlo mean over the D
+    frequencies of cos(w^T (x - x')), i.e. the estimate of K(x, x') in eq. 5.
+
+    c [..., H, d]; omega [H, d, D].  Returns [..., H, 2D]."""
+    c = np.asarray(c, dtype=F64)
+    omega = np.asarray(omega, dtype=F64)
+    D = omega.shape[-1]
+    phase = np.einsum("...hi,hif->...hf", c, omega)
+    return np.concatenate([np.cos(phase), np.sin(phase)], axis=-1) / np.sqrt(D)
+
+
+FEATURE_NORMS = ("squared", "unit", "rff")
 
 
 def rms_norm(x, gain, bias, eps_norm):
@@ -175,8 +196,9 @@ def forward(q, k, v, params, eps_feat=1e-6, eps_norm=1e-6,
                then value half); log_dt [H]; A, Bc [H, M, 2]
     state_in   complex [B, H, M, 2d] (U then Gamma) or None (zeros)
     tail_in    [B, H, 2, W-1, d] raw q then k tokens before position 0, or None
-    feature_norm  "squared" (xi = y / (||y||^2 + eps), the printed form) or
-               "unit" (xi = y / sqrt(||y||^2 + eps))
+    feature_norm  "squared" (xi = y / (||y||^2 + eps), the printed form),
+               "unit" (xi = y / sqrt(||y||^2 + eps)) or "rff" (random Fourier
+               features of c with params["rff_omega"] [H, d, d/2])
 
     Returns (o [B, N, H, d] float64, state_out complex128 [B, H, M, 2d],
     tail_out [B, H, 2, W-1, d] float64) and, with intermediates=True, a dict
@@ -203,9 +225,14 @@ def forward(q, k, v, params, eps_feat=1e-6, eps_norm=1e-6,
     c_k = short_conv(k, params["conv_k"], tail_in[:, :, 1])
     if feature_norm not in FEATURE_NORMS:
         raise ValueError(f"feature_norm must be one of {FEATURE_NORMS}")
-    fmap = feature_map if feature_norm == "squared" else feature_map_unit
-    xi_q = fmap(c_q, eps_feat)
-    xi_k = fmap(c_k, eps_feat)
+    if feature_norm == "rff":
+        # queries and keys share one feature space (p1 Fig. 1): the same frequencies
+        xi_q = feature_map_rff(c_q, params["rff_omega"])
+        xi_k = feature_map_rff(c_k, params["rff_omega"])
+    else:
+        fmap = feature_map if feature_norm == "squared" else feature_map_unit
+        xi_q = fmap(c_q, eps_feat)
+        xi_k = fmap(c_k, eps_feat)
     # 3. input RMSNorm on the key-feature half and the value half
     z_k = rms_norm(xi_k, gain[:, :d], bias[:, :d], eps_norm)
     z_v = rms_norm(v, gain[:, d:], bias[:, d:], eps_norm)

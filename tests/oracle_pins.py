@@ -99,6 +99,69 @@ def pin_feature_map_unit(O) -> float:
     return max(float(e1), float(e2))
 
 
+def pin_rff_special(O) -> float:
+    """Random Fourier features at phases where cos and sin are exact: x = 0
+    gives [1, ..., 1, 0, ..., 0]/sqrt(D) (cosine half first); x = e_0 with every
+    frequency's first entry pi/2 gives [0, ..., 0, 1, ..., 1]/sqrt(D) (sin
+    taken with a plus sign, of x itself and not of SiLU(x)); entries pi give
+    [-1, ..., -1, 0, ..., 0]/sqrt(D)."""
+    r = np.random.default_rng(21)
+    H, d, D = 2, 8, 4
+    omega = r.normal(size=(H, d, D))
+    x = np.zeros((3, H, d))
+    x[1:, :, 0] = 1.0
+    omega[:, 0, :] = np.pi / 2
+    want = np.zeros((3, H, 2 * D))
+    want[0, :, :D] = 1.0
+    want[1, :, D:] = 1.0
+    xi = O.feature_map_rff(x[:2], omega)
+    omega[:, 0, :] = np.pi
+    want[2, :, :D] = -1.0
+    xi = np.concatenate([xi, O.feature_map_rff(x[2:], omega)])
+    return float(np.abs(xi - want / np.sqrt(D)).max())
+
+
+def pin_rff_norm(O) -> float:
+    """||xi(x)|| = 1 for every x (cos^2 + sin^2 = 1, D terms of 1/D)."""
+    r = np.random.default_rng(22)
+    xi = O.feature_map_rff(r.normal(size=(5, 6, 3, 16)) * 3, r.normal(size=(3, 16, 8)))
+    return float(np.abs(np.linalg.norm(xi, axis=-1) - 1).max())
+
+
+def pin_rff_bochner(O) -> float:
+    """p1 eq. 5: with frequencies w ~ N(0, I / sigma^2), the mean of
+    xi(x) . xi(x') over many frequencies estimates the Gaussian kernel
+    exp(-||x - x'||^2 / (2 sigma^2)), the Fourier transform of that density.
+    D = 40000 frequencies: the Monte-Carlo standard error is below 0.004, so
+    the returned error is divided by 0.02 (the pin's tolerance is 1)."""
+    r = np.random.default_rng(23)
+    d, D, sigma = 5, 40000, 1.3
+    omega = r.normal(size=(1, d, D)) / sigma
+    x = r.normal(size=(6, 1, d)) * 0.8
+    xi = O.feature_map_rff(x, omega)[:, 0]
+    est = xi @ xi.T
+    dist2 = ((x[:, None, 0] - x[None, :, 0]) ** 2).sum(-1)
+    return float(np.abs(est - np.exp(-dist2 / (2 * sigma * sigma))).max() / 0.02)
+
+
+def pin_rff_wiring(O) -> float:
+    """In the forward with the RFF map, queries and keys use the same
+    frequencies on the conv outputs: xi_q(i) . xi_k(j) equals
+    mean_f cos(w_f^T (c_q(i) - c_k(j))) for every pair of positions."""
+    c = pin_case()
+    p = dict(c["p"])
+    H, d = c["q"].shape[2], c["q"].shape[3]
+    p["rff_omega"] = np.random.default_rng(24).normal(size=(H, d, d // 2))
+    _, _, _, it = O.forward(c["q"], c["k"], c["v"], p, 1e-6, 1e-6, None, c["tail"], True, feature_norm="rff")
+    err = 0.0
+    for h in range(H):
+        dots = np.einsum("bih,bjh->bij", it["xi_q"][:, :, h], it["xi_k"][:, :, h])
+        diff = it["c_q"][:, :, None, h] - it["c_k"][:, None, :, h]          # [B, N, N, d]
+        want = np.cos(np.einsum("bijc,cf->bijf", diff, p["rff_omega"][h])).mean(-1)
+        err = max(err, float(np.abs(dots - want).max()))
+    return err
+
+
 def pin_unit_scaling(O) -> float:
     """With eps_feat = eps_norm = 0 the key features enter only through RMSNorm,
     which is blind to a per-token scale, and the query features scale s (hence
@@ -339,6 +402,10 @@ PINS = {
     "feature_map": (pin_feature_map, 1e-12),
     "feature_map_unit": (pin_feature_map_unit, 1e-12),
     "unit_scaling": (pin_unit_scaling, 1e-11),
+    "rff_special": (pin_rff_special, 1e-15),
+    "rff_norm": (pin_rff_norm, 1e-14),
+    "rff_bochner": (pin_rff_bochner, 1.0),
+    "rff_wiring": (pin_rff_wiring, 1e-13),
     "rms_norm": (pin_rms_norm, 1e-12),
     "zoh": (pin_zoh, 1e-10),
     "wiring": (pin_wiring, 1e-10),

@@ -45,6 +45,30 @@ def _featmap_unit_no_sqrt(c, eps):
     return y / ((y * y).sum(-1, keepdims=True) + eps)
 
 
+def _rff_sin_negated(c, omega):
+    xi = _orig["feature_map_rff"](c, omega)
+    D = np.asarray(omega).shape[-1]
+    return np.concatenate([xi[..., :D], -xi[..., D:]], axis=-1)
+
+
+def _rff_halves_swapped(c, omega):
+    xi = _orig["feature_map_rff"](c, omega)
+    D = np.asarray(omega).shape[-1]
+    return np.concatenate([xi[..., D:], xi[..., :D]], axis=-1)
+
+
+def _rff_of_silu(c, omega):
+    return _orig["feature_map_rff"](O.silu(c), omega)
+
+
+def _rff_unscaled(c, omega):
+    return _orig["feature_map_rff"](c, omega) * np.sqrt(np.asarray(omega).shape[-1])
+
+
+def _rff_half_frequency(c, omega):
+    return _orig["feature_map_rff"](c, 0.5 * np.asarray(omega))
+
+
 def _rms_sum(x, g, b, eps):
     x = np.asarray(x, float)
     return np.asarray(g)[None, None] * x / np.sqrt((x * x).sum(-1, keepdims=True) + eps) + np.asarray(b)[None, None]
@@ -93,7 +117,8 @@ def _step_imag_dropped(U, G, xq, zk, zv, a, b):
     return U, G, s, np.einsum("bhm,bhmc->bhc", s.real, G.real)
 
 
-_orig = {name: getattr(O, name) for name in ("short_conv", "silu", "feature_map", "feature_map_unit", "rms_norm",
+_orig = {name: getattr(O, name) for name in ("short_conv", "silu", "feature_map", "feature_map_unit", "feature_map_rff",
+                                             "rms_norm",
                                              "zoh", "ssm_step")}
 
 MUTANTS = {
@@ -102,6 +127,11 @@ MUTANTS = {
     "silu_wrong_sign": ("silu", _silu_sign),
     "featmap_unsquared_norm": ("feature_map", _featmap_unsquared),
     "featmap_unit_without_sqrt": ("feature_map_unit", _featmap_unit_no_sqrt),
+    "rff_sin_negated": ("feature_map_rff", _rff_sin_negated),
+    "rff_halves_swapped": ("feature_map_rff", _rff_halves_swapped),
+    "rff_of_silu": ("feature_map_rff", _rff_of_silu),
+    "rff_unscaled": ("feature_map_rff", _rff_unscaled),
+    "rff_half_frequency": ("feature_map_rff", _rff_half_frequency),
     "rms_sum_not_mean": ("rms_norm", _rms_sum),
     "rms_dropped_bias": ("rms_norm", _rms_no_bias),
     "zoh_euler_bbar": ("zoh", _zoh_euler),
