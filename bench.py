@@ -75,15 +75,16 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="1p3b", choices=["125m", "1p3b", "14k"])
     ap.add_argument("--algo", default="auto", choices=["auto", "sequential", "chunked"])
-    ap.add_argument("--feature-norm", default="squared", choices=["squared", "unit"],
-                    help="feature map xi = y / (||y||^2 + eps) (squared) or y / sqrt(||y||^2 + eps) (unit)")
+    ap.add_argument("--feature-norm", default="squared", choices=["squared", "unit", "rff"],
+                    help="feature map xi = y / (||y||^2 + eps) (squared), y / sqrt(||y||^2 + eps) (unit), or "
+                         "random Fourier features of the conv output (rff; sequential path only)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU sample")
     return ap.parse_args()
 
 
-def cpu_baseline(s, q, k, v, params, target_s: float):
+def cpu_baseline(s, q, k, v, params, target_s: float, feature_norm: str = "squared"):
     """The oracle as it stands, one thread, on a bounded sample: the first
     batch rows (every head), whole sequences when they fit the time target,
     else a prefix of row 0."""
@@ -94,13 +95,13 @@ def cpu_baseline(s, q, k, v, params, target_s: float):
     with threadpool_limits(limits=1):
         n0 = 32
         t = time.perf_counter()
-        oracle.forward(q[:1, :n0], k[:1, :n0], v[:1, :n0], params)
+        oracle.forward(q[:1, :n0], k[:1, :n0], v[:1, :n0], params, feature_norm=feature_norm)
         per_tok = (time.perf_counter() - t) / n0  # one row, every head
         budget_tok = target_s / max(per_tok, 1e-9)
         rows = int(max(1, min(s["B"], budget_tok // s["N"])))
         n = int(max(n0, min(s["N"], budget_tok)))
         t = time.perf_counter()
-        o, _, _ = oracle.forward(q[:rows, :n], k[:rows, :n], v[:rows, :n], params)
+        o, _, _ = oracle.forward(q[:rows, :n], k[:rows, :n], v[:rows, :n], params, feature_norm=feature_norm)
         dt = time.perf_counter() - t
     assert np.isfinite(o).all()
     return {"value": rows * n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
@@ -201,6 +202,8 @@ def main():
     B, N, H, d, M, W = s["B"], s["N"], s["H"], s["d"], s["M"], s["W"]
     q, k, v = WL.make_rows(s)
     params = WL.make_params(s)
+    if args.feature_norm == "rff":
+        params["rff_omega"] = WL.make_rff_omega(s)
     p = fs.params_to_device(params)
     prm = fs.make_params(p)
 
@@ -220,7 +223,8 @@ def main():
     algo = args.algo
     if algo == "auto":
         try:
-            fs.idattn_forward_workspace_size(fs.make_dims(B, N, H, d, M, W, "bf16", "chunked"))
+            fs.idattn_forward_workspace_size(fs.make_dims(B, N, H, d, M, W, "bf16", "chunked",
+                                                          feature_norm=args.feature_norm))
             algo = "chunked"
         except fs.IdattnError:
             algo = "sequential"
@@ -262,7 +266,8 @@ def main():
         "dtype": "f32" if algo == "sequential" else "f16-mfma/f32",
         "data": "synthetic (seeded N(0,1) bf16 q,k,v; S4D-Lin init)",
         "config": {"workload": f"{args.config}: B={B} H={H} N={N} d=R={d} M={M} W={W}, bf16 I/O, fp32 state"
-                               + ("" if args.feature_norm == "squared" else ", unit-norm feature map"),
+                               + {"squared": "", "unit": ", unit-norm feature map",
+                                  "rff": ", random Fourier feature map"}[args.feature_norm],
                    "B": B, "N": N, "H": H, "d": d, "M": M, "W": W, "io": "bf16", "algo": algo,
                    "feature_norm": args.feature_norm},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -281,7 +286,7 @@ def main():
     del sets, ws
     torch.cuda.empty_cache()
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(s, q, k, v, params, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(s, q, k, v, params, args.cpu_seconds, args.feature_norm)
     print(json.dumps(out), flush=True)
 
 

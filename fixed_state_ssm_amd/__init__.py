@@ -22,9 +22,11 @@ PARAM_KEYS = ("conv_q", "conv_k", "gain", "bias", "log_dt", "A", "Bc")
 
 
 def params_to_device(p: dict, device="cuda"):
-    """Copy a dict of float32 arrays/tensors (the idattn_params layout) to the device."""
+    """Copy a dict of float32 arrays/tensors (the idattn_params layout, with
+    rff_omega when present) to the device."""
     import torch
-    return {k: torch.as_tensor(p[k], dtype=torch.float32).contiguous().to(device) for k in PARAM_KEYS}
+    keys = PARAM_KEYS + (("rff_omega",) if p.get("rff_omega") is not None else ())
+    return {k: torch.as_tensor(p[k], dtype=torch.float32).contiguous().to(device) for k in keys}
 
 
 def _io_name(t):

@@ -18,7 +18,7 @@ STATUS = {0: "IDATTN_OK", 1: "IDATTN_ERR_NULL", 2: "IDATTN_ERR_SHAPE", 3: "IDATT
           4: "IDATTN_ERR_WORKSPACE", 5: "IDATTN_ERR_ALIAS", 6: "IDATTN_ERR_ARG", 7: "IDATTN_ERR_HIP"}
 IO = {"f32": 0, "bf16": 1}
 ALGO = {"auto": 0, "sequential": 1, "chunked": 2}
-FEATURE_NORM = {"squared": 0, "unit": 1}
+FEATURE_NORM = {"squared": 0, "unit": 1, "rff": 2}
 
 EXPORTS = ("idattn_forward_workspace_size", "idattn_forward", "idattn_decode_step",
            "idattn_status_string", "idattn_last_error", "idattn_version")
@@ -32,7 +32,7 @@ class IdattnDims(ctypes.Structure):
 
 class IdattnParams(ctypes.Structure):
     _fields_ = [("conv_q", c_void_p), ("conv_k", c_void_p), ("gain", c_void_p), ("bias", c_void_p),
-                ("log_dt", c_void_p), ("A", c_void_p), ("Bc", c_void_p)]
+                ("log_dt", c_void_p), ("A", c_void_p), ("Bc", c_void_p), ("rff_omega", c_void_p)]
 
 
 class IdattnError(RuntimeError):
@@ -108,9 +108,11 @@ def make_dims(B, N, H, d, M, W=4, io="bf16", algo="auto", eps_feat=1e-6, eps_nor
 
 
 def make_params(p: dict) -> IdattnParams:
-    """p: dict of float32 device tensors conv_q, conv_k, gain, bias, log_dt, A, Bc.
+    """p: dict of float32 device tensors conv_q, conv_k, gain, bias, log_dt, A, Bc
+    and, for the RFF feature map, rff_omega [H, d, d/2] (else absent or None).
     The caller keeps the tensors alive while the struct is in use."""
-    return IdattnParams(*(_ptr(p[k]) for k in ("conv_q", "conv_k", "gain", "bias", "log_dt", "A", "Bc")))
+    keys = ("conv_q", "conv_k", "gain", "bias", "log_dt", "A", "Bc")
+    return IdattnParams(*(_ptr(p[k]) for k in keys), _ptr(p.get("rff_omega")))
 
 
 # ------------------------------------------------------------------ C entry points

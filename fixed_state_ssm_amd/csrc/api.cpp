@@ -62,7 +62,8 @@ idattn_status check_dims(const idattn_dims* dims, bool decode) {
         return fail(IDATTN_ERR_ARG, "eps_feat must be finite and >= 0");
     if (!(D.eps_norm >= 0.f) || !std::isfinite(D.eps_norm))
         return fail(IDATTN_ERR_ARG, "eps_norm must be finite and >= 0");
-    if (D.feature_norm != IDATTN_FEATURE_SQUARED && D.feature_norm != IDATTN_FEATURE_UNIT)
+    if (D.feature_norm != IDATTN_FEATURE_SQUARED && D.feature_norm != IDATTN_FEATURE_UNIT &&
+        D.feature_norm != IDATTN_FEATURE_RFF)
         return fail(IDATTN_ERR_ARG, "feature_norm %d is not a known idattn_feature_norm", D.feature_norm);
     // element counts must stay far from int64 overflow
     const double elems = static_cast<double>(D.B) * D.N * D.H * D.d;
@@ -79,10 +80,27 @@ idattn_status check_dims(const idattn_dims* dims, bool decode) {
     return IDATTN_OK;
 }
 
-idattn_status check_params(const idattn_params* prm) {
+idattn_status check_params(const idattn_dims& D, const idattn_params* prm) {
     if (prm == nullptr) return fail(IDATTN_ERR_NULL, "params is NULL");
     if (!prm->conv_q || !prm->conv_k || !prm->gain || !prm->bias || !prm->log_dt || !prm->A || !prm->Bc)
         return fail(IDATTN_ERR_NULL, "a parameter pointer is NULL");
+    if (D.feature_norm == IDATTN_FEATURE_RFF && !prm->rff_omega)
+        return fail(IDATTN_ERR_NULL, "rff_omega is NULL with IDATTN_FEATURE_RFF");
+    return IDATTN_OK;
+}
+
+// Output buffers must not overlap any parameter the kernels read.
+idattn_status check_params_disjoint(const idattn_dims& D, const idattn_params& P, const Range* outs, int n_outs) {
+    const size_t conv = static_cast<size_t>(D.H * D.d * D.W) * 4, gb = static_cast<size_t>(D.H * 2 * D.d) * 4;
+    const size_t mb = static_cast<size_t>(D.H * D.M * 2) * 4;
+    const size_t ob = D.feature_norm == IDATTN_FEATURE_RFF ? static_cast<size_t>(D.H * D.d * (D.d / 2)) * 4 : 0;
+    const Range prm[] = {range("conv_q", P.conv_q, conv), range("conv_k", P.conv_k, conv),
+                         range("gain", P.gain, gb),        range("bias", P.bias, gb),
+                         range("log_dt", P.log_dt, D.H * 4), range("A", P.A, mb),
+                         range("Bc", P.Bc, mb),            range("rff_omega", P.rff_omega, ob)};
+    for (int i = 0; i < n_outs; ++i)
+        for (const Range& b : prm)
+            if (overlap(outs[i], b)) return fail(IDATTN_ERR_ALIAS, "%s overlaps parameter %s", outs[i].name, b.name);
     return IDATTN_OK;
 }
 
@@ -98,6 +116,7 @@ idattn::Problem problem(const idattn_dims& D) {
     p.eps_feat = D.eps_feat;
     p.eps_norm = D.eps_norm;
     p.unit_feat = D.feature_norm == IDATTN_FEATURE_UNIT;
+    p.rff_feat = D.feature_norm == IDATTN_FEATURE_RFF;
     return p;
 }
 
@@ -124,6 +143,7 @@ idattn_status workspace_bytes(const idattn_dims& D, int algo, size_t* bytes) {
         const idattn::Problem p = problem(D);
         if (D.io_dtype != IDATTN_IO_BF16)
             return fail(IDATTN_ERR_UNSUPPORTED, "the chunked algorithm needs bf16 I/O");
+        if (p.rff_feat) return fail(IDATTN_ERR_UNSUPPORTED, "the chunked algorithm has no RFF feature map");
         if (!idattn::chunked_supported(p))
             return fail(IDATTN_ERR_UNSUPPORTED, "the chunked algorithm has no kernel for d=%lld M=%lld",
                         (long long)D.d, (long long)D.M);
@@ -138,7 +158,7 @@ idattn_status workspace_bytes(const idattn_dims& D, int algo, size_t* bytes) {
 
 extern "C" {
 
-int idattn_version(void) { return 100; }
+int idattn_version(void) { return 200; }
 
 const char* idattn_status_string(idattn_status st) {
     // A C caller may pass any int; reading it as the C++ enum type would be
@@ -174,7 +194,7 @@ idattn_status idattn_forward(const idattn_dims* dims, const idattn_params* param
                              size_t workspace_bytes_given, void* stream) {
     idattn_status st = check_dims(dims, false);
     if (st != IDATTN_OK) return st;
-    st = check_params(params);
+    st = check_params(*dims, params);
     if (st != IDATTN_OK) return st;
     const idattn_dims& D = *dims;
     const int algo = resolve_algo(D);
@@ -212,17 +232,8 @@ idattn_status idattn_forward(const idattn_dims* dims, const idattn_params* param
             }
             return fail(IDATTN_ERR_ALIAS, "%s overlaps %s", a.name, b.name);
         }
-    {
-        const size_t conv = static_cast<size_t>(D.H * D.d * D.W) * 4, gb = static_cast<size_t>(D.H * 2 * D.d) * 4;
-        const size_t mb = static_cast<size_t>(D.H * D.M * 2) * 4;
-        const Range prm[] = {range("conv_q", params->conv_q, conv), range("conv_k", params->conv_k, conv),
-                             range("gain", params->gain, gb),        range("bias", params->bias, gb),
-                             range("log_dt", params->log_dt, D.H * 4), range("A", params->A, mb),
-                             range("Bc", params->Bc, mb)};
-        for (const Range& a : outs)
-            for (const Range& b : prm)
-                if (overlap(a, b)) return fail(IDATTN_ERR_ALIAS, "%s overlaps parameter %s", a.name, b.name);
-    }
+    st = check_params_disjoint(D, *params, outs, 4);
+    if (st != IDATTN_OK) return st;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const idattn::Problem p = problem(D);
@@ -271,7 +282,7 @@ idattn_status idattn_decode_step(const idattn_dims* dims, const idattn_params* p
                                  void* stream) {
     idattn_status st = check_dims(dims, true);
     if (st != IDATTN_OK) return st;
-    st = check_params(params);
+    st = check_params(*dims, params);
     if (st != IDATTN_OK) return st;
     const idattn_dims& D = *dims;
     if (!q_t || !k_t || !v_t || !o_t || !state) return fail(IDATTN_ERR_NULL, "q_t, k_t, v_t, o_t and state must be non-NULL");
@@ -297,6 +308,8 @@ idattn_status idattn_decode_step(const idattn_dims* dims, const idattn_params* p
             if (a.name == b.name) continue;
             if (overlap(a, b)) return fail(IDATTN_ERR_ALIAS, "%s overlaps %s", a.name, b.name);
         }
+    st = check_params_disjoint(D, *params, outs, 3);
+    if (st != IDATTN_OK) return st;
     const hipError_t e = idattn::launch_decode_step(problem(D), *params, q_t, k_t, v_t, o_t, state, tail,
                                                     static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode_step");

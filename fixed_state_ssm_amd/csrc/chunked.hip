@@ -10,6 +10,7 @@ namespace idattn {
 bool chunked_supported(const Problem& p) {
     // M = 64 modes, d = R in {64, 128}, conv width up to 4
     if (!(p.bf16 && p.M == 64 && (p.d == 64 || p.d == 128) && p.W >= 1 && p.W <= 4)) return false;
+    if (p.rff_feat) return false;  // the chunked feature code has the SiLU maps only
     // the kernels address one (b, h) sequence with 32-bit byte offsets
     return p.N * p.H * p.d * 2 < (int64_t{1} << 31);
 }

@@ -54,6 +54,53 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// ------------------------------------------------------------------ RFF
+// Random Fourier features of one token-head held by one wave (Chinese
+// rendering of the paper, section 3.1, eq. 6): with D = d/2 frequencies, the
+// columns of om = Omega_h (row-major [d][D]),
+// xi = [cos(Omega^T c), sin(Omega^T c)] / sqrt(D), cosine half first.
+// Lane l holds the conv outputs of channels l + 64 j in cq[j], ck[j] (zero
+// past d) and receives the features of the same channels.  Those need only
+// the phase of frequency l mod D, so each lane forms one query and one key
+// phase: every input is broadcast from its lane with readlane and multiplied
+// by that lane's entry of the input's row of Omega (one coalesced row per
+// input, shared by queries and keys).
+template <int DJ>
+__device__ __forceinline__ void rff_features(const float (&cq)[DJ], const float (&ck)[DJ],
+                                             const float* __restrict__ om, int d, float (&yq)[DJ],
+                                             float (&yk)[DJ]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int D = d >> 1;         // a power of two, at most 64
+    const int f = lane & (D - 1);
+    float pq = 0.f, pk = 0.f;
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+        const int n = min(d - kWave * j, kWave);  // inputs held in slot j: 0, 16, 32 or 64
+        for (int l0 = 0; l0 < n; l0 += 16) {
+            // sixteen rows of Omega in flight at once
+            float w[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) w[u] = om[(kWave * j + l0 + u) * D + f];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                pq = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(cq[j]), l0 + u)), w[u], pq);
+                pk = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ck[j]), l0 + u)), w[u], pk);
+            }
+        }
+    }
+    float sq, cs_q, sk, cs_k;
+    sincosf(pq, &sq, &cs_q);
+    sincosf(pk, &sk, &cs_k);
+    const float sc = 1.f / sqrtf(static_cast<float>(D));
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+        const int c = lane + kWave * j;
+        const bool in = c < d, sn = c >= D;
+        yq[j] = in ? (sn ? sq : cs_q) * sc : 0.f;
+        yk[j] = in ? (sn ? sk : cs_k) * sc : 0.f;
+    }
+}
+
 // ------------------------------------------------------------------ ZOH
 // Zero-order hold of u' = lambda u + B z over a step Delta = exp(log_dt),
 // evaluated in fp64:  abar = exp(Delta lambda),

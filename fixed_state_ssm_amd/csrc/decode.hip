@@ -2,7 +2,7 @@
 // in HBM.
 //
 // One block of 4 waves per (b, h).  Wave 0 first builds the tokens' features
-// (conv over the tail and the new tokens, SiLU feature map, per-half RMSNorm)
+// (conv over the tail and the new tokens, feature map, per-half RMSNorm)
 // into LDS and shifts the conv tail; wave 1 evaluates the ZOH coefficients of
 // all M modes (one mode per lane).  Then every wave streams its quarter of
 // the M rows of the complex state [M][2d]: a row is read once as float4s,
@@ -66,10 +66,39 @@ __device__ __forceinline__ float wave_total(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Features of one token from its conv outputs (lane owns channels lane and
+// lane + 64; zero past d): xi = y * inv with y = SiLU(c) and the squared or
+// the unit norm, or (RFF) the random Fourier features of c with inv = 1.
+template <bool RFF>
+__device__ __forceinline__ void token_features(const Problem& p, const float* __restrict__ om,
+                                               const float (&cq)[2], const float (&ck)[2], float (&yq)[2],
+                                               float (&yk)[2], float& inv_q, float& inv_k) {
+    if constexpr (RFF) {
+        rff_features<2>(cq, ck, om, static_cast<int>(p.d), yq, yk);
+        inv_q = inv_k = 1.f;
+        return;
+    }
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        yq[j] = cq[j] / (1.f + expf(-cq[j]));
+        yk[j] = ck[j] / (1.f + expf(-ck[j]));
+        sq = fmaf(yq[j], yq[j], sq);
+        sk = fmaf(yk[j], yk[j], sk);
+    }
+    sq = wave_sum(sq);
+    sk = wave_sum(sk);
+    // squared norm, or its square root for the unit-norm map
+    inv_q = p.unit_feat ? 1.f / sqrtf(sq + p.eps_feat) : 1.f / (sq + p.eps_feat);
+    inv_k = p.unit_feat ? 1.f / sqrtf(sk + p.eps_feat) : 1.f / (sk + p.eps_feat);
+}
+
 // NT = most tokens of the instance (1, or kDecodeMaxTokens with the call's
 // n = p.N <= NT); FJ = float4 chunks of a state row per lane (d / 64, at least
-// 1); RPW = rows per wave (M / 4).  Tokens are [B][n][H][d].
-template <bool BF16, int NT, int FJ, int RPW>
+// 1); RPW = rows per wave (M / 4); RFF = random Fourier feature map (its own
+// instances, so that the SiLU maps keep their register count).  Tokens are
+// [B][n][H][d].
+template <bool BF16, int NT, int FJ, int RPW, bool RFF>
 __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_params prm,
                                                           const void* __restrict__ q_t,
                                                           const void* __restrict__ k_t,
@@ -92,15 +121,15 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
     if (w == 0) {
         if constexpr (NT == 1) {
             // features of the new token; lane owns channels lane and lane + 64
-            float yq[2], yk[2], vv[2];
-            float sq = 0.f, sk = 0.f, sv = 0.f;
+            float cqv[2], ckv[2], yq[2], yk[2], vv[2];
+            float sv = 0.f;
             const int64_t tok = bh * d;  // [B][H][d]
             const int64_t E = 2 * static_cast<int64_t>(W - 1) * d;
     #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int c = lane + kWave * j;
                 float cq = 0.f, ck = 0.f;
-                yq[j] = yk[j] = vv[j] = 0.f;
+                vv[j] = 0.f;
                 if (c < d) {
                     const float* wq = prm.conv_q + (h * d + c) * W;
                     const float* wk = prm.conv_k + (h * d + c) * W;
@@ -127,19 +156,14 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
                         store_io<BF16>(tail, bh * E + static_cast<int64_t>(2 * W - 3) * d + c, xk);
                     }
                     vv[j] = load_io<BF16>(v_t, tok + c);
-                    yq[j] = cq / (1.f + expf(-cq));
-                    yk[j] = ck / (1.f + expf(-ck));
                 }
-                sq = fmaf(yq[j], yq[j], sq);
-                sk = fmaf(yk[j], yk[j], sk);
+                cqv[j] = cq;
+                ckv[j] = ck;
                 sv = fmaf(vv[j], vv[j], sv);
             }
-            sq = wave_sum(sq);
-            sk = wave_sum(sk);
             sv = wave_sum(sv);
-            // xi = y * inv: squared norm, or its square root for the unit-norm map
-            const float inv_q = p.unit_feat ? 1.f / sqrtf(sq + p.eps_feat) : 1.f / (sq + p.eps_feat);
-            const float inv_k = p.unit_feat ? 1.f / sqrtf(sk + p.eps_feat) : 1.f / (sk + p.eps_feat);
+            float inv_q, inv_k;
+            token_features<RFF>(p, prm.rff_omega + h * d * (d / 2), cqv, ckv, yq, yk, inv_q, inv_k);
             float xk2 = 0.f, xik[2];
     #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -183,12 +207,12 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
             for (int t = 0; t < NT; ++t) {
                 if (t < n) {
                     const int64_t tok = ((b * n + t) * p.H + h) * d;  // [B][n][H][d]
-                    float yq[2], yk[2], vv[2];
-                    float sq = 0.f, sk = 0.f, sv = 0.f;
+                    float cqv[2], ckv[2], yq[2], yk[2], vv[2];
+                    float sv = 0.f;
     #pragma unroll
                     for (int j = 0; j < 2; ++j) {
                         const int c = lane + kWave * j;
-                        yq[j] = yk[j] = vv[j] = 0.f;
+                        cqv[j] = ckv[j] = vv[j] = 0.f;
                         if (c < d) {
                             const float xq = load_io<BF16>(q_t, tok + c);
                             const float xk = load_io<BF16>(k_t, tok + c);
@@ -205,19 +229,14 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
                                 hk[j][u] = u + 1 < W - 1 ? hk[j][u < 6 ? u + 1 : 6] : (u == W - 2 ? xk : hk[j][u]);
                             }
                             vv[j] = load_io<BF16>(v_t, tok + c);
-                            yq[j] = cq / (1.f + expf(-cq));
-                            yk[j] = ck / (1.f + expf(-ck));
+                            cqv[j] = cq;
+                            ckv[j] = ck;
                         }
-                        sq = fmaf(yq[j], yq[j], sq);
-                        sk = fmaf(yk[j], yk[j], sk);
                         sv = fmaf(vv[j], vv[j], sv);
                     }
-                    sq = wave_sum(sq);
-                    sk = wave_sum(sk);
                     sv = wave_sum(sv);
-                    // xi = y * inv: squared norm, or its square root for the unit-norm map
-                    const float inv_q = p.unit_feat ? 1.f / sqrtf(sq + p.eps_feat) : 1.f / (sq + p.eps_feat);
-                    const float inv_k = p.unit_feat ? 1.f / sqrtf(sk + p.eps_feat) : 1.f / (sk + p.eps_feat);
+                    float inv_q, inv_k;
+                    token_features<RFF>(p, prm.rff_omega + h * d * (d / 2), cqv, ckv, yq, yk, inv_q, inv_k);
                     float xk2 = 0.f, xik[2];
     #pragma unroll
                     for (int j = 0; j < 2; ++j) {
@@ -347,12 +366,17 @@ hipError_t launch_decode_step(const Problem& p, const idattn_params& prm, const 
                               const void* k_t, const void* v_t, void* o_t, float* state,
                               void* tail, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(p.B * p.H));
-#define IDATTN_DEC_NT(NT, FJ, RPW)                                                                            \
-    do {                                                                                                      \
-        if (p.bf16)                                                                                           \
-            decode_step_kernel<true, NT, FJ, RPW><<<grid, 256, 0, stream>>>(p, prm, q_t, k_t, v_t, o_t, state, tail); \
-        else                                                                                                  \
-            decode_step_kernel<false, NT, FJ, RPW><<<grid, 256, 0, stream>>>(p, prm, q_t, k_t, v_t, o_t, state, tail); \
+#define IDATTN_DEC_K(BF, NT, FJ, RPW)                                                                          \
+    do {                                                                                                        \
+        if (p.rff_feat)                                                                                         \
+            decode_step_kernel<BF, NT, FJ, RPW, true><<<grid, 256, 0, stream>>>(p, prm, q_t, k_t, v_t, o_t, state, tail);  \
+        else                                                                                                    \
+            decode_step_kernel<BF, NT, FJ, RPW, false><<<grid, 256, 0, stream>>>(p, prm, q_t, k_t, v_t, o_t, state, tail); \
+    } while (0)
+#define IDATTN_DEC_NT(NT, FJ, RPW)                  \
+    do {                                            \
+        if (p.bf16) IDATTN_DEC_K(true, NT, FJ, RPW);  \
+        else IDATTN_DEC_K(false, NT, FJ, RPW);        \
     } while (0)
 #define IDATTN_DEC(FJ, RPW)                                 \
     do {                                                    \
@@ -370,6 +394,7 @@ hipError_t launch_decode_step(const Problem& p, const idattn_params& prm, const 
     else return hipErrorInvalidValue;
 #undef IDATTN_DEC
 #undef IDATTN_DEC_NT
+#undef IDATTN_DEC_K
     return hipGetLastError();
 }
 

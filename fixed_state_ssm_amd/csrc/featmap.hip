@@ -1,7 +1,9 @@
 // featmap_conv_norm: causal depthwise short conv of q and k, the SiLU feature
 // map with squared-norm normalisation, and the per-half input RMSNorm
 // (gist.science German summary, "Skalierbare Implementierung": feature-map
-// and normalisation bullets).  Also the conv-tail update and a copy kernel.
+// and normalisation bullets), or one of the other feature maps (unit norm;
+// random Fourier features, Chinese rendering, section 3.1, eq. 6).  Also the
+// conv-tail update and a copy kernel.
 //
 // One wave per token-head; lane l owns channels l and l + 64.  Token-heads are
 // numbered in [B][N][H] order so that neighbouring waves read neighbouring
@@ -28,8 +30,8 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
     const int64_t n = (th / H) % N;
     const int64_t b = th / (H * N);
 
-    float yq[DJ], yk[DJ], xv[DJ];
-    float sq = 0.f, sk = 0.f, sv = 0.f;
+    float cqv[DJ], ckv[DJ], yq[DJ], yk[DJ], xv[DJ];
+    float sv = 0.f;
 #pragma unroll
     for (int j = 0; j < DJ; ++j) {
         const int c = lane + kWave * j;
@@ -54,20 +56,32 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
             }
             vv = load_io<BF16>(v, ((b * N + n) * H + h) * d + c);
         }
-        // SiLU(c) = c / (1 + exp(-c)); lanes past d hold c = 0 -> y = 0.
-        yq[j] = cq / (1.f + expf(-cq));
-        yk[j] = ck / (1.f + expf(-ck));
+        cqv[j] = cq;
+        ckv[j] = ck;
         xv[j] = vv;
-        sq = fmaf(yq[j], yq[j], sq);
-        sk = fmaf(yk[j], yk[j], sk);
         sv = fmaf(vv, vv, sv);
     }
-    sq = wave_sum(sq);
-    sk = wave_sum(sk);
     sv = wave_sum(sv);
-    // xi = y * inv: squared norm, or its square root for the unit-norm map
-    const float inv_q = p.unit_feat ? 1.f / sqrtf(sq + p.eps_feat) : 1.f / (sq + p.eps_feat);
-    const float inv_k = p.unit_feat ? 1.f / sqrtf(sk + p.eps_feat) : 1.f / (sk + p.eps_feat);
+    // xi = y * inv
+    float inv_q = 1.f, inv_k = 1.f;
+    if (p.rff_feat) {
+        rff_features<DJ>(cqv, ckv, prm.rff_omega + h * d * (d / 2), d, yq, yk);
+    } else {
+        // SiLU(c) = c / (1 + exp(-c)); lanes past d hold c = 0 -> y = 0.
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            yq[j] = cqv[j] / (1.f + expf(-cqv[j]));
+            yk[j] = ckv[j] / (1.f + expf(-ckv[j]));
+            sq = fmaf(yq[j], yq[j], sq);
+            sk = fmaf(yk[j], yk[j], sk);
+        }
+        sq = wave_sum(sq);
+        sk = wave_sum(sk);
+        // squared norm, or its square root for the unit-norm map
+        inv_q = p.unit_feat ? 1.f / sqrtf(sq + p.eps_feat) : 1.f / (sq + p.eps_feat);
+        inv_k = p.unit_feat ? 1.f / sqrtf(sk + p.eps_feat) : 1.f / (sk + p.eps_feat);
+    }
     float xk2 = 0.f;
     float xik[DJ];
 #pragma unroll

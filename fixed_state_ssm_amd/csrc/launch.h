@@ -14,6 +14,7 @@ struct Problem {
     bool bf16;
     float eps_feat, eps_norm;
     bool unit_feat;  // xi = y / sqrt(||y||^2 + eps_feat) instead of y / (||y||^2 + eps_feat)
+    bool rff_feat;   // xi = random Fourier features of c with prm.rff_omega (overrides unit_feat)
 };
 
 // ---- stage kernels of the sequential (fp32) path; workspace layout [B][H][N][*]

@@ -10,7 +10,8 @@
  *   per batch row b, head h, position i, with R = d channels per head,
  *   c   = SC(x), a causal depthwise conv of width W, on q and on k
  *   xi  = SiLU(c) / (||SiLU(c)||^2 + eps_feat)             (norm over R; or,
- *         with IDATTN_FEATURE_UNIT, SiLU(c) / sqrt(||SiLU(c)||^2 + eps_feat))
+ *         with IDATTN_FEATURE_UNIT, SiLU(c) / sqrt(||SiLU(c)||^2 + eps_feat);
+ *         or, with IDATTN_FEATURE_RFF, [cos(Omega^T c), sin(Omega^T c)]/sqrt(d/2))
  *   z_k = g_k * xi_k / sqrt(mean(xi_k^2) + eps_norm) + b_k  (RMSNorm, key half)
  *   z_v = g_v * v    / sqrt(mean(v^2)    + eps_norm) + b_v  (RMSNorm, value half)
  *   abar_m = exp(Delta lambda_m), bbar_m = (abar_m - 1)/lambda_m * B_m,
@@ -75,12 +76,21 @@ typedef enum idattn_algo {
                                     fp32 accumulation and state; bf16 I/O only           */
 } idattn_algo;
 
-/* Norm of the feature map.  The gist.science summaries print the squared
- * norm; the Chinese rendering, section 1, names the feature map "SiLU/l_2",
- * whose plain reading is the unit-norm map. */
+/* The feature map xi applied to the conv outputs c of queries and keys
+ * (y = SiLU(c)).  The gist.science summaries print the squared norm; the
+ * Chinese rendering, section 1, names the feature map "SiLU/l_2", whose plain
+ * reading is the unit-norm map.  Its section 3.1 (eqs. 5 and 6) gives random
+ * Fourier features of a stationary kernel: here D = d/2 frequencies per head,
+ * the columns of Omega_h = params->rff_omega[h], shared by queries and keys,
+ * with the cosine half first and a 1/sqrt(D) factor so that xi(x) . xi(x') is
+ * the mean of cos(w^T (x - x')) over the D frequencies.  The caller draws the
+ * frequencies; eps_feat is unused with it.  The chunked algorithm has no
+ * kernel for IDATTN_FEATURE_RFF (IDATTN_ERR_UNSUPPORTED; AUTO picks the
+ * sequential one). */
 typedef enum idattn_feature_norm {
     IDATTN_FEATURE_SQUARED = 0,  /* xi = y / (||y||^2 + eps_feat)        (default) */
-    IDATTN_FEATURE_UNIT = 1      /* xi = y / sqrt(||y||^2 + eps_feat)              */
+    IDATTN_FEATURE_UNIT = 1,     /* xi = y / sqrt(||y||^2 + eps_feat)              */
+    IDATTN_FEATURE_RFF = 2       /* xi = [cos(Omega^T c), sin(Omega^T c)] / sqrt(d/2) */
 } idattn_feature_norm;
 
 /* Sizes.  R == d.  Layout of q, k, v, o: contiguous [B][N][H][d]. */
@@ -107,6 +117,9 @@ typedef struct idattn_params {
     const float *log_dt;  /* [H]: Delta_h = exp(log_dt[h])                    */
     const float *A;       /* [H][M][2]: lambda (re, im), Re < 0               */
     const float *Bc;      /* [H][M][2]: B (re, im)                            */
+    const float *rff_omega; /* [H][d][d/2]: Omega_h, column f = frequency w_f;
+                               read only with IDATTN_FEATURE_RFF (then
+                               non-NULL), else ignored and may be NULL        */
 } idattn_params;
 
 /*

@@ -53,6 +53,7 @@ static idattn_params params() {
     p.log_dt = static_cast<const float*>(fake(24));
     p.A = static_cast<const float*>(fake(25));
     p.Bc = static_cast<const float*>(fake(26));
+    p.rff_omega = static_cast<const float*>(fake(27));
     return p;
 }
 
@@ -120,8 +121,14 @@ int main() {
         y.eps_feat = -1.f;
         expect(forward(y, p, 1ull << 40), IDATTN_ERR_ARG, "eps_feat < 0");
         y = x;
-        y.feature_norm = 2;
+        y.feature_norm = 3;
         expect(forward(y, p, 1ull << 40), IDATTN_ERR_ARG, "feature_norm");
+        y = x;
+        y.feature_norm = IDATTN_FEATURE_RFF;
+        idattn_params r = p;
+        r.rff_omega = nullptr;
+        expect(forward(y, r, 1ull << 40), IDATTN_ERR_NULL, "NULL rff_omega");
+        expect(forward(y, p, 1ull << 40, fake(27, 64)), IDATTN_ERR_ALIAS, "o over rff_omega");
         y = x;
         y.N = int64_t{1} << 50;
         expect(forward(y, p, 1ull << 40), IDATTN_ERR_SHAPE, "N too large");

@@ -40,9 +40,9 @@ def test_struct_layout_matches_header():
     #include <stddef.h>
     #include "idattn.h"
     int main(void) {
-      printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(idattn_dims), offsetof(idattn_dims, io_dtype),
+      printf("%zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(idattn_dims), offsetof(idattn_dims, io_dtype),
              offsetof(idattn_dims, eps_norm), offsetof(idattn_dims, feature_norm), sizeof(idattn_params),
-             offsetof(idattn_params, log_dt), offsetof(idattn_params, Bc));
+             offsetof(idattn_params, log_dt), offsetof(idattn_params, Bc), offsetof(idattn_params, rff_omega));
       return 0;
     }"""
     with tempfile.TemporaryDirectory() as td:
@@ -53,7 +53,7 @@ def test_struct_layout_matches_header():
         got = list(map(int, subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()))
     want = [ctypes.sizeof(IdattnDims), IdattnDims.io_dtype.offset, IdattnDims.eps_norm.offset,
             IdattnDims.feature_norm.offset, ctypes.sizeof(IdattnParams), IdattnParams.log_dt.offset,
-            IdattnParams.Bc.offset]
+            IdattnParams.Bc.offset, IdattnParams.rff_omega.offset]
     assert got == want
 
 
@@ -70,10 +70,13 @@ def dims(**kw):
     return fs.make_dims(**base)
 
 
+PKEYS = ("conv_q", "conv_k", "gain", "bias", "log_dt", "A", "Bc", "rff_omega")
+
+
 def params(**kw):
-    vals = {k: FAKE + 0x1000000 * (i + 1) for i, k in enumerate(("conv_q", "conv_k", "gain", "bias", "log_dt", "A", "Bc"))}
+    vals = {k: FAKE + 0x1000000 * (i + 1) for i, k in enumerate(PKEYS)}
     vals.update(kw)
-    return IdattnParams(*(vals[k] for k in ("conv_q", "conv_k", "gain", "bias", "log_dt", "A", "Bc")))
+    return IdattnParams(*(vals[k] for k in PKEYS))
 
 
 QB = 0x200000000  # q, k, v, o, ... spaced far apart
@@ -103,7 +106,7 @@ def expect(status, name):
     ("M", 8, "IDATTN_ERR_UNSUPPORTED"), ("M", 128, "IDATTN_ERR_UNSUPPORTED"), ("W", 9, "IDATTN_ERR_UNSUPPORTED"),
     ("io", 7, "IDATTN_ERR_ARG"), ("algo", 9, "IDATTN_ERR_ARG"), ("eps_feat", -1.0, "IDATTN_ERR_ARG"),
     ("eps_norm", float("nan"), "IDATTN_ERR_ARG"), ("eps_norm", float("inf"), "IDATTN_ERR_ARG"),
-    ("feature_norm", 2, "IDATTN_ERR_ARG"), ("feature_norm", -1, "IDATTN_ERR_ARG"),
+    ("feature_norm", 3, "IDATTN_ERR_ARG"), ("feature_norm", -1, "IDATTN_ERR_ARG"),
 ])
 def test_forward_rejects_bad_dims(field, value, name):
     d = dims(**{field: value})
@@ -183,3 +186,34 @@ def test_decode_validation():
     expect(dec(dims(N=1), o=QB + 16), "IDATTN_ERR_ALIAS")
     expect(dec(dims(N=1), s=5 * QB + 4), "IDATTN_ERR_ARG")
     expect(dec(dims(N=1, d=100)), "IDATTN_ERR_UNSUPPORTED")
+
+
+def test_rff_feature_map_validation():
+    """The RFF map needs its frequencies, has no chunked kernel (AUTO takes the
+    sequential path), and its frequency table counts as a parameter for the
+    overlap checks.  Without the flag the table is not looked at: a NULL
+    rff_omega passes on to the next check (here a short workspace)."""
+    d = dims(feature_norm="rff", M=64, d=128)
+    expect(call_forward(d, params(rff_omega=0)), "IDATTN_ERR_NULL")
+    expect(call_forward(dims(M=64, d=128), params(rff_omega=0), ws_bytes=1), "IDATTN_ERR_WORKSPACE")
+    with pytest.raises(fs.IdattnError) as e:
+        fs.idattn_forward_workspace_size(dims(feature_norm="rff", M=64, d=128, algo="chunked"))
+    assert e.value.status_name == "IDATTN_ERR_UNSUPPORTED"
+    assert fs.idattn_forward_workspace_size(d) == fs.idattn_forward_workspace_size(
+        dims(feature_norm="rff", M=64, d=128, algo="sequential"))
+    om = params().rff_omega
+    table = 3 * 128 * 64 * 4  # H d (d/2) floats
+    expect(call_forward(d, params(), o=om + table - 16), "IDATTN_ERR_ALIAS")   # o over the table's end
+    expect(call_forward(d, params(), so=om), "IDATTN_ERR_ALIAS")               # state_out over the table
+
+
+def test_decode_outputs_must_not_overlap_parameters():
+    lib = fs.load_library()
+    p = params()
+    d = dims(N=1, feature_norm="rff", M=64, d=128)
+    a = dict(q=QB, k=2 * QB, v=3 * QB, o=4 * QB, s=5 * QB, t=6 * QB)
+    for key, where in (("o", p.gain), ("s", p.rff_omega), ("t", p.A)):
+        b = dict(a)
+        b[key] = where
+        expect(lib.idattn_decode_step(ctypes.byref(d), ctypes.byref(p), b["q"], b["k"], b["v"], b["o"], b["s"],
+                                      b["t"], None), "IDATTN_ERR_ALIAS")

@@ -146,6 +146,61 @@ def test_decode_step_unit_feature_map(fs, io):
     assert np.array_equal(down(tl), tl_ref.astype(np.float32))
 
 
+# Random Fourier features (Chinese rendering, section 3.1, eq. 6): the
+# sequential path of every d (D = d/2 = 8 .. 64 frequencies) from a given state
+# and tail; AUTO must take the sequential path for bf16 as well, since the
+# chunked kernels have no RFF map.  Phases are of order 2 (up to about 10).
+RFF = ["tiny_f32", "d16_m64_w2_f32", "d32_m16_bf16", "d64_m32_ragged_bf16", "d64_m64_ragged_f32",
+       "d128_m64_ragged_bf16", "d128_m16_f32", "d128_w8_bf16"]
+
+
+@pytest.mark.parametrize("name", RFF)
+def test_forward_rff_feature_map(fs, name):
+    base, over, tag = SMALL[name]
+    c = WL.make_case(base, seed=1, tag=tag, **over)
+    s = c.spec
+    io = s["io"]
+    params = dict(c.params, rff_omega=WL.make_rff_omega(s, seed=5))
+    st0, tl0 = WL.make_decode_state(s, seed=2)
+    o_ref, st_ref, tl_ref = oracle.forward(c.q, c.k, c.v, params, state_in=st0, tail_in=tl0, feature_norm="rff")
+    p = fs.params_to_device(params)
+    for algo in ("sequential", "auto"):
+        o, st, tl = fs.forward(up(c.q, io), up(c.k, io), up(c.v, io), p, return_state=True, algo=algo,
+                               state_in=state_dev(st0), tail_in=up(tl0, io), feature_norm="rff")
+        _sync()
+        e_o = rel_l2(down(o), o_ref)
+        e_s = rel_l2(state_np(st), st_ref)
+        print(f"rff {name} {algo}: o relL2 {e_o:.2e}, state relL2 {e_s:.2e}")
+        assert e_o <= gate(io), (algo, e_o)
+        assert e_s <= gate(io), (algo, e_s)
+        assert np.array_equal(down(tl), tl_ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("n_tok", [1, 3])
+@pytest.mark.parametrize("name", ["d128_m64_ragged_bf16", "d32_m16_bf16"])
+def test_decode_step_rff(fs, io, n_tok, name):
+    """One and three tokens per call against the oracle's forward over those
+    tokens from the same state and tail (the RFF instances of the decode kernel)."""
+    base, over, tag = SMALL[name]
+    c = WL.make_case(base, seed=3, tag=tag, **dict(over, io=io))
+    s = c.spec
+    params = dict(c.params, rff_omega=WL.make_rff_omega(s, seed=6))
+    st0, tl0 = WL.make_decode_state(s, seed=4)
+    q, k, v = (x[:, :n_tok] for x in (c.q, c.k, c.v))
+    o_ref, st_ref, tl_ref = oracle.forward(q, k, v, params, state_in=st0, tail_in=tl0, feature_norm="rff")
+    p = fs.params_to_device(params)
+    st = state_dev(st0)
+    tl = up(tl0, io)
+    ot = fs.decode_step(up(q, io), up(k, io), up(v, io), p, st, tl, feature_norm="rff")
+    _sync()
+    e_o = rel_l2(down(ot), o_ref)
+    e_s = rel_l2(state_np(st), st_ref)
+    print(f"rff decode {name} {io} n={n_tok}: o relL2 {e_o:.2e}, state relL2 {e_s:.2e}")
+    assert e_o <= gate(io) and e_s <= gate(io), (e_o, e_s)
+    assert np.array_equal(down(tl), tl_ref.astype(np.float32))
+
+
 # Learned decays can be much faster than the S4D-Lin init: Delta |Re lambda| up
 # to 6 per token.  A ragged last chunk must still leave an exact end state
 # (before the fix, a zero-padded chunk corrected by abar^-(L-n) lost the state:

@@ -6,8 +6,8 @@ can both consume it without sharing any part of the method.
 """
 from .configs import (CONFIGS, Case, bf16_bits, bf16_from_bits, bf16_round,
                       make_case, make_decode_state, make_decode_token,
-                      make_params, make_rows, spec)
+                      make_params, make_rff_omega, make_rows, spec)
 
 __all__ = ["CONFIGS", "Case", "bf16_bits", "bf16_from_bits", "bf16_round",
            "make_case", "make_decode_state", "make_decode_token",
-           "make_params", "make_rows", "spec"]
+           "make_params", "make_rff_omega", "make_rows", "spec"]

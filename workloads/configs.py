@@ -40,7 +40,7 @@ CONFIGS = {
     "decode": dict(tag=4, B=256, H=16, N=2048, d=128, M=64, W=4, io="bf16"),
 }
 
-KIND_PARAMS, KIND_ROW, KIND_DECODE_TOKEN, KIND_DECODE_STATE = 0, 1, 2, 3
+KIND_PARAMS, KIND_ROW, KIND_DECODE_TOKEN, KIND_DECODE_STATE, KIND_RFF = 0, 1, 2, 3, 4
 
 
 def spec(name_or_spec, **overrides) -> dict:
@@ -134,6 +134,17 @@ def make_params(s: dict, seed: int = 0) -> dict:
     Bc[:, :, 0] = 1.0
     return dict(conv_q=conv_q, conv_k=conv_k, gain=gain, bias=bias,
                 log_dt=log_dt, A=A, Bc=Bc)
+
+
+def make_rff_omega(s: dict, seed: int = 0, sigma: float | None = None) -> np.ndarray:
+    """Frequencies for the random-Fourier-feature map, float32 [H, d, d/2]:
+    i.i.d. N(0, 1/sigma^2) entries (the spectral density of a Gaussian kernel
+    of length scale sigma), sigma = sqrt(d)/2 by default so that with unit
+    normal inputs the phases are of order 2."""
+    H, d = s["H"], s["d"]
+    sigma = math.sqrt(d) / 2 if sigma is None else sigma
+    g = _rng(seed, s["tag"], KIND_RFF)
+    return (g.standard_normal((H, d, d // 2)) / sigma).astype(np.float32)
 
 
 # ---------------------------------------------------------------- activations
