@@ -55,6 +55,10 @@ Parity pins (tests/test_oracle_pins.py):
                of o, M=1 real-EMA limit via scipy.signal.lfilter, Delta -> 0
                limit, causality, row/head independence, split-sequence resume.
   decode_step  pinned: equals the next position of a longer forward.
+  forward_varlen  pinned: equal lengths give the batched forward; an empty
+               sequence passes its state and tail through; a sequence split
+               into two packed pieces, the second resumed from the first's
+               state and tail, gives the unsplit result.
   Parity unpinned (fixed by reading only, no printed value exists): the
   complex-product convention, eps_feat and eps_norm values, the conv tap
   order, and the gain/bias shapes.
@@ -261,6 +265,41 @@ def forward(q, k, v, params, eps_feat=1e-6, eps_norm=1e-6,
     inter = dict(c_q=c_q, c_k=c_k, xi_q=xi_q, xi_k=xi_k, z_k=z_k, z_v=z_v,
                  abar=abar, bbar=bbar, s=s_all)
     return o, state_out, tail_out, inter
+
+
+def forward_varlen(q, k, v, cu_seqlens, params, eps_feat=1e-6, eps_norm=1e-6,
+                   state_in=None, tail_in=None, feature_norm="squared"):
+    """Packed variable-length batch: B independent sequences laid end to end.
+    Sequence b is tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of the packed
+    q, k, v [T, H, d]; it starts from state_in[b] and tail_in[b] (zeros when
+    None) and its conv never reaches into a neighbouring sequence.  This is
+    the forward above applied to each sequence on its own; a fixed-size state
+    per sequence is what lets a server pack prompts of different lengths (p1
+    section 1; the serving use of the fixed state).
+
+    Returns (o [T, H, d], state_out [B, H, M, 2d], tail_out [B, H, 2, W-1, d])."""
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    cu = [int(x) for x in cu_seqlens]
+    B = len(cu) - 1
+    T, H, d = q.shape
+    if cu[0] != 0 or cu[-1] != T or any(cu[b + 1] < cu[b] for b in range(B)):
+        raise ValueError("cu_seqlens must rise from 0 to T")
+    W = params["conv_q"].shape[-1]
+    M = params["A"].shape[1]
+    o = np.empty((T, H, d), dtype=F64)
+    state_out = np.empty((B, H, M, 2 * d), dtype=C128)
+    tail_out = np.empty((B, H, 2, W - 1, d), dtype=F64)
+    for b in range(B):
+        sl = slice(cu[b], cu[b + 1])
+        st = None if state_in is None else np.asarray(state_in)[b:b + 1]
+        tl = None if tail_in is None else np.asarray(tail_in)[b:b + 1]
+        ob, state_out[b:b + 1], tail_out[b:b + 1] = forward(q[None, sl], k[None, sl], v[None, sl], params,
+                                                            eps_feat, eps_norm, state_in=st, tail_in=tl,
+                                                            feature_norm=feature_norm)
+        o[sl] = ob[0]
+    return o, state_out, tail_out
 
 
 def decode_step(q_t, k_t, v_t, state, tail, params, eps_feat=1e-6, eps_norm=1e-6, feature_norm="squared"):

@@ -396,6 +396,46 @@ def pin_independence(O) -> float:
     return max(rel(o_row, o[1:2]), rel(o_head, o[:, :, 2:3]))
 
 
+def pin_varlen(O) -> float:
+    """Packed variable-length batches: (a) equal lengths equal the batched
+    forward of the same rows; (b) a zero-length sequence returns its state and
+    tail unchanged; (c) one row cut into two packed pieces, the second
+    resumed from the first's end state and tail, equals the row in one piece;
+    (d) no output leaks between neighbouring sequences (changing one
+    sequence's tokens leaves the others' outputs bit-identical)."""
+    c = pin_case(with_state=True)
+    p = c["p"]
+    B, N, H, d = c["q"].shape
+    st, tl = c["state"], c["tail"]
+    o, so, to = O.forward(c["q"], c["k"], c["v"], p, state_in=st, tail_in=tl)
+    pack = lambda x: x.reshape(B * N, H, d)
+    cu = [b * N for b in range(B + 1)]
+    ov, sv, tv = O.forward_varlen(pack(c["q"]), pack(c["k"]), pack(c["v"]), cu, p, state_in=st, tail_in=tl)
+    errs = [rel(ov.reshape(B, N, H, d), o), rel(sv, so), rel(tv, to)]
+    # (b) empty first sequence, then row 0 whole
+    cu2 = [0, 0, N]
+    st2 = np.concatenate([st[1:2], st[0:1]])
+    tl2 = np.concatenate([tl[1:2], tl[0:1]])
+    o2, s2, t2 = O.forward_varlen(c["q"][0], c["k"][0], c["v"][0], cu2, p, state_in=st2, tail_in=tl2)
+    errs += [rel(s2[0], st[1]), rel(t2[0], tl[1]), rel(o2, o[0]), rel(s2[1], so[0])]
+    # (c) row 0 cut at n1 into two sequences of one packed batch: the second piece
+    # resumes from the first's end state and tail
+    n1 = 13
+    a_o, a_s, a_t = O.forward_varlen(c["q"][0, :n1], c["k"][0, :n1], c["v"][0, :n1], [0, n1], p,
+                                     state_in=st[:1], tail_in=tl[:1])
+    cu3 = [0, n1, N]
+    st3 = np.concatenate([st[:1], a_s])
+    tl3 = np.concatenate([tl[:1], a_t])
+    o3, s3, t3 = O.forward_varlen(c["q"][0], c["k"][0], c["v"][0], cu3, p, state_in=st3, tail_in=tl3)
+    errs += [rel(o3, o[0]), rel(s3[1], so[0]), rel(t3[1], to[0])]
+    # (d) isolation
+    q4 = pack(c["q"]).copy()
+    q4[N:] += 1.0
+    o4, _, _ = O.forward_varlen(q4, pack(c["k"]), pack(c["v"]), cu, p, state_in=st, tail_in=tl)
+    errs.append(float(np.abs(o4[:N] - ov[:N]).max()))
+    return max(errs)
+
+
 PINS = {
     "conv": (pin_conv, 1e-13),
     "silu": (pin_silu, 1e-14),
@@ -416,5 +456,6 @@ PINS = {
     "causality": (pin_causality, 0.0),
     "split_resume": (pin_split_resume, 1e-12),
     "decode": (pin_decode, 1e-12),
+    "varlen": (pin_varlen, 1e-12),
     "independence": (pin_independence, 1e-13),
 }

@@ -69,6 +69,29 @@ def _rff_half_frequency(c, omega):
     return _orig["feature_map_rff"](c, 0.5 * np.asarray(omega))
 
 
+def _varlen_first_tail(q, k, v, cu, params, eps_feat=1e-6, eps_norm=1e-6, state_in=None, tail_in=None,
+                       feature_norm="squared"):
+    # every sequence takes sequence 0's conv history
+    if tail_in is not None:
+        tail_in = np.repeat(np.asarray(tail_in)[:1], len(cu) - 1, axis=0)
+    return _orig["forward_varlen"](q, k, v, cu, params, eps_feat, eps_norm, state_in, tail_in, feature_norm)
+
+
+def _varlen_conv_leaks(q, k, v, cu, params, eps_feat=1e-6, eps_norm=1e-6, state_in=None, tail_in=None,
+                       feature_norm="squared"):
+    # the conv of each sequence reads the raw tokens before it in the packed batch
+    q, k = np.asarray(q, float), np.asarray(k, float)
+    W = params["conv_q"].shape[-1]
+    tail = None if tail_in is None else np.array(tail_in, float)
+    for b in range(1, len(cu) - 1):
+        for j in range(W - 1):
+            t = cu[b] - (W - 1) + j
+            if t >= 0 and tail is not None:
+                tail[b, :, 0, j] = q[t]
+                tail[b, :, 1, j] = k[t]
+    return _orig["forward_varlen"](q, k, v, cu, params, eps_feat, eps_norm, state_in, tail, feature_norm)
+
+
 def _rms_sum(x, g, b, eps):
     x = np.asarray(x, float)
     return np.asarray(g)[None, None] * x / np.sqrt((x * x).sum(-1, keepdims=True) + eps) + np.asarray(b)[None, None]
@@ -118,7 +141,7 @@ def _step_imag_dropped(U, G, xq, zk, zv, a, b):
 
 
 _orig = {name: getattr(O, name) for name in ("short_conv", "silu", "feature_map", "feature_map_unit", "feature_map_rff",
-                                             "rms_norm",
+                                             "rms_norm", "forward_varlen",
                                              "zoh", "ssm_step")}
 
 MUTANTS = {
@@ -132,6 +155,8 @@ MUTANTS = {
     "rff_of_silu": ("feature_map_rff", _rff_of_silu),
     "rff_unscaled": ("feature_map_rff", _rff_unscaled),
     "rff_half_frequency": ("feature_map_rff", _rff_half_frequency),
+    "varlen_first_tail_for_all": ("forward_varlen", _varlen_first_tail),
+    "varlen_conv_crosses_sequences": ("forward_varlen", _varlen_conv_leaks),
     "rms_sum_not_mean": ("rms_norm", _rms_sum),
     "rms_dropped_bias": ("rms_norm", _rms_no_bias),
     "zoh_euler_bbar": ("zoh", _zoh_euler),
