@@ -182,6 +182,47 @@ def decode_bench(torch, fs, steps, warmup):
                          "algorithmic_bytes": nbytes}}
 
 
+def varlen_bench(torch, fs, WL, steps=20, warmup=5):
+    """Packed variable-length batch at the 1.3B head shape (H=16, d=128, M=64,
+    W=4, bf16): 16 384 tokens in 8 sequences of mixed lengths (long prompts
+    beside short ones), on the sequential path, which is the one that takes
+    packed batches."""
+    import numpy as np
+    lens = [6000, 3500, 2500, 2048, 1200, 700, 400, 36]
+    s = WL.spec("1p3b", B=1, N=sum(lens), tag=90)
+    q, k, v = WL.make_rows(s)
+    p = fs.params_to_device(WL.make_params(s))
+    prm = fs.make_params(p)
+    B, T, H, d, M, W = len(lens), sum(lens), s["H"], s["d"], s["M"], s["W"]
+
+    def up(x):
+        return torch.from_numpy(WL.bf16_bits(x[0]).view(np.int16)).view(torch.bfloat16).cuda()
+
+    qd, kd, vd = up(q), up(k), up(v)
+    o = torch.empty_like(qd)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+    state = torch.zeros((B, H, M, 2 * d, 2), dtype=torch.float32, device="cuda")
+    tail = torch.zeros((B, H, 2, W - 1, d), dtype=torch.bfloat16, device="cuda")
+    dims = fs.make_dims(B, T, H, d, M, W, "bf16", "auto")
+    nbytes = fs.idattn_forward_varlen_workspace_size(dims)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+
+    def call():
+        fs.idattn_forward_varlen(dims, prm, cu, qd, kd, vd, o, None, None, state, tail, ws, nbytes)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    return {"workload": f"packed batch: {B} sequences, lengths {lens} (T={T}), H={H} d=R={d} M={M} W={W}, "
+                        f"bf16 I/O, sequential fp32 path",
+            "ms_per_call": dt * 1e3, "tokens_per_s": T / dt}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -283,6 +324,7 @@ def main():
     out["measured_copy_gbps"] = measure_copy_gbps(torch)
     if not args.no_decode:
         out["decode"] = decode_bench(torch, fs, steps=20, warmup=20)
+        out["varlen"] = varlen_bench(torch, fs, WL)
     del sets, ws
     torch.cuda.empty_cache()
     if not args.no_cpu:

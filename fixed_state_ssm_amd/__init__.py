@@ -2,21 +2,23 @@
 
 The work runs in libidattn.so (HIP kernels behind a C ABI, include/idattn.h).
 This package holds the ctypes binding (functions named like the C entry
-points) and two conveniences, forward() and decode_step(), that allocate
-outputs and workspace with PyTorch and call the binding on the current
-stream.
+points) and three conveniences, forward(), forward_varlen() and
+decode_step(), that allocate outputs and workspace with PyTorch and call the
+binding on the current stream.
 """
 from __future__ import annotations
 
 from .binding import (ALGO, EXPORTS, FEATURE_NORM, IO, LIB_PATH, STATUS, IdattnDims, IdattnError, IdattnParams,
-                      idattn_decode_step, idattn_forward, idattn_forward_workspace_size,
+                      idattn_decode_step, idattn_forward, idattn_forward_varlen,
+                      idattn_forward_varlen_workspace_size, idattn_forward_workspace_size,
                       idattn_last_error, idattn_status_string, idattn_version, load_library,
                       make_dims, make_params)
 
 __all__ = ["ALGO", "EXPORTS", "FEATURE_NORM", "IO", "LIB_PATH", "STATUS", "IdattnDims", "IdattnError", "IdattnParams",
-           "idattn_decode_step", "idattn_forward", "idattn_forward_workspace_size",
+           "idattn_decode_step", "idattn_forward", "idattn_forward_varlen", "idattn_forward_varlen_workspace_size",
+           "idattn_forward_workspace_size",
            "idattn_last_error", "idattn_status_string", "idattn_version", "load_library",
-           "make_dims", "make_params", "forward", "decode_step", "params_to_device"]
+           "make_dims", "make_params", "forward", "forward_varlen", "decode_step", "params_to_device"]
 
 PARAM_KEYS = ("conv_q", "conv_k", "gain", "bias", "log_dt", "A", "Bc")
 
@@ -63,6 +65,36 @@ def forward(q, k, v, params: dict, *, state_in=None, tail_in=None, return_state=
         tail_out = torch.empty((B, H, 2, W - 1, d), dtype=q.dtype, device=q.device)
     idattn_forward(dims, make_params(params), q, k, v, o, state_in, tail_in, state_out, tail_out,
                    ws, nbytes, stream)
+    return (o, state_out, tail_out) if return_state else o
+
+
+def forward_varlen(q, k, v, params: dict, cu_seqlens, *, state_in=None, tail_in=None, return_state=False,
+                   algo="auto", eps_feat=1e-6, eps_norm=1e-6, feature_norm="squared", stream=None):
+    """o = mixer over a packed batch: q, k, v [T, H, d] on the GPU hold B
+    sequences end to end, sequence b being tokens cu_seqlens[b] ..
+    cu_seqlens[b+1]-1 (cu_seqlens: int32 device tensor [B + 1]).  state_in
+    [B, H, M, 2d, 2] and tail_in [B, H, 2, W-1, d] or None.  With
+    return_state=True returns (o, state_out, tail_out)."""
+    import torch
+    T, H, d = q.shape
+    B = cu_seqlens.shape[0] - 1
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    M = params["A"].shape[1]
+    W = params["conv_q"].shape[-1]
+    for t in (k, v):
+        if t.dtype != q.dtype or t.shape != q.shape:
+            raise ValueError("q, k, v must share shape and dtype")
+    dims = make_dims(B, T, H, d, M, W, _io_name(q), algo, eps_feat, eps_norm, feature_norm)
+    nbytes = idattn_forward_varlen_workspace_size(dims)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    state_out = tail_out = None
+    if return_state:
+        state_out = torch.empty((B, H, M, 2 * d, 2), dtype=torch.float32, device=q.device)
+        tail_out = torch.empty((B, H, 2, W - 1, d), dtype=q.dtype, device=q.device)
+    idattn_forward_varlen(dims, make_params(params), cu_seqlens, q, k, v, o, state_in, tail_in, state_out, tail_out,
+                          ws, nbytes, stream)
     return (o, state_out, tail_out) if return_state else o
 
 

@@ -117,6 +117,8 @@ idattn::Problem problem(const idattn_dims& D) {
     p.eps_norm = D.eps_norm;
     p.unit_feat = D.feature_norm == IDATTN_FEATURE_UNIT;
     p.rff_feat = D.feature_norm == IDATTN_FEATURE_RFF;
+    p.T = D.B * D.N;
+    p.cu = nullptr;
     return p;
 }
 
@@ -126,9 +128,10 @@ int resolve_algo(const idattn_dims& D) {
                                                                                  : IDATTN_ALGO_SEQUENTIAL;
 }
 
-size_t seq_workspace_bytes(const idattn_dims& D) {
-    // xi_q, z_k, z_v: float [B][H][N][d]; s: complex float [B][H][N][M]
-    const size_t tok = static_cast<size_t>(D.B) * D.H * D.N;
+// tokens on the [T] axis: B N for the dense entry point, N for the packed one
+size_t seq_workspace_bytes(const idattn_dims& D, int64_t T) {
+    // xi_q, z_k, z_v: float [H][T][d]; s: complex float [H][T][M]
+    const size_t tok = static_cast<size_t>(D.H) * T;
     const size_t a = 3 * tok * D.d * sizeof(float);
     const size_t s = tok * D.M * 2 * sizeof(float);
     return ((a + 255) / 256) * 256 + s;
@@ -149,7 +152,82 @@ idattn_status workspace_bytes(const idattn_dims& D, int algo, size_t* bytes) {
                         (long long)D.d, (long long)D.M);
         *bytes = idattn::chunked_workspace_bytes(p);
     } else {
-        *bytes = seq_workspace_bytes(D);
+        *bytes = seq_workspace_bytes(D, D.B * D.N);
+    }
+    return IDATTN_OK;
+}
+
+// The sequential path: feature kernel, key scan, value scan with readout, tail.
+idattn_status run_sequential(const idattn::Problem& p, const idattn_params& prm, const void* q, const void* k,
+                             const void* v, void* o, const float* state_in, const void* tail_in, float* state_out,
+                             void* tail_out, void* workspace, hipStream_t s) {
+    const size_t tok = static_cast<size_t>(p.H) * p.T;
+    float* xi_q = static_cast<float*>(workspace);
+    float* z_k = xi_q + tok * p.d;
+    float* z_v = z_k + tok * p.d;
+    float* sbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           ((3 * tok * p.d * sizeof(float) + 255) / 256) * 256);
+    hipError_t e = idattn::launch_featmap_conv_norm(p, prm, q, k, v, tail_in, xi_q, z_k, z_v, s);
+    if (e != hipSuccess) return hip_fail(e, "featmap_conv_norm");
+    e = idattn::launch_ssm_key_scan_seq(p, prm, xi_q, z_k, state_in, sbuf, state_out, s);
+    if (e != hipSuccess) return hip_fail(e, "ssm_key_scan");
+    e = idattn::launch_ssm_value_scan_readout_seq(p, prm, sbuf, z_v, state_in, o, state_out, s);
+    if (e != hipSuccess) return hip_fail(e, "ssm_value_scan_readout");
+    if (tail_out) {
+        e = idattn::launch_tail_update(p, q, k, tail_in, tail_out, s);
+        if (e != hipSuccess) return hip_fail(e, "tail update");
+    }
+    return IDATTN_OK;
+}
+
+// Buffer checks shared by both forward entry points: alignment, overlaps
+// between the outputs and every other buffer (exact in-place state and tail
+// allowed), and between the outputs and the parameters.  act = bytes of q
+// (and of k, v, o); extra = one more read-only buffer (or an empty range).
+idattn_status check_forward_buffers(const idattn_dims& D, const idattn_params& P, const void* q, const void* k,
+                                    const void* v, void* o, const float* state_in, const void* tail_in,
+                                    float* state_out, void* tail_out, void* workspace, size_t need, size_t act,
+                                    const Range& extra) {
+    const void* ptrs[] = {q, k, v, o, state_in, tail_in, state_out, tail_out, workspace};
+    for (const void* ptr : ptrs)
+        if (misaligned(ptr)) return fail(IDATTN_ERR_ARG, "device buffers must be 16-byte aligned");
+    const size_t io = D.io_dtype == IDATTN_IO_BF16 ? 2 : 4;
+    const size_t stb = static_cast<size_t>(D.B) * D.H * D.M * 2 * D.d * 2 * sizeof(float);
+    const size_t tlb = static_cast<size_t>(D.B) * D.H * 2 * (D.W - 1) * D.d * io;
+    const Range rq = range("q", q, act), rk = range("k", k, act), rv = range("v", v, act);
+    const Range ro = range("o", o, act);
+    const Range rsi = range("state_in", state_in, stb), rso = range("state_out", state_out, stb);
+    const Range rti = range("tail_in", tail_in, tlb), rto = range("tail_out", tail_out, tlb);
+    const Range rws = range("workspace", workspace, need);
+    const Range outs[] = {ro, rso, rto, rws};
+    const Range all[] = {rq, rk, rv, ro, rsi, rso, rti, rto, rws, extra};
+    for (const Range& a : outs)
+        for (const Range& b : all) {
+            if (&a == &b || a.name == b.name) continue;
+            if (!overlap(a, b)) continue;
+            // exact in-place pairs are allowed
+            if ((a.name == rso.name && b.name == rsi.name) || (a.name == rto.name && b.name == rti.name)) {
+                if (a.lo == b.lo) continue;
+            }
+            return fail(IDATTN_ERR_ALIAS, "%s overlaps %s", a.name, b.name);
+        }
+    return check_params_disjoint(D, P, outs, 4);
+}
+
+// N = 0: copy state_in / tail_in to the outputs (zeros when not given).
+idattn_status copy_through(const idattn_dims& D, const float* state_in, const void* tail_in, float* state_out,
+                           void* tail_out, hipStream_t s) {
+    const size_t io = D.io_dtype == IDATTN_IO_BF16 ? 2 : 4;
+    const size_t stb = static_cast<size_t>(D.B) * D.H * D.M * 2 * D.d * 2 * sizeof(float);
+    const size_t tlb = static_cast<size_t>(D.B) * D.H * 2 * (D.W - 1) * D.d * io;
+    hipError_t e;
+    if (state_out) {
+        e = idattn::launch_copy_or_zero(state_in, state_out, static_cast<int64_t>(stb / 4), s);
+        if (e != hipSuccess) return hip_fail(e, "state copy");
+    }
+    if (tail_out && tlb > 0) {
+        e = idattn::launch_copy_or_zero(tail_in, tail_out, static_cast<int64_t>(tlb / 4), s);
+        if (e != hipSuccess) return hip_fail(e, "tail copy");
     }
     return IDATTN_OK;
 }
@@ -206,75 +284,65 @@ idattn_status idattn_forward(const idattn_dims* dims, const idattn_params* param
     if (workspace_bytes_given < need)
         return fail(IDATTN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_given, need);
 
-    {
-        const void* ptrs[] = {q, k, v, o, state_in, tail_in, state_out, tail_out, workspace};
-        for (const void* ptr : ptrs)
-            if (misaligned(ptr)) return fail(IDATTN_ERR_ARG, "device buffers must be 16-byte aligned");
-    }
     const size_t io = D.io_dtype == IDATTN_IO_BF16 ? 2 : 4;
     const size_t act = static_cast<size_t>(D.B) * D.N * D.H * D.d * io;
-    const size_t stb = static_cast<size_t>(D.B) * D.H * D.M * 2 * D.d * 2 * sizeof(float);
-    const size_t tlb = static_cast<size_t>(D.B) * D.H * 2 * (D.W - 1) * D.d * io;
-    const Range rq = range("q", q, act), rk = range("k", k, act), rv = range("v", v, act);
-    const Range ro = range("o", o, act);
-    const Range rsi = range("state_in", state_in, stb), rso = range("state_out", state_out, stb);
-    const Range rti = range("tail_in", tail_in, tlb), rto = range("tail_out", tail_out, tlb);
-    const Range rws = range("workspace", workspace, need);
-    const Range outs[] = {ro, rso, rto, rws};
-    const Range all[] = {rq, rk, rv, ro, rsi, rso, rti, rto, rws};
-    for (const Range& a : outs)
-        for (const Range& b : all) {
-            if (&a == &b || a.name == b.name) continue;
-            if (!overlap(a, b)) continue;
-            // exact in-place pairs are allowed
-            if ((a.name == rso.name && b.name == rsi.name) || (a.name == rto.name && b.name == rti.name)) {
-                if (a.lo == b.lo) continue;
-            }
-            return fail(IDATTN_ERR_ALIAS, "%s overlaps %s", a.name, b.name);
-        }
-    st = check_params_disjoint(D, *params, outs, 4);
+    st = check_forward_buffers(D, *params, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, need, act,
+                               range("none", nullptr, 0));
     if (st != IDATTN_OK) return st;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const idattn::Problem p = problem(D);
-    hipError_t e;
-    if (D.N == 0) {
-        if (state_out) {
-            e = idattn::launch_copy_or_zero(state_in, state_out, static_cast<int64_t>(stb / 4), s);
-            if (e != hipSuccess) return hip_fail(e, "state copy");
-        }
-        if (tail_out && tlb > 0) {
-            e = idattn::launch_copy_or_zero(tail_in, tail_out, static_cast<int64_t>(tlb / 4), s);
-            if (e != hipSuccess) return hip_fail(e, "tail copy");
-        }
-        return IDATTN_OK;
-    }
-
+    if (D.N == 0) return copy_through(D, state_in, tail_in, state_out, tail_out, s);
     if (algo == IDATTN_ALGO_CHUNKED) {
-        e = idattn::launch_forward_chunked(p, *params, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace,
-                                           s);
+        const hipError_t e = idattn::launch_forward_chunked(p, *params, q, k, v, o, state_in, tail_in, state_out,
+                                                            tail_out, workspace, s);
         if (e != hipSuccess) return hip_fail(e, "chunked forward");
         return IDATTN_OK;  // the chunked forward writes tail_out itself
-    } else {
-        const size_t tok = static_cast<size_t>(D.B) * D.H * D.N;
-        float* ws = static_cast<float*>(workspace);
-        float* xi_q = ws;
-        float* z_k = xi_q + tok * D.d;
-        float* z_v = z_k + tok * D.d;
-        float* sbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                               ((3 * tok * D.d * sizeof(float) + 255) / 256) * 256);
-        e = idattn::launch_featmap_conv_norm(p, *params, q, k, v, tail_in, xi_q, z_k, z_v, s);
-        if (e != hipSuccess) return hip_fail(e, "featmap_conv_norm");
-        e = idattn::launch_ssm_key_scan_seq(p, *params, xi_q, z_k, state_in, sbuf, state_out, s);
-        if (e != hipSuccess) return hip_fail(e, "ssm_key_scan");
-        e = idattn::launch_ssm_value_scan_readout_seq(p, *params, sbuf, z_v, state_in, o, state_out, s);
-        if (e != hipSuccess) return hip_fail(e, "ssm_value_scan_readout");
     }
-    if (tail_out) {
-        e = idattn::launch_tail_update(p, q, k, tail_in, tail_out, s);
-        if (e != hipSuccess) return hip_fail(e, "tail update");
-    }
+    return run_sequential(p, *params, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, s);
+}
+
+idattn_status idattn_forward_varlen_workspace_size(const idattn_dims* dims, size_t* bytes) {
+    if (bytes == nullptr) return fail(IDATTN_ERR_NULL, "bytes is NULL");
+    idattn_status st = check_dims(dims, false);
+    if (st != IDATTN_OK) return st;
+    if (dims->algo == IDATTN_ALGO_CHUNKED)
+        return fail(IDATTN_ERR_UNSUPPORTED, "packed batches run on the sequential algorithm only");
+    *bytes = dims->N == 0 ? 0 : seq_workspace_bytes(*dims, dims->N);
     return IDATTN_OK;
+}
+
+idattn_status idattn_forward_varlen(const idattn_dims* dims, const idattn_params* params, const int32_t* cu_seqlens,
+                                    const void* q, const void* k, const void* v, void* o, const float* state_in,
+                                    const void* tail_in, float* state_out, void* tail_out, void* workspace,
+                                    size_t workspace_bytes_given, void* stream) {
+    idattn_status st = check_dims(dims, false);
+    if (st != IDATTN_OK) return st;
+    st = check_params(*dims, params);
+    if (st != IDATTN_OK) return st;
+    const idattn_dims& D = *dims;
+    if (D.algo == IDATTN_ALGO_CHUNKED)
+        return fail(IDATTN_ERR_UNSUPPORTED, "packed batches run on the sequential algorithm only");
+    if (D.N > 0x7fffffffLL) return fail(IDATTN_ERR_SHAPE, "N=%lld: a packed batch holds < 2^31 tokens", (long long)D.N);
+    if (cu_seqlens == nullptr) return fail(IDATTN_ERR_NULL, "cu_seqlens is NULL");
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return fail(IDATTN_ERR_ARG, "cu_seqlens must be 4-byte aligned");
+    if (D.N > 0 && (!q || !k || !v || !o)) return fail(IDATTN_ERR_NULL, "q, k, v and o must be non-NULL");
+    const size_t need = D.N == 0 ? 0 : seq_workspace_bytes(D, D.N);
+    if (need > 0 && workspace == nullptr) return fail(IDATTN_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+    if (workspace_bytes_given < need)
+        return fail(IDATTN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_given, need);
+    const size_t io = D.io_dtype == IDATTN_IO_BF16 ? 2 : 4;
+    const size_t act = static_cast<size_t>(D.N) * D.H * D.d * io;
+    st = check_forward_buffers(D, *params, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, need, act,
+                               range("cu_seqlens", cu_seqlens, static_cast<size_t>(D.B + 1) * 4));
+    if (st != IDATTN_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (D.N == 0) return copy_through(D, state_in, tail_in, state_out, tail_out, s);
+    idattn::Problem p = problem(D);
+    p.T = D.N;
+    p.cu = cu_seqlens;
+    return run_sequential(p, *params, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, s);
 }
 
 idattn_status idattn_decode_step(const idattn_dims* dims, const idattn_params* params, const void* q_t,

@@ -33,6 +33,37 @@ __device__ __forceinline__ void store_io(void* base, int64_t idx, float x) {
     else static_cast<float*>(base)[idx] = x;
 }
 
+// ------------------------------------------------------------------ sequences
+// Tokens [start, start + len) of sequence b on a token axis of T tokens: b N ..
+// b N + N - 1 when cu is NULL, else cu[b] .. cu[b+1] - 1 of a packed batch.
+// The packed bounds are clamped into [0, T], so that any contents of cu keep
+// every access in bounds (a malformed cu gives wrong results, never a fault).
+__device__ __forceinline__ void seq_range(const int32_t* cu, int64_t N, int64_t T, int64_t b, int64_t& start,
+                                          int64_t& len) {
+    if (cu == nullptr) {
+        start = b * N;
+        len = N;
+        return;
+    }
+    const int64_t s = min(max(static_cast<int64_t>(cu[b]), int64_t{0}), T);
+    const int64_t e = min(max(static_cast<int64_t>(cu[b + 1]), s), T);
+    start = s;
+    len = e - s;
+}
+
+// The sequence of token t: t / N, or the last b in [0, B) with cu[b] <= t
+// (binary search; ends in [0, B) whatever cu holds).
+__device__ __forceinline__ int64_t seq_of_token(const int32_t* cu, int64_t N, int64_t B, int64_t t) {
+    if (cu == nullptr) return t / N;
+    int64_t lo = 0, hi = B - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if (static_cast<int64_t>(cu[mid]) <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
 // ------------------------------------------------------------------ barriers
 // Workgroup barrier that waits only for this wave's LDS operations.  Unlike
 // __syncthreads() it does not wait for outstanding global loads, so loads

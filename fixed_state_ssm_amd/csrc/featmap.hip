@@ -6,9 +6,10 @@
 // conv-tail update and a copy kernel.
 //
 // One wave per token-head; lane l owns channels l and l + 64.  Token-heads are
-// numbered in [B][N][H] order so that neighbouring waves read neighbouring
-// rows of q, k, v.  Outputs go to the workspace in [B][H][N][d] float32 order,
-// which the sequential scans read one (b, h) sequence at a time.
+// numbered in [T][H] order (T tokens of the dense [B][N] or of a packed
+// batch) so that neighbouring waves read neighbouring rows of q, k, v.
+// Outputs go to the workspace in [H][T][d] float32 order, where each (b, h)
+// sequence is a contiguous run that the sequential scans read in turn.
 #include "common.h"
 #include "launch.h"
 
@@ -23,12 +24,15 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
     float* __restrict__ z_k, float* __restrict__ z_v) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t th = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    const int64_t H = p.H, N = p.N;
+    const int64_t H = p.H, T = p.T;
     const int d = static_cast<int>(p.d), W = static_cast<int>(p.W);
-    if (th >= p.B * N * H) return;  // whole wave exits; no barriers below
+    if (th >= T * H) return;  // whole wave exits; no barriers below
     const int64_t h = th % H;
-    const int64_t n = (th / H) % N;
-    const int64_t b = th / (H * N);
+    const int64_t t = th / H;  // token on the [T] axis
+    const int64_t b = seq_of_token(p.cu, p.N, p.B, t);
+    int64_t start, len;
+    seq_range(p.cu, p.N, T, b, start, len);
+    const int64_t n = t >= start ? t - start : 0;  // position in its sequence (0 <= n <= t)
 
     float cqv[DJ], ckv[DJ], yq[DJ], yk[DJ], xv[DJ];
     float sv = 0.f;
@@ -39,11 +43,11 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
         if (c < d) {
             const float* wq = prm.conv_q + (h * d + c) * W;
             const float* wk = prm.conv_k + (h * d + c) * W;
-            for (int t = 0; t < W; ++t) {
-                const int64_t pos = n - (W - 1) + t;
+            for (int j2 = 0; j2 < W; ++j2) {
+                const int64_t pos = n - (W - 1) + j2;
                 float xq = 0.f, xk = 0.f;
                 if (pos >= 0) {
-                    const int64_t idx = ((b * N + pos) * H + h) * d + c;
+                    const int64_t idx = ((t - (W - 1) + j2) * H + h) * d + c;  // token t - n + pos
                     xq = load_io<BF16>(q, idx);
                     xk = load_io<BF16>(k, idx);
                 } else if (tail_in != nullptr) {
@@ -51,10 +55,10 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
                     xq = load_io<BF16>(tail_in, tq);
                     xk = load_io<BF16>(tail_in, tq + static_cast<int64_t>(W - 1) * d);
                 }
-                cq = fmaf(wq[t], xq, cq);
-                ck = fmaf(wk[t], xk, ck);
+                cq = fmaf(wq[j2], xq, cq);
+                ck = fmaf(wk[j2], xk, ck);
             }
-            vv = load_io<BF16>(v, ((b * N + n) * H + h) * d + c);
+            vv = load_io<BF16>(v, (t * H + h) * d + c);
         }
         cqv[j] = cq;
         ckv[j] = ck;
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
     xk2 = wave_sum(xk2);
     const float rk = 1.f / sqrtf(xk2 / d + p.eps_norm);
     const float rv = 1.f / sqrtf(sv / d + p.eps_norm);
-    const int64_t orow = ((b * H + h) * N + n) * d;
+    const int64_t orow = (h * T + t) * d;
 #pragma unroll
     for (int j = 0; j < DJ; ++j) {
         const int c = lane + kWave * j;
@@ -116,6 +120,8 @@ __global__ __launch_bounds__(256) void tail_update_kernel(Problem p, const void*
     const int Wm1 = static_cast<int>(p.W) - 1;
     const int d = static_cast<int>(p.d);
     const int E = 2 * Wm1 * d;
+    int64_t start, len;
+    seq_range(p.cu, p.N, p.T, b, start, len);
     float val[kMaxPer];
 #pragma unroll
     for (int j = 0; j < kMaxPer; ++j) {
@@ -125,13 +131,13 @@ __global__ __launch_bounds__(256) void tail_update_kernel(Problem p, const void*
             const int sel = e / (Wm1 * d);          // 0 = q, 1 = k
             const int t = (e / d) % Wm1;            // slot in the new tail
             const int c = e % d;
-            const int64_t src = p.N + t;            // index in [tail_in ; x]
+            const int64_t src = len + t;            // index in [tail_in ; this sequence's tokens]
             if (src < Wm1) {
                 if (tail_in != nullptr)
                     val[j] = load_io<BF16>(tail_in, bh * E + (static_cast<int64_t>(sel) * Wm1 + src) * d + c);
             } else {
                 const int64_t pos = src - Wm1;
-                val[j] = load_io<BF16>(sel == 0 ? q : k, ((b * p.N + pos) * p.H + h) * d + c);
+                val[j] = load_io<BF16>(sel == 0 ? q : k, ((start + pos) * p.H + h) * d + c);
             }
         }
     }
@@ -155,7 +161,7 @@ __global__ __launch_bounds__(256) void copy_or_zero_kernel(const uint32_t* __res
 hipError_t launch_featmap_conv_norm(const Problem& p, const idattn_params& prm, const void* q,
                                     const void* k, const void* v, const void* tail_in,
                                     float* xi_q, float* z_k, float* z_v, hipStream_t stream) {
-    const int64_t th = p.B * p.N * p.H;
+    const int64_t th = p.T * p.H;
     const dim3 grid(static_cast<unsigned>((th + 3) / 4));
     if (p.d > 64) {
         if (p.bf16)

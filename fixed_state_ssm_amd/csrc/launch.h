@@ -15,9 +15,13 @@ struct Problem {
     float eps_feat, eps_norm;
     bool unit_feat;  // xi = y / sqrt(||y||^2 + eps_feat) instead of y / (||y||^2 + eps_feat)
     bool rff_feat;   // xi = random Fourier features of c with prm.rff_omega (overrides unit_feat)
+    // Token axis: T tokens in [T][H][d].  cu == nullptr: B sequences of N tokens
+    // each (T = B N); else a packed batch, sequence b = tokens cu[b] .. cu[b+1]-1.
+    int64_t T;
+    const int32_t* cu;
 };
 
-// ---- stage kernels of the sequential (fp32) path; workspace layout [B][H][N][*]
+// ---- stage kernels of the sequential (fp32) path; workspace layout [H][T][*]
 hipError_t launch_featmap_conv_norm(const Problem& p, const idattn_params& prm,
                                     const void* q, const void* k, const void* v,
                                     const void* tail_in, float* xi_q, float* z_k,

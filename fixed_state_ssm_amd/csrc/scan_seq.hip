@@ -28,10 +28,12 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t bh = blockIdx.x;
     const int64_t m = static_cast<int64_t>(blockIdx.y) * 4 + (threadIdx.x >> 6);
-    const int64_t M = p.M, N = p.N;
+    const int64_t M = p.M;
     const int d = static_cast<int>(p.d);
     if (m >= M) return;  // whole wave; no barriers in this kernel
     const int64_t h = bh % p.H;
+    int64_t start, N;  // this sequence's tokens on the [T] axis
+    seq_range(p.cu, p.N, p.T, bh / p.H, start, N);
     const Zoh z = zoh_mode(prm.log_dt[h], prm.A[(h * M + m) * 2], prm.A[(h * M + m) * 2 + 1],
                            prm.Bc[(h * M + m) * 2], prm.Bc[(h * M + m) * 2 + 1]);
     const float ar = static_cast<float>(z.ar), ai = static_cast<float>(z.ai);
@@ -48,9 +50,10 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
             ui[j] = state_in[st_row + 2 * r + 1];
         }
     }
-    const float* xq = xi_q + bh * N * d;
-    const float* zk = z_k + bh * N * d;
-    float2* srow = s + bh * N * M + m;
+    const int64_t row0 = h * p.T + start;  // workspace rows [H][T]
+    const float* xq = xi_q + row0 * d;
+    const float* zk = z_k + row0 * d;
+    float2* srow = s + row0 * M + m;
     for (int64_t i0 = 0; i0 < N; i0 += kTok) {
         float xv[kTok][RJ], zv[kTok][RJ];
 #pragma unroll
@@ -106,9 +109,12 @@ __global__ __launch_bounds__(256) void value_scan_seq_kernel(Problem p, idattn_p
     const int w = threadIdx.x >> 6;
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / p.H, h = bh % p.H;
-    const int64_t M = p.M, N = p.N, H = p.H;
+    const int64_t M = p.M, H = p.H;
     const int d = static_cast<int>(p.d);
     const int c = static_cast<int>(blockIdx.y) * kWave + lane;
+    int64_t start, N;  // this sequence's tokens on the [T] axis
+    seq_range(p.cu, p.N, p.T, b, start, N);
+    const int64_t row0 = h * p.T + start;  // workspace rows [H][T]
     const bool cok = c < d;
 
     float ar[MW], ai[MW], br[MW], bi[MW], gr[MW], gi[MW];
@@ -128,10 +134,10 @@ __global__ __launch_bounds__(256) void value_scan_seq_kernel(Problem p, idattn_p
             gi[mm] = state_in[idx + 1];
         }
     }
-    const float* zv = z_v + bh * N * d;
+    const float* zv = z_v + row0 * d;
     for (int64_t i0 = 0; i0 < N; i0 += kBlk) {
         const int nt = static_cast<int>(N - i0 < kBlk ? N - i0 : kBlk);
-        for (int e = threadIdx.x; e < nt * M; e += 256) s_blk[e] = s[(bh * N + i0) * M + e];
+        for (int e = threadIdx.x; e < nt * M; e += 256) s_blk[e] = s[(row0 + i0) * M + e];
         float zz[kBlk];
 #pragma unroll
         for (int t = 0; t < kBlk; ++t) zz[t] = (t < nt && cok) ? zv[(i0 + t) * d + c] : 0.f;
@@ -158,7 +164,7 @@ __global__ __launch_bounds__(256) void value_scan_seq_kernel(Problem p, idattn_p
             const int cc = static_cast<int>(blockIdx.y) * kWave + l;
             if (cc < d) {
                 const float sum = (red[0][t][l] + red[1][t][l]) + (red[2][t][l] + red[3][t][l]);
-                store_io<BF16>(o, ((b * N + i0 + t) * H + h) * d + cc, sum);
+                store_io<BF16>(o, ((start + i0 + t) * H + h) * d + cc, sum);
             }
         }
         __syncthreads();

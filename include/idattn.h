@@ -96,7 +96,8 @@ typedef enum idattn_feature_norm {
 /* Sizes.  R == d.  Layout of q, k, v, o: contiguous [B][N][H][d]. */
 typedef struct idattn_dims {
     int64_t B;        /* batch rows, >= 1                                     */
-    int64_t N;        /* tokens in this call, >= 0 (forward) or 1..8 (decode) */
+    int64_t N;        /* tokens per sequence, >= 0 (forward), 1..8 (decode);
+                         all tokens T of a packed batch (varlen)           */
     int64_t H;        /* heads, >= 1                                          */
     int64_t d;        /* channels per head (= R); supported 16, 32, 64, 128   */
     int64_t M;        /* complex modes per head; supported 16, 32, 64         */
@@ -156,6 +157,38 @@ idattn_status idattn_forward(const idattn_dims *dims, const idattn_params *param
                              const float *state_in, const void *tail_in,
                              float *state_out, void *tail_out,
                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Packed variable-length batch: dims->B sequences of different lengths laid
+ * end to end on one token axis of dims->N = T tokens, each sequence
+ * independent of the others with its own state and conv tail.  The
+ * fixed-size state per sequence (Chinese rendering, section 1) is what makes
+ * prompts of mixed lengths one call.  Same result, sequence by sequence, as
+ * idattn_forward with B = 1 on that sequence's tokens.
+ *
+ *  cu_seqlens in   device int32 [B + 1], 4-byte aligned: sequence b is tokens
+ *                  cu_seqlens[b] .. cu_seqlens[b+1]-1; it must rise from 0 to
+ *                  T (zero-length sequences allowed).  Not checked (device
+ *                  memory): the kernels clamp every bound into [0, T], so a
+ *                  malformed table gives wrong results but no access out of
+ *                  bounds.
+ *  q, k, v    in   [T][H][d] io dtype
+ *  o          out  [T][H][d] io dtype
+ *  state_in, tail_in, state_out, tail_out  as for idattn_forward, with B
+ *                  sequences ([B][H][M][2d][2] and [B][H][2][W-1][d])
+ *  workspace       at least idattn_forward_varlen_workspace_size bytes
+ * dims->algo: AUTO or SEQUENTIAL (the fp32 recurrence; CHUNKED returns
+ * IDATTN_ERR_UNSUPPORTED).  T < 2^31.  Overlap rules as for idattn_forward;
+ * cu_seqlens must not overlap any output.
+ */
+idattn_status idattn_forward_varlen_workspace_size(const idattn_dims *dims, size_t *bytes);
+
+idattn_status idattn_forward_varlen(const idattn_dims *dims, const idattn_params *params,
+                                    const int32_t *cu_seqlens,
+                                    const void *q, const void *k, const void *v, void *o,
+                                    const float *state_in, const void *tail_in,
+                                    float *state_out, void *tail_out,
+                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Autoregressive steps for every batch row (O(1) work and a fixed-size

@@ -7,8 +7,10 @@ product package and the product never imports it.
 
 Parity status of every function is listed in idattn_oracle's module header.
 """
-from .idattn_oracle import (decode_step, feature_map, forward, rms_norm,
+from .idattn_oracle import (decode_step, feature_map, feature_map_rff,
+                            feature_map_unit, forward, forward_varlen, rms_norm,
                             short_conv, silu, ssm_step, zoh)
 
-__all__ = ["decode_step", "feature_map", "forward", "rms_norm", "short_conv",
-           "silu", "ssm_step", "zoh"]
+__all__ = ["decode_step", "feature_map", "feature_map_rff", "feature_map_unit",
+           "forward", "forward_varlen", "rms_norm", "short_conv", "silu",
+           "ssm_step", "zoh"]

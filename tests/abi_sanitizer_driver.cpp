@@ -139,6 +139,28 @@ int main() {
         expect(forward(x, q, need), IDATTN_ERR_NULL, "NULL lambda");
     }
 
+    // packed variable-length batches: argument errors
+    {
+        idattn_dims y = dims(5, 1000, 3, 64, 32, 4, IDATTN_IO_BF16, IDATTN_ALGO_AUTO);
+        size_t vneed = 0;
+        expect(idattn_forward_varlen_workspace_size(&y, &vneed), IDATTN_OK, "varlen workspace size");
+        const int32_t* cu = static_cast<const int32_t*>(fake(30));
+        auto var = [&](const idattn_dims& z, const int32_t* c, size_t ws, void* o) {
+            return idattn_forward_varlen(&z, &p, c, fake(1), fake(2), fake(3), o, static_cast<const float*>(fake(5)),
+                                         fake(6), static_cast<float*>(fake(7)), fake(8), fake(9), ws, nullptr);
+        };
+        expect(var(y, nullptr, vneed, fake(4)), IDATTN_ERR_NULL, "NULL cu_seqlens");
+        expect(var(y, static_cast<const int32_t*>(fake(30, 2)), vneed, fake(4)), IDATTN_ERR_ARG, "misaligned cu_seqlens");
+        expect(var(y, cu, vneed - 1, fake(4)), IDATTN_ERR_WORKSPACE, "varlen workspace one byte short");
+        expect(var(y, cu, vneed, fake(30, 16)), IDATTN_ERR_ALIAS, "o over cu_seqlens");
+        idattn_dims z = y;
+        z.algo = IDATTN_ALGO_CHUNKED;
+        expect(var(z, cu, vneed, fake(4)), IDATTN_ERR_UNSUPPORTED, "varlen chunked");
+        z = y;
+        z.N = int64_t{1} << 31;
+        expect(var(z, cu, ~size_t{0}, fake(4)), IDATTN_ERR_SHAPE, "varlen T >= 2^31");
+    }
+
     // decode: 1..8 tokens, argument errors
     {
         idattn_dims y = dims(2, 4, 3, 64, 32, 4, IDATTN_IO_BF16, IDATTN_ALGO_AUTO);

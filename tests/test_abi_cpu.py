@@ -217,3 +217,38 @@ def test_decode_outputs_must_not_overlap_parameters():
         b[key] = where
         expect(lib.idattn_decode_step(ctypes.byref(d), ctypes.byref(p), b["q"], b["k"], b["v"], b["o"], b["s"],
                                       b["t"], None), "IDATTN_ERR_ALIAS")
+
+
+def call_varlen(d, p, cu, ws_bytes=None, **over):
+    a = dict(ADDR)
+    a.update(over)
+    if ws_bytes is None:
+        ws_bytes = fs.idattn_forward_varlen_workspace_size(d)
+    lib = fs.load_library()
+    return lib.idattn_forward_varlen(ctypes.byref(d), ctypes.byref(p), cu, a["q"], a["k"], a["v"], a["o"], a["si"],
+                                     a["ti"], a["so"], a["to"], a["ws"], ws_bytes, None)
+
+
+def test_varlen_validation():
+    """Packed batches: B sequences on N = T tokens.  The workspace is that of
+    one dense sequence of T tokens; the chunked algorithm is refused; the
+    cu_seqlens table must be given, 4-byte aligned and clear of the outputs."""
+    d = dims(B=5, N=1000)
+    assert fs.idattn_forward_varlen_workspace_size(d) == fs.idattn_forward_workspace_size(
+        dims(B=1, N=1000, algo="sequential"))
+    assert fs.idattn_forward_varlen_workspace_size(dims(B=5, N=0)) == 0
+    with pytest.raises(fs.IdattnError) as e:
+        fs.idattn_forward_varlen_workspace_size(dims(B=5, N=1000, algo="chunked"))
+    assert e.value.status_name == "IDATTN_ERR_UNSUPPORTED"
+    cu = 10 * QB
+    p = params()
+    expect(call_varlen(d, p, None), "IDATTN_ERR_NULL")
+    expect(call_varlen(d, p, cu + 2), "IDATTN_ERR_ARG")
+    expect(call_varlen(dims(B=5, N=1000, algo="chunked"), p, cu, ws_bytes=1 << 40), "IDATTN_ERR_UNSUPPORTED")
+    expect(call_varlen(dims(B=5, N=1 << 31), p, cu, ws_bytes=1 << 50), "IDATTN_ERR_SHAPE")
+    expect(call_varlen(d, p, cu, ws_bytes=fs.idattn_forward_varlen_workspace_size(d) - 1), "IDATTN_ERR_WORKSPACE")
+    expect(call_varlen(d, p, cu, o=cu - 64), "IDATTN_ERR_ALIAS")          # o runs into cu_seqlens
+    expect(call_varlen(d, p, cu, so=cu - 16), "IDATTN_ERR_ALIAS")         # state_out runs over cu_seqlens
+    expect(call_varlen(d, p, cu, o=ADDR["q"] + 1000 * 3 * 64 * 2 - 16), "IDATTN_ERR_ALIAS")  # o over q's last row
+    expect(call_varlen(d, p, cu, q=0), "IDATTN_ERR_NULL")
+    expect(call_varlen(dims(B=5, N=1000, feature_norm="rff"), params(rff_omega=0), cu), "IDATTN_ERR_NULL")
