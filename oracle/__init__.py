@@ -8,9 +8,9 @@ product package and the product never imports it.
 Parity status of every function is listed in idattn_oracle's module header.
 """
 from .idattn_oracle import (decode_step, feature_map, feature_map_rff,
-                            feature_map_unit, forward, forward_varlen, rms_norm,
+                            feature_map_unit, forward, forward_normalized, forward_varlen, rms_norm,
                             short_conv, silu, ssm_step, zoh)
 
 __all__ = ["decode_step", "feature_map", "feature_map_rff", "feature_map_unit",
-           "forward", "forward_varlen", "rms_norm", "short_conv", "silu",
+           "forward", "forward_normalized", "forward_varlen", "rms_norm", "short_conv", "silu",
            "ssm_step", "zoh"]

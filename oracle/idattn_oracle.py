@@ -55,6 +55,11 @@ Parity pins (tests/test_oracle_pins.py):
                of o, M=1 real-EMA limit via scipy.signal.lfilter, Delta -> 0
                limit, causality, row/head independence, split-sequence resume.
   decode_step  pinned: equals the next position of a longer forward.
+  forward_normalized  pinned: eta against its geometric-series closed form
+               from a given start; with M = 1 and a real mode the readout is the
+               ratio of two first-order IIR filters (scipy.signal.lfilter of z_v
+               over lfilter of ones), whatever the queries; invariance of o
+               under rescaling the query features (unit against squared map).
   forward_varlen  pinned: equal lengths give the batched forward; an empty
                sequence passes its state and tail through; a sequence split
                into two packed pieces, the second resumed from the first's
@@ -265,6 +270,37 @@ def forward(q, k, v, params, eps_feat=1e-6, eps_norm=1e-6,
     inter = dict(c_q=c_q, c_k=c_k, xi_q=xi_q, xi_k=xi_k, z_k=z_k, z_v=z_v,
                  abar=abar, bbar=bbar, s=s_all)
     return o, state_out, tail_out, inter
+
+
+def forward_normalized(q, k, v, params, eps_feat=1e-6, eps_norm=1e-6, state_in=None, tail_in=None,
+                       eta_in=None, feature_norm="squared", parts=False):
+    """Forward with the normalised readout of the derivation (p2 "Theoretische
+    Herleitung" and p1 Fig. 1: the third in-loop state eta, M x 1, and the
+    readout F_q U^T Gamma / (F_q U^T eta)); the scalable layer of the
+    summaries drops it.  eta is read as the SSM response to a constant input
+    of one, with the same abar, bbar as the other channels:
+        eta_m(i) = abar_m eta_m(i-1) + bbar_m,
+        o_i = Re sum_m s_m(i) Gamma_m(i) / Re sum_m s_m(i) eta_m(i),
+    plain bilinear like the rest, no epsilon in the denominator.  The
+    numerator is the output of forward() above.
+
+    eta_in complex [B, H, M] or None (zeros).  Returns (o, state_out,
+    tail_out, eta_out) and, with parts=True, also (num, den) [B, N, H, d] and
+    [B, N, H]."""
+    num, state_out, tail_out, it = forward(q, k, v, params, eps_feat, eps_norm, state_in=state_in,
+                                           tail_in=tail_in, intermediates=True, feature_norm=feature_norm)
+    B, N, H, _ = num.shape
+    M = it["abar"].shape[1]
+    eta = np.zeros((B, H, M), dtype=C128) if eta_in is None else np.asarray(eta_in, dtype=C128).copy()
+    den = np.empty((B, N, H), dtype=F64)
+    for i in range(N):
+        eta = it["abar"][None] * eta + it["bbar"][None]
+        den[:, i] = np.einsum("bhm,bhm->bh", it["s"][:, i], eta).real
+    with np.errstate(divide="ignore", invalid="ignore"):
+        o = num / den[..., None]
+    if parts:
+        return o, state_out, tail_out, eta, num, den
+    return o, state_out, tail_out, eta
 
 
 def forward_varlen(q, k, v, cu_seqlens, params, eps_feat=1e-6, eps_norm=1e-6,

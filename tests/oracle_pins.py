@@ -329,6 +329,80 @@ def pin_m1_lfilter(O) -> float:
     return rel(o, o_ref)
 
 
+def pin_eta_closed_form(O) -> float:
+    """The normaliser state from a start eta0 after n tokens is the geometric
+    series abar^n eta0 + bbar (1 - abar^n) / (1 - abar)."""
+    c = pin_case(with_state=True)
+    p = c["p"]
+    B, N, H, _ = c["q"].shape
+    M = np.asarray(p["A"]).shape[1]
+    eta0 = np.random.default_rng(31).normal(size=(B, H, M)) + 1j * np.random.default_rng(32).normal(size=(B, H, M))
+    _, _, _, eta = O.forward_normalized(c["q"], c["k"], c["v"], p, state_in=c["state"], tail_in=c["tail"],
+                                        eta_in=eta0)
+    dt = np.exp(np.asarray(p["log_dt"], float))[:, None]
+    lam = np.asarray(p["A"], float)[..., 0] + 1j * np.asarray(p["A"], float)[..., 1]
+    bc = np.asarray(p["Bc"], float)[..., 0] + 1j * np.asarray(p["Bc"], float)[..., 1]
+    abar = np.exp(dt * lam)
+    bbar = (abar - 1) / lam * bc
+    want = abar[None] ** N * eta0 + bbar[None] * (1 - abar[None] ** N) / (1 - abar[None])
+    return rel(eta, want)
+
+
+def pin_eta_m1_ratio(O) -> float:
+    """M = 1 with a real mode: s is a scalar per token that multiplies both
+    Gamma and eta, so o = lfilter(z_v) / lfilter(ones), the ratio of two
+    first-order IIR filters, whatever the queries."""
+    c = pin_case(M=1, N=60)
+    p = c["p"]
+    p["A"] = np.array(p["A"])
+    p["A"][..., 1] = 0.0
+    p["Bc"] = np.array(p["Bc"])
+    p["Bc"][..., 1] = 0.0
+    o, _, _, _ = O.forward_normalized(c["q"], c["k"], c["v"], p, tail_in=c["tail"])
+    _, _, _, it = O.forward(c["q"], c["k"], c["v"], p, 1e-6, 1e-6, None, c["tail"], True)
+    dt = np.exp(np.asarray(p["log_dt"], float))
+    lam = np.asarray(p["A"], float)[:, 0, 0]
+    ab = np.exp(dt * lam)
+    bb = (ab - 1) / lam * np.asarray(p["Bc"], float)[:, 0, 0]
+    o_ref = np.empty_like(o)
+    for h in range(o.shape[2]):
+        g = scipy.signal.lfilter([bb[h]], [1.0, -ab[h]], it["z_v"][:, :, h], axis=1)
+        e = scipy.signal.lfilter([bb[h]], [1.0, -ab[h]], np.ones(o.shape[1]))
+        o_ref[:, :, h] = g / e[None, :, None]
+    return rel(o, o_ref)
+
+
+def pin_eta_kernel_form(O) -> float:
+    """State-free form of the normalised readout's denominator:
+    den(i) = sum_{j,l<=i} (xi_q(i).z_k(j)) K(2i-j-l) with the same kernel
+    K(t) = Re sum_m bbar_m^2 abar_m^t as the numerator's (z_v(l) replaced by
+    the constant input 1).  A conjugated product gives another kernel."""
+    c = pin_case(N=24)
+    p = c["p"]
+    o, _, _, _, num, den = O.forward_normalized(c["q"], c["k"], c["v"], p, tail_in=c["tail"], parts=True)
+    _, _, _, it = O.forward(c["q"], c["k"], c["v"], p, 1e-6, 1e-6, None, c["tail"], True)
+    B, N, H, d = o.shape
+    abar, bbar = O.zoh(p["log_dt"], p["A"], p["Bc"])
+    K = np.einsum("hm,hmt->ht", bbar ** 2, abar[:, :, None] ** np.arange(2 * N)[None, None]).real
+    den_ref = np.zeros((B, N, H))
+    for i in range(N):
+        j = np.arange(i + 1)
+        gram = np.einsum("bhr,bjhr->bhj", it["xi_q"][:, i], it["z_k"][:, :i + 1])
+        den_ref[:, i] = np.einsum("bhj,hjl->bh", gram, K[:, 2 * i - j[:, None] - j[None, :]])
+    return max(rel(den, den_ref), rel(o * den[..., None], num))
+
+
+def pin_eta_query_scale(O) -> float:
+    """The normalised readout does not depend on the scale of the query
+    features: with eps = 0 the unit-norm and the squared map (which differ by
+    the factor ||y_q|| per token) give the same o."""
+    c = pin_case(with_state=True)
+    args = (c["q"], c["k"], c["v"], c["p"], 0.0, 0.0, c["state"], c["tail"])
+    o_sq = O.forward_normalized(*args, feature_norm="squared")[0]
+    o_un = O.forward_normalized(*args, feature_norm="unit")[0]
+    return rel(o_un, o_sq)
+
+
 def pin_dt_zero(O) -> float:
     """Delta -> 0: abar -> 1, bbar -> Delta B, so
     o_i / Delta^2 -> (sum_m B_m^2) (xi_q(i) . sum_{j<=i} z_k(j)) sum_{l<=i} z_v(l).
@@ -457,5 +531,9 @@ PINS = {
     "split_resume": (pin_split_resume, 1e-12),
     "decode": (pin_decode, 1e-12),
     "varlen": (pin_varlen, 1e-12),
+    "eta_closed_form": (pin_eta_closed_form, 1e-12),
+    "eta_m1_ratio": (pin_eta_m1_ratio, 1e-11),
+    "eta_query_scale": (pin_eta_query_scale, 1e-10),
+    "eta_kernel_form": (pin_eta_kernel_form, 1e-11),
     "independence": (pin_independence, 1e-13),
 }

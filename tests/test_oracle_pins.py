@@ -92,6 +92,38 @@ def _varlen_conv_leaks(q, k, v, cu, params, eps_feat=1e-6, eps_norm=1e-6, state_
     return _orig["forward_varlen"](q, k, v, cu, params, eps_feat, eps_norm, state_in, tail, feature_norm)
 
 
+def _eta_without_bbar(q, k, v, params, eps_feat=1e-6, eps_norm=1e-6, state_in=None, tail_in=None, eta_in=None,
+                      feature_norm="squared", parts=False):
+    # the normaliser driven by ones without the input coefficient
+    p = dict(params)
+    out = _orig["forward_normalized"](q, k, v, p, eps_feat, eps_norm, state_in, tail_in, eta_in, feature_norm, True)
+    o, st, tl, eta, num, den = out
+    abar, bbar = O.zoh(p["log_dt"], p["A"], p["Bc"])
+    _, _, _, it = O.forward(q, k, v, p, eps_feat, eps_norm, state_in, tail_in, True, feature_norm)
+    e = np.zeros_like(eta) if eta_in is None else np.asarray(eta_in, complex).copy()
+    den2 = np.empty_like(den)
+    for i in range(den.shape[1]):
+        e = abar[None] * e + 1.0
+        den2[:, i] = np.einsum("bhm,bhm->bh", it["s"][:, i], e).real
+    o2 = num / den2[..., None]
+    return (o2, st, tl, e, num, den2) if parts else (o2, st, tl, e)
+
+
+def _eta_conjugated(q, k, v, params, eps_feat=1e-6, eps_norm=1e-6, state_in=None, tail_in=None, eta_in=None,
+                    feature_norm="squared", parts=False):
+    o, st, tl, eta, num, den = _orig["forward_normalized"](q, k, v, params, eps_feat, eps_norm, state_in, tail_in,
+                                                           eta_in, feature_norm, True)
+    abar, bbar = O.zoh(params["log_dt"], params["A"], params["Bc"])
+    _, _, _, it = O.forward(q, k, v, params, eps_feat, eps_norm, state_in, tail_in, True, feature_norm)
+    e = np.zeros_like(eta) if eta_in is None else np.asarray(eta_in, complex).copy()
+    den2 = np.empty_like(den)
+    for i in range(den.shape[1]):
+        e = abar[None] * e + bbar[None]
+        den2[:, i] = np.einsum("bhm,bhm->bh", np.conj(it["s"][:, i]), e).real
+    o2 = num / den2[..., None]
+    return (o2, st, tl, e, num, den2) if parts else (o2, st, tl, e)
+
+
 def _rms_sum(x, g, b, eps):
     x = np.asarray(x, float)
     return np.asarray(g)[None, None] * x / np.sqrt((x * x).sum(-1, keepdims=True) + eps) + np.asarray(b)[None, None]
@@ -141,7 +173,7 @@ def _step_imag_dropped(U, G, xq, zk, zv, a, b):
 
 
 _orig = {name: getattr(O, name) for name in ("short_conv", "silu", "feature_map", "feature_map_unit", "feature_map_rff",
-                                             "rms_norm", "forward_varlen",
+                                             "rms_norm", "forward_varlen", "forward_normalized",
                                              "zoh", "ssm_step")}
 
 MUTANTS = {
@@ -157,6 +189,8 @@ MUTANTS = {
     "rff_half_frequency": ("feature_map_rff", _rff_half_frequency),
     "varlen_first_tail_for_all": ("forward_varlen", _varlen_first_tail),
     "varlen_conv_crosses_sequences": ("forward_varlen", _varlen_conv_leaks),
+    "eta_driven_without_bbar": ("forward_normalized", _eta_without_bbar),
+    "eta_conjugated_scores": ("forward_normalized", _eta_conjugated),
     "rms_sum_not_mean": ("rms_norm", _rms_sum),
     "rms_dropped_bias": ("rms_norm", _rms_no_bias),
     "zoh_euler_bbar": ("zoh", _zoh_euler),
