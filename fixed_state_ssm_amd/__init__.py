@@ -2,23 +2,26 @@
 
 The work runs in libidattn.so (HIP kernels behind a C ABI, include/idattn.h).
 This package holds the ctypes binding (functions named like the C entry
-points) and three conveniences, forward(), forward_varlen() and
-decode_step(), that allocate outputs and workspace with PyTorch and call the
+points) and four conveniences, forward(), forward_normalized(),
+forward_varlen() and decode_step(), that allocate outputs and workspace with PyTorch and call the
 binding on the current stream.
 """
 from __future__ import annotations
 
 from .binding import (ALGO, EXPORTS, FEATURE_NORM, IO, LIB_PATH, STATUS, IdattnDims, IdattnError, IdattnParams,
-                      idattn_decode_step, idattn_forward, idattn_forward_varlen,
+                      idattn_decode_step, idattn_forward, idattn_forward_normalized,
+                      idattn_forward_normalized_workspace_size, idattn_forward_varlen,
                       idattn_forward_varlen_workspace_size, idattn_forward_workspace_size,
                       idattn_last_error, idattn_status_string, idattn_version, load_library,
                       make_dims, make_params)
 
 __all__ = ["ALGO", "EXPORTS", "FEATURE_NORM", "IO", "LIB_PATH", "STATUS", "IdattnDims", "IdattnError", "IdattnParams",
-           "idattn_decode_step", "idattn_forward", "idattn_forward_varlen", "idattn_forward_varlen_workspace_size",
+           "idattn_decode_step", "idattn_forward", "idattn_forward_normalized",
+           "idattn_forward_normalized_workspace_size", "idattn_forward_varlen", "idattn_forward_varlen_workspace_size",
            "idattn_forward_workspace_size",
            "idattn_last_error", "idattn_status_string", "idattn_version", "load_library",
-           "make_dims", "make_params", "forward", "forward_varlen", "decode_step", "params_to_device"]
+           "make_dims", "make_params", "forward", "forward_normalized", "forward_varlen", "decode_step",
+           "params_to_device"]
 
 PARAM_KEYS = ("conv_q", "conv_k", "gain", "bias", "log_dt", "A", "Bc")
 
@@ -66,6 +69,32 @@ def forward(q, k, v, params: dict, *, state_in=None, tail_in=None, return_state=
     idattn_forward(dims, make_params(params), q, k, v, o, state_in, tail_in, state_out, tail_out,
                    ws, nbytes, stream)
     return (o, state_out, tail_out) if return_state else o
+
+
+def forward_normalized(q, k, v, params: dict, *, state_in=None, tail_in=None, eta_in=None, return_state=False,
+                       algo="auto", eps_feat=1e-6, eps_norm=1e-6, feature_norm="squared", stream=None):
+    """o = mixer with the normalised readout (eta state) for q, k, v
+    [B, N, H, d].  eta_in: float32 [B, H, M, 2] or None.  With
+    return_state=True returns (o, state_out, tail_out, eta_out)."""
+    import torch
+    B, N, H, d = q.shape
+    M = params["A"].shape[1]
+    W = params["conv_q"].shape[-1]
+    for t in (k, v):
+        if t.dtype != q.dtype or t.shape != q.shape:
+            raise ValueError("q, k, v must share shape and dtype")
+    dims = make_dims(B, N, H, d, M, W, _io_name(q), algo, eps_feat, eps_norm, feature_norm)
+    nbytes = idattn_forward_normalized_workspace_size(dims)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    state_out = tail_out = eta_out = None
+    if return_state:
+        state_out = torch.empty((B, H, M, 2 * d, 2), dtype=torch.float32, device=q.device)
+        tail_out = torch.empty((B, H, 2, W - 1, d), dtype=q.dtype, device=q.device)
+        eta_out = torch.empty((B, H, M, 2), dtype=torch.float32, device=q.device)
+    idattn_forward_normalized(dims, make_params(params), q, k, v, o, state_in, tail_in, eta_in, state_out, tail_out,
+                              eta_out, ws, nbytes, stream)
+    return (o, state_out, tail_out, eta_out) if return_state else o
 
 
 def forward_varlen(q, k, v, params: dict, cu_seqlens, *, state_in=None, tail_in=None, return_state=False,

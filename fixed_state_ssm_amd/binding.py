@@ -20,9 +20,9 @@ IO = {"f32": 0, "bf16": 1}
 ALGO = {"auto": 0, "sequential": 1, "chunked": 2}
 FEATURE_NORM = {"squared": 0, "unit": 1, "rff": 2}
 
-EXPORTS = ("idattn_forward_workspace_size", "idattn_forward", "idattn_forward_varlen_workspace_size",
-           "idattn_forward_varlen", "idattn_decode_step", "idattn_status_string", "idattn_last_error",
-           "idattn_version")
+EXPORTS = ("idattn_forward_workspace_size", "idattn_forward", "idattn_forward_normalized_workspace_size",
+           "idattn_forward_normalized", "idattn_forward_varlen_workspace_size", "idattn_forward_varlen",
+           "idattn_decode_step", "idattn_status_string", "idattn_last_error", "idattn_version")
 
 
 class IdattnDims(ctypes.Structure):
@@ -59,6 +59,10 @@ def load_library(path: str = LIB_PATH):
     lib.idattn_forward_workspace_size.restype = c_int
     lib.idattn_forward.argtypes = [P(IdattnDims), P(IdattnParams)] + [c_void_p] * 9 + [c_size_t, c_void_p]
     lib.idattn_forward.restype = c_int
+    lib.idattn_forward_normalized_workspace_size.argtypes = [P(IdattnDims), P(c_size_t)]
+    lib.idattn_forward_normalized_workspace_size.restype = c_int
+    lib.idattn_forward_normalized.argtypes = [P(IdattnDims), P(IdattnParams)] + [c_void_p] * 11 + [c_size_t, c_void_p]
+    lib.idattn_forward_normalized.restype = c_int
     lib.idattn_forward_varlen_workspace_size.argtypes = [P(IdattnDims), P(c_size_t)]
     lib.idattn_forward_varlen_workspace_size.restype = c_int
     lib.idattn_forward_varlen.argtypes = [P(IdattnDims), P(IdattnParams)] + [c_void_p] * 10 + [c_size_t, c_void_p]
@@ -144,6 +148,20 @@ def idattn_forward(dims, params, q, k, v, o, state_in=None, tail_in=None, state_
     _check(load_library().idattn_forward(
         ctypes.byref(dims), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
         _ptr(state_in), _ptr(tail_in), _ptr(state_out), _ptr(tail_out), _ptr(workspace),
+        int(workspace_bytes), _stream(stream)))
+
+
+def idattn_forward_normalized_workspace_size(dims: IdattnDims) -> int:
+    out = c_size_t(0)
+    _check(load_library().idattn_forward_normalized_workspace_size(ctypes.byref(dims), ctypes.byref(out)))
+    return out.value
+
+
+def idattn_forward_normalized(dims, params, q, k, v, o, state_in=None, tail_in=None, eta_in=None, state_out=None,
+                              tail_out=None, eta_out=None, workspace=None, workspace_bytes=0, stream=None) -> None:
+    _check(load_library().idattn_forward_normalized(
+        ctypes.byref(dims), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state_in),
+        _ptr(tail_in), _ptr(eta_in), _ptr(state_out), _ptr(tail_out), _ptr(eta_out), _ptr(workspace),
         int(workspace_bytes), _stream(stream)))
 
 

@@ -128,13 +128,15 @@ int resolve_algo(const idattn_dims& D) {
                                                                                  : IDATTN_ALGO_SEQUENTIAL;
 }
 
-// tokens on the [T] axis: B N for the dense entry point, N for the packed one
-size_t seq_workspace_bytes(const idattn_dims& D, int64_t T) {
-    // xi_q, z_k, z_v: float [H][T][d]; s: complex float [H][T][M]
+// tokens on the [T] axis: B N for the dense entry points, N for the packed one
+size_t seq_workspace_bytes(const idattn_dims& D, int64_t T, bool eta = false) {
+    // xi_q, z_k, z_v: float [H][T][d]; s: complex float [H][T][M]; with the
+    // normalised readout also the denominator shares, float [H][T][M]
     const size_t tok = static_cast<size_t>(D.H) * T;
     const size_t a = 3 * tok * D.d * sizeof(float);
     const size_t s = tok * D.M * 2 * sizeof(float);
-    return ((a + 255) / 256) * 256 + s;
+    const size_t e = eta ? tok * D.M * sizeof(float) : 0;
+    return ((a + 255) / 256) * 256 + ((s + 255) / 256) * 256 + e;
 }
 
 idattn_status workspace_bytes(const idattn_dims& D, int algo, size_t* bytes) {
@@ -158,20 +160,25 @@ idattn_status workspace_bytes(const idattn_dims& D, int algo, size_t* bytes) {
 }
 
 // The sequential path: feature kernel, key scan, value scan with readout, tail.
+// With eta (normalised readout) eta_in / eta_out are the normaliser states.
 idattn_status run_sequential(const idattn::Problem& p, const idattn_params& prm, const void* q, const void* k,
                              const void* v, void* o, const float* state_in, const void* tail_in, float* state_out,
-                             void* tail_out, void* workspace, hipStream_t s) {
+                             void* tail_out, void* workspace, hipStream_t s, bool eta = false,
+                             const float* eta_in = nullptr, float* eta_out = nullptr) {
     const size_t tok = static_cast<size_t>(p.H) * p.T;
     float* xi_q = static_cast<float*>(workspace);
     float* z_k = xi_q + tok * p.d;
     float* z_v = z_k + tok * p.d;
-    float* sbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                           ((3 * tok * p.d * sizeof(float) + 255) / 256) * 256);
+    char* base = static_cast<char*>(workspace);
+    const size_t off_s = ((3 * tok * p.d * sizeof(float) + 255) / 256) * 256;
+    float* sbuf = reinterpret_cast<float*>(base + off_s);
+    float* pden = eta ? reinterpret_cast<float*>(base + off_s + ((tok * p.M * 2 * sizeof(float) + 255) / 256) * 256)
+                      : nullptr;
     hipError_t e = idattn::launch_featmap_conv_norm(p, prm, q, k, v, tail_in, xi_q, z_k, z_v, s);
     if (e != hipSuccess) return hip_fail(e, "featmap_conv_norm");
-    e = idattn::launch_ssm_key_scan_seq(p, prm, xi_q, z_k, state_in, sbuf, state_out, s);
+    e = idattn::launch_ssm_key_scan_seq(p, prm, xi_q, z_k, state_in, sbuf, state_out, eta_in, eta_out, pden, s);
     if (e != hipSuccess) return hip_fail(e, "ssm_key_scan");
-    e = idattn::launch_ssm_value_scan_readout_seq(p, prm, sbuf, z_v, state_in, o, state_out, s);
+    e = idattn::launch_ssm_value_scan_readout_seq(p, prm, sbuf, z_v, state_in, o, state_out, pden, s);
     if (e != hipSuccess) return hip_fail(e, "ssm_value_scan_readout");
     if (tail_out) {
         e = idattn::launch_tail_update(p, q, k, tail_in, tail_out, s);
@@ -300,6 +307,68 @@ idattn_status idattn_forward(const idattn_dims* dims, const idattn_params* param
         return IDATTN_OK;  // the chunked forward writes tail_out itself
     }
     return run_sequential(p, *params, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, s);
+}
+
+idattn_status idattn_forward_normalized_workspace_size(const idattn_dims* dims, size_t* bytes) {
+    if (bytes == nullptr) return fail(IDATTN_ERR_NULL, "bytes is NULL");
+    idattn_status st = check_dims(dims, false);
+    if (st != IDATTN_OK) return st;
+    if (dims->algo == IDATTN_ALGO_CHUNKED)
+        return fail(IDATTN_ERR_UNSUPPORTED, "the normalised readout runs on the sequential algorithm only");
+    *bytes = dims->N == 0 ? 0 : seq_workspace_bytes(*dims, dims->B * dims->N, true);
+    return IDATTN_OK;
+}
+
+idattn_status idattn_forward_normalized(const idattn_dims* dims, const idattn_params* params, const void* q,
+                                        const void* k, const void* v, void* o, const float* state_in,
+                                        const void* tail_in, const float* eta_in, float* state_out, void* tail_out,
+                                        float* eta_out, void* workspace, size_t workspace_bytes_given, void* stream) {
+    idattn_status st = check_dims(dims, false);
+    if (st != IDATTN_OK) return st;
+    st = check_params(*dims, params);
+    if (st != IDATTN_OK) return st;
+    const idattn_dims& D = *dims;
+    if (D.algo == IDATTN_ALGO_CHUNKED)
+        return fail(IDATTN_ERR_UNSUPPORTED, "the normalised readout runs on the sequential algorithm only");
+    if (D.N > 0 && (!q || !k || !v || !o)) return fail(IDATTN_ERR_NULL, "q, k, v and o must be non-NULL");
+    const size_t need = D.N == 0 ? 0 : seq_workspace_bytes(D, D.B * D.N, true);
+    if (need > 0 && workspace == nullptr) return fail(IDATTN_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+    if (workspace_bytes_given < need)
+        return fail(IDATTN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_given, need);
+    if (misaligned(eta_in) || misaligned(eta_out)) return fail(IDATTN_ERR_ARG, "device buffers must be 16-byte aligned");
+    const size_t io = D.io_dtype == IDATTN_IO_BF16 ? 2 : 4;
+    const size_t act = static_cast<size_t>(D.B) * D.N * D.H * D.d * io;
+    const size_t etab = static_cast<size_t>(D.B) * D.H * D.M * 2 * sizeof(float);
+    const Range rei = range("eta_in", eta_in, etab), reo = range("eta_out", eta_out, etab);
+    // eta_out: an output like the others; it may equal eta_in exactly
+    st = check_forward_buffers(D, *params, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, need, act,
+                               rei);
+    if (st != IDATTN_OK) return st;
+    {
+        const size_t stb = static_cast<size_t>(D.B) * D.H * D.M * 2 * D.d * 2 * sizeof(float);
+        const size_t tlb = static_cast<size_t>(D.B) * D.H * 2 * (D.W - 1) * D.d * io;
+        const Range others[] = {range("q", q, act), range("k", k, act), range("v", v, act), range("o", o, act),
+                                range("state_in", state_in, stb), range("state_out", state_out, stb),
+                                range("tail_in", tail_in, tlb), range("tail_out", tail_out, tlb),
+                                range("workspace", workspace, need), rei};
+        for (const Range& b : others) {
+            if (!overlap(reo, b)) continue;
+            if (b.name == rei.name && reo.lo == b.lo) continue;
+            return fail(IDATTN_ERR_ALIAS, "eta_out overlaps %s", b.name);
+        }
+        st = check_params_disjoint(D, *params, &reo, 1);
+        if (st != IDATTN_OK) return st;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (D.N == 0) {
+        st = copy_through(D, state_in, tail_in, state_out, tail_out, s);
+        if (st != IDATTN_OK || eta_out == nullptr) return st;
+        const hipError_t e = idattn::launch_copy_or_zero(eta_in, eta_out, static_cast<int64_t>(etab / 4), s);
+        if (e != hipSuccess) return hip_fail(e, "eta copy");
+        return IDATTN_OK;
+    }
+    return run_sequential(problem(D), *params, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, s, true,
+                          eta_in, eta_out);
 }
 
 idattn_status idattn_forward_varlen_workspace_size(const idattn_dims* dims, size_t* bytes) {

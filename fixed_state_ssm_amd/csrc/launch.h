@@ -27,15 +27,19 @@ hipError_t launch_featmap_conv_norm(const Problem& p, const idattn_params& prm,
                                     const void* tail_in, float* xi_q, float* z_k,
                                     float* z_v, hipStream_t stream);
 
+// With pden != nullptr (normalised readout) the key scan also carries eta
+// ([B][H][M] complex; eta_in NULL = zeros, eta_out may be NULL or eta_in) and
+// writes each mode's share of the denominator to pden [H][T][M].
 hipError_t launch_ssm_key_scan_seq(const Problem& p, const idattn_params& prm,
                                    const float* xi_q, const float* z_k,
                                    const float* state_in, float* s, float* state_out,
+                                   const float* eta_in, float* eta_out, float* pden,
                                    hipStream_t stream);
 
 hipError_t launch_ssm_value_scan_readout_seq(const Problem& p, const idattn_params& prm,
                                              const float* s, const float* z_v,
                                              const float* state_in, void* o,
-                                             float* state_out, hipStream_t stream);
+                                             float* state_out, const float* pden, hipStream_t stream);
 
 // ---- chunked MFMA path (bf16 I/O)
 size_t chunked_workspace_bytes(const Problem& p);

@@ -4,7 +4,11 @@
 //
 // ssm_key_scan_seq: one wave per (b, h, mode m); lane l owns channels l, l+64
 // of U_m.  Each step updates U_m(i) = abar U_m(i-1) + bbar z_k(i) and reduces
-// s_m(i) = xi_q(i) . U_m(i) over the R channels with a wave butterfly.
+// s_m(i) = xi_q(i) . U_m(i) over the R channels with a wave butterfly.  With
+// the normalised readout (ETA) the wave also carries the mode's normaliser
+// eta_m(i) = abar eta_m(i-1) + bbar and writes Re(s_m(i) eta_m(i)), the mode's
+// share of the denominator; it alone reads and writes eta_m, so eta may be
+// updated in place.
 //
 // ssm_value_scan_readout_seq: one block per (b, h, 64-channel group); wave w
 // owns a contiguous quarter of the modes, lane l one channel, so Gamma_{m,c}
@@ -19,12 +23,14 @@ namespace {
 
 constexpr int kTok = 8;  // tokens whose inputs are loaded ahead of the key recurrence
 
-template <int RJ>
+template <int RJ, bool ETA>
 __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_params prm,
                                                            const float* __restrict__ xi_q,
                                                            const float* __restrict__ z_k,
                                                            const float* state_in,
-                                                           float2* __restrict__ s, float* state_out) {
+                                                           float2* __restrict__ s, float* state_out,
+                                                           const float* eta_in, float* eta_out,
+                                                           float* __restrict__ pden) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t bh = blockIdx.x;
     const int64_t m = static_cast<int64_t>(blockIdx.y) * 4 + (threadIdx.x >> 6);
@@ -54,6 +60,11 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
     const float* xq = xi_q + row0 * d;
     const float* zk = z_k + row0 * d;
     float2* srow = s + row0 * M + m;
+    float er = 0.f, ei = 0.f;  // eta_m, the same in every lane
+    if (ETA && eta_in != nullptr) {
+        er = eta_in[(bh * M + m) * 2];
+        ei = eta_in[(bh * M + m) * 2 + 1];
+    }
     for (int64_t i0 = 0; i0 < N; i0 += kTok) {
         float xv[kTok][RJ], zv[kTok][RJ];
 #pragma unroll
@@ -81,6 +92,13 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
             pr = wave_sum(pr);
             pi = wave_sum(pi);
             if (lane == 0) srow[(i0 + t) * M] = make_float2(pr, pi);
+            if constexpr (ETA) {
+                const float nr = fmaf(ar, er, fmaf(-ai, ei, br));
+                const float ni = fmaf(ar, ei, fmaf(ai, er, bi));
+                er = nr;
+                ei = ni;
+                if (lane == 0) pden[(row0 + i0 + t) * M + m] = fmaf(pr, nr, -pi * ni);
+            }
         }
     }
     if (state_out != nullptr) {
@@ -93,18 +111,26 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
             }
         }
     }
+    if (ETA && eta_out != nullptr && lane == 0) {
+        eta_out[(bh * M + m) * 2] = er;
+        eta_out[(bh * M + m) * 2 + 1] = ei;
+    }
 }
 
 constexpr int kBlk = 16;  // tokens per LDS round of the value scan
 
-template <bool BF16, int MW>
+// ETA: o = numerator / denominator, the denominator summed over the modes
+// from the key scan's per-mode shares pden [H][T][M].
+template <bool BF16, int MW, bool ETA>
 __global__ __launch_bounds__(256) void value_scan_seq_kernel(Problem p, idattn_params prm,
                                                              const float2* __restrict__ s,
                                                              const float* __restrict__ z_v,
                                                              const float* state_in, void* __restrict__ o,
-                                                             float* state_out) {
+                                                             float* state_out, const float* __restrict__ pden) {
     __shared__ float2 s_blk[kBlk * 64];
     __shared__ float red[4][kBlk][kWave];
+    __shared__ float p_blk[ETA ? kBlk * 64 : 1];
+    __shared__ float den_s[4][kBlk];
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x >> 6;
     const int64_t bh = blockIdx.x;
@@ -138,6 +164,8 @@ __global__ __launch_bounds__(256) void value_scan_seq_kernel(Problem p, idattn_p
     for (int64_t i0 = 0; i0 < N; i0 += kBlk) {
         const int nt = static_cast<int>(N - i0 < kBlk ? N - i0 : kBlk);
         for (int e = threadIdx.x; e < nt * M; e += 256) s_blk[e] = s[(row0 + i0) * M + e];
+        if constexpr (ETA)
+            for (int e = threadIdx.x; e < nt * M; e += 256) p_blk[e] = pden[(row0 + i0) * M + e];
         float zz[kBlk];
 #pragma unroll
         for (int t = 0; t < kBlk; ++t) zz[t] = (t < nt && cok) ? zv[(i0 + t) * d + c] : 0.f;
@@ -156,6 +184,12 @@ __global__ __launch_bounds__(256) void value_scan_seq_kernel(Problem p, idattn_p
                     acc = fmaf(sv.x, nr, fmaf(-sv.y, ni, acc));
                 }
                 red[w][t][lane] = acc;
+                if constexpr (ETA) {
+                    float dn = 0.f;
+#pragma unroll
+                    for (int mm = 0; mm < MW; ++mm) dn += p_blk[t * M + w * MW + mm];
+                    if (lane == 0) den_s[w][t] = dn;
+                }
             }
         }
         __syncthreads();
@@ -163,7 +197,8 @@ __global__ __launch_bounds__(256) void value_scan_seq_kernel(Problem p, idattn_p
             const int t = e / kWave, l = e % kWave;
             const int cc = static_cast<int>(blockIdx.y) * kWave + l;
             if (cc < d) {
-                const float sum = (red[0][t][l] + red[1][t][l]) + (red[2][t][l] + red[3][t][l]);
+                float sum = (red[0][t][l] + red[1][t][l]) + (red[2][t][l] + red[3][t][l]);
+                if constexpr (ETA) sum /= (den_s[0][t] + den_s[1][t]) + (den_s[2][t] + den_s[3][t]);
                 store_io<BF16>(o, ((start + i0 + t) * H + h) * d + cc, sum);
             }
         }
@@ -183,28 +218,40 @@ __global__ __launch_bounds__(256) void value_scan_seq_kernel(Problem p, idattn_p
 
 hipError_t launch_ssm_key_scan_seq(const Problem& p, const idattn_params& prm, const float* xi_q,
                                    const float* z_k, const float* state_in, float* s,
-                                   float* state_out, hipStream_t stream) {
+                                   float* state_out, const float* eta_in, float* eta_out, float* pden,
+                                   hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(p.B * p.H), static_cast<unsigned>((p.M + 3) / 4));
     float2* s2 = reinterpret_cast<float2*>(s);
-    if (p.d > 64)
-        key_scan_seq_kernel<2><<<grid, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, s2, state_out);
-    else
-        key_scan_seq_kernel<1><<<grid, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, s2, state_out);
+#define IDATTN_KSCAN(RJ, ETA) \
+    key_scan_seq_kernel<RJ, ETA><<<grid, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, s2, state_out, eta_in, eta_out, pden)
+    if (pden != nullptr) {
+        if (p.d > 64) IDATTN_KSCAN(2, true);
+        else IDATTN_KSCAN(1, true);
+    } else {
+        if (p.d > 64) IDATTN_KSCAN(2, false);
+        else IDATTN_KSCAN(1, false);
+    }
+#undef IDATTN_KSCAN
     return hipGetLastError();
 }
 
 hipError_t launch_ssm_value_scan_readout_seq(const Problem& p, const idattn_params& prm,
                                              const float* s, const float* z_v,
                                              const float* state_in, void* o, float* state_out,
-                                             hipStream_t stream) {
+                                             const float* pden, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(p.B * p.H), static_cast<unsigned>((p.d + kWave - 1) / kWave));
     const float2* s2 = reinterpret_cast<const float2*>(s);
-#define IDATTN_VSCAN(MW)                                                                         \
+#define IDATTN_VSCAN_E(MW, ETA)                                                                  \
     do {                                                                                         \
         if (p.bf16)                                                                              \
-            value_scan_seq_kernel<true, MW><<<grid, 256, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out); \
+            value_scan_seq_kernel<true, MW, ETA><<<grid, 256, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out, pden); \
         else                                                                                     \
-            value_scan_seq_kernel<false, MW><<<grid, 256, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out); \
+            value_scan_seq_kernel<false, MW, ETA><<<grid, 256, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out, pden); \
+    } while (0)
+#define IDATTN_VSCAN(MW)                          \
+    do {                                          \
+        if (pden != nullptr) IDATTN_VSCAN_E(MW, true); \
+        else IDATTN_VSCAN_E(MW, false);           \
     } while (0)
     switch (p.M / 4) {
         case 4: IDATTN_VSCAN(4); break;
@@ -213,6 +260,7 @@ hipError_t launch_ssm_value_scan_readout_seq(const Problem& p, const idattn_para
         default: return hipErrorInvalidValue;
     }
 #undef IDATTN_VSCAN
+#undef IDATTN_VSCAN_E
     return hipGetLastError();
 }
 

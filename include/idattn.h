@@ -159,6 +159,32 @@ idattn_status idattn_forward(const idattn_dims *dims, const idattn_params *param
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Forward with the normalised readout of the derivation (German summary,
+ * "Theoretische Herleitung"; Chinese rendering, Fig. 1: a third in-loop state
+ * eta, M x 1, and the readout F_q U^T Gamma / (F_q U^T eta)), which the
+ * scalable layer drops.  eta is the S4D response to a constant input of one,
+ * with the same abar and bbar as the other channels:
+ *   eta_m(i) = abar_m eta_m(i-1) + bbar_m,
+ *   o_i = Re sum_m s_m(i) Gamma_m(i) / Re sum_m s_m(i) eta_m(i)
+ * (no epsilon: a zero denominator gives Inf or NaN, passed through).
+ *
+ *  eta_in   in   NULL (zeros) or float32 [B][H][M][2] (complex, re, im)
+ *  eta_out  out  NULL or [B][H][M][2]; may equal eta_in exactly (in place)
+ *  all other arguments as for idattn_forward; the workspace is
+ *  idattn_forward_normalized_workspace_size bytes.
+ * dims->algo: AUTO or SEQUENTIAL (CHUNKED returns IDATTN_ERR_UNSUPPORTED).
+ * One token per call from a carried state, tail and eta is the decode step
+ * of this readout.
+ */
+idattn_status idattn_forward_normalized_workspace_size(const idattn_dims *dims, size_t *bytes);
+
+idattn_status idattn_forward_normalized(const idattn_dims *dims, const idattn_params *params,
+                                        const void *q, const void *k, const void *v, void *o,
+                                        const float *state_in, const void *tail_in, const float *eta_in,
+                                        float *state_out, void *tail_out, float *eta_out,
+                                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Packed variable-length batch: dims->B sequences of different lengths laid
  * end to end on one token axis of dims->N = T tokens, each sequence
  * independent of the others with its own state and conv tail.  The

@@ -285,21 +285,24 @@ def forward_normalized(q, k, v, params, eps_feat=1e-6, eps_norm=1e-6, state_in=N
     numerator is the output of forward() above.
 
     eta_in complex [B, H, M] or None (zeros).  Returns (o, state_out,
-    tail_out, eta_out) and, with parts=True, also (num, den) [B, N, H, d] and
-    [B, N, H]."""
+    tail_out, eta_out) and, with parts=True, a fifth element: a dict of num
+    [B, N, H, d], den [B, N, H] and den_abs = sum_m |s_m eta_m| [B, N, H],
+    the size of the terms that the denominator sums (its conditioning)."""
     num, state_out, tail_out, it = forward(q, k, v, params, eps_feat, eps_norm, state_in=state_in,
                                            tail_in=tail_in, intermediates=True, feature_norm=feature_norm)
     B, N, H, _ = num.shape
     M = it["abar"].shape[1]
     eta = np.zeros((B, H, M), dtype=C128) if eta_in is None else np.asarray(eta_in, dtype=C128).copy()
     den = np.empty((B, N, H), dtype=F64)
+    den_abs = np.empty((B, N, H), dtype=F64)
     for i in range(N):
         eta = it["abar"][None] * eta + it["bbar"][None]
         den[:, i] = np.einsum("bhm,bhm->bh", it["s"][:, i], eta).real
+        den_abs[:, i] = np.abs(it["s"][:, i] * eta).sum(-1)
     with np.errstate(divide="ignore", invalid="ignore"):
         o = num / den[..., None]
     if parts:
-        return o, state_out, tail_out, eta, num, den
+        return o, state_out, tail_out, eta, dict(num=num, den=den, den_abs=den_abs)
     return o, state_out, tail_out, eta
 
 

@@ -379,7 +379,8 @@ def pin_eta_kernel_form(O) -> float:
     the constant input 1).  A conjugated product gives another kernel."""
     c = pin_case(N=24)
     p = c["p"]
-    o, _, _, _, num, den = O.forward_normalized(c["q"], c["k"], c["v"], p, tail_in=c["tail"], parts=True)
+    o, _, _, _, pt = O.forward_normalized(c["q"], c["k"], c["v"], p, tail_in=c["tail"], parts=True)
+    num, den = pt["num"], pt["den"]
     _, _, _, it = O.forward(c["q"], c["k"], c["v"], p, 1e-6, 1e-6, None, c["tail"], True)
     B, N, H, d = o.shape
     abar, bbar = O.zoh(p["log_dt"], p["A"], p["Bc"])

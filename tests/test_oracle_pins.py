@@ -96,8 +96,9 @@ def _eta_without_bbar(q, k, v, params, eps_feat=1e-6, eps_norm=1e-6, state_in=No
                       feature_norm="squared", parts=False):
     # the normaliser driven by ones without the input coefficient
     p = dict(params)
-    out = _orig["forward_normalized"](q, k, v, p, eps_feat, eps_norm, state_in, tail_in, eta_in, feature_norm, True)
-    o, st, tl, eta, num, den = out
+    o, st, tl, eta, pt = _orig["forward_normalized"](q, k, v, p, eps_feat, eps_norm, state_in, tail_in, eta_in,
+                                                     feature_norm, True)
+    num, den = pt["num"], pt["den"]
     abar, bbar = O.zoh(p["log_dt"], p["A"], p["Bc"])
     _, _, _, it = O.forward(q, k, v, p, eps_feat, eps_norm, state_in, tail_in, True, feature_norm)
     e = np.zeros_like(eta) if eta_in is None else np.asarray(eta_in, complex).copy()
@@ -106,13 +107,14 @@ def _eta_without_bbar(q, k, v, params, eps_feat=1e-6, eps_norm=1e-6, state_in=No
         e = abar[None] * e + 1.0
         den2[:, i] = np.einsum("bhm,bhm->bh", it["s"][:, i], e).real
     o2 = num / den2[..., None]
-    return (o2, st, tl, e, num, den2) if parts else (o2, st, tl, e)
+    return (o2, st, tl, e, dict(pt, den=den2)) if parts else (o2, st, tl, e)
 
 
 def _eta_conjugated(q, k, v, params, eps_feat=1e-6, eps_norm=1e-6, state_in=None, tail_in=None, eta_in=None,
                     feature_norm="squared", parts=False):
-    o, st, tl, eta, num, den = _orig["forward_normalized"](q, k, v, params, eps_feat, eps_norm, state_in, tail_in,
-                                                           eta_in, feature_norm, True)
+    o, st, tl, eta, pt = _orig["forward_normalized"](q, k, v, params, eps_feat, eps_norm, state_in, tail_in,
+                                                     eta_in, feature_norm, True)
+    num, den = pt["num"], pt["den"]
     abar, bbar = O.zoh(params["log_dt"], params["A"], params["Bc"])
     _, _, _, it = O.forward(q, k, v, params, eps_feat, eps_norm, state_in, tail_in, True, feature_norm)
     e = np.zeros_like(eta) if eta_in is None else np.asarray(eta_in, complex).copy()
@@ -121,7 +123,7 @@ def _eta_conjugated(q, k, v, params, eps_feat=1e-6, eps_norm=1e-6, state_in=None
         e = abar[None] * e + bbar[None]
         den2[:, i] = np.einsum("bhm,bhm->bh", np.conj(it["s"][:, i]), e).real
     o2 = num / den2[..., None]
-    return (o2, st, tl, e, num, den2) if parts else (o2, st, tl, e)
+    return (o2, st, tl, e, dict(pt, den=den2)) if parts else (o2, st, tl, e)
 
 
 def _rms_sum(x, g, b, eps):

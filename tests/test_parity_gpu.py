@@ -201,6 +201,87 @@ def test_decode_step_rff(fs, io, n_tok, name):
     assert np.array_equal(down(tl), tl_ref.astype(np.float32))
 
 
+# The normalised readout o = num / den (eta state).  Its denominator sums terms
+# of both signs and can pass near zero, so o itself is not compared element by
+# element: the gate is the componentwise backward error of the ratio,
+#   |o_gpu den - num| / (|num| + |o_gpu| sum_m |s_m eta_m|),
+# in relative L2 over all outputs.  It is about the rounding unit when o_gpu is
+# the exact ratio of a numerator and denominator each computed with rounding
+# errors of that size, and of order one when the denominator or the numerator
+# is wrong.
+def _eta_backward_error(o_gpu, pt):
+    num, den, den_abs = pt["num"], pt["den"][..., None], pt["den_abs"][..., None]
+    r = o_gpu * den - num
+    scale = np.abs(num) + np.abs(o_gpu) * den_abs
+    return float(np.linalg.norm(r) / np.linalg.norm(scale))
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "d16_m64_w2_f32", "d64_m32_ragged_bf16", "d128_m64_ragged_bf16",
+                                  "d128_m16_f32"])
+def test_forward_normalized(fs, name):
+    import torch
+    base, over, tag = SMALL[name]
+    c = WL.make_case(base, seed=1, tag=tag, **over)
+    s = c.spec
+    io = s["io"]
+    st0, tl0 = WL.make_decode_state(s, seed=2)
+    r = np.random.default_rng(5)
+    eta0 = 0.1 * (r.standard_normal((s["B"], s["H"], s["M"])) + 1j * r.standard_normal((s["B"], s["H"], s["M"])))
+    o_ref, st_ref, tl_ref, eta_ref, pt = oracle.forward_normalized(c.q, c.k, c.v, c.params, state_in=st0,
+                                                                   tail_in=tl0, eta_in=eta0, parts=True)
+    eta_d = torch.from_numpy(np.stack([eta0.real, eta0.imag], -1).astype(np.float32)).cuda()
+    p = fs.params_to_device(c.params)
+    o, st, tl, eta = fs.forward_normalized(up(c.q, io), up(c.k, io), up(c.v, io), p, state_in=state_dev(st0),
+                                           tail_in=up(tl0, io), eta_in=eta_d, return_state=True)
+    _sync()
+    e_o = _eta_backward_error(down(o).astype(np.float64), pt)
+    e_s = rel_l2(state_np(st), st_ref)
+    e_eta = rel_l2(state_np(eta), eta_ref)
+    print(f"normalized {name}: o backward error {e_o:.2e}, state {e_s:.2e}, eta {e_eta:.2e}, "
+          f"den < 0 at {float((pt['den'] < 0).mean()):.3f}", flush=True)
+    assert e_o <= gate(io), e_o
+    assert e_s <= gate(io), e_s
+    assert e_eta <= GATE_F32, e_eta  # eta is fp32 whatever the I/O type
+    assert np.array_equal(down(tl), tl_ref.astype(np.float32))
+    # the numerator is the plain readout: the same call through idattn_forward
+    o_plain = fs.forward(up(c.q, io), up(c.k, io), up(c.v, io), p, state_in=state_dev(st0), tail_in=up(tl0, io),
+                         algo="sequential")
+    _sync()
+    assert rel_l2(down(o_plain), pt["num"]) <= gate(io)
+
+
+def test_forward_normalized_split_and_in_place(fs):
+    """Two calls, the second resumed from the first's state, tail and eta
+    (updated in place), give the one-call result; N = 0 copies eta through."""
+    import torch
+    base, over, tag = SMALL["d128_m64_ragged_bf16"]
+    c = WL.make_case(base, seed=3, tag=tag, **dict(over, io="f32"))
+    s = c.spec
+    p = fs.params_to_device(c.params)
+    q, k, v = up(c.q, "f32"), up(c.k, "f32"), up(c.v, "f32")
+    o_all = fs.forward_normalized(q, k, v, p)
+    n1 = 150
+    o1, st, tl, eta = fs.forward_normalized(q[:, :n1].contiguous(), k[:, :n1].contiguous(), v[:, :n1].contiguous(),
+                                            p, return_state=True)
+    dims = fs.make_dims(s["B"], s["N"] - n1, s["H"], s["d"], s["M"], s["W"], "f32", "auto")
+    nb = fs.idattn_forward_normalized_workspace_size(dims)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    q2, k2, v2 = (x[:, n1:].contiguous() for x in (q, k, v))
+    o2 = torch.empty_like(q2)
+    fs.idattn_forward_normalized(dims, fs.make_params(p), q2, k2, v2, o2, st, tl, eta, st, tl, eta, ws, nb)
+    _sync()
+    got = torch.cat([o1, o2], 1).cpu().numpy()
+    want = o_all.cpu().numpy()
+    assert np.abs(got - want).max() <= 1e-5 * np.abs(want).max() + 1e-30 or rel_l2(got, want) <= 1e-5
+    eta_before = eta.clone()
+    dz = fs.make_dims(s["B"], 0, s["H"], s["d"], s["M"], s["W"], "f32", "auto")
+    eta_out = torch.empty_like(eta)
+    fs.idattn_forward_normalized(dz, fs.make_params(p), None, None, None, None, None, None, eta, None, None, eta_out,
+                                 None, 0)
+    _sync()
+    assert torch.equal(eta_out, eta_before)
+
+
 # Packed variable-length batches: sequences of mixed lengths, some empty and
 # some shorter than the conv history, each from its own state and tail.
 VARLEN_LENS = [37, 0, 1, 200, 2, 64, 130, 0, 5]
