@@ -223,6 +223,43 @@ def varlen_bench(torch, fs, WL, steps=20, warmup=5):
             "ms_per_call": dt * 1e3, "tokens_per_s": T / dt}
 
 
+def normalized_bench(torch, fs, WL, config, steps=20, warmup=5):
+    """The forward with the normalised readout (eta state) at the bench's
+    shape, on the sequential path, which is the one that has it."""
+    import numpy as np
+    s = WL.spec(config)
+    q, k, v = WL.make_rows(s)
+    p = fs.params_to_device(WL.make_params(s))
+    B, N, H, d, M, W = s["B"], s["N"], s["H"], s["d"], s["M"], s["W"]
+
+    def up(x):
+        return torch.from_numpy(WL.bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    qd, kd, vd = up(q), up(k), up(v)
+    o = torch.empty_like(qd)
+    state = torch.empty((B, H, M, 2 * d, 2), dtype=torch.float32, device="cuda")
+    eta = torch.empty((B, H, M, 2), dtype=torch.float32, device="cuda")
+    dims = fs.make_dims(B, N, H, d, M, W, "bf16", "auto")
+    nbytes = fs.idattn_forward_normalized_workspace_size(dims)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    prm = fs.make_params(p)
+
+    def call():
+        fs.idattn_forward_normalized(dims, prm, qd, kd, vd, o, None, None, None, state, None, eta, ws, nbytes)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    return {"workload": f"{config}: B={B} H={H} N={N} d=R={d} M={M} W={W}, bf16 I/O, normalised readout (eta), "
+                        f"sequential fp32 path",
+            "ms_per_call": dt * 1e3, "tokens_per_s": B * N / dt}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -325,6 +362,7 @@ def main():
     if not args.no_decode:
         out["decode"] = decode_bench(torch, fs, steps=20, warmup=20)
         out["varlen"] = varlen_bench(torch, fs, WL)
+        out["normalized"] = normalized_bench(torch, fs, WL, args.config)
     del sets, ws
     torch.cuda.empty_cache()
     if not args.no_cpu:

@@ -161,6 +161,27 @@ int main() {
         expect(var(z, cu, ~size_t{0}, fake(4)), IDATTN_ERR_SHAPE, "varlen T >= 2^31");
     }
 
+    // normalised readout: argument errors
+    {
+        idattn_dims y = dims(2, 64, 3, 64, 32, 4, IDATTN_IO_BF16, IDATTN_ALGO_AUTO);
+        size_t nneed = 0;
+        expect(idattn_forward_normalized_workspace_size(&y, &nneed), IDATTN_OK, "normalized workspace size");
+        auto nor = [&](const idattn_dims& z, size_t ws, const float* ei, float* eo) {
+            return idattn_forward_normalized(&z, &p, fake(1), fake(2), fake(3), fake(4),
+                                             static_cast<const float*>(fake(5)), fake(6), ei,
+                                             static_cast<float*>(fake(7)), fake(8), eo, fake(9), ws, nullptr);
+        };
+        const float* ei = static_cast<const float*>(fake(31));
+        float* eo = static_cast<float*>(fake(32));
+        expect(nor(y, nneed - 1, ei, eo), IDATTN_ERR_WORKSPACE, "normalized workspace one byte short");
+        expect(nor(y, nneed, static_cast<const float*>(fake(31, 8)), eo), IDATTN_ERR_ARG, "misaligned eta_in");
+        expect(nor(y, nneed, ei, static_cast<float*>(fake(31, 16))), IDATTN_ERR_ALIAS, "eta_out partly over eta_in");
+        expect(nor(y, nneed, ei, static_cast<float*>(fake(4, 64))), IDATTN_ERR_ALIAS, "eta_out over o");
+        idattn_dims z = y;
+        z.algo = IDATTN_ALGO_CHUNKED;
+        expect(nor(z, nneed, ei, eo), IDATTN_ERR_UNSUPPORTED, "normalized chunked");
+    }
+
     // decode: 1..8 tokens, argument errors
     {
         idattn_dims y = dims(2, 4, 3, 64, 32, 4, IDATTN_IO_BF16, IDATTN_ALGO_AUTO);

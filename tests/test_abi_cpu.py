@@ -252,3 +252,34 @@ def test_varlen_validation():
     expect(call_varlen(d, p, cu, o=ADDR["q"] + 1000 * 3 * 64 * 2 - 16), "IDATTN_ERR_ALIAS")  # o over q's last row
     expect(call_varlen(d, p, cu, q=0), "IDATTN_ERR_NULL")
     expect(call_varlen(dims(B=5, N=1000, feature_norm="rff"), params(rff_omega=0), cu), "IDATTN_ERR_NULL")
+
+
+def call_normalized(d, p, ws_bytes=None, ei=11 * QB, eo=12 * QB, **over):
+    a = dict(ADDR)
+    a.update(over)
+    if ws_bytes is None:
+        ws_bytes = fs.idattn_forward_normalized_workspace_size(d)
+    lib = fs.load_library()
+    return lib.idattn_forward_normalized(ctypes.byref(d), ctypes.byref(p), a["q"], a["k"], a["v"], a["o"], a["si"],
+                                         a["ti"], ei, a["so"], a["to"], eo, a["ws"], ws_bytes, None)
+
+
+def test_normalized_validation():
+    """The normalised readout: sequential only, a workspace larger than the
+    plain sequential one by the denominator shares, eta buffers aligned and
+    clear of every other buffer (eta_out == eta_in exactly is allowed)."""
+    d = dims(algo="sequential")
+    plain = fs.idattn_forward_workspace_size(d)
+    need = fs.idattn_forward_normalized_workspace_size(d)
+    assert need >= plain + 2 * 64 * 3 * 32 * 4
+    with pytest.raises(fs.IdattnError) as e:
+        fs.idattn_forward_normalized_workspace_size(dims(algo="chunked"))
+    assert e.value.status_name == "IDATTN_ERR_UNSUPPORTED"
+    p = params()
+    expect(call_normalized(d, p, ws_bytes=need - 1), "IDATTN_ERR_WORKSPACE")
+    expect(call_normalized(d, p, ei=11 * QB + 8), "IDATTN_ERR_ARG")
+    expect(call_normalized(d, p, eo=ADDR["o"] + 32), "IDATTN_ERR_ALIAS")        # eta_out over o
+    expect(call_normalized(d, p, eo=11 * QB + 16), "IDATTN_ERR_ALIAS")          # partial overlap with eta_in
+    expect(call_normalized(d, p, ei=ADDR["so"]), "IDATTN_ERR_ALIAS")            # state_out over eta_in
+    expect(call_normalized(d, p, eo=p.A), "IDATTN_ERR_ALIAS")                   # eta_out over a parameter
+    expect(call_normalized(dims(algo="chunked"), p, ws_bytes=1 << 40), "IDATTN_ERR_UNSUPPORTED")
