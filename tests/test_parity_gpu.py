@@ -250,6 +250,28 @@ def test_forward_normalized(fs, name):
     assert rel_l2(down(o_plain), pt["num"]) <= gate(io)
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("feature_norm", ["unit", "rff"])
+def test_forward_normalized_feature_maps(fs, feature_norm, io):
+    import torch
+    base, over, tag = SMALL["d64_m32_ragged_bf16"]
+    c = WL.make_case(base, seed=14, tag=tag, **dict(over, io=io))
+    s = c.spec
+    params = dict(c.params, rff_omega=WL.make_rff_omega(s, seed=15))
+    st0, tl0 = WL.make_decode_state(s, seed=16)
+    o_ref, st_ref, _, eta_ref, pt = oracle.forward_normalized(c.q, c.k, c.v, params, state_in=st0, tail_in=tl0,
+                                                              feature_norm=feature_norm, parts=True)
+    o, st, _, eta = fs.forward_normalized(up(c.q, io), up(c.k, io), up(c.v, io), fs.params_to_device(params),
+                                          state_in=state_dev(st0), tail_in=up(tl0, io), return_state=True,
+                                          feature_norm=feature_norm)
+    _sync()
+    e_o = _eta_backward_error(down(o).astype(np.float64), pt)
+    print(f"normalized {feature_norm} {io}: o backward error {e_o:.2e}", flush=True)
+    assert e_o <= gate(io), e_o
+    assert rel_l2(state_np(st), st_ref) <= gate(io)
+    assert rel_l2(state_np(eta), eta_ref) <= GATE_F32
+
+
 def test_forward_normalized_split_and_in_place(fs):
     """Two calls, the second resumed from the first's state, tail and eta
     (updated in place), give the one-call result; N = 0 copies eta through."""
@@ -318,6 +340,24 @@ def test_forward_varlen(fs, name):
     # an empty sequence passes its state through unchanged
     for b in np.flatnonzero(np.diff(cu) == 0):
         assert np.array_equal(state_np(st)[b], st0[b].astype(np.complex64))
+
+
+@pytest.mark.parametrize("feature_norm", ["unit", "rff"])
+def test_forward_varlen_feature_maps(fs, feature_norm):
+    """Packed batches with the other feature maps (the flag reaches the packed
+    path's feature kernel unchanged)."""
+    import torch
+    c, s, cu, q, k, v, st0, tl0 = _packed_case("d128_m64_ragged_bf16", [70, 0, 3, 150, 1], seed=12)
+    params = dict(c.params, rff_omega=WL.make_rff_omega(s, seed=13))
+    o_ref, st_ref, tl_ref = oracle.forward_varlen(q, k, v, cu, params, state_in=st0, tail_in=tl0,
+                                                  feature_norm=feature_norm)
+    o, st, tl = fs.forward_varlen(up(q, "bf16"), up(k, "bf16"), up(v, "bf16"), fs.params_to_device(params),
+                                  torch.from_numpy(cu).cuda(), state_in=state_dev(st0), tail_in=up(tl0, "bf16"),
+                                  return_state=True, feature_norm=feature_norm)
+    _sync()
+    assert rel_l2(down(o), o_ref) <= GATE_BF16
+    assert rel_l2(state_np(st), st_ref) <= GATE_BF16
+    assert np.array_equal(down(tl), tl_ref.astype(np.float32))
 
 
 def test_forward_varlen_without_state(fs):
