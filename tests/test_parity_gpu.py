@@ -540,6 +540,42 @@ def test_full_config_sampled_pairs(fs, cfg):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("variant", ["unit", "rff", "normalized"])
+def test_full_shape_variants_sampled_pairs(fs, variant):
+    """The feature-map and readout variants at the full 1.3B shape (B=4 H=16
+    N=4096 d=128 M=64, bf16 I/O): unit-norm map on the chunked path, RFF map
+    and normalised readout on the sequential path; the oracle recomputes two
+    (b, h) sequences end to end."""
+    import torch
+    s = WL.spec("1p3b")
+    q, k, v = WL.make_rows(s)
+    params = WL.make_params(s)
+    if variant == "rff":
+        params["rff_omega"] = WL.make_rff_omega(s, seed=1)
+    p = fs.params_to_device(params)
+    qd, kd, vd = up(q, "bf16"), up(k, "bf16"), up(v, "bf16")
+    fn = "squared" if variant == "normalized" else variant
+    if variant == "normalized":
+        o, st, _, eta = fs.forward_normalized(qd, kd, vd, p, return_state=True)
+    else:
+        o, st, _ = fs.forward(qd, kd, vd, p, return_state=True, feature_norm=fn)
+    _sync()
+    for b, h in _pairs(s, 2, seed=11):
+        args = (q[b:b + 1, :, h:h + 1], k[b:b + 1, :, h:h + 1], v[b:b + 1, :, h:h + 1], _head_params(params, h))
+        if variant == "normalized":
+            _, st_ref, _, eta_ref, pt = oracle.forward_normalized(*args, parts=True)
+            e = _eta_backward_error(down(o[b:b + 1, :, h:h + 1]).astype(np.float64), pt)
+            assert rel_l2(state_np(eta[b, h]), eta_ref[0, 0]) <= GATE_F32
+        else:
+            o_ref, st_ref, _ = oracle.forward(*args, feature_norm=fn)
+            e = rel_l2(down(o[b, :, h]), o_ref[0, :, 0])
+        e_s = rel_l2(state_np(st[b, h]), st_ref[0, 0])
+        print(f"1p3b {variant} pair b={b} h={h}: o error {e:.3e} state relL2 {e_s:.3e}", flush=True)
+        assert e <= GATE_BF16 and e_s <= GATE_BF16
+    del o, st
+    torch.cuda.empty_cache()
+
+
 def test_length_statistics_14k(fs):
     """At 3.5x the 4K context the per-head rms of o over 1024-token windows
     is flat after warm-up: max/min over [7168, 14336) <= 1.25 for every head."""
