@@ -9,14 +9,15 @@ binding on the current stream.
 from __future__ import annotations
 
 from .binding import (ALGO, EXPORTS, FEATURE_NORM, IO, LIB_PATH, STATUS, IdattnDims, IdattnError, IdattnParams,
-                      idattn_decode_step, idattn_forward, idattn_forward_normalized,
+                      idattn_decode_step, idattn_decode_step_normalized, idattn_forward,
+                      idattn_forward_normalized,
                       idattn_forward_normalized_workspace_size, idattn_forward_varlen,
                       idattn_forward_varlen_workspace_size, idattn_forward_workspace_size,
                       idattn_last_error, idattn_status_string, idattn_version, load_library,
                       make_dims, make_params)
 
 __all__ = ["ALGO", "EXPORTS", "FEATURE_NORM", "IO", "LIB_PATH", "STATUS", "IdattnDims", "IdattnError", "IdattnParams",
-           "idattn_decode_step", "idattn_forward", "idattn_forward_normalized",
+           "idattn_decode_step", "idattn_decode_step_normalized", "idattn_forward", "idattn_forward_normalized",
            "idattn_forward_normalized_workspace_size", "idattn_forward_varlen", "idattn_forward_varlen_workspace_size",
            "idattn_forward_workspace_size",
            "idattn_last_error", "idattn_status_string", "idattn_version", "load_library",
@@ -128,10 +129,11 @@ def forward_varlen(q, k, v, params: dict, cu_seqlens, *, state_in=None, tail_in=
 
 
 def decode_step(q_t, k_t, v_t, params: dict, state, tail, *, eps_feat=1e-6, eps_norm=1e-6, feature_norm="squared",
-                stream=None):
+                eta=None, stream=None):
     """One token per sequence, q_t, k_t, v_t [B, H, d], or 1..8 tokens,
     [B, N, H, d]; state float32 [B, H, M, 2d, 2] and tail [B, H, 2, W-1, d]
-    are updated in place.  Returns o_t shaped like q_t."""
+    are updated in place.  With eta (float32 [B, H, M, 2], updated in place)
+    the readout is the normalised one.  Returns o_t shaped like q_t."""
     import torch
     if q_t.dim() == 3:
         B, H, d = q_t.shape
@@ -142,5 +144,8 @@ def decode_step(q_t, k_t, v_t, params: dict, state, tail, *, eps_feat=1e-6, eps_
     W = params["conv_q"].shape[-1]
     dims = make_dims(B, N, H, d, M, W, _io_name(q_t), "auto", eps_feat, eps_norm, feature_norm)
     o_t = torch.empty_like(q_t)
-    idattn_decode_step(dims, make_params(params), q_t, k_t, v_t, o_t, state, tail, stream)
+    if eta is None:
+        idattn_decode_step(dims, make_params(params), q_t, k_t, v_t, o_t, state, tail, stream)
+    else:
+        idattn_decode_step_normalized(dims, make_params(params), q_t, k_t, v_t, o_t, state, tail, eta, stream)
     return o_t

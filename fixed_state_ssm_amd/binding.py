@@ -22,7 +22,8 @@ FEATURE_NORM = {"squared": 0, "unit": 1, "rff": 2}
 
 EXPORTS = ("idattn_forward_workspace_size", "idattn_forward", "idattn_forward_normalized_workspace_size",
            "idattn_forward_normalized", "idattn_forward_varlen_workspace_size", "idattn_forward_varlen",
-           "idattn_decode_step", "idattn_status_string", "idattn_last_error", "idattn_version")
+           "idattn_decode_step", "idattn_decode_step_normalized", "idattn_status_string", "idattn_last_error",
+           "idattn_version")
 
 
 class IdattnDims(ctypes.Structure):
@@ -67,6 +68,8 @@ def load_library(path: str = LIB_PATH):
     lib.idattn_forward_varlen_workspace_size.restype = c_int
     lib.idattn_forward_varlen.argtypes = [P(IdattnDims), P(IdattnParams)] + [c_void_p] * 10 + [c_size_t, c_void_p]
     lib.idattn_forward_varlen.restype = c_int
+    lib.idattn_decode_step_normalized.argtypes = [P(IdattnDims), P(IdattnParams)] + [c_void_p] * 8
+    lib.idattn_decode_step_normalized.restype = c_int
     lib.idattn_decode_step.argtypes = [P(IdattnDims), P(IdattnParams)] + [c_void_p] * 7
     lib.idattn_decode_step.restype = c_int
     lib.idattn_status_string.argtypes = [c_int]
@@ -183,3 +186,9 @@ def idattn_decode_step(dims, params, q_t, k_t, v_t, o_t, state, tail, stream=Non
     _check(load_library().idattn_decode_step(
         ctypes.byref(dims), ctypes.byref(params), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(o_t),
         _ptr(state), _ptr(tail), _stream(stream)))
+
+
+def idattn_decode_step_normalized(dims, params, q_t, k_t, v_t, o_t, state, tail, eta, stream=None) -> None:
+    _check(load_library().idattn_decode_step_normalized(
+        ctypes.byref(dims), ctypes.byref(params), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(o_t),
+        _ptr(state), _ptr(tail), _ptr(eta), _stream(stream)))

@@ -414,9 +414,14 @@ idattn_status idattn_forward_varlen(const idattn_dims* dims, const idattn_params
     return run_sequential(p, *params, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, s);
 }
 
-idattn_status idattn_decode_step(const idattn_dims* dims, const idattn_params* params, const void* q_t,
-                                 const void* k_t, const void* v_t, void* o_t, float* state, void* tail,
-                                 void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both decode entry points; eta (normalised readout) is NULL for the plain one.
+idattn_status decode_impl(const idattn_dims* dims, const idattn_params* params, const void* q_t, const void* k_t,
+                          const void* v_t, void* o_t, float* state, void* tail, float* eta, bool normalized,
+                          void* stream) {
     idattn_status st = check_dims(dims, true);
     if (st != IDATTN_OK) return st;
     st = check_params(*dims, params);
@@ -424,8 +429,9 @@ idattn_status idattn_decode_step(const idattn_dims* dims, const idattn_params* p
     const idattn_dims& D = *dims;
     if (!q_t || !k_t || !v_t || !o_t || !state) return fail(IDATTN_ERR_NULL, "q_t, k_t, v_t, o_t and state must be non-NULL");
     if (D.W > 1 && !tail) return fail(IDATTN_ERR_NULL, "tail must be non-NULL when W > 1");
+    if (normalized && !eta) return fail(IDATTN_ERR_NULL, "eta must be non-NULL");
     {
-        const void* ptrs[] = {q_t, k_t, v_t, o_t, state, tail};
+        const void* ptrs[] = {q_t, k_t, v_t, o_t, state, tail, eta};
         for (const void* ptr : ptrs)
             if (misaligned(ptr)) return fail(IDATTN_ERR_ARG, "device buffers must be 16-byte aligned");
     }
@@ -436,21 +442,39 @@ idattn_status idattn_decode_step(const idattn_dims* dims, const idattn_params* p
     const size_t tokb = static_cast<size_t>(D.B) * D.N * D.H * D.d * io;
     const size_t stb = static_cast<size_t>(D.B) * D.H * D.M * 2 * D.d * 2 * sizeof(float);
     const size_t tlb = static_cast<size_t>(D.B) * D.H * 2 * (D.W - 1) * D.d * io;
+    const size_t etab = static_cast<size_t>(D.B) * D.H * D.M * 2 * sizeof(float);
     const Range rq = range("q_t", q_t, tokb), rk = range("k_t", k_t, tokb), rv = range("v_t", v_t, tokb);
     const Range ro = range("o_t", o_t, tokb), rs = range("state", state, stb), rt = range("tail", tail, tlb);
-    const Range outs[] = {ro, rs, rt};
-    const Range all[] = {rq, rk, rv, ro, rs, rt};
+    const Range re = range("eta", normalized ? eta : nullptr, etab);
+    const Range outs[] = {ro, rs, rt, re};
+    const Range all[] = {rq, rk, rv, ro, rs, rt, re};
     for (const Range& a : outs)
         for (const Range& b : all) {
             if (a.name == b.name) continue;
             if (overlap(a, b)) return fail(IDATTN_ERR_ALIAS, "%s overlaps %s", a.name, b.name);
         }
-    st = check_params_disjoint(D, *params, outs, 3);
+    st = check_params_disjoint(D, *params, outs, 4);
     if (st != IDATTN_OK) return st;
     const hipError_t e = idattn::launch_decode_step(problem(D), *params, q_t, k_t, v_t, o_t, state, tail,
-                                                    static_cast<hipStream_t>(stream));
+                                                    normalized ? eta : nullptr, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode_step");
     return IDATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+idattn_status idattn_decode_step(const idattn_dims* dims, const idattn_params* params, const void* q_t,
+                                 const void* k_t, const void* v_t, void* o_t, float* state, void* tail,
+                                 void* stream) {
+    return decode_impl(dims, params, q_t, k_t, v_t, o_t, state, tail, nullptr, false, stream);
+}
+
+idattn_status idattn_decode_step_normalized(const idattn_dims* dims, const idattn_params* params, const void* q_t,
+                                            const void* k_t, const void* v_t, void* o_t, float* state, void* tail,
+                                            float* eta, void* stream) {
+    return decode_impl(dims, params, q_t, k_t, v_t, o_t, state, tail, eta, true, stream);
 }
 
 }  // extern "C"

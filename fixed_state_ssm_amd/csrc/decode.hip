@@ -96,18 +96,21 @@ __device__ __forceinline__ void token_features(const Problem& p, const float* __
 // NT = most tokens of the instance (1, or kDecodeMaxTokens with the call's
 // n = p.N <= NT); FJ = float4 chunks of a state row per lane (d / 64, at least
 // 1); RPW = rows per wave (M / 4); RFF = random Fourier feature map (its own
-// instances, so that the SiLU maps keep their register count).  Tokens are
-// [B][n][H][d].
-template <bool BF16, int NT, int FJ, int RPW, bool RFF>
+// instances, so that the SiLU maps keep their register count); ETA =
+// normalised readout: the wave that owns state row m also carries the mode's
+// normaliser eta_m (updated in place in eta [B][H][M][2]) and sums
+// Re(s_m eta_m) into each token's denominator.  Tokens are [B][n][H][d].
+template <bool BF16, int NT, int FJ, int RPW, bool RFF, bool ETA>
 __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_params prm,
                                                           const void* __restrict__ q_t,
                                                           const void* __restrict__ k_t,
                                                           const void* __restrict__ v_t,
                                                           void* __restrict__ o_t, float* state,
-                                                          void* tail) {
+                                                          void* tail, float* eta) {
     __shared__ float xq_s[NT][128], zk_s[NT][128], zv_s[NT][128];
     __shared__ float4 coef_s[64];
     __shared__ float part_s[4][NT][128];
+    __shared__ float den_s[4][NT];
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x >> 6;
     const int64_t bh = blockIdx.x;
@@ -284,10 +287,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
     // is read once, takes every token's update and readout in turn, and is written
     // once.
     float acc[NT][FJ][2];
+    float den[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t) {
+        den[t] = 0.f;
 #pragma unroll
         for (int j = 0; j < FJ; ++j) acc[t][j][0] = acc[t][j][1] = 0.f;
+    }
 #pragma unroll 1
     for (int rr = 0; rr < RPW; ++rr) {
         const int m = w * RPW + rr;
@@ -298,6 +304,11 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
             row[j] = f < nf ? st4[m * nf + f] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         const float4 cf = coef_s[m];
+        float er = 0.f, ei = 0.f;  // eta_m, the same in every lane
+        if constexpr (ETA) {
+            er = eta[(bh * M + m) * 2];
+            ei = eta[(bh * M + m) * 2 + 1];
+        }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             if (t < n) {
@@ -325,6 +336,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
                 }
                 pr = wave_total(pr);
                 pi = wave_total(pi);
+                if constexpr (ETA) {
+                    const float nr = fmaf(cf.x, er, fmaf(-cf.y, ei, cf.z));
+                    const float ni = fmaf(cf.x, ei, fmaf(cf.y, er, cf.w));
+                    er = nr;
+                    ei = ni;
+                    den[t] = fmaf(pr, nr, fmaf(-pi, ni, den[t]));
+                }
 #pragma unroll
                 for (int j = 0; j < FJ; ++j) {
                     const int f = lane + kWave * j;
@@ -341,6 +359,14 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
             const int f = lane + kWave * j;
             if (f < nf) st4[m * nf + f] = row[j];
         }
+        if (ETA && lane == 0) {
+            eta[(bh * M + m) * 2] = er;
+            eta[(bh * M + m) * 2 + 1] = ei;
+        }
+    }
+    if (ETA && lane == 0) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) den_s[w][t] = den[t];
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -355,7 +381,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
     __syncthreads();
     for (int e = threadIdx.x; e < n * d; e += 256) {
         const int t = e / d, c = e % d;
-        const float sum = (part_s[0][t][c] + part_s[1][t][c]) + (part_s[2][t][c] + part_s[3][t][c]);
+        float sum = (part_s[0][t][c] + part_s[1][t][c]) + (part_s[2][t][c] + part_s[3][t][c]);
+        if constexpr (ETA) sum /= (den_s[0][t] + den_s[1][t]) + (den_s[2][t] + den_s[3][t]);
         store_io<BF16>(o_t, ((b * n + t) * p.H + h) * d + c, sum);
     }
 }
@@ -364,24 +391,26 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
 
 hipError_t launch_decode_step(const Problem& p, const idattn_params& prm, const void* q_t,
                               const void* k_t, const void* v_t, void* o_t, float* state,
-                              void* tail, hipStream_t stream) {
+                              void* tail, float* eta, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(p.B * p.H));
-#define IDATTN_DEC_K(BF, NT, FJ, RPW)                                                                          \
+#define IDATTN_DEC_K(BF, NT, FJ, RPW, ETA)                                                                      \
     do {                                                                                                        \
         if (p.rff_feat)                                                                                         \
-            decode_step_kernel<BF, NT, FJ, RPW, true><<<grid, 256, 0, stream>>>(p, prm, q_t, k_t, v_t, o_t, state, tail);  \
+            decode_step_kernel<BF, NT, FJ, RPW, true, ETA><<<grid, 256, 0, stream>>>(p, prm, q_t, k_t, v_t, o_t, state, tail, eta);  \
         else                                                                                                    \
-            decode_step_kernel<BF, NT, FJ, RPW, false><<<grid, 256, 0, stream>>>(p, prm, q_t, k_t, v_t, o_t, state, tail); \
+            decode_step_kernel<BF, NT, FJ, RPW, false, ETA><<<grid, 256, 0, stream>>>(p, prm, q_t, k_t, v_t, o_t, state, tail, eta); \
     } while (0)
-#define IDATTN_DEC_NT(NT, FJ, RPW)                  \
-    do {                                            \
-        if (p.bf16) IDATTN_DEC_K(true, NT, FJ, RPW);  \
-        else IDATTN_DEC_K(false, NT, FJ, RPW);        \
+#define IDATTN_DEC_NT(NT, FJ, RPW, ETA)                  \
+    do {                                                 \
+        if (p.bf16) IDATTN_DEC_K(true, NT, FJ, RPW, ETA);  \
+        else IDATTN_DEC_K(false, NT, FJ, RPW, ETA);        \
     } while (0)
-#define IDATTN_DEC(FJ, RPW)                                 \
-    do {                                                    \
-        if (p.N == 1) IDATTN_DEC_NT(1, FJ, RPW);            \
-        else IDATTN_DEC_NT(kDecodeMaxTokens, FJ, RPW);      \
+    // the normalised readout has the several-token instances only (any 1..8 tokens)
+#define IDATTN_DEC(FJ, RPW)                                           \
+    do {                                                              \
+        if (eta != nullptr) IDATTN_DEC_NT(kDecodeMaxTokens, FJ, RPW, true); \
+        else if (p.N == 1) IDATTN_DEC_NT(1, FJ, RPW, false);          \
+        else IDATTN_DEC_NT(kDecodeMaxTokens, FJ, RPW, false);         \
     } while (0)
     const int fj = p.d > 64 ? 2 : 1;
     const int rpw = static_cast<int>(p.M / 4);

@@ -66,8 +66,9 @@ hipError_t launch_copy_or_zero(const void* src, void* dst, int64_t n_words, hipS
 
 // ---- decode (1 .. kDecodeMaxTokens tokens per sequence, [B][N][H][d])
 constexpr int kDecodeMaxTokens = 8;
+// eta != nullptr: normalised readout, eta [B][H][M] complex updated in place.
 hipError_t launch_decode_step(const Problem& p, const idattn_params& prm,
                               const void* q_t, const void* k_t, const void* v_t, void* o_t,
-                              float* state, void* tail, hipStream_t stream);
+                              float* state, void* tail, float* eta, hipStream_t stream);
 
 }  // namespace idattn

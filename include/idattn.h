@@ -235,6 +235,17 @@ idattn_status idattn_decode_step(const idattn_dims *dims, const idattn_params *p
                                  const void *q_t, const void *k_t, const void *v_t, void *o_t,
                                  float *state, void *tail, void *stream);
 
+/*
+ * Decode steps with the normalised readout (see idattn_forward_normalized):
+ * the same result as idattn_forward_normalized over these 1..8 tokens from
+ * the carried state, tail and eta.
+ *  eta  in/out  float32 [B][H][M][2] (complex), updated in place; non-NULL
+ * Other arguments and rules as for idattn_decode_step.
+ */
+idattn_status idattn_decode_step_normalized(const idattn_dims *dims, const idattn_params *params,
+                                            const void *q_t, const void *k_t, const void *v_t, void *o_t,
+                                            float *state, void *tail, float *eta, void *stream);
+
 /* Static text for a status code ("IDATTN_OK", ...). */
 const char *idattn_status_string(idattn_status status);
 

@@ -283,3 +283,21 @@ def test_normalized_validation():
     expect(call_normalized(d, p, ei=ADDR["so"]), "IDATTN_ERR_ALIAS")            # state_out over eta_in
     expect(call_normalized(d, p, eo=p.A), "IDATTN_ERR_ALIAS")                   # eta_out over a parameter
     expect(call_normalized(dims(algo="chunked"), p, ws_bytes=1 << 40), "IDATTN_ERR_UNSUPPORTED")
+
+
+def test_decode_normalized_validation():
+    lib = fs.load_library()
+    p = params()
+    d = dims(N=2)
+
+    def dec(**over):
+        a = dict(q=QB, k=2 * QB, v=3 * QB, o=4 * QB, s=5 * QB, t=6 * QB, e=11 * QB)
+        a.update(over)
+        return lib.idattn_decode_step_normalized(ctypes.byref(d), ctypes.byref(p), a["q"], a["k"], a["v"], a["o"],
+                                                 a["s"], a["t"], a["e"], None)
+
+    expect(dec(e=None), "IDATTN_ERR_NULL")
+    expect(dec(e=11 * QB + 8), "IDATTN_ERR_ARG")
+    expect(dec(e=5 * QB + 64), "IDATTN_ERR_ALIAS")   # eta inside the state
+    expect(dec(o=11 * QB), "IDATTN_ERR_ALIAS")       # o_t over eta
+    expect(dec(e=p.Bc), "IDATTN_ERR_ALIAS")          # eta over a parameter

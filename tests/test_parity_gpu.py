@@ -272,6 +272,34 @@ def test_forward_normalized_feature_maps(fs, feature_norm, io):
     assert rel_l2(state_np(eta), eta_ref) <= GATE_F32
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("n_tok", [1, 3, 8])
+@pytest.mark.parametrize("name", ["d128_m64_ragged_bf16", "d32_m16_bf16"])
+def test_decode_step_normalized(fs, name, n_tok, io):
+    """Decode with the normalised readout against the oracle's normalised
+    forward over those tokens from the same state, tail and eta."""
+    import torch
+    base, over, tag = SMALL[name]
+    c = WL.make_case(base, seed=17, tag=tag, **dict(over, io=io))
+    s = c.spec
+    st0, tl0 = WL.make_decode_state(s, seed=18)
+    r = np.random.default_rng(19)
+    eta0 = 0.5 * (r.standard_normal((s["B"], s["H"], s["M"])) + 1j * r.standard_normal((s["B"], s["H"], s["M"])))
+    q, k, v = (x[:, :n_tok] for x in (c.q, c.k, c.v))
+    _, st_ref, tl_ref, eta_ref, pt = oracle.forward_normalized(q, k, v, c.params, state_in=st0, tail_in=tl0,
+                                                               eta_in=eta0, parts=True)
+    st, tl = state_dev(st0), up(tl0, io)
+    eta = torch.from_numpy(np.stack([eta0.real, eta0.imag], -1).astype(np.float32)).cuda()
+    ot = fs.decode_step(up(q, io), up(k, io), up(v, io), fs.params_to_device(c.params), st, tl, eta=eta)
+    _sync()
+    e_o = _eta_backward_error(down(ot).astype(np.float64), pt)
+    print(f"normalized decode {name} {io} n={n_tok}: o backward error {e_o:.2e}", flush=True)
+    assert e_o <= gate(io), e_o
+    assert rel_l2(state_np(st), st_ref) <= gate(io)
+    assert rel_l2(state_np(eta), eta_ref) <= GATE_F32
+    assert np.array_equal(down(tl), tl_ref.astype(np.float32))
+
+
 def test_forward_normalized_split_and_in_place(fs):
     """Two calls, the second resumed from the first's state, tail and eta
     (updated in place), give the one-call result; N = 0 copies eta through."""
