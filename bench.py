@@ -173,10 +173,25 @@ def decode_bench(torch, fs, steps, warmup):
         ms_m = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
         med_m = ms_m[len(ms_m) // 2]
         multi[f"tokens_{NT}"] = {"ms_per_call_median": med_m, "tokens_per_s": B * NT / (med_m * 1e-3)}
+    # the normalised readout: one token per sequence, eta carried in place
+    eta = torch.zeros((B, H, M, 2), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        fs.idattn_decode_step_normalized(dims, prm, tok[0], tok[1], tok[2], o_t, state, tail, eta)
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record()
+        fs.idattn_decode_step_normalized(dims, prm, tok[0], tok[1], tok[2], o_t, state, tail, eta)
+        e1.record()
+    torch.cuda.synchronize()
+    ms_n = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    med_n = ms_n[len(ms_n) // 2]
+    normalized = {"path": "idattn_decode_step_normalized, one token per sequence, eta in place",
+                  "ms_per_step_median": med_n, "tokens_per_s": B / (med_n * 1e-3)}
     return {"workload": "decode: 256 sequences x 16 heads, d=R=128, M=64, W=4, bf16 I/O, fp32 state "
                         "prefilled by a 2048-token forward",
             "tokens_per_s": B / (med * 1e-3), "ms_per_step_median": med,
             "multi_token": dict(multi, path="idattn_decode_step with several tokens per sequence, state and tail in place"),
+            "normalized": normalized,
             "roofline": {"bound": "hbm", "achieved": nbytes / (med * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                          "algorithmic_bytes": nbytes}}
