@@ -200,8 +200,9 @@ def decode_bench(torch, fs, steps, warmup):
 def varlen_bench(torch, fs, WL, steps=20, warmup=5):
     """Packed variable-length batch at the 1.3B head shape (H=16, d=128, M=64,
     W=4, bf16): 16 384 tokens in 8 sequences of mixed lengths (long prompts
-    beside short ones), on the sequential path, which is the one that takes
-    packed batches."""
+    beside short ones).  With the lengths also on the host the library runs
+    one chunked forward per sequence; with the device table alone, the
+    sequential path."""
     import numpy as np
     lens = [6000, 3500, 2500, 2048, 1200, 700, 400, 36]
     s = WL.spec("1p3b", B=1, N=sum(lens), tag=90)
@@ -215,27 +216,36 @@ def varlen_bench(torch, fs, WL, steps=20, warmup=5):
 
     qd, kd, vd = up(q), up(k), up(v)
     o = torch.empty_like(qd)
-    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+    cu_host = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cu = torch.from_numpy(cu_host).cuda()
     state = torch.zeros((B, H, M, 2 * d, 2), dtype=torch.float32, device="cuda")
     tail = torch.zeros((B, H, 2, W - 1, d), dtype=torch.bfloat16, device="cuda")
     dims = fs.make_dims(B, T, H, d, M, W, "bf16", "auto")
     nbytes = fs.idattn_forward_varlen_workspace_size(dims)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
 
-    def call():
-        fs.idattn_forward_varlen(dims, prm, cu, qd, kd, vd, o, None, None, state, tail, ws, nbytes)
+    def timed(host):
+        def call():
+            fs.idattn_forward_varlen(dims, prm, cu, qd, kd, vd, o, None, None, state, tail, ws, nbytes,
+                                     cu_seqlens_host=host)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        call()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / steps
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    dt = timed(cu_host)
+    dt_seq = timed(None)
     return {"workload": f"packed batch: {B} sequences, lengths {lens} (T={T}), H={H} d=R={d} M={M} W={W}, "
-                        f"bf16 I/O, sequential fp32 path",
-            "ms_per_call": dt * 1e3, "tokens_per_s": T / dt}
+                        f"bf16 I/O",
+            "ms_per_call": dt * 1e3, "tokens_per_s": T / dt,
+            "path": "host lengths given: one chunked forward per sequence",
+            "sequential": {"ms_per_call": dt_seq * 1e3, "tokens_per_s": T / dt_seq,
+                           "path": "device table only: sequential fp32 path"}}
 
 
 def normalized_bench(torch, fs, WL, config, steps=20, warmup=5):

@@ -99,12 +99,15 @@ def forward_normalized(q, k, v, params: dict, *, state_in=None, tail_in=None, et
 
 
 def forward_varlen(q, k, v, params: dict, cu_seqlens, *, state_in=None, tail_in=None, return_state=False,
-                   algo="auto", eps_feat=1e-6, eps_norm=1e-6, feature_norm="squared", stream=None):
+                   algo="auto", eps_feat=1e-6, eps_norm=1e-6, feature_norm="squared", stream=None,
+                   host_lengths=True):
     """o = mixer over a packed batch: q, k, v [T, H, d] on the GPU hold B
     sequences end to end, sequence b being tokens cu_seqlens[b] ..
     cu_seqlens[b+1]-1 (cu_seqlens: int32 device tensor [B + 1]).  state_in
-    [B, H, M, 2d, 2] and tail_in [B, H, 2, W-1, d] or None.  With
-    return_state=True returns (o, state_out, tail_out)."""
+    [B, H, M, 2d, 2] and tail_in [B, H, 2, W-1, d] or None.  host_lengths
+    also hands a host copy of the table to the library (one device-to-host
+    copy), which lets it run the chunked algorithm.  With return_state=True
+    returns (o, state_out, tail_out)."""
     import torch
     T, H, d = q.shape
     B = cu_seqlens.shape[0] - 1
@@ -123,8 +126,9 @@ def forward_varlen(q, k, v, params: dict, cu_seqlens, *, state_in=None, tail_in=
     if return_state:
         state_out = torch.empty((B, H, M, 2 * d, 2), dtype=torch.float32, device=q.device)
         tail_out = torch.empty((B, H, 2, W - 1, d), dtype=q.dtype, device=q.device)
+    host = cu_seqlens.cpu().tolist() if host_lengths else None
     idattn_forward_varlen(dims, make_params(params), cu_seqlens, q, k, v, o, state_in, tail_in, state_out, tail_out,
-                          ws, nbytes, stream)
+                          ws, nbytes, stream, cu_seqlens_host=host)
     return (o, state_out, tail_out) if return_state else o
 
 

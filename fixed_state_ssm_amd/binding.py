@@ -66,7 +66,7 @@ def load_library(path: str = LIB_PATH):
     lib.idattn_forward_normalized.restype = c_int
     lib.idattn_forward_varlen_workspace_size.argtypes = [P(IdattnDims), P(c_size_t)]
     lib.idattn_forward_varlen_workspace_size.restype = c_int
-    lib.idattn_forward_varlen.argtypes = [P(IdattnDims), P(IdattnParams)] + [c_void_p] * 10 + [c_size_t, c_void_p]
+    lib.idattn_forward_varlen.argtypes = [P(IdattnDims), P(IdattnParams)] + [c_void_p] * 11 + [c_size_t, c_void_p]
     lib.idattn_forward_varlen.restype = c_int
     lib.idattn_decode_step_normalized.argtypes = [P(IdattnDims), P(IdattnParams)] + [c_void_p] * 8
     lib.idattn_decode_step_normalized.restype = c_int
@@ -175,9 +175,15 @@ def idattn_forward_varlen_workspace_size(dims: IdattnDims) -> int:
 
 
 def idattn_forward_varlen(dims, params, cu_seqlens, q, k, v, o, state_in=None, tail_in=None, state_out=None,
-                          tail_out=None, workspace=None, workspace_bytes=0, stream=None) -> None:
+                          tail_out=None, workspace=None, workspace_bytes=0, stream=None, cu_seqlens_host=None) -> None:
+    """cu_seqlens: device int32 table (tensor or address) or None; cu_seqlens_host:
+    None or a host copy (sequence of ints), which lets the chunked algorithm run."""
+    host = None
+    if cu_seqlens_host is not None:
+        vals = [int(x) for x in cu_seqlens_host]
+        host = (ctypes.c_int32 * len(vals))(*vals)
     _check(load_library().idattn_forward_varlen(
-        ctypes.byref(dims), ctypes.byref(params), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+        ctypes.byref(dims), ctypes.byref(params), _ptr(cu_seqlens), host, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
         _ptr(state_in), _ptr(tail_in), _ptr(state_out), _ptr(tail_out), _ptr(workspace),
         int(workspace_bytes), _stream(stream)))
 

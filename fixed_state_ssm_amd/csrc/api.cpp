@@ -371,32 +371,71 @@ idattn_status idattn_forward_normalized(const idattn_dims* dims, const idattn_pa
                           eta_in, eta_out);
 }
 
+// The chunked algorithm runs a packed batch one sequence at a time (B = 1
+// launches on the caller's stream); its workspace for any sequence of at most
+// T tokens is bounded by that of T + 16 chunks (at most 16 segments of whole
+// chunks cover N tokens with less than 16 chunks to spare).
+bool varlen_chunked_possible(const idattn_dims& D) {
+    idattn::Problem p = problem(D);
+    p.B = 1;
+    p.N = D.N + 1024;
+    return D.io_dtype == IDATTN_IO_BF16 && idattn::chunked_supported(p);
+}
+
+size_t varlen_chunked_bound(const idattn_dims& D) {
+    idattn::Problem p = problem(D);
+    p.B = 1;
+    p.N = D.N + 1024;
+    p.T = p.N;
+    return idattn::chunked_workspace_bytes(p);
+}
+
+size_t varlen_workspace(const idattn_dims& D) {
+    if (D.N == 0) return 0;
+    size_t bytes = seq_workspace_bytes(D, D.N);
+    if (D.algo != IDATTN_ALGO_SEQUENTIAL && varlen_chunked_possible(D)) {
+        const size_t c = varlen_chunked_bound(D);
+        if (c > bytes) bytes = c;
+    }
+    return bytes;
+}
+
 idattn_status idattn_forward_varlen_workspace_size(const idattn_dims* dims, size_t* bytes) {
     if (bytes == nullptr) return fail(IDATTN_ERR_NULL, "bytes is NULL");
     idattn_status st = check_dims(dims, false);
     if (st != IDATTN_OK) return st;
-    if (dims->algo == IDATTN_ALGO_CHUNKED)
-        return fail(IDATTN_ERR_UNSUPPORTED, "packed batches run on the sequential algorithm only");
-    *bytes = dims->N == 0 ? 0 : seq_workspace_bytes(*dims, dims->N);
+    if (dims->algo == IDATTN_ALGO_CHUNKED && !varlen_chunked_possible(*dims))
+        return fail(IDATTN_ERR_UNSUPPORTED, "the chunked algorithm has no kernel for these dims");
+    *bytes = varlen_workspace(*dims);
     return IDATTN_OK;
 }
 
 idattn_status idattn_forward_varlen(const idattn_dims* dims, const idattn_params* params, const int32_t* cu_seqlens,
-                                    const void* q, const void* k, const void* v, void* o, const float* state_in,
-                                    const void* tail_in, float* state_out, void* tail_out, void* workspace,
-                                    size_t workspace_bytes_given, void* stream) {
+                                    const int32_t* cu_seqlens_host, const void* q, const void* k, const void* v,
+                                    void* o, const float* state_in, const void* tail_in, float* state_out,
+                                    void* tail_out, void* workspace, size_t workspace_bytes_given, void* stream) {
     idattn_status st = check_dims(dims, false);
     if (st != IDATTN_OK) return st;
     st = check_params(*dims, params);
     if (st != IDATTN_OK) return st;
     const idattn_dims& D = *dims;
-    if (D.algo == IDATTN_ALGO_CHUNKED)
-        return fail(IDATTN_ERR_UNSUPPORTED, "packed batches run on the sequential algorithm only");
     if (D.N > 0x7fffffffLL) return fail(IDATTN_ERR_SHAPE, "N=%lld: a packed batch holds < 2^31 tokens", (long long)D.N);
-    if (cu_seqlens == nullptr) return fail(IDATTN_ERR_NULL, "cu_seqlens is NULL");
+    // the chunked plan needs the lengths on the host; the sequential path reads the device table
+    const bool chunked = cu_seqlens_host != nullptr && D.algo != IDATTN_ALGO_SEQUENTIAL && varlen_chunked_possible(D);
+    if (D.algo == IDATTN_ALGO_CHUNKED && !chunked)
+        return fail(IDATTN_ERR_UNSUPPORTED, cu_seqlens_host ? "the chunked algorithm has no kernel for these dims"
+                                                            : "the chunked algorithm needs cu_seqlens_host");
+    if (!chunked && cu_seqlens == nullptr) return fail(IDATTN_ERR_NULL, "cu_seqlens is NULL");
     if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return fail(IDATTN_ERR_ARG, "cu_seqlens must be 4-byte aligned");
+    if (cu_seqlens_host != nullptr) {
+        if (cu_seqlens_host[0] != 0 || cu_seqlens_host[D.B] != D.N)
+            return fail(IDATTN_ERR_SHAPE, "cu_seqlens_host must run from 0 to N=%lld", (long long)D.N);
+        for (int64_t b = 0; b < D.B; ++b)
+            if (cu_seqlens_host[b + 1] < cu_seqlens_host[b])
+                return fail(IDATTN_ERR_SHAPE, "cu_seqlens_host decreases at %lld", (long long)b);
+    }
     if (D.N > 0 && (!q || !k || !v || !o)) return fail(IDATTN_ERR_NULL, "q, k, v and o must be non-NULL");
-    const size_t need = D.N == 0 ? 0 : seq_workspace_bytes(D, D.N);
+    const size_t need = varlen_workspace(D);
     if (need > 0 && workspace == nullptr) return fail(IDATTN_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
     if (workspace_bytes_given < need)
         return fail(IDATTN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_given, need);
@@ -408,10 +447,38 @@ idattn_status idattn_forward_varlen(const idattn_dims* dims, const idattn_params
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (D.N == 0) return copy_through(D, state_in, tail_in, state_out, tail_out, s);
-    idattn::Problem p = problem(D);
-    p.T = D.N;
-    p.cu = cu_seqlens;
-    return run_sequential(p, *params, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, s);
+    if (!chunked) {
+        idattn::Problem p = problem(D);
+        p.T = D.N;
+        p.cu = cu_seqlens;
+        return run_sequential(p, *params, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, s);
+    }
+    // one B = 1 chunked forward per sequence, pointers offset to its rows
+    const size_t row_state = static_cast<size_t>(D.H) * D.M * 2 * D.d * 2;  // floats
+    const size_t row_tail = static_cast<size_t>(D.H) * 2 * (D.W - 1) * D.d * io;  // bytes
+    const size_t tok = static_cast<size_t>(D.H) * D.d * io;  // bytes per token
+    for (int64_t b = 0; b < D.B; ++b) {
+        const int64_t n = cu_seqlens_host[b + 1] - cu_seqlens_host[b];
+        const size_t t0 = static_cast<size_t>(cu_seqlens_host[b]) * tok;
+        const float* si = state_in ? state_in + b * row_state : nullptr;
+        float* so = state_out ? state_out + b * row_state : nullptr;
+        const void* ti = tail_in ? static_cast<const char*>(tail_in) + b * row_tail : nullptr;
+        void* to = tail_out ? static_cast<char*>(tail_out) + b * row_tail : nullptr;
+        idattn_dims one = D;
+        one.B = 1;
+        one.N = n;
+        if (n == 0) {
+            st = copy_through(one, si, ti, so, to, s);
+            if (st != IDATTN_OK) return st;
+            continue;
+        }
+        const idattn::Problem p = problem(one);
+        const hipError_t e = idattn::launch_forward_chunked(
+            p, *params, static_cast<const char*>(q) + t0, static_cast<const char*>(k) + t0,
+            static_cast<const char*>(v) + t0, static_cast<char*>(o) + t0, si, ti, so, to, workspace, s);
+        if (e != hipSuccess) return hip_fail(e, "chunked forward (packed batch)");
+    }
+    return IDATTN_OK;
 }
 
 }  // extern "C"

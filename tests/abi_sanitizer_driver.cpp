@@ -146,8 +146,9 @@ int main() {
         expect(idattn_forward_varlen_workspace_size(&y, &vneed), IDATTN_OK, "varlen workspace size");
         const int32_t* cu = static_cast<const int32_t*>(fake(30));
         auto var = [&](const idattn_dims& z, const int32_t* c, size_t ws, void* o) {
-            return idattn_forward_varlen(&z, &p, c, fake(1), fake(2), fake(3), o, static_cast<const float*>(fake(5)),
-                                         fake(6), static_cast<float*>(fake(7)), fake(8), fake(9), ws, nullptr);
+            return idattn_forward_varlen(&z, &p, c, nullptr, fake(1), fake(2), fake(3), o,
+                                         static_cast<const float*>(fake(5)), fake(6), static_cast<float*>(fake(7)),
+                                         fake(8), fake(9), ws, nullptr);
         };
         expect(var(y, nullptr, vneed, fake(4)), IDATTN_ERR_NULL, "NULL cu_seqlens");
         expect(var(y, static_cast<const int32_t*>(fake(30, 2)), vneed, fake(4)), IDATTN_ERR_ARG, "misaligned cu_seqlens");
@@ -159,6 +160,11 @@ int main() {
         z = y;
         z.N = int64_t{1} << 31;
         expect(var(z, cu, ~size_t{0}, fake(4)), IDATTN_ERR_SHAPE, "varlen T >= 2^31");
+        const int32_t bad_host[6] = {0, 100, 50, 600, 900, 1000};
+        expect(idattn_forward_varlen(&y, &p, cu, bad_host, fake(1), fake(2), fake(3), fake(4),
+                                     static_cast<const float*>(fake(5)), fake(6), static_cast<float*>(fake(7)),
+                                     fake(8), fake(9), vneed, nullptr),
+               IDATTN_ERR_SHAPE, "decreasing cu_seqlens_host");
     }
 
     // normalised readout: argument errors

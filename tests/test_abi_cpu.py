@@ -225,8 +225,9 @@ def call_varlen(d, p, cu, ws_bytes=None, **over):
     if ws_bytes is None:
         ws_bytes = fs.idattn_forward_varlen_workspace_size(d)
     lib = fs.load_library()
-    return lib.idattn_forward_varlen(ctypes.byref(d), ctypes.byref(p), cu, a["q"], a["k"], a["v"], a["o"], a["si"],
-                                     a["ti"], a["so"], a["to"], a["ws"], ws_bytes, None)
+    host = over.get("host")
+    return lib.idattn_forward_varlen(ctypes.byref(d), ctypes.byref(p), cu, host, a["q"], a["k"], a["v"], a["o"],
+                                     a["si"], a["ti"], a["so"], a["to"], a["ws"], ws_bytes, None)
 
 
 def test_varlen_validation():
@@ -252,6 +253,25 @@ def test_varlen_validation():
     expect(call_varlen(d, p, cu, o=ADDR["q"] + 1000 * 3 * 64 * 2 - 16), "IDATTN_ERR_ALIAS")  # o over q's last row
     expect(call_varlen(d, p, cu, q=0), "IDATTN_ERR_NULL")
     expect(call_varlen(dims(B=5, N=1000, feature_norm="rff"), params(rff_omega=0), cu), "IDATTN_ERR_NULL")
+
+
+def test_varlen_host_lengths_validation():
+    """With a host copy of the lengths the chunked plan becomes possible; the
+    copy is checked on the host, and CHUNKED without it is refused."""
+    d = dims(B=3, N=1000, M=64, d=128)
+    cu = 10 * QB
+    p = params()
+    ok = (ctypes.c_int32 * 4)(0, 10, 10, 1000)
+    chunked = fs.idattn_forward_varlen_workspace_size(dims(B=3, N=1000, M=64, d=128, algo="chunked"))
+    seq = fs.idattn_forward_varlen_workspace_size(dims(B=3, N=1000, M=64, d=128, algo="sequential"))
+    assert fs.idattn_forward_varlen_workspace_size(d) == max(chunked, seq)
+    for bad in ((1, 10, 10, 1000), (0, 10, 5, 1000), (0, 10, 10, 999)):
+        expect(call_varlen(d, p, cu, host=(ctypes.c_int32 * 4)(*bad)), "IDATTN_ERR_SHAPE")
+    expect(call_varlen(dims(B=3, N=1000, M=64, d=128, algo="chunked"), p, cu, ws_bytes=1 << 40),
+           "IDATTN_ERR_UNSUPPORTED")                                        # no host lengths
+    expect(call_varlen(dims(B=3, N=1000, M=32, d=128, algo="chunked"), p, cu, ws_bytes=1 << 40, host=ok),
+           "IDATTN_ERR_UNSUPPORTED")                                        # no kernel for M = 32
+    expect(call_varlen(d, p, None, host=ok, ws_bytes=1), "IDATTN_ERR_WORKSPACE")  # device table optional here
 
 
 def call_normalized(d, p, ws_bytes=None, ei=11 * QB, eo=12 * QB, **over):

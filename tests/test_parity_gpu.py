@@ -347,9 +347,13 @@ def _packed_case(name, lens, seed, tag_off=0):
     return c, s, cu, c.q[0, :T], c.k[0, :T], c.v[0, :T], st0, tl0
 
 
+# With the lengths also on the host, shapes the chunked kernels take (bf16,
+# d = 64 or 128, M = 64, W <= 4) run one chunked forward per sequence; the
+# others, and every case without host lengths, run the sequential path.
+@pytest.mark.parametrize("host_lengths", [False, True], ids=["device_table", "host_lengths"])
 @pytest.mark.parametrize("name", ["tiny_f32", "d16_m64_w2_f32", "d64_m32_ragged_bf16", "d128_m64_ragged_bf16",
-                                  "d128_w8_bf16"])
-def test_forward_varlen(fs, name):
+                                  "d128_w8_bf16", "d64_w1_bf16"])
+def test_forward_varlen(fs, name, host_lengths):
     import torch
     c, s, cu, q, k, v, st0, tl0 = _packed_case(name, VARLEN_LENS, seed=7)
     io = s["io"]
@@ -357,11 +361,12 @@ def test_forward_varlen(fs, name):
     p = fs.params_to_device(c.params)
     cu_d = torch.from_numpy(cu).cuda()
     o, st, tl = fs.forward_varlen(up(q, io), up(k, io), up(v, io), p, cu_d, state_in=state_dev(st0),
-                                  tail_in=up(tl0, io), return_state=True)
+                                  tail_in=up(tl0, io), return_state=True, host_lengths=host_lengths)
     _sync()
     e_o = rel_l2(down(o), o_ref)
     e_s = rel_l2(state_np(st), st_ref)
-    print(f"varlen {name} T={int(cu[-1])} B={len(cu) - 1}: o relL2 {e_o:.2e}, state relL2 {e_s:.2e}", flush=True)
+    print(f"varlen {name} host={host_lengths} T={int(cu[-1])} B={len(cu) - 1}: o relL2 {e_o:.2e}, "
+          f"state relL2 {e_s:.2e}", flush=True)
     assert e_o <= gate(io), e_o
     assert e_s <= gate(io), e_s
     assert np.array_equal(down(tl), tl_ref.astype(np.float32))
@@ -401,12 +406,13 @@ def test_forward_varlen_without_state(fs):
     assert np.array_equal(down(tl), tl_ref.astype(np.float32))
 
 
-@pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_forward_varlen_matches_dense_at_scale(fs, io):
+@pytest.mark.parametrize("io,algo", [("f32", "sequential"), ("bf16", "sequential"), ("bf16", "chunked")])
+def test_forward_varlen_matches_dense_at_scale(fs, io, algo):
     """At the 1.3B head shape (H = 16, d = 128, M = 64) with 9 400 packed tokens:
-    every sequence of the packed call gives bit for bit what the dense
-    sequential forward gives for that sequence alone (the same kernels in the
-    same order; the dense path is itself compared with the oracle)."""
+    every sequence of the packed call gives bit for bit what the dense forward
+    of the same algorithm gives for that sequence alone (the same kernels in
+    the same order; the dense paths are themselves compared with the oracle).
+    The chunked plan needs the lengths on the host."""
     import torch
     lens = [4096, 1, 3000, 0, 17, 2286]
     s = WL.spec("1p3b", B=1, N=sum(lens), io=io, tag=81)
@@ -417,11 +423,12 @@ def test_forward_varlen_matches_dense_at_scale(fs, io):
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     qd, kd, vd = up(q[0], io), up(k[0], io), up(v[0], io)
     o, st, tl = fs.forward_varlen(qd, kd, vd, p, torch.from_numpy(cu).cuda(), state_in=state_dev(st0),
-                                  tail_in=up(tl0, io), return_state=True)
+                                  tail_in=up(tl0, io), return_state=True, algo=algo,
+                                  host_lengths=algo == "chunked")
     stb, tlb = state_dev(st0), up(tl0, io)
     for b, n in enumerate(lens):
         sl = slice(int(cu[b]), int(cu[b + 1]))
-        ob, sb, tb = fs.forward(qd[None, sl], kd[None, sl], vd[None, sl], p, algo="sequential",
+        ob, sb, tb = fs.forward(qd[None, sl], kd[None, sl], vd[None, sl], p, algo=algo,
                                 state_in=stb[b:b + 1], tail_in=tlb[b:b + 1], return_state=True)
         _sync()
         assert torch.equal(o[sl], ob[0]), b
