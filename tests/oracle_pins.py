@@ -511,6 +511,78 @@ def pin_varlen(O) -> float:
     return max(errs)
 
 
+def pin_backward_forward_torch(O) -> float:
+    """The differentiable torch forward of the backward oracle equals the
+    NumPy oracle's forward (output and end state), for every feature map."""
+    from oracle import idattn_backward as BW
+    c = pin_case(with_state=True)
+    p = dict(c["p"])
+    H, d = c["q"].shape[2], c["q"].shape[3]
+    p["rff_omega"] = np.random.default_rng(41).normal(size=(H, d, d // 2))
+    err = 0.0
+    for fm in ("squared", "unit", "rff"):
+        o, st, _ = O.forward(c["q"], c["k"], c["v"], p, 1e-6, 1e-6, c["state"], c["tail"], feature_norm=fm)
+        pt = {k: torch_t(v) for k, v in p.items()}
+        ot, stt = BW.forward_torch(torch_t(c["q"]), torch_t(c["k"]), torch_t(c["v"]), pt, 1e-6, 1e-6,
+                                   torch_c(c["state"]), torch_t(c["tail"]), fm)
+        err = max(err, rel(ot.numpy(), o), rel(stt.numpy(), st))
+    return err
+
+
+def torch_t(x):
+    import torch
+    return torch.as_tensor(np.asarray(x, dtype=np.float64))
+
+
+def torch_c(z):
+    import torch
+    return torch.as_tensor(np.asarray(z, dtype=np.complex128))
+
+
+def pin_backward_finite_differences(O) -> float:
+    """Directional derivatives of L = sum(g_o * o) + Re sum(conj(g_s) * state_out)
+    from the backward oracle against central differences of the NumPy
+    forward, along a random direction in each input: q, k, v, every parameter
+    and the carried state.  Returns the largest relative mismatch."""
+    from oracle import idattn_backward as BW
+    c = pin_case(with_state=True, N=12)
+    p = c["p"]
+    r = np.random.default_rng(42)
+    g_o = r.normal(size=c["q"].shape)
+    g_s = r.normal(size=c["state"].shape) + 1j * r.normal(size=c["state"].shape)
+
+    def loss(q, k, v, pp, st):
+        o, so, _ = O.forward(q, k, v, pp, 1e-6, 1e-6, st, c["tail"])
+        return float((g_o * o).sum() + (np.conj(g_s) * so).real.sum())
+
+    grads = BW.backward(c["q"], c["k"], c["v"], p, g_o, 1e-6, 1e-6, c["state"], c["tail"], g_s)
+    h = 1e-5
+    worst = 0.0
+    names = ["q", "k", "v"] + list(BW.PARAM_KEYS) + ["state"]
+    for name in names:
+        base = c["state"] if name == "state" else (c[name] if name in ("q", "k", "v") else p[name])
+        base = np.asarray(base)
+        delta = r.normal(size=base.shape)
+        if name == "state":
+            delta = delta + 1j * r.normal(size=base.shape)
+
+        def at(x):
+            args = dict(q=c["q"], k=c["k"], v=c["v"], st=c["state"])
+            pp = dict(p)
+            if name in ("q", "k", "v"):
+                args[name] = x
+            elif name == "state":
+                args["st"] = x
+            else:
+                pp[name] = x
+            return loss(args["q"], args["k"], args["v"], pp, args["st"])
+
+        fd = (at(base + h * delta) - at(base - h * delta)) / (2 * h)
+        an = float((np.conj(grads[name]) * delta).real.sum()) if name == "state" else float((grads[name] * delta).sum())
+        worst = max(worst, abs(an - fd) / max(abs(fd), 1e-12))
+    return worst
+
+
 PINS = {
     "conv": (pin_conv, 1e-13),
     "silu": (pin_silu, 1e-14),
@@ -532,6 +604,8 @@ PINS = {
     "split_resume": (pin_split_resume, 1e-12),
     "decode": (pin_decode, 1e-12),
     "varlen": (pin_varlen, 1e-12),
+    "backward_forward_torch": (pin_backward_forward_torch, 1e-12),
+    "backward_finite_differences": (pin_backward_finite_differences, 1e-6),
     "eta_closed_form": (pin_eta_closed_form, 1e-12),
     "eta_m1_ratio": (pin_eta_m1_ratio, 1e-11),
     "eta_query_scale": (pin_eta_query_scale, 1e-10),
