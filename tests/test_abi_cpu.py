@@ -321,3 +321,18 @@ def test_decode_normalized_validation():
     expect(dec(e=5 * QB + 64), "IDATTN_ERR_ALIAS")   # eta inside the state
     expect(dec(o=11 * QB), "IDATTN_ERR_ALIAS")       # o_t over eta
     expect(dec(e=p.Bc), "IDATTN_ERR_ALIAS")          # eta over a parameter
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without the built library every entry point raises."""
+    from fixed_state_ssm_amd import binding
+    monkeypatch.setattr(binding, "_lib", None)
+    missing = str(tmp_path / "libidattn.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.load_library(missing)
+    monkeypatch.setattr(binding, "LIB_PATH", missing)
+    monkeypatch.setattr(binding.load_library, "__defaults__", (missing,))
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.idattn_version()
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.idattn_forward_workspace_size(dims())
