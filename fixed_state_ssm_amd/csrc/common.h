@@ -85,6 +85,25 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// The same total with lower latency, for reductions on a serial path: lane
+// swaps by DPP within rows of 16 (xor 1, xor 2, rotate by 4 and 8), then
+// across rows with v_permlane16_swap and v_permlane32_swap, with no trip
+// through the LDS crossbar.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float wave_total(float x) {
+    x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_f<0x124>(x);  // row_ror:4
+    x += dpp_f<0x128>(x);  // row_ror:8
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // ------------------------------------------------------------------ RFF
 // Random Fourier features of one token-head held by one wave (Chinese
 // rendering of the paper, section 3.1, eq. 6): with D = d/2 frequencies, the

@@ -89,8 +89,8 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
                 pr = fmaf(xv[t][j], nr, pr);
                 pi = fmaf(xv[t][j], ni, pi);
             }
-            pr = wave_sum(pr);
-            pi = wave_sum(pi);
+            pr = wave_total(pr);
+            pi = wave_total(pi);
             if (lane == 0) srow[(i0 + t) * M] = make_float2(pr, pi);
             if constexpr (ETA) {
                 const float nr = fmaf(ar, er, fmaf(-ai, ei, br));
