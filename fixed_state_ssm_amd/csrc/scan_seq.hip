@@ -11,9 +11,11 @@
 // updated in place.
 //
 // ssm_value_scan_readout_seq: one block per (b, h, 64-channel group); wave w
-// owns a contiguous quarter of the modes, lane l one channel, so Gamma_{m,c}
-// stays in registers and o_i,c = Re sum_m s_m(i) Gamma_{m,c}(i) needs only a
-// 4-way cross-wave sum through LDS, done once per block of 16 tokens.
+// owns a contiguous eighth of the modes, lane l one channel, so Gamma_{m,c}
+// stays in registers and o_i,c = Re sum_m s_m(i) Gamma_{m,c}(i) needs only an
+// 8-way cross-wave sum through LDS, done once per block of 16 tokens.  Eight
+// waves (two per SIMD) rather than four: there are only B H d/64 blocks, fewer
+// than compute units at the model shapes, so each one needs the latency hiding.
 #include "common.h"
 #include "launch.h"
 
@@ -118,19 +120,20 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
 }
 
 constexpr int kBlk = 16;  // tokens per LDS round of the value scan
+constexpr int kVW = 8;    // waves per value-scan block: M / 8 modes each, two waves per SIMD
 
 // ETA: o = numerator / denominator, the denominator summed over the modes
 // from the key scan's per-mode shares pden [H][T][M].
 template <bool BF16, int MW, bool ETA>
-__global__ __launch_bounds__(256) void value_scan_seq_kernel(Problem p, idattn_params prm,
+__global__ __launch_bounds__(kVW * 64) void value_scan_seq_kernel(Problem p, idattn_params prm,
                                                              const float2* __restrict__ s,
                                                              const float* __restrict__ z_v,
                                                              const float* state_in, void* __restrict__ o,
                                                              float* state_out, const float* __restrict__ pden) {
     __shared__ float2 s_blk[kBlk * 64];
-    __shared__ float red[4][kBlk][kWave];
+    __shared__ float red[kVW][kBlk][kWave];
     __shared__ float p_blk[ETA ? kBlk * 64 : 1];
-    __shared__ float den_s[4][kBlk];
+    __shared__ float den_s[kVW][kBlk];
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x >> 6;
     const int64_t bh = blockIdx.x;
@@ -163,9 +166,9 @@ __global__ __launch_bounds__(256) void value_scan_seq_kernel(Problem p, idattn_p
     const float* zv = z_v + row0 * d;
     for (int64_t i0 = 0; i0 < N; i0 += kBlk) {
         const int nt = static_cast<int>(N - i0 < kBlk ? N - i0 : kBlk);
-        for (int e = threadIdx.x; e < nt * M; e += 256) s_blk[e] = s[(row0 + i0) * M + e];
+        for (int e = threadIdx.x; e < nt * M; e += kVW * 64) s_blk[e] = s[(row0 + i0) * M + e];
         if constexpr (ETA)
-            for (int e = threadIdx.x; e < nt * M; e += 256) p_blk[e] = pden[(row0 + i0) * M + e];
+            for (int e = threadIdx.x; e < nt * M; e += kVW * 64) p_blk[e] = pden[(row0 + i0) * M + e];
         float zz[kBlk];
 #pragma unroll
         for (int t = 0; t < kBlk; ++t) zz[t] = (t < nt && cok) ? zv[(i0 + t) * d + c] : 0.f;
@@ -193,12 +196,16 @@ __global__ __launch_bounds__(256) void value_scan_seq_kernel(Problem p, idattn_p
             }
         }
         __syncthreads();
-        for (int e = threadIdx.x; e < nt * kWave; e += 256) {
+        for (int e = threadIdx.x; e < nt * kWave; e += kVW * 64) {
             const int t = e / kWave, l = e % kWave;
             const int cc = static_cast<int>(blockIdx.y) * kWave + l;
             if (cc < d) {
-                float sum = (red[0][t][l] + red[1][t][l]) + (red[2][t][l] + red[3][t][l]);
-                if constexpr (ETA) sum /= (den_s[0][t] + den_s[1][t]) + (den_s[2][t] + den_s[3][t]);
+                // fixed pairwise order over the eight waves' partial sums
+                float sum = ((red[0][t][l] + red[1][t][l]) + (red[2][t][l] + red[3][t][l])) +
+                            ((red[4][t][l] + red[5][t][l]) + (red[6][t][l] + red[7][t][l]));
+                if constexpr (ETA)
+                    sum /= ((den_s[0][t] + den_s[1][t]) + (den_s[2][t] + den_s[3][t])) +
+                           ((den_s[4][t] + den_s[5][t]) + (den_s[6][t] + den_s[7][t]));
                 store_io<BF16>(o, ((start + i0 + t) * H + h) * d + cc, sum);
             }
         }
@@ -244,19 +251,20 @@ hipError_t launch_ssm_value_scan_readout_seq(const Problem& p, const idattn_para
 #define IDATTN_VSCAN_E(MW, ETA)                                                                  \
     do {                                                                                         \
         if (p.bf16)                                                                              \
-            value_scan_seq_kernel<true, MW, ETA><<<grid, 256, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out, pden); \
+            value_scan_seq_kernel<true, MW, ETA><<<grid, kVW * 64, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out, pden); \
         else                                                                                     \
-            value_scan_seq_kernel<false, MW, ETA><<<grid, 256, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out, pden); \
+            value_scan_seq_kernel<false, MW, ETA><<<grid, kVW * 64, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out, pden); \
     } while (0)
 #define IDATTN_VSCAN(MW)                          \
     do {                                          \
         if (pden != nullptr) IDATTN_VSCAN_E(MW, true); \
         else IDATTN_VSCAN_E(MW, false);           \
     } while (0)
-    switch (p.M / 4) {
+    static_assert(kVW == 8, "the output sum is written out for eight waves");
+    switch (p.M / kVW) {
+        case 2: IDATTN_VSCAN(2); break;
         case 4: IDATTN_VSCAN(4); break;
         case 8: IDATTN_VSCAN(8); break;
-        case 16: IDATTN_VSCAN(16); break;
         default: return hipErrorInvalidValue;
     }
 #undef IDATTN_VSCAN
