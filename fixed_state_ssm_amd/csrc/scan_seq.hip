@@ -11,11 +11,12 @@
 // updated in place.
 //
 // ssm_value_scan_readout_seq: one block per (b, h, 64-channel group); wave w
-// owns a contiguous eighth of the modes, lane l one channel, so Gamma_{m,c}
-// stays in registers and o_i,c = Re sum_m s_m(i) Gamma_{m,c}(i) needs only an
-// 8-way cross-wave sum through LDS, done once per block of 16 tokens.  Eight
-// waves (two per SIMD) rather than four: there are only B H d/64 blocks, fewer
-// than compute units at the model shapes, so each one needs the latency hiding.
+// owns a contiguous sixteenth of the modes, lane l one channel, so
+// Gamma_{m,c} stays in registers and o_i,c = Re sum_m s_m(i) Gamma_{m,c}(i)
+// needs only a 16-way cross-wave sum through LDS, done once per block of 16
+// tokens.  Sixteen waves (four per SIMD): there are only B H d/64 blocks,
+// fewer than compute units at the model shapes, so each one needs the latency
+// hiding.
 #include "common.h"
 #include "launch.h"
 
@@ -120,7 +121,17 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
 }
 
 constexpr int kBlk = 16;  // tokens per LDS round of the value scan
-constexpr int kVW = 8;    // waves per value-scan block: M / 8 modes each, two waves per SIMD
+constexpr int kVW = 16;   // waves per value-scan block: M / 16 modes each, four waves per SIMD
+
+// Sum of x[0..kVW) in a fixed pairwise order (deterministic).
+template <int K>
+__device__ __forceinline__ float tree_sum(float (&x)[K]) {
+#pragma unroll
+    for (int step = 1; step < K; step *= 2)
+#pragma unroll
+        for (int i = 0; i + step < K; i += 2 * step) x[i] += x[i + step];
+    return x[0];
+}
 
 // ETA: o = numerator / denominator, the denominator summed over the modes
 // from the key scan's per-mode shares pden [H][T][M].
@@ -200,12 +211,16 @@ __global__ __launch_bounds__(kVW * 64) void value_scan_seq_kernel(Problem p, ida
             const int t = e / kWave, l = e % kWave;
             const int cc = static_cast<int>(blockIdx.y) * kWave + l;
             if (cc < d) {
-                // fixed pairwise order over the eight waves' partial sums
-                float sum = ((red[0][t][l] + red[1][t][l]) + (red[2][t][l] + red[3][t][l])) +
-                            ((red[4][t][l] + red[5][t][l]) + (red[6][t][l] + red[7][t][l]));
-                if constexpr (ETA)
-                    sum /= ((den_s[0][t] + den_s[1][t]) + (den_s[2][t] + den_s[3][t])) +
-                           ((den_s[4][t] + den_s[5][t]) + (den_s[6][t] + den_s[7][t]));
+                // fixed pairwise order over the waves' partial sums
+                float part[kVW];
+#pragma unroll
+                for (int i = 0; i < kVW; ++i) part[i] = red[i][t][l];
+                float sum = tree_sum(part);
+                if constexpr (ETA) {
+#pragma unroll
+                    for (int i = 0; i < kVW; ++i) part[i] = den_s[i][t];
+                    sum /= tree_sum(part);
+                }
                 store_io<BF16>(o, ((start + i0 + t) * H + h) * d + cc, sum);
             }
         }
@@ -260,11 +275,10 @@ hipError_t launch_ssm_value_scan_readout_seq(const Problem& p, const idattn_para
         if (pden != nullptr) IDATTN_VSCAN_E(MW, true); \
         else IDATTN_VSCAN_E(MW, false);           \
     } while (0)
-    static_assert(kVW == 8, "the output sum is written out for eight waves");
     switch (p.M / kVW) {
+        case 1: IDATTN_VSCAN(1); break;
         case 2: IDATTN_VSCAN(2); break;
         case 4: IDATTN_VSCAN(4); break;
-        case 8: IDATTN_VSCAN(8); break;
         default: return hipErrorInvalidValue;
     }
 #undef IDATTN_VSCAN
