@@ -68,8 +68,8 @@ __device__ __forceinline__ void token_features(const Problem& p, const float* __
         sq = fmaf(yq[j], yq[j], sq);
         sk = fmaf(yk[j], yk[j], sk);
     }
-    sq = wave_sum(sq);
-    sk = wave_sum(sk);
+    sq = wave_total(sq);
+    sk = wave_total(sk);
     // squared norm, or its square root for the unit-norm map
     inv_q = p.unit_feat ? 1.f / sqrtf(sq + p.eps_feat) : 1.f / (sq + p.eps_feat);
     inv_k = p.unit_feat ? 1.f / sqrtf(sk + p.eps_feat) : 1.f / (sk + p.eps_feat);
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
                 ckv[j] = ck;
                 sv = fmaf(vv[j], vv[j], sv);
             }
-            sv = wave_sum(sv);
+            sv = wave_total(sv);
             float inv_q, inv_k;
             token_features<RFF>(p, prm.rff_omega + h * d * (d / 2), cqv, ckv, yq, yk, inv_q, inv_k);
             float xk2 = 0.f, xik[2];
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
                 xik[j] = yk[j] * inv_k;
                 xk2 = fmaf(xik[j], xik[j], xk2);
             }
-            xk2 = wave_sum(xk2);
+            xk2 = wave_total(xk2);
             const float rk = 1.f / sqrtf(xk2 / d + p.eps_norm);
             const float rv = 1.f / sqrtf(sv / d + p.eps_norm);
     #pragma unroll
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
                         }
                         sv = fmaf(vv[j], vv[j], sv);
                     }
-                    sv = wave_sum(sv);
+                    sv = wave_total(sv);
                     float inv_q, inv_k;
                     token_features<RFF>(p, prm.rff_omega + h * d * (d / 2), cqv, ckv, yq, yk, inv_q, inv_k);
                     float xk2 = 0.f, xik[2];
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
                         xik[j] = yk[j] * inv_k;
                         xk2 = fmaf(xik[j], xik[j], xk2);
                     }
-                    xk2 = wave_sum(xk2);
+                    xk2 = wave_total(xk2);
                     const float rk = 1.f / sqrtf(xk2 / d + p.eps_norm);
                     const float rv = 1.f / sqrtf(sv / d + p.eps_norm);
     #pragma unroll

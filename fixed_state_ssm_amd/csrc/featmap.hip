@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
         xv[j] = vv;
         sv = fmaf(vv, vv, sv);
     }
-    sv = wave_sum(sv);
+    sv = wave_total(sv);
     // xi = y * inv
     float inv_q = 1.f, inv_k = 1.f;
     if (p.rff_feat) {
@@ -80,8 +80,8 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
             sq = fmaf(yq[j], yq[j], sq);
             sk = fmaf(yk[j], yk[j], sk);
         }
-        sq = wave_sum(sq);
-        sk = wave_sum(sk);
+        sq = wave_total(sq);
+        sk = wave_total(sk);
         // squared norm, or its square root for the unit-norm map
         inv_q = p.unit_feat ? 1.f / sqrtf(sq + p.eps_feat) : 1.f / (sq + p.eps_feat);
         inv_k = p.unit_feat ? 1.f / sqrtf(sk + p.eps_feat) : 1.f / (sk + p.eps_feat);
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
         xik[j] = yk[j] * inv_k;
         xk2 = fmaf(xik[j], xik[j], xk2);
     }
-    xk2 = wave_sum(xk2);
+    xk2 = wave_total(xk2);
     const float rk = 1.f / sqrtf(xk2 / d + p.eps_norm);
     const float rv = 1.f / sqrtf(sv / d + p.eps_norm);
     const int64_t orow = (h * T + t) * d;
