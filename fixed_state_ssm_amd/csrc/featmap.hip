@@ -66,26 +66,21 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
         sv = fmaf(vv, vv, sv);
     }
     sv = wave_total(sv);
-    // xi = y * inv
-    float inv_q = 1.f, inv_k = 1.f;
-    if (p.rff_feat) {
-        rff_features<DJ>(cqv, ckv, prm.rff_omega + h * d * (d / 2), d, yq, yk);
-    } else {
-        // SiLU(c) = c / (1 + exp(-c)); lanes past d hold c = 0 -> y = 0.
-        float sq = 0.f, sk = 0.f;
+    // xi = y * inv with y = SiLU(c) = c / (1 + exp(-c)); lanes past d hold c = 0 -> y = 0.
+    // (The RFF map has its own kernel below.)
+    float sq = 0.f, sk = 0.f;
 #pragma unroll
-        for (int j = 0; j < DJ; ++j) {
-            yq[j] = cqv[j] / (1.f + expf(-cqv[j]));
-            yk[j] = ckv[j] / (1.f + expf(-ckv[j]));
-            sq = fmaf(yq[j], yq[j], sq);
-            sk = fmaf(yk[j], yk[j], sk);
-        }
-        sq = wave_total(sq);
-        sk = wave_total(sk);
-        // squared norm, or its square root for the unit-norm map
-        inv_q = p.unit_feat ? 1.f / sqrtf(sq + p.eps_feat) : 1.f / (sq + p.eps_feat);
-        inv_k = p.unit_feat ? 1.f / sqrtf(sk + p.eps_feat) : 1.f / (sk + p.eps_feat);
+    for (int j = 0; j < DJ; ++j) {
+        yq[j] = cqv[j] / (1.f + expf(-cqv[j]));
+        yk[j] = ckv[j] / (1.f + expf(-ckv[j]));
+        sq = fmaf(yq[j], yq[j], sq);
+        sk = fmaf(yk[j], yk[j], sk);
     }
+    sq = wave_total(sq);
+    sk = wave_total(sk);
+    // squared norm, or its square root for the unit-norm map
+    const float inv_q = p.unit_feat ? 1.f / sqrtf(sq + p.eps_feat) : 1.f / (sq + p.eps_feat);
+    const float inv_k = p.unit_feat ? 1.f / sqrtf(sk + p.eps_feat) : 1.f / (sk + p.eps_feat);
     float xk2 = 0.f;
     float xik[DJ];
 #pragma unroll
@@ -104,6 +99,88 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
             xi_q[orow + c] = yq[j] * inv_q;
             z_k[orow + c] = fmaf(prm.gain[h * 2 * d + c] * xik[j], rk, prm.bias[h * 2 * d + c]);
             z_v[orow + c] = fmaf(prm.gain[h * 2 * d + d + c] * xv[j], rv, prm.bias[h * 2 * d + d + c]);
+        }
+    }
+}
+
+// The RFF map: one wave per TPW consecutive tokens of one head (waves numbered
+// [T / TPW][H]), so that each row of the head's frequency table is loaded once
+// for TPW tokens; otherwise the same steps as featmap_conv_norm_kernel.
+template <bool BF16, int DJ, int TPW>
+__global__ __launch_bounds__(256) void featmap_rff_kernel(
+    Problem p, idattn_params prm, const void* __restrict__ q, const void* __restrict__ k,
+    const void* __restrict__ v, const void* __restrict__ tail_in, float* __restrict__ xi_q,
+    float* __restrict__ z_k, float* __restrict__ z_v) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t th = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t H = p.H, T = p.T;
+    const int d = static_cast<int>(p.d), W = static_cast<int>(p.W);
+    const int64_t groups = (T + TPW - 1) / TPW;
+    if (th >= groups * H) return;  // whole wave exits; no barriers below
+    const int64_t h = th % H;
+    const int64_t t0 = (th / H) * TPW;
+    float cq[TPW][DJ], ck[TPW][DJ], xv[TPW][DJ], sv[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int64_t t = t0 + u;  // tokens past T compute zeros and store nothing
+        const bool tok = t < T;
+        const int64_t b = tok ? seq_of_token(p.cu, p.N, p.B, t) : 0;
+        int64_t start = 0, len = 0;
+        if (tok) seq_range(p.cu, p.N, T, b, start, len);
+        const int64_t n = t >= start ? t - start : 0;
+        sv[u] = 0.f;
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            const int c = lane + kWave * j;
+            float a = 0.f, e = 0.f, vv = 0.f;
+            if (tok && c < d) {
+                const float* wq = prm.conv_q + (h * d + c) * W;
+                const float* wk = prm.conv_k + (h * d + c) * W;
+                for (int j2 = 0; j2 < W; ++j2) {
+                    const int64_t pos = n - (W - 1) + j2;
+                    float xq = 0.f, xk = 0.f;
+                    if (pos >= 0) {
+                        const int64_t idx = ((t - (W - 1) + j2) * H + h) * d + c;
+                        xq = load_io<BF16>(q, idx);
+                        xk = load_io<BF16>(k, idx);
+                    } else if (tail_in != nullptr) {
+                        const int64_t tq = ((b * H + h) * 2 * (W - 1) + (W - 1 + pos)) * d + c;
+                        xq = load_io<BF16>(tail_in, tq);
+                        xk = load_io<BF16>(tail_in, tq + static_cast<int64_t>(W - 1) * d);
+                    }
+                    a = fmaf(wq[j2], xq, a);
+                    e = fmaf(wk[j2], xk, e);
+                }
+                vv = load_io<BF16>(v, (t * H + h) * d + c);
+            }
+            cq[u][j] = a;
+            ck[u][j] = e;
+            xv[u][j] = vv;
+            sv[u] = fmaf(vv, vv, sv[u]);
+        }
+    }
+    float yq[TPW][DJ], yk[TPW][DJ];
+    rff_features_multi<DJ, TPW>(cq, ck, prm.rff_omega + h * d * (d / 2), d, yq, yk);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int64_t t = t0 + u;
+        float xk2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) xk2 = fmaf(yk[u][j], yk[u][j], xk2);
+        xk2 = wave_total(xk2);
+        const float svt = wave_total(sv[u]);
+        if (t >= T) continue;  // uniform over the wave
+        const float rk = 1.f / sqrtf(xk2 / d + p.eps_norm);
+        const float rv = 1.f / sqrtf(svt / d + p.eps_norm);
+        const int64_t orow = (h * T + t) * d;
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            const int c = lane + kWave * j;
+            if (c < d) {
+                xi_q[orow + c] = yq[u][j];
+                z_k[orow + c] = fmaf(prm.gain[h * 2 * d + c] * yk[u][j], rk, prm.bias[h * 2 * d + c]);
+                z_v[orow + c] = fmaf(prm.gain[h * 2 * d + d + c] * xv[u][j], rv, prm.bias[h * 2 * d + d + c]);
+            }
         }
     }
 }
@@ -161,6 +238,21 @@ __global__ __launch_bounds__(256) void copy_or_zero_kernel(const uint32_t* __res
 hipError_t launch_featmap_conv_norm(const Problem& p, const idattn_params& prm, const void* q,
                                     const void* k, const void* v, const void* tail_in,
                                     float* xi_q, float* z_k, float* z_v, hipStream_t stream) {
+    if (p.rff_feat) {
+        constexpr int kTPW = 4;
+        const int64_t waves = (p.T + kTPW - 1) / kTPW * p.H;
+        const dim3 g(static_cast<unsigned>((waves + 3) / 4));
+#define IDATTN_RFF(BF, DJ) featmap_rff_kernel<BF, DJ, kTPW><<<g, 256, 0, stream>>>(p, prm, q, k, v, tail_in, xi_q, z_k, z_v)
+        if (p.d > 64) {
+            if (p.bf16) IDATTN_RFF(true, 2);
+            else IDATTN_RFF(false, 2);
+        } else {
+            if (p.bf16) IDATTN_RFF(true, 1);
+            else IDATTN_RFF(false, 1);
+        }
+#undef IDATTN_RFF
+        return hipGetLastError();
+    }
     const int64_t th = p.T * p.H;
     const dim3 grid(static_cast<unsigned>((th + 3) / 4));
     if (p.d > 64) {
