@@ -18,6 +18,11 @@ source, else null.
 The CPU baseline is the fp64 oracle, single-threaded, on a bounded sample of
 the same workload (the first batch rows with every head and whole sequences,
 or a prefix of row 0 when one row exceeds the time target).
+
+Before the W warmup steps the forward runs back to back for --settle-s
+seconds (0.3 by default), untimed: the GPU's clocks take several dozen
+launches to reach their steady state, and without it a short warmup times
+that ramp instead of the kernels.  The number of settle launches is reported.
 """
 from __future__ import annotations
 
@@ -37,7 +42,7 @@ METRIC = "mixer tokens/sec fwd (1.3B shape, N=4096) + % of HBM roofline, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 FP32_PEAK_TFLOPS = 157.3
 FP16_MFMA_PEAK_TFLOPS = 2500.0
-KERNEL_SOURCES = ["fixed_state_ssm_amd/csrc/chunked.hip", "fixed_state_ssm_amd/csrc/chunked_ws.hip",
+KERNEL_SOURCES = ["fixed_state_ssm_amd/csrc/chunked_ws.hip",
                   "fixed_state_ssm_amd/csrc/featmap.hip", "fixed_state_ssm_amd/csrc/scan_seq.hip",
                   "fixed_state_ssm_amd/csrc/decode.hip", "fixed_state_ssm_amd/csrc/common.h",
                   "fixed_state_ssm_amd/csrc/launch.h", "fixed_state_ssm_amd/csrc/api.cpp"]
@@ -65,6 +70,37 @@ def committed_traffic(config: str, algo: str):
     return float(m_b.group(1))
 
 
+def plan_segments(B, N, H, L=64):
+    """The chunked forward's time split (the library's plan): S segments of
+    Lseg tokens per (b, h) so that B H S is about one workgroup per CU."""
+    pairs = B * H
+    chunks = (N + L - 1) // L
+    s = max(1, 256 // pairs)
+    s = min(s, chunks) if chunks > 0 else 1
+    cps = (chunks + s - 1) // s
+    lseg = cps * L
+    return max(1, (N + lseg - 1) // lseg), lseg
+
+
+def chunked_mfma_flops(B, N, H, d, L=64):
+    """Flops the chunked forward issues on v_mfma_f32_16x16x32_f16 (16 384
+    each) per launch, counted from the kernels' loops, every product with the
+    decay table counted twice (its high and low fp16 parts).  Per chunk of one
+    (b, h): the forward runs G (10 causal 16x16 tiles, d/32 K steps), Y U^T
+    (4 d/32 per key wave, 8 waves), the U update (4 d/16 per key wave), S (16
+    per key wave), the P~ tiles (10 x 8), X Gamma (16 per value wave owning
+    columns, d/16 of them), the Gamma update (32 each) and P~ Z_v (8 each);
+    the feature pass repeats the two state updates for every segment but the
+    last of a sequence."""
+    S, lseg = plan_segments(B, N, H, L)
+    rt, kb, own = d // 16, d // 32, d // 16
+    fwd = 10 * kb + 8 * 4 * kb + 8 * 4 * rt + 8 * 16 + 80 + own * (16 + 32 + 8)
+    feat = 8 * 4 * rt + own * 32
+    chunks_total = B * H * ((N + L - 1) // L)
+    chunks_upd = B * H * (S - 1) * (lseg // L)
+    return 16384.0 * (fwd * chunks_total + feat * chunks_upd)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -81,6 +117,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU sample")
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="seconds of untimed back-to-back forwards before the warmup steps (clock settle)")
     return ap.parse_args()
 
 
@@ -336,6 +374,13 @@ def main():
         qq, kk, vv, oo = sets[i % len(sets)]
         fs.idattn_forward(dims, prm, qq, kk, vv, oo, None, None, state_out, tail_out, ws, nbytes)
 
+    settle = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(10):
+            step(settle)
+            settle += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -354,6 +399,7 @@ def main():
     alg_bytes = B * N * H * d * 2 * 4
     achieved = alg_bytes / (mean_launch_ms * 1e-3) / 1e9
     flops_literal = 14.0 * M * 2 * d * B * N * H
+    flops_mfma = chunked_mfma_flops(B, N, H, d) if algo == "chunked" else 0.0
 
     out = {
         "metric": METRIC,
@@ -380,7 +426,12 @@ def main():
                      "launch_ms_mean": mean_launch_ms, "launch_ms_min": min(launch_ms)},
         "flops": {"literal_per_launch": flops_literal,
                   "literal_tflops": flops_literal / (mean_launch_ms * 1e-3) / 1e12,
-                  "frac_fp32_peak": flops_literal / (mean_launch_ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS},
+                  "note": "the literal recurrence's flops are what the method defines, not what the chunked "
+                          "kernels execute; mfma_* counts the matrix-core work the kernels issue",
+                  "mfma_executed_per_launch": flops_mfma,
+                  "mfma_tflops": flops_mfma / (mean_launch_ms * 1e-3) / 1e12,
+                  "mfma_frac_fp16_peak": flops_mfma / (mean_launch_ms * 1e-3) / 1e12 / FP16_MFMA_PEAK_TFLOPS},
+        "settle_launches": settle,
         "source_sha": source_sha(),
     }
     out["measured_copy_gbps"] = measure_copy_gbps(torch)

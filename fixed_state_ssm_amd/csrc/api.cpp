@@ -372,22 +372,19 @@ idattn_status idattn_forward_normalized(const idattn_dims* dims, const idattn_pa
 }
 
 // The chunked algorithm runs a packed batch one sequence at a time (B = 1
-// launches on the caller's stream); its workspace for any sequence of at most
-// T tokens is bounded by that of T + 16 chunks (at most 16 segments of whole
-// chunks cover N tokens with less than 16 chunks to spare).
+// launches on the caller's stream); its workspace is the library's bound over
+// every sequence of at most T tokens.
 bool varlen_chunked_possible(const idattn_dims& D) {
     idattn::Problem p = problem(D);
     p.B = 1;
-    p.N = D.N + 1024;
     return D.io_dtype == IDATTN_IO_BF16 && idattn::chunked_supported(p);
 }
 
 size_t varlen_chunked_bound(const idattn_dims& D) {
     idattn::Problem p = problem(D);
     p.B = 1;
-    p.N = D.N + 1024;
     p.T = p.N;
-    return idattn::chunked_workspace_bytes(p);
+    return idattn::chunked_workspace_bound(p);
 }
 
 size_t varlen_workspace(const idattn_dims& D) {
@@ -473,6 +470,10 @@ idattn_status idattn_forward_varlen(const idattn_dims* dims, const idattn_params
             continue;
         }
         const idattn::Problem p = problem(one);
+        const size_t need_one = idattn::chunked_workspace_bytes(p);
+        if (need_one > workspace_bytes_given)
+            return fail(IDATTN_ERR_WORKSPACE, "sequence %lld needs %zu bytes of workspace, %zu given", (long long)b,
+                        need_one, workspace_bytes_given);
         const hipError_t e = idattn::launch_forward_chunked(
             p, *params, static_cast<const char*>(q) + t0, static_cast<const char*>(k) + t0,
             static_cast<const char*>(v) + t0, static_cast<char*>(o) + t0, si, ti, so, to, workspace, s);

@@ -937,8 +937,10 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
                                                             const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ v,
                                                             const uint16_t* __restrict__ tail_in,
-                                                            const uint8_t* __restrict__ tab, float* __restrict__ ws,
-                                                            _Float16* __restrict__ zt, int64_t Lseg, int S) {
+                                                            const float* __restrict__ state_in,
+                                                            const uint8_t* __restrict__ tab, float* __restrict__ c0,
+                                                            float* __restrict__ ws, _Float16* __restrict__ zt,
+                                                            int64_t Lseg, int S) {
     __shared__ SmemSeg<D> sm;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool key = w < 8;
@@ -960,9 +962,21 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
     const int rsb = static_cast<int>(p.H * D * 2);  // token stride, bytes
     // tile of chunk c of this segment: z_k^T, then z_v^T
     _Float16* zseg = zt + ((bh * S + seg) * (Lseg / L)) * 2 * D * L;
+    // The state entering the sequence, times the table scale kappa, staged in
+    // lane order for the forward (and the carry chain), which read only this
+    // copy: state_in is read here, in a kernel that completes before any block
+    // of the forward can write state_out, so the two may be one buffer.
+    const bool stage = seg == 0 && state_in != nullptr;
+    const float kap = reinterpret_cast<const float4*>(th + kTabHc)[0].z;
+    const float* sin = stage ? state_in + bh * MM * 2 * D * 2 : nullptr;
+    float* cst = c0 + bh * MM * 2 * D * 2;
     if (key) {
         const int kw = w;
         f4 U[Cfg<D>::RT];
+        if (stage) {
+            u_load<D>(U, sin, kw, kap);
+            u_store_lane<D>(U, cst, kw);
+        }
         u_load<D>(U, nullptr, kw, 1.f);
         const __amdgpu_buffer_rsrc_t rk = seq_rsrc<D>(k, b, h, p.N, p.H, t_end);
         uint32_t rkk[11];
@@ -991,6 +1005,10 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
         const int vw = w - 8;
         const bool own = upd && vw < D / 16;
         f4 G[8];
+        if (stage && vw < D / 16) {
+            g_load<D>(G, sin, vw, kap);
+            g_store_lane<D>(G, cst, vw);
+        }
         if (own) g_load<D>(G, nullptr, vw, 1.f);
         const __amdgpu_buffer_rsrc_t rv = seq_rsrc<D>(v, b, h, p.N, p.H, t_end);
         uint32_t rvv[8];
@@ -1024,8 +1042,9 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
 // and the next lane's): ws[seg] <- state entering segment seg+1.  The end
 // states of up to eight segments are loaded before any of them is combined,
 // so that the loads overlap instead of forming a chain of dependent round
-// trips.  state_in is read in its own layout.
-__global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, const float* __restrict__ state_in,
+// trips.  The state entering the sequence comes from the staged copy c0.
+__global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, bool has_state,
+                                                            const float* __restrict__ c0,
                                                             const uint8_t* __restrict__ tab,
                                                             float* __restrict__ ws, int S) {
     constexpr int kBatch = 8;
@@ -1036,26 +1055,23 @@ __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, const flo
     const int64_t bh = e / per, h = bh % p.H;
     const int o = static_cast<int>((e % per) >> 2) * 8;  // float offset of the group of eight
     const int k = static_cast<int>(e & 3);
-    int mode, pre, pim, abi;  // mode, positions of re / im in the eight floats, re in state_in
+    int mode, pre, pim;  // mode, positions of re / im in the eight floats
     if (o < 128 * D) {        // U: [kw][rt][lane][jj], re in lane i, im in lane i + 1
         const int kw = o / (16 * D), rem = o % (16 * D), rt = rem / 256, ln = (rem % 256) / 4;
         const int g = ln >> 4, i = ln & 15;
         mode = 8 * kw + i / 2;
         pre = k;
         pim = 4 + k;
-        abi = (mode * 2 * D + 16 * rt + 4 * g + k) * 2;
     } else {  // Gamma: [vw][mt][lane][jj], (re, im) of modes m0, m0 + 1 in jj, channel 16 vw + i of the lane
         const int o2 = o - 128 * D, vw = o2 / 2048, mt = (o2 % 2048) / 256, ln = (o2 % 256) / 4;
         const int g = ln >> 4, i = ln & 15;
         mode = 8 * mt + 2 * g + (k & 1);
         pre = 2 * k;
         pim = 2 * k + 1;
-        abi = (mode * 2 * D + D + 16 * vw + i + (k >> 1)) * 2;
     }
     const float2 a = reinterpret_cast<const float2*>(tab + h * kTabBytes + kTabPwSeg)[mode];
-    const float kap = reinterpret_cast<const float4*>(tab + h * kTabBytes + kTabHc)[0].z;  // states carry kappa
-    float2 c = state_in ? make_float2(kap * state_in[bh * 256 * D + abi], kap * state_in[bh * 256 * D + abi + 1])
-                        : make_float2(0.f, 0.f);
+    // the staged state_in (lane order, already times kappa) or zero
+    float2 c = has_state ? make_float2(c0[bh * 256 * D + o + pre], c0[bh * 256 * D + o + pim]) : make_float2(0.f, 0.f);
     const int64_t sst = p.B * p.H * 256 * D;  // floats per segment
     float* base = ws + bh * 256 * D + o;
     for (int s0 = 0; s0 + 1 < S; s0 += kBatch) {
@@ -1132,6 +1148,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                                                               const float* state_in, const uint16_t* tail_in,
                                                               float* state_out, uint16_t* tail_out,
                                                               const uint8_t* __restrict__ tab,
+                                                              const float* __restrict__ c0,
                                                               const float* __restrict__ carry, int64_t Lseg, int S,
                                                               int fold) {
     constexpr int RT = Cfg<D>::RT, KB = Cfg<D>::KB, YR = Cfg<D>::YR;
@@ -1170,17 +1187,17 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
     // carry kappa, undone by K and omega (both carry 1 / kappa) and on
     // the state's way in and out
     const float4 hc = reinterpret_cast<const float4*>(th + kTabHc)[0];
-    const float kap = hc.z, inv_kap = hc.w;
+    const float inv_kap = hc.w;
     const float odt = 4.f * hc.x * hc.w;        // 4 Delta / kappa, the output factor's constant part
     const float ks = -0.25f * kLn2 * hc.y * hc.w;  // K = -ln2 / (4 Delta kappa), the mode scores' scale
     const int rsb = static_cast<int>(H * D * 2);  // token stride, bytes
     // state entering the segment: state_in, the carry chain's output, or (fold)
     // state_in followed by the end states of the segments before this one.
-    // state_in is read here, in the prologue; only the last segment's block writes
-    // state_out, after its whole loop, and blocks are dispatched in index order
-    // with that block last, so the state may be updated in place.
+    // This kernel never reads state_in itself: the feature pass has staged
+    // kappa state_in in lane order (c0), so the last segment's block may write
+    // state_out into the same buffer whatever the order in which blocks run.
     const int64_t sstride = MM * 2 * D * 2;  // floats per (b, h) state
-    const float* sin = state_in ? state_in + bh * sstride : nullptr;
+    const float* sin = state_in ? c0 + bh * sstride : nullptr;
     const float* src = carry + (static_cast<int64_t>(seg > 0 ? seg - 1 : 0) * p.B * p.H + bh) * sstride;
     const float* e0 = carry + bh * sstride;
     const int64_t estride = p.B * p.H * sstride;
@@ -1199,7 +1216,8 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         if (seg > 0 && !fold) {
             u_load_lane<D>(U, src, kw);
         } else {
-            u_load<D>(U, sin, kw, kap);
+            if (sin != nullptr) u_load_lane<D>(U, sin, kw);
+            else u_load<D>(U, nullptr, kw, 1.f);
             if (nfold > 0) u_fold<D, kFoldTiles>(U, e0, estride, nfold, aseg, kw);
         }
         const __amdgpu_buffer_rsrc_t rq = seq_rsrc<D>(q, b, h, N, H, t_end);
@@ -1336,7 +1354,8 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             if (seg > 0 && !fold) {
                 g_load_lane<D>(G, src, vw);
             } else {
-                g_load<D>(G, sin, vw, kap);
+                if (sin != nullptr) g_load_lane<D>(G, sin, vw);
+                else g_load<D>(G, nullptr, vw, 1.f);
                 if (nfold > 0) g_fold<D, kFoldTiles>(G, e0, estride, nfold, aseg, vw);
             }
         }
@@ -1445,6 +1464,24 @@ void plan_segments(const Problem& p, int& S, int64_t& Lseg) {
     if (S < 1) S = 1;
 }
 
+// Workspace: per-head tables | the staged kappa state_in, [B H] states in lane
+// order | segment end states, [S-1][B H] | fp16 feature tiles, one z_k^T, z_v^T
+// pair per chunk slot of every segment.
+struct WsLayout {
+    size_t tab, c0, seg, zt, total;
+};
+WsLayout ws_layout(const Problem& p, int S, int64_t Lseg) {
+    const size_t state = static_cast<size_t>(MM) * 2 * p.d * 2 * sizeof(float);
+    const size_t pairs = static_cast<size_t>(p.B * p.H);
+    WsLayout w;
+    w.tab = 0;
+    w.c0 = static_cast<size_t>(p.H) * kTabBytes;
+    w.seg = w.c0 + pairs * state;
+    w.zt = w.seg + static_cast<size_t>(S - 1) * pairs * state;
+    w.total = w.zt + pairs * S * static_cast<size_t>(Lseg) * 2 * p.d * sizeof(_Float16);
+    return w;
+}
+
 template <int D>
 hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, const void* k, const void* v, void* o,
                   const float* state_in, const void* tail_in, float* state_out, void* tail_out, void* workspace,
@@ -1452,52 +1489,73 @@ hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, con
     int S;
     int64_t Lseg;
     plan_segments(p, S, Lseg);
+    const WsLayout lay = ws_layout(p, S, Lseg);
     const auto* q16 = static_cast<const uint16_t*>(q);
     const auto* k16 = static_cast<const uint16_t*>(k);
     const auto* v16 = static_cast<const uint16_t*>(v);
     const auto* t16 = static_cast<const uint16_t*>(tail_in);
-    uint8_t* tab = static_cast<uint8_t*>(workspace);
-    float* ws = reinterpret_cast<float*>(tab + static_cast<size_t>(p.H) * kTabBytes);
+    uint8_t* base = static_cast<uint8_t*>(workspace);
+    uint8_t* tab = base + lay.tab;
+    float* c0 = reinterpret_cast<float*>(base + lay.c0);
+    float* ws = reinterpret_cast<float*>(base + lay.seg);
+    _Float16* zt = reinterpret_cast<_Float16*>(base + lay.zt);
     const int64_t pairs = p.B * p.H;
-    _Float16* zt = reinterpret_cast<_Float16*>(ws + static_cast<size_t>(S - 1) * pairs * MM * 2 * D * 2);
-    const int64_t last_len = p.N - (S - 1) * Lseg;
     zoh_tables_kernel<<<dim3(static_cast<unsigned>(p.H), 17), kTabThreads, 0, stream>>>(p, prm, Lseg, tab);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    segment_state_kernel<D><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(p, prm, k16, v16, t16, tab, ws,
-                                                                                      zt, Lseg, S);
+    segment_state_kernel<D><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(p, prm, k16, v16, t16, state_in,
+                                                                                      tab, c0, ws, zt, Lseg, S);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int fold = S <= kFoldMax ? 1 : 0;
     if (S > 1 && !fold) {
         const int64_t threads = pairs * 128 * p.d;  // one complex element each
-        segment_carry_kernel<<<dim3(static_cast<unsigned>((threads + 255) / 256)), 256, 0, stream>>>(p, state_in, tab,
-                                                                                                  ws, S);
+        segment_carry_kernel<<<dim3(static_cast<unsigned>((threads + 255) / 256)), 256, 0, stream>>>(
+            p, state_in != nullptr, c0, tab, ws, S);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     chunked_forward_kernel<D><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(
         p, prm, q16, k16, zt, static_cast<uint16_t*>(o), state_in, t16, state_out, static_cast<uint16_t*>(tail_out),
-        tab, ws, Lseg, S, fold);
+        tab, c0, ws, Lseg, S, fold);
     return hipGetLastError();
 }
 
 }  // namespace
 }  // namespace cws
 
-size_t chunked_ws_workspace_bytes(const Problem& p) {
+bool chunked_supported(const Problem& p) {
+    // M = 64 modes, d = R in {64, 128}, conv width up to 4, the SiLU feature maps
+    if (!(p.bf16 && p.M == 64 && (p.d == 64 || p.d == 128) && p.W >= 1 && p.W <= 4)) return false;
+    if (p.rff_feat) return false;
+    // the kernels address one (b, h) sequence with 32-bit byte offsets
+    return p.N * p.H * p.d * 2 < (int64_t{1} << 31);
+}
+
+size_t chunked_workspace_bytes(const Problem& p) {
     int S;
     int64_t Lseg;
     cws::plan_segments(p, S, Lseg);
-    // tables, segment states, and one z_k^T, z_v^T tile pair per chunk slot
-    return static_cast<size_t>(p.H) * cws::kTabBytes +
-           static_cast<size_t>(S - 1) * p.B * p.H * p.M * 2 * p.d * 2 * sizeof(float) +
-           static_cast<size_t>(p.B * p.H) * S * static_cast<size_t>(Lseg) * 2 * p.d * sizeof(_Float16);
+    return cws::ws_layout(p, S, Lseg).total;
 }
 
-hipError_t launch_forward_chunked_ws(const Problem& p, const idattn_params& prm, const void* q, const void* k,
-                                     const void* v, void* o, const float* state_in, const void* tail_in,
-                                     float* state_out, void* tail_out, void* workspace, hipStream_t stream) {
+size_t chunked_workspace_bound(const Problem& p) {
+    // For one sequence (B = 1) of any n <= p.N tokens.  The plan gives
+    // s = min(smax, chunks) segments of cps = ceil(chunks / s) chunks; S cps <
+    // chunks + cps, and cps <= ceil(chunks / 2) once s >= 2 (S cps = chunks when
+    // s = 1), so the tiles cover at most chunks + ceil(chunks / 2) chunk slots
+    // and the end states at most smax - 1 segments: every term grows with N.
+    const size_t state = static_cast<size_t>(cws::MM) * 2 * p.d * 2 * sizeof(float);
+    const int64_t smax = p.H >= 256 ? 1 : 256 / p.H;
+    const int64_t chunks = (p.N + cws::L - 1) / cws::L;
+    const size_t slots = static_cast<size_t>(chunks + (chunks + 1) / 2);
+    return static_cast<size_t>(p.H) * cws::kTabBytes + static_cast<size_t>(p.H) * state +
+           static_cast<size_t>(smax - 1) * p.H * state + static_cast<size_t>(p.H) * slots * cws::L * 2 * p.d * 2;
+}
+
+hipError_t launch_forward_chunked(const Problem& p, const idattn_params& prm, const void* q, const void* k,
+                                  const void* v, void* o, const float* state_in, const void* tail_in,
+                                  float* state_out, void* tail_out, void* workspace, hipStream_t stream) {
     if (p.d == 128)
         return cws::launch<128>(p, prm, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, stream);
     return cws::launch<64>(p, prm, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, stream);

@@ -41,21 +41,18 @@ hipError_t launch_ssm_value_scan_readout_seq(const Problem& p, const idattn_para
                                              const float* state_in, void* o,
                                              float* state_out, const float* pden, hipStream_t stream);
 
-// ---- chunked MFMA path (bf16 I/O)
+// ---- chunked MFMA path (bf16 I/O; wave-specialised kernels for d = R in
+// {64, 128}, M = 64, W <= 4, the SiLU feature maps)
 size_t chunked_workspace_bytes(const Problem& p);
+// A bound on chunked_workspace_bytes over every B = 1 sequence of at most p.N
+// tokens (monotone in p.N).
+size_t chunked_workspace_bound(const Problem& p);
 bool chunked_supported(const Problem& p);
 // Also writes tail_out (when not NULL) like launch_tail_update.
 hipError_t launch_forward_chunked(const Problem& p, const idattn_params& prm,
                                   const void* q, const void* k, const void* v, void* o,
                                   const float* state_in, const void* tail_in,
                                   float* state_out, void* tail_out, void* workspace, hipStream_t stream);
-
-// wave-specialised kernels for d = R in {64, 128}, M = 64 (called by the two above)
-size_t chunked_ws_workspace_bytes(const Problem& p);
-hipError_t launch_forward_chunked_ws(const Problem& p, const idattn_params& prm,
-                                     const void* q, const void* k, const void* v, void* o,
-                                     const float* state_in, const void* tail_in,
-                                     float* state_out, void* tail_out, void* workspace, hipStream_t stream);
 
 // ---- state and tail plumbing
 // tail_out = last W-1 raw tokens of [tail_in (or zeros) ; x]; safe in place.

@@ -336,3 +336,23 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         binding.idattn_version()
     with pytest.raises(RuntimeError, match="missing"):
         binding.idattn_forward_workspace_size(dims())
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("H", [1, 2, 4, 8, 12, 16])
+def test_varlen_workspace_covers_every_sequence(H, d):
+    """The packed-batch workspace covers the chunked workspace of every
+    single sequence of 1..T tokens (the chunked plan runs one launch per
+    sequence), and it never shrinks as T grows."""
+    prev = 0
+    for T in list(range(1, 2200, 7)) + [4096, 6000, 16384]:
+        got = fs.idattn_forward_varlen_workspace_size(fs.make_dims(3, T, H, d, 64, 4, "bf16", "auto"))
+        assert got >= prev, (T, got, prev)
+        prev = got
+    worst = 0
+    for n in range(1, 2200):
+        one = fs.idattn_forward_workspace_size(fs.make_dims(1, n, H, d, 64, 4, "bf16", "chunked"))
+        worst = max(worst, one)
+        if n % 97 == 0 or n in (961, 1601, 2199):
+            bound = fs.idattn_forward_varlen_workspace_size(fs.make_dims(2, n, H, d, 64, 4, "bf16", "auto"))
+            assert bound >= worst, (n, bound, worst)
