@@ -9,14 +9,15 @@ binding on the current stream.
 from __future__ import annotations
 
 from .binding import (ALGO, EXPORTS, FEATURE_NORM, IO, LIB_PATH, STATUS, IdattnDims, IdattnError, IdattnParams,
-                      idattn_decode_step, idattn_decode_step_normalized, idattn_forward,
+                      NOALLOC_SCRATCH_BYTES, idattn_decode_step, idattn_decode_step_normalized, idattn_forward,
+                      idattn_forward_noalloc,
                       idattn_forward_normalized,
                       idattn_forward_normalized_workspace_size, idattn_forward_varlen,
                       idattn_forward_varlen_workspace_size, idattn_forward_workspace_size,
                       idattn_last_error, idattn_status_string, idattn_version, load_library,
                       make_dims, make_params)
 
-__all__ = ["ALGO", "EXPORTS", "FEATURE_NORM", "IO", "LIB_PATH", "STATUS", "IdattnDims", "IdattnError", "IdattnParams",
+__all__ = ["ALGO", "EXPORTS", "NOALLOC_SCRATCH_BYTES", "idattn_forward_noalloc", "FEATURE_NORM", "IO", "LIB_PATH", "STATUS", "IdattnDims", "IdattnError", "IdattnParams",
            "idattn_decode_step", "idattn_decode_step_normalized", "idattn_forward", "idattn_forward_normalized",
            "idattn_forward_normalized_workspace_size", "idattn_forward_varlen", "idattn_forward_varlen_workspace_size",
            "idattn_forward_workspace_size",

@@ -20,7 +20,8 @@ IO = {"f32": 0, "bf16": 1}
 ALGO = {"auto": 0, "sequential": 1, "chunked": 2}
 FEATURE_NORM = {"squared": 0, "unit": 1, "rff": 2}
 
-EXPORTS = ("idattn_forward_workspace_size", "idattn_forward", "idattn_forward_normalized_workspace_size",
+EXPORTS = ("idattn_forward_workspace_size", "idattn_forward", "idattn_forward_noalloc",
+           "idattn_forward_normalized_workspace_size",
            "idattn_forward_normalized", "idattn_forward_varlen_workspace_size", "idattn_forward_varlen",
            "idattn_decode_step", "idattn_decode_step_normalized", "idattn_status_string", "idattn_last_error",
            "idattn_version")
@@ -60,6 +61,8 @@ def load_library(path: str = LIB_PATH):
     lib.idattn_forward_workspace_size.restype = c_int
     lib.idattn_forward.argtypes = [P(IdattnDims), P(IdattnParams)] + [c_void_p] * 9 + [c_size_t, c_void_p]
     lib.idattn_forward.restype = c_int
+    lib.idattn_forward_noalloc.argtypes = [P(IdattnDims), P(IdattnParams)] + [c_void_p] * 9
+    lib.idattn_forward_noalloc.restype = c_int
     lib.idattn_forward_normalized_workspace_size.argtypes = [P(IdattnDims), P(c_size_t)]
     lib.idattn_forward_normalized_workspace_size.restype = c_int
     lib.idattn_forward_normalized.argtypes = [P(IdattnDims), P(IdattnParams)] + [c_void_p] * 11 + [c_size_t, c_void_p]
@@ -152,6 +155,16 @@ def idattn_forward(dims, params, q, k, v, o, state_in=None, tail_in=None, state_
         ctypes.byref(dims), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
         _ptr(state_in), _ptr(tail_in), _ptr(state_out), _ptr(tail_out), _ptr(workspace),
         int(workspace_bytes), _stream(stream)))
+
+
+def idattn_forward_noalloc(dims, params, q, k, v, o, state_in=None, tail_in=None, state_out=None,
+                           tail_out=None, stream=None) -> None:
+    _check(load_library().idattn_forward_noalloc(
+        ctypes.byref(dims), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+        _ptr(state_in), _ptr(tail_in), _ptr(state_out), _ptr(tail_out), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 192 << 20
 
 
 def idattn_forward_normalized_workspace_size(dims: IdattnDims) -> int:

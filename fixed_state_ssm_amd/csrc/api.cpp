@@ -10,6 +10,8 @@
 #include "../../include/idattn.h"
 #include "launch.h"
 
+static_assert(idattn::kNoallocScratchBytes == IDATTN_NOALLOC_SCRATCH_BYTES, "scratch size must match the header");
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -273,10 +275,16 @@ idattn_status idattn_forward_workspace_size(const idattn_dims* dims, size_t* byt
     return workspace_bytes(*dims, resolve_algo(*dims), bytes);
 }
 
-idattn_status idattn_forward(const idattn_dims* dims, const idattn_params* params, const void* q,
-                             const void* k, const void* v, void* o, const float* state_in,
-                             const void* tail_in, float* state_out, void* tail_out, void* workspace,
-                             size_t workspace_bytes_given, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both dense forward entry points.  noalloc: the workspace is the library's
+// scratch array (its address looked up after validation), else the caller's.
+idattn_status forward_impl(const idattn_dims* dims, const idattn_params* params, const void* q, const void* k,
+                           const void* v, void* o, const float* state_in, const void* tail_in, float* state_out,
+                           void* tail_out, void* workspace, size_t workspace_bytes_given, void* stream,
+                           bool noalloc) {
     idattn_status st = check_dims(dims, false);
     if (st != IDATTN_OK) return st;
     st = check_params(*dims, params);
@@ -287,19 +295,33 @@ idattn_status idattn_forward(const idattn_dims* dims, const idattn_params* param
     size_t need = 0;
     st = workspace_bytes(D, algo, &need);
     if (st != IDATTN_OK) return st;
-    if (need > 0 && workspace == nullptr) return fail(IDATTN_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
-    if (workspace_bytes_given < need)
-        return fail(IDATTN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_given, need);
+    if (noalloc) {
+        if (need > idattn::kNoallocScratchBytes)
+            return fail(IDATTN_ERR_WORKSPACE,
+                        "these dims need %zu bytes of scratch; idattn_forward_noalloc has %zu "
+                        "(IDATTN_NOALLOC_SCRATCH_BYTES); use idattn_forward with a workspace",
+                        need, idattn::kNoallocScratchBytes);
+    } else {
+        if (need > 0 && workspace == nullptr)
+            return fail(IDATTN_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+        if (workspace_bytes_given < need)
+            return fail(IDATTN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_given, need);
+    }
 
     const size_t io = D.io_dtype == IDATTN_IO_BF16 ? 2 : 4;
     const size_t act = static_cast<size_t>(D.B) * D.N * D.H * D.d * io;
-    st = check_forward_buffers(D, *params, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, need, act,
-                               range("none", nullptr, 0));
+    // the scratch array cannot overlap a caller's buffer: check without it
+    st = check_forward_buffers(D, *params, q, k, v, o, state_in, tail_in, state_out, tail_out,
+                               noalloc ? nullptr : workspace, noalloc ? 0 : need, act, range("none", nullptr, 0));
     if (st != IDATTN_OK) return st;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const idattn::Problem p = problem(D);
     if (D.N == 0) return copy_through(D, state_in, tail_in, state_out, tail_out, s);
+    if (noalloc && need > 0) {
+        const hipError_t e = idattn::noalloc_scratch(&workspace);
+        if (e != hipSuccess) return hip_fail(e, "scratch address");
+    }
+    const idattn::Problem p = problem(D);
     if (algo == IDATTN_ALGO_CHUNKED) {
         const hipError_t e = idattn::launch_forward_chunked(p, *params, q, k, v, o, state_in, tail_in, state_out,
                                                             tail_out, workspace, s);
@@ -307,6 +329,25 @@ idattn_status idattn_forward(const idattn_dims* dims, const idattn_params* param
         return IDATTN_OK;  // the chunked forward writes tail_out itself
     }
     return run_sequential(p, *params, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+idattn_status idattn_forward(const idattn_dims* dims, const idattn_params* params, const void* q,
+                             const void* k, const void* v, void* o, const float* state_in,
+                             const void* tail_in, float* state_out, void* tail_out, void* workspace,
+                             size_t workspace_bytes_given, void* stream) {
+    return forward_impl(dims, params, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace,
+                        workspace_bytes_given, stream, false);
+}
+
+idattn_status idattn_forward_noalloc(const idattn_dims* dims, const idattn_params* params, const void* q,
+                                     const void* k, const void* v, void* o, const float* state_in,
+                                     const void* tail_in, float* state_out, void* tail_out, void* stream) {
+    return forward_impl(dims, params, q, k, v, o, state_in, tail_in, state_out, tail_out, nullptr, 0, stream,
+                        true);
 }
 
 idattn_status idattn_forward_normalized_workspace_size(const idattn_dims* dims, size_t* bytes) {

@@ -54,6 +54,11 @@ hipError_t launch_forward_chunked(const Problem& p, const idattn_params& prm,
                                   const float* state_in, const void* tail_in,
                                   float* state_out, void* tail_out, void* workspace, hipStream_t stream);
 
+// ---- the library's own scratch memory (idattn_forward_noalloc)
+constexpr size_t kNoallocScratchBytes = size_t{192} << 20;
+// Device address of this device's scratch array (looked up once per device).
+hipError_t noalloc_scratch(void** ptr);
+
 // ---- state and tail plumbing
 // tail_out = last W-1 raw tokens of [tail_in (or zeros) ; x]; safe in place.
 hipError_t launch_tail_update(const Problem& p, const void* q, const void* k,

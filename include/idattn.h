@@ -159,6 +159,31 @@ idattn_status idattn_forward(const idattn_dims *dims, const idattn_params *param
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * idattn_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same kernels and the same result as idattn_forward, with the workspace
+ * taken from the library's own scratch array instead of the caller's:
+ * IDATTN_NOALLOC_SCRATCH_BYTES of device memory that each GPU the library runs
+ * on holds from the first use of the library on that device until the
+ * process ends.  The call allocates and frees nothing.
+ *
+ *  arguments as for idattn_forward, without workspace and workspace_bytes.
+ * Dims whose workspace (idattn_forward_workspace_size) exceeds
+ * IDATTN_NOALLOC_SCRATCH_BYTES return IDATTN_ERR_WORKSPACE before any HIP
+ * call; 192 MiB covers the chunked forward of B=8 H=12 N=4096 d=64,
+ * B=4 H=16 N=4096 d=128 and B=1 H=16 N=14336 d=128.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give wrong results.  Nothing needs
+ * clearing between calls: each call writes every scratch byte it reads.
+ */
+#define IDATTN_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
+
+idattn_status idattn_forward_noalloc(const idattn_dims *dims, const idattn_params *params,
+                                     const void *q, const void *k, const void *v, void *o,
+                                     const float *state_in, const void *tail_in,
+                                     float *state_out, void *tail_out, void *stream);
+
+/*
  * Forward with the normalised readout of the derivation (German summary,
  * "Theoretische Herleitung"; Chinese rendering, Fig. 1: a third in-loop state
  * eta, M x 1, and the readout F_q U^T Gamma / (F_q U^T eta)), which the

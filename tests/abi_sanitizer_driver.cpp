@@ -98,6 +98,22 @@ int main() {
     expect(forward(x, p, need, fake(1, 64)), IDATTN_ERR_ALIAS, "o overlaps q");
     expect(forward(x, p, need, fake(4), fake(4)), IDATTN_ERR_ALIAS, "state_out overlaps o");
     expect(forward(x, p, need, fake(4), fake(7), fake(1, 2)), IDATTN_ERR_ARG, "misaligned q");
+    // the allocation-free forward: too large for the scratch array, and argument errors
+    {
+        const idattn_dims big = dims(64, 4096, 16, 128, 64, 4, IDATTN_IO_BF16, IDATTN_ALGO_CHUNKED);
+        expect(idattn_forward_noalloc(&big, &p, fake(1), fake(2), fake(3), fake(4), nullptr, nullptr, nullptr,
+                                      nullptr, nullptr),
+               IDATTN_ERR_WORKSPACE, "noalloc beyond the scratch array");
+        expect(idattn_forward_noalloc(nullptr, &p, fake(1), fake(2), fake(3), fake(4), nullptr, nullptr, nullptr,
+                                      nullptr, nullptr),
+               IDATTN_ERR_NULL, "noalloc NULL dims");
+        expect(idattn_forward_noalloc(&x, &p, fake(1), fake(2), fake(3), fake(1, 64), nullptr, nullptr, nullptr,
+                                      nullptr, nullptr),
+               IDATTN_ERR_ALIAS, "noalloc o overlaps q");
+        expect(idattn_forward_noalloc(&x, &p, fake(1), fake(2), fake(3), nullptr, nullptr, nullptr, nullptr, nullptr,
+                                      nullptr),
+               IDATTN_ERR_NULL, "noalloc NULL o");
+    }
     {
         idattn_dims y = x;
         y.B = 0;

@@ -356,3 +356,28 @@ def test_varlen_workspace_covers_every_sequence(H, d):
         if n % 97 == 0 or n in (961, 1601, 2199):
             bound = fs.idattn_forward_varlen_workspace_size(fs.make_dims(2, n, H, d, 64, 4, "bf16", "auto"))
             assert bound >= worst, (n, bound, worst)
+
+
+def test_noalloc_validation():
+    """idattn_forward_noalloc rejects, before any HIP call, dims whose
+    workspace exceeds the scratch array, and the usual argument errors."""
+    lib = fs.load_library()
+    prm = fs.make_params({k: FAKE for k in fs.PARAM_KEYS})
+    big = fs.make_dims(64, 4096, 16, 128, 64, 4, "bf16", "chunked")
+    assert fs.idattn_forward_workspace_size(big) > fs.NOALLOC_SCRATCH_BYTES
+    st = lib.idattn_forward_noalloc(ctypes.byref(big), ctypes.byref(prm), FAKE, FAKE + (1 << 32),
+                                    FAKE + (2 << 32), FAKE + (3 << 32), None, None, None, None, None)
+    assert fs.STATUS[st] == "IDATTN_ERR_WORKSPACE"
+    assert "IDATTN_NOALLOC_SCRATCH_BYTES" in fs.idattn_last_error()
+    ok = fs.make_dims(4, 4096, 16, 128, 64, 4, "bf16", "chunked")
+    assert fs.idattn_forward_workspace_size(ok) <= fs.NOALLOC_SCRATCH_BYTES
+    st = lib.idattn_forward_noalloc(ctypes.byref(ok), ctypes.byref(prm), None, FAKE, FAKE, FAKE, None, None,
+                                    None, None, None)
+    assert fs.STATUS[st] == "IDATTN_ERR_NULL"
+    # o overlaps q
+    st = lib.idattn_forward_noalloc(ctypes.byref(ok), ctypes.byref(prm), FAKE, FAKE + (1 << 32), FAKE + (2 << 32),
+                                    FAKE + 4096, None, None, None, None, None)
+    assert fs.STATUS[st] == "IDATTN_ERR_ALIAS"
+    text = open(HEADER).read()
+    assert "#define IDATTN_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)" in text
+    assert fs.NOALLOC_SCRATCH_BYTES == 192 << 20

@@ -12,7 +12,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "fixed_state_ssm_amd", "csrc")
-SOURCES = ["api.cpp", "featmap.hip", "scan_seq.hip", "chunked.hip", "chunked_ws.hip", "decode.hip"]
+from fixed_state_ssm_amd.build import SOURCES  # noqa: E402
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
