@@ -42,7 +42,7 @@ METRIC = "mixer tokens/sec fwd (1.3B shape, N=4096) + % of HBM roofline, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 FP32_PEAK_TFLOPS = 157.3
 FP16_MFMA_PEAK_TFLOPS = 2500.0
-KERNEL_SOURCES = ["fixed_state_ssm_amd/csrc/chunked_ws.hip",
+KERNEL_SOURCES = ["fixed_state_ssm_amd/csrc/chunked_ws.hip", "fixed_state_ssm_amd/csrc/backward.hip",
                   "fixed_state_ssm_amd/csrc/featmap.hip", "fixed_state_ssm_amd/csrc/scan_seq.hip",
                   "fixed_state_ssm_amd/csrc/decode.hip", "fixed_state_ssm_amd/csrc/common.h",
                   "fixed_state_ssm_amd/csrc/launch.h", "fixed_state_ssm_amd/csrc/api.cpp"]
@@ -323,6 +323,50 @@ def normalized_bench(torch, fs, WL, config, steps=20, warmup=5):
             "ms_per_call": dt * 1e3, "tokens_per_s": B * N / dt}
 
 
+def backward_bench(torch, fs, WL, config, steps=5, warmup=2):
+    """idattn_backward at the bench's shape (bf16 I/O, fp32 arithmetic, the
+    sequential algorithm): every gradient of a forward over the workload,
+    inputs and the output gradient resident in HBM."""
+    import numpy as np
+    s = WL.spec(config)
+    q, k, v = WL.make_rows(s)
+    p = fs.params_to_device(WL.make_params(s))
+    B, N, H, d, M, W = s["B"], s["N"], s["H"], s["d"], s["M"], s["W"]
+
+    def up(x):
+        return torch.from_numpy(WL.bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    qd, kd, vd = up(q), up(k), up(v)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    go = torch.randn(qd.shape, generator=g, device="cuda").to(torch.bfloat16)
+    dims = fs.make_dims(B, N, H, d, M, W, "bf16", "auto")
+    nbytes = fs.idattn_backward_workspace_size(dims)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    out = {"q": torch.empty_like(qd), "k": torch.empty_like(kd), "v": torch.empty_like(vd)}
+    for key in fs.PARAM_KEYS:
+        out[key] = torch.empty_like(p[key])
+    gp = fs.make_param_grads(out)
+    prm = fs.make_params(p)
+
+    def call():
+        fs.idattn_backward(dims, prm, qd, kd, vd, None, None, go, None, out["q"], out["k"], out["v"], gp, None, ws,
+                           nbytes)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"workload": f"{config}: B={B} H={H} N={N} d=R={d} M={M} W={W}, bf16 I/O, gradients of q, k, v and every "
+                        f"parameter, sequential fp32 algorithm", "ms_per_call": ms, "tokens_per_s": B * N / (ms * 1e-3)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -439,6 +483,7 @@ def main():
         out["decode"] = decode_bench(torch, fs, steps=20, warmup=20)
         out["varlen"] = varlen_bench(torch, fs, WL)
         out["normalized"] = normalized_bench(torch, fs, WL, args.config)
+        out["backward"] = backward_bench(torch, fs, WL, args.config)
     del sets, ws
     torch.cuda.empty_cache()
     if not args.no_cpu:

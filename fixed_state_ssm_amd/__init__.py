@@ -8,7 +8,8 @@ binding on the current stream.
 """
 from __future__ import annotations
 
-from .binding import (ALGO, EXPORTS, FEATURE_NORM, IO, LIB_PATH, STATUS, IdattnDims, IdattnError, IdattnParams,
+from .binding import (ALGO, EXPORTS, IdattnParamGrads, idattn_backward, idattn_backward_workspace_size,
+                      make_param_grads, FEATURE_NORM, IO, LIB_PATH, STATUS, IdattnDims, IdattnError, IdattnParams,
                       NOALLOC_SCRATCH_BYTES, idattn_decode_step, idattn_decode_step_normalized, idattn_forward,
                       idattn_forward_noalloc,
                       idattn_forward_normalized,
@@ -17,7 +18,8 @@ from .binding import (ALGO, EXPORTS, FEATURE_NORM, IO, LIB_PATH, STATUS, IdattnD
                       idattn_last_error, idattn_status_string, idattn_version, load_library,
                       make_dims, make_params)
 
-__all__ = ["ALGO", "EXPORTS", "NOALLOC_SCRATCH_BYTES", "idattn_forward_noalloc", "FEATURE_NORM", "IO", "LIB_PATH", "STATUS", "IdattnDims", "IdattnError", "IdattnParams",
+__all__ = ["IdattnParamGrads", "idattn_backward", "idattn_backward_workspace_size", "make_param_grads", "backward",
+           "ALGO", "EXPORTS", "NOALLOC_SCRATCH_BYTES", "idattn_forward_noalloc", "FEATURE_NORM", "IO", "LIB_PATH", "STATUS", "IdattnDims", "IdattnError", "IdattnParams",
            "idattn_decode_step", "idattn_decode_step_normalized", "idattn_forward", "idattn_forward_normalized",
            "idattn_forward_normalized_workspace_size", "idattn_forward_varlen", "idattn_forward_varlen_workspace_size",
            "idattn_forward_workspace_size",
@@ -131,6 +133,29 @@ def forward_varlen(q, k, v, params: dict, cu_seqlens, *, state_in=None, tail_in=
     idattn_forward_varlen(dims, make_params(params), cu_seqlens, q, k, v, o, state_in, tail_in, state_out, tail_out,
                           ws, nbytes, stream, cu_seqlens_host=host)
     return (o, state_out, tail_out) if return_state else o
+
+
+def backward(q, k, v, params: dict, grad_o, *, state_in=None, tail_in=None, grad_state=None, eps_feat=1e-6,
+             eps_norm=1e-6, feature_norm="squared", stream=None):
+    """Gradients of sum(grad_o * o) + Re sum(conj(grad_state) * state_out) for
+    the forward over q, k, v [B, N, H, d] (same dtype for all) with params,
+    state_in and tail_in.  Returns a dict: q, k, v (q's dtype), the parameter
+    keys (float32, shaped like the parameters) and state (float32 [B, H, M,
+    2d, 2], the state_in gradient)."""
+    import torch
+    B, N, H, d = q.shape
+    M = params["A"].shape[1]
+    W = params["conv_q"].shape[-1]
+    dims = make_dims(B, N, H, d, M, W, _io_name(q), "auto", eps_feat, eps_norm, feature_norm)
+    nbytes = idattn_backward_workspace_size(dims)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    out = {"q": torch.empty_like(q), "k": torch.empty_like(k), "v": torch.empty_like(v)}
+    for key in PARAM_KEYS:
+        out[key] = torch.empty_like(params[key])
+    out["state"] = torch.empty((B, H, M, 2 * d, 2), dtype=torch.float32, device=q.device)
+    idattn_backward(dims, make_params(params), q, k, v, state_in, tail_in, grad_o, grad_state, out["q"], out["k"],
+                    out["v"], make_param_grads(out), out["state"], ws, nbytes, stream)
+    return out
 
 
 def decode_step(q_t, k_t, v_t, params: dict, state, tail, *, eps_feat=1e-6, eps_norm=1e-6, feature_norm="squared",

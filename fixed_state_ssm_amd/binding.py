@@ -23,8 +23,8 @@ FEATURE_NORM = {"squared": 0, "unit": 1, "rff": 2}
 EXPORTS = ("idattn_forward_workspace_size", "idattn_forward", "idattn_forward_noalloc",
            "idattn_forward_normalized_workspace_size",
            "idattn_forward_normalized", "idattn_forward_varlen_workspace_size", "idattn_forward_varlen",
-           "idattn_decode_step", "idattn_decode_step_normalized", "idattn_status_string", "idattn_last_error",
-           "idattn_version")
+           "idattn_decode_step", "idattn_decode_step_normalized", "idattn_backward_workspace_size",
+           "idattn_backward", "idattn_status_string", "idattn_last_error", "idattn_version")
 
 
 class IdattnDims(ctypes.Structure):
@@ -36,6 +36,11 @@ class IdattnDims(ctypes.Structure):
 class IdattnParams(ctypes.Structure):
     _fields_ = [("conv_q", c_void_p), ("conv_k", c_void_p), ("gain", c_void_p), ("bias", c_void_p),
                 ("log_dt", c_void_p), ("A", c_void_p), ("Bc", c_void_p), ("rff_omega", c_void_p)]
+
+
+class IdattnParamGrads(ctypes.Structure):
+    _fields_ = [("conv_q", c_void_p), ("conv_k", c_void_p), ("gain", c_void_p), ("bias", c_void_p),
+                ("log_dt", c_void_p), ("A", c_void_p), ("Bc", c_void_p)]
 
 
 class IdattnError(RuntimeError):
@@ -75,6 +80,11 @@ def load_library(path: str = LIB_PATH):
     lib.idattn_decode_step_normalized.restype = c_int
     lib.idattn_decode_step.argtypes = [P(IdattnDims), P(IdattnParams)] + [c_void_p] * 7
     lib.idattn_decode_step.restype = c_int
+    lib.idattn_backward_workspace_size.argtypes = [P(IdattnDims), P(c_size_t)]
+    lib.idattn_backward_workspace_size.restype = c_int
+    lib.idattn_backward.argtypes = ([P(IdattnDims), P(IdattnParams)] + [c_void_p] * 10 + [P(IdattnParamGrads)]
+                                    + [c_void_p, c_void_p, c_size_t, c_void_p])
+    lib.idattn_backward.restype = c_int
     lib.idattn_status_string.argtypes = [c_int]
     lib.idattn_status_string.restype = ctypes.c_char_p
     lib.idattn_last_error.argtypes = []
@@ -199,6 +209,27 @@ def idattn_forward_varlen(dims, params, cu_seqlens, q, k, v, o, state_in=None, t
         ctypes.byref(dims), ctypes.byref(params), _ptr(cu_seqlens), host, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
         _ptr(state_in), _ptr(tail_in), _ptr(state_out), _ptr(tail_out), _ptr(workspace),
         int(workspace_bytes), _stream(stream)))
+
+
+def make_param_grads(g: dict) -> IdattnParamGrads:
+    """g: dict of float32 device tensors conv_q, conv_k, gain, bias, log_dt,
+    A, Bc shaped like the parameters (the outputs of idattn_backward)."""
+    keys = ("conv_q", "conv_k", "gain", "bias", "log_dt", "A", "Bc")
+    return IdattnParamGrads(*(_ptr(g[k]) for k in keys))
+
+
+def idattn_backward_workspace_size(dims: IdattnDims) -> int:
+    out = c_size_t(0)
+    _check(load_library().idattn_backward_workspace_size(ctypes.byref(dims), ctypes.byref(out)))
+    return out.value
+
+
+def idattn_backward(dims, params, q, k, v, state_in, tail_in, grad_o, grad_state, grad_q, grad_k, grad_v,
+                    grad_params, grad_state_in=None, workspace=None, workspace_bytes=0, stream=None) -> None:
+    _check(load_library().idattn_backward(
+        ctypes.byref(dims), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(state_in), _ptr(tail_in),
+        _ptr(grad_o), _ptr(grad_state), _ptr(grad_q), _ptr(grad_k), _ptr(grad_v), ctypes.byref(grad_params),
+        _ptr(grad_state_in), _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def idattn_decode_step(dims, params, q_t, k_t, v_t, o_t, state, tail, stream=None) -> None:

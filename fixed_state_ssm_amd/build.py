@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libidattn.so")
 OBJ_DIR = os.path.join(PKG, "_build")
-SOURCES = ["api.cpp", "featmap.hip", "scan_seq.hip", "chunked_ws.hip", "decode.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "featmap.hip", "scan_seq.hip", "chunked_ws.hip", "decode.hip", "backward.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -527,6 +527,100 @@ idattn_status idattn_forward_varlen(const idattn_dims* dims, const idattn_params
 
 namespace {
 
+idattn_status check_backward_dims(const idattn_dims* dims) {
+    idattn_status st = check_dims(dims, false);
+    if (st != IDATTN_OK) return st;
+    if (dims->feature_norm == IDATTN_FEATURE_RFF)
+        return fail(IDATTN_ERR_UNSUPPORTED, "the backward pass has the SiLU feature maps only (squared, unit)");
+    if (dims->algo == IDATTN_ALGO_CHUNKED)
+        return fail(IDATTN_ERR_UNSUPPORTED, "the backward pass runs on the sequential algorithm only");
+    return IDATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+idattn_status idattn_backward_workspace_size(const idattn_dims* dims, size_t* bytes) {
+    if (bytes == nullptr) return fail(IDATTN_ERR_NULL, "bytes is NULL");
+    const idattn_status st = check_backward_dims(dims);
+    if (st != IDATTN_OK) return st;
+    *bytes = dims->N == 0 ? 0 : idattn::backward_workspace_bytes(problem(*dims));
+    return IDATTN_OK;
+}
+
+idattn_status idattn_backward(const idattn_dims* dims, const idattn_params* params, const void* q, const void* k,
+                              const void* v, const float* state_in, const void* tail_in, const void* grad_o,
+                              const float* grad_state, void* grad_q, void* grad_k, void* grad_v,
+                              const idattn_param_grads* grad_params, float* grad_state_in, void* workspace,
+                              size_t workspace_bytes_given, void* stream) {
+    idattn_status st = check_backward_dims(dims);
+    if (st != IDATTN_OK) return st;
+    st = check_params(*dims, params);
+    if (st != IDATTN_OK) return st;
+    const idattn_dims& D = *dims;
+    if (grad_params == nullptr) return fail(IDATTN_ERR_NULL, "grad_params is NULL");
+    const idattn_param_grads& G = *grad_params;
+    if (!G.conv_q || !G.conv_k || !G.gain || !G.bias || !G.log_dt || !G.A || !G.Bc)
+        return fail(IDATTN_ERR_NULL, "a parameter-gradient pointer is NULL");
+    if (D.N > 0 && (!q || !k || !v || !grad_o || !grad_q || !grad_k || !grad_v))
+        return fail(IDATTN_ERR_NULL, "q, k, v, grad_o, grad_q, grad_k and grad_v must be non-NULL");
+    const size_t need = D.N == 0 ? 0 : idattn::backward_workspace_bytes(problem(D));
+    if (need > 0 && workspace == nullptr) return fail(IDATTN_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+    if (workspace_bytes_given < need)
+        return fail(IDATTN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_given, need);
+    {
+        const void* ptrs[] = {q, k, v, state_in, tail_in, grad_o, grad_state, grad_q, grad_k, grad_v, grad_state_in,
+                              workspace, G.conv_q, G.conv_k, G.gain, G.bias, G.log_dt, G.A, G.Bc};
+        for (const void* ptr : ptrs)
+            if (misaligned(ptr)) return fail(IDATTN_ERR_ARG, "device buffers must be 16-byte aligned");
+    }
+    const size_t io = D.io_dtype == IDATTN_IO_BF16 ? 2 : 4;
+    const size_t act = static_cast<size_t>(D.B) * D.N * D.H * D.d * io;
+    const size_t stb = static_cast<size_t>(D.B) * D.H * D.M * 2 * D.d * 2 * sizeof(float);
+    const size_t tlb = static_cast<size_t>(D.B) * D.H * 2 * (D.W - 1) * D.d * io;
+    const size_t conv = static_cast<size_t>(D.H * D.d * D.W) * 4, gb = static_cast<size_t>(D.H * 2 * D.d) * 4;
+    const size_t mb = static_cast<size_t>(D.H * D.M * 2) * 4;
+    const Range outs[] = {range("grad_q", grad_q, act), range("grad_k", grad_k, act), range("grad_v", grad_v, act),
+                          range("grad_state_in", grad_state_in, stb), range("workspace", workspace, need),
+                          range("grad_conv_q", G.conv_q, conv), range("grad_conv_k", G.conv_k, conv),
+                          range("grad_gain", G.gain, gb), range("grad_bias", G.bias, gb),
+                          range("grad_log_dt", G.log_dt, D.H * 4), range("grad_A", G.A, mb), range("grad_Bc", G.Bc, mb)};
+    const Range ins[] = {range("q", q, act), range("k", k, act), range("v", v, act), range("state_in", state_in, stb),
+                         range("tail_in", tail_in, tlb), range("grad_o", grad_o, act),
+                         range("grad_state", grad_state, stb)};
+    constexpr int n_outs = sizeof(outs) / sizeof(outs[0]);
+    for (int i = 0; i < n_outs; ++i) {
+        for (int j = 0; j < n_outs; ++j)
+            if (i != j && overlap(outs[i], outs[j])) return fail(IDATTN_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+        for (const Range& b : ins)
+            if (overlap(outs[i], b)) return fail(IDATTN_ERR_ALIAS, "%s overlaps %s", outs[i].name, b.name);
+    }
+    st = check_params_disjoint(D, *params, outs, n_outs);
+    if (st != IDATTN_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (D.N == 0) {
+        hipError_t e = hipSuccess;
+        float* const zero_outs[] = {G.conv_q, G.conv_k, G.gain, G.bias, G.log_dt, G.A, G.Bc};
+        const size_t zero_bytes[] = {conv, conv, gb, gb, static_cast<size_t>(D.H) * 4, mb, mb};
+        for (int i = 0; i < 7 && e == hipSuccess; ++i)
+            e = idattn::launch_copy_or_zero(nullptr, zero_outs[i], static_cast<int64_t>(zero_bytes[i] / 4), s);
+        if (e == hipSuccess && grad_state_in != nullptr)
+            e = idattn::launch_copy_or_zero(grad_state, grad_state_in, static_cast<int64_t>(stb / 4), s);
+        if (e != hipSuccess) return hip_fail(e, "backward with no tokens");
+        return IDATTN_OK;
+    }
+    const hipError_t e = idattn::launch_backward(problem(D), *params, q, k, v, state_in, tail_in, grad_o, grad_state,
+                                                 grad_q, grad_k, grad_v, G, grad_state_in, workspace, s);
+    if (e != hipSuccess) return hip_fail(e, "backward");
+    return IDATTN_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
 // Both decode entry points; eta (normalised readout) is NULL for the plain one.
 idattn_status decode_impl(const idattn_dims* dims, const idattn_params* params, const void* q_t, const void* k_t,
                           const void* v_t, void* o_t, float* state, void* tail, float* eta, bool normalized,

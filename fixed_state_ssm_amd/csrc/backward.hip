@@ -1,0 +1,916 @@
+// Backward pass of the mixer: gradients of a scalar loss
+//   L = sum grad_o . o + Re sum conj(grad_state) . state_out
+// with respect to q, k, v, every parameter and the carried state, in fp32 and
+// one time step after another (the sequential algorithm).  The pages train
+// the layer inside language models (Chinese rendering, abstract and section
+// 1; German summary, "Skalierbare Implementierung"), which is what needs these
+// gradients; they print no backward pass, so this differentiates the forward
+// exactly as it is read (plain bilinear products, per-half RMSNorm, ZOH).
+//
+// Complex gradients follow g_z = dL/dRe z + i dL/dIm z; for a holomorphic
+// map w = f(z) that gives g_z = conj(f'(z)) g_w.  Per (b, h), with the
+// forward's U_m(i), Gamma_m(i), s_m(i) = xi_q(i) . U_m(i):
+//   g_s_m(i)   = sum_c g_o(i)_c conj(Gamma_m,c(i))
+//   g_xi_q(i)  = sum_m Re(g_s_m(i) conj(U_m(i)))
+//   Ubar(i)    = xi_q(i) g_s(i) + conj(abar) Ubar(i+1)      (reverse time)
+//   Gbar(i)    = g_o(i) conj(s(i)) + conj(abar) Gbar(i+1)   (reverse time)
+//   g_z_k(i)   = Re sum_m conj(bbar_m) Ubar_m(i),   g_z_v likewise with Gbar
+//   g_bbar_m   = sum_i [Ubar_m(i) . z_k(i) + Gbar_m(i) . z_v(i)]
+//   g_abar_m   = sum_i [g_s_m(i) conj(xi_q(i) . V_m(i)) + conj(s_m(i)) sum_c g_o(i)_c conj(W_m,c(i))]
+//                (+ the state_out terms), with V = dU/dabar and W = dGamma/dabar
+//                carried forward: V(i) = abar V(i-1) + U(i-1), W likewise.
+// g_abar is taken in this forward form so that no kernel needs U or Gamma
+// in reverse time order.  The state_in gradient is conj(abar) Ubar(0) (and
+// Gbar).  Feature maps, RMSNorm and the conv are differentiated per token.
+// Parameter gradients are sums over batch rows and tokens: each wave writes
+// its partial sums, and one kernel adds them in a fixed order (no atomics).
+#include "common.h"
+#include "launch.h"
+
+namespace idattn {
+
+namespace {
+
+constexpr int kTok = 8;    // tokens loaded ahead in the per-mode scans
+constexpr int kBlk = 16;   // tokens per LDS round of the per-channel scans
+constexpr int kVW = 16;    // waves per per-channel scan block
+constexpr int kRun = 64;   // tokens per wave in the feature and conv kernels
+constexpr int kWMax = 8;   // largest conv width
+
+__device__ __forceinline__ Zoh zoh_of(const idattn_params& prm, int64_t h, int64_t M, int64_t m) {
+    return zoh_mode(prm.log_dt[h], prm.A[(h * M + m) * 2], prm.A[(h * M + m) * 2 + 1], prm.Bc[(h * M + m) * 2],
+                    prm.Bc[(h * M + m) * 2 + 1]);
+}
+
+// ------------------------------------------------------------------ per-mode scans
+// One wave per (b, h, m); lane l owns channels l and l + 64 (RJ of them).
+//
+// Key side: U and V = dU/dabar; writes s = xi_q . U and s_a = xi_q . V
+// [H][T][M] and, when the state_out gradient is given, the mode's share
+// sum_r g_S,U[r] conj(V_r(N-1)) of g_abar to ga_key [B H][M].
+template <int RJ>
+__global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_params prm, const float* __restrict__ xi_q,
+                                                           const float* __restrict__ z_k, const float* state_in,
+                                                           const float* grad_state, float2* __restrict__ s,
+                                                           float2* __restrict__ s_a, float2* __restrict__ ga_key) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t bh = blockIdx.x;
+    const int64_t m = static_cast<int64_t>(blockIdx.y) * 4 + (threadIdx.x >> 6);
+    const int64_t M = p.M, N = p.N;
+    const int d = static_cast<int>(p.d);
+    if (m >= M) return;  // whole wave; no barriers in this kernel
+    const int64_t h = bh % p.H;
+    const Zoh z = zoh_of(prm, h, M, m);
+    const float ar = static_cast<float>(z.ar), ai = static_cast<float>(z.ai);
+    const float br = static_cast<float>(z.br), bi = static_cast<float>(z.bi);
+    const int64_t st_row = ((bh * M + m) * 2 * d) * 2;
+    float ur[RJ], ui[RJ], vr[RJ], vi[RJ];
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+        const int r = lane + kWave * j;
+        ur[j] = ui[j] = vr[j] = vi[j] = 0.f;
+        if (state_in != nullptr && r < d) {
+            ur[j] = state_in[st_row + 2 * r];
+            ui[j] = state_in[st_row + 2 * r + 1];
+        }
+    }
+    const int64_t row0 = h * p.T + (bh / p.H) * N;
+    const float* xq = xi_q + row0 * d;
+    const float* zk = z_k + row0 * d;
+    for (int64_t i0 = 0; i0 < N; i0 += kTok) {
+        float xv[kTok][RJ], zv[kTok][RJ];
+#pragma unroll
+        for (int t = 0; t < kTok; ++t)
+#pragma unroll
+            for (int j = 0; j < RJ; ++j) {
+                const int r = lane + kWave * j;
+                const bool ok = (i0 + t < N) && (r < d);
+                xv[t][j] = ok ? xq[(i0 + t) * d + r] : 0.f;
+                zv[t][j] = ok ? zk[(i0 + t) * d + r] : 0.f;
+            }
+#pragma unroll
+        for (int t = 0; t < kTok; ++t) {
+            if (i0 + t >= N) break;
+            float pr = 0.f, pi = 0.f, qr = 0.f, qi = 0.f;
+#pragma unroll
+            for (int j = 0; j < RJ; ++j) {
+                // V(i) = abar V(i-1) + U(i-1), then U(i) = abar U(i-1) + bbar z_k(i)
+                const float nvr = fmaf(ar, vr[j], fmaf(-ai, vi[j], ur[j]));
+                const float nvi = fmaf(ar, vi[j], fmaf(ai, vr[j], ui[j]));
+                const float nur = fmaf(ar, ur[j], fmaf(-ai, ui[j], br * zv[t][j]));
+                const float nui = fmaf(ar, ui[j], fmaf(ai, ur[j], bi * zv[t][j]));
+                vr[j] = nvr;
+                vi[j] = nvi;
+                ur[j] = nur;
+                ui[j] = nui;
+                pr = fmaf(xv[t][j], nur, pr);
+                pi = fmaf(xv[t][j], nui, pi);
+                qr = fmaf(xv[t][j], nvr, qr);
+                qi = fmaf(xv[t][j], nvi, qi);
+            }
+            pr = wave_total(pr);
+            pi = wave_total(pi);
+            qr = wave_total(qr);
+            qi = wave_total(qi);
+            if (lane == 0) {
+                s[(row0 + i0 + t) * M + m] = make_float2(pr, pi);
+                s_a[(row0 + i0 + t) * M + m] = make_float2(qr, qi);
+            }
+        }
+    }
+    if (grad_state != nullptr) {
+        float gr = 0.f, gi = 0.f;  // sum_r g_S[r] conj(V_r)
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) {
+            const int r = lane + kWave * j;
+            if (r < d) {
+                const float sr = grad_state[st_row + 2 * r], si = grad_state[st_row + 2 * r + 1];
+                gr = fmaf(sr, vr[j], fmaf(si, vi[j], gr));
+                gi = fmaf(si, vr[j], fmaf(-sr, vi[j], gi));
+            }
+        }
+        gr = wave_total(gr);
+        gi = wave_total(gi);
+        if (lane == 0) ga_key[bh * M + m] = make_float2(gr, gi);
+    }
+}
+
+// Value side: Gamma and W = dGamma/dabar, driven by z_v; per token
+// g_s = sum_c g_o[c] conj(Gamma_c) (to gs [H][T][M]) and
+// gw = sum_c g_o[c] conj(W_c); the mode's g_abar partial
+// sum_i [conj(s) gw + g_s conj(s_a)] plus the state_out terms goes to
+// ga [B H][M].
+template <int RJ, bool BF16>
+__global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_params prm, const float* __restrict__ z_v,
+                                                             const void* __restrict__ grad_o, const float* state_in,
+                                                             const float* grad_state, const float2* __restrict__ s,
+                                                             const float2* __restrict__ s_a,
+                                                             const float2* __restrict__ ga_key,
+                                                             float2* __restrict__ gs, float2* __restrict__ ga) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t bh = blockIdx.x;
+    const int64_t m = static_cast<int64_t>(blockIdx.y) * 4 + (threadIdx.x >> 6);
+    const int64_t M = p.M, N = p.N, H = p.H;
+    const int d = static_cast<int>(p.d);
+    if (m >= M) return;
+    const int64_t b = bh / H, h = bh % H;
+    const Zoh z = zoh_of(prm, h, M, m);
+    const float ar = static_cast<float>(z.ar), ai = static_cast<float>(z.ai);
+    const float br = static_cast<float>(z.br), bi = static_cast<float>(z.bi);
+    const int64_t st_row = ((bh * M + m) * 2 * d) * 2;
+    float gmr[RJ], gmi[RJ], wr[RJ], wi[RJ];
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+        const int c = lane + kWave * j;
+        gmr[j] = gmi[j] = wr[j] = wi[j] = 0.f;
+        if (state_in != nullptr && c < d) {
+            gmr[j] = state_in[st_row + 2 * (d + c)];
+            gmi[j] = state_in[st_row + 2 * (d + c) + 1];
+        }
+    }
+    const int64_t row0 = h * p.T + b * N;
+    const float* zvp = z_v + row0 * d;
+    double accr = 0.0, acci = 0.0;  // g_abar share of this mode
+    for (int64_t i0 = 0; i0 < N; i0 += kTok) {
+        float zz[kTok][RJ], go[kTok][RJ];
+#pragma unroll
+        for (int t = 0; t < kTok; ++t)
+#pragma unroll
+            for (int j = 0; j < RJ; ++j) {
+                const int c = lane + kWave * j;
+                const bool ok = (i0 + t < N) && (c < d);
+                zz[t][j] = ok ? zvp[(i0 + t) * d + c] : 0.f;
+                go[t][j] = ok ? load_io<BF16>(grad_o, ((b * N + i0 + t) * H + h) * d + c) : 0.f;
+            }
+#pragma unroll
+        for (int t = 0; t < kTok; ++t) {
+            if (i0 + t >= N) break;
+            float pr = 0.f, pi = 0.f, qr = 0.f, qi = 0.f;
+#pragma unroll
+            for (int j = 0; j < RJ; ++j) {
+                const float nwr = fmaf(ar, wr[j], fmaf(-ai, wi[j], gmr[j]));
+                const float nwi = fmaf(ar, wi[j], fmaf(ai, wr[j], gmi[j]));
+                const float ngr = fmaf(ar, gmr[j], fmaf(-ai, gmi[j], br * zz[t][j]));
+                const float ngi = fmaf(ar, gmi[j], fmaf(ai, gmr[j], bi * zz[t][j]));
+                wr[j] = nwr;
+                wi[j] = nwi;
+                gmr[j] = ngr;
+                gmi[j] = ngi;
+                pr = fmaf(go[t][j], ngr, pr);   // g_s = sum g_o conj(Gamma)
+                pi = fmaf(-go[t][j], ngi, pi);
+                qr = fmaf(go[t][j], nwr, qr);   // gw = sum g_o conj(W)
+                qi = fmaf(-go[t][j], nwi, qi);
+            }
+            pr = wave_total(pr);
+            pi = wave_total(pi);
+            qr = wave_total(qr);
+            qi = wave_total(qi);
+            const int64_t idx = (row0 + i0 + t) * M + m;
+            if (lane == 0) {
+                gs[idx] = make_float2(pr, pi);
+                const float2 sv = s[idx], sa = s_a[idx];
+                // conj(s) gw + g_s conj(s_a)
+                accr += static_cast<double>(sv.x * qr + sv.y * qi) + static_cast<double>(pr * sa.x + pi * sa.y);
+                acci += static_cast<double>(sv.x * qi - sv.y * qr) + static_cast<double>(pi * sa.x - pr * sa.y);
+            }
+        }
+    }
+    if (grad_state != nullptr) {
+        float gr = 0.f, gi = 0.f;  // sum_c g_S[c] conj(W_c)
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) {
+            const int c = lane + kWave * j;
+            if (c < d) {
+                const float sr = grad_state[st_row + 2 * (d + c)], si = grad_state[st_row + 2 * (d + c) + 1];
+                gr = fmaf(sr, wr[j], fmaf(si, wi[j], gr));
+                gi = fmaf(si, wr[j], fmaf(-sr, wi[j], gi));
+            }
+        }
+        gr = wave_total(gr);
+        gi = wave_total(gi);
+        if (lane == 0) {
+            const float2 k = ga_key[bh * M + m];
+            accr += static_cast<double>(gr) + k.x;
+            acci += static_cast<double>(gi) + k.y;
+        }
+    }
+    if (lane == 0) ga[bh * M + m] = make_float2(static_cast<float>(accr), static_cast<float>(acci));
+}
+
+// Sum of x[0..K) in a fixed pairwise order (deterministic).
+template <int K>
+__device__ __forceinline__ float tree_sum(float (&x)[K]) {
+#pragma unroll
+    for (int step = 1; step < K; step *= 2)
+#pragma unroll
+        for (int i = 0; i + step < K; i += 2 * step) x[i] += x[i + step];
+    return x[0];
+}
+
+// ------------------------------------------------------------------ per-channel scans
+// One block per (b, h, 64-channel group): wave w owns modes [w MW, (w+1) MW),
+// lane l one channel c; per token the waves' partial sums over their modes
+// meet in LDS and are added in a fixed order.
+//
+// g_xi_q(i)_r = sum_m Re(g_s_m(i) conj(U_m,r(i))), U run forward again from
+// state_in; the result goes to g_xi [H][T][d].
+template <int MW>
+__global__ __launch_bounds__(kVW * 64) void bwd_xi_scan_kernel(Problem p, idattn_params prm,
+                                                               const float* __restrict__ z_k, const float* state_in,
+                                                               const float2* __restrict__ gs,
+                                                               float* __restrict__ g_xi) {
+    __shared__ float2 w_blk[kBlk * 64];
+    __shared__ float red[kVW][kBlk][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x >> 6;
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / p.H, h = bh % p.H;
+    const int64_t M = p.M, N = p.N;
+    const int d = static_cast<int>(p.d);
+    const int c = static_cast<int>(blockIdx.y) * kWave + lane;
+    const bool cok = c < d;
+    const int64_t row0 = h * p.T + b * N;
+    float ar[MW], ai[MW], br[MW], bi[MW], ur[MW], ui[MW];
+#pragma unroll
+    for (int mm = 0; mm < MW; ++mm) {
+        const int64_t m = w * MW + mm;
+        const Zoh zz = zoh_of(prm, h, M, m);
+        ar[mm] = static_cast<float>(zz.ar);
+        ai[mm] = static_cast<float>(zz.ai);
+        br[mm] = static_cast<float>(zz.br);
+        bi[mm] = static_cast<float>(zz.bi);
+        ur[mm] = ui[mm] = 0.f;
+        if (state_in != nullptr && cok) {
+            const int64_t idx = ((bh * M + m) * 2 * d + c) * 2;
+            ur[mm] = state_in[idx];
+            ui[mm] = state_in[idx + 1];
+        }
+    }
+    const float* zkp = z_k + row0 * d;
+    for (int64_t i0 = 0; i0 < N; i0 += kBlk) {
+        const int nt = static_cast<int>(N - i0 < kBlk ? N - i0 : kBlk);
+        for (int e = threadIdx.x; e < nt * M; e += kVW * 64) w_blk[e] = gs[(row0 + i0) * M + e];
+        float zz[kBlk];
+#pragma unroll
+        for (int t = 0; t < kBlk; ++t) zz[t] = (t < nt && cok) ? zkp[(i0 + t) * d + c] : 0.f;
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < kBlk; ++t) {
+            if (t < nt) {
+                float acc = 0.f;
+#pragma unroll
+                for (int mm = 0; mm < MW; ++mm) {
+                    const float2 g = w_blk[t * M + w * MW + mm];
+                    const float nr = fmaf(ar[mm], ur[mm], fmaf(-ai[mm], ui[mm], br[mm] * zz[t]));
+                    const float ni = fmaf(ar[mm], ui[mm], fmaf(ai[mm], ur[mm], bi[mm] * zz[t]));
+                    ur[mm] = nr;
+                    ui[mm] = ni;
+                    acc = fmaf(g.x, nr, fmaf(g.y, ni, acc));  // Re(g conj(U))
+                }
+                red[w][t][lane] = acc;
+            }
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < nt * kWave; e += kVW * 64) {
+            const int t = e / kWave, l = e % kWave;
+            const int cc = static_cast<int>(blockIdx.y) * kWave + l;
+            if (cc < d) {
+                float part[kVW];
+#pragma unroll
+                for (int i = 0; i < kVW; ++i) part[i] = red[i][t][l];
+                g_xi[(row0 + i0 + t) * d + cc] = tree_sum(part);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// The adjoint of one state in reverse time:
+//   A_m(i) = x(i) w_m(i) + conj(abar_m) A_m(i+1),   A_m(N-1) = x w + g_S,
+//   y(i) = Re sum_m conj(bbar_m) A_m(i)           -> g_z [H][T][d]
+//   g_bbar_m partial = sum_i sum_c A_m,c(i) z(i)_c  -> gb [B H][channel groups][M]
+//   g_state_in = conj(abar) A(0)                    (columns off .. off + d - 1)
+// Key side: x = xi_q, w = g_s, z = z_k, off = 0.  Value side: x = g_o (io
+// dtype, [B][N][H][d]), w = conj(s), z = z_v, off = d.
+template <int MW, bool X_IO, bool BF16, bool CONJ_W>
+__global__ __launch_bounds__(kVW * 64) void bwd_adjoint_kernel(Problem p, idattn_params prm,
+                                                               const void* __restrict__ x,
+                                                               const float2* __restrict__ wv,
+                                                               const float* __restrict__ zsrc,
+                                                               const float* grad_state, int off,
+                                                               float* __restrict__ g_z, float* grad_state_in,
+                                                               float2* __restrict__ gb) {
+    __shared__ float2 w_blk[kBlk * 64];
+    __shared__ float red[kVW][kBlk][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x >> 6;
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / p.H, h = bh % p.H, H = p.H;
+    const int64_t M = p.M, N = p.N;
+    const int d = static_cast<int>(p.d);
+    const int c = static_cast<int>(blockIdx.y) * kWave + lane;
+    const bool cok = c < d;
+    const int64_t row0 = h * p.T + b * N;
+    float ar[MW], ai[MW], br[MW], bi[MW], cr[MW], ci[MW], gbr[MW], gbi[MW];
+#pragma unroll
+    for (int mm = 0; mm < MW; ++mm) {
+        const int64_t m = w * MW + mm;
+        const Zoh zz = zoh_of(prm, h, M, m);
+        ar[mm] = static_cast<float>(zz.ar);
+        ai[mm] = static_cast<float>(zz.ai);
+        br[mm] = static_cast<float>(zz.br);
+        bi[mm] = static_cast<float>(zz.bi);
+        cr[mm] = ci[mm] = gbr[mm] = gbi[mm] = 0.f;
+        if (grad_state != nullptr && cok) {  // the carry into the last token: g_S
+            const int64_t idx = ((bh * M + m) * 2 * d + off + c) * 2;
+            cr[mm] = grad_state[idx];
+            ci[mm] = grad_state[idx + 1];
+        }
+    }
+    const float* zp = zsrc + row0 * d;
+    for (int64_t i1 = N; i1 > 0; i1 -= kBlk) {
+        const int64_t i0 = i1 - kBlk > 0 ? i1 - kBlk : 0;
+        const int nt = static_cast<int>(i1 - i0);
+        for (int e = threadIdx.x; e < nt * M; e += kVW * 64) w_blk[e] = wv[(row0 + i0) * M + e];
+        float xx[kBlk], zz[kBlk];
+#pragma unroll
+        for (int t = 0; t < kBlk; ++t) {
+            const bool ok = t < nt && cok;
+            float xv = 0.f;
+            if (ok) {
+                if constexpr (X_IO) xv = load_io<BF16>(x, ((b * N + i0 + t) * H + h) * d + c);
+                else xv = static_cast<const float*>(x)[(row0 + i0 + t) * d + c];
+            }
+            xx[t] = xv;
+            zz[t] = ok ? zp[(i0 + t) * d + c] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = kBlk - 1; t >= 0; --t) {
+            if (t < nt) {
+                float acc = 0.f;
+#pragma unroll
+                for (int mm = 0; mm < MW; ++mm) {
+                    float2 g = w_blk[t * M + w * MW + mm];
+                    if constexpr (CONJ_W) g.y = -g.y;
+                    const float nr = fmaf(xx[t], g.x, cr[mm]);
+                    const float ni = fmaf(xx[t], g.y, ci[mm]);
+                    acc = fmaf(br[mm], nr, fmaf(bi[mm], ni, acc));  // Re(conj(bbar) A)
+                    gbr[mm] = fmaf(nr, zz[t], gbr[mm]);
+                    gbi[mm] = fmaf(ni, zz[t], gbi[mm]);
+                    // carry into the previous token: conj(abar) A
+                    cr[mm] = fmaf(ar[mm], nr, ai[mm] * ni);
+                    ci[mm] = fmaf(ar[mm], ni, -ai[mm] * nr);
+                }
+                red[w][t][lane] = acc;
+            }
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < nt * kWave; e += kVW * 64) {
+            const int t = e / kWave, l = e % kWave;
+            const int cc = static_cast<int>(blockIdx.y) * kWave + l;
+            if (cc < d) {
+                float part[kVW];
+#pragma unroll
+                for (int i = 0; i < kVW; ++i) part[i] = red[i][t][l];
+                g_z[(row0 + i0 + t) * d + cc] = tree_sum(part);
+            }
+        }
+        __syncthreads();
+    }
+    if (grad_state_in != nullptr && cok) {
+#pragma unroll
+        for (int mm = 0; mm < MW; ++mm) {
+            const int64_t idx = ((bh * M + w * MW + mm) * 2 * d + off + c) * 2;
+            grad_state_in[idx] = cr[mm];
+            grad_state_in[idx + 1] = ci[mm];
+        }
+    }
+    // g_bbar: sum over the wave's channels, one value per (mode, channel group)
+#pragma unroll
+    for (int mm = 0; mm < MW; ++mm) {
+        const float sr = wave_total(gbr[mm]), si = wave_total(gbi[mm]);
+        if (lane == 0) gb[(bh * gridDim.y + blockIdx.y) * M + w * MW + mm] = make_float2(sr, si);
+    }
+}
+
+// ------------------------------------------------------------------ features
+// One wave per (b, h, run of kRun tokens); lane l owns channels l and l + 64.
+// Per token: the forward's conv, SiLU, norms and RMSNorms again, then
+//   g_v        = rho_v u - rho_v^3 v (u . v) / d,        u = g_v g_z_v
+//   g_xi_k     = rho_k u - rho_k^3 xi_k (u . xi_k) / d,  u = g_k g_z_k
+//   g_y        = g_xi / D - 2 y (y . g_xi) / D^2  (xi = y / D, D = ||y||^2 + eps)
+//              = g_xi / D - y (y . g_xi) / D^3    (unit norm: D = sqrt(||y||^2 + eps))
+//   g_c        = g_y sigma(c) (1 + c (1 - sigma(c)))
+// g_c of queries and keys overwrite g_xi and g_z_k in place (same token, same
+// lanes); the run's sums for the gain and bias gradients go to
+// part [B H][runs][4 d]: gain key half, gain value half, bias key, bias value.
+template <bool BF16, int DJ>
+__global__ __launch_bounds__(256) void bwd_feature_kernel(Problem p, idattn_params prm, const void* __restrict__ q,
+                                                          const void* __restrict__ k, const void* __restrict__ v,
+                                                          const void* __restrict__ tail_in,
+                                                          float* __restrict__ g_xi, float* __restrict__ g_zk,
+                                                          const float* __restrict__ g_zv, void* __restrict__ grad_v,
+                                                          float* __restrict__ part, int64_t runs) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t H = p.H, N = p.N;
+    const int d = static_cast<int>(p.d), W = static_cast<int>(p.W);
+    if (wid >= p.B * H * runs) return;  // whole wave; no barriers below
+    const int64_t bh = wid / runs, run = wid % runs;
+    const int64_t b = bh / H, h = bh % H;
+    const int64_t t0 = run * kRun, t1 = t0 + kRun < N ? t0 + kRun : N;
+    const int64_t row0 = h * p.T + b * N;
+    float gk[DJ], bk[DJ], gv[DJ], bv[DJ];  // this head's gain and bias
+    float agk[DJ], abk[DJ], agv[DJ], abv[DJ];
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+        const int c = lane + kWave * j;
+        const bool in = c < d;
+        gk[j] = in ? prm.gain[h * 2 * d + c] : 0.f;
+        gv[j] = in ? prm.gain[h * 2 * d + d + c] : 0.f;
+        bk[j] = in ? prm.bias[h * 2 * d + c] : 0.f;
+        bv[j] = in ? prm.bias[h * 2 * d + d + c] : 0.f;
+        agk[j] = abk[j] = agv[j] = abv[j] = 0.f;
+    }
+    (void)bk;
+    (void)bv;
+    const float inv_d = 1.f / static_cast<float>(d);
+    for (int64_t t = t0; t < t1; ++t) {
+        float cq[DJ], ck[DJ], vv[DJ];
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            const int c = lane + kWave * j;
+            float aq = 0.f, ak = 0.f, xv = 0.f;
+            if (c < d) {
+                const float* wq = prm.conv_q + (h * d + c) * W;
+                const float* wk = prm.conv_k + (h * d + c) * W;
+                for (int j2 = 0; j2 < W; ++j2) {
+                    const int64_t pos = t - (W - 1) + j2;
+                    float xq = 0.f, xk = 0.f;
+                    if (pos >= 0) {
+                        const int64_t idx = ((b * N + pos) * H + h) * d + c;
+                        xq = load_io<BF16>(q, idx);
+                        xk = load_io<BF16>(k, idx);
+                    } else if (tail_in != nullptr) {
+                        const int64_t tq = ((b * H + h) * 2 * (W - 1) + (W - 1 + pos)) * d + c;
+                        xq = load_io<BF16>(tail_in, tq);
+                        xk = load_io<BF16>(tail_in, tq + static_cast<int64_t>(W - 1) * d);
+                    }
+                    aq = fmaf(wq[j2], xq, aq);
+                    ak = fmaf(wk[j2], xk, ak);
+                }
+                xv = load_io<BF16>(v, ((b * N + t) * H + h) * d + c);
+            }
+            cq[j] = aq;
+            ck[j] = ak;
+            vv[j] = xv;
+        }
+        // forward quantities: y = SiLU(c) with its sigmoid, norms
+        float sq[DJ], sk[DJ], yq[DJ], yk[DJ];
+        float nq = 0.f, nk = 0.f, nv = 0.f;
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            sq[j] = 1.f / (1.f + expf(-cq[j]));
+            sk[j] = 1.f / (1.f + expf(-ck[j]));
+            yq[j] = cq[j] * sq[j];
+            yk[j] = ck[j] * sk[j];
+            nq = fmaf(yq[j], yq[j], nq);
+            nk = fmaf(yk[j], yk[j], nk);
+            nv = fmaf(vv[j], vv[j], nv);
+        }
+        nq = wave_total(nq);
+        nk = wave_total(nk);
+        nv = wave_total(nv);
+        const float Dq = p.unit_feat ? sqrtf(nq + p.eps_feat) : nq + p.eps_feat;
+        const float Dk = p.unit_feat ? sqrtf(nk + p.eps_feat) : nk + p.eps_feat;
+        const float iDk = 1.f / Dk;
+        float xk[DJ], gzk[DJ], gzv[DJ], gxq[DJ];
+        float nxk = 0.f;
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            const int c = lane + kWave * j;
+            const bool in = c < d;
+            xk[j] = yk[j] * iDk;
+            nxk = fmaf(xk[j], xk[j], nxk);
+            gzk[j] = in ? g_zk[(row0 + t) * d + c] : 0.f;
+            gzv[j] = in ? g_zv[(row0 + t) * d + c] : 0.f;
+            gxq[j] = in ? g_xi[(row0 + t) * d + c] : 0.f;
+        }
+        nxk = wave_total(nxk);
+        const float rk = 1.f / sqrtf(nxk * inv_d + p.eps_norm);
+        const float rv = 1.f / sqrtf(nv * inv_d + p.eps_norm);
+        // backward through the RMSNorms, and the query side's y . g_xi
+        float uxk = 0.f, uvv = 0.f, yqg = 0.f;
+        float uk[DJ], uv[DJ];
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            agk[j] = fmaf(gzk[j], xk[j] * rk, agk[j]);
+            abk[j] += gzk[j];
+            agv[j] = fmaf(gzv[j], vv[j] * rv, agv[j]);
+            abv[j] += gzv[j];
+            uk[j] = gk[j] * gzk[j];
+            uv[j] = gv[j] * gzv[j];
+            uxk = fmaf(uk[j], xk[j], uxk);
+            uvv = fmaf(uv[j], vv[j], uvv);
+            yqg = fmaf(yq[j], gxq[j], yqg);
+        }
+        uxk = wave_total(uxk);
+        uvv = wave_total(uvv);
+        yqg = wave_total(yqg);
+        const float ck3 = rk * rk * rk * uxk * inv_d, cv3 = rv * rv * rv * uvv * inv_d;
+        float gxk[DJ];
+        float ykg = 0.f;
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            const int c = lane + kWave * j;
+            gxk[j] = rk * uk[j] - ck3 * xk[j];
+            ykg = fmaf(yk[j], gxk[j], ykg);
+            if (c < d) store_io<BF16>(grad_v, ((b * N + t) * H + h) * d + c, rv * uv[j] - cv3 * vv[j]);
+        }
+        ykg = wave_total(ykg);
+        // through the feature map and SiLU
+        const float iDq = 1.f / Dq;
+        const float fq = p.unit_feat ? yqg * iDq * iDq * iDq : 2.f * yqg * iDq * iDq;
+        const float fk = p.unit_feat ? ykg * iDk * iDk * iDk : 2.f * ykg * iDk * iDk;
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            const int c = lane + kWave * j;
+            if (c < d) {
+                const float gyq = gxq[j] * iDq - fq * yq[j];
+                const float gyk = gxk[j] * iDk - fk * yk[j];
+                g_xi[(row0 + t) * d + c] = gyq * sq[j] * (1.f + cq[j] * (1.f - sq[j]));
+                g_zk[(row0 + t) * d + c] = gyk * sk[j] * (1.f + ck[j] * (1.f - sk[j]));
+            }
+        }
+    }
+    float* pp = part + wid * 4 * d;
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+        const int c = lane + kWave * j;
+        if (c < d) {
+            pp[c] = agk[j];
+            pp[d + c] = agv[j];
+            pp[2 * d + c] = abk[j];
+            pp[3 * d + c] = abv[j];
+        }
+    }
+}
+
+// Conv backward, one wave per (b, h, run of kRun tokens):
+//   g_x(t)_c = sum_j w[c][j] g_c(t + W - 1 - j)_c   (terms past the sequence end are zero)
+//   g_w[c][j] += g_c(t)_c x(t - W + 1 + j)_c         (x before position 0 from the tail)
+// for queries (g_c in g_cq) and keys (g_ck); partial weight gradients to
+// part [B H][runs][2][d][W].
+template <bool BF16, int DJ>
+__global__ __launch_bounds__(256) void bwd_conv_kernel(Problem p, idattn_params prm, const void* __restrict__ q,
+                                                       const void* __restrict__ k, const void* __restrict__ tail_in,
+                                                       const float* __restrict__ g_cq, const float* __restrict__ g_ck,
+                                                       void* __restrict__ grad_q, void* __restrict__ grad_k,
+                                                       float* __restrict__ part, int64_t runs) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t H = p.H, N = p.N;
+    const int d = static_cast<int>(p.d), W = static_cast<int>(p.W);
+    if (wid >= p.B * H * runs) return;  // whole wave; no barriers below
+    const int64_t bh = wid / runs, run = wid % runs;
+    const int64_t b = bh / H, h = bh % H;
+    const int64_t t0 = run * kRun, t1 = t0 + kRun < N ? t0 + kRun : N;
+    const int64_t row0 = h * p.T + b * N;
+    float wq[DJ][kWMax], wk[DJ][kWMax], aq[DJ][kWMax], ak[DJ][kWMax];
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+        const int c = lane + kWave * j;
+#pragma unroll
+        for (int e = 0; e < kWMax; ++e) {
+            const bool ok = c < d && e < W;
+            wq[j][e] = ok ? prm.conv_q[(h * d + c) * W + e] : 0.f;
+            wk[j][e] = ok ? prm.conv_k[(h * d + c) * W + e] : 0.f;
+            aq[j][e] = ak[j][e] = 0.f;
+        }
+    }
+    for (int64_t t = t0; t < t1; ++t) {
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            const int c = lane + kWave * j;
+            if (c >= d) continue;
+            const float gq_t = g_cq[(row0 + t) * d + c], gk_t = g_ck[(row0 + t) * d + c];
+            float sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int e = 0; e < kWMax; ++e) {
+                if (e >= W) break;
+                // g_x(t) takes g_c(t + W - 1 - e) through tap e
+                const int64_t tt = t + W - 1 - e;
+                if (tt < N) {
+                    sq = fmaf(wq[j][e], g_cq[(row0 + tt) * d + c], sq);
+                    sk = fmaf(wk[j][e], g_ck[(row0 + tt) * d + c], sk);
+                }
+                // tap e of token t reads x(t - W + 1 + e)
+                const int64_t pos = t - (W - 1) + e;
+                float xq = 0.f, xk = 0.f;
+                if (pos >= 0) {
+                    const int64_t idx = ((b * N + pos) * H + h) * d + c;
+                    xq = load_io<BF16>(q, idx);
+                    xk = load_io<BF16>(k, idx);
+                } else if (tail_in != nullptr) {
+                    const int64_t tq = ((b * H + h) * 2 * (W - 1) + (W - 1 + pos)) * d + c;
+                    xq = load_io<BF16>(tail_in, tq);
+                    xk = load_io<BF16>(tail_in, tq + static_cast<int64_t>(W - 1) * d);
+                }
+                aq[j][e] = fmaf(gq_t, xq, aq[j][e]);
+                ak[j][e] = fmaf(gk_t, xk, ak[j][e]);
+            }
+            const int64_t o = ((b * N + t) * H + h) * d + c;
+            store_io<BF16>(grad_q, o, sq);
+            store_io<BF16>(grad_k, o, sk);
+        }
+    }
+    float* pp = part + wid * 2 * d * W;
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+        const int c = lane + kWave * j;
+        if (c >= d) continue;
+#pragma unroll
+        for (int e = 0; e < kWMax; ++e) {
+            if (e >= W) break;
+            pp[c * W + e] = aq[j][e];
+            pp[d * W + c * W + e] = ak[j][e];
+        }
+    }
+}
+
+// ------------------------------------------------------------------ parameters
+// (exp(z) (z - 1) + 1) / z^2 = sum_{n>=2} z^(n-2) (n-1)/n!: the part of
+// d bbar / d lambda that cancels for small z = Delta lambda.
+__device__ inline void phi_z(double zr, double zi, double& pr, double& pi) {
+    const double az = sqrt(zr * zr + zi * zi);
+    if (az < 0.5) {
+        // series: term_n = z^(n-2) (n-1)/n!
+        double tr = 1.0, ti = 0.0;  // z^(n-2) / n!, from n = 2: 1/2
+        double sr = 0.0, si = 0.0;
+        double inv_fact = 0.5;
+        for (int n = 2; n < 30; ++n) {
+            if (n > 2) {
+                const double nr = tr * zr - ti * zi, ni = tr * zi + ti * zr;
+                tr = nr;
+                ti = ni;
+                inv_fact /= n;
+            }
+            sr += (n - 1) * inv_fact * tr;
+            si += (n - 1) * inv_fact * ti;
+        }
+        pr = sr;
+        pi = si;
+        return;
+    }
+    double sy, cy;
+    sincos(zi, &sy, &cy);
+    const double e = exp(zr);
+    const double er = e * cy, ei = e * sy;  // exp(z)
+    const double nr = er * (zr - 1.0) - ei * zi + 1.0, ni = er * zi + ei * (zr - 1.0);
+    const double z2r = zr * zr - zi * zi, z2i = 2.0 * zr * zi;
+    const double den = z2r * z2r + z2i * z2i;
+    pr = (nr * z2r + ni * z2i) / den;
+    pi = (ni * z2r - nr * z2i) / den;
+}
+
+// One block per head: the gain, bias and conv gradients summed over batch
+// rows and runs in a fixed order, and the ZOH chain rule from g_abar,
+// g_bbar (summed over batch rows and channel groups) to lambda, B and
+// log_dt:
+//   g_lambda = conj(Delta abar) g_abar + conj(B Delta^2 phi(Delta lambda)) g_bbar
+//   g_B      = conj((abar - 1) / lambda) g_bbar
+//   g_log_dt = Delta sum_m Re(conj(lambda abar) g_abar + conj(B abar) g_bbar)
+constexpr int kRedThreads = 256;
+__global__ __launch_bounds__(kRedThreads) void bwd_param_kernel(Problem p, idattn_params prm,
+                                                                const float* __restrict__ part_f,
+                                                                const float* __restrict__ part_c,
+                                                                const float2* __restrict__ ga,
+                                                                const float2* __restrict__ gbk,
+                                                                const float2* __restrict__ gbv, int64_t runs,
+                                                                int groups, idattn_param_grads out) {
+    __shared__ double ldt[kRedThreads];
+    const int64_t h = blockIdx.x, H = p.H, B = p.B, M = p.M;
+    const int d = static_cast<int>(p.d), W = static_cast<int>(p.W);
+    for (int e = threadIdx.x; e < 4 * d; e += kRedThreads) {
+        double acc = 0.0;
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t r = 0; r < runs; ++r) acc += part_f[((b * H + h) * runs + r) * 4 * d + e];
+        const int half = e / d, c = e % d;  // gain key, gain value, bias key, bias value
+        float* dst = half < 2 ? out.gain : out.bias;
+        dst[h * 2 * d + (half & 1) * d + c] = static_cast<float>(acc);
+    }
+    for (int e = threadIdx.x; e < 2 * d * W; e += kRedThreads) {
+        double acc = 0.0;
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t r = 0; r < runs; ++r) acc += part_c[((b * H + h) * runs + r) * 2 * d * W + e];
+        const int sel = e / (d * W), rest = e % (d * W);
+        (sel == 0 ? out.conv_q : out.conv_k)[h * d * W + rest] = static_cast<float>(acc);
+    }
+    double my_ldt = 0.0;
+    for (int64_t m = threadIdx.x; m < M; m += kRedThreads) {
+        double gar = 0.0, gai = 0.0, gbr = 0.0, gbi = 0.0;
+        for (int64_t b = 0; b < B; ++b) {
+            const float2 a = ga[(b * H + h) * M + m];
+            gar += a.x;
+            gai += a.y;
+            for (int g = 0; g < groups; ++g) {
+                const float2 x = gbk[((b * H + h) * groups + g) * M + m];
+                const float2 y = gbv[((b * H + h) * groups + g) * M + m];
+                gbr += static_cast<double>(x.x) + y.x;
+                gbi += static_cast<double>(x.y) + y.y;
+            }
+        }
+        const double dt = exp(static_cast<double>(prm.log_dt[h]));
+        const double lr = prm.A[(h * M + m) * 2], li = prm.A[(h * M + m) * 2 + 1];
+        const double Br = prm.Bc[(h * M + m) * 2], Bi = prm.Bc[(h * M + m) * 2 + 1];
+        const Zoh z = zoh_of(prm, h, M, m);
+        // (abar - 1) / lambda = bbar / B when B != 0; recomputed here from the ZOH step
+        double qr, qi;
+        {
+            const double zr = dt * lr, zi = dt * li;
+            double sy, cy;
+            sincos(zi, &sy, &cy);
+            const double sh = sin(0.5 * zi);
+            const double em1r = expm1(zr) * cy - 2.0 * sh * sh, em1i = exp(zr) * sy;
+            const double l2 = lr * lr + li * li;
+            if (l2 == 0.0) {
+                qr = dt;
+                qi = 0.0;
+            } else {
+                qr = (em1r * lr + em1i * li) / l2;
+                qi = (em1i * lr - em1r * li) / l2;
+            }
+        }
+        double pr, pi;
+        phi_z(dt * lr, dt * li, pr, pi);
+        // d abar / d lambda = Delta abar; d bbar / d lambda = B Delta^2 phi
+        const double dar = dt * z.ar, dai = dt * z.ai;
+        const double dbr = dt * dt * (Br * pr - Bi * pi), dbi = dt * dt * (Br * pi + Bi * pr);
+        // conj(x) g = (x.r g.r + x.i g.i) + i (x.r g.i - x.i g.r)
+        const double glr = (dar * gar + dai * gai) + (dbr * gbr + dbi * gbi);
+        const double gli = (dar * gai - dai * gar) + (dbr * gbi - dbi * gbr);
+        out.A[(h * M + m) * 2] = static_cast<float>(glr);
+        out.A[(h * M + m) * 2 + 1] = static_cast<float>(gli);
+        out.Bc[(h * M + m) * 2] = static_cast<float>(qr * gbr + qi * gbi);
+        out.Bc[(h * M + m) * 2 + 1] = static_cast<float>(qr * gbi - qi * gbr);
+        // d abar / d Delta = lambda abar, d bbar / d Delta = B abar
+        const double lar = lr * z.ar - li * z.ai, lai = lr * z.ai + li * z.ar;
+        const double bar = Br * z.ar - Bi * z.ai, bai = Br * z.ai + Bi * z.ar;
+        my_ldt += dt * ((lar * gar + lai * gai) + (bar * gbr + bai * gbi));
+    }
+    ldt[threadIdx.x] = my_ldt;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double acc = 0.0;
+        for (int i = 0; i < kRedThreads; ++i) acc += ldt[i];
+        out.log_dt[h] = static_cast<float>(acc);
+    }
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(const Problem& p) {
+    const size_t tok = static_cast<size_t>(p.H) * p.T;
+    const size_t runs = static_cast<size_t>((p.N + kRun - 1) / kRun);
+    const size_t groups = static_cast<size_t>((p.d + kWave - 1) / kWave);
+    const size_t bh = static_cast<size_t>(p.B * p.H);
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    return 6 * up(tok * p.d * sizeof(float)) + 3 * up(tok * p.M * sizeof(float2)) +
+           2 * up(bh * p.M * sizeof(float2)) + 2 * up(bh * groups * p.M * sizeof(float2)) +
+           up(bh * runs * 4 * p.d * sizeof(float)) + up(bh * runs * 2 * p.d * p.W * sizeof(float));
+}
+
+hipError_t launch_backward(const Problem& p, const idattn_params& prm, const void* q, const void* k, const void* v,
+                           const float* state_in, const void* tail_in, const void* grad_o, const float* grad_state,
+                           void* grad_q, void* grad_k, void* grad_v, const idattn_param_grads& grads,
+                           float* grad_state_in, void* workspace, hipStream_t stream) {
+    const size_t tok = static_cast<size_t>(p.H) * p.T;
+    const int64_t runs = (p.N + kRun - 1) / kRun;
+    const int groups = static_cast<int>((p.d + kWave - 1) / kWave);
+    const size_t bh = static_cast<size_t>(p.B * p.H);
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    char* base = static_cast<char*>(workspace);
+    auto take = [&](size_t bytes) {
+        char* r = base;
+        base += up(bytes);
+        return r;
+    };
+    float* xi_q = reinterpret_cast<float*>(take(tok * p.d * sizeof(float)));
+    float* z_k = reinterpret_cast<float*>(take(tok * p.d * sizeof(float)));
+    float* z_v = reinterpret_cast<float*>(take(tok * p.d * sizeof(float)));
+    float* g_xi = reinterpret_cast<float*>(take(tok * p.d * sizeof(float)));
+    float* g_zk = reinterpret_cast<float*>(take(tok * p.d * sizeof(float)));
+    float* g_zv = reinterpret_cast<float*>(take(tok * p.d * sizeof(float)));
+    float2* s = reinterpret_cast<float2*>(take(tok * p.M * sizeof(float2)));
+    float2* s_a = reinterpret_cast<float2*>(take(tok * p.M * sizeof(float2)));
+    float2* gs = reinterpret_cast<float2*>(take(tok * p.M * sizeof(float2)));
+    float2* ga_key = reinterpret_cast<float2*>(take(bh * p.M * sizeof(float2)));
+    float2* ga = reinterpret_cast<float2*>(take(bh * p.M * sizeof(float2)));
+    float2* gbk = reinterpret_cast<float2*>(take(bh * groups * p.M * sizeof(float2)));
+    float2* gbv = reinterpret_cast<float2*>(take(bh * groups * p.M * sizeof(float2)));
+    float* part_f = reinterpret_cast<float*>(take(bh * runs * 4 * p.d * sizeof(float)));
+    float* part_c = reinterpret_cast<float*>(take(bh * runs * 2 * p.d * p.W * sizeof(float)));
+
+    hipError_t e = launch_featmap_conv_norm(p, prm, q, k, v, tail_in, xi_q, z_k, z_v, stream);
+    if (e != hipSuccess) return e;
+    const dim3 gm(static_cast<unsigned>(bh), static_cast<unsigned>((p.M + 3) / 4));
+    if (p.d > 64)
+        bwd_key_scan_kernel<2><<<gm, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, grad_state, s, s_a, ga_key);
+    else
+        bwd_key_scan_kernel<1><<<gm, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, grad_state, s, s_a, ga_key);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+#define IDATTN_BV(RJ, BF)                                                                                         \
+    bwd_value_scan_kernel<RJ, BF><<<gm, 256, 0, stream>>>(p, prm, z_v, grad_o, state_in, grad_state, s, s_a, ga_key, \
+                                                          gs, ga)
+    if (p.d > 64) {
+        if (p.bf16) IDATTN_BV(2, true);
+        else IDATTN_BV(2, false);
+    } else {
+        if (p.bf16) IDATTN_BV(1, true);
+        else IDATTN_BV(1, false);
+    }
+#undef IDATTN_BV
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const dim3 gc(static_cast<unsigned>(bh), static_cast<unsigned>(groups));
+#define IDATTN_BX(MW) bwd_xi_scan_kernel<MW><<<gc, kVW * 64, 0, stream>>>(p, prm, z_k, state_in, gs, g_xi)
+#define IDATTN_BA(MW)                                                                                          \
+    do {                                                                                                       \
+        bwd_adjoint_kernel<MW, false, false, false><<<gc, kVW * 64, 0, stream>>>(p, prm, xi_q, gs, z_k, grad_state, \
+                                                                                 0, g_zk, grad_state_in, gbk);  \
+        if (p.bf16)                                                                                            \
+            bwd_adjoint_kernel<MW, true, true, true><<<gc, kVW * 64, 0, stream>>>(                              \
+                p, prm, grad_o, s, z_v, grad_state, static_cast<int>(p.d), g_zv, grad_state_in, gbv);          \
+        else                                                                                                   \
+            bwd_adjoint_kernel<MW, true, false, true><<<gc, kVW * 64, 0, stream>>>(                             \
+                p, prm, grad_o, s, z_v, grad_state, static_cast<int>(p.d), g_zv, grad_state_in, gbv);          \
+    } while (0)
+    switch (p.M / kVW) {
+        case 1: IDATTN_BX(1); IDATTN_BA(1); break;
+        case 2: IDATTN_BX(2); IDATTN_BA(2); break;
+        case 4: IDATTN_BX(4); IDATTN_BA(4); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef IDATTN_BX
+#undef IDATTN_BA
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const dim3 gr(static_cast<unsigned>((bh * runs + 3) / 4));
+#define IDATTN_BF(BF, DJ)                                                                                            \
+    bwd_feature_kernel<BF, DJ><<<gr, 256, 0, stream>>>(p, prm, q, k, v, tail_in, g_xi, g_zk, g_zv, grad_v, part_f, \
+                                                       runs);                                                        \
+    bwd_conv_kernel<BF, DJ><<<gr, 256, 0, stream>>>(p, prm, q, k, tail_in, g_xi, g_zk, grad_q, grad_k, part_c, runs)
+    if (p.d > 64) {
+        if (p.bf16) { IDATTN_BF(true, 2); }
+        else { IDATTN_BF(false, 2); }
+    } else {
+        if (p.bf16) { IDATTN_BF(true, 1); }
+        else { IDATTN_BF(false, 1); }
+    }
+#undef IDATTN_BF
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    bwd_param_kernel<<<dim3(static_cast<unsigned>(p.H)), kRedThreads, 0, stream>>>(p, prm, part_f, part_c, ga, gbk, gbv,
+                                                                                   runs, groups, grads);
+    return hipGetLastError();
+}
+
+}  // namespace idattn

@@ -54,6 +54,13 @@ hipError_t launch_forward_chunked(const Problem& p, const idattn_params& prm,
                                   const float* state_in, const void* tail_in,
                                   float* state_out, void* tail_out, void* workspace, hipStream_t stream);
 
+// ---- backward (sequential fp32; dense batches, SiLU feature maps)
+size_t backward_workspace_bytes(const Problem& p);
+hipError_t launch_backward(const Problem& p, const idattn_params& prm, const void* q, const void* k, const void* v,
+                           const float* state_in, const void* tail_in, const void* grad_o, const float* grad_state,
+                           void* grad_q, void* grad_k, void* grad_v, const idattn_param_grads& grads,
+                           float* grad_state_in, void* workspace, hipStream_t stream);
+
 // ---- the library's own scratch memory (idattn_forward_noalloc)
 constexpr size_t kNoallocScratchBytes = size_t{192} << 20;
 // Device address of this device's scratch array (looked up once per device).

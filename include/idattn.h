@@ -279,6 +279,58 @@ idattn_status idattn_decode_step_normalized(const idattn_dims *dims, const idatt
                                             const void *q_t, const void *k_t, const void *v_t, void *o_t,
                                             float *state, void *tail, float *eta, void *stream);
 
+/* Gradient outputs for the parameters, float32 device buffers laid out like
+ * the matching fields of idattn_params (complex ones as (d/dRe, d/dIm)). */
+typedef struct idattn_param_grads {
+    float *conv_q;  /* [H][d][W] */
+    float *conv_k;  /* [H][d][W] */
+    float *gain;    /* [H][2d]   */
+    float *bias;    /* [H][2d]   */
+    float *log_dt;  /* [H]       */
+    float *A;       /* [H][M][2] */
+    float *Bc;      /* [H][M][2] */
+} idattn_param_grads;
+
+/* Bytes of device workspace idattn_backward needs for these dims. */
+idattn_status idattn_backward_workspace_size(const idattn_dims *dims, size_t *bytes);
+
+/*
+ * Backward pass of idattn_forward: the gradients of
+ *   L = sum(grad_o * o) + Re sum(conj(grad_state) * state_out)
+ * with respect to q, k, v, every parameter and state_in, for the forward
+ * over the same q, k, v, params, state_in and tail_in.  The layer is trained
+ * inside language models (Chinese rendering, abstract and section 1; German
+ * summary, "Skalierbare Implementierung"); the pages print no backward pass,
+ * so these are the exact derivatives of the forward as this library reads
+ * it.  Complex gradients are d/dRe + i d/dIm.  All arithmetic is fp32, one
+ * time step after another (the sequential algorithm); the forward's
+ * quantities are recomputed, not stored.  Feature maps SQUARED and UNIT
+ * (RFF: IDATTN_ERR_UNSUPPORTED); dims->algo AUTO or SEQUENTIAL (CHUNKED:
+ * IDATTN_ERR_UNSUPPORTED); dense batches only.  No gradient is returned for
+ * tail_in.
+ *
+ *  q, k, v      in   [B][N][H][d] io dtype (the forward's inputs)
+ *  state_in     in   NULL (zero state) or the state layout
+ *  tail_in      in   NULL (zero history) or the tail layout
+ *  grad_o       in   [B][N][H][d] io dtype
+ *  grad_state   in   NULL (no loss on state_out) or the state layout
+ *  grad_q, grad_k, grad_v  out  [B][N][H][d] io dtype
+ *  grad_params  out  every field non-NULL; overwritten (not accumulated)
+ *  grad_state_in out NULL or the state layout
+ *  workspace    at least idattn_backward_workspace_size bytes
+ * Results are bitwise reproducible: parameter gradients are summed over
+ * batch rows and tokens in a fixed order.  No output may overlap another
+ * buffer; N == 0 gives grad_state_in = grad_state (or zeros) and zero
+ * parameter gradients.
+ */
+idattn_status idattn_backward(const idattn_dims *dims, const idattn_params *params,
+                              const void *q, const void *k, const void *v,
+                              const float *state_in, const void *tail_in,
+                              const void *grad_o, const float *grad_state,
+                              void *grad_q, void *grad_k, void *grad_v,
+                              const idattn_param_grads *grad_params, float *grad_state_in,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static text for a status code ("IDATTN_OK", ...). */
 const char *idattn_status_string(idattn_status status);
 

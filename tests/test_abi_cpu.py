@@ -381,3 +381,55 @@ def test_noalloc_validation():
     text = open(HEADER).read()
     assert "#define IDATTN_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)" in text
     assert fs.NOALLOC_SCRATCH_BYTES == 192 << 20
+
+
+def test_backward_struct_and_validation():
+    """idattn_param_grads matches its C layout; idattn_backward rejects bad
+    arguments before any HIP call."""
+    from fixed_state_ssm_amd.binding import IdattnParamGrads
+    src = r"""
+    #include <stdio.h>
+    #include <stddef.h>
+    #include "idattn.h"
+    int main(void) {
+      printf("%zu %zu %zu\n", sizeof(idattn_param_grads), offsetof(idattn_param_grads, log_dt),
+             offsetof(idattn_param_grads, Bc));
+      return 0;
+    }"""
+    with tempfile.TemporaryDirectory() as td:
+        c = os.path.join(td, "t.c")
+        exe = os.path.join(td, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        got = list(map(int, subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()))
+    assert got == [ctypes.sizeof(IdattnParamGrads), IdattnParamGrads.log_dt.offset, IdattnParamGrads.Bc.offset]
+
+    lib = fs.load_library()
+    prm = fs.make_params({k: FAKE for k in fs.PARAM_KEYS})
+    g = IdattnParamGrads(*[FAKE + (i + 10 << 32) for i in range(7)])
+    dims = fs.make_dims(2, 64, 3, 64, 32, 4, "f32")
+    need = fs.idattn_backward_workspace_size(dims)
+    assert need > 0
+
+    def call(d=dims, gp=g, ws_bytes=None, **kw):
+        a = dict(q=FAKE + (1 << 32), k=FAKE + (2 << 32), v=FAKE + (3 << 32), si=None, ti=None, go=FAKE + (4 << 32),
+                 gs=None, gq=FAKE + (5 << 32), gk=FAKE + (6 << 32), gv=FAKE + (7 << 32), gsi=None, ws=FAKE + (8 << 32))
+        a.update(kw)
+        return fs.STATUS[lib.idattn_backward(ctypes.byref(d), ctypes.byref(prm), a["q"], a["k"], a["v"], a["si"],
+                                             a["ti"], a["go"], a["gs"], a["gq"], a["gk"], a["gv"],
+                                             ctypes.byref(gp) if gp is not None else None, a["gsi"], a["ws"],
+                                             need if ws_bytes is None else ws_bytes, None)]
+
+    assert call(gp=None) == "IDATTN_ERR_NULL"
+    assert call(gp=IdattnParamGrads(FAKE + (10 << 32), None, FAKE, FAKE, FAKE, FAKE, FAKE)) == "IDATTN_ERR_NULL"
+    assert call(go=None) == "IDATTN_ERR_NULL"
+    assert call(ws_bytes=need - 1) == "IDATTN_ERR_WORKSPACE"
+    assert call(gq=FAKE + (1 << 32) + 256) == "IDATTN_ERR_ALIAS"          # grad_q overlaps q
+    assert call(gk=FAKE + (5 << 32) + 256) == "IDATTN_ERR_ALIAS"          # grad_k overlaps grad_q
+    assert call(gsi=FAKE + (8 << 32)) == "IDATTN_ERR_ALIAS"               # grad_state_in overlaps workspace
+    assert call(gq=FAKE + (5 << 32) + 8) == "IDATTN_ERR_ARG"              # misaligned
+    assert call(d=fs.make_dims(2, 64, 3, 64, 32, 4, "f32", feature_norm="rff")) == "IDATTN_ERR_UNSUPPORTED"
+    assert call(d=fs.make_dims(2, 64, 3, 64, 64, 4, "bf16", "chunked")) == "IDATTN_ERR_UNSUPPORTED"
+    with pytest.raises(fs.IdattnError):
+        fs.idattn_backward_workspace_size(fs.make_dims(2, 64, 3, 64, 32, 4, "f32", feature_norm="rff"))
+    assert fs.idattn_backward_workspace_size(fs.make_dims(2, 0, 3, 64, 32, 4, "f32")) == 0
