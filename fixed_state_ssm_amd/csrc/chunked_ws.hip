@@ -658,6 +658,29 @@ __device__ __forceinline__ void shift_tile(const void* dst, const _Float16* src,
     }
 }
 
+// The same for a tile already in shared memory, in two steps around a
+// barrier: each of the role's 512 threads reads its elements of the shifted
+// tile, then writes them.
+template <int D>
+__device__ __forceinline__ void shift_tile_read(_Float16 (&r)[D * L / 512], const void* buf, int back) {
+    const int x = tid_now() & 511;
+#pragma unroll
+    for (int u = 0; u < D * L / 512; ++u) {
+        const int e = x + 512 * u, row = e / L, j = e % L;
+        r[u] = j >= back ? *(__attribute__((address_space(3))) const _Float16*)(uintptr_t)(lds_addr(buf) + 2 * o128(row, j - back))
+                         : static_cast<_Float16>(0.f);
+    }
+}
+template <int D>
+__device__ __forceinline__ void shift_tile_write(const void* buf, const _Float16 (&r)[D * L / 512]) {
+    const int x = tid_now() & 511;
+#pragma unroll
+    for (int u = 0; u < D * L / 512; ++u) {
+        const int e = x + 512 * u, row = e / L, j = e % L;
+        *(__attribute__((address_space(3))) _Float16*)(uintptr_t)(lds_addr(buf) + 2 * o128(row, j)) = r[u];
+    }
+}
+
 // ------------------------------------------------------------------ state
 // Key wave kw (0..7), lane (g, i):  U[rt][jj] = U_m[r],  r = 16rt + 4g + jj, m' = 16kw + i
 // Value wave vw (0..D/16-1):        G[mt][jj] = Gamma_m[c], m' = 16mt + 4g + jj, c = 16vw + i
@@ -960,8 +983,8 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
     __syncthreads();
     float* dst = ws + (static_cast<int64_t>(seg) * p.B * p.H + bh) * MM * 2 * D * 2;
     const int rsb = static_cast<int>(p.H * D * 2);  // token stride, bytes
-    // tile of chunk c of this segment: z_k^T, then z_v^T
-    _Float16* zseg = zt + ((bh * S + seg) * (Lseg / L)) * 2 * D * L;
+    // z_k^T tile of chunk c of this segment (the forward builds z_v itself)
+    _Float16* zseg = zt + ((bh * S + seg) * (Lseg / L)) * D * L;
     // The state entering the sequence, times the table scale kappa, staged in
     // lane order for the forward (and the carry chain), which read only this
     // copy: state_in is read here, in a kernel that completes before any block
@@ -987,8 +1010,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
         lds_barrier();  // chunk 0 features
         for (int c = 0; c < nch; ++c) {
             const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
-            tile_copy_out<D>(sm.zkT[c & 1], zseg + c * 2 * D * L);
-            tile_copy_out<D>(sm.zvT[c & 1], zseg + c * 2 * D * L + D * L);  // both tiles: the value waves are the longer role
+            tile_copy_out<D>(sm.zkT[c & 1], zseg + c * D * L);
             if (upd) key_update<D>(U, sm.aL, kw, sm.zkT[c & 1], sm.ft, tid_now() & 63);
             if (c + 1 < nch) {
                 fm_keys<D>(rkk, sm, sm.zkT[(c + 1) & 1], c + 2 < nch ? L : n_last, p.eps_feat, p.eps_norm,
@@ -1010,11 +1032,14 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
             g_store_lane<D>(G, cst, vw);
         }
         if (own) g_load<D>(G, nullptr, vw, 1.f);
+        // the values' features are needed here only for the end state (upd)
         const __amdgpu_buffer_rsrc_t rv = seq_rsrc<D>(v, b, h, p.N, p.H, t_end);
         uint32_t rvv[8];
-        fm_load<D, false>(rvv, rv, rsb, t_begin);
-        fm_values<D>(rvv, sm, sm.zvT[0], nch > 1 ? L : n_last, p.eps_norm);
-        if (nch > 1) fm_load<D, false>(rvv, rv, rsb, t_begin + L);
+        if (upd) {
+            fm_load<D, false>(rvv, rv, rsb, t_begin);
+            fm_values<D>(rvv, sm, sm.zvT[0], nch > 1 ? L : n_last, p.eps_norm);
+            if (nch > 1) fm_load<D, false>(rvv, rv, rsb, t_begin + L);
+        }
         lds_barrier();  // chunk 0 features
         for (int c = 0; c < nch; ++c) {
             const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
@@ -1024,7 +1049,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
                 load_bz(bZ, vw, sm.zvT[c & 1], frag_off(ln));
                 value_update_plain<D>(G, sm.aL, bZ, sm.ft, ln);
             }
-            if (c + 1 < nch) {
+            if (upd && c + 1 < nch) {
                 fm_values<D>(rvv, sm, sm.zvT[(c + 1) & 1], c + 2 < nch ? L : n_last, p.eps_norm);
                 if (c + 2 < nch) {
                     step_fence();
@@ -1144,6 +1169,7 @@ template <int D>
 __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_params prm,
                                                               const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
+                                                              const uint16_t* __restrict__ v,
                                                               const _Float16* __restrict__ zt, uint16_t* __restrict__ o,
                                                               const float* state_in, const uint16_t* tail_in,
                                                               float* state_out, uint16_t* tail_out,
@@ -1204,7 +1230,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
     const int nfold = fold ? seg : 0;
     constexpr int kFoldTiles = D == 128 ? 4 : 2;  // tiles per round trip of the fold (register bound)
     const float2* aseg = reinterpret_cast<const float2*>(th + kTabPwSeg);
-    constexpr int64_t tile2 = 2 * D * L;  // halfs per chunk: z_k^T, z_v^T
+    constexpr int64_t tile2 = D * L;  // halfs per chunk: z_k^T
     const _Float16* zseg = zt + (bh * S + seg) * (Lseg / L) * tile2;
     __syncthreads();
 
@@ -1360,10 +1386,11 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             }
         }
         const __amdgpu_buffer_rsrc_t ob = seq_rsrc<D>(o, b, h, N, H, t_end);
-        u4 zr[kTilePieces<D>];  // z_v^T of the next chunk to enter
+        const __amdgpu_buffer_rsrc_t rv = seq_rsrc<D>(v, b, h, N, H, t_end);
+        uint32_t rvv[8];        // raw v of the next chunk to enter
         u4 kr[kTilePieces<D>];  // z_k^T of the chunk after it
         tile_load<D>(kr, zseg);
-        tile_load<D>(zr, zseg + D * L);
+        fm_load<D, false>(rvv, rv, rsb, t_begin);
         tile_store<D>(sm.zkT, kr);
         if (nch > 1) tile_load<D>(kr, zseg + tile2);
         // lane addresses of this wave's P~ tile and of the s~, X fragment reads, kept
@@ -1377,8 +1404,8 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         for (int c = 0; c <= nch; ++c) {
             const int64_t t0 = t_begin + static_cast<int64_t>(c) * L;
             f4 accO[4];
-            // ---- phase 1: z_v^T (c); P~ tiles, X Gamma, Gamma update (c-1)
-            if (c < nch) tile_store<D>(sm.zvT, zr);
+            // ---- phase 1: z_v^T (c) from v; P~ tiles, X Gamma, Gamma update (c-1)
+            if (c < nch) fm_values<D>(rvv, sm, sm.zvT, c + 1 < nch ? L : n_last, p.eps_norm);
             const int ln = tid_now() & 63;
             if (c >= 1) p_tile_run(sm, ptv, xoff);  // P~ tiles 0..7 of chunk c-1 (8, 9: key waves 2, 3)
             if (c >= 1 && own) {
@@ -1400,7 +1427,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             // ---- phase 2: z_k^T (c+1); o^T += Z_v^T P~^T, Delta o (c-1); Z_v fragments (c)
             if (c + 1 < nch) {
                 tile_store<D>(sm.zkT, kr);  // read by the key waves in phase 1 of step c+1
-                tile_load<D>(zr, zseg + (c + 1) * tile2 + D * L);
+                fm_load<D, false>(rvv, rv, rsb, t0 + L);
                 if (c + 2 < nch) tile_load<D>(kr, zseg + (c + 2) * tile2);
             }
             const int ln2 = tid_now() & 63;
@@ -1426,8 +1453,12 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             lds_barrier();
         }
         if (tail_fix) {
+            // z_v^T of the last chunk is still in shared memory: read it, then
+            // write it back with the valid tokens moved to the end
+            _Float16 zs[D * L / 512];
+            shift_tile_read<D>(zs, sm.zvT, L - n_last);
             lds_barrier();
-            shift_tile<D>(sm.zvT, zseg + (nch - 1) * tile2 + D * L, L - n_last);
+            shift_tile_write<D>(sm.zvT, zs);
             lds_barrier();
             if (own) {
                 const int ln = tid_now() & 63;
@@ -1465,8 +1496,8 @@ void plan_segments(const Problem& p, int& S, int64_t& Lseg) {
 }
 
 // Workspace: per-head tables | the staged kappa state_in, [B H] states in lane
-// order | segment end states, [S-1][B H] | fp16 feature tiles, one z_k^T, z_v^T
-// pair per chunk slot of every segment.
+// order | segment end states, [S-1][B H] | fp16 key-feature tiles, one z_k^T
+// per chunk slot of every segment.
 struct WsLayout {
     size_t tab, c0, seg, zt, total;
 };
@@ -1478,7 +1509,7 @@ WsLayout ws_layout(const Problem& p, int S, int64_t Lseg) {
     w.c0 = static_cast<size_t>(p.H) * kTabBytes;
     w.seg = w.c0 + pairs * state;
     w.zt = w.seg + static_cast<size_t>(S - 1) * pairs * state;
-    w.total = w.zt + pairs * S * static_cast<size_t>(Lseg) * 2 * p.d * sizeof(_Float16);
+    w.total = w.zt + pairs * S * static_cast<size_t>(Lseg) * p.d * sizeof(_Float16);
     return w;
 }
 
@@ -1516,7 +1547,7 @@ hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, con
         if (e != hipSuccess) return e;
     }
     chunked_forward_kernel<D><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(
-        p, prm, q16, k16, zt, static_cast<uint16_t*>(o), state_in, t16, state_out, static_cast<uint16_t*>(tail_out),
+        p, prm, q16, k16, v16, zt, static_cast<uint16_t*>(o), state_in, t16, state_out, static_cast<uint16_t*>(tail_out),
         tab, c0, ws, Lseg, S, fold);
     return hipGetLastError();
 }
@@ -1550,7 +1581,7 @@ size_t chunked_workspace_bound(const Problem& p) {
     const int64_t chunks = (p.N + cws::L - 1) / cws::L;
     const size_t slots = static_cast<size_t>(chunks + (chunks + 1) / 2);
     return static_cast<size_t>(p.H) * cws::kTabBytes + static_cast<size_t>(p.H) * state +
-           static_cast<size_t>(smax - 1) * p.H * state + static_cast<size_t>(p.H) * slots * cws::L * 2 * p.d * 2;
+           static_cast<size_t>(smax - 1) * p.H * state + static_cast<size_t>(p.H) * slots * cws::L * p.d * 2;
 }
 
 hipError_t launch_forward_chunked(const Problem& p, const idattn_params& prm, const void* q, const void* k,
