@@ -1260,16 +1260,6 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
         for (int c = 0; c <= nch; ++c) {
             // ---- phase 1
             f4 accQ[4];
-            half2v yo[8];  // y' of chunk c+1, written to the tile in phase 2
-            if (c + 1 < nch) {
-                // queries' features of chunk c+1 (omega goes to buffer (c+1) mod 3, last
-                // read in phase 2 of the previous step); the raw tokens of c+2 follow
-                fm_queries<D>(yo, rqq, sm, sm.om[(c + 1) % 3], p.eps_feat, odt, p.unit_feat);
-                if (c + 2 < nch) {
-                    step_fence();
-                    fm_load<D, true>(rqq, rq, rsb, t_begin + static_cast<int64_t>(c + 2) * L);
-                }
-            }
             if (c < nch) {
                 // G tiles -> G'; Q^T = U Y^T (rows m' = 16kw + 4g + jj, columns t); U update
                 const int ln = tid_now() & 63, g = ln >> 4, i = ln & 15;
@@ -1361,7 +1351,19 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                     wr4(s_st + 2 * 16 * tt * M2, sv[0], sv[1], sv[2], sv[3]);
                 }
             }
-            if (c + 1 < nch) fm_write_q<D>(yo, sm.yq);  // y' of chunk c+1, built in phase 1
+            if (c + 1 < nch) {
+                // queries' features of chunk c+1, after the combine so that no accumulator
+                // is live: y' to the tile (read in phase 1 of step c+1), omega to buffer
+                // (c+1) mod 3 (last read in phase 2 of step c-1); the raw tokens of c+2 follow
+                step_fence();
+                half2v yo[8];
+                fm_queries<D>(yo, rqq, sm, sm.om[(c + 1) % 3], p.eps_feat, odt, p.unit_feat);
+                fm_write_q<D>(yo, sm.yq);
+                if (c + 2 < nch) {
+                    step_fence();
+                    fm_load<D, true>(rqq, rq, rsb, t_begin + static_cast<int64_t>(c + 2) * L);
+                }
+            }
             lds_barrier();
         }
         if (tail_fix) {
