@@ -286,9 +286,10 @@ def varlen_bench(torch, fs, WL, steps=20, warmup=5):
                            "path": "device table only: sequential fp32 path"}}
 
 
-def normalized_bench(torch, fs, WL, config, steps=20, warmup=5):
+def normalized_bench(torch, fs, WL, config, steps=20, warmup=40):
     """The forward with the normalised readout (eta state) at the bench's
-    shape, on the sequential path, which is the one that has it."""
+    shape: the chunked path where the plain readout has one (AUTO), with eta
+    carried out; also the sequential path for comparison."""
     import numpy as np
     s = WL.spec(config)
     q, k, v = WL.make_rows(s)
@@ -302,25 +303,37 @@ def normalized_bench(torch, fs, WL, config, steps=20, warmup=5):
     o = torch.empty_like(qd)
     state = torch.empty((B, H, M, 2 * d, 2), dtype=torch.float32, device="cuda")
     eta = torch.empty((B, H, M, 2), dtype=torch.float32, device="cuda")
-    dims = fs.make_dims(B, N, H, d, M, W, "bf16", "auto")
-    nbytes = fs.idattn_forward_normalized_workspace_size(dims)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
     prm = fs.make_params(p)
+    out = {}
+    for algo in ("auto", "sequential"):
+        dims = fs.make_dims(B, N, H, d, M, W, "bf16", algo)
+        nbytes = fs.idattn_forward_normalized_workspace_size(dims)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
 
-    def call():
-        fs.idattn_forward_normalized(dims, prm, qd, kd, vd, o, None, None, None, state, None, eta, ws, nbytes)
+        def call():
+            fs.idattn_forward_normalized(dims, prm, qd, kd, vd, o, None, None, None, state, None, eta, ws, nbytes)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        call()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / steps
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps if algo == "auto" else 3):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (steps if algo == "auto" else 3)
+        out[algo] = {"ms_per_call": ms, "tokens_per_s": B * N / (ms * 1e-3)}
+        del ws
+    try:
+        fs.idattn_forward_normalized_workspace_size(fs.make_dims(B, N, H, d, M, W, "bf16", "chunked"))
+        path = "chunked (MFMA) path"
+    except fs.IdattnError:
+        path = "sequential fp32 path"
     return {"workload": f"{config}: B={B} H={H} N={N} d=R={d} M={M} W={W}, bf16 I/O, normalised readout (eta), "
-                        f"sequential fp32 path",
-            "ms_per_call": dt * 1e3, "tokens_per_s": B * N / dt}
+                        f"{path}", "ms_per_call": out["auto"]["ms_per_call"],
+            "tokens_per_s": out["auto"]["tokens_per_s"],
+            "sequential": dict(out["sequential"], path="sequential fp32 path")}
 
 
 def backward_bench(torch, fs, WL, config, steps=5, warmup=2):

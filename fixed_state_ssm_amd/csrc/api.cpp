@@ -350,14 +350,33 @@ idattn_status idattn_forward_noalloc(const idattn_dims* dims, const idattn_param
                         true);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The normalised readout's algorithm and workspace: the chunked one wherever
+// the plain readout has it (AUTO picks it there), else the sequential one.
+idattn_status normalized_plan(const idattn_dims& D, int* algo, size_t* bytes) {
+    *algo = resolve_algo(D);
+    if (*algo == IDATTN_ALGO_CHUNKED) {
+        idattn_status st = workspace_bytes(D, IDATTN_ALGO_CHUNKED, bytes);
+        if (st != IDATTN_OK) return st;
+        return IDATTN_OK;
+    }
+    *bytes = D.N == 0 ? 0 : seq_workspace_bytes(D, D.B * D.N, true);
+    return IDATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 idattn_status idattn_forward_normalized_workspace_size(const idattn_dims* dims, size_t* bytes) {
     if (bytes == nullptr) return fail(IDATTN_ERR_NULL, "bytes is NULL");
     idattn_status st = check_dims(dims, false);
     if (st != IDATTN_OK) return st;
-    if (dims->algo == IDATTN_ALGO_CHUNKED)
-        return fail(IDATTN_ERR_UNSUPPORTED, "the normalised readout runs on the sequential algorithm only");
-    *bytes = dims->N == 0 ? 0 : seq_workspace_bytes(*dims, dims->B * dims->N, true);
-    return IDATTN_OK;
+    int algo;
+    return normalized_plan(*dims, &algo, bytes);
 }
 
 idattn_status idattn_forward_normalized(const idattn_dims* dims, const idattn_params* params, const void* q,
@@ -369,10 +388,11 @@ idattn_status idattn_forward_normalized(const idattn_dims* dims, const idattn_pa
     st = check_params(*dims, params);
     if (st != IDATTN_OK) return st;
     const idattn_dims& D = *dims;
-    if (D.algo == IDATTN_ALGO_CHUNKED)
-        return fail(IDATTN_ERR_UNSUPPORTED, "the normalised readout runs on the sequential algorithm only");
+    int algo;
+    size_t need = 0;
+    st = normalized_plan(D, &algo, &need);
+    if (st != IDATTN_OK) return st;
     if (D.N > 0 && (!q || !k || !v || !o)) return fail(IDATTN_ERR_NULL, "q, k, v and o must be non-NULL");
-    const size_t need = D.N == 0 ? 0 : seq_workspace_bytes(D, D.B * D.N, true);
     if (need > 0 && workspace == nullptr) return fail(IDATTN_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
     if (workspace_bytes_given < need)
         return fail(IDATTN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_given, need);
@@ -406,6 +426,14 @@ idattn_status idattn_forward_normalized(const idattn_dims* dims, const idattn_pa
         if (st != IDATTN_OK || eta_out == nullptr) return st;
         const hipError_t e = idattn::launch_copy_or_zero(eta_in, eta_out, static_cast<int64_t>(etab / 4), s);
         if (e != hipSuccess) return hip_fail(e, "eta copy");
+        return IDATTN_OK;
+    }
+    if (algo == IDATTN_ALGO_CHUNKED) {
+        idattn::Problem p = problem(D);
+        p.eta = true;
+        const hipError_t e = idattn::launch_forward_chunked(p, *params, q, k, v, o, state_in, tail_in, state_out,
+                                                            tail_out, workspace, s, eta_in, eta_out);
+        if (e != hipSuccess) return hip_fail(e, "chunked forward (normalised readout)");
         return IDATTN_OK;
     }
     return run_sequential(problem(D), *params, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, s, true,

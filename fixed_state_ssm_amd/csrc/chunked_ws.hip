@@ -248,6 +248,8 @@ __device__ __forceinline__ half8 to_half8(const f4& a, const f4& b) {
 //   ft, ftl [M2][L] fp16, swizzled rows: F^T[m'][j] = T_{m'}[L-1-j] = ft + ftl
 //   pw [L][MM] float2: abar^{k+1}
 //   pwseg[MM] float2: abar^{Lseg};  hc float4: Delta, 1/Delta, kappa, 1/kappa
+//   hs [L][MM] float2: bbar sum_{j<=k} abar^j, dz [MM] double4: abar, bbar
+//   (normalised readout only)
 // with kappa a power of two per head such that kappa max_m |bbar_m| is in
 // [1/2, 1): F carries kappa (so that a small Delta |B| leaves the fp16 table
 // in the normal range), and so do the states derived from it.
@@ -257,7 +259,47 @@ constexpr int kTabFTL = kTabFT + M2 * L * 2;
 constexpr int kTabPw = kTabFTL + M2 * L * 2;
 constexpr int kTabPwSeg = kTabPw + L * MM * 8;
 constexpr int kTabHc = kTabPwSeg + MM * 8;
-constexpr int kTabBytes = ((kTabHc + 16 + 255) / 256) * 256;
+constexpr int kTabHs = ((kTabHc + 16 + 255) / 256) * 256;  // [L][MM] float2: bbar sum_{j<=k} abar^j
+constexpr int kTabDz = kTabHs + L * MM * 8;                  // [MM] double4: abar, bbar
+constexpr int kTabBytes = kTabDz + MM * 32;
+
+// abar^n by repeated squaring in fp64 (n >= 0): about 2 log2(n) complex
+// products, so the relative error stays near 1e-14 for any n here, with no
+// transcendental function (and no argument reduction of a large n Delta Im
+// lambda).
+__device__ inline void cpow_int(double ar, double ai, int64_t n, double& pr, double& pi) {
+    pr = 1.0;
+    pi = 0.0;
+    double br = ar, bi = ai;
+    while (n > 0) {
+        if (n & 1) {
+            const double t = pr * br - pi * bi;
+            pi = pr * bi + pi * br;
+            pr = t;
+        }
+        const double t = br * br - bi * bi;
+        bi = 2.0 * br * bi;
+        br = t;
+        n >>= 1;
+    }
+}
+// bbar sum_{j<n} abar^j = bbar (abar^n - 1) / (abar - 1), given abar^n (n bbar
+// when abar = 1): the response of the S4D system to n steps of a constant
+// input of one, which is what the normaliser eta accumulates.  abar - 1 has
+// a relative error near 1e-16 / |Delta lambda| in fp64, far below fp32.
+__device__ inline void geo_from_pow(double ar, double ai, double br, double bi, double pnr, double pni, double n,
+                                    double& sr, double& si) {
+    const double dr = ar - 1.0, di = ai;
+    const double den = dr * dr + di * di;
+    double qr = n, qi = 0.0;
+    if (den > 1e-280) {
+        const double nr = pnr - 1.0, ni = pni;
+        qr = (nr * dr + ni * di) / den;
+        qi = (ni * dr - nr * di) / den;
+    }
+    sr = br * qr - bi * qi;
+    si = br * qi + bi * qr;
+}
 
 // Complex fp64 power abar^n = exp(n Delta lambda).
 __device__ __forceinline__ void cpow(double dt, float lre, float lim, double n, double& pr, double& pi) {
@@ -325,6 +367,14 @@ __global__ __launch_bounds__(kTabThreads) void zoh_tables_kernel(Problem p, idat
     }
     reinterpret_cast<float2*>(th + kTabPw)[k * MM + m] =
         make_float2(static_cast<float>(pr * z.ar - pi * z.ai), static_cast<float>(pr * z.ai + pi * z.ar));
+    if (p.eta) {  // Hsum(k) = bbar sum_{j<=k} abar^j, for the normaliser
+        double hr, hi;
+        geo_from_pow(z.ar, z.ai, z.br, z.bi, pr * z.ar - pi * z.ai, pr * z.ai + pi * z.ar, static_cast<double>(k + 1), hr,
+                     hi);
+        reinterpret_cast<float2*>(th + kTabHs)[k * MM + m] = make_float2(static_cast<float>(hr), static_cast<float>(hi));
+        if (blockIdx.y == 0 && k == 0)
+            reinterpret_cast<double4*>(th + kTabDz)[m] = make_double4(z.ar, z.ai, z.br, z.bi);
+    }
 }
 
 // ------------------------------------------------------------------ shared memory
@@ -356,6 +406,10 @@ struct SmemFwd {
     float wq[D * kMaxW], wk[D * kMaxW];  // conv weights times -log2(e), right-aligned taps (layout: wt_index)
     uint16_t halo[2][3][D];              // raw q, k at positions -3..-1 of the sequence
     float fac[16][2][8];                 // per-token feature factors, by wave and token block
+    // normalised readout: eta before the chunk, Hsum(15), Hsum(L-1), and the key
+    // waves' partial denominators [chunk parity][token][key wave]
+    float2 ec0[MM], hs15[MM], hsL[MM];
+    float dpart[2][L][8];
 };
 static_assert(offsetof(SmemFwd<128>, pp) == offsetof(SmemFwd<128>, gp) + sizeof(_Float16) * L * RP &&
                   offsetof(SmemFwd<64>, pp) == offsetof(SmemFwd<64>, gp) + sizeof(_Float16) * L * RP && RP >= L + 15,
@@ -963,7 +1017,8 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
                                                             const float* __restrict__ state_in,
                                                             const uint8_t* __restrict__ tab, float* __restrict__ c0,
                                                             float* __restrict__ ws, _Float16* __restrict__ zt,
-                                                            int64_t Lseg, int S) {
+                                                            int64_t Lseg, int S, const float* eta_in, float* eta_out,
+                                                            float2* __restrict__ c0eta) {
     __shared__ SmemSeg<D> sm;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool key = w < 8;
@@ -991,6 +1046,22 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
     // of the forward can write state_out, so the two may be one buffer.
     const bool stage = seg == 0 && state_in != nullptr;
     const float kap = reinterpret_cast<const float4*>(th + kTabHc)[0].z;
+    if (p.eta && seg == 0 && tid < MM) {
+        // the normaliser: eta_in staged for the forward, and eta_out = abar^N eta_in +
+        // bbar sum_{j<N} abar^j in closed form (the same thread reads eta_in and
+        // writes eta_out, so the two may be one buffer)
+        const int m = tid;
+        const double ein_r = eta_in ? eta_in[(bh * MM + m) * 2] : 0.0, ein_i = eta_in ? eta_in[(bh * MM + m) * 2 + 1] : 0.0;
+        c0eta[bh * MM + m] = make_float2(static_cast<float>(ein_r), static_cast<float>(ein_i));
+        if (eta_out != nullptr) {
+            const double4 z = reinterpret_cast<const double4*>(th + kTabDz)[m];  // abar, bbar
+            double ar, ai, gr, gi;
+            cpow_int(z.x, z.y, p.N, ar, ai);
+            geo_from_pow(z.x, z.y, z.z, z.w, ar, ai, static_cast<double>(p.N), gr, gi);
+            eta_out[(bh * MM + m) * 2] = static_cast<float>(ar * ein_r - ai * ein_i + gr);
+            eta_out[(bh * MM + m) * 2 + 1] = static_cast<float>(ar * ein_i + ai * ein_r + gi);
+        }
+    }
     const float* sin = stage ? state_in + bh * MM * 2 * D * 2 : nullptr;
     float* cst = c0 + bh * MM * 2 * D * 2;
     if (key) {
@@ -1165,7 +1236,14 @@ __device__ __forceinline__ void p_tile(const SM& sm, int qt, int ln, uint32_t xo
 // (c) written in 2 of step c, read in 1 of step c+1; P~ (c-1) written in 1,
 // read in 2 of step c; z_v (c) written in 1 and read in 2 of step c into
 // registers that the readout of step c+1 uses.
-template <int D>
+// With ETA (the normalised readout o = Re sum s Gamma / Re sum s eta), the key
+// waves also form each token's denominator from the fp32 scores before their
+// fp16 rounding: eta_m(t) = abar^{t+1} eta_m(before the chunk) + Hsum_m(t), so
+// den_t = Re sum_m s_m(t) eta_m(t) = omega_t kappa Re sum_m s~_m(t) eta_m(t); the
+// token factor omega_t cancels in the ratio, so o_t = (P~ Z_v + Re X Gamma)_t /
+// (kappa sum_m Re s~ eta).  eta needs no scan: its value at any position is a
+// closed form of the staged eta_in (fp64 in the prologue).
+template <int D, bool ETA>
 __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_params prm,
                                                               const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
@@ -1176,7 +1254,8 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                                                               const uint8_t* __restrict__ tab,
                                                               const float* __restrict__ c0,
                                                               const float* __restrict__ carry, int64_t Lseg, int S,
-                                                              int fold) {
+                                                              int fold, const float2* __restrict__ c0eta,
+                                                              bool has_eta) {
     constexpr int RT = Cfg<D>::RT, KB = Cfg<D>::KB, YR = Cfg<D>::YR;
     constexpr uint32_t dl = WinOff<D>::ftl - WinOff<D>::ft;
     __shared__ SmemFwd<D> sm;
@@ -1213,7 +1292,20 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
     // carry kappa, undone by K and omega (both carry 1 / kappa) and on
     // the state's way in and out
     const float4 hc = reinterpret_cast<const float4*>(th + kTabHc)[0];
-    const float inv_kap = hc.w;
+    const float inv_kap = hc.w, kap = hc.z;
+    if (ETA && tid < MM) {
+        const int m = tid;
+        const double4 z = reinterpret_cast<const double4*>(th + kTabDz)[m];  // abar, bbar
+        double ar, ai, gr, gi;
+        cpow_int(z.x, z.y, t_begin, ar, ai);
+        geo_from_pow(z.x, z.y, z.z, z.w, ar, ai, static_cast<double>(t_begin), gr, gi);
+        const float2 e = has_eta ? c0eta[bh * MM + m] : make_float2(0.f, 0.f);
+        sm.ec0[m] = make_float2(static_cast<float>(ar * e.x - ai * e.y + gr), static_cast<float>(ar * e.y + ai * e.x + gi));
+        const float2* hs = reinterpret_cast<const float2*>(th + kTabHs);
+        sm.hs15[m] = hs[15 * MM + m];
+        sm.hsL[m] = hs[(L - 1) * MM + m];
+    }
+    (void)kap;
     const float odt = 4.f * hc.x * hc.w;        // 4 Delta / kappa, the output factor's constant part
     const float ks = -0.25f * kLn2 * hc.y * hc.w;  // K = -ln2 / (4 Delta kappa), the mode scores' scale
     const int rsb = static_cast<int>(H * D * 2);  // token stride, bytes
@@ -1237,6 +1329,9 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
     if (key) {
         // ---------------- key waves
         const int kw = w;
+        float4 hsi = {};  // Hsum(i) of the lane's two modes (normalised readout)
+        if constexpr (ETA)
+            hsi = reinterpret_cast<const float4*>(th + kTabHs)[((tid & 15) * MM + 8 * kw + 2 * ((tid & 63) >> 4)) / 2];
         f4 U[RT];
         // before the token loads, which are waited for first
         if (seg > 0 && !fold) {
@@ -1330,6 +1425,20 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                 // s~ and X: 8-byte stores at the perm32 position of m' = 16kw + 4g
                 const uint32_t pst = opaque(2 * x256(i, perm32(16 * kw + 4 * g)));
                 const uint32_t x_st = lds_addr(sm.xc) + pst, s_st = lds_addr(sm.sc) + pst;
+                // normalised readout: eta_m(t) of tokens t = i, 16 + i, ..., modes 8kw + 2g + qq
+                float etr[2] = {}, eti[2] = {}, h15r[2] = {}, h15i[2] = {}, dp[4] = {};
+                if constexpr (ETA) {
+                    const float4 c0v = *reinterpret_cast<const float4*>(&sm.ec0[8 * kw + 2 * g]);
+                    const float4 h15 = *reinterpret_cast<const float4*>(&sm.hs15[8 * kw + 2 * g]);
+                    const float c0r[2] = {c0v.x, c0v.z}, c0i[2] = {c0v.y, c0v.w};
+                    const float hr[2] = {hsi.x, hsi.z}, hi[2] = {hsi.y, hsi.w};
+                    h15r[0] = h15.x; h15i[0] = h15.y; h15r[1] = h15.z; h15i[1] = h15.w;
+#pragma unroll
+                    for (int qq = 0; qq < 2; ++qq) {
+                        etr[qq] = er[qq] * c0r[qq] - ei[qq] * c0i[qq] + hr[qq];
+                        eti[qq] = er[qq] * c0i[qq] + ei[qq] * c0r[qq] + hi[qq];
+                    }
+                }
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     const float sg = ks;
@@ -1346,9 +1455,37 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                         const float nr = er[qq] * e16r[qq] - ei[qq] * e16i[qq];
                         ei[qq] = er[qq] * e16i[qq] + ei[qq] * e16r[qq];
                         er[qq] = nr;
+                        if constexpr (ETA) {
+                            // Re(s~ eta) of this token, then eta 16 tokens on: abar^16 eta + Hsum(15)
+                            dp[tt] = fmaf(sr, etr[qq], fmaf(-si, eti[qq], dp[tt]));
+                            const float ar_ = e16r[qq] * etr[qq] - e16i[qq] * eti[qq] + h15r[qq];
+                            eti[qq] = e16r[qq] * eti[qq] + e16i[qq] * etr[qq] + h15i[qq];
+                            etr[qq] = ar_;
+                        }
                     }
                     wr4(x_st + 2 * 16 * tt * M2, xv[0], xv[1], xv[2], xv[3]);
                     wr4(s_st + 2 * 16 * tt * M2, sv[0], sv[1], sv[2], sv[3]);
+                }
+                if constexpr (ETA) {
+                    // sum over the four lane groups (the wave's 8 modes), one partial per
+                    // token and key wave; then eta before the next chunk, abar^L eta + Hsum(L-1)
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) {
+                        float x = dp[tt];
+                        const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+                        x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+                        const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+                        x = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+                        if (g == 0) sm.dpart[c & 1][16 * tt + i][kw] = x;
+                    }
+                    if (i == 0) {
+#pragma unroll
+                        for (int qq = 0; qq < 2; ++qq) {
+                            const int m = 8 * kw + 2 * g + qq;
+                            const float2 a = sm.aL[m], e = sm.ec0[m], hl = sm.hsL[m];
+                            sm.ec0[m] = make_float2(a.x * e.x - a.y * e.y + hl.x, a.x * e.y + a.y * e.x + hl.y);
+                        }
+                    }
                 }
             }
             if (c + 1 < nch) {
@@ -1446,7 +1583,15 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     const uint32_t toff = static_cast<uint32_t>((tp + 16 * tt) * rsb);
-                    const float w = om[16 * tt + i];
+                    float w;
+                    if constexpr (ETA) {
+                        // 1 / den_t from the key waves' partials of chunk c-1, in a fixed order
+                        const float4 a = *reinterpret_cast<const float4*>(&sm.dpart[(c - 1) & 1][16 * tt + i][0]);
+                        const float4 bq = *reinterpret_cast<const float4*>(&sm.dpart[(c - 1) & 1][16 * tt + i][4]);
+                        w = 1.f / (kap * (((a.x + a.y) + (a.z + a.w)) + ((bq.x + bq.y) + (bq.z + bq.w))));
+                    } else {
+                        w = om[16 * tt + i];
+                    }
                     const u2 pk = {pack_bf16(accO[tt][0] * w, accO[tt][1] * w), pack_bf16(accO[tt][2] * w, accO[tt][3] * w)};
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, pk), ob, olane + toff, 0, 0);
                 }
@@ -1498,10 +1643,10 @@ void plan_segments(const Problem& p, int& S, int64_t& Lseg) {
 }
 
 // Workspace: per-head tables | the staged kappa state_in, [B H] states in lane
-// order | segment end states, [S-1][B H] | fp16 key-feature tiles, one z_k^T
-// per chunk slot of every segment.
+// order | the staged eta_in, [B H][M] complex | segment end states, [S-1][B H]
+// | fp16 key-feature tiles, one z_k^T per chunk slot of every segment.
 struct WsLayout {
-    size_t tab, c0, seg, zt, total;
+    size_t tab, c0, c0eta, seg, zt, total;
 };
 WsLayout ws_layout(const Problem& p, int S, int64_t Lseg) {
     const size_t state = static_cast<size_t>(MM) * 2 * p.d * 2 * sizeof(float);
@@ -1509,7 +1654,8 @@ WsLayout ws_layout(const Problem& p, int S, int64_t Lseg) {
     WsLayout w;
     w.tab = 0;
     w.c0 = static_cast<size_t>(p.H) * kTabBytes;
-    w.seg = w.c0 + pairs * state;
+    w.c0eta = w.c0 + pairs * state;
+    w.seg = w.c0eta + ((pairs * MM * 8 + 255) / 256) * 256;
     w.zt = w.seg + static_cast<size_t>(S - 1) * pairs * state;
     w.total = w.zt + pairs * S * static_cast<size_t>(Lseg) * p.d * sizeof(_Float16);
     return w;
@@ -1518,7 +1664,7 @@ WsLayout ws_layout(const Problem& p, int S, int64_t Lseg) {
 template <int D>
 hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, const void* k, const void* v, void* o,
                   const float* state_in, const void* tail_in, float* state_out, void* tail_out, void* workspace,
-                  hipStream_t stream) {
+                  hipStream_t stream, const float* eta_in, float* eta_out) {
     int S;
     int64_t Lseg;
     plan_segments(p, S, Lseg);
@@ -1530,14 +1676,15 @@ hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, con
     uint8_t* base = static_cast<uint8_t*>(workspace);
     uint8_t* tab = base + lay.tab;
     float* c0 = reinterpret_cast<float*>(base + lay.c0);
+    float2* c0eta = reinterpret_cast<float2*>(base + lay.c0eta);
     float* ws = reinterpret_cast<float*>(base + lay.seg);
     _Float16* zt = reinterpret_cast<_Float16*>(base + lay.zt);
     const int64_t pairs = p.B * p.H;
     zoh_tables_kernel<<<dim3(static_cast<unsigned>(p.H), 17), kTabThreads, 0, stream>>>(p, prm, Lseg, tab);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    segment_state_kernel<D><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(p, prm, k16, v16, t16, state_in,
-                                                                                      tab, c0, ws, zt, Lseg, S);
+    segment_state_kernel<D><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(
+        p, prm, k16, v16, t16, state_in, tab, c0, ws, zt, Lseg, S, eta_in, eta_out, c0eta);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int fold = S <= kFoldMax ? 1 : 0;
@@ -1548,9 +1695,14 @@ hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, con
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    chunked_forward_kernel<D><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(
-        p, prm, q16, k16, v16, zt, static_cast<uint16_t*>(o), state_in, t16, state_out, static_cast<uint16_t*>(tail_out),
-        tab, c0, ws, Lseg, S, fold);
+    if (p.eta)
+        chunked_forward_kernel<D, true><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(
+            p, prm, q16, k16, v16, zt, static_cast<uint16_t*>(o), state_in, t16, state_out,
+            static_cast<uint16_t*>(tail_out), tab, c0, ws, Lseg, S, fold, c0eta, eta_in != nullptr);
+    else
+        chunked_forward_kernel<D, false><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(
+            p, prm, q16, k16, v16, zt, static_cast<uint16_t*>(o), state_in, t16, state_out,
+            static_cast<uint16_t*>(tail_out), tab, c0, ws, Lseg, S, fold, c0eta, false);
     return hipGetLastError();
 }
 
@@ -1583,15 +1735,19 @@ size_t chunked_workspace_bound(const Problem& p) {
     const int64_t chunks = (p.N + cws::L - 1) / cws::L;
     const size_t slots = static_cast<size_t>(chunks + (chunks + 1) / 2);
     return static_cast<size_t>(p.H) * cws::kTabBytes + static_cast<size_t>(p.H) * state +
+           ((static_cast<size_t>(p.H) * cws::MM * 8 + 255) / 256) * 256 +
            static_cast<size_t>(smax - 1) * p.H * state + static_cast<size_t>(p.H) * slots * cws::L * p.d * 2;
 }
 
 hipError_t launch_forward_chunked(const Problem& p, const idattn_params& prm, const void* q, const void* k,
                                   const void* v, void* o, const float* state_in, const void* tail_in,
-                                  float* state_out, void* tail_out, void* workspace, hipStream_t stream) {
+                                  float* state_out, void* tail_out, void* workspace, hipStream_t stream,
+                                  const float* eta_in, float* eta_out) {
     if (p.d == 128)
-        return cws::launch<128>(p, prm, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, stream);
-    return cws::launch<64>(p, prm, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, stream);
+        return cws::launch<128>(p, prm, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, stream, eta_in,
+                                eta_out);
+    return cws::launch<64>(p, prm, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, stream, eta_in,
+                           eta_out);
 }
 
 }  // namespace idattn

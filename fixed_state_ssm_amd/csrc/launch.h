@@ -19,6 +19,8 @@ struct Problem {
     // each (T = B N); else a packed batch, sequence b = tokens cu[b] .. cu[b+1]-1.
     int64_t T;
     const int32_t* cu;
+    // normalised readout on the chunked path (o = Re sum s Gamma / Re sum s eta)
+    bool eta = false;
 };
 
 // ---- stage kernels of the sequential (fp32) path; workspace layout [H][T][*]
@@ -48,11 +50,14 @@ size_t chunked_workspace_bytes(const Problem& p);
 // tokens (monotone in p.N).
 size_t chunked_workspace_bound(const Problem& p);
 bool chunked_supported(const Problem& p);
-// Also writes tail_out (when not NULL) like launch_tail_update.
+// Also writes tail_out (when not NULL) like launch_tail_update.  With p.eta the
+// readout is the normalised one, eta_in / eta_out the normaliser ([B][H][M]
+// complex; NULL = zeros / no output; eta_out may equal eta_in).
 hipError_t launch_forward_chunked(const Problem& p, const idattn_params& prm,
                                   const void* q, const void* k, const void* v, void* o,
                                   const float* state_in, const void* tail_in,
-                                  float* state_out, void* tail_out, void* workspace, hipStream_t stream);
+                                  float* state_out, void* tail_out, void* workspace, hipStream_t stream,
+                                  const float* eta_in = nullptr, float* eta_out = nullptr);
 
 // ---- backward (sequential fp32; dense batches, SiLU feature maps)
 size_t backward_workspace_bytes(const Problem& p);

@@ -197,9 +197,13 @@ idattn_status idattn_forward_noalloc(const idattn_dims *dims, const idattn_param
  *  eta_out  out  NULL or [B][H][M][2]; may equal eta_in exactly (in place)
  *  all other arguments as for idattn_forward; the workspace is
  *  idattn_forward_normalized_workspace_size bytes.
- * dims->algo: AUTO or SEQUENTIAL (CHUNKED returns IDATTN_ERR_UNSUPPORTED).
- * One token per call from a carried state, tail and eta is the decode step
- * of this readout.
+ * dims->algo: AUTO takes the chunked algorithm wherever idattn_forward has it
+ * (bf16, d in {64, 128}, M = 64, W <= 4, not the RFF map), else the
+ * sequential one; CHUNKED elsewhere returns IDATTN_ERR_UNSUPPORTED.  The
+ * chunked algorithm forms the denominator in fp32 from the mode scores before
+ * their fp16 rounding and eta in closed form (fp64), so eta_out is exact to
+ * fp32 rounding.  One token per call from a carried state, tail and eta is
+ * the decode step of this readout.
  */
 idattn_status idattn_forward_normalized_workspace_size(const idattn_dims *dims, size_t *bytes);
 

@@ -285,9 +285,10 @@ def call_normalized(d, p, ws_bytes=None, ei=11 * QB, eo=12 * QB, **over):
 
 
 def test_normalized_validation():
-    """The normalised readout: sequential only, a workspace larger than the
-    plain sequential one by the denominator shares, eta buffers aligned and
-    clear of every other buffer (eta_out == eta_in exactly is allowed)."""
+    """The normalised readout: a workspace larger than the plain sequential one
+    by the denominator shares; the chunked algorithm where the plain readout
+    has one (M = 64 here, not M = 32); eta buffers aligned and clear of every
+    other buffer (eta_out == eta_in exactly is allowed)."""
     d = dims(algo="sequential")
     plain = fs.idattn_forward_workspace_size(d)
     need = fs.idattn_forward_normalized_workspace_size(d)
@@ -303,6 +304,9 @@ def test_normalized_validation():
     expect(call_normalized(d, p, ei=ADDR["so"]), "IDATTN_ERR_ALIAS")            # state_out over eta_in
     expect(call_normalized(d, p, eo=p.A), "IDATTN_ERR_ALIAS")                   # eta_out over a parameter
     expect(call_normalized(dims(algo="chunked"), p, ws_bytes=1 << 40), "IDATTN_ERR_UNSUPPORTED")
+    chunked = fs.idattn_forward_normalized_workspace_size(dims(M=64, algo="chunked"))
+    assert chunked == fs.idattn_forward_workspace_size(dims(M=64, algo="chunked"))
+    assert fs.idattn_forward_normalized_workspace_size(dims(M=64)) == chunked  # AUTO picks it
 
 
 def test_decode_normalized_validation():

@@ -205,8 +205,14 @@ def _eta_backward_error(o_gpu, pt):
     return float(np.linalg.norm(r) / np.linalg.norm(scale))
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "d16_m64_w2_f32", "d64_m32_ragged_bf16", "d128_m64_ragged_bf16",
-                                  "d128_m16_f32"])
+# shapes on the sequential path (fp32, M = 32 or 16, d = 16) and on the chunked
+# one (bf16, d = 64 or 128, M = 64), with one segment and with four (the folded
+# carry), and conv widths 1 and 2
+NORMALIZED = ["tiny_f32", "d16_m64_w2_f32", "d64_m32_ragged_bf16", "d128_m64_ragged_bf16", "d128_m16_f32",
+              "d128_segments_bf16", "d64_segments_bf16", "d64_w1_bf16", "d128_w2_bf16"]
+
+
+@pytest.mark.parametrize("name", NORMALIZED)
 def test_forward_normalized(fs, name):
     import torch
     base, over, tag = SMALL[name]
@@ -220,23 +226,57 @@ def test_forward_normalized(fs, name):
                                                                    tail_in=tl0, eta_in=eta0, parts=True)
     eta_d = torch.from_numpy(np.stack([eta0.real, eta0.imag], -1).astype(np.float32)).cuda()
     p = fs.params_to_device(c.params)
-    o, st, tl, eta = fs.forward_normalized(up(c.q, io), up(c.k, io), up(c.v, io), p, state_in=state_dev(st0),
-                                           tail_in=up(tl0, io), eta_in=eta_d, return_state=True)
-    _sync()
-    e_o = _eta_backward_error(down(o).astype(np.float64), pt)
-    e_s = rel_l2(state_np(st), st_ref)
-    e_eta = rel_l2(state_np(eta), eta_ref)
-    print(f"normalized {name}: o backward error {e_o:.2e}, state {e_s:.2e}, eta {e_eta:.2e}, "
-          f"den < 0 at {float((pt['den'] < 0).mean()):.3f}", flush=True)
-    assert e_o <= gate(io), e_o
-    assert e_s <= gate(io), e_s
-    assert e_eta <= GATE_F32, e_eta  # eta is fp32 whatever the I/O type
-    assert np.array_equal(down(tl), tl_ref.astype(np.float32))
+    for algo in _algos(io):
+        if algo == "chunked" and not _chunked_available(fs, s):
+            continue
+        o, st, tl, eta = fs.forward_normalized(up(c.q, io), up(c.k, io), up(c.v, io), p, state_in=state_dev(st0),
+                                               tail_in=up(tl0, io), eta_in=eta_d, return_state=True, algo=algo)
+        _sync()
+        e_o = _eta_backward_error(down(o).astype(np.float64), pt)
+        e_eta = rel_l2(state_np(eta), eta_ref)
+        print(f"normalized {name} {algo}: o backward error {e_o:.2e}, eta {e_eta:.2e}, "
+              f"den < 0 at {float((pt['den'] < 0).mean()):.3f}", flush=True)
+        assert e_o <= gate(io), e_o
+        check(f"normalized {name} {algo} state", state_np(st), st_ref, gate(io), io)
+        assert e_eta <= GATE_F32, e_eta  # eta is fp32 whatever the I/O type
+        assert np.array_equal(down(tl), tl_ref.astype(np.float32))
     # the numerator is the plain readout: the same call through idattn_forward
     o_plain = fs.forward(up(c.q, io), up(c.k, io), up(c.v, io), p, state_in=state_dev(st0), tail_in=up(tl0, io),
                          algo="sequential")
     _sync()
     assert rel_l2(down(o_plain), pt["num"]) <= gate(io)
+
+
+@pytest.mark.parametrize("shape", [dict(B=4, H=16, N=200), dict(B=1, H=2, N=1000)], ids=["fold", "carry"])
+def test_forward_normalized_chunked_in_place(fs, shape):
+    """The chunked normalised readout with state, tail and eta updated in
+    place (one buffer each for input and output), on the folded-carry plan
+    (four segments) and the carry-kernel plan (sixteen)."""
+    import torch
+    c = WL.make_case("1p3b", seed=4, tag=76, **shape)
+    s = c.spec
+    st0, tl0 = WL.make_decode_state(s, seed=5)
+    r = np.random.default_rng(6)
+    eta0 = 0.1 * (r.standard_normal((s["B"], s["H"], s["M"])) + 1j * r.standard_normal((s["B"], s["H"], s["M"])))
+    _, st_ref, tl_ref, eta_ref, pt = oracle.forward_normalized(c.q, c.k, c.v, c.params, state_in=st0, tail_in=tl0,
+                                                               eta_in=eta0, parts=True)
+    p = fs.params_to_device(c.params)
+    B, N, H, d, M, W = s["B"], s["N"], s["H"], s["d"], s["M"], s["W"]
+    dims = fs.make_dims(B, N, H, d, M, W, "bf16", "chunked")
+    nb = fs.idattn_forward_normalized_workspace_size(dims)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    st, tl = state_dev(st0), up(tl0, "bf16")
+    eta = torch.from_numpy(np.stack([eta0.real, eta0.imag], -1).astype(np.float32)).cuda()
+    o = torch.empty((B, N, H, d), dtype=torch.bfloat16, device="cuda")
+    fs.idattn_forward_normalized(dims, fs.make_params(p), up(c.q, "bf16"), up(c.k, "bf16"), up(c.v, "bf16"), o, st, tl,
+                                 eta, st, tl, eta, ws, nb)
+    _sync()
+    e_o = _eta_backward_error(down(o).astype(np.float64), pt)
+    print(f"normalized chunked in place {shape}: o backward error {e_o:.2e}", flush=True)
+    assert e_o <= GATE_BF16, e_o
+    check(f"normalized chunked in place {shape} state", state_np(st), st_ref, GATE_BF16, "bf16")
+    assert rel_l2(state_np(eta), eta_ref) <= GATE_F32
+    assert np.array_equal(down(tl), tl_ref.astype(np.float32))
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
@@ -566,8 +606,8 @@ def test_full_config_all_pairs(fs, cfg):
 @pytest.mark.parametrize("variant", ["unit", "rff", "normalized"])
 def test_full_shape_variants_sampled_pairs(fs, variant):
     """The feature-map and readout variants at the full 1.3B shape (B=4 H=16
-    N=4096 d=128 M=64, bf16 I/O): unit-norm map on the chunked path, RFF map
-    and normalised readout on the sequential path; the oracle recomputes two
+    N=4096 d=128 M=64, bf16 I/O): unit-norm map and normalised readout on the
+    chunked path, RFF map on the sequential path; the oracle recomputes two
     (b, h) sequences end to end."""
     import torch
     s = WL.spec("1p3b")
