@@ -235,12 +235,13 @@ def decode_bench(torch, fs, steps, warmup):
                          "algorithmic_bytes": nbytes}}
 
 
-def varlen_bench(torch, fs, WL, steps=20, warmup=5):
+def varlen_bench(torch, fs, WL, dense_ms=None, steps=20, warmup=40):
     """Packed variable-length batch at the 1.3B head shape (H=16, d=128, M=64,
-    W=4, bf16): 16 384 tokens in 8 sequences of mixed lengths (long prompts
-    beside short ones).  With the lengths also on the host the library runs
-    one chunked forward per sequence; with the device table alone, the
-    sequential path."""
+    W=4, bf16): 16 384 tokens (the dense 1.3B batch's count) in 8 sequences
+    of mixed lengths (long prompts beside short ones).  AUTO runs the chunked
+    kernels in one launch sequence whose plan is built on the device from
+    the sequence table; the sequential fp32 path is timed beside it.  Each
+    call is timed with HIP events on the stream, as the dense forward is."""
     import numpy as np
     lens = [6000, 3500, 2500, 2048, 1200, 700, 400, 36]
     s = WL.spec("1p3b", B=1, N=sum(lens), tag=90)
@@ -254,36 +255,41 @@ def varlen_bench(torch, fs, WL, steps=20, warmup=5):
 
     qd, kd, vd = up(q), up(k), up(v)
     o = torch.empty_like(qd)
-    cu_host = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    cu = torch.from_numpy(cu_host).cuda()
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
     state = torch.zeros((B, H, M, 2 * d, 2), dtype=torch.float32, device="cuda")
     tail = torch.zeros((B, H, 2, W - 1, d), dtype=torch.bfloat16, device="cuda")
-    dims = fs.make_dims(B, T, H, d, M, W, "bf16", "auto")
-    nbytes = fs.idattn_forward_varlen_workspace_size(dims)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
 
-    def timed(host):
+    def timed(algo):
+        dims = fs.make_dims(B, T, H, d, M, W, "bf16", algo)
+        nbytes = fs.idattn_forward_varlen_workspace_size(dims)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+
         def call():
-            fs.idattn_forward_varlen(dims, prm, cu, qd, kd, vd, o, None, None, state, tail, ws, nbytes,
-                                     cu_seqlens_host=host)
+            fs.idattn_forward_varlen(dims, prm, cu, qd, kd, vd, o, None, None, state, tail, ws, nbytes)
 
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for e0, e1 in ev:
+            e0.record()
             call()
+            e1.record()
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps
+        return sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
 
-    dt = timed(cu_host)
-    dt_seq = timed(None)
-    return {"workload": f"packed batch: {B} sequences, lengths {lens} (T={T}), H={H} d=R={d} M={M} W={W}, "
-                        f"bf16 I/O",
-            "ms_per_call": dt * 1e3, "tokens_per_s": T / dt,
-            "path": "host lengths given: one chunked forward per sequence",
-            "sequential": {"ms_per_call": dt_seq * 1e3, "tokens_per_s": T / dt_seq,
-                           "path": "device table only: sequential fp32 path"}}
+    ms = timed("auto")
+    ms_seq = timed("sequential")
+    out = {"workload": f"packed batch: {B} sequences, lengths {lens} (T={T}), H={H} d=R={d} M={M} W={W}, "
+                       f"bf16 I/O",
+           "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
+           "path": "chunked kernels, one launch sequence, plan built on the device from the sequence table",
+           "sequential": {"ms_per_call": ms_seq, "tokens_per_s": T / (ms_seq * 1e-3),
+                          "path": "sequential fp32 path"}}
+    if dense_ms:
+        out["dense_1p3b_ms_per_call"] = dense_ms
+        out["ratio_to_dense"] = ms / dense_ms
+    return out
 
 
 def normalized_bench(torch, fs, WL, config, steps=20, warmup=40):
@@ -494,7 +500,7 @@ def main():
     out["measured_copy_gbps"] = measure_copy_gbps(torch)
     if not args.no_decode:
         out["decode"] = decode_bench(torch, fs, steps=20, warmup=20)
-        out["varlen"] = varlen_bench(torch, fs, WL)
+        out["varlen"] = varlen_bench(torch, fs, WL, mean_launch_ms if args.config == "1p3b" else None)
         out["normalized"] = normalized_bench(torch, fs, WL, args.config)
         out["backward"] = backward_bench(torch, fs, WL, args.config)
     del sets, ws

@@ -2,8 +2,9 @@
 
 The work runs in libidattn.so (HIP kernels behind a C ABI, include/idattn.h).
 This package holds the ctypes binding (functions named like the C entry
-points) and four conveniences, forward(), forward_normalized(),
-forward_varlen() and decode_step(), that allocate outputs and workspace with PyTorch and call the
+points) and conveniences, forward(), forward_normalized(), forward_varlen()
+(and forward_varlen_into() for caller-provided outputs), decode_step() and
+backward(), that allocate outputs and workspace with PyTorch and call the
 binding on the current stream.
 """
 from __future__ import annotations
@@ -24,7 +25,8 @@ __all__ = ["IdattnParamGrads", "idattn_backward", "idattn_backward_workspace_siz
            "idattn_forward_normalized_workspace_size", "idattn_forward_varlen", "idattn_forward_varlen_workspace_size",
            "idattn_forward_workspace_size",
            "idattn_last_error", "idattn_status_string", "idattn_version", "load_library",
-           "make_dims", "make_params", "forward", "forward_normalized", "forward_varlen", "decode_step",
+           "make_dims", "make_params", "forward", "forward_normalized", "forward_varlen", "forward_varlen_into",
+           "decode_step",
            "params_to_device"]
 
 PARAM_KEYS = ("conv_q", "conv_k", "gain", "bias", "log_dt", "A", "Bc")
@@ -103,14 +105,35 @@ def forward_normalized(q, k, v, params: dict, *, state_in=None, tail_in=None, et
 
 def forward_varlen(q, k, v, params: dict, cu_seqlens, *, state_in=None, tail_in=None, return_state=False,
                    algo="auto", eps_feat=1e-6, eps_norm=1e-6, feature_norm="squared", stream=None,
-                   host_lengths=True):
+                   host_lengths=False):
     """o = mixer over a packed batch: q, k, v [T, H, d] on the GPU hold B
     sequences end to end, sequence b being tokens cu_seqlens[b] ..
     cu_seqlens[b+1]-1 (cu_seqlens: int32 device tensor [B + 1]).  state_in
     [B, H, M, 2d, 2] and tail_in [B, H, 2, W-1, d] or None.  host_lengths
-    also hands a host copy of the table to the library (one device-to-host
-    copy), which lets it run the chunked algorithm.  With return_state=True
-    returns (o, state_out, tail_out)."""
+    also hands a host copy of the table to the library, which checks it (one
+    device-to-host copy).  With return_state=True returns (o, state_out,
+    tail_out)."""
+    import torch
+    T, H, d = q.shape
+    B = cu_seqlens.shape[0] - 1
+    M = params["A"].shape[1]
+    W = params["conv_q"].shape[-1]
+    state_out = tail_out = None
+    if return_state:
+        state_out = torch.empty((B, H, M, 2 * d, 2), dtype=torch.float32, device=q.device)
+        tail_out = torch.empty((B, H, 2, W - 1, d), dtype=q.dtype, device=q.device)
+    o = forward_varlen_into(q, k, v, params, cu_seqlens, state_in=state_in, tail_in=tail_in, state_out=state_out,
+                            tail_out=tail_out, algo=algo, eps_feat=eps_feat, eps_norm=eps_norm,
+                            feature_norm=feature_norm, stream=stream, host_lengths=host_lengths)
+    return (o, state_out, tail_out) if return_state else o
+
+
+def forward_varlen_into(q, k, v, params: dict, cu_seqlens, *, o=None, state_in=None, tail_in=None, state_out=None,
+                        tail_out=None, algo="auto", eps_feat=1e-6, eps_norm=1e-6, feature_norm="squared",
+                        stream=None, host_lengths=False):
+    """forward_varlen into caller-provided outputs (any of o, state_out,
+    tail_out; o is allocated when None): state_out may be state_in and
+    tail_out tail_in (in place).  Returns o."""
     import torch
     T, H, d = q.shape
     B = cu_seqlens.shape[0] - 1
@@ -124,15 +147,12 @@ def forward_varlen(q, k, v, params: dict, cu_seqlens, *, state_in=None, tail_in=
     dims = make_dims(B, T, H, d, M, W, _io_name(q), algo, eps_feat, eps_norm, feature_norm)
     nbytes = idattn_forward_varlen_workspace_size(dims)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q)
-    state_out = tail_out = None
-    if return_state:
-        state_out = torch.empty((B, H, M, 2 * d, 2), dtype=torch.float32, device=q.device)
-        tail_out = torch.empty((B, H, 2, W - 1, d), dtype=q.dtype, device=q.device)
+    if o is None:
+        o = torch.empty_like(q)
     host = cu_seqlens.cpu().tolist() if host_lengths else None
     idattn_forward_varlen(dims, make_params(params), cu_seqlens, q, k, v, o, state_in, tail_in, state_out, tail_out,
                           ws, nbytes, stream, cu_seqlens_host=host)
-    return (o, state_out, tail_out) if return_state else o
+    return o
 
 
 def backward(q, k, v, params: dict, grad_o, *, state_in=None, tail_in=None, grad_state=None, eps_feat=1e-6,

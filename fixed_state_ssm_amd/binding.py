@@ -199,8 +199,8 @@ def idattn_forward_varlen_workspace_size(dims: IdattnDims) -> int:
 
 def idattn_forward_varlen(dims, params, cu_seqlens, q, k, v, o, state_in=None, tail_in=None, state_out=None,
                           tail_out=None, workspace=None, workspace_bytes=0, stream=None, cu_seqlens_host=None) -> None:
-    """cu_seqlens: device int32 table (tensor or address) or None; cu_seqlens_host:
-    None or a host copy (sequence of ints), which lets the chunked algorithm run."""
+    """cu_seqlens: device int32 table (tensor or address); cu_seqlens_host:
+    None or a host copy (sequence of ints), which the library checks."""
     host = None
     if cu_seqlens_host is not None:
         vals = [int(x) for x in cu_seqlens_host]

@@ -440,27 +440,18 @@ idattn_status idattn_forward_normalized(const idattn_dims* dims, const idattn_pa
                           eta_in, eta_out);
 }
 
-// The chunked algorithm runs a packed batch one sequence at a time (B = 1
-// launches on the caller's stream); its workspace is the library's bound over
-// every sequence of at most T tokens.
+// The chunked algorithm runs a packed batch in one launch sequence whose plan
+// (segments per sequence, offsets) is built on the device from cu_seqlens;
+// its workspace depends on B, H and T only.
 bool varlen_chunked_possible(const idattn_dims& D) {
-    idattn::Problem p = problem(D);
-    p.B = 1;
-    return D.io_dtype == IDATTN_IO_BF16 && idattn::chunked_supported(p);
-}
-
-size_t varlen_chunked_bound(const idattn_dims& D) {
-    idattn::Problem p = problem(D);
-    p.B = 1;
-    p.T = p.N;
-    return idattn::chunked_workspace_bound(p);
+    return D.io_dtype == IDATTN_IO_BF16 && idattn::chunked_packed_supported(problem(D));
 }
 
 size_t varlen_workspace(const idattn_dims& D) {
     if (D.N == 0) return 0;
     size_t bytes = seq_workspace_bytes(D, D.N);
     if (D.algo != IDATTN_ALGO_SEQUENTIAL && varlen_chunked_possible(D)) {
-        const size_t c = varlen_chunked_bound(D);
+        const size_t c = idattn::chunked_packed_workspace_bytes(problem(D));
         if (c > bytes) bytes = c;
     }
     return bytes;
@@ -486,12 +477,10 @@ idattn_status idattn_forward_varlen(const idattn_dims* dims, const idattn_params
     if (st != IDATTN_OK) return st;
     const idattn_dims& D = *dims;
     if (D.N > 0x7fffffffLL) return fail(IDATTN_ERR_SHAPE, "N=%lld: a packed batch holds < 2^31 tokens", (long long)D.N);
-    // the chunked plan needs the lengths on the host; the sequential path reads the device table
-    const bool chunked = cu_seqlens_host != nullptr && D.algo != IDATTN_ALGO_SEQUENTIAL && varlen_chunked_possible(D);
+    const bool chunked = D.algo != IDATTN_ALGO_SEQUENTIAL && varlen_chunked_possible(D);
     if (D.algo == IDATTN_ALGO_CHUNKED && !chunked)
-        return fail(IDATTN_ERR_UNSUPPORTED, cu_seqlens_host ? "the chunked algorithm has no kernel for these dims"
-                                                            : "the chunked algorithm needs cu_seqlens_host");
-    if (!chunked && cu_seqlens == nullptr) return fail(IDATTN_ERR_NULL, "cu_seqlens is NULL");
+        return fail(IDATTN_ERR_UNSUPPORTED, "the chunked algorithm has no kernel for these dims");
+    if (cu_seqlens == nullptr) return fail(IDATTN_ERR_NULL, "cu_seqlens is NULL");
     if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return fail(IDATTN_ERR_ARG, "cu_seqlens must be 4-byte aligned");
     if (cu_seqlens_host != nullptr) {
         if (cu_seqlens_host[0] != 0 || cu_seqlens_host[D.B] != D.N)
@@ -519,35 +508,9 @@ idattn_status idattn_forward_varlen(const idattn_dims* dims, const idattn_params
         p.cu = cu_seqlens;
         return run_sequential(p, *params, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, s);
     }
-    // one B = 1 chunked forward per sequence, pointers offset to its rows
-    const size_t row_state = static_cast<size_t>(D.H) * D.M * 2 * D.d * 2;  // floats
-    const size_t row_tail = static_cast<size_t>(D.H) * 2 * (D.W - 1) * D.d * io;  // bytes
-    const size_t tok = static_cast<size_t>(D.H) * D.d * io;  // bytes per token
-    for (int64_t b = 0; b < D.B; ++b) {
-        const int64_t n = cu_seqlens_host[b + 1] - cu_seqlens_host[b];
-        const size_t t0 = static_cast<size_t>(cu_seqlens_host[b]) * tok;
-        const float* si = state_in ? state_in + b * row_state : nullptr;
-        float* so = state_out ? state_out + b * row_state : nullptr;
-        const void* ti = tail_in ? static_cast<const char*>(tail_in) + b * row_tail : nullptr;
-        void* to = tail_out ? static_cast<char*>(tail_out) + b * row_tail : nullptr;
-        idattn_dims one = D;
-        one.B = 1;
-        one.N = n;
-        if (n == 0) {
-            st = copy_through(one, si, ti, so, to, s);
-            if (st != IDATTN_OK) return st;
-            continue;
-        }
-        const idattn::Problem p = problem(one);
-        const size_t need_one = idattn::chunked_workspace_bytes(p);
-        if (need_one > workspace_bytes_given)
-            return fail(IDATTN_ERR_WORKSPACE, "sequence %lld needs %zu bytes of workspace, %zu given", (long long)b,
-                        need_one, workspace_bytes_given);
-        const hipError_t e = idattn::launch_forward_chunked(
-            p, *params, static_cast<const char*>(q) + t0, static_cast<const char*>(k) + t0,
-            static_cast<const char*>(v) + t0, static_cast<char*>(o) + t0, si, ti, so, to, workspace, s);
-        if (e != hipSuccess) return hip_fail(e, "chunked forward (packed batch)");
-    }
+    const hipError_t e = idattn::launch_forward_chunked_packed(problem(D), *params, cu_seqlens, q, k, v, o, state_in,
+                                                               tail_in, state_out, tail_out, workspace, s);
+    if (e != hipSuccess) return hip_fail(e, "chunked forward (packed batch)");
     return IDATTN_OK;
 }
 

@@ -66,6 +66,23 @@ constexpr int PWS = MM + 4;  // padded row length (float2) of the abar^{k+1} row
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLn2Sq = 0.4804530139182014f;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kFoldMax = 4;  // largest segment count whose carry the forward folds in
+
+// Packed batches.  With C = ceil(H sum_b c_b / 256) chunks per segment
+// (c_b chunks in sequence b), sequence b has S_b = max(1, ceil(c_b / C))
+// segments, and since ceil(c_b / C) - 1 < c_b / C:
+//   blocks       H sum_b S_b       <= 256 + B H
+//   end states   H sum_b (S_b - 1) <  256
+//   carry list   the b with S_b > kFoldMax have c_b > kFoldMax C, so there
+//                are fewer than 256 / (kFoldMax H) of them.
+__host__ __device__ constexpr int64_t plan_blocks_max(int64_t B, int64_t H) { return 256 + B * H; }
+constexpr int64_t kPlanEndStates = 256;
+__host__ __device__ constexpr int64_t carry_cap(int64_t H) { return 256 / (kFoldMax * H) + 1; }
+constexpr int kPlanHead = 4;
+__host__ __device__ constexpr int64_t plan_ints(int64_t B, int64_t H) {
+    return kPlanHead + 6 * B + 1 + carry_cap(H);
+}
+constexpr int kPlanSortMax = 256;  // batches up to this many sequences get their last segments by size
 
 template <int D>
 struct Cfg {
@@ -310,18 +327,156 @@ __device__ __forceinline__ void cpow(double dt, float lre, float lim, double n, 
     pi = e * sy;
 }
 
+constexpr int kTabThreads = 320;
+
+// Sum (or max) over the block of the tables kernel; every thread gets it.
+__device__ __forceinline__ int64_t block_reduce(int64_t v, bool mx, int64_t* red) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const int64_t o = __shfl_xor(v, off, kWave);
+        v = mx ? (o > v ? o : v) : v + o;
+    }
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = red[0];
+    for (int j = 1; j < kTabThreads / 64; ++j) v = mx ? (red[j] > v ? red[j] : v) : v + red[j];
+    __syncthreads();
+    return v;
+}
+
+// The plan of a packed batch, built by one block from the sequence table cu
+// (device int32 [B + 1]): the segment size C (see plan_blocks_max), the
+// offsets of every sequence (exclusive scans over b), the order of the last
+// segments, the carry list, and abar^{C L} of every head and mode.  A table
+// that does not rise from 0 to T gives a plan of no blocks: nothing runs and
+// no output is written.
+__device__ void packed_plan(const Problem& p, const idattn_params& prm, const int32_t* __restrict__ cu,
+                            int32_t* __restrict__ plan, uint8_t* __restrict__ tab) {
+    __shared__ int64_t red[kTabThreads / 64];
+    __shared__ int64_t scan[kTabThreads / 64][4];
+    __shared__ int32_t key[kPlanSortMax];
+    const int tid = threadIdx.x, nt = kTabThreads;
+    const int64_t B = p.B, T = p.N, H = p.H;
+    auto chunks = [&](int64_t b) -> int64_t {
+        const int64_t n = static_cast<int64_t>(cu[b + 1]) - cu[b];
+        return n > 0 ? (n + L - 1) / L : 0;
+    };
+    int64_t tc = 0, bad = 0;
+    for (int64_t b = tid; b < B; b += nt) {
+        if (cu[b + 1] < cu[b]) bad = 1;
+        tc += chunks(b);
+    }
+    if (tid == 0 && (cu[0] != 0 || cu[B] != T)) bad = 1;
+    bad = block_reduce(bad, true, red);
+    tc = block_reduce(tc, false, red);
+    if (bad) {
+        if (tid == 0) {
+            plan[0] = 1;
+            plan[1] = plan[2] = plan[3] = 0;
+        }
+        return;
+    }
+    int64_t cps = (H * tc + 255) / 256;
+    cps = cps < 1 ? 1 : cps;
+    // exclusive scans over b of c_b, S_b - 1, [S_b > kFoldMax], on contiguous
+    // runs of sequences per thread
+    const int64_t per = (B + nt - 1) / nt, b0 = tid * per < B ? tid * per : B, b1 = b0 + per < B ? b0 + per : B;
+    int64_t v[3] = {0, 0, 0};
+    for (int64_t b = b0; b < b1; ++b) {
+        const int64_t c = chunks(b), sb = c > cps ? (c + cps - 1) / cps : 1;
+        v[0] += c;
+        v[1] += sb - 1;
+        v[2] += sb > kFoldMax ? 1 : 0;
+    }
+    int64_t inc[3], tot[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        int64_t x = v[j];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int64_t y = __shfl_up(x, off, kWave);
+            if ((tid & 63) >= off) x += y;
+        }
+        inc[j] = x;
+        if ((tid & 63) == 63) scan[tid >> 6][j] = x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        tot[j] = 0;
+        for (int w = 0; w < kTabThreads / 64; ++w) {
+            if (w < (tid >> 6)) inc[j] += scan[w][j];
+            tot[j] += scan[w][j];
+        }
+    }
+    int64_t ec = inc[0] - v[0], es = inc[1] - v[1], ek = inc[2] - v[2];
+    const int64_t cap = carry_cap(H);
+    int32_t* soff = plan + kPlanHead + 4 * B;
+    int32_t* order = plan + kPlanHead + 5 * B + 1;
+    for (int64_t b = b0; b < b1; ++b) {
+        const int64_t c = chunks(b), sb = c > cps ? (c + cps - 1) / cps : 1;
+        plan[kPlanHead + b] = cu[b];
+        plan[kPlanHead + B + b] = cu[b + 1] - cu[b];
+        plan[kPlanHead + 2 * B + b] = static_cast<int32_t>(sb);
+        plan[kPlanHead + 3 * B + b] = static_cast<int32_t>(ec);
+        soff[b] = static_cast<int32_t>(es);
+        if (sb > kFoldMax) {
+            if (ek < cap) plan[kPlanHead + 6 * B + 1 + ek] = static_cast<int32_t>(b);
+            ++ek;
+        }
+        if (B <= kPlanSortMax) key[b] = static_cast<int32_t>(c - (sb - 1) * cps);  // last segment's chunks
+        ec += c;
+        es += sb - 1;
+    }
+    if (tid == 0) {
+        plan[0] = static_cast<int32_t>(cps);
+        plan[1] = static_cast<int32_t>(H * (tot[1] + B));
+        plan[2] = static_cast<int32_t>(tot[2] < cap ? tot[2] : cap);
+        plan[3] = static_cast<int32_t>(H * tot[1]);
+        soff[B] = static_cast<int32_t>(tot[1]);
+    }
+    // the order of the last segments: by size, longest first (ties by b), for
+    // batches of up to kPlanSortMax sequences; else b itself
+    __syncthreads();
+    for (int64_t b = tid; b < B; b += nt) {
+        int64_t rank = b;
+        if (B <= kPlanSortMax) {
+            rank = 0;
+            const int32_t kb = key[b];
+            for (int64_t j = 0; j < B; ++j) rank += (key[j] > kb || (key[j] == kb && j < b)) ? 1 : 0;
+        }
+        order[rank] = static_cast<int32_t>(b);
+    }
+    // abar^{C L} of every head and mode (the carry across segments)
+    for (int64_t e = tid; e < H * MM; e += nt) {
+        const int64_t h = e / MM;
+        const int m = static_cast<int>(e % MM);
+        double pr, pi;
+        cpow(exp(static_cast<double>(prm.log_dt[h])), prm.A[(h * MM + m) * 2], prm.A[(h * MM + m) * 2 + 1],
+             static_cast<double>(cps * L), pr, pi);
+        reinterpret_cast<float2*>(tab + h * kTabBytes + kTabPwSeg)[m] =
+            make_float2(static_cast<float>(pr), static_cast<float>(pi));
+    }
+}
+
 // grid (H, 17), 320 threads.  Blocks y < 16: threads 0..255 take one (k, m)
 // each and evaluate abar^k while threads 256..319 run the ZOH step of mode m
 // into shared memory, then T = bbar abar^k and abar^{k+1} = abar^k abar;
-// block y = 16: abar^Lseg (threads 0..63).  The ZOH wave of a block y < 16
-// also finds the head's scale kappa.  No
-// thread runs more than one fp64 power or ZOH step before the combine.
-constexpr int kTabThreads = 320;
+// block y = 16: abar^Lseg (threads 0..63), or for a packed batch (plan !=
+// nullptr) the plan, built by block (0, 16) alone.  The ZOH wave of a block
+// y < 16 also finds the head's scale kappa.  No thread runs more than one
+// fp64 power or ZOH step before the combine.
 __global__ __launch_bounds__(kTabThreads) void zoh_tables_kernel(Problem p, idattn_params prm, int64_t Lseg,
-                                                                 uint8_t* __restrict__ tab) {
+                                                                 uint8_t* __restrict__ tab,
+                                                                 const int32_t* __restrict__ cu,
+                                                                 int32_t* __restrict__ plan) {
     __shared__ Zoh zs[MM];
     __shared__ double kap_s;
     const int64_t h = blockIdx.x;
+    if (blockIdx.y == 16 && plan != nullptr) {
+        if (h == 0) packed_plan(p, prm, cu, plan, tab);
+        return;
+    }
     uint8_t* th = tab + h * kTabBytes;
     const int m = threadIdx.x & (MM - 1);
     const float log_dt = prm.log_dt[h];
@@ -434,6 +589,93 @@ struct WinOff {
     static constexpr uint32_t zv = D * L * 2, ft = 2 * D * L * 2, ftl = 2 * D * L * 2 + M2 * L * 2;
 };
 
+// ------------------------------------------------------------------ work of a block
+// A block runs one segment of one (b, h) sequence.  Dense batches (plan ==
+// nullptr): blockIdx = (b H + h) S + seg, sequence b at token b N of the token
+// axis, N tokens, S segments of Lseg tokens each (the last one ragged).
+// Packed batches: the plan (built on the device from the sequence table)
+// gives every sequence its first token, length and segment count S_b, all
+// segments of C chunks but each sequence's last.  Blocks 0..F-1 run the F =
+// H sum_b (S_b - 1) full segments in (b, h, seg) order; the blocks after them
+// run the last segments, in the plan's order of sequences (longest last
+// segment first, so that the blocks that do not fit in the first wave of the
+// chip are the short ones), heads innermost; blocks past the plan's total
+// are idle.  A sequence of no tokens has one block per head, which passes
+// its state and tail through.
+// Per (b, h) the z_k^T tiles of its chunks are contiguous from tile0, and
+// the end states of its segments 0..S_b-2 contiguous from st0 (in units of
+// one state).
+// Plan layout (int32): [0] C, [1] blocks, [2] sequences in the carry list,
+// [3] F, then start[B], len[B], S[B], chunk offset[B], end-state offset[B + 1]
+// (exclusive scan of S_b - 1), order[B], carry list[carry_cap(H)].
+struct Blk {
+    int64_t b, h, bh, t0, n, tile0, st0, Lseg;
+    int seg, S;
+    bool idle;
+};
+__device__ __forceinline__ Blk block_work(const Problem& p, const int32_t* plan, int S_dense, int64_t Lseg_dense) {
+    Blk k;
+    const int64_t x = blockIdx.x;
+    if (plan == nullptr) {
+        k.bh = x / S_dense;
+        k.seg = static_cast<int>(x % S_dense);
+        k.S = S_dense;
+        k.b = k.bh / p.H;
+        k.h = k.bh % p.H;
+        k.t0 = k.b * p.N;
+        k.n = p.N;
+        k.Lseg = Lseg_dense;
+        k.tile0 = k.bh * S_dense * (Lseg_dense / L);
+        k.st0 = k.bh * (S_dense - 1);
+        k.idle = false;
+        return k;
+    }
+    const int64_t B = p.B, H = p.H, F = plan[3];
+    const int32_t* soff = plan + kPlanHead + 4 * B;
+    k.idle = x >= plan[1];
+    if (k.idle) return k;
+    if (x < F) {
+        int64_t lo = 0, hi = B - 1;  // the last b with H soff[b] <= x: it has a full segment x
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) >> 1;
+            if (H * soff[mid] <= x) lo = mid;
+            else hi = mid - 1;
+        }
+        k.b = lo;
+        k.S = plan[kPlanHead + 2 * B + lo];
+        const int64_t local = x - H * soff[lo];
+        k.h = local / (k.S - 1);
+        k.seg = static_cast<int>(local % (k.S - 1));
+    } else {
+        const int64_t r = x - F;
+        k.b = plan[kPlanHead + 5 * B + 1 + r / H];
+        k.h = r % H;
+        k.S = plan[kPlanHead + 2 * B + k.b];
+        k.seg = k.S - 1;
+    }
+    k.bh = k.b * H + k.h;
+    k.t0 = plan[kPlanHead + k.b];
+    k.n = plan[kPlanHead + B + k.b];
+    k.Lseg = static_cast<int64_t>(plan[0]) * L;
+    const int64_t cb = (k.n + L - 1) / L;  // chunks of the sequence
+    k.tile0 = H * static_cast<int64_t>(plan[kPlanHead + 3 * B + k.b]) + k.h * cb;
+    k.st0 = H * static_cast<int64_t>(soff[k.b]) + k.h * (k.S - 1);
+    return k;
+}
+
+// A sequence of no tokens: state_out = state_in (or zeros) and tail_out =
+// tail_in (or zeros) for this (b, h), by the whole block (each thread reads
+// and writes the same elements, so in place is safe).
+template <int D>
+__device__ __forceinline__ void copy_through_block(const Problem& p, const Blk& k, const float* state_in,
+                                                   float* state_out, const uint16_t* tail_in, uint16_t* tail_out) {
+    const int64_t sn = MM * 2 * D * 2, tn = 2 * (p.W - 1) * D;
+    if (state_out != nullptr)
+        for (int64_t e = threadIdx.x; e < sn; e += NTH) state_out[k.bh * sn + e] = state_in ? state_in[k.bh * sn + e] : 0.f;
+    if (tail_out != nullptr)
+        for (int64_t e = threadIdx.x; e < tn; e += NTH) tail_out[k.bh * tn + e] = tail_in ? tail_in[k.bh * tn + e] : 0;
+}
+
 // ------------------------------------------------------------------ features
 // Within a role (512 threads), feature thread fi < NF owns channels 2 cgi and
 // 2 cgi + 1 (cgi = fi % CP) of tokens 8 tb .. 8 tb + 7 (tb = fi / CP) of a
@@ -447,14 +689,14 @@ __device__ __forceinline__ int feat_index() {
     return (tid_now() & 511) ^ (Cfg<D>::NF < 512 ? 256 : 0);
 }
 
-// Buffer resources over one (b, h) sequence up to the end of the segment:
-// token t, channel c sits at byte 2 (t H D + c) from the sequence's first
-// token.  Offsets are whole VGPR operands, which the hardware range-checks;
+// Buffer resources over one (b, h) sequence (first token t0 on the token
+// axis) up to the end of the segment: token t, channel c sits at byte
+// 2 (t H D + c) from the sequence's first token.  Offsets are whole VGPR operands, which the hardware range-checks;
 // loads past the end of a resource return zeros.
 template <int D>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const uint16_t* x, int64_t b, int64_t h, int64_t N,
-                                                           int64_t H, int64_t t_end) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x + b * N * H * D + h * D), 0,
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const uint16_t* x, int64_t t0, int64_t h, int64_t H,
+                                                           int64_t t_end) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x + (t0 * H + h) * D), 0,
                                              static_cast<int>(t_end * H * D * 2), 0x00020000);
 }
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
@@ -819,7 +1061,6 @@ __device__ __forceinline__ void g_store_lane(const f4 (&G)[8], float* dst, int v
 // past seg) before any is combined, so that the loads overlap; the combine of
 // a j >= seg is discarded.  U: the real and imaginary rows of a mode sit in
 // lanes i, i ^ 1; Gamma: in elements 2q, 2q + 1 of a lane.
-constexpr int kFoldMax = 4;  // largest segment count folded into the forward
 template <int D, int TG>
 __device__ __forceinline__ void u_fold(f4 (&U)[Cfg<D>::RT], const float* e0, int64_t estride, int seg,
                                        const float2* aseg, int kw) {
@@ -1017,17 +1258,29 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
                                                             const float* __restrict__ state_in,
                                                             const uint8_t* __restrict__ tab, float* __restrict__ c0,
                                                             float* __restrict__ ws, _Float16* __restrict__ zt,
-                                                            int64_t Lseg, int S, const float* eta_in, float* eta_out,
-                                                            float2* __restrict__ c0eta) {
+                                                            int64_t Lseg_dense, int S_dense, const float* eta_in,
+                                                            float* eta_out, float2* __restrict__ c0eta,
+                                                            const int32_t* __restrict__ plan) {
     __shared__ SmemSeg<D> sm;
+    const Blk wk = block_work(p, plan, S_dense, Lseg_dense);
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (wk.idle) return;
+    if (wk.n == 0) {  // no tokens: eta passes through (the forward copies state and tail)
+        if (p.eta && eta_out != nullptr && tid < MM) {
+            const int64_t e = (wk.bh * MM + tid) * 2;
+            const float r = eta_in ? eta_in[e] : 0.f, i = eta_in ? eta_in[e + 1] : 0.f;
+            eta_out[e] = r;
+            eta_out[e + 1] = i;
+        }
+        return;
+    }
     const bool key = w < 8;
-    const int64_t bh = blockIdx.x / S;
-    const int seg = static_cast<int>(blockIdx.x % S);
+    const int64_t bh = wk.bh, b = wk.b, h = wk.h;
+    const int seg = wk.seg, S = wk.S;
+    const int64_t Lseg = wk.Lseg;
     const bool upd = seg + 1 < S;  // this segment's end state is needed
-    const int64_t b = bh / p.H, h = bh % p.H;
     const int64_t t_begin = seg * Lseg;
-    const int64_t t_end = t_begin + Lseg < p.N ? t_begin + Lseg : p.N;
+    const int64_t t_end = t_begin + Lseg < wk.n ? t_begin + Lseg : wk.n;
     const int nch = static_cast<int>((t_end - t_begin + L - 1) / L);
     const int n_last = static_cast<int>(t_end - t_begin - static_cast<int64_t>(nch - 1) * L);
     const uint8_t* th = tab + h * kTabBytes;
@@ -1036,10 +1289,10 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
     copy16(sm.ftl, th + kTabFTL, M2 * L * 2);
     if (tid < MM) sm.aL[tid] = reinterpret_cast<const float2*>(th + kTabPw)[(L - 1) * MM + tid];
     __syncthreads();
-    float* dst = ws + (static_cast<int64_t>(seg) * p.B * p.H + bh) * MM * 2 * D * 2;
+    float* dst = ws + (wk.st0 + seg) * MM * 2 * D * 2;  // this segment's end state (when upd)
     const int rsb = static_cast<int>(p.H * D * 2);  // token stride, bytes
     // z_k^T tile of chunk c of this segment (the forward builds z_v itself)
-    _Float16* zseg = zt + ((bh * S + seg) * (Lseg / L)) * D * L;
+    _Float16* zseg = zt + (wk.tile0 + seg * (Lseg / L)) * D * L;
     // The state entering the sequence, times the table scale kappa, staged in
     // lane order for the forward (and the carry chain), which read only this
     // copy: state_in is read here, in a kernel that completes before any block
@@ -1056,8 +1309,8 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
         if (eta_out != nullptr) {
             const double4 z = reinterpret_cast<const double4*>(th + kTabDz)[m];  // abar, bbar
             double ar, ai, gr, gi;
-            cpow_int(z.x, z.y, p.N, ar, ai);
-            geo_from_pow(z.x, z.y, z.z, z.w, ar, ai, static_cast<double>(p.N), gr, gi);
+            cpow_int(z.x, z.y, wk.n, ar, ai);
+            geo_from_pow(z.x, z.y, z.z, z.w, ar, ai, static_cast<double>(wk.n), gr, gi);
             eta_out[(bh * MM + m) * 2] = static_cast<float>(ar * ein_r - ai * ein_i + gr);
             eta_out[(bh * MM + m) * 2 + 1] = static_cast<float>(ar * ein_i + ai * ein_r + gi);
         }
@@ -1072,7 +1325,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
             u_store_lane<D>(U, cst, kw);
         }
         u_load<D>(U, nullptr, kw, 1.f);
-        const __amdgpu_buffer_rsrc_t rk = seq_rsrc<D>(k, b, h, p.N, p.H, t_end);
+        const __amdgpu_buffer_rsrc_t rk = seq_rsrc<D>(k, wk.t0, h, p.H, t_end);
         uint32_t rkk[11];
         fm_load<D, true>(rkk, rk, rsb, t_begin);
         halo_fix<D>(rkk, sm, 1, t_begin);
@@ -1104,7 +1357,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
         }
         if (own) g_load<D>(G, nullptr, vw, 1.f);
         // the values' features are needed here only for the end state (upd)
-        const __amdgpu_buffer_rsrc_t rv = seq_rsrc<D>(v, b, h, p.N, p.H, t_end);
+        const __amdgpu_buffer_rsrc_t rv = seq_rsrc<D>(v, wk.t0, h, p.H, t_end);
         uint32_t rvv[8];
         if (upd) {
             fm_load<D, false>(rvv, rv, rsb, t_begin);
@@ -1139,37 +1392,54 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
 // states of up to eight segments are loaded before any of them is combined,
 // so that the loads overlap instead of forming a chain of dependent round
 // trips.  The state entering the sequence comes from the staged copy c0.
+// Dense batches: every (b, h) of S segments.  Packed batches: the (b, h) of
+// the sequences in the plan's carry list (those with more segments than the
+// forward folds), S_b segments each; threads beyond them exit.
 __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, bool has_state,
                                                             const float* __restrict__ c0,
                                                             const uint8_t* __restrict__ tab,
-                                                            float* __restrict__ ws, int S) {
+                                                            float* __restrict__ ws, int S_dense,
+                                                            const int32_t* __restrict__ plan) {
     constexpr int kBatch = 8;
     const int D = static_cast<int>(p.d);
     const int64_t per = 128 * D;  // threads per (b, h)
     const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (e >= p.B * p.H * per) return;
-    const int64_t bh = e / per, h = bh % p.H;
+    int64_t bh, st0;
+    int S;
+    if (plan == nullptr) {
+        if (e >= p.B * p.H * per) return;
+        bh = e / per;
+        S = S_dense;
+        st0 = bh * (S - 1);
+    } else {
+        const int64_t j = e / per;  // pair of the carry list
+        if (j >= static_cast<int64_t>(plan[2]) * p.H) return;
+        const int64_t B = p.B;
+        const int64_t b = plan[kPlanHead + 6 * B + 1 + j / p.H], hh = j % p.H;  // the carry list
+        bh = b * p.H + hh;
+        S = plan[kPlanHead + 2 * B + b];
+        st0 = p.H * static_cast<int64_t>(plan[kPlanHead + 4 * B + b]) + hh * (S - 1);
+    }
+    const int64_t h = bh % p.H;
     const int o = static_cast<int>((e % per) >> 2) * 8;  // float offset of the group of eight
     const int k = static_cast<int>(e & 3);
     int mode, pre, pim;  // mode, positions of re / im in the eight floats
     if (o < 128 * D) {        // U: [kw][rt][lane][jj], re in lane i, im in lane i + 1
-        const int kw = o / (16 * D), rem = o % (16 * D), rt = rem / 256, ln = (rem % 256) / 4;
-        const int g = ln >> 4, i = ln & 15;
-        mode = 8 * kw + i / 2;
+        const int kw = o / (16 * D), ln = (o % 256) / 4;  // (16 D is a multiple of 256)
+        mode = 8 * kw + (ln & 15) / 2;
         pre = k;
         pim = 4 + k;
     } else {  // Gamma: [vw][mt][lane][jj], (re, im) of modes m0, m0 + 1 in jj, channel 16 vw + i of the lane
-        const int o2 = o - 128 * D, vw = o2 / 2048, mt = (o2 % 2048) / 256, ln = (o2 % 256) / 4;
-        const int g = ln >> 4, i = ln & 15;
-        mode = 8 * mt + 2 * g + (k & 1);
+        const int o2 = o - 128 * D, mt = (o2 % 2048) / 256, ln = (o2 % 256) / 4;
+        mode = 8 * mt + 2 * (ln >> 4) + (k & 1);
         pre = 2 * k;
         pim = 2 * k + 1;
     }
     const float2 a = reinterpret_cast<const float2*>(tab + h * kTabBytes + kTabPwSeg)[mode];
     // the staged state_in (lane order, already times kappa) or zero
     float2 c = has_state ? make_float2(c0[bh * 256 * D + o + pre], c0[bh * 256 * D + o + pim]) : make_float2(0.f, 0.f);
-    const int64_t sst = p.B * p.H * 256 * D;  // floats per segment
-    float* base = ws + bh * 256 * D + o;
+    const int64_t sst = 256 * D;  // floats per state
+    float* base = ws + st0 * sst + o;
     for (int s0 = 0; s0 + 1 < S; s0 += kBatch) {
         const int n = S - 1 - s0 < kBatch ? S - 1 - s0 : kBatch;
         float2 loc[kBatch];
@@ -1253,19 +1523,25 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                                                               float* state_out, uint16_t* tail_out,
                                                               const uint8_t* __restrict__ tab,
                                                               const float* __restrict__ c0,
-                                                              const float* __restrict__ carry, int64_t Lseg, int S,
-                                                              int fold, const float2* __restrict__ c0eta,
-                                                              bool has_eta) {
+                                                              const float* __restrict__ carry, int64_t Lseg_dense,
+                                                              int S_dense, const float2* __restrict__ c0eta,
+                                                              bool has_eta, const int32_t* __restrict__ plan) {
     constexpr int RT = Cfg<D>::RT, KB = Cfg<D>::KB, YR = Cfg<D>::YR;
     constexpr uint32_t dl = WinOff<D>::ftl - WinOff<D>::ft;
     __shared__ SmemFwd<D> sm;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool key = w < 8;
-    const int64_t bh = blockIdx.x / S;
-    const int seg = static_cast<int>(blockIdx.x % S);
-    const int64_t b = bh / p.H, h = bh % p.H;
-    const int64_t N = p.N, H = p.H;
+    const Blk wk = block_work(p, plan, S_dense, Lseg_dense);
+    if (wk.idle) return;
+    if (wk.n == 0) {
+        copy_through_block<D>(p, wk, state_in, state_out, tail_in, tail_out);
+        return;
+    }
+    const int64_t bh = wk.bh, b = wk.b, h = wk.h;
+    const int seg = wk.seg, S = wk.S;
+    const int64_t Lseg = wk.Lseg;
+    const int64_t N = wk.n, H = p.H;  // N: tokens of this sequence
     const int64_t t_begin = seg * Lseg;
     const int64_t t_end = t_begin + Lseg < N ? t_begin + Lseg : N;
     const int nch = static_cast<int>((t_end - t_begin + L - 1) / L);
@@ -1316,14 +1592,15 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
     // state_out into the same buffer whatever the order in which blocks run.
     const int64_t sstride = MM * 2 * D * 2;  // floats per (b, h) state
     const float* sin = state_in ? c0 + bh * sstride : nullptr;
-    const float* src = carry + (static_cast<int64_t>(seg > 0 ? seg - 1 : 0) * p.B * p.H + bh) * sstride;
-    const float* e0 = carry + bh * sstride;
-    const int64_t estride = p.B * p.H * sstride;
+    const float* src = carry + (wk.st0 + (seg > 0 ? seg - 1 : 0)) * sstride;
+    const float* e0 = carry + wk.st0 * sstride;
+    const int64_t estride = sstride;
+    const bool fold = S <= kFoldMax;  // else the carry kernel has run
     const int nfold = fold ? seg : 0;
     constexpr int kFoldTiles = D == 128 ? 4 : 2;  // tiles per round trip of the fold (register bound)
     const float2* aseg = reinterpret_cast<const float2*>(th + kTabPwSeg);
     constexpr int64_t tile2 = D * L;  // halfs per chunk: z_k^T
-    const _Float16* zseg = zt + (bh * S + seg) * (Lseg / L) * tile2;
+    const _Float16* zseg = zt + (wk.tile0 + seg * (Lseg / L)) * tile2;
     __syncthreads();
 
     if (key) {
@@ -1341,7 +1618,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             else u_load<D>(U, nullptr, kw, 1.f);
             if (nfold > 0) u_fold<D, kFoldTiles>(U, e0, estride, nfold, aseg, kw);
         }
-        const __amdgpu_buffer_rsrc_t rq = seq_rsrc<D>(q, b, h, N, H, t_end);
+        const __amdgpu_buffer_rsrc_t rq = seq_rsrc<D>(q, wk.t0, h, H, t_end);
         uint32_t rqq[11];  // raw queries of the chunk after the next
         fm_load<D, true>(rqq, rq, rsb, t_begin);
         halo_fix<D>(rqq, sm, 0, t_begin);
@@ -1524,8 +1801,8 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                 if (nfold > 0) g_fold<D, kFoldTiles>(G, e0, estride, nfold, aseg, vw);
             }
         }
-        const __amdgpu_buffer_rsrc_t ob = seq_rsrc<D>(o, b, h, N, H, t_end);
-        const __amdgpu_buffer_rsrc_t rv = seq_rsrc<D>(v, b, h, N, H, t_end);
+        const __amdgpu_buffer_rsrc_t ob = seq_rsrc<D>(o, wk.t0, h, H, t_end);
+        const __amdgpu_buffer_rsrc_t rv = seq_rsrc<D>(v, wk.t0, h, H, t_end);
         uint32_t rvv[8];        // raw v of the next chunk to enter
         u4 kr[kTilePieces<D>];  // z_k^T of the chunk after it
         tile_load<D>(kr, zseg);
@@ -1625,7 +1902,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             const int sel = e / (Wm1 * D), t = (e / D) % Wm1, c = e % D;
             const int64_t pos = N - Wm1 + t;
             tail_out[bh * E + e] = pos < 0 ? sm.halo[sel][3 + pos][c]
-                                           : (sel == 0 ? q : k)[((b * N + pos) * H + h) * D + c];
+                                           : (sel == 0 ? q : k)[((wk.t0 + pos) * H + h) * D + c];
         }
     }
 }
@@ -1642,67 +1919,99 @@ void plan_segments(const Problem& p, int& S, int64_t& Lseg) {
     if (S < 1) S = 1;
 }
 
-// Workspace: per-head tables | the staged kappa state_in, [B H] states in lane
-// order | the staged eta_in, [B H][M] complex | segment end states, [S-1][B H]
-// | fp16 key-feature tiles, one z_k^T per chunk slot of every segment.
+// Workspace: the packed plan (packed batches only) | per-head tables | the
+// staged kappa state_in, [B H] states in lane order | the staged eta_in,
+// [B H][M] complex | segment end states, S_b - 1 per (b, h) | fp16 key-feature
+// tiles, one z_k^T per chunk slot.
 struct WsLayout {
-    size_t tab, c0, c0eta, seg, zt, total;
+    size_t plan, tab, c0, c0eta, seg, zt, total;
 };
-WsLayout ws_layout(const Problem& p, int S, int64_t Lseg) {
+WsLayout ws_layout_parts(const Problem& p, size_t plan_bytes, size_t end_states, size_t chunk_slots) {
     const size_t state = static_cast<size_t>(MM) * 2 * p.d * 2 * sizeof(float);
     const size_t pairs = static_cast<size_t>(p.B * p.H);
     WsLayout w;
-    w.tab = 0;
-    w.c0 = static_cast<size_t>(p.H) * kTabBytes;
+    w.plan = 0;
+    w.tab = ((plan_bytes + 255) / 256) * 256;
+    w.c0 = w.tab + static_cast<size_t>(p.H) * kTabBytes;
     w.c0eta = w.c0 + pairs * state;
     w.seg = w.c0eta + ((pairs * MM * 8 + 255) / 256) * 256;
-    w.zt = w.seg + static_cast<size_t>(S - 1) * pairs * state;
-    w.total = w.zt + pairs * S * static_cast<size_t>(Lseg) * p.d * sizeof(_Float16);
+    w.zt = w.seg + end_states * state;
+    w.total = w.zt + chunk_slots * L * p.d * sizeof(_Float16);
     return w;
 }
+// Dense: S segments of Lseg tokens per (b, h).
+WsLayout ws_layout(const Problem& p, int S, int64_t Lseg) {
+    const size_t pairs = static_cast<size_t>(p.B * p.H);
+    return ws_layout_parts(p, 0, static_cast<size_t>(S - 1) * pairs, pairs * S * static_cast<size_t>(Lseg / L));
+}
+// Packed (B sequences on p.N = T tokens): the plan's bounds on the end
+// states (plan_blocks_max); the chunks, ceil(n_b / L) each, number at most
+// min(T, (T + B (L - 1)) / L) per head.
+WsLayout ws_layout_packed(const Problem& p) {
+    int64_t chunks = (p.N + p.B * (L - 1)) / L;
+    chunks = chunks < p.N ? chunks : p.N;
+    return ws_layout_parts(p, static_cast<size_t>(plan_ints(p.B, p.H)) * 4, static_cast<size_t>(kPlanEndStates),
+                           static_cast<size_t>(p.H * chunks));
+}
 
+// Dense (cu == nullptr): B sequences of N tokens, segments planned here.
+// Packed (cu != nullptr, device table of p.B + 1 entries on p.N = T tokens):
+// the plan is built on the device and the grids cover its largest size.
 template <int D>
 hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, const void* k, const void* v, void* o,
                   const float* state_in, const void* tail_in, float* state_out, void* tail_out, void* workspace,
-                  hipStream_t stream, const float* eta_in, float* eta_out) {
-    int S;
-    int64_t Lseg;
-    plan_segments(p, S, Lseg);
-    const WsLayout lay = ws_layout(p, S, Lseg);
+                  hipStream_t stream, const float* eta_in, float* eta_out, const int32_t* cu) {
+    const bool packed = cu != nullptr;
+    int S = 1;
+    int64_t Lseg = L;
+    const int64_t pairs = p.B * p.H;
+    int64_t grid;
+    WsLayout lay;
+    if (packed) {
+        lay = ws_layout_packed(p);
+        grid = plan_blocks_max(p.B, p.H);
+    } else {
+        plan_segments(p, S, Lseg);
+        lay = ws_layout(p, S, Lseg);
+        grid = pairs * S;
+    }
     const auto* q16 = static_cast<const uint16_t*>(q);
     const auto* k16 = static_cast<const uint16_t*>(k);
     const auto* v16 = static_cast<const uint16_t*>(v);
     const auto* t16 = static_cast<const uint16_t*>(tail_in);
     uint8_t* base = static_cast<uint8_t*>(workspace);
+    int32_t* plan = packed ? reinterpret_cast<int32_t*>(base + lay.plan) : nullptr;
     uint8_t* tab = base + lay.tab;
     float* c0 = reinterpret_cast<float*>(base + lay.c0);
     float2* c0eta = reinterpret_cast<float2*>(base + lay.c0eta);
     float* ws = reinterpret_cast<float*>(base + lay.seg);
     _Float16* zt = reinterpret_cast<_Float16*>(base + lay.zt);
-    const int64_t pairs = p.B * p.H;
-    zoh_tables_kernel<<<dim3(static_cast<unsigned>(p.H), 17), kTabThreads, 0, stream>>>(p, prm, Lseg, tab);
+    zoh_tables_kernel<<<dim3(static_cast<unsigned>(p.H), 17), kTabThreads, 0, stream>>>(p, prm, Lseg, tab, cu, plan);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    segment_state_kernel<D><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(
-        p, prm, k16, v16, t16, state_in, tab, c0, ws, zt, Lseg, S, eta_in, eta_out, c0eta);
+    segment_state_kernel<D><<<dim3(static_cast<unsigned>(grid)), NTH, 0, stream>>>(
+        p, prm, k16, v16, t16, state_in, tab, c0, ws, zt, Lseg, S, eta_in, eta_out, c0eta, plan);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int fold = S <= kFoldMax ? 1 : 0;
-    if (S > 1 && !fold) {
-        const int64_t threads = pairs * 128 * p.d;  // one complex element each
+    // the carry kernel: dense with more segments than the forward folds; packed
+    // when some sequence may have that many (its list says which)
+    const int64_t carry_pairs = packed ? (p.N / L >= kFoldMax ? carry_cap(p.H) * p.H : 0)
+                                       : (S > kFoldMax ? pairs : 0);
+    if (carry_pairs > 0) {
+        const int64_t threads = carry_pairs * 128 * p.d;  // one complex element each
         segment_carry_kernel<<<dim3(static_cast<unsigned>((threads + 255) / 256)), 256, 0, stream>>>(
-            p, state_in != nullptr, c0, tab, ws, S);
+            p, state_in != nullptr, c0, tab, ws, S, plan);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (p.eta)
-        chunked_forward_kernel<D, true><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(
+        chunked_forward_kernel<D, true><<<dim3(static_cast<unsigned>(grid)), NTH, 0, stream>>>(
             p, prm, q16, k16, v16, zt, static_cast<uint16_t*>(o), state_in, t16, state_out,
-            static_cast<uint16_t*>(tail_out), tab, c0, ws, Lseg, S, fold, c0eta, eta_in != nullptr);
+            static_cast<uint16_t*>(tail_out), tab, c0, ws, Lseg, S, c0eta, eta_in != nullptr, plan);
     else
-        chunked_forward_kernel<D, false><<<dim3(static_cast<unsigned>(pairs * S)), NTH, 0, stream>>>(
+        chunked_forward_kernel<D, false><<<dim3(static_cast<unsigned>(grid)), NTH, 0, stream>>>(
             p, prm, q16, k16, v16, zt, static_cast<uint16_t*>(o), state_in, t16, state_out,
-            static_cast<uint16_t*>(tail_out), tab, c0, ws, Lseg, S, fold, c0eta, false);
+            static_cast<uint16_t*>(tail_out), tab, c0, ws, Lseg, S, c0eta, false, plan);
     return hipGetLastError();
 }
 
@@ -1724,20 +2033,12 @@ size_t chunked_workspace_bytes(const Problem& p) {
     return cws::ws_layout(p, S, Lseg).total;
 }
 
-size_t chunked_workspace_bound(const Problem& p) {
-    // For one sequence (B = 1) of any n <= p.N tokens.  The plan gives
-    // s = min(smax, chunks) segments of cps = ceil(chunks / s) chunks; S cps <
-    // chunks + cps, and cps <= ceil(chunks / 2) once s >= 2 (S cps = chunks when
-    // s = 1), so the tiles cover at most chunks + ceil(chunks / 2) chunk slots
-    // and the end states at most smax - 1 segments: every term grows with N.
-    const size_t state = static_cast<size_t>(cws::MM) * 2 * p.d * 2 * sizeof(float);
-    const int64_t smax = p.H >= 256 ? 1 : 256 / p.H;
-    const int64_t chunks = (p.N + cws::L - 1) / cws::L;
-    const size_t slots = static_cast<size_t>(chunks + (chunks + 1) / 2);
-    return static_cast<size_t>(p.H) * cws::kTabBytes + static_cast<size_t>(p.H) * state +
-           ((static_cast<size_t>(p.H) * cws::MM * 8 + 255) / 256) * 256 +
-           static_cast<size_t>(smax - 1) * p.H * state + static_cast<size_t>(p.H) * slots * cws::L * p.d * 2;
+bool chunked_packed_supported(const Problem& p) {
+    // the plan's int32 entries: block counts up to 256 + B H and token offsets up to T
+    return chunked_supported(p) && p.B * p.H <= (int64_t{1} << 22) && p.N < (int64_t{1} << 31);
 }
+
+size_t chunked_packed_workspace_bytes(const Problem& p) { return cws::ws_layout_packed(p).total; }
 
 hipError_t launch_forward_chunked(const Problem& p, const idattn_params& prm, const void* q, const void* k,
                                   const void* v, void* o, const float* state_in, const void* tail_in,
@@ -1745,9 +2046,20 @@ hipError_t launch_forward_chunked(const Problem& p, const idattn_params& prm, co
                                   const float* eta_in, float* eta_out) {
     if (p.d == 128)
         return cws::launch<128>(p, prm, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, stream, eta_in,
-                                eta_out);
+                                eta_out, nullptr);
     return cws::launch<64>(p, prm, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, stream, eta_in,
-                           eta_out);
+                           eta_out, nullptr);
+}
+
+hipError_t launch_forward_chunked_packed(const Problem& p, const idattn_params& prm, const int32_t* cu_seqlens,
+                                         const void* q, const void* k, const void* v, void* o, const float* state_in,
+                                         const void* tail_in, float* state_out, void* tail_out, void* workspace,
+                                         hipStream_t stream) {
+    if (p.d == 128)
+        return cws::launch<128>(p, prm, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, stream,
+                                nullptr, nullptr, cu_seqlens);
+    return cws::launch<64>(p, prm, q, k, v, o, state_in, tail_in, state_out, tail_out, workspace, stream, nullptr,
+                           nullptr, cu_seqlens);
 }
 
 }  // namespace idattn

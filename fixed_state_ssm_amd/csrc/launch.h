@@ -46,10 +46,12 @@ hipError_t launch_ssm_value_scan_readout_seq(const Problem& p, const idattn_para
 // ---- chunked MFMA path (bf16 I/O; wave-specialised kernels for d = R in
 // {64, 128}, M = 64, W <= 4, the SiLU feature maps)
 size_t chunked_workspace_bytes(const Problem& p);
-// A bound on chunked_workspace_bytes over every B = 1 sequence of at most p.N
-// tokens (monotone in p.N).
-size_t chunked_workspace_bound(const Problem& p);
 bool chunked_supported(const Problem& p);
+// Packed batch in one launch sequence: p.B sequences on p.N = T tokens, the
+// plan built on the device from cu_seqlens (device int32 [B + 1]).  The
+// workspace depends on B, H and T only (monotone in T).
+bool chunked_packed_supported(const Problem& p);
+size_t chunked_packed_workspace_bytes(const Problem& p);
 // Also writes tail_out (when not NULL) like launch_tail_update.  With p.eta the
 // readout is the normalised one, eta_in / eta_out the normaliser ([B][H][M]
 // complex; NULL = zeros / no output; eta_out may equal eta_in).
@@ -58,6 +60,10 @@ hipError_t launch_forward_chunked(const Problem& p, const idattn_params& prm,
                                   const float* state_in, const void* tail_in,
                                   float* state_out, void* tail_out, void* workspace, hipStream_t stream,
                                   const float* eta_in = nullptr, float* eta_out = nullptr);
+hipError_t launch_forward_chunked_packed(const Problem& p, const idattn_params& prm, const int32_t* cu_seqlens,
+                                         const void* q, const void* k, const void* v, void* o,
+                                         const float* state_in, const void* tail_in, float* state_out,
+                                         void* tail_out, void* workspace, hipStream_t stream);
 
 // ---- backward (sequential fp32; dense batches, SiLU feature maps)
 size_t backward_workspace_bytes(const Problem& p);

@@ -221,28 +221,33 @@ idattn_status idattn_forward_normalized(const idattn_dims *dims, const idattn_pa
  * prompts of mixed lengths one call.  Same result, sequence by sequence, as
  * idattn_forward with B = 1 on that sequence's tokens.
  *
- *  cu_seqlens      in  device int32 [B + 1], 4-byte aligned: sequence b is
- *                      tokens cu_seqlens[b] .. cu_seqlens[b+1]-1; it must rise
- *                      from 0 to T (zero-length sequences allowed).  Not
- *                      checked (device memory): the kernels clamp every bound
- *                      into [0, T], so a malformed table gives wrong results
- *                      but no access out of bounds.  Needed by the
- *                      sequential algorithm; may be NULL when the chunked one
- *                      runs.
- *  cu_seqlens_host in  NULL or the same table in host memory (checked: it must
- *                      rise from 0 to T, else IDATTN_ERR_SHAPE).  With it,
- *                      AUTO and CHUNKED run the chunked algorithm where it
- *                      has a kernel (bf16, d in {64, 128}, M = 64, W <= 4, not
- *                      the RFF map), one sequence after another on the stream.
+ *  cu_seqlens      in  device int32 [B + 1], 4-byte aligned, non-NULL:
+ *                      sequence b is tokens cu_seqlens[b] .. cu_seqlens[b+1]-1;
+ *                      it must rise from 0 to T (zero-length sequences
+ *                      allowed).  Not checked on the host (device memory):
+ *                      the sequential kernels clamp every bound into [0, T],
+ *                      and the chunked path checks the table on the device
+ *                      and runs nothing for a malformed one (outputs left
+ *                      unwritten); either way a malformed table gives wrong
+ *                      results but no access out of bounds.
+ *  cu_seqlens_host in  NULL or the same table in host memory, checked (it must
+ *                      rise from 0 to T, else IDATTN_ERR_SHAPE); the
+ *                      algorithms do not need it.
+ *  AUTO and CHUNKED run the chunked algorithm where it has a kernel (bf16,
+ *  d in {64, 128}, M = 64, W <= 4, not the RFF map, B H <= 2^22): one launch
+ *  sequence for the whole batch, whose plan (segments per sequence, chosen
+ *  so that the segments spread over the compute units) is built on the
+ *  device from cu_seqlens, so the call never waits on the device.
  *  q, k, v    in   [T][H][d] io dtype
  *  o          out  [T][H][d] io dtype
  *  state_in, tail_in, state_out, tail_out  as for idattn_forward, with B
  *                  sequences ([B][H][M][2d][2] and [B][H][2][W-1][d])
  *  workspace       at least idattn_forward_varlen_workspace_size bytes (enough
  *                  for either algorithm unless dims->algo is SEQUENTIAL)
- * T < 2^31.  CHUNKED without cu_seqlens_host, or without a kernel, returns
- * IDATTN_ERR_UNSUPPORTED.  Overlap rules as for idattn_forward; cu_seqlens
- * must not overlap any output.
+ * T < 2^31.  CHUNKED without a kernel for these dims returns
+ * IDATTN_ERR_UNSUPPORTED.  The workspace size depends on B, H and T only.
+ * Overlap rules as for idattn_forward; cu_seqlens must not overlap any
+ * output.
  */
 idattn_status idattn_forward_varlen_workspace_size(const idattn_dims *dims, size_t *bytes);
 

@@ -255,9 +255,10 @@ def test_varlen_validation():
     expect(call_varlen(dims(B=5, N=1000, feature_norm="rff"), params(rff_omega=0), cu), "IDATTN_ERR_NULL")
 
 
-def test_varlen_host_lengths_validation():
-    """With a host copy of the lengths the chunked plan becomes possible; the
-    copy is checked on the host, and CHUNKED without it is refused."""
+def test_varlen_chunked_validation():
+    """Shapes with a chunked kernel run the packed batch chunked (its plan is
+    built on the device, so the device table is required and a host copy is
+    optional); a host copy, when given, is checked on the host."""
     d = dims(B=3, N=1000, M=64, d=128)
     cu = 10 * QB
     p = params()
@@ -267,11 +268,12 @@ def test_varlen_host_lengths_validation():
     assert fs.idattn_forward_varlen_workspace_size(d) == max(chunked, seq)
     for bad in ((1, 10, 10, 1000), (0, 10, 5, 1000), (0, 10, 10, 999)):
         expect(call_varlen(d, p, cu, host=(ctypes.c_int32 * 4)(*bad)), "IDATTN_ERR_SHAPE")
-    expect(call_varlen(dims(B=3, N=1000, M=64, d=128, algo="chunked"), p, cu, ws_bytes=1 << 40),
-           "IDATTN_ERR_UNSUPPORTED")                                        # no host lengths
+    dc = dims(B=3, N=1000, M=64, d=128, algo="chunked")
+    expect(call_varlen(dc, p, cu, ws_bytes=chunked - 1), "IDATTN_ERR_WORKSPACE")          # no host copy needed
+    expect(call_varlen(dc, p, cu, ws_bytes=chunked - 1, host=ok), "IDATTN_ERR_WORKSPACE")
     expect(call_varlen(dims(B=3, N=1000, M=32, d=128, algo="chunked"), p, cu, ws_bytes=1 << 40, host=ok),
            "IDATTN_ERR_UNSUPPORTED")                                        # no kernel for M = 32
-    expect(call_varlen(d, p, None, host=ok, ws_bytes=1), "IDATTN_ERR_WORKSPACE")  # device table optional here
+    expect(call_varlen(d, p, None, host=ok, ws_bytes=1 << 40), "IDATTN_ERR_NULL")  # the device table is required
 
 
 def call_normalized(d, p, ws_bytes=None, ei=11 * QB, eo=12 * QB, **over):
@@ -343,23 +345,51 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("H", [1, 2, 4, 8, 12, 16])
-def test_varlen_workspace_covers_every_sequence(H, d):
-    """The packed-batch workspace covers the chunked workspace of every
-    single sequence of 1..T tokens (the chunked plan runs one launch per
-    sequence), and it never shrinks as T grows."""
-    prev = 0
-    for T in list(range(1, 2200, 7)) + [4096, 6000, 16384]:
-        got = fs.idattn_forward_varlen_workspace_size(fs.make_dims(3, T, H, d, 64, 4, "bf16", "auto"))
-        assert got >= prev, (T, got, prev)
-        prev = got
-    worst = 0
-    for n in range(1, 2200):
-        one = fs.idattn_forward_workspace_size(fs.make_dims(1, n, H, d, 64, 4, "bf16", "chunked"))
-        worst = max(worst, one)
-        if n % 97 == 0 or n in (961, 1601, 2199):
-            bound = fs.idattn_forward_varlen_workspace_size(fs.make_dims(2, n, H, d, 64, 4, "bf16", "auto"))
-            assert bound >= worst, (n, bound, worst)
+@pytest.mark.parametrize("H", [1, 2, 3, 8, 16, 40])
+def test_varlen_workspace_covers_the_plan(H, d):
+    """The packed batch's chunked workspace is sized from B, H and T alone;
+    the plan the device builds from the lengths (tests/plan_model.py) must
+    fit it for every length mix: at most 256 + B H blocks (the grid), fewer
+    than 256 end states, at most min(T, (T + 63 B) / 64) chunks per head, a
+    carry list within its capacity.  The workspace also never shrinks as T
+    or B grows."""
+    import numpy as np
+
+    from tests import plan_model as PM
+    rng = np.random.default_rng(H * 1000 + d)
+    state = 64 * 2 * d * 2 * 4
+    prev_t = {}
+    for trial in range(300):
+        B = int(rng.choice([1, 2, 3, 8, 40, 300]))
+        kind = trial % 3
+        if kind == 0:
+            lens = rng.integers(0, 3000, size=B)
+        elif kind == 1:  # one long sequence among short or empty ones
+            lens = rng.integers(0, 70, size=B)
+            lens[rng.integers(B)] = int(rng.integers(1000, 40000))
+        else:
+            lens = rng.geometric(1 / 500, size=B) - 1
+        lens = [int(x) for x in lens]
+        T = sum(lens)
+        if T == 0 or T * H * d * 2 >= 1 << 31:  # the kernels' 32-bit offsets
+            continue
+        pl = PM.plan(lens, H)
+        assert pl["blocks"] <= PM.blocks_max(B, H), (lens, H)
+        assert pl["end_states"] < PM.END_STATES, (lens, H)
+        assert pl["chunk_slots"] <= H * min(T, (T + 63 * B) // 64), (lens, H)
+        assert len(pl["carry"]) <= PM.carry_cap(H), (lens, H)
+        assert sorted(b for b, h, seg, c in pl["work"] if seg == pl["S"][b] - 1) == sorted(
+            b for b in range(B) for _ in range(H))
+        ws = fs.idattn_forward_varlen_workspace_size(fs.make_dims(B, T, H, d, 64, 4, "bf16", "chunked"))
+        # the plan-dependent parts alone: plan ints, end states, key-feature tiles
+        assert ws >= PM.plan_ints(B, H) * 4 + PM.END_STATES * state + pl["chunk_slots"] * 64 * d * 2
+        prev_t.setdefault(B, []).append((T, ws))
+    for B, pts in prev_t.items():
+        pts.sort()
+        assert all(b[1] >= a[1] for a, b in zip(pts, pts[1:])), B
+    sizes = [fs.idattn_forward_varlen_workspace_size(fs.make_dims(B, 5000, H, d, 64, 4, "bf16", "chunked"))
+             for B in (1, 2, 5, 17, 100)]
+    assert sizes == sorted(sizes)
 
 
 def test_noalloc_validation():

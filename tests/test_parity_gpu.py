@@ -376,13 +376,13 @@ def _packed_case(name, lens, seed, tag_off=0):
     return c, s, cu, c.q[0, :T], c.k[0, :T], c.v[0, :T], st0, tl0
 
 
-# With the lengths also on the host, shapes the chunked kernels take (bf16,
-# d = 64 or 128, M = 64, W <= 4) run one chunked forward per sequence; the
-# others, and every case without host lengths, run the sequential path.
-@pytest.mark.parametrize("host_lengths", [False, True], ids=["device_table", "host_lengths"])
+# Shapes the chunked kernels take (bf16, d = 64 or 128, M = 64, W <= 4) run
+# the packed batch chunked under AUTO (one launch sequence, plan built on the
+# device); the others, and SEQUENTIAL, run the sequential path.
+@pytest.mark.parametrize("algo", ["auto", "sequential"])
 @pytest.mark.parametrize("name", ["tiny_f32", "d16_m64_w2_f32", "d64_m32_ragged_bf16", "d128_m64_ragged_bf16",
-                                  "d128_w8_bf16", "d64_w1_bf16"])
-def test_forward_varlen(fs, name, host_lengths):
+                                  "d128_w8_bf16", "d64_w1_bf16", "d128_w2_bf16", "d64_w3_bf16"])
+def test_forward_varlen(fs, name, algo):
     import torch
     c, s, cu, q, k, v, st0, tl0 = _packed_case(name, VARLEN_LENS, seed=7)
     io = s["io"]
@@ -390,15 +390,124 @@ def test_forward_varlen(fs, name, host_lengths):
     p = fs.params_to_device(c.params)
     cu_d = torch.from_numpy(cu).cuda()
     o, st, tl = fs.forward_varlen(up(q, io), up(k, io), up(v, io), p, cu_d, state_in=state_dev(st0),
-                                  tail_in=up(tl0, io), return_state=True, host_lengths=host_lengths)
+                                  tail_in=up(tl0, io), return_state=True, algo=algo)
     _sync()
-    tag = f"varlen {name} host={host_lengths} T={int(cu[-1])} B={len(cu) - 1}"
+    tag = f"varlen {name} {algo} T={int(cu[-1])} B={len(cu) - 1}"
     check_packed(f"{tag} o", down(o), o_ref, cu, gate(io), io)
     check(f"{tag} state", state_np(st), st_ref, gate(io), io)
     assert np.array_equal(down(tl), tl_ref.astype(np.float32))
     # an empty sequence passes its state through unchanged
     for b in np.flatnonzero(np.diff(cu) == 0):
         assert np.array_equal(state_np(st)[b], st0[b].astype(np.complex64))
+
+
+def _oracle_varlen_pool(q, k, v, cu, params, state_in, tail_in):
+    """oracle.forward_varlen with each sequence's heads split over threads
+    (the same oracle forward per sequence)."""
+    outs = [oracle_forward_pool(q[None, cu[b]:cu[b + 1]], k[None, cu[b]:cu[b + 1]], v[None, cu[b]:cu[b + 1]], params,
+                                state_in=None if state_in is None else state_in[b:b + 1],
+                                tail_in=None if tail_in is None else tail_in[b:b + 1])
+            for b in range(len(cu) - 1)]
+    return (np.concatenate([r[0][0] for r in outs]), np.concatenate([r[1] for r in outs]),
+            np.concatenate([r[2] for r in outs]))
+
+
+# Packed batches that reach every branch of the device plan (tests/plan_model.py):
+# name: (base, overrides, lengths, seed tag)
+PACKED = {
+    # H = 2: one-chunk segments; sequences of 32 and 11 segments take the carry kernel
+    "carry_h2_d128": ("1p3b", dict(H=2), [2000, 30, 0, 700, 5], 201),
+    # H = 16: a sequence of 5 segments (carry kernel) beside one of 3 (folded)
+    "carry_fold_h16_d128": ("1p3b", dict(H=16), [600, 300, 100], 202),
+    # 40 sequences x 16 heads: more pairs than compute units
+    "many_h16_d64": ("125m", dict(H=16), None, 203),
+    # 300 sequences: last segments in sequence order (no size sort)
+    "b300_h1_d64": ("125m", dict(H=1), None, 204),
+}
+
+
+def _packed_lens(name):
+    base, over, lens, tag = PACKED[name]
+    if lens is None:
+        r = np.random.default_rng(tag)
+        lens = [int(x) for x in r.integers(0, 300, size=40 if name.startswith("many") else 300)]
+        lens[3] = 0
+    return lens
+
+
+@pytest.mark.parametrize("name", sorted(PACKED))
+def test_forward_varlen_chunked_plans(fs, name):
+    """The packed chunked path against the oracle on batches whose plans take
+    the carry kernel, the folded carry, more pairs than compute units and
+    more sequences than the plan sorts, with state and tail updated in place
+    (state_out = state_in, tail_out = tail_in)."""
+    import torch
+    base, over, _, tag = PACKED[name]
+    lens = _packed_lens(name)
+    T = int(sum(lens))
+    c = WL.make_case(base, seed=1, tag=tag, **dict(over, B=1, N=T))
+    s = dict(c.spec, B=len(lens))
+    st0, tl0 = WL.make_decode_state(s, seed=tag)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q, k, v = c.q[0], c.k[0], c.v[0]
+    print(f"packed {name}: B={len(lens)} T={T} H={s['H']} d={s['d']}", flush=True)
+    p = fs.params_to_device(c.params)
+    st, tl = state_dev(st0), up(tl0, "bf16")
+    o = fs.forward_varlen_into(up(q, "bf16"), up(k, "bf16"), up(v, "bf16"), p, torch.from_numpy(cu).cuda(),
+                               state_in=st, tail_in=tl, state_out=st, tail_out=tl, algo="chunked")
+    _sync()
+    o_ref, st_ref, tl_ref = _oracle_varlen_pool(q, k, v, cu, c.params, st0, tl0)
+    check_packed(f"packed {name} o", down(o), o_ref, cu, GATE_BF16, "bf16")
+    check(f"packed {name} state", state_np(st), st_ref, GATE_BF16, "bf16")
+    assert np.array_equal(down(tl), tl_ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("case", ["varlen_h2", "bench_mix_h16", "many_h16", "b300_h1"])
+def test_varlen_device_plan(fs, case):
+    """The plan the tables kernel builds from the device table, read back from
+    the workspace, equals the plan model's (segment size, block counts, the
+    per-sequence offsets, the order of the last segments, the carry list)."""
+    import torch
+
+    from tests import plan_model as PM
+    lens, H, d = {"varlen_h2": (VARLEN_LENS, 2, 128),
+                  "bench_mix_h16": ([6000, 3500, 2500, 2048, 1200, 700, 400, 36], 16, 128),
+                  "many_h16": (_packed_lens("many_h16_d64"), 16, 64),
+                  "b300_h1": (_packed_lens("b300_h1_d64"), 1, 64)}[case]
+    B, T = len(lens), int(sum(lens))
+    s = WL.spec("1p3b" if d == 128 else "125m", B=1, N=T, H=H, tag=205)
+    params = WL.make_params(s)
+    p = fs.params_to_device(params)
+    x = torch.zeros((T, H, d), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(x)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+    dims = fs.make_dims(B, T, H, d, 64, 4, "bf16", "chunked")
+    nbytes = fs.idattn_forward_varlen_workspace_size(dims)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    fs.idattn_forward_varlen(dims, fs.make_params(p), cu, x, x, x, o, None, None, None, None, ws, nbytes)
+    _sync()
+    n = PM.plan_ints(B, H)
+    got = ws[:4 * n].cpu().view(torch.int32).numpy()
+    want = PM.plan_array(lens, H)
+    assert list(got[:len(want)]) == want, case
+
+
+def test_varlen_malformed_table_writes_nothing(fs):
+    """A device table that does not rise from 0 to T gives the packed chunked
+    path a plan of no blocks: no output, state or tail is written."""
+    import torch
+    T, H, d = 300, 2, 128
+    s = WL.spec("1p3b", B=1, N=T, H=H, tag=206)
+    p = fs.params_to_device(WL.make_params(s))
+    x = torch.ones((T, H, d), dtype=torch.bfloat16, device="cuda")
+    for bad in ([0, 200, 100, 300], [5, 100, 200, 300], [0, 100, 200, 299]):
+        o = torch.full_like(x, 7.0)
+        st = torch.full((3, H, 64, 2 * d, 2), 7.0, device="cuda")
+        tl = torch.full((3, H, 2, 3, d), 7.0, dtype=torch.bfloat16, device="cuda")
+        fs.forward_varlen_into(x, x, x, p, torch.tensor(bad, dtype=torch.int32, device="cuda"), o=o,
+                               state_out=st, tail_out=tl, algo="chunked")
+        _sync()
+        assert bool((o == 7).all()) and bool((st == 7).all()) and bool((tl == 7).all()), bad
 
 
 @pytest.mark.parametrize("feature_norm", ["unit", "rff"])
@@ -432,13 +541,12 @@ def test_forward_varlen_without_state(fs):
     assert np.array_equal(down(tl), tl_ref.astype(np.float32))
 
 
-@pytest.mark.parametrize("io,algo", [("f32", "sequential"), ("bf16", "sequential"), ("bf16", "chunked")])
-def test_forward_varlen_matches_dense_at_scale(fs, io, algo):
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_forward_varlen_sequential_matches_dense_at_scale(fs, io):
     """At the 1.3B head shape (H = 16, d = 128, M = 64) with 9 400 packed tokens:
-    every sequence of the packed call gives bit for bit what the dense forward
-    of the same algorithm gives for that sequence alone (the same kernels in
-    the same order; the dense paths are themselves compared with the oracle).
-    The chunked plan needs the lengths on the host."""
+    every sequence of the packed sequential call gives bit for bit what the
+    dense sequential forward gives for that sequence alone (the same kernels
+    in the same order; the dense path is itself compared with the oracle)."""
     import torch
     lens = [4096, 1, 3000, 0, 17, 2286]
     s = WL.spec("1p3b", B=1, N=sum(lens), io=io, tag=81)
@@ -449,17 +557,42 @@ def test_forward_varlen_matches_dense_at_scale(fs, io, algo):
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     qd, kd, vd = up(q[0], io), up(k[0], io), up(v[0], io)
     o, st, tl = fs.forward_varlen(qd, kd, vd, p, torch.from_numpy(cu).cuda(), state_in=state_dev(st0),
-                                  tail_in=up(tl0, io), return_state=True, algo=algo,
-                                  host_lengths=algo == "chunked")
+                                  tail_in=up(tl0, io), return_state=True, algo="sequential")
     stb, tlb = state_dev(st0), up(tl0, io)
     for b, n in enumerate(lens):
         sl = slice(int(cu[b]), int(cu[b + 1]))
-        ob, sb, tb = fs.forward(qd[None, sl], kd[None, sl], vd[None, sl], p, algo=algo,
+        ob, sb, tb = fs.forward(qd[None, sl], kd[None, sl], vd[None, sl], p, algo="sequential",
                                 state_in=stb[b:b + 1], tail_in=tlb[b:b + 1], return_state=True)
         _sync()
         assert torch.equal(o[sl], ob[0]), b
         assert torch.equal(st[b], sb[0]), b
         assert torch.equal(tl[b], tb[0]), b
+
+
+def test_forward_varlen_chunked_at_scale(fs):
+    """The packed batch the benchmark times (1.3B head shape, 8 sequences of
+    6000 .. 36 tokens, T = 16 384), from a seeded state and tail, against the
+    oracle over every (sequence, head) pair: output, end state and tail."""
+    import torch
+    lens = [6000, 3500, 2500, 2048, 1200, 700, 400, 36]
+    s = WL.spec("1p3b", B=1, N=sum(lens), tag=90)
+    q, k, v = WL.make_rows(s)
+    params = WL.make_params(s)
+    st0, tl0 = WL.make_decode_state(dict(s, B=len(lens)), seed=91)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    p = fs.params_to_device(params)
+    print("packed 1.3B mix: GPU", flush=True)
+    o, st, tl = fs.forward_varlen(up(q[0], "bf16"), up(k[0], "bf16"), up(v[0], "bf16"), p,
+                                  torch.from_numpy(cu).cuda(), state_in=state_dev(st0), tail_in=up(tl0, "bf16"),
+                                  return_state=True, algo="chunked")
+    _sync()
+    o_np, st_np, tl_np = down(o), state_np(st), down(tl)
+    del o, st, tl
+    print("packed 1.3B mix: oracle over all (sequence, head) pairs", flush=True)
+    o_ref, st_ref, tl_ref = _oracle_varlen_pool(q[0], k[0], v[0], cu, params, st0, tl0)
+    check_packed("packed 1.3B mix o", o_np, o_ref, cu, GATE_BF16, "bf16")
+    check("packed 1.3B mix state", st_np, st_ref, GATE_BF16, "bf16")
+    assert np.array_equal(tl_np, tl_ref.astype(np.float32))
 
 
 # Learned decays can be much faster than the S4D-Lin init: Delta |Re lambda| up
