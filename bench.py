@@ -117,6 +117,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU sample")
+    ap.add_argument("--only", choices=["varlen", "normalized", "backward", "decode"],
+                    help="run one of the secondary measurements alone and print it (for profiling)")
     ap.add_argument("--settle-s", type=float, default=0.3,
                     help="seconds of untimed back-to-back forwards before the warmup steps (clock settle)")
     return ap.parse_args()
@@ -235,13 +237,35 @@ def decode_bench(torch, fs, steps, warmup):
                          "algorithmic_bytes": nbytes}}
 
 
-def varlen_bench(torch, fs, WL, dense_ms=None, steps=20, warmup=40):
+def time_calls(torch, call, steps, warmup, settle_s=0.3):
+    """Mean time of one call (HIP events around each call on the current
+    stream) after settle_s seconds of back-to-back calls and warmup more, the
+    same clock settle the main forward measurement gets."""
+    t = time.perf_counter()
+    while time.perf_counter() - t < settle_s:
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    return sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
+
+
+def varlen_bench(torch, fs, WL, dense_ms=None, steps=20, warmup=5):
     """Packed variable-length batch at the 1.3B head shape (H=16, d=128, M=64,
     W=4, bf16): 16 384 tokens (the dense 1.3B batch's count) in 8 sequences
     of mixed lengths (long prompts beside short ones).  AUTO runs the chunked
     kernels in one launch sequence whose plan is built on the device from
     the sequence table; the sequential fp32 path is timed beside it.  Each
-    call is timed with HIP events on the stream, as the dense forward is."""
+    call is timed with HIP events on the stream after the same clock settle
+    as the dense forward."""
     import numpy as np
     lens = [6000, 3500, 2500, 2048, 1200, 700, 400, 36]
     s = WL.spec("1p3b", B=1, N=sum(lens), tag=90)
@@ -267,16 +291,7 @@ def varlen_bench(torch, fs, WL, dense_ms=None, steps=20, warmup=40):
         def call():
             fs.idattn_forward_varlen(dims, prm, cu, qd, kd, vd, o, None, None, state, tail, ws, nbytes)
 
-        for _ in range(warmup):
-            call()
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for e0, e1 in ev:
-            e0.record()
-            call()
-            e1.record()
-        torch.cuda.synchronize()
-        return sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
+        return time_calls(torch, call, steps if algo == "auto" else 3, warmup, 0.3 if algo == "auto" else 0.0)
 
     ms = timed("auto")
     ms_seq = timed("sequential")
@@ -292,7 +307,7 @@ def varlen_bench(torch, fs, WL, dense_ms=None, steps=20, warmup=40):
     return out
 
 
-def normalized_bench(torch, fs, WL, config, steps=20, warmup=40):
+def normalized_bench(torch, fs, WL, config, steps=20, warmup=5):
     """The forward with the normalised readout (eta state) at the bench's
     shape: the chunked path where the plain readout has one (AUTO), with eta
     carried out; also the sequential path for comparison."""
@@ -319,16 +334,7 @@ def normalized_bench(torch, fs, WL, config, steps=20, warmup=40):
         def call():
             fs.idattn_forward_normalized(dims, prm, qd, kd, vd, o, None, None, None, state, None, eta, ws, nbytes)
 
-        for _ in range(warmup):
-            call()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps if algo == "auto" else 3):
-            call()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / (steps if algo == "auto" else 3)
+        ms = time_calls(torch, call, steps if algo == "auto" else 3, warmup, 0.3 if algo == "auto" else 0.0)
         out[algo] = {"ms_per_call": ms, "tokens_per_s": B * N / (ms * 1e-3)}
         del ws
     try:
@@ -402,6 +408,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     fs.load_library()
+    if args.only:
+        part = {"varlen": lambda: varlen_bench(torch, fs, WL),
+                "normalized": lambda: normalized_bench(torch, fs, WL, args.config),
+                "backward": lambda: backward_bench(torch, fs, WL, args.config),
+                "decode": lambda: decode_bench(torch, fs, steps=20, warmup=20)}[args.only]()
+        print(json.dumps({args.only: part}), flush=True)
+        return
     s = WL.spec(args.config)
     B, N, H, d, M, W = s["B"], s["N"], s["H"], s["d"], s["M"], s["W"]
     q, k, v = WL.make_rows(s)

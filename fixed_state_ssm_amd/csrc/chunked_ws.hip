@@ -347,11 +347,11 @@ __device__ __forceinline__ int64_t block_reduce(int64_t v, bool mx, int64_t* red
 // The plan of a packed batch, built by one block from the sequence table cu
 // (device int32 [B + 1]): the segment size C (see plan_blocks_max), the
 // offsets of every sequence (exclusive scans over b), the order of the last
-// segments, the carry list, and abar^{C L} of every head and mode.  A table
+// segments and the carry list (abar^{C L} of each head follows in the
+// feature pass, from the fp64 abar of the tables).  A table
 // that does not rise from 0 to T gives a plan of no blocks: nothing runs and
 // no output is written.
-__device__ void packed_plan(const Problem& p, const idattn_params& prm, const int32_t* __restrict__ cu,
-                            int32_t* __restrict__ plan, uint8_t* __restrict__ tab) {
+__device__ void packed_plan(const Problem& p, const int32_t* __restrict__ cu, int32_t* __restrict__ plan) {
     __shared__ int64_t red[kTabThreads / 64];
     __shared__ int64_t scan[kTabThreads / 64][4];
     __shared__ int32_t key[kPlanSortMax];
@@ -447,23 +447,14 @@ __device__ void packed_plan(const Problem& p, const idattn_params& prm, const in
         }
         order[rank] = static_cast<int32_t>(b);
     }
-    // abar^{C L} of every head and mode (the carry across segments)
-    for (int64_t e = tid; e < H * MM; e += nt) {
-        const int64_t h = e / MM;
-        const int m = static_cast<int>(e % MM);
-        double pr, pi;
-        cpow(exp(static_cast<double>(prm.log_dt[h])), prm.A[(h * MM + m) * 2], prm.A[(h * MM + m) * 2 + 1],
-             static_cast<double>(cps * L), pr, pi);
-        reinterpret_cast<float2*>(tab + h * kTabBytes + kTabPwSeg)[m] =
-            make_float2(static_cast<float>(pr), static_cast<float>(pi));
-    }
 }
 
 // grid (H, 17), 320 threads.  Blocks y < 16: threads 0..255 take one (k, m)
 // each and evaluate abar^k while threads 256..319 run the ZOH step of mode m
 // into shared memory, then T = bbar abar^k and abar^{k+1} = abar^k abar;
 // block y = 16: abar^Lseg (threads 0..63), or for a packed batch (plan !=
-// nullptr) the plan, built by block (0, 16) alone.  The ZOH wave of a block
+// nullptr) the plan, built by block (0, 16) alone.  Also abar, bbar in fp64
+// (dz), for the closed forms of the normaliser and of packed segment powers.  The ZOH wave of a block
 // y < 16 also finds the head's scale kappa.  No thread runs more than one
 // fp64 power or ZOH step before the combine.
 __global__ __launch_bounds__(kTabThreads) void zoh_tables_kernel(Problem p, idattn_params prm, int64_t Lseg,
@@ -474,7 +465,7 @@ __global__ __launch_bounds__(kTabThreads) void zoh_tables_kernel(Problem p, idat
     __shared__ double kap_s;
     const int64_t h = blockIdx.x;
     if (blockIdx.y == 16 && plan != nullptr) {
-        if (h == 0) packed_plan(p, prm, cu, plan, tab);
+        if (h == 0) packed_plan(p, cu, plan);
         return;
     }
     uint8_t* th = tab + h * kTabBytes;
@@ -522,13 +513,12 @@ __global__ __launch_bounds__(kTabThreads) void zoh_tables_kernel(Problem p, idat
     }
     reinterpret_cast<float2*>(th + kTabPw)[k * MM + m] =
         make_float2(static_cast<float>(pr * z.ar - pi * z.ai), static_cast<float>(pr * z.ai + pi * z.ar));
+    if (blockIdx.y == 0 && k == 0) reinterpret_cast<double4*>(th + kTabDz)[m] = make_double4(z.ar, z.ai, z.br, z.bi);
     if (p.eta) {  // Hsum(k) = bbar sum_{j<=k} abar^j, for the normaliser
         double hr, hi;
         geo_from_pow(z.ar, z.ai, z.br, z.bi, pr * z.ar - pi * z.ai, pr * z.ai + pi * z.ar, static_cast<double>(k + 1), hr,
                      hi);
         reinterpret_cast<float2*>(th + kTabHs)[k * MM + m] = make_float2(static_cast<float>(hr), static_cast<float>(hi));
-        if (blockIdx.y == 0 && k == 0)
-            reinterpret_cast<double4*>(th + kTabDz)[m] = make_double4(z.ar, z.ai, z.br, z.bi);
     }
 }
 
@@ -1256,7 +1246,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
                                                             const uint16_t* __restrict__ v,
                                                             const uint16_t* __restrict__ tail_in,
                                                             const float* __restrict__ state_in,
-                                                            const uint8_t* __restrict__ tab, float* __restrict__ c0,
+                                                            uint8_t* __restrict__ tab, float* __restrict__ c0,
                                                             float* __restrict__ ws, _Float16* __restrict__ zt,
                                                             int64_t Lseg_dense, int S_dense, const float* eta_in,
                                                             float* eta_out, float2* __restrict__ c0eta,
@@ -1265,6 +1255,17 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
     const Blk wk = block_work(p, plan, S_dense, Lseg_dense);
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (wk.idle) return;
+    if (plan != nullptr && blockIdx.x < plan[3] + p.H && blockIdx.x >= plan[3] && tid < MM) {
+        // one block per head (the heads of the first last-segment sequence):
+        // abar^{C L} of the head's modes, the carry across segments, by
+        // repeated squaring of the fp64 abar (read by the carry kernel and the
+        // forward, both later on the stream)
+        const double4 z = reinterpret_cast<const double4*>(tab + wk.h * kTabBytes + kTabDz)[tid];
+        double pr, pi;
+        cpow_int(z.x, z.y, wk.Lseg, pr, pi);
+        reinterpret_cast<float2*>(tab + wk.h * kTabBytes + kTabPwSeg)[tid] =
+            make_float2(static_cast<float>(pr), static_cast<float>(pi));
+    }
     if (wk.n == 0) {  // no tokens: eta passes through (the forward copies state and tail)
         if (p.eta && eta_out != nullptr && tid < MM) {
             const int64_t e = (wk.bh * MM + tid) * 2;
@@ -1386,15 +1387,17 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
     }
 }
 
-// Carry chain over segments (states in lane order), one complex state element
-// per thread (four threads share the eight floats of an even lane's float4
-// and the next lane's): ws[seg] <- state entering segment seg+1.  The end
-// states of up to eight segments are loaded before any of them is combined,
-// so that the loads overlap instead of forming a chain of dependent round
-// trips.  The state entering the sequence comes from the staged copy c0.
-// Dense batches: every (b, h) of S segments.  Packed batches: the (b, h) of
-// the sequences in the plan's carry list (those with more segments than the
-// forward folds), S_b segments each; threads beyond them exit.
+// Carry chain over segments (states in lane order): ws[st0 + seg] <- the state
+// entering segment seg + 1.  A thread takes one group of eight consecutive
+// floats of a (b, h) state, four complex elements, and walks the segments,
+// loading the groups of up to eight segments before combining any of them so
+// that the loads overlap instead of forming a chain of dependent round trips.
+// The state entering the sequence comes from the staged copy c0.  Dense
+// batches: every (b, h) of S segments.  Packed batches: the (b, h) of the
+// sequences in the plan's carry list (those with more segments than the
+// forward folds), S_b segments each.  Grid-stride over the groups, so that
+// the grid need not match the (device-side) length of the carry list.
+constexpr int kCarryBlocks = 1024;
 __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, bool has_state,
                                                             const float* __restrict__ c0,
                                                             const uint8_t* __restrict__ tab,
@@ -1402,57 +1405,87 @@ __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, bool has_
                                                             const int32_t* __restrict__ plan) {
     constexpr int kBatch = 8;
     const int D = static_cast<int>(p.d);
-    const int64_t per = 128 * D;  // threads per (b, h)
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    int64_t bh, st0;
-    int S;
-    if (plan == nullptr) {
-        if (e >= p.B * p.H * per) return;
-        bh = e / per;
-        S = S_dense;
-        st0 = bh * (S - 1);
-    } else {
-        const int64_t j = e / per;  // pair of the carry list
-        if (j >= static_cast<int64_t>(plan[2]) * p.H) return;
-        const int64_t B = p.B;
-        const int64_t b = plan[kPlanHead + 6 * B + 1 + j / p.H], hh = j % p.H;  // the carry list
-        bh = b * p.H + hh;
-        S = plan[kPlanHead + 2 * B + b];
-        st0 = p.H * static_cast<int64_t>(plan[kPlanHead + 4 * B + b]) + hh * (S - 1);
-    }
-    const int64_t h = bh % p.H;
-    const int o = static_cast<int>((e % per) >> 2) * 8;  // float offset of the group of eight
-    const int k = static_cast<int>(e & 3);
-    int mode, pre, pim;  // mode, positions of re / im in the eight floats
-    if (o < 128 * D) {        // U: [kw][rt][lane][jj], re in lane i, im in lane i + 1
-        const int kw = o / (16 * D), ln = (o % 256) / 4;  // (16 D is a multiple of 256)
-        mode = 8 * kw + (ln & 15) / 2;
-        pre = k;
-        pim = 4 + k;
-    } else {  // Gamma: [vw][mt][lane][jj], (re, im) of modes m0, m0 + 1 in jj, channel 16 vw + i of the lane
-        const int o2 = o - 128 * D, mt = (o2 % 2048) / 256, ln = (o2 % 256) / 4;
-        mode = 8 * mt + 2 * (ln >> 4) + (k & 1);
-        pre = 2 * k;
-        pim = 2 * k + 1;
-    }
-    const float2 a = reinterpret_cast<const float2*>(tab + h * kTabBytes + kTabPwSeg)[mode];
-    // the staged state_in (lane order, already times kappa) or zero
-    float2 c = has_state ? make_float2(c0[bh * 256 * D + o + pre], c0[bh * 256 * D + o + pim]) : make_float2(0.f, 0.f);
+    const int64_t per = 32 * D;  // groups of eight floats per (b, h) state (256 D floats)
+    const int64_t npairs = plan == nullptr ? p.B * p.H : static_cast<int64_t>(plan[2]) * p.H;
     const int64_t sst = 256 * D;  // floats per state
-    float* base = ws + st0 * sst + o;
-    for (int s0 = 0; s0 + 1 < S; s0 += kBatch) {
-        const int n = S - 1 - s0 < kBatch ? S - 1 - s0 : kBatch;
-        float2 loc[kBatch];
+    for (int64_t gi = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; gi < npairs * per;
+         gi += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t j = gi / per;
+        int64_t bh, st0;
+        int S;
+        if (plan == nullptr) {
+            bh = j;
+            S = S_dense;
+            st0 = bh * (S - 1);
+        } else {  // pair j of the carry list
+            const int64_t B = p.B;
+            const int64_t b = plan[kPlanHead + 6 * B + 1 + j / p.H], hh = j % p.H;
+            bh = b * p.H + hh;
+            S = plan[kPlanHead + 2 * B + b];
+            st0 = p.H * static_cast<int64_t>(plan[kPlanHead + 4 * B + b]) + hh * (S - 1);
+        }
+        const int64_t h = bh % p.H;
+        const int o = static_cast<int>(gi % per) * 8;  // float offset of the group
+        // the four complex elements: real part at float re[k], imaginary at im[k]
+        int mode[4], re[4], im[4];
+        if (o < 128 * D) {  // U: [kw][rt][lane][jj], re in lane i, im in lane i + 1: one mode
+            const int kw = o / (16 * D), ln = (o % 256) / 4;  // (16 D is a multiple of 256)
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j)
-            if (j < n) loc[j] = make_float2(base[(s0 + j) * sst + pre], base[(s0 + j) * sst + pim]);
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j)
-            if (j < n) {
-                c = make_float2(a.x * c.x - a.y * c.y + loc[j].x, a.x * c.y + a.y * c.x + loc[j].y);
-                base[(s0 + j) * sst + pre] = c.x;
-                base[(s0 + j) * sst + pim] = c.y;
+            for (int k = 0; k < 4; ++k) {
+                mode[k] = 8 * kw + (ln & 15) / 2;
+                re[k] = k;
+                im[k] = 4 + k;
             }
+        } else {  // Gamma: [vw][mt][lane][jj], (re, im) of modes m0, m0 + 1 in jj
+            const int o2 = o - 128 * D, mt = (o2 % 2048) / 256, ln = (o2 % 256) / 4;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                mode[k] = 8 * mt + 2 * (ln >> 4) + (k & 1);
+                re[k] = 2 * k;
+                im[k] = 2 * k + 1;
+            }
+        }
+        const float2* pws = reinterpret_cast<const float2*>(tab + h * kTabBytes + kTabPwSeg);
+        float2 a[4], c[4];
+        float ci[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (has_state) {  // the staged state_in (lane order, already times kappa)
+            const float4* src = reinterpret_cast<const float4*>(c0 + bh * sst + o);
+            const float4 x0 = src[0], x1 = src[1];
+            ci[0] = x0.x; ci[1] = x0.y; ci[2] = x0.z; ci[3] = x0.w;
+            ci[4] = x1.x; ci[5] = x1.y; ci[6] = x1.z; ci[7] = x1.w;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            a[k] = pws[mode[k]];
+            c[k] = make_float2(ci[re[k]], ci[im[k]]);
+        }
+        float4* base = reinterpret_cast<float4*>(ws + st0 * sst + o);
+        const int64_t s4 = sst / 4;  // float4s per state
+        for (int s0 = 0; s0 + 1 < S; s0 += kBatch) {
+            const int n = S - 1 - s0 < kBatch ? S - 1 - s0 : kBatch;
+            float4 l0[kBatch], l1[kBatch];
+#pragma unroll
+            for (int jj = 0; jj < kBatch; ++jj)
+                if (jj < n) {
+                    l0[jj] = base[(s0 + jj) * s4];
+                    l1[jj] = base[(s0 + jj) * s4 + 1];
+                }
+#pragma unroll
+            for (int jj = 0; jj < kBatch; ++jj)
+                if (jj < n) {
+                    const float e[8] = {l0[jj].x, l0[jj].y, l0[jj].z, l0[jj].w, l1[jj].x, l1[jj].y, l1[jj].z, l1[jj].w};
+                    float r[8];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        c[k] = make_float2(a[k].x * c[k].x - a[k].y * c[k].y + e[re[k]],
+                                           a[k].x * c[k].y + a[k].y * c[k].x + e[im[k]]);
+                        r[re[k]] = c[k].x;
+                        r[im[k]] = c[k].y;
+                    }
+                    base[(s0 + jj) * s4] = make_float4(r[0], r[1], r[2], r[3]);
+                    base[(s0 + jj) * s4 + 1] = make_float4(r[4], r[5], r[6], r[7]);
+                }
+        }
     }
 }
 
@@ -1998,9 +2031,11 @@ hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, con
     const int64_t carry_pairs = packed ? (p.N / L >= kFoldMax ? carry_cap(p.H) * p.H : 0)
                                        : (S > kFoldMax ? pairs : 0);
     if (carry_pairs > 0) {
-        const int64_t threads = carry_pairs * 128 * p.d;  // one complex element each
-        segment_carry_kernel<<<dim3(static_cast<unsigned>((threads + 255) / 256)), 256, 0, stream>>>(
-            p, state_in != nullptr, c0, tab, ws, S, plan);
+        const int64_t groups = carry_pairs * 32 * p.d;  // groups of eight state floats
+        int64_t blocks = (groups + 255) / 256;
+        blocks = blocks < kCarryBlocks ? blocks : kCarryBlocks;
+        segment_carry_kernel<<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(p, state_in != nullptr, c0,
+                                                                                     tab, ws, S, plan);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
