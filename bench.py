@@ -117,7 +117,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU sample")
-    ap.add_argument("--only", choices=["varlen", "normalized", "backward", "decode"],
+    ap.add_argument("--only", choices=["varlen", "normalized", "rff", "backward", "decode"],
                     help="run one of the secondary measurements alone and print it (for profiling)")
     ap.add_argument("--settle-s", type=float, default=0.3,
                     help="seconds of untimed back-to-back forwards before the warmup steps (clock settle)")
@@ -307,7 +307,7 @@ def varlen_bench(torch, fs, WL, dense_ms=None, steps=20, warmup=5):
     return out
 
 
-def normalized_bench(torch, fs, WL, config, steps=20, warmup=5):
+def normalized_bench(torch, fs, WL, config, plain_ms=None, steps=20, warmup=5):
     """The forward with the normalised readout (eta state) at the bench's
     shape: the chunked path where the plain readout has one (AUTO), with eta
     carried out; also the sequential path for comparison."""
@@ -342,10 +342,58 @@ def normalized_bench(torch, fs, WL, config, steps=20, warmup=5):
         path = "chunked (MFMA) path"
     except fs.IdattnError:
         path = "sequential fp32 path"
-    return {"workload": f"{config}: B={B} H={H} N={N} d=R={d} M={M} W={W}, bf16 I/O, normalised readout (eta), "
-                        f"{path}", "ms_per_call": out["auto"]["ms_per_call"],
-            "tokens_per_s": out["auto"]["tokens_per_s"],
-            "sequential": dict(out["sequential"], path="sequential fp32 path")}
+    res = {"workload": f"{config}: B={B} H={H} N={N} d=R={d} M={M} W={W}, bf16 I/O, normalised readout (eta), "
+                       f"{path}", "ms_per_call": out["auto"]["ms_per_call"],
+           "tokens_per_s": out["auto"]["tokens_per_s"],
+           "sequential": dict(out["sequential"], path="sequential fp32 path")}
+    if plain_ms:
+        res["ratio_to_plain_forward"] = out["auto"]["ms_per_call"] / plain_ms
+    return res
+
+
+def rff_bench(torch, fs, WL, config, plain_ms=None, steps=20, warmup=5):
+    """The forward with the random-Fourier-feature map (frequencies drawn as
+    in the tests) at the bench's shape: AUTO (the chunked path, its RFF
+    pre-pass included) and the sequential path for comparison."""
+    import numpy as np
+    s = WL.spec(config)
+    q, k, v = WL.make_rows(s)
+    params = WL.make_params(s)
+    params["rff_omega"] = WL.make_rff_omega(s, seed=1)
+    p = fs.params_to_device(params)
+    B, N, H, d, M, W = s["B"], s["N"], s["H"], s["d"], s["M"], s["W"]
+
+    def up(x):
+        return torch.from_numpy(WL.bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    qd, kd, vd = up(q), up(k), up(v)
+    o = torch.empty_like(qd)
+    state = torch.empty((B, H, M, 2 * d, 2), dtype=torch.float32, device="cuda")
+    prm = fs.make_params(p)
+    out = {}
+    for algo in ("auto", "sequential"):
+        dims = fs.make_dims(B, N, H, d, M, W, "bf16", algo, feature_norm="rff")
+        nbytes = fs.idattn_forward_workspace_size(dims)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+
+        def call():
+            fs.idattn_forward(dims, prm, qd, kd, vd, o, None, None, state, None, ws, nbytes)
+
+        ms = time_calls(torch, call, steps if algo == "auto" else 3, warmup, 0.3 if algo == "auto" else 0.0)
+        out[algo] = {"ms_per_call": ms, "tokens_per_s": B * N / (ms * 1e-3)}
+        del ws
+    try:
+        fs.idattn_forward_workspace_size(fs.make_dims(B, N, H, d, M, W, "bf16", "chunked", feature_norm="rff"))
+        path = "chunked (MFMA) path with the RFF pre-pass"
+    except fs.IdattnError:
+        path = "sequential fp32 path"
+    res = {"workload": f"{config}: B={B} H={H} N={N} d=R={d} M={M} W={W}, bf16 I/O, random Fourier features "
+                       f"(d/2 frequencies per head), {path}", "ms_per_call": out["auto"]["ms_per_call"],
+           "tokens_per_s": out["auto"]["tokens_per_s"],
+           "sequential": dict(out["sequential"], path="sequential fp32 path")}
+    if plain_ms:
+        res["ratio_to_plain_forward"] = out["auto"]["ms_per_call"] / plain_ms
+    return res
 
 
 def backward_bench(torch, fs, WL, config, steps=5, warmup=2):
@@ -411,6 +459,7 @@ def main():
     if args.only:
         part = {"varlen": lambda: varlen_bench(torch, fs, WL),
                 "normalized": lambda: normalized_bench(torch, fs, WL, args.config),
+                "rff": lambda: rff_bench(torch, fs, WL, args.config),
                 "backward": lambda: backward_bench(torch, fs, WL, args.config),
                 "decode": lambda: decode_bench(torch, fs, steps=20, warmup=20)}[args.only]()
         print(json.dumps({args.only: part}), flush=True)
@@ -514,7 +563,8 @@ def main():
     if not args.no_decode:
         out["decode"] = decode_bench(torch, fs, steps=20, warmup=20)
         out["varlen"] = varlen_bench(torch, fs, WL, mean_launch_ms if args.config == "1p3b" else None)
-        out["normalized"] = normalized_bench(torch, fs, WL, args.config)
+        out["normalized"] = normalized_bench(torch, fs, WL, args.config, mean_launch_ms)
+        out["rff"] = rff_bench(torch, fs, WL, args.config, mean_launch_ms)
         out["backward"] = backward_bench(torch, fs, WL, args.config)
     del sets, ws
     torch.cuda.empty_cache()

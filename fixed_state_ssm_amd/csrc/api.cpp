@@ -150,7 +150,6 @@ idattn_status workspace_bytes(const idattn_dims& D, int algo, size_t* bytes) {
         const idattn::Problem p = problem(D);
         if (D.io_dtype != IDATTN_IO_BF16)
             return fail(IDATTN_ERR_UNSUPPORTED, "the chunked algorithm needs bf16 I/O");
-        if (p.rff_feat) return fail(IDATTN_ERR_UNSUPPORTED, "the chunked algorithm has no RFF feature map");
         if (!idattn::chunked_supported(p))
             return fail(IDATTN_ERR_UNSUPPORTED, "the chunked algorithm has no kernel for d=%lld M=%lld",
                         (long long)D.d, (long long)D.M);

@@ -777,15 +777,28 @@ __device__ __forceinline__ void share_factor(SM& sm, float f, float (&out)[8]) {
     out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
-// z_k of the thread's 8 tokens to z_k^T (zero past n valid tokens).
+// z_k of the thread's 8 tokens to z_k^T (zero past n valid tokens).  With
+// pre (random Fourier features), slots 3..10 of r hold the features xi_k
+// themselves as fp16 pairs (conv and map applied by rff_features_kernel), and
+// only the RMSNorm remains.
 template <int D, class SM>
 __device__ __forceinline__ void fm_keys(const uint32_t (&r)[11], const SM& sm, const void* zT, int n, float eps_feat,
-                                        float eps_norm, bool unit, int fi = feat_index<D>()) {
+                                        float eps_norm, bool unit, bool pre, int fi = feat_index<D>()) {
     if (fi >= Cfg<D>::NF) return;
     const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
     float y[2][8], ss[8], rho[8];
-    conv_silu<D>(r, sm.wk, cgi, y, ss);
-    {
+    if (pre) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const half2v x = __builtin_bit_cast(half2v, r[3 + s]);
+            y[0][s] = static_cast<float>(x[0]);
+            y[1][s] = static_cast<float>(x[1]);
+            ss[s] = fmaf(y[1][s], y[1][s], y[0][s] * y[0][s]);
+        }
+        share_factor<D>(const_cast<SM&>(sm),
+                        __builtin_amdgcn_rsqf(fmaf(1.f / D, reduce_scatter8<Cfg<D>::CP>(ss), eps_norm)), rho);
+    } else {
+        conv_silu<D>(r, sm.wk, cgi, y, ss);
         // xi = -ln2 inv y',  mean xi^2 = ln^2 2 inv^2 ||y'||^2 / D, with inv the
         // reciprocal of ||y||^2 + eps (or of its square root for the unit-norm map)
         const float tot = reduce_scatter8<Cfg<D>::CP>(ss);
@@ -839,11 +852,21 @@ __device__ __forceinline__ void fm_values(const uint32_t (&r)[8], const SM& sm, 
 //   o_t = omega_t (P~ Z_v + Re X Gamma)_t,
 //   omega_t = 4 Delta / (kappa r_t (ln^2 2 ||y'||^2 + eps))  (the root of the
 // bracket for the unit-norm map); odt = 4 Delta / kappa.
+// With pre (random Fourier features), slots 3..10 of r hold the features xi_q
+// themselves as fp16 pairs, of norm one: they are the operand as they stand
+// (r_t = 1), and omega_t = 1 / (K kappa^2) = -odt / ln 2 makes omega_t K xi_q =
+// xi_q / kappa^2, what the scaled y' gives the SiLU maps.
 template <int D, class SM>
 __device__ __forceinline__ void fm_queries(half2v (&yo)[8], const uint32_t (&r)[11], SM& sm, float* om,
-                                           float eps_feat, float odt, bool unit, int fi = feat_index<D>()) {
+                                           float eps_feat, float odt, bool unit, bool pre, int fi = feat_index<D>()) {
     if (fi >= Cfg<D>::NF) return;
     const int cgi = fi % Cfg<D>::CP, tb = fi / Cfg<D>::CP;
+    if (pre) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) yo[s] = __builtin_bit_cast(half2v, r[3 + s]);
+        if (cgi < 8) om[8 * tb + scatter_token(cgi)] = -odt * (1.f / kLn2);
+        return;
+    }
     float y[2][8], ss[8], rs[8];
     conv_silu<D>(r, sm.wq, cgi, y, ss);
     const float tot = reduce_scatter8<Cfg<D>::CP>(ss);
@@ -867,6 +890,167 @@ __device__ __forceinline__ void fm_write_q(const half2v (&yo)[8], const void* yq
     const uint32_t y0 = 2u * yq_off<D>(8 * tb, 2 * cgi);
 #pragma unroll
     for (int s = 0; s < 8; ++s) *(lds_h2*)(uintptr_t)(lds_addr(yq) + (y0 ^ yq_sx<D>(s)) + s * kYqRow<D>) = yo[s];
+}
+
+// ------------------------------------------------------------------ random Fourier features
+// Channel pair cp of the tokens TPT tg - 3 .. TPT tg + TPT - 1 of the 64-token
+// tile at t0 of one (b, h) sequence (rs: a buffer resource over it, token
+// stride rsb bytes; positions before 0 or past the end read zeros); at the
+// start of the sequence the positions before it come from the stored tail
+// (tl: that operand's [W-1][D] part of the (b, h) tail, or nullptr).
+template <int D, int TPT>
+__device__ __forceinline__ void rff_load_raw(uint32_t (&rv)[TPT + 3], __amdgpu_buffer_rsrc_t rs, int rsb,
+                                             const uint16_t* __restrict__ tl, int W, int64_t t0, int cp, int tg) {
+    const uint32_t lane_b = static_cast<uint32_t>(4 * cp + (TPT * tg - 3) * rsb);
+#pragma unroll
+    for (int s2 = 0; s2 < TPT + 3; ++s2)
+        rv[s2] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane_b + static_cast<uint32_t>((t0 + s2) * rsb), 0, 0);
+    if (t0 == 0 && TPT * tg < 3 && tl != nullptr) {
+#pragma unroll
+        for (int s2 = 0; s2 < 3; ++s2) {
+            const int pos = TPT * tg + s2 - 3;
+            if (pos < 0 && pos >= -(W - 1)) rv[s2] = reinterpret_cast<const uint32_t*>(tl + ((W - 1) + pos) * D)[cp];
+        }
+    }
+}
+
+// xi_w(x) = [cos(w_f^T x), sin(w_f^T x)]_f / sqrt(F) of the conv output x, with
+// F = D/2 frequencies per head (the columns of rff_omega[h], d x F), written
+// for queries and keys as fp16 [B][N][H][D] (the token layout of q), from
+// which the feature pass and the forward read them in place of conv + SiLU.
+// Grid (ceil(N / (64 tpb)), B H), one wave per (token tile, frequency tile)
+// of a 64-token tile (1024 threads for D = 128, 512 for D = 64); a block takes
+// tpb 64-token tiles of one (b, h), one after another, with tpb chosen so
+// that the blocks fill the chip about once (the Omega fragments are loaded
+// once per block).  The phases are one [F x D] x [D x 64] product
+// per operand and 64 tokens on the matrix cores, in fp16 with both factors
+// split into high and low parts (three products: hi hi + hi lo + lo hi, fp32
+// accumulation), which keeps the phase to about 2^-21 of its terms; cos and
+// sin then take the phase in revolutions reduced to [-1/2, 1/2].  Each wave
+// keeps the Omega^T fragments of its frequency tile in registers for the
+// whole block; the features go through shared memory to 16-byte stores.
+template <int D>
+constexpr int kRffThreads = 4 * (D / 32) * 64;
+template <int D>
+__global__ __launch_bounds__(kRffThreads<D>) void rff_features_kernel(Problem p, idattn_params prm,
+                                                                   const uint16_t* __restrict__ q,
+                                                                   const uint16_t* __restrict__ k,
+                                                                   const uint16_t* __restrict__ tail_in,
+                                                                   _Float16* __restrict__ xq,
+                                                                   _Float16* __restrict__ xk, int tpb) {
+    constexpr int NT = kRffThreads<D>;
+    constexpr int F = D / 2;               // frequencies
+    constexpr int KB = D / 32;             // K steps
+    constexpr int AP = D + 8;              // row length (halfs) of the [t][channel] tiles: 16-byte
+                                           // reads of 16 rows fall on 16 distinct groups of banks
+    constexpr int NCP = D / 2;             // channel pairs
+    constexpr int TG = NT / NCP;           // token groups
+    constexpr int TPT = L / TG;            // tokens per thread
+    __shared__ _Float16 ah[2][L * AP], al[2][L * AP];  // conv output [t][c], high and low parts (q, k)
+    __shared__ _Float16 xo[2][L * AP];                 // features [t][f] on their way out (q, k)
+    const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, g = ln >> 4, i = ln & 15;
+    const int tw = wv & 3, fw = wv >> 2;   // token tile, frequency tile
+    const int64_t bhi = blockIdx.y, b = bhi / p.H, h = bhi % p.H, H = p.H, N = p.N;
+    const int W = static_cast<int>(p.W);
+    // Omega^T fragments, rows f = 16 ft + i, K = 32 kb + 8 g + j
+    half8 oh[KB], ol[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int f = 16 * fw + i, c = 32 * kb + 8 * g + j;
+            const float x = prm.rff_omega[(h * D + c) * F + f];
+            const _Float16 hi = static_cast<_Float16>(x);
+            oh[kb][j] = hi;
+            ol[kb][j] = static_cast<_Float16>(x - static_cast<float>(hi));
+        }
+    // conv taps of the thread's channel pair, right-aligned: tap j multiplies token t - 3 + j
+    const int cp = tid % NCP, tg = tid / NCP;
+    float wt[2][2][kMaxW];  // [q, k][channel 2 cp + e][tap]
+#pragma unroll
+    for (int j = 0; j < kMaxW; ++j) {
+        const int tap = j - (kMaxW - W);
+        const bool on = tap >= 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            wt[0][e][j] = on ? prm.conv_q[(h * D + 2 * cp + e) * W + tap] : 0.f;
+            wt[1][e][j] = on ? prm.conv_k[(h * D + 2 * cp + e) * W + tap] : 0.f;
+        }
+    }
+    const float inv_sqrt_f = 1.f / sqrtf(static_cast<float>(F));
+    // the (b, h) tail: queries' part, then keys'
+    const uint16_t* tlq = tail_in != nullptr ? tail_in + (b * H + h) * 2 * (W - 1) * D : nullptr;
+    const uint16_t* tlk = tail_in != nullptr ? tlq + (W - 1) * D : nullptr;
+    const int rsb = static_cast<int>(H * D * 2);  // token stride, bytes
+    const __amdgpu_buffer_rsrc_t rq = seq_rsrc<D>(q, b * N, h, H, N), rk = seq_rsrc<D>(k, b * N, h, H, N);
+    const __amdgpu_buffer_rsrc_t oq = seq_rsrc<D>(reinterpret_cast<const uint16_t*>(xq), b * N, h, H, N);
+    const __amdgpu_buffer_rsrc_t ok = seq_rsrc<D>(reinterpret_cast<const uint16_t*>(xk), b * N, h, H, N);
+    // tiles of 64 tokens, queries and keys together; the raw values of tile + 1 are
+    // loaded while tile runs its products
+    const int64_t tb0 = static_cast<int64_t>(blockIdx.x) * tpb * L;
+    const int ntl = static_cast<int>(N - tb0 < static_cast<int64_t>(tpb) * L ? (N - tb0 + L - 1) / L : tpb);
+    uint32_t rv[2][TPT + 3];
+    rff_load_raw<D, TPT>(rv[0], rq, rsb, tlq, W, tb0, cp, tg);
+    rff_load_raw<D, TPT>(rv[1], rk, rsb, tlk, W, tb0, cp, tg);
+    for (int tl = 0; tl < ntl; ++tl) {
+        const int64_t t0 = tb0 + static_cast<int64_t>(tl) * L;
+        const int n = static_cast<int>(N - t0 < L ? N - t0 : L);
+#pragma unroll
+        for (int sel = 0; sel < 2; ++sel)
+#pragma unroll
+            for (int s2 = 0; s2 < TPT; ++s2) {
+                float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+                for (int j = 0; j < kMaxW; ++j) {
+                    a0 = fmaf(wt[sel][0][j], lo_bf16(rv[sel][s2 + j]), a0);
+                    a1 = fmaf(wt[sel][1][j], hi_bf16(rv[sel][s2 + j]), a1);
+                }
+                const int t = TPT * tg + s2;
+                const _Float16 h0 = static_cast<_Float16>(a0), h1 = static_cast<_Float16>(a1);
+                *reinterpret_cast<half2v*>(&ah[sel][t * AP + 2 * cp]) = half2v{h0, h1};
+                *reinterpret_cast<half2v*>(&al[sel][t * AP + 2 * cp]) = half2v{
+                    static_cast<_Float16>(a0 - static_cast<float>(h0)), static_cast<_Float16>(a1 - static_cast<float>(h1))};
+            }
+        if (tl + 1 < ntl) {
+            rff_load_raw<D, TPT>(rv[0], rq, rsb, tlq, W, t0 + L, cp, tg);
+            rff_load_raw<D, TPT>(rv[1], rk, rsb, tlk, W, t0 + L, cp, tg);
+        }
+        lds_barrier();  // conv tiles written; the last tile's stores have read xo (the prefetch stays in flight)
+        // phases of frequencies 16 fw + 4 g + jj and token 16 tw + i, queries then keys
+#pragma unroll
+        for (int sel = 0; sel < 2; ++sel) {
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int bo = (16 * tw + i) * AP + 32 * kb + 8 * g;
+                const half8 c_h = rd8(lds_addr(ah[sel]) + 2 * bo), c_l = rd8(lds_addr(al[sel]) + 2 * bo);
+                acc = mfma(oh[kb], c_h, acc);
+                acc = mfma(oh[kb], c_l, acc);
+                acc = mfma(ol[kb], c_h, acc);
+            }
+            float cs[4], sn[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                float r = acc[jj] * 0.15915494309189535f;  // revolutions
+                r -= rintf(r);
+                cs[jj] = __builtin_amdgcn_cosf(r) * inv_sqrt_f;
+                sn[jj] = __builtin_amdgcn_sinf(r) * inv_sqrt_f;
+            }
+            const int f0 = 16 * fw + 4 * g, row = (16 * tw + i) * AP;
+            wr4(lds_addr(xo[sel]) + 2 * (row + f0), cs[0], cs[1], cs[2], cs[3]);
+            wr4(lds_addr(xo[sel]) + 2 * (row + F + f0), sn[0], sn[1], sn[2], sn[3]);
+        }
+        lds_barrier();  // features staged; every wave is past its reads of the conv tiles
+#pragma unroll
+        for (int sel = 0; sel < 2; ++sel)
+            for (int e = tid; e < L * (D / 8); e += NT) {
+                const int t = e / (D / 8), ch = e % (D / 8);
+                if (t < n)  // (the resource ends at the sequence's last token as well)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(u4, rd8(lds_addr(xo[sel]) + 2 * (t * AP + 8 * ch))), sel == 0 ? oq : ok,
+                        static_cast<uint32_t>((t0 + t) * rsb + 16 * ch), 0, 0);
+            }
+    }
 }
 
 // Conv weights (times -log2 e, taps right-aligned into 4 slots), gain, bias,
@@ -1330,7 +1514,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
         uint32_t rkk[11];
         fm_load<D, true>(rkk, rk, rsb, t_begin);
         halo_fix<D>(rkk, sm, 1, t_begin);
-        fm_keys<D>(rkk, sm, sm.zkT[0], nch > 1 ? L : n_last, p.eps_feat, p.eps_norm, p.unit_feat);
+        fm_keys<D>(rkk, sm, sm.zkT[0], nch > 1 ? L : n_last, p.eps_feat, p.eps_norm, p.unit_feat, p.rff_feat);
         if (nch > 1) fm_load<D, true>(rkk, rk, rsb, t_begin + L);
         lds_barrier();  // chunk 0 features
         for (int c = 0; c < nch; ++c) {
@@ -1339,7 +1523,7 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
             if (upd) key_update<D>(U, sm.aL, kw, sm.zkT[c & 1], sm.ft, tid_now() & 63);
             if (c + 1 < nch) {
                 fm_keys<D>(rkk, sm, sm.zkT[(c + 1) & 1], c + 2 < nch ? L : n_last, p.eps_feat, p.eps_norm,
-                           p.unit_feat);
+                           p.unit_feat, p.rff_feat);
                 if (c + 2 < nch) {
                     step_fence();
                     fm_load<D, true>(rkk, rk, rsb, t0 + 2 * L);
@@ -1551,6 +1735,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                                                               const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v,
+                                                              const uint16_t* __restrict__ qf,
                                                               const _Float16* __restrict__ zt, uint16_t* __restrict__ o,
                                                               const float* state_in, const uint16_t* tail_in,
                                                               float* state_out, uint16_t* tail_out,
@@ -1651,13 +1836,13 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
             else u_load<D>(U, nullptr, kw, 1.f);
             if (nfold > 0) u_fold<D, kFoldTiles>(U, e0, estride, nfold, aseg, kw);
         }
-        const __amdgpu_buffer_rsrc_t rq = seq_rsrc<D>(q, wk.t0, h, H, t_end);
+        const __amdgpu_buffer_rsrc_t rq = seq_rsrc<D>(qf, wk.t0, h, H, t_end);  // raw q, or its features
         uint32_t rqq[11];  // raw queries of the chunk after the next
         fm_load<D, true>(rqq, rq, rsb, t_begin);
         halo_fix<D>(rqq, sm, 0, t_begin);
         {
             half2v yo[8];
-            fm_queries<D>(yo, rqq, sm, sm.om[0], p.eps_feat, odt, p.unit_feat);
+            fm_queries<D>(yo, rqq, sm, sm.om[0], p.eps_feat, odt, p.unit_feat, p.rff_feat);
             fm_write_q<D>(yo, sm.yq);
         }
         if (nch > 1) fm_load<D, true>(rqq, rq, rsb, t_begin + L);
@@ -1804,7 +1989,7 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
                 // (c+1) mod 3 (last read in phase 2 of step c-1); the raw tokens of c+2 follow
                 step_fence();
                 half2v yo[8];
-                fm_queries<D>(yo, rqq, sm, sm.om[(c + 1) % 3], p.eps_feat, odt, p.unit_feat);
+                fm_queries<D>(yo, rqq, sm, sm.om[(c + 1) % 3], p.eps_feat, odt, p.unit_feat, p.rff_feat);
                 fm_write_q<D>(yo, sm.yq);
                 if (c + 2 < nch) {
                     step_fence();
@@ -1955,9 +2140,10 @@ void plan_segments(const Problem& p, int& S, int64_t& Lseg) {
 // Workspace: the packed plan (packed batches only) | per-head tables | the
 // staged kappa state_in, [B H] states in lane order | the staged eta_in,
 // [B H][M] complex | segment end states, S_b - 1 per (b, h) | fp16 key-feature
-// tiles, one z_k^T per chunk slot.
+// tiles, one z_k^T per chunk slot | (random Fourier features) xi_q and xi_k,
+// fp16 [B][N][H][D] each.
 struct WsLayout {
-    size_t plan, tab, c0, c0eta, seg, zt, total;
+    size_t plan, tab, c0, c0eta, seg, zt, rff, total;
 };
 WsLayout ws_layout_parts(const Problem& p, size_t plan_bytes, size_t end_states, size_t chunk_slots) {
     const size_t state = static_cast<size_t>(MM) * 2 * p.d * 2 * sizeof(float);
@@ -1969,7 +2155,8 @@ WsLayout ws_layout_parts(const Problem& p, size_t plan_bytes, size_t end_states,
     w.c0eta = w.c0 + pairs * state;
     w.seg = w.c0eta + ((pairs * MM * 8 + 255) / 256) * 256;
     w.zt = w.seg + end_states * state;
-    w.total = w.zt + chunk_slots * L * p.d * sizeof(_Float16);
+    w.rff = w.zt + chunk_slots * L * p.d * sizeof(_Float16);
+    w.total = w.rff + (p.rff_feat ? 2 * static_cast<size_t>(p.B * p.N * p.H * p.d) * sizeof(_Float16) : 0);
     return w;
 }
 // Dense: S segments of Lseg tokens per (b, h).
@@ -2019,11 +2206,26 @@ hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, con
     float2* c0eta = reinterpret_cast<float2*>(base + lay.c0eta);
     float* ws = reinterpret_cast<float*>(base + lay.seg);
     _Float16* zt = reinterpret_cast<_Float16*>(base + lay.zt);
+    const uint16_t* qf = q16;  // the queries' and keys' feature sources
+    const uint16_t* kf = k16;
+    if (p.rff_feat) {  // dense batches only (chunked_packed_supported)
+        _Float16* xq = reinterpret_cast<_Float16*>(base + lay.rff);
+        _Float16* xk = xq + p.B * p.N * p.H * p.d;
+        const int64_t tiles = (p.N + L - 1) / L;  // per (b, h)
+        int64_t tpb = (tiles * pairs + 255) / 256;  // tiles per block: about one block per compute unit
+        tpb = tpb < 1 ? 1 : tpb > tiles ? tiles : tpb;
+        rff_features_kernel<D><<<dim3(static_cast<unsigned>((tiles + tpb - 1) / tpb), static_cast<unsigned>(pairs)),
+                                 kRffThreads<D>, 0, stream>>>(p, prm, q16, k16, t16, xq, xk, static_cast<int>(tpb));
+        hipError_t e0 = hipGetLastError();
+        if (e0 != hipSuccess) return e0;
+        qf = reinterpret_cast<const uint16_t*>(xq);
+        kf = reinterpret_cast<const uint16_t*>(xk);
+    }
     zoh_tables_kernel<<<dim3(static_cast<unsigned>(p.H), 17), kTabThreads, 0, stream>>>(p, prm, Lseg, tab, cu, plan);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     segment_state_kernel<D><<<dim3(static_cast<unsigned>(grid)), NTH, 0, stream>>>(
-        p, prm, k16, v16, t16, state_in, tab, c0, ws, zt, Lseg, S, eta_in, eta_out, c0eta, plan);
+        p, prm, kf, v16, t16, state_in, tab, c0, ws, zt, Lseg, S, eta_in, eta_out, c0eta, plan);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // the carry kernel: dense with more segments than the forward folds; packed
@@ -2041,11 +2243,11 @@ hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, con
     }
     if (p.eta)
         chunked_forward_kernel<D, true><<<dim3(static_cast<unsigned>(grid)), NTH, 0, stream>>>(
-            p, prm, q16, k16, v16, zt, static_cast<uint16_t*>(o), state_in, t16, state_out,
+            p, prm, q16, k16, v16, qf, zt, static_cast<uint16_t*>(o), state_in, t16, state_out,
             static_cast<uint16_t*>(tail_out), tab, c0, ws, Lseg, S, c0eta, eta_in != nullptr, plan);
     else
         chunked_forward_kernel<D, false><<<dim3(static_cast<unsigned>(grid)), NTH, 0, stream>>>(
-            p, prm, q16, k16, v16, zt, static_cast<uint16_t*>(o), state_in, t16, state_out,
+            p, prm, q16, k16, v16, qf, zt, static_cast<uint16_t*>(o), state_in, t16, state_out,
             static_cast<uint16_t*>(tail_out), tab, c0, ws, Lseg, S, c0eta, false, plan);
     return hipGetLastError();
 }
@@ -2054,9 +2256,9 @@ hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, con
 }  // namespace cws
 
 bool chunked_supported(const Problem& p) {
-    // M = 64 modes, d = R in {64, 128}, conv width up to 4, the SiLU feature maps
+    // M = 64 modes, d = R in {64, 128}, conv width up to 4; any feature map (random
+    // Fourier features through a pre-pass)
     if (!(p.bf16 && p.M == 64 && (p.d == 64 || p.d == 128) && p.W >= 1 && p.W <= 4)) return false;
-    if (p.rff_feat) return false;
     // the kernels address one (b, h) sequence with 32-bit byte offsets
     return p.N * p.H * p.d * 2 < (int64_t{1} << 31);
 }
@@ -2070,7 +2272,8 @@ size_t chunked_workspace_bytes(const Problem& p) {
 
 bool chunked_packed_supported(const Problem& p) {
     // the plan's int32 entries: block counts up to 256 + B H and token offsets up to T
-    return chunked_supported(p) && p.B * p.H <= (int64_t{1} << 22) && p.N < (int64_t{1} << 31);
+    // (random Fourier features: dense batches only, their pre-pass has no plan)
+    return chunked_supported(p) && !p.rff_feat && p.B * p.H <= (int64_t{1} << 22) && p.N < (int64_t{1} << 31);
 }
 
 size_t chunked_packed_workspace_bytes(const Problem& p) { return cws::ws_layout_packed(p).total; }

@@ -84,9 +84,10 @@ typedef enum idattn_algo {
  * the columns of Omega_h = params->rff_omega[h], shared by queries and keys,
  * with the cosine half first and a 1/sqrt(D) factor so that xi(x) . xi(x') is
  * the mean of cos(w^T (x - x')) over the D frequencies.  The caller draws the
- * frequencies; eps_feat is unused with it.  The chunked algorithm has no
- * kernel for IDATTN_FEATURE_RFF (IDATTN_ERR_UNSUPPORTED; AUTO picks the
- * sequential one). */
+ * frequencies; eps_feat is unused with it.  The chunked algorithm computes
+ * these features in a pre-pass (phases on the matrix cores in split fp16,
+ * features stored in fp16 in the workspace) for dense batches; packed
+ * batches with it run the sequential algorithm. */
 typedef enum idattn_feature_norm {
     IDATTN_FEATURE_SQUARED = 0,  /* xi = y / (||y||^2 + eps_feat)        (default) */
     IDATTN_FEATURE_UNIT = 1,     /* xi = y / sqrt(||y||^2 + eps_feat)              */
@@ -198,7 +199,7 @@ idattn_status idattn_forward_noalloc(const idattn_dims *dims, const idattn_param
  *  all other arguments as for idattn_forward; the workspace is
  *  idattn_forward_normalized_workspace_size bytes.
  * dims->algo: AUTO takes the chunked algorithm wherever idattn_forward has it
- * (bf16, d in {64, 128}, M = 64, W <= 4, not the RFF map), else the
+ * (bf16, d in {64, 128}, M = 64, W <= 4), else the
  * sequential one; CHUNKED elsewhere returns IDATTN_ERR_UNSUPPORTED.  The
  * chunked algorithm forms the denominator in fp32 from the mode scores before
  * their fp16 rounding and eta in closed form (fp64), so eta_out is exact to

@@ -189,18 +189,23 @@ def test_decode_validation():
 
 
 def test_rff_feature_map_validation():
-    """The RFF map needs its frequencies, has no chunked kernel (AUTO takes the
-    sequential path), and its frequency table counts as a parameter for the
-    overlap checks.  Without the flag the table is not looked at: a NULL
-    rff_omega passes on to the next check (here a short workspace)."""
+    """The RFF map needs its frequencies; on the chunked path (which AUTO takes
+    for bf16 where it has a kernel) its workspace adds the fp16 features of
+    queries and keys, B N H d halves each; its frequency table counts as a
+    parameter for the overlap checks.  Without the flag the table is not
+    looked at: a NULL rff_omega passes on to the next check (here a short
+    workspace)."""
     d = dims(feature_norm="rff", M=64, d=128)
     expect(call_forward(d, params(rff_omega=0)), "IDATTN_ERR_NULL")
     expect(call_forward(dims(M=64, d=128), params(rff_omega=0), ws_bytes=1), "IDATTN_ERR_WORKSPACE")
-    with pytest.raises(fs.IdattnError) as e:
-        fs.idattn_forward_workspace_size(dims(feature_norm="rff", M=64, d=128, algo="chunked"))
+    chunked = fs.idattn_forward_workspace_size(dims(feature_norm="rff", M=64, d=128, algo="chunked"))
+    assert chunked == fs.idattn_forward_workspace_size(dims(M=64, d=128, algo="chunked")) + 2 * 2 * 64 * 3 * 128 * 2
+    assert fs.idattn_forward_workspace_size(d) == chunked
+    assert fs.idattn_forward_workspace_size(dims(feature_norm="rff", M=64, d=128, io="f32")) == \
+        fs.idattn_forward_workspace_size(dims(feature_norm="rff", M=64, d=128, algo="sequential", io="f32"))
+    with pytest.raises(fs.IdattnError) as e:  # packed batches with it have no chunked kernel
+        fs.idattn_forward_varlen_workspace_size(dims(feature_norm="rff", M=64, d=128, algo="chunked"))
     assert e.value.status_name == "IDATTN_ERR_UNSUPPORTED"
-    assert fs.idattn_forward_workspace_size(d) == fs.idattn_forward_workspace_size(
-        dims(feature_norm="rff", M=64, d=128, algo="sequential"))
     om = params().rff_omega
     table = 3 * 128 * 64 * 4  # H d (d/2) floats
     expect(call_forward(d, params(), o=om + table - 16), "IDATTN_ERR_ALIAS")   # o over the table's end

@@ -142,10 +142,12 @@ def test_decode_step_unit_feature_map(fs, io):
 
 # Random Fourier features (Chinese rendering, section 3.1, eq. 6): the
 # sequential path of every d (D = d/2 = 8 .. 64 frequencies) from a given state
-# and tail; AUTO must take the sequential path for bf16 as well, since the
-# chunked kernels have no RFF map.  Phases are of order 2 (up to about 10).
+# and tail, and under AUTO the chunked path where it has a kernel (bf16, d 64 or
+# 128, M = 64, W <= 4: the RFF pre-pass feeds the chunked kernels), including
+# the folded carry over four segments.  Phases are of order 2 (up to about 10).
 RFF = ["tiny_f32", "d16_m64_w2_f32", "d32_m16_bf16", "d64_m32_ragged_bf16", "d64_m64_ragged_f32",
-       "d128_m64_ragged_bf16", "d128_m16_f32", "d128_w8_bf16"]
+       "d128_m64_ragged_bf16", "d128_m16_f32", "d128_w8_bf16", "d64_w1_bf16", "d128_w2_bf16", "d64_w3_bf16",
+       "d128_segments_bf16", "d64_segments_bf16"]
 
 
 @pytest.mark.parametrize("name", RFF)
@@ -739,9 +741,8 @@ def test_full_config_all_pairs(fs, cfg):
 @pytest.mark.parametrize("variant", ["unit", "rff", "normalized"])
 def test_full_shape_variants_sampled_pairs(fs, variant):
     """The feature-map and readout variants at the full 1.3B shape (B=4 H=16
-    N=4096 d=128 M=64, bf16 I/O): unit-norm map and normalised readout on the
-    chunked path, RFF map on the sequential path; the oracle recomputes two
-    (b, h) sequences end to end."""
+    N=4096 d=128 M=64, bf16 I/O), all on the chunked path (RFF through its
+    pre-pass); the oracle recomputes two (b, h) sequences end to end."""
     import torch
     s = WL.spec("1p3b")
     q, k, v = WL.make_rows(s)
