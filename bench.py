@@ -71,15 +71,33 @@ def committed_traffic(config: str, algo: str):
 
 
 def plan_segments(B, N, H, L=64):
-    """The chunked forward's time split (the library's plan): S segments of
-    Lseg tokens per (b, h) so that B H S is about one workgroup per CU."""
-    pairs = B * H
-    chunks = (N + L - 1) // L
-    s = max(1, 256 // pairs)
-    s = min(s, chunks) if chunks > 0 else 1
-    cps = (chunks + s - 1) // s
-    lseg = cps * L
-    return max(1, (N + lseg - 1) // lseg), lseg
+    """The chunked forward's time split of a dense batch, as the library plans
+    it: S segments of Lseg tokens per (b, h), the segment size (in chunks)
+    with the least modelled makespan on 256 compute units (full segments
+    dispatched first, then the shorter last ones; 1.5 chunk times of fixed
+    work per workgroup), searched from half to twice the even split."""
+    import heapq
+    P, c = B * H, (N + L - 1) // L
+    if c <= 1:
+        return 1, L
+
+    def makespan(C):
+        S = -(-c // C)
+        loads = [0.0] * 256
+        for size in [C] * (P * (S - 1)) + [c - (S - 1) * C] * P:
+            heapq.heappush(loads, heapq.heappop(loads) + size + 1.5)
+        return max(loads)
+
+    even = -(-P * c // 256)
+    lo, hi = max(1, even // 2), min(2 * even, c)
+    lo = min(lo, hi)
+    step = (hi - lo) // 512 + 1
+    best, best_t = c, makespan(c)
+    for C in range(hi, lo - 1, -step):
+        t = makespan(C)
+        if t < best_t - 1e-9:
+            best, best_t = C, t
+    return -(-c // best), best * L
 
 
 def chunked_mfma_flops(B, N, H, d, L=64):

@@ -581,8 +581,10 @@ struct WinOff {
 
 // ------------------------------------------------------------------ work of a block
 // A block runs one segment of one (b, h) sequence.  Dense batches (plan ==
-// nullptr): blockIdx = (b H + h) S + seg, sequence b at token b N of the token
-// axis, N tokens, S segments of Lseg tokens each (the last one ragged).
+// nullptr): sequence b at token b N of the token axis, N tokens, S segments
+// of Lseg tokens each (the last one shorter or ragged); blocks 0..F-1 run
+// the F = B H (S - 1) full segments in ((b, h), seg) order, blocks F.. the
+// last segments in (b, h) order, so that the short ones are dispatched last.
 // Packed batches: the plan (built on the device from the sequence table)
 // gives every sequence its first token, length and segment count S_b, all
 // segments of C chunks but each sequence's last.  Blocks 0..F-1 run the F =
@@ -607,8 +609,14 @@ __device__ __forceinline__ Blk block_work(const Problem& p, const int32_t* plan,
     Blk k;
     const int64_t x = blockIdx.x;
     if (plan == nullptr) {
-        k.bh = x / S_dense;
-        k.seg = static_cast<int>(x % S_dense);
+        const int64_t F = p.B * p.H * (S_dense - 1);  // full segments, dispatched first
+        if (x < F) {
+            k.bh = x / (S_dense - 1);
+            k.seg = static_cast<int>(x % (S_dense - 1));
+        } else {
+            k.bh = x - F;
+            k.seg = S_dense - 1;
+        }
         k.S = S_dense;
         k.b = k.bh / p.H;
         k.h = k.bh % p.H;
@@ -2125,16 +2133,87 @@ __global__ __launch_bounds__(NTH) void chunked_forward_kernel(Problem p, idattn_
     }
 }
 
+// Makespan, in chunk times, of P (b, h) sequences of c chunks each cut into
+// segments of C chunks (the last one r = c - (S - 1) C) on kCUs compute units
+// with one workgroup each at a time, when the full segments are dispatched
+// first and the last segments after them (block_work's order): every
+// workgroup costs its chunks plus kBlockCost of fixed work (prologue, state
+// load and store).  The dispatcher hands each next workgroup to the unit
+// that frees first, so the full segments spread evenly and the last ones
+// fill the lowest loads first.
+constexpr int kCUs = 256;
+constexpr double kBlockCost = 1.5;
+double plan_makespan(int64_t P, int64_t c, int64_t C) {
+    const int64_t S = (c + C - 1) / C, r = c - (S - 1) * C;
+    const double a = static_cast<double>(C) + kBlockCost, b = static_cast<double>(r) + kBlockCost;
+    const int64_t nf = P * (S - 1), q = nf / kCUs, rem = nf % kCUs;
+    // loads: (kCUs - rem) units at q a, rem units at (q + 1) a; then P last segments
+    double lvl[2] = {static_cast<double>(q) * a, static_cast<double>(q + 1) * a};
+    int64_t cnt[2] = {kCUs - rem, rem};
+    int64_t left = P;
+    double top = rem > 0 ? lvl[1] : lvl[0];
+    // water-fill: the units at the lowest level take one segment each; a level
+    // that rises past the other one swaps roles with it
+    while (left > 0) {
+        const int lo = (cnt[0] > 0 && (cnt[1] == 0 || lvl[0] <= lvl[1])) ? 0 : 1;
+        const int64_t t = cnt[lo] < left ? cnt[lo] : left;
+        left -= t;
+        const double nv = lvl[lo] + b;
+        top = nv > top ? nv : top;
+        if (t == cnt[lo]) {
+            lvl[lo] = nv;  // the whole level moves up
+        } else {           // part of it: those units join a new level above
+            const int hi = 1 - lo;
+            if (cnt[hi] == 0 || lvl[hi] == nv) {
+                lvl[hi] = nv;
+                cnt[hi] += t;
+                cnt[lo] -= t;
+            } else {
+                // three distinct levels: the remaining units of lo are the lowest
+                // and receive nothing more (left is 0 here, since t < cnt[lo])
+                cnt[lo] -= t;
+            }
+        }
+        if (cnt[0] == 0 && cnt[1] == 0) break;
+    }
+    return top;
+}
+
+// Segments of Lseg tokens per (b, h), S of them: the segment size (in chunks)
+// that minimises plan_makespan over sizes from half to twice the even split
+// P c / kCUs (at most 512 of them, evenly spaced), ties going to fewer
+// segments.  Remembered for the last shape asked.
 void plan_segments(const Problem& p, int& S, int64_t& Lseg) {
-    const int64_t pairs = p.B * p.H;
-    const int64_t chunks = (p.N + L - 1) / L;
-    int64_t s = 256 / pairs;  // one workgroup per compute unit
-    if (s < 1) s = 1;
-    if (s > chunks) s = chunks > 0 ? chunks : 1;
-    const int64_t cps = (chunks + s - 1) / s;
-    Lseg = cps * L;
-    S = static_cast<int>((p.N + Lseg - 1) / Lseg);
-    if (S < 1) S = 1;
+    const int64_t P = p.B * p.H;
+    const int64_t c = (p.N + L - 1) / L;
+    if (c <= 1) {
+        S = 1;
+        Lseg = L;
+        return;
+    }
+    static thread_local int64_t memo_P = -1, memo_c = -1, memo_C = 1;
+    int64_t best = c;
+    if (P == memo_P && c == memo_c) {
+        best = memo_C;
+    } else {
+        const int64_t even = (P * c + kCUs - 1) / kCUs;
+        int64_t lo = even / 2 > 1 ? even / 2 : 1, hi = 2 * even < c ? 2 * even : c;
+        if (lo > hi) lo = hi;
+        const int64_t step = (hi - lo) / 512 + 1;
+        double best_t = plan_makespan(P, c, c);
+        for (int64_t C = hi; C >= lo; C -= step) {  // larger sizes first: ties keep fewer segments
+            const double t = plan_makespan(P, c, C);
+            if (t < best_t - 1e-9) {
+                best_t = t;
+                best = C;
+            }
+        }
+        memo_P = P;
+        memo_c = c;
+        memo_C = best;
+    }
+    Lseg = best * L;
+    S = static_cast<int>((c + best - 1) / best);
 }
 
 // Workspace: the packed plan (packed batches only) | per-head tables | the

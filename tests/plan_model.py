@@ -71,3 +71,44 @@ def plan_array(lens, H: int) -> list:
     cap = carry_cap(H)
     head = [p["C"], p["blocks"], min(len(p["carry"]), cap), p["full"]]
     return head + p["start"] + p["len"] + p["S"] + p["coff"] + p["soff"] + p["order"] + p["carry"][:cap]
+
+
+# ---------------------------------------------------------------- dense batches
+CUS = 256
+BLOCK_COST = 1.5  # fixed work of a workgroup, in chunk times
+
+
+def dense_makespan(P: int, c: int, C: int) -> float:
+    """Chunk times to run P sequences of c chunks in segments of C chunks on
+    256 units, one workgroup each at a time, full segments first and the
+    shorter last segments after them, each next workgroup on the unit that
+    frees first (a plain simulation)."""
+    import heapq
+    S = -(-c // C)
+    r = c - (S - 1) * C
+    loads = [0.0] * CUS
+    for size in [C] * (P * (S - 1)) + [r] * P:
+        t = heapq.heappop(loads)
+        heapq.heappush(loads, t + size + BLOCK_COST)
+    return max(loads)
+
+
+def dense_plan(B: int, H: int, N: int) -> tuple:
+    """(S, C): the segment count and size in chunks of a dense batch: the C
+    with the least makespan among sizes from half to twice the even split
+    (at most 512 of them, evenly spaced), ties to fewer segments."""
+    P, c = B * H, -(-N // L)
+    if c <= 1:
+        return 1, 1
+    even = -(-P * c // CUS)
+    lo, hi = max(1, even // 2), min(2 * even, c)
+    lo = min(lo, hi)
+    step = (hi - lo) // 512 + 1
+    best, best_t = c, dense_makespan(P, c, c)
+    C = hi
+    while C >= lo:
+        t = dense_makespan(P, c, C)
+        if t < best_t - 1e-9:
+            best, best_t = C, t
+        C -= step
+    return -(-c // best), best

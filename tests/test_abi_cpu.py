@@ -397,6 +397,30 @@ def test_varlen_workspace_covers_the_plan(H, d):
     assert sizes == sorted(sizes)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_dense_chunked_plan_matches_model(d):
+    """The chunked forward's time split of a dense batch (segment count S and
+    size C chunks, chosen by the library's makespan model) equals the plan
+    model's, read through the workspace size: with c = 1 chunk the workspace
+    is a fixed part plus one tile per (b, h); otherwise it adds S - 1 end
+    states and S C tiles per (b, h).  Also the makespan the model minimises,
+    for the 125M, 1.3B and 14K shapes: 26 x 3, 16 x 4 and 14 x 16."""
+    from tests import plan_model as PM
+    state = 64 * 2 * d * 2 * 4
+    tile = 64 * d * 2
+    for B, H, N in [(8, 12, 4096), (4, 16, 4096), (1, 16, 14336), (8, 16, 700), (8, 12, 700), (4, 16, 200),
+                    (1, 2, 1000), (3, 5, 3000), (2, 1, 64 * 37 + 5), (16, 16, 2048), (64, 16, 512)]:
+        P = B * H
+        ws1 = fs.idattn_forward_workspace_size(fs.make_dims(B, 64, H, d, 64, 4, "bf16", "chunked"))
+        fixed = ws1 - P * tile
+        S, C = PM.dense_plan(B, H, N)
+        ws = fs.idattn_forward_workspace_size(fs.make_dims(B, N, H, d, 64, 4, "bf16", "chunked"))
+        assert ws == fixed + (S - 1) * P * state + P * S * C * tile, (B, H, N, S, C)
+    assert PM.dense_plan(8, 12, 4096) == (3, 26)
+    assert PM.dense_plan(4, 16, 4096) == (4, 16)
+    assert PM.dense_plan(1, 16, 14336) == (16, 14)
+
+
 def test_noalloc_validation():
     """idattn_forward_noalloc rejects, before any HIP call, dims whose
     workspace exceeds the scratch array, and the usual argument errors."""

@@ -960,12 +960,14 @@ def test_in_place_state_and_zero_tokens(fs):
     assert not st2.any() and not tl2.any()
 
 
-# (B, H, N, d) -> time segments per sequence: 1 (short, one segment), 2, 3 and 4
-# (the carry folded into the forward, the 125M and 1.3B plans) and 16 (the
-# carry kernel).
+# (B, H, N, d) -> time segments per sequence in the library's plan (modelled in
+# tests/plan_model.py): 1 (short, one segment), 2, 3 and 4 (the carry folded
+# into the forward, as in the 125M and 1.3B plans; fold_s3_uneven has segments
+# of 5, 5 and 1 chunks) and 16 (the carry kernel).
 IN_PLACE = {"n2_s1": (1, 2, 2, 128), "n50_s1": (1, 2, 50, 128), "fold_s4_d128": (4, 16, 200, 128),
-            "fold_s4_d64": (4, 16, 200, 64), "fold_s3_d128": (4, 16, 150, 128), "fold_s2_d64": (8, 12, 700, 64),
-            "carry_s16": (1, 2, 1000, 128), "carry_s16_h16": (1, 16, 1000, 128)}
+            "fold_s4_d64": (4, 16, 200, 64), "fold_s3_d128": (4, 16, 150, 128), "fold_s2_d64": (8, 16, 700, 64),
+            "fold_s3_uneven_d64": (8, 12, 700, 64), "carry_s16": (1, 2, 1000, 128),
+            "carry_s16_h16": (1, 16, 1000, 128)}
 
 
 @pytest.mark.parametrize("case", sorted(IN_PLACE))
