@@ -1580,16 +1580,17 @@ __global__ __launch_bounds__(NTH) void segment_state_kernel(Problem p, idattn_pa
 }
 
 // Carry chain over segments (states in lane order): ws[st0 + seg] <- the state
-// entering segment seg + 1.  A thread takes one group of eight consecutive
-// floats of a (b, h) state, four complex elements, and walks the segments,
-// loading the groups of up to eight segments before combining any of them so
-// that the loads overlap instead of forming a chain of dependent round trips.
-// The state entering the sequence comes from the staged copy c0.  Dense
-// batches: every (b, h) of S segments.  Packed batches: the (b, h) of the
-// sequences in the plan's carry list (those with more segments than the
-// forward folds), S_b segments each.  Grid-stride over the groups, so that
-// the grid need not match the (device-side) length of the carry list.
-constexpr int kCarryBlocks = 1024;
+// entering segment seg + 1.  One complex state element per thread (four
+// threads share the eight floats of a group: re / im of a U lane pair, or
+// two modes of a Gamma lane), walking the segments with the end states of up
+// to eight segments loaded before any of them is combined, so that the loads
+// overlap instead of forming a chain of dependent round trips.  The state
+// entering the sequence comes from the staged copy c0.  Dense batches: every
+// (b, h) of S segments.  Packed batches: the (b, h) of the sequences in the
+// plan's carry list (those with more segments than the forward folds), S_b
+// segments each.  Grid-stride over the elements, so that the grid need not
+// match the (device-side) length of the carry list.
+constexpr int kCarryBlocks = 2048;
 __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, bool has_state,
                                                             const float* __restrict__ c0,
                                                             const uint8_t* __restrict__ tab,
@@ -1597,12 +1598,12 @@ __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, bool has_
                                                             const int32_t* __restrict__ plan) {
     constexpr int kBatch = 8;
     const int D = static_cast<int>(p.d);
-    const int64_t per = 32 * D;  // groups of eight floats per (b, h) state (256 D floats)
+    const int64_t per = 128 * D;  // threads per (b, h): one complex element each
     const int64_t npairs = plan == nullptr ? p.B * p.H : static_cast<int64_t>(plan[2]) * p.H;
     const int64_t sst = 256 * D;  // floats per state
-    for (int64_t gi = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; gi < npairs * per;
-         gi += static_cast<int64_t>(gridDim.x) * 256) {
-        const int64_t j = gi / per;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < npairs * per;
+         e += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t j = e / per;
         int64_t bh, st0;
         int S;
         if (plan == nullptr) {
@@ -1617,65 +1618,36 @@ __global__ __launch_bounds__(256) void segment_carry_kernel(Problem p, bool has_
             st0 = p.H * static_cast<int64_t>(plan[kPlanHead + 4 * B + b]) + hh * (S - 1);
         }
         const int64_t h = bh % p.H;
-        const int o = static_cast<int>(gi % per) * 8;  // float offset of the group
-        // the four complex elements: real part at float re[k], imaginary at im[k]
-        int mode[4], re[4], im[4];
-        if (o < 128 * D) {  // U: [kw][rt][lane][jj], re in lane i, im in lane i + 1: one mode
+        const int o = static_cast<int>((e % per) >> 2) * 8;  // float offset of the group of eight
+        const int k = static_cast<int>(e & 3);
+        int mode, pre, pim;  // mode, positions of re / im in the eight floats
+        if (o < 128 * D) {   // U: [kw][rt][lane][jj], re in lane i, im in lane i + 1
             const int kw = o / (16 * D), ln = (o % 256) / 4;  // (16 D is a multiple of 256)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                mode[k] = 8 * kw + (ln & 15) / 2;
-                re[k] = k;
-                im[k] = 4 + k;
-            }
+            mode = 8 * kw + (ln & 15) / 2;
+            pre = k;
+            pim = 4 + k;
         } else {  // Gamma: [vw][mt][lane][jj], (re, im) of modes m0, m0 + 1 in jj
             const int o2 = o - 128 * D, mt = (o2 % 2048) / 256, ln = (o2 % 256) / 4;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                mode[k] = 8 * mt + 2 * (ln >> 4) + (k & 1);
-                re[k] = 2 * k;
-                im[k] = 2 * k + 1;
-            }
+            mode = 8 * mt + 2 * (ln >> 4) + (k & 1);
+            pre = 2 * k;
+            pim = 2 * k + 1;
         }
-        const float2* pws = reinterpret_cast<const float2*>(tab + h * kTabBytes + kTabPwSeg);
-        float2 a[4], c[4];
-        float ci[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (has_state) {  // the staged state_in (lane order, already times kappa)
-            const float4* src = reinterpret_cast<const float4*>(c0 + bh * sst + o);
-            const float4 x0 = src[0], x1 = src[1];
-            ci[0] = x0.x; ci[1] = x0.y; ci[2] = x0.z; ci[3] = x0.w;
-            ci[4] = x1.x; ci[5] = x1.y; ci[6] = x1.z; ci[7] = x1.w;
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            a[k] = pws[mode[k]];
-            c[k] = make_float2(ci[re[k]], ci[im[k]]);
-        }
-        float4* base = reinterpret_cast<float4*>(ws + st0 * sst + o);
-        const int64_t s4 = sst / 4;  // float4s per state
+        const float2 a = reinterpret_cast<const float2*>(tab + h * kTabBytes + kTabPwSeg)[mode];
+        // the staged state_in (lane order, already times kappa) or zero
+        float2 c = has_state ? make_float2(c0[bh * sst + o + pre], c0[bh * sst + o + pim]) : make_float2(0.f, 0.f);
+        float* base = ws + st0 * sst + o;
         for (int s0 = 0; s0 + 1 < S; s0 += kBatch) {
             const int n = S - 1 - s0 < kBatch ? S - 1 - s0 : kBatch;
-            float4 l0[kBatch], l1[kBatch];
+            float2 loc[kBatch];
+#pragma unroll
+            for (int jj = 0; jj < kBatch; ++jj)
+                if (jj < n) loc[jj] = make_float2(base[(s0 + jj) * sst + pre], base[(s0 + jj) * sst + pim]);
 #pragma unroll
             for (int jj = 0; jj < kBatch; ++jj)
                 if (jj < n) {
-                    l0[jj] = base[(s0 + jj) * s4];
-                    l1[jj] = base[(s0 + jj) * s4 + 1];
-                }
-#pragma unroll
-            for (int jj = 0; jj < kBatch; ++jj)
-                if (jj < n) {
-                    const float e[8] = {l0[jj].x, l0[jj].y, l0[jj].z, l0[jj].w, l1[jj].x, l1[jj].y, l1[jj].z, l1[jj].w};
-                    float r[8];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        c[k] = make_float2(a[k].x * c[k].x - a[k].y * c[k].y + e[re[k]],
-                                           a[k].x * c[k].y + a[k].y * c[k].x + e[im[k]]);
-                        r[re[k]] = c[k].x;
-                        r[im[k]] = c[k].y;
-                    }
-                    base[(s0 + jj) * s4] = make_float4(r[0], r[1], r[2], r[3]);
-                    base[(s0 + jj) * s4 + 1] = make_float4(r[4], r[5], r[6], r[7]);
+                    c = make_float2(a.x * c.x - a.y * c.y + loc[jj].x, a.x * c.y + a.y * c.x + loc[jj].y);
+                    base[(s0 + jj) * sst + pre] = c.x;
+                    base[(s0 + jj) * sst + pim] = c.y;
                 }
         }
     }
@@ -2312,8 +2284,8 @@ hipError_t launch(const Problem& p, const idattn_params& prm, const void* q, con
     const int64_t carry_pairs = packed ? (p.N / L >= kFoldMax ? carry_cap(p.H) * p.H : 0)
                                        : (S > kFoldMax ? pairs : 0);
     if (carry_pairs > 0) {
-        const int64_t groups = carry_pairs * 32 * p.d;  // groups of eight state floats
-        int64_t blocks = (groups + 255) / 256;
+        const int64_t threads = carry_pairs * 128 * p.d;  // one complex element each
+        int64_t blocks = (threads + 255) / 256;
         blocks = blocks < kCarryBlocks ? blocks : kCarryBlocks;
         segment_carry_kernel<<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(p, state_in != nullptr, c0,
                                                                                      tab, ws, S, plan);

@@ -425,6 +425,8 @@ PACKED = {
     "many_h16_d64": ("125m", dict(H=16), None, 203),
     # 300 sequences: last segments in sequence order (no size sort)
     "b300_h1_d64": ("125m", dict(H=1), None, 204),
+    # a long and a one-chunk sequence at the 1.3B head shape
+    "lens_961_64_h16_d128": ("1p3b", dict(H=16), [961, 64], 207),
 }
 
 
