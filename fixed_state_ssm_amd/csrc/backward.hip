@@ -88,10 +88,13 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
                 xv[t][j] = ok ? xq[(i0 + t) * d + r] : 0.f;
                 zv[t][j] = ok ? zk[(i0 + t) * d + r] : 0.f;
             }
+        // the lane's shares of s and s_a of the kTok tokens, then one reduce-scatter
+        // per quantity (lane t < 8 ends with token slot8(t)'s totals)
+        float spr[kTok], spi[kTok], sqr[kTok], sqi[kTok];
 #pragma unroll
         for (int t = 0; t < kTok; ++t) {
-            if (i0 + t >= N) break;
             float pr = 0.f, pi = 0.f, qr = 0.f, qi = 0.f;
+            if (i0 + t < N) {
 #pragma unroll
             for (int j = 0; j < RJ; ++j) {
                 // V(i) = abar V(i-1) + U(i-1), then U(i) = abar U(i-1) + bbar z_k(i)
@@ -108,14 +111,19 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
                 qr = fmaf(xv[t][j], nvr, qr);
                 qi = fmaf(xv[t][j], nvi, qi);
             }
-            pr = wave_total(pr);
-            pi = wave_total(pi);
-            qr = wave_total(qr);
-            qi = wave_total(qi);
-            if (lane == 0) {
-                s[(row0 + i0 + t) * M + m] = make_float2(pr, pi);
-                s_a[(row0 + i0 + t) * M + m] = make_float2(qr, qi);
             }
+            spr[t] = pr;
+            spi[t] = pi;
+            sqr[t] = qr;
+            sqi[t] = qi;
+        }
+        static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
+        const float tpr = wave_reduce_scatter8(spr, lane), tpi = wave_reduce_scatter8(spi, lane);
+        const float tqr = wave_reduce_scatter8(sqr, lane), tqi = wave_reduce_scatter8(sqi, lane);
+        const int t = slot8(lane);
+        if (lane < kTok && i0 + t < N) {
+            s[(row0 + i0 + t) * M + m] = make_float2(tpr, tpi);
+            s_a[(row0 + i0 + t) * M + m] = make_float2(tqr, tqi);
         }
     }
     if (grad_state != nullptr) {
@@ -182,10 +190,13 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
                 zz[t][j] = ok ? zvp[(i0 + t) * d + c] : 0.f;
                 go[t][j] = ok ? load_io<BF16>(grad_o, ((b * N + i0 + t) * H + h) * d + c) : 0.f;
             }
+        // the lane's shares of g_s and gw of the kTok tokens, then one reduce-scatter
+        // per quantity (lane t < 8 ends with token slot8(t)'s totals)
+        float spr[kTok], spi[kTok], sqr[kTok], sqi[kTok];
 #pragma unroll
         for (int t = 0; t < kTok; ++t) {
-            if (i0 + t >= N) break;
             float pr = 0.f, pi = 0.f, qr = 0.f, qi = 0.f;
+            if (i0 + t < N) {
 #pragma unroll
             for (int j = 0; j < RJ; ++j) {
                 const float nwr = fmaf(ar, wr[j], fmaf(-ai, wi[j], gmr[j]));
@@ -201,19 +212,30 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
                 qr = fmaf(go[t][j], nwr, qr);   // gw = sum g_o conj(W)
                 qi = fmaf(-go[t][j], nwi, qi);
             }
-            pr = wave_total(pr);
-            pi = wave_total(pi);
-            qr = wave_total(qr);
-            qi = wave_total(qi);
-            const int64_t idx = (row0 + i0 + t) * M + m;
-            if (lane == 0) {
-                gs[idx] = make_float2(pr, pi);
-                const float2 sv = s[idx], sa = s_a[idx];
-                // conj(s) gw + g_s conj(s_a)
-                accr += static_cast<double>(sv.x * qr + sv.y * qi) + static_cast<double>(pr * sa.x + pi * sa.y);
-                acci += static_cast<double>(sv.x * qi - sv.y * qr) + static_cast<double>(pi * sa.x - pr * sa.y);
             }
+            spr[t] = pr;
+            spi[t] = pi;
+            sqr[t] = qr;
+            sqi[t] = qi;
         }
+        static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
+        const float pr = wave_reduce_scatter8(spr, lane), pi = wave_reduce_scatter8(spi, lane);
+        const float qr = wave_reduce_scatter8(sqr, lane), qi = wave_reduce_scatter8(sqi, lane);
+        const int t = slot8(lane);
+        if (lane < kTok && i0 + t < N) {
+            const int64_t idx = (row0 + i0 + t) * M + m;
+            gs[idx] = make_float2(pr, pi);
+            const float2 sv = s[idx], sa = s_a[idx];
+            // conj(s) gw + g_s conj(s_a), summed per lane (every eighth token) in fp64
+            accr += static_cast<double>(sv.x * qr + sv.y * qi) + static_cast<double>(pr * sa.x + pi * sa.y);
+            acci += static_cast<double>(sv.x * qi - sv.y * qr) + static_cast<double>(pi * sa.x - pr * sa.y);
+        }
+    }
+    // the eight lanes' sums in a fixed order (lanes >= 8 hold zeros)
+#pragma unroll
+    for (int off = 4; off >= 1; off >>= 1) {
+        accr += __shfl_xor(accr, off, kWave);
+        acci += __shfl_xor(acci, off, kWave);
     }
     if (grad_state != nullptr) {
         float gr = 0.f, gi = 0.f;  // sum_c g_S[c] conj(W_c)
@@ -248,9 +270,12 @@ __device__ __forceinline__ float tree_sum(float (&x)[K]) {
 }
 
 // ------------------------------------------------------------------ per-channel scans
-// One block per (b, h, 64-channel group): wave w owns modes [w MW, (w+1) MW),
-// lane l one channel c; per token the waves' partial sums over their modes
-// meet in LDS and are added in a fixed order.
+// One block per (b, h, 64-channel group, mode split z): wave w owns modes
+// z kVW MW + [w MW, (w+1) MW), lane l one channel c; per token the waves'
+// partial sums over their modes meet in LDS and are added in a fixed order.
+// With two mode splits (M >= 32, so that the chip has twice the blocks),
+// each split writes its partial sums to its own copy of the output, zs
+// floats apart, and the feature kernel adds the two.
 //
 // g_xi_q(i)_r = sum_m Re(g_s_m(i) conj(U_m,r(i))), U run forward again from
 // state_in; the result goes to g_xi [H][T][d].
@@ -258,7 +283,7 @@ template <int MW>
 __global__ __launch_bounds__(kVW * 64) void bwd_xi_scan_kernel(Problem p, idattn_params prm,
                                                                const float* __restrict__ z_k, const float* state_in,
                                                                const float2* __restrict__ gs,
-                                                               float* __restrict__ g_xi) {
+                                                               float* __restrict__ g_xi, int64_t zs) {
     __shared__ float2 w_blk[kBlk * 64];
     __shared__ float red[kVW][kBlk][kWave];
     const int lane = threadIdx.x & (kWave - 1);
@@ -270,10 +295,12 @@ __global__ __launch_bounds__(kVW * 64) void bwd_xi_scan_kernel(Problem p, idattn
     const int c = static_cast<int>(blockIdx.y) * kWave + lane;
     const bool cok = c < d;
     const int64_t row0 = h * p.T + b * N;
+    const int moff = static_cast<int>(blockIdx.z) * kVW * MW;  // the split's first mode
+    g_xi += blockIdx.z * zs;
     float ar[MW], ai[MW], br[MW], bi[MW], ur[MW], ui[MW];
 #pragma unroll
     for (int mm = 0; mm < MW; ++mm) {
-        const int64_t m = w * MW + mm;
+        const int64_t m = moff + w * MW + mm;
         const Zoh zz = zoh_of(prm, h, M, m);
         ar[mm] = static_cast<float>(zz.ar);
         ai[mm] = static_cast<float>(zz.ai);
@@ -300,7 +327,7 @@ __global__ __launch_bounds__(kVW * 64) void bwd_xi_scan_kernel(Problem p, idattn
                 float acc = 0.f;
 #pragma unroll
                 for (int mm = 0; mm < MW; ++mm) {
-                    const float2 g = w_blk[t * M + w * MW + mm];
+                    const float2 g = w_blk[t * M + moff + w * MW + mm];
                     const float nr = fmaf(ar[mm], ur[mm], fmaf(-ai[mm], ui[mm], br[mm] * zz[t]));
                     const float ni = fmaf(ar[mm], ui[mm], fmaf(ai[mm], ur[mm], bi[mm] * zz[t]));
                     ur[mm] = nr;
@@ -339,7 +366,7 @@ __global__ __launch_bounds__(kVW * 64) void bwd_adjoint_kernel(Problem p, idattn
                                                                const float* __restrict__ zsrc,
                                                                const float* grad_state, int off,
                                                                float* __restrict__ g_z, float* grad_state_in,
-                                                               float2* __restrict__ gb) {
+                                                               float2* __restrict__ gb, int64_t zs) {
     __shared__ float2 w_blk[kBlk * 64];
     __shared__ float red[kVW][kBlk][kWave];
     const int lane = threadIdx.x & (kWave - 1);
@@ -351,10 +378,12 @@ __global__ __launch_bounds__(kVW * 64) void bwd_adjoint_kernel(Problem p, idattn
     const int c = static_cast<int>(blockIdx.y) * kWave + lane;
     const bool cok = c < d;
     const int64_t row0 = h * p.T + b * N;
+    const int moff = static_cast<int>(blockIdx.z) * kVW * MW;  // the split's first mode
+    g_z += blockIdx.z * zs;
     float ar[MW], ai[MW], br[MW], bi[MW], cr[MW], ci[MW], gbr[MW], gbi[MW];
 #pragma unroll
     for (int mm = 0; mm < MW; ++mm) {
-        const int64_t m = w * MW + mm;
+        const int64_t m = moff + w * MW + mm;
         const Zoh zz = zoh_of(prm, h, M, m);
         ar[mm] = static_cast<float>(zz.ar);
         ai[mm] = static_cast<float>(zz.ai);
@@ -391,7 +420,7 @@ __global__ __launch_bounds__(kVW * 64) void bwd_adjoint_kernel(Problem p, idattn
                 float acc = 0.f;
 #pragma unroll
                 for (int mm = 0; mm < MW; ++mm) {
-                    float2 g = w_blk[t * M + w * MW + mm];
+                    float2 g = w_blk[t * M + moff + w * MW + mm];
                     if constexpr (CONJ_W) g.y = -g.y;
                     const float nr = fmaf(xx[t], g.x, cr[mm]);
                     const float ni = fmaf(xx[t], g.y, ci[mm]);
@@ -421,7 +450,7 @@ __global__ __launch_bounds__(kVW * 64) void bwd_adjoint_kernel(Problem p, idattn
     if (grad_state_in != nullptr && cok) {
 #pragma unroll
         for (int mm = 0; mm < MW; ++mm) {
-            const int64_t idx = ((bh * M + w * MW + mm) * 2 * d + off + c) * 2;
+            const int64_t idx = ((bh * M + moff + w * MW + mm) * 2 * d + off + c) * 2;
             grad_state_in[idx] = cr[mm];
             grad_state_in[idx + 1] = ci[mm];
         }
@@ -430,7 +459,7 @@ __global__ __launch_bounds__(kVW * 64) void bwd_adjoint_kernel(Problem p, idattn
 #pragma unroll
     for (int mm = 0; mm < MW; ++mm) {
         const float sr = wave_total(gbr[mm]), si = wave_total(gbi[mm]);
-        if (lane == 0) gb[(bh * gridDim.y + blockIdx.y) * M + w * MW + mm] = make_float2(sr, si);
+        if (lane == 0) gb[(bh * gridDim.y + blockIdx.y) * M + moff + w * MW + mm] = make_float2(sr, si);
     }
 }
 
@@ -450,7 +479,8 @@ __global__ __launch_bounds__(256) void bwd_feature_kernel(Problem p, idattn_para
                                                           const void* __restrict__ k, const void* __restrict__ v,
                                                           const void* __restrict__ tail_in,
                                                           float* __restrict__ g_xi, float* __restrict__ g_zk,
-                                                          const float* __restrict__ g_zv, void* __restrict__ grad_v,
+                                                          const float* __restrict__ g_zv, int64_t zs,
+                                                          void* __restrict__ grad_v,
                                                           float* __restrict__ part, int64_t runs) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -533,9 +563,12 @@ __global__ __launch_bounds__(256) void bwd_feature_kernel(Problem p, idattn_para
             const bool in = c < d;
             xk[j] = yk[j] * iDk;
             nxk = fmaf(xk[j], xk[j], nxk);
-            gzk[j] = in ? g_zk[(row0 + t) * d + c] : 0.f;
-            gzv[j] = in ? g_zv[(row0 + t) * d + c] : 0.f;
-            gxq[j] = in ? g_xi[(row0 + t) * d + c] : 0.f;
+            // the scans' partial sums over the two mode splits, added in a fixed order
+            // (zs = 0: one split)
+            const int64_t o = (row0 + t) * d + c;
+            gzk[j] = in ? (zs ? g_zk[o] + g_zk[o + zs] : g_zk[o]) : 0.f;
+            gzv[j] = in ? (zs ? g_zv[o] + g_zv[o + zs] : g_zv[o]) : 0.f;
+            gxq[j] = in ? (zs ? g_xi[o] + g_xi[o + zs] : g_xi[o]) : 0.f;
         }
         nxk = wave_total(nxk);
         const float rk = 1.f / sqrtf(nxk * inv_d + p.eps_norm);
@@ -816,7 +849,8 @@ size_t backward_workspace_bytes(const Problem& p) {
     const size_t groups = static_cast<size_t>((p.d + kWave - 1) / kWave);
     const size_t bh = static_cast<size_t>(p.B * p.H);
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    return 6 * up(tok * p.d * sizeof(float)) + 3 * up(tok * p.M * sizeof(float2)) +
+    const size_t splits = p.M / kVW >= 2 ? 2 : 1;  // mode splits of the per-channel scans
+    return (3 + 3 * splits) * up(tok * p.d * sizeof(float)) + 3 * up(tok * p.M * sizeof(float2)) +
            2 * up(bh * p.M * sizeof(float2)) + 2 * up(bh * groups * p.M * sizeof(float2)) +
            up(bh * runs * 4 * p.d * sizeof(float)) + up(bh * runs * 2 * p.d * p.W * sizeof(float));
 }
@@ -839,9 +873,12 @@ hipError_t launch_backward(const Problem& p, const idattn_params& prm, const voi
     float* xi_q = reinterpret_cast<float*>(take(tok * p.d * sizeof(float)));
     float* z_k = reinterpret_cast<float*>(take(tok * p.d * sizeof(float)));
     float* z_v = reinterpret_cast<float*>(take(tok * p.d * sizeof(float)));
-    float* g_xi = reinterpret_cast<float*>(take(tok * p.d * sizeof(float)));
-    float* g_zk = reinterpret_cast<float*>(take(tok * p.d * sizeof(float)));
-    float* g_zv = reinterpret_cast<float*>(take(tok * p.d * sizeof(float)));
+    const int splits = p.M / kVW >= 2 ? 2 : 1;  // mode splits of the per-channel scans
+    // each split's copy of the scans' outputs, zs floats apart (0: one split)
+    const int64_t zs = splits > 1 ? static_cast<int64_t>(up(tok * p.d * sizeof(float)) / sizeof(float)) : 0;
+    float* g_xi = reinterpret_cast<float*>(take(splits * up(tok * p.d * sizeof(float))));
+    float* g_zk = reinterpret_cast<float*>(take(splits * up(tok * p.d * sizeof(float))));
+    float* g_zv = reinterpret_cast<float*>(take(splits * up(tok * p.d * sizeof(float))));
     float2* s = reinterpret_cast<float2*>(take(tok * p.M * sizeof(float2)));
     float2* s_a = reinterpret_cast<float2*>(take(tok * p.M * sizeof(float2)));
     float2* gs = reinterpret_cast<float2*>(take(tok * p.M * sizeof(float2)));
@@ -872,20 +909,20 @@ hipError_t launch_backward(const Problem& p, const idattn_params& prm, const voi
     }
 #undef IDATTN_BV
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const dim3 gc(static_cast<unsigned>(bh), static_cast<unsigned>(groups));
-#define IDATTN_BX(MW) bwd_xi_scan_kernel<MW><<<gc, kVW * 64, 0, stream>>>(p, prm, z_k, state_in, gs, g_xi)
+    const dim3 gc(static_cast<unsigned>(bh), static_cast<unsigned>(groups), static_cast<unsigned>(splits));
+#define IDATTN_BX(MW) bwd_xi_scan_kernel<MW><<<gc, kVW * 64, 0, stream>>>(p, prm, z_k, state_in, gs, g_xi, zs)
 #define IDATTN_BA(MW)                                                                                          \
     do {                                                                                                       \
         bwd_adjoint_kernel<MW, false, false, false><<<gc, kVW * 64, 0, stream>>>(p, prm, xi_q, gs, z_k, grad_state, \
-                                                                                 0, g_zk, grad_state_in, gbk);  \
+                                                                                 0, g_zk, grad_state_in, gbk, zs); \
         if (p.bf16)                                                                                            \
             bwd_adjoint_kernel<MW, true, true, true><<<gc, kVW * 64, 0, stream>>>(                              \
-                p, prm, grad_o, s, z_v, grad_state, static_cast<int>(p.d), g_zv, grad_state_in, gbv);          \
+                p, prm, grad_o, s, z_v, grad_state, static_cast<int>(p.d), g_zv, grad_state_in, gbv, zs);      \
         else                                                                                                   \
             bwd_adjoint_kernel<MW, true, false, true><<<gc, kVW * 64, 0, stream>>>(                             \
-                p, prm, grad_o, s, z_v, grad_state, static_cast<int>(p.d), g_zv, grad_state_in, gbv);          \
+                p, prm, grad_o, s, z_v, grad_state, static_cast<int>(p.d), g_zv, grad_state_in, gbv, zs);      \
     } while (0)
-    switch (p.M / kVW) {
+    switch (p.M / (kVW * splits)) {
         case 1: IDATTN_BX(1); IDATTN_BA(1); break;
         case 2: IDATTN_BX(2); IDATTN_BA(2); break;
         case 4: IDATTN_BX(4); IDATTN_BA(4); break;
@@ -896,7 +933,7 @@ hipError_t launch_backward(const Problem& p, const idattn_params& prm, const voi
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 gr(static_cast<unsigned>((bh * runs + 3) / 4));
 #define IDATTN_BF(BF, DJ)                                                                                            \
-    bwd_feature_kernel<BF, DJ><<<gr, 256, 0, stream>>>(p, prm, q, k, v, tail_in, g_xi, g_zk, g_zv, grad_v, part_f, \
+    bwd_feature_kernel<BF, DJ><<<gr, 256, 0, stream>>>(p, prm, q, k, v, tail_in, g_xi, g_zk, g_zv, zs, grad_v, part_f, \
                                                        runs);                                                        \
     bwd_conv_kernel<BF, DJ><<<gr, 256, 0, stream>>>(p, prm, q, k, tail_in, g_xi, g_zk, grad_q, grad_k, part_c, runs)
     if (p.d > 64) {
