@@ -454,8 +454,14 @@ def backward_bench(torch, fs, WL, config, steps=5, warmup=2):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    nbytes = 7 * B * N * H * d * 2  # q, k, v and grad_o read once; grad_q, grad_k, grad_v written once (bf16)
+    gbps = nbytes / (ms * 1e-3) / 1e9
     return {"workload": f"{config}: B={B} H={H} N={N} d=R={d} M={M} W={W}, bf16 I/O, gradients of q, k, v and every "
-                        f"parameter, sequential fp32 algorithm", "ms_per_call": ms, "tokens_per_s": B * N / (ms * 1e-3)}
+                        f"parameter, sequential fp32 algorithm", "ms_per_call": ms, "tokens_per_s": B * N / (ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": gbps / HBM_PEAK_GBPS, "algorithmic_bytes": nbytes,
+                         "note": "the sequential scans are serial in time; the algorithmic bytes are the tensors "
+                                 "read and written once"}}
 
 
 def main():
