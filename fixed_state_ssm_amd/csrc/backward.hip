@@ -45,6 +45,82 @@ __device__ __forceinline__ Zoh zoh_of(const idattn_params& prm, int64_t h, int64
 // ------------------------------------------------------------------ per-mode scans
 // One wave per (b, h, m); lane l owns channels l and l + 64 (RJ of them).
 //
+// Each scan takes kTok tokens at a time.  All their loads are issued first,
+// at token and channel indices clamped into range (addressed from a uniform
+// base with 32-bit lane offsets); a ragged batch (fewer than kTok tokens left,
+// or d below 64 RJ) then zeroes what lies out of range and steps only its
+// tokens.  A full batch runs with no per-token condition.
+
+// One batch of the key-side recurrence: V(i) = abar V(i-1) + U(i-1), then
+// U(i) = abar U(i-1) + bbar z_k(i); the lane's shares of s = xi_q . U and
+// s_a = xi_q . V per token.
+template <int RJ, bool RAGGED>
+__device__ __forceinline__ void key_batch(int nt, float (&ur)[RJ], float (&ui)[RJ], float (&vr)[RJ], float (&vi)[RJ],
+                                          const float (&xv)[kTok][RJ], const float (&zv)[kTok][RJ], float ar, float ai,
+                                          float br, float bi, float (&spr)[kTok], float (&spi)[kTok],
+                                          float (&sqr)[kTok], float (&sqi)[kTok]) {
+#pragma unroll
+    for (int t = 0; t < kTok; ++t) {
+        float pr = 0.f, pi = 0.f, qr = 0.f, qi = 0.f;
+        if (!RAGGED || t < nt) {
+#pragma unroll
+            for (int j = 0; j < RJ; ++j) {
+                const float nvr = fmaf(ar, vr[j], fmaf(-ai, vi[j], ur[j]));
+                const float nvi = fmaf(ar, vi[j], fmaf(ai, vr[j], ui[j]));
+                const float nur = fmaf(ar, ur[j], fmaf(-ai, ui[j], br * zv[t][j]));
+                const float nui = fmaf(ar, ui[j], fmaf(ai, ur[j], bi * zv[t][j]));
+                vr[j] = nvr;
+                vi[j] = nvi;
+                ur[j] = nur;
+                ui[j] = nui;
+                pr = fmaf(xv[t][j], nur, pr);
+                pi = fmaf(xv[t][j], nui, pi);
+                qr = fmaf(xv[t][j], nvr, qr);
+                qi = fmaf(xv[t][j], nvi, qi);
+            }
+        }
+        spr[t] = pr;
+        spi[t] = pi;
+        sqr[t] = qr;
+        sqi[t] = qi;
+    }
+}
+
+// One batch of the value-side recurrence: W(i) = abar W(i-1) + Gamma(i-1),
+// then Gamma(i) = abar Gamma(i-1) + bbar z_v(i); the lane's shares of
+// g_s = sum_c g_o[c] conj(Gamma_c) and gw = sum_c g_o[c] conj(W_c) per token.
+template <int RJ, bool RAGGED>
+__device__ __forceinline__ void value_batch(int nt, float (&gmr)[RJ], float (&gmi)[RJ], float (&wr)[RJ],
+                                            float (&wi)[RJ], const float (&zz)[kTok][RJ], const float (&go)[kTok][RJ],
+                                            float ar, float ai, float br, float bi, float (&spr)[kTok],
+                                            float (&spi)[kTok], float (&sqr)[kTok], float (&sqi)[kTok]) {
+#pragma unroll
+    for (int t = 0; t < kTok; ++t) {
+        float pr = 0.f, pi = 0.f, qr = 0.f, qi = 0.f;
+        if (!RAGGED || t < nt) {
+#pragma unroll
+            for (int j = 0; j < RJ; ++j) {
+                const float nwr = fmaf(ar, wr[j], fmaf(-ai, wi[j], gmr[j]));
+                const float nwi = fmaf(ar, wi[j], fmaf(ai, wr[j], gmi[j]));
+                const float ngr = fmaf(ar, gmr[j], fmaf(-ai, gmi[j], br * zz[t][j]));
+                const float ngi = fmaf(ar, gmi[j], fmaf(ai, gmr[j], bi * zz[t][j]));
+                wr[j] = nwr;
+                wi[j] = nwi;
+                gmr[j] = ngr;
+                gmi[j] = ngi;
+                pr = fmaf(go[t][j], ngr, pr);
+                pi = fmaf(-go[t][j], ngi, pi);
+                qr = fmaf(go[t][j], nwr, qr);
+                qi = fmaf(-go[t][j], nwi, qi);
+            }
+        }
+        spr[t] = pr;
+        spi[t] = pi;
+        sqr[t] = qr;
+        sqi[t] = qi;
+    }
+}
+//
 // Key side: U and V = dU/dabar; writes s = xi_q . U and s_a = xi_q . V
 // [H][T][M] and, when the state_out gradient is given, the mode's share
 // sum_r g_S,U[r] conj(V_r(N-1)) of g_abar to ga_key [B H][M].
@@ -75,53 +151,42 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
         }
     }
     const int64_t row0 = h * p.T + (bh / p.H) * N;
-    const float* xq = xi_q + row0 * d;
-    const float* zk = z_k + row0 * d;
+    const bool dfull = d == kWave * RJ;
+    uint32_t off[RJ];  // the lane's channels (clamped below d)
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) off[j] = static_cast<uint32_t>(min(lane + kWave * j, d - 1));
     for (int64_t i0 = 0; i0 < N; i0 += kTok) {
+        const int nt = static_cast<int>(min(N - i0, static_cast<int64_t>(kTok)));
         float xv[kTok][RJ], zv[kTok][RJ];
 #pragma unroll
-        for (int t = 0; t < kTok; ++t)
+        for (int t = 0; t < kTok; ++t) {
+            const int64_t row = (row0 + i0 + min(t, nt - 1)) * d;  // uniform
+            const float* xr = xi_q + row;
+            const float* zr = z_k + row;
 #pragma unroll
             for (int j = 0; j < RJ; ++j) {
-                const int r = lane + kWave * j;
-                const bool ok = (i0 + t < N) && (r < d);
-                xv[t][j] = ok ? xq[(i0 + t) * d + r] : 0.f;
-                zv[t][j] = ok ? zk[(i0 + t) * d + r] : 0.f;
+                xv[t][j] = xr[off[j]];
+                zv[t][j] = zr[off[j]];
             }
+        }
         // the lane's shares of s and s_a of the kTok tokens, then one reduce-scatter
         // per quantity (lane t < 8 ends with token slot8(t)'s totals)
         float spr[kTok], spi[kTok], sqr[kTok], sqi[kTok];
+        if (nt == kTok && dfull) {
+            key_batch<RJ, false>(nt, ur, ui, vr, vi, xv, zv, ar, ai, br, bi, spr, spi, sqr, sqi);
+        } else {
 #pragma unroll
-        for (int t = 0; t < kTok; ++t) {
-            float pr = 0.f, pi = 0.f, qr = 0.f, qi = 0.f;
-            if (i0 + t < N) {
+            for (int t = 0; t < kTok; ++t)
 #pragma unroll
-            for (int j = 0; j < RJ; ++j) {
-                // V(i) = abar V(i-1) + U(i-1), then U(i) = abar U(i-1) + bbar z_k(i)
-                const float nvr = fmaf(ar, vr[j], fmaf(-ai, vi[j], ur[j]));
-                const float nvi = fmaf(ar, vi[j], fmaf(ai, vr[j], ui[j]));
-                const float nur = fmaf(ar, ur[j], fmaf(-ai, ui[j], br * zv[t][j]));
-                const float nui = fmaf(ar, ui[j], fmaf(ai, ur[j], bi * zv[t][j]));
-                vr[j] = nvr;
-                vi[j] = nvi;
-                ur[j] = nur;
-                ui[j] = nui;
-                pr = fmaf(xv[t][j], nur, pr);
-                pi = fmaf(xv[t][j], nui, pi);
-                qr = fmaf(xv[t][j], nvr, qr);
-                qi = fmaf(xv[t][j], nvi, qi);
-            }
-            }
-            spr[t] = pr;
-            spi[t] = pi;
-            sqr[t] = qr;
-            sqi[t] = qi;
+                for (int j = 0; j < RJ; ++j)
+                    if (t >= nt || lane + kWave * j >= d) xv[t][j] = zv[t][j] = 0.f;
+            key_batch<RJ, true>(nt, ur, ui, vr, vi, xv, zv, ar, ai, br, bi, spr, spi, sqr, sqi);
         }
         static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
         const float tpr = wave_reduce_scatter8(spr, lane), tpi = wave_reduce_scatter8(spi, lane);
         const float tqr = wave_reduce_scatter8(sqr, lane), tqi = wave_reduce_scatter8(sqi, lane);
         const int t = slot8(lane);
-        if (lane < kTok && i0 + t < N) {
+        if (lane < kTok && t < nt) {
             s[(row0 + i0 + t) * M + m] = make_float2(tpr, tpi);
             s_a[(row0 + i0 + t) * M + m] = make_float2(tqr, tqi);
         }
@@ -179,53 +244,46 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
     const int64_t row0 = h * p.T + b * N;
     const float* zvp = z_v + row0 * d;
     double accr = 0.0, acci = 0.0;  // g_abar share of this mode
+    const bool dfull = d == kWave * RJ;
+    const int ts = slot8(lane);  // the token whose totals this lane ends with
+    uint32_t coff[RJ];           // the lane's channels (clamped below d)
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) coff[j] = static_cast<uint32_t>(min(lane + kWave * j, d - 1));
     for (int64_t i0 = 0; i0 < N; i0 += kTok) {
+        const int nt = static_cast<int>(min(N - i0, static_cast<int64_t>(kTok)));
         float zz[kTok][RJ], go[kTok][RJ];
 #pragma unroll
-        for (int t = 0; t < kTok; ++t)
+        for (int t = 0; t < kTok; ++t) {
+            const int64_t ti = i0 + min(t, nt - 1);
+            const float* zr = zvp + ti * d;  // uniform
+            const int64_t gr = ((b * N + ti) * H + h) * d;
 #pragma unroll
             for (int j = 0; j < RJ; ++j) {
-                const int c = lane + kWave * j;
-                const bool ok = (i0 + t < N) && (c < d);
-                zz[t][j] = ok ? zvp[(i0 + t) * d + c] : 0.f;
-                go[t][j] = ok ? load_io<BF16>(grad_o, ((b * N + i0 + t) * H + h) * d + c) : 0.f;
+                zz[t][j] = zr[coff[j]];
+                go[t][j] = BF16 ? bf16_to_f32((static_cast<const uint16_t*>(grad_o) + gr)[coff[j]])
+                                : (static_cast<const float*>(grad_o) + gr)[coff[j]];
             }
+        }
+        const int64_t sidx = (row0 + i0 + min(ts, nt - 1)) * M + m;
+        const float2 sv = s[sidx], sa = s_a[sidx];  // used after the reduce-scatter
         // the lane's shares of g_s and gw of the kTok tokens, then one reduce-scatter
         // per quantity (lane t < 8 ends with token slot8(t)'s totals)
         float spr[kTok], spi[kTok], sqr[kTok], sqi[kTok];
+        if (nt == kTok && dfull) {
+            value_batch<RJ, false>(nt, gmr, gmi, wr, wi, zz, go, ar, ai, br, bi, spr, spi, sqr, sqi);
+        } else {
 #pragma unroll
-        for (int t = 0; t < kTok; ++t) {
-            float pr = 0.f, pi = 0.f, qr = 0.f, qi = 0.f;
-            if (i0 + t < N) {
+            for (int t = 0; t < kTok; ++t)
 #pragma unroll
-            for (int j = 0; j < RJ; ++j) {
-                const float nwr = fmaf(ar, wr[j], fmaf(-ai, wi[j], gmr[j]));
-                const float nwi = fmaf(ar, wi[j], fmaf(ai, wr[j], gmi[j]));
-                const float ngr = fmaf(ar, gmr[j], fmaf(-ai, gmi[j], br * zz[t][j]));
-                const float ngi = fmaf(ar, gmi[j], fmaf(ai, gmr[j], bi * zz[t][j]));
-                wr[j] = nwr;
-                wi[j] = nwi;
-                gmr[j] = ngr;
-                gmi[j] = ngi;
-                pr = fmaf(go[t][j], ngr, pr);   // g_s = sum g_o conj(Gamma)
-                pi = fmaf(-go[t][j], ngi, pi);
-                qr = fmaf(go[t][j], nwr, qr);   // gw = sum g_o conj(W)
-                qi = fmaf(-go[t][j], nwi, qi);
-            }
-            }
-            spr[t] = pr;
-            spi[t] = pi;
-            sqr[t] = qr;
-            sqi[t] = qi;
+                for (int j = 0; j < RJ; ++j)
+                    if (t >= nt || lane + kWave * j >= d) zz[t][j] = go[t][j] = 0.f;
+            value_batch<RJ, true>(nt, gmr, gmi, wr, wi, zz, go, ar, ai, br, bi, spr, spi, sqr, sqi);
         }
         static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
         const float pr = wave_reduce_scatter8(spr, lane), pi = wave_reduce_scatter8(spi, lane);
         const float qr = wave_reduce_scatter8(sqr, lane), qi = wave_reduce_scatter8(sqi, lane);
-        const int t = slot8(lane);
-        if (lane < kTok && i0 + t < N) {
-            const int64_t idx = (row0 + i0 + t) * M + m;
-            gs[idx] = make_float2(pr, pi);
-            const float2 sv = s[idx], sa = s_a[idx];
+        if (lane < kTok && ts < nt) {
+            gs[sidx] = make_float2(pr, pi);
             // conj(s) gw + g_s conj(s_a), summed per lane (every eighth token) in fp64
             accr += static_cast<double>(sv.x * qr + sv.y * qi) + static_cast<double>(pr * sa.x + pi * sa.y);
             acci += static_cast<double>(sv.x * qi - sv.y * qr) + static_cast<double>(pi * sa.x - pr * sa.y);
@@ -279,6 +337,31 @@ __device__ __forceinline__ float tree_sum(float (&x)[K]) {
 //
 // g_xi_q(i)_r = sum_m Re(g_s_m(i) conj(U_m,r(i))), U run forward again from
 // state_in; the result goes to g_xi [H][T][d].
+// One block of kBlk tokens of the xi scan for the wave's MW modes: U steps
+// forward and the wave's share sum_m Re(g_s conj(U_m)) of each token goes to
+// red.  A ragged block steps only its first nt tokens.
+template <int MW, bool RAGGED>
+__device__ __forceinline__ void xi_block(int nt, const float2* g_row, float (*red_t)[kWave], int lane,
+                                         const float (&zz)[kBlk], const float (&ar)[MW], const float (&ai)[MW],
+                                         const float (&br)[MW], const float (&bi)[MW], float (&ur)[MW],
+                                         float (&ui)[MW], int64_t M) {
+#pragma unroll
+    for (int t = 0; t < kBlk; ++t) {
+        if (RAGGED && t >= nt) continue;
+        float acc = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < MW; ++mm) {
+            const float2 g = g_row[t * M + mm];
+            const float nr = fmaf(ar[mm], ur[mm], fmaf(-ai[mm], ui[mm], br[mm] * zz[t]));
+            const float ni = fmaf(ar[mm], ui[mm], fmaf(ai[mm], ur[mm], bi[mm] * zz[t]));
+            ur[mm] = nr;
+            ui[mm] = ni;
+            acc = fmaf(g.x, nr, fmaf(g.y, ni, acc));  // Re(g conj(U))
+        }
+        red_t[t][lane] = acc;
+    }
+}
+
 template <int MW>
 __global__ __launch_bounds__(kVW * 64) void bwd_xi_scan_kernel(Problem p, idattn_params prm,
                                                                const float* __restrict__ z_k, const float* state_in,
@@ -314,28 +397,24 @@ __global__ __launch_bounds__(kVW * 64) void bwd_xi_scan_kernel(Problem p, idattn
         }
     }
     const float* zkp = z_k + row0 * d;
+    const uint32_t cl = static_cast<uint32_t>(cok ? c : d - 1);  // the lane's channel, clamped
     for (int64_t i0 = 0; i0 < N; i0 += kBlk) {
         const int nt = static_cast<int>(N - i0 < kBlk ? N - i0 : kBlk);
         for (int e = threadIdx.x; e < nt * M; e += kVW * 64) w_blk[e] = gs[(row0 + i0) * M + e];
+        // loads at clamped indices, all issued before the first use; a ragged
+        // block zeroes what lies out of range
         float zz[kBlk];
 #pragma unroll
-        for (int t = 0; t < kBlk; ++t) zz[t] = (t < nt && cok) ? zkp[(i0 + t) * d + c] : 0.f;
+        for (int t = 0; t < kBlk; ++t) zz[t] = (zkp + (i0 + min(t, nt - 1)) * d)[cl];
         __syncthreads();
+        const float2* g_row = w_blk + moff + w * MW;
+        if (nt == kBlk && cok) {
+            xi_block<MW, false>(nt, g_row, red[w], lane, zz, ar, ai, br, bi, ur, ui, M);
+        } else {
 #pragma unroll
-        for (int t = 0; t < kBlk; ++t) {
-            if (t < nt) {
-                float acc = 0.f;
-#pragma unroll
-                for (int mm = 0; mm < MW; ++mm) {
-                    const float2 g = w_blk[t * M + moff + w * MW + mm];
-                    const float nr = fmaf(ar[mm], ur[mm], fmaf(-ai[mm], ui[mm], br[mm] * zz[t]));
-                    const float ni = fmaf(ar[mm], ui[mm], fmaf(ai[mm], ur[mm], bi[mm] * zz[t]));
-                    ur[mm] = nr;
-                    ui[mm] = ni;
-                    acc = fmaf(g.x, nr, fmaf(g.y, ni, acc));  // Re(g conj(U))
-                }
-                red[w][t][lane] = acc;
-            }
+            for (int t = 0; t < kBlk; ++t)
+                if (t >= nt || !cok) zz[t] = 0.f;
+            xi_block<MW, true>(nt, g_row, red[w], lane, zz, ar, ai, br, bi, ur, ui, M);
         }
         __syncthreads();
         for (int e = threadIdx.x; e < nt * kWave; e += kVW * 64) {
@@ -359,6 +438,38 @@ __global__ __launch_bounds__(kVW * 64) void bwd_xi_scan_kernel(Problem p, idattn
 //   g_state_in = conj(abar) A(0)                    (columns off .. off + d - 1)
 // Key side: x = xi_q, w = g_s, z = z_k, off = 0.  Value side: x = g_o (io
 // dtype, [B][N][H][d]), w = conj(s), z = z_v, off = d.
+// One block of kBlk tokens of an adjoint scan for the wave's MW modes, in
+// reverse token order: the adjoint A = x g + carry, the wave's share
+// sum_m Re(conj(bbar_m) A_m) of each token to red, the g_bbar sums, and the
+// carry conj(abar) A into the previous token.  A ragged block steps only its
+// first nt tokens.
+template <int MW, bool CONJ_W, bool RAGGED>
+__device__ __forceinline__ void adjoint_block(int nt, const float2* g_row, float (*red_t)[kWave], int lane,
+                                              const float (&xx)[kBlk], const float (&zz)[kBlk],
+                                              const float (&ar)[MW], const float (&ai)[MW], const float (&br)[MW],
+                                              const float (&bi)[MW], float (&cr)[MW], float (&ci)[MW],
+                                              float (&gbr)[MW], float (&gbi)[MW], int64_t M) {
+#pragma unroll
+    for (int t = kBlk - 1; t >= 0; --t) {
+        if (RAGGED && t >= nt) continue;
+        float acc = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < MW; ++mm) {
+            float2 g = g_row[t * M + mm];
+            if constexpr (CONJ_W) g.y = -g.y;
+            const float nr = fmaf(xx[t], g.x, cr[mm]);
+            const float ni = fmaf(xx[t], g.y, ci[mm]);
+            acc = fmaf(br[mm], nr, fmaf(bi[mm], ni, acc));  // Re(conj(bbar) A)
+            gbr[mm] = fmaf(nr, zz[t], gbr[mm]);
+            gbi[mm] = fmaf(ni, zz[t], gbi[mm]);
+            // carry into the previous token: conj(abar) A
+            cr[mm] = fmaf(ar[mm], nr, ai[mm] * ni);
+            ci[mm] = fmaf(ar[mm], ni, -ai[mm] * nr);
+        }
+        red_t[t][lane] = acc;
+    }
+}
+
 template <int MW, bool X_IO, bool BF16, bool CONJ_W>
 __global__ __launch_bounds__(kVW * 64) void bwd_adjoint_kernel(Problem p, idattn_params prm,
                                                                const void* __restrict__ x,
@@ -397,42 +508,35 @@ __global__ __launch_bounds__(kVW * 64) void bwd_adjoint_kernel(Problem p, idattn
         }
     }
     const float* zp = zsrc + row0 * d;
+    const uint32_t cl = static_cast<uint32_t>(cok ? c : d - 1);  // the lane's channel, clamped
     for (int64_t i1 = N; i1 > 0; i1 -= kBlk) {
         const int64_t i0 = i1 - kBlk > 0 ? i1 - kBlk : 0;
         const int nt = static_cast<int>(i1 - i0);
         for (int e = threadIdx.x; e < nt * M; e += kVW * 64) w_blk[e] = wv[(row0 + i0) * M + e];
+        // loads at clamped indices, all issued before the first use; a ragged
+        // block zeroes what lies out of range
         float xx[kBlk], zz[kBlk];
 #pragma unroll
         for (int t = 0; t < kBlk; ++t) {
-            const bool ok = t < nt && cok;
-            float xv = 0.f;
-            if (ok) {
-                if constexpr (X_IO) xv = load_io<BF16>(x, ((b * N + i0 + t) * H + h) * d + c);
-                else xv = static_cast<const float*>(x)[(row0 + i0 + t) * d + c];
+            const int64_t ti = i0 + min(t, nt - 1);
+            if constexpr (X_IO) {
+                const int64_t xr = ((b * N + ti) * H + h) * d;
+                xx[t] = BF16 ? bf16_to_f32((static_cast<const uint16_t*>(x) + xr)[cl])
+                             : (static_cast<const float*>(x) + xr)[cl];
+            } else {
+                xx[t] = (static_cast<const float*>(x) + (row0 + ti) * d)[cl];
             }
-            xx[t] = xv;
-            zz[t] = ok ? zp[(i0 + t) * d + c] : 0.f;
+            zz[t] = (zp + ti * d)[cl];
         }
         __syncthreads();
+        const float2* g_row = w_blk + moff + w * MW;
+        if (nt == kBlk && cok) {
+            adjoint_block<MW, CONJ_W, false>(nt, g_row, red[w], lane, xx, zz, ar, ai, br, bi, cr, ci, gbr, gbi, M);
+        } else {
 #pragma unroll
-        for (int t = kBlk - 1; t >= 0; --t) {
-            if (t < nt) {
-                float acc = 0.f;
-#pragma unroll
-                for (int mm = 0; mm < MW; ++mm) {
-                    float2 g = w_blk[t * M + moff + w * MW + mm];
-                    if constexpr (CONJ_W) g.y = -g.y;
-                    const float nr = fmaf(xx[t], g.x, cr[mm]);
-                    const float ni = fmaf(xx[t], g.y, ci[mm]);
-                    acc = fmaf(br[mm], nr, fmaf(bi[mm], ni, acc));  // Re(conj(bbar) A)
-                    gbr[mm] = fmaf(nr, zz[t], gbr[mm]);
-                    gbi[mm] = fmaf(ni, zz[t], gbi[mm]);
-                    // carry into the previous token: conj(abar) A
-                    cr[mm] = fmaf(ar[mm], nr, ai[mm] * ni);
-                    ci[mm] = fmaf(ar[mm], ni, -ai[mm] * nr);
-                }
-                red[w][t][lane] = acc;
-            }
+            for (int t = 0; t < kBlk; ++t)
+                if (t >= nt || !cok) xx[t] = zz[t] = 0.f;
+            adjoint_block<MW, CONJ_W, true>(nt, g_row, red[w], lane, xx, zz, ar, ai, br, bi, cr, ci, gbr, gbi, M);
         }
         __syncthreads();
         for (int e = threadIdx.x; e < nt * kWave; e += kVW * 64) {
