@@ -335,25 +335,99 @@ __device__ __forceinline__ float tree_sum(float (&x)[K]) {
 // each split writes its partial sums to its own copy of the output, zs
 // floats apart, and the feature kernel adds the two.
 //
+// Tokens go in blocks of kBlk.  The block's threads stage one block's inputs
+// in LDS, one element of each per thread: the per-token mode input (kBlk x M
+// complex) and the channel inputs (kBlk x 64).  The next block's elements are
+// loaded into registers while this block's tokens are stepped, so no wave
+// waits on memory between blocks; two barriers per block.
+constexpr int kStage = kVW * kWave;  // threads per block = staged elements per input
+static_assert(kBlk * kWave == kStage, "one channel-input element per thread");
+static_assert(kBlk * 64 <= kStage, "one mode-input element per thread for M <= 64");
+
+// One thread's staged elements of the block of tokens [i0, i0 + nt): the mode
+// input of (token e / M, mode e % M) and the channel inputs of (token e / 64,
+// channel 64 group + e % 64), e = threadIdx.x, loaded at indices clamped into
+// the block and below d.  x is kept as loaded (bf16 bits or fp32 bits) and
+// widened when it is stored, so that nothing waits on the loads before then.
+struct Stage {
+    float2 w;
+    uint32_t xb;
+    float z;
+};
+
+// X: whether the scan has a channel input x; X_IO: x is the caller's [B][N][H][d]
+// tensor (else the workspace's [H][T][d] fp32); BF16: its elements are bf16.
+template <bool X, bool X_IO, bool BF16>
+__device__ __forceinline__ Stage stage_fetch(const Problem& p, int64_t b, int64_t h, int64_t row0, int64_t i0, int nt,
+                                             int group, const float2* __restrict__ wv, const void* __restrict__ x,
+                                             const float* __restrict__ zsrc) {
+    const int e = static_cast<int>(threadIdx.x);
+    const int M = static_cast<int>(p.M), d = static_cast<int>(p.d);
+    Stage s;
+    s.w = wv[(row0 + i0 + min(e / M, nt - 1)) * M + e % M];
+    const int64_t ti = i0 + min(e / kWave, nt - 1);
+    const uint32_t cl = static_cast<uint32_t>(min(group * kWave + e % kWave, d - 1));
+    s.z = (zsrc + (row0 + ti) * d)[cl];
+    s.xb = 0u;
+    if constexpr (X) {
+        if constexpr (X_IO) {
+            const int64_t xr = ((b * p.N + ti) * p.H + h) * d;
+            if constexpr (BF16) s.xb = (static_cast<const uint16_t*>(x) + xr)[cl];
+            else s.xb = (static_cast<const uint32_t*>(x) + xr)[cl];
+        } else {
+            s.xb = (static_cast<const uint32_t*>(x) + (row0 + ti) * d)[cl];
+        }
+    }
+    return s;
+}
+
+// The staged elements into LDS, zero past the block's nt tokens and past d.
+template <bool X, bool BF16>
+__device__ __forceinline__ void stage_store(const Stage& s, int nt, int M, int group, int d, float2* w_blk,
+                                            float* x_blk, float* z_blk) {
+    const int e = static_cast<int>(threadIdx.x);
+    w_blk[e] = e < nt * M ? s.w : make_float2(0.f, 0.f);
+    const bool ok = e / kWave < nt && group * kWave + e % kWave < d;
+    z_blk[e] = ok ? s.z : 0.f;
+    if constexpr (X) x_blk[e] = ok ? __uint_as_float(BF16 ? s.xb << 16 : s.xb) : 0.f;
+}
+
+// The waves' partial sums of the block's tokens, added in a fixed order, to
+// out [token][d] (rows row0 + i0 .. row0 + i0 + nt - 1).
+__device__ __forceinline__ void reduce_block(const float (*red)[kBlk][kWave], int nt, int group, int d,
+                                             float* __restrict__ out) {
+    for (int e = static_cast<int>(threadIdx.x); e < nt * kWave; e += kStage) {
+        const int t = e / kWave, l = e % kWave;
+        const int cc = group * kWave + l;
+        if (cc < d) {
+            float part[kVW];
+#pragma unroll
+            for (int i = 0; i < kVW; ++i) part[i] = red[i][t][l];
+            out[static_cast<int64_t>(t) * d + cc] = tree_sum(part);
+        }
+    }
+}
+
 // g_xi_q(i)_r = sum_m Re(g_s_m(i) conj(U_m,r(i))), U run forward again from
 // state_in; the result goes to g_xi [H][T][d].
 // One block of kBlk tokens of the xi scan for the wave's MW modes: U steps
 // forward and the wave's share sum_m Re(g_s conj(U_m)) of each token goes to
 // red.  A ragged block steps only its first nt tokens.
 template <int MW, bool RAGGED>
-__device__ __forceinline__ void xi_block(int nt, const float2* g_row, float (*red_t)[kWave], int lane,
-                                         const float (&zz)[kBlk], const float (&ar)[MW], const float (&ai)[MW],
+__device__ __forceinline__ void xi_block(int nt, const float2* g_row, const float* z_col, float (*red_t)[kWave],
+                                         int lane, const float (&ar)[MW], const float (&ai)[MW],
                                          const float (&br)[MW], const float (&bi)[MW], float (&ur)[MW],
-                                         float (&ui)[MW], int64_t M) {
+                                         float (&ui)[MW], int M) {
 #pragma unroll
     for (int t = 0; t < kBlk; ++t) {
         if (RAGGED && t >= nt) continue;
+        const float zz = z_col[t * kWave];
         float acc = 0.f;
 #pragma unroll
         for (int mm = 0; mm < MW; ++mm) {
             const float2 g = g_row[t * M + mm];
-            const float nr = fmaf(ar[mm], ur[mm], fmaf(-ai[mm], ui[mm], br[mm] * zz[t]));
-            const float ni = fmaf(ar[mm], ui[mm], fmaf(ai[mm], ur[mm], bi[mm] * zz[t]));
+            const float nr = fmaf(ar[mm], ur[mm], fmaf(-ai[mm], ui[mm], br[mm] * zz));
+            const float ni = fmaf(ar[mm], ui[mm], fmaf(ai[mm], ur[mm], bi[mm] * zz));
             ur[mm] = nr;
             ui[mm] = ni;
             acc = fmaf(g.x, nr, fmaf(g.y, ni, acc));  // Re(g conj(U))
@@ -363,22 +437,25 @@ __device__ __forceinline__ void xi_block(int nt, const float2* g_row, float (*re
 }
 
 template <int MW>
-__global__ __launch_bounds__(kVW * 64) void bwd_xi_scan_kernel(Problem p, idattn_params prm,
-                                                               const float* __restrict__ z_k, const float* state_in,
-                                                               const float2* __restrict__ gs,
-                                                               float* __restrict__ g_xi, int64_t zs) {
-    __shared__ float2 w_blk[kBlk * 64];
+__global__ __launch_bounds__(kStage) void bwd_xi_scan_kernel(Problem p, idattn_params prm,
+                                                             const float* __restrict__ z_k, const float* state_in,
+                                                             const float2* __restrict__ gs,
+                                                             float* __restrict__ g_xi, int64_t zs) {
+    __shared__ float2 w_blk[kStage];
+    __shared__ float z_blk[kStage];
     __shared__ float red[kVW][kBlk][kWave];
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x >> 6;
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / p.H, h = bh % p.H;
-    const int64_t M = p.M, N = p.N;
-    const int d = static_cast<int>(p.d);
-    const int c = static_cast<int>(blockIdx.y) * kWave + lane;
+    const int64_t N = p.N;
+    const int M = static_cast<int>(p.M), d = static_cast<int>(p.d);
+    const int group = static_cast<int>(blockIdx.y);
+    const int c = group * kWave + lane;
     const bool cok = c < d;
     const int64_t row0 = h * p.T + b * N;
     const int moff = static_cast<int>(blockIdx.z) * kVW * MW;  // the split's first mode
+    if (N <= 0) return;  // whole block
     g_xi += blockIdx.z * zs;
     float ar[MW], ai[MW], br[MW], bi[MW], ur[MW], ui[MW];
 #pragma unroll
@@ -396,38 +473,24 @@ __global__ __launch_bounds__(kVW * 64) void bwd_xi_scan_kernel(Problem p, idattn
             ui[mm] = state_in[idx + 1];
         }
     }
-    const float* zkp = z_k + row0 * d;
-    const uint32_t cl = static_cast<uint32_t>(cok ? c : d - 1);  // the lane's channel, clamped
-    for (int64_t i0 = 0; i0 < N; i0 += kBlk) {
-        const int nt = static_cast<int>(N - i0 < kBlk ? N - i0 : kBlk);
-        for (int e = threadIdx.x; e < nt * M; e += kVW * 64) w_blk[e] = gs[(row0 + i0) * M + e];
-        // loads at clamped indices, all issued before the first use; a ragged
-        // block zeroes what lies out of range
-        float zz[kBlk];
-#pragma unroll
-        for (int t = 0; t < kBlk; ++t) zz[t] = (zkp + (i0 + min(t, nt - 1)) * d)[cl];
+    const float2* g_row = w_blk + moff + w * MW;
+    int64_t i0 = 0;
+    int nt = static_cast<int>(min(N, static_cast<int64_t>(kBlk)));
+    Stage nx = stage_fetch<false, false, false>(p, b, h, row0, i0, nt, group, gs, nullptr, z_k);
+    while (i0 < N) {
+        stage_store<false, false>(nx, nt, M, group, d, w_blk, nullptr, z_blk);
         __syncthreads();
-        const float2* g_row = w_blk + moff + w * MW;
-        if (nt == kBlk && cok) {
-            xi_block<MW, false>(nt, g_row, red[w], lane, zz, ar, ai, br, bi, ur, ui, M);
-        } else {
-#pragma unroll
-            for (int t = 0; t < kBlk; ++t)
-                if (t >= nt || !cok) zz[t] = 0.f;
-            xi_block<MW, true>(nt, g_row, red[w], lane, zz, ar, ai, br, bi, ur, ui, M);
-        }
+        const int64_t j0 = i0 + kBlk;  // the next block, loaded while this one runs
+        const int jnt = static_cast<int>(min(N - j0, static_cast<int64_t>(kBlk)));
+        if (j0 < N) nx = stage_fetch<false, false, false>(p, b, h, row0, j0, jnt, group, gs, nullptr, z_k);
+        if (nt == kBlk)
+            xi_block<MW, false>(nt, g_row, z_blk + lane, red[w], lane, ar, ai, br, bi, ur, ui, M);
+        else
+            xi_block<MW, true>(nt, g_row, z_blk + lane, red[w], lane, ar, ai, br, bi, ur, ui, M);
         __syncthreads();
-        for (int e = threadIdx.x; e < nt * kWave; e += kVW * 64) {
-            const int t = e / kWave, l = e % kWave;
-            const int cc = static_cast<int>(blockIdx.y) * kWave + l;
-            if (cc < d) {
-                float part[kVW];
-#pragma unroll
-                for (int i = 0; i < kVW; ++i) part[i] = red[i][t][l];
-                g_xi[(row0 + i0 + t) * d + cc] = tree_sum(part);
-            }
-        }
-        __syncthreads();
+        reduce_block(red, nt, group, d, g_xi + (row0 + i0) * d);
+        i0 = j0;
+        nt = jnt;
     }
 }
 
@@ -444,24 +507,25 @@ __global__ __launch_bounds__(kVW * 64) void bwd_xi_scan_kernel(Problem p, idattn
 // carry conj(abar) A into the previous token.  A ragged block steps only its
 // first nt tokens.
 template <int MW, bool CONJ_W, bool RAGGED>
-__device__ __forceinline__ void adjoint_block(int nt, const float2* g_row, float (*red_t)[kWave], int lane,
-                                              const float (&xx)[kBlk], const float (&zz)[kBlk],
-                                              const float (&ar)[MW], const float (&ai)[MW], const float (&br)[MW],
-                                              const float (&bi)[MW], float (&cr)[MW], float (&ci)[MW],
-                                              float (&gbr)[MW], float (&gbi)[MW], int64_t M) {
+__device__ __forceinline__ void adjoint_block(int nt, const float2* g_row, const float* x_col, const float* z_col,
+                                              float (*red_t)[kWave], int lane, const float (&ar)[MW],
+                                              const float (&ai)[MW], const float (&br)[MW], const float (&bi)[MW],
+                                              float (&cr)[MW], float (&ci)[MW], float (&gbr)[MW], float (&gbi)[MW],
+                                              int M) {
 #pragma unroll
     for (int t = kBlk - 1; t >= 0; --t) {
         if (RAGGED && t >= nt) continue;
+        const float xx = x_col[t * kWave], zz = z_col[t * kWave];
         float acc = 0.f;
 #pragma unroll
         for (int mm = 0; mm < MW; ++mm) {
             float2 g = g_row[t * M + mm];
             if constexpr (CONJ_W) g.y = -g.y;
-            const float nr = fmaf(xx[t], g.x, cr[mm]);
-            const float ni = fmaf(xx[t], g.y, ci[mm]);
+            const float nr = fmaf(xx, g.x, cr[mm]);
+            const float ni = fmaf(xx, g.y, ci[mm]);
             acc = fmaf(br[mm], nr, fmaf(bi[mm], ni, acc));  // Re(conj(bbar) A)
-            gbr[mm] = fmaf(nr, zz[t], gbr[mm]);
-            gbi[mm] = fmaf(ni, zz[t], gbi[mm]);
+            gbr[mm] = fmaf(nr, zz, gbr[mm]);
+            gbi[mm] = fmaf(ni, zz, gbi[mm]);
             // carry into the previous token: conj(abar) A
             cr[mm] = fmaf(ar[mm], nr, ai[mm] * ni);
             ci[mm] = fmaf(ar[mm], ni, -ai[mm] * nr);
@@ -471,22 +535,25 @@ __device__ __forceinline__ void adjoint_block(int nt, const float2* g_row, float
 }
 
 template <int MW, bool X_IO, bool BF16, bool CONJ_W>
-__global__ __launch_bounds__(kVW * 64) void bwd_adjoint_kernel(Problem p, idattn_params prm,
-                                                               const void* __restrict__ x,
-                                                               const float2* __restrict__ wv,
-                                                               const float* __restrict__ zsrc,
-                                                               const float* grad_state, int off,
-                                                               float* __restrict__ g_z, float* grad_state_in,
-                                                               float2* __restrict__ gb, int64_t zs) {
-    __shared__ float2 w_blk[kBlk * 64];
+__global__ __launch_bounds__(kStage) void bwd_adjoint_kernel(Problem p, idattn_params prm,
+                                                             const void* __restrict__ x,
+                                                             const float2* __restrict__ wv,
+                                                             const float* __restrict__ zsrc,
+                                                             const float* grad_state, int off,
+                                                             float* __restrict__ g_z, float* grad_state_in,
+                                                             float2* __restrict__ gb, int64_t zs) {
+    __shared__ float2 w_blk[kStage];
+    __shared__ float x_blk[kStage];
+    __shared__ float z_blk[kStage];
     __shared__ float red[kVW][kBlk][kWave];
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x >> 6;
     const int64_t bh = blockIdx.x;
-    const int64_t b = bh / p.H, h = bh % p.H, H = p.H;
-    const int64_t M = p.M, N = p.N;
-    const int d = static_cast<int>(p.d);
-    const int c = static_cast<int>(blockIdx.y) * kWave + lane;
+    const int64_t b = bh / p.H, h = bh % p.H;
+    const int64_t N = p.N;
+    const int M = static_cast<int>(p.M), d = static_cast<int>(p.d);
+    const int group = static_cast<int>(blockIdx.y);
+    const int c = group * kWave + lane;
     const bool cok = c < d;
     const int64_t row0 = h * p.T + b * N;
     const int moff = static_cast<int>(blockIdx.z) * kVW * MW;  // the split's first mode
@@ -507,49 +574,30 @@ __global__ __launch_bounds__(kVW * 64) void bwd_adjoint_kernel(Problem p, idattn
             ci[mm] = grad_state[idx + 1];
         }
     }
-    const float* zp = zsrc + row0 * d;
-    const uint32_t cl = static_cast<uint32_t>(cok ? c : d - 1);  // the lane's channel, clamped
-    for (int64_t i1 = N; i1 > 0; i1 -= kBlk) {
-        const int64_t i0 = i1 - kBlk > 0 ? i1 - kBlk : 0;
-        const int nt = static_cast<int>(i1 - i0);
-        for (int e = threadIdx.x; e < nt * M; e += kVW * 64) w_blk[e] = wv[(row0 + i0) * M + e];
-        // loads at clamped indices, all issued before the first use; a ragged
-        // block zeroes what lies out of range
-        float xx[kBlk], zz[kBlk];
-#pragma unroll
-        for (int t = 0; t < kBlk; ++t) {
-            const int64_t ti = i0 + min(t, nt - 1);
-            if constexpr (X_IO) {
-                const int64_t xr = ((b * N + ti) * H + h) * d;
-                xx[t] = BF16 ? bf16_to_f32((static_cast<const uint16_t*>(x) + xr)[cl])
-                             : (static_cast<const float*>(x) + xr)[cl];
-            } else {
-                xx[t] = (static_cast<const float*>(x) + (row0 + ti) * d)[cl];
-            }
-            zz[t] = (zp + ti * d)[cl];
-        }
-        __syncthreads();
+    if (N > 0) {  // uniform over the block
+        constexpr bool XB = X_IO && BF16;
         const float2* g_row = w_blk + moff + w * MW;
-        if (nt == kBlk && cok) {
-            adjoint_block<MW, CONJ_W, false>(nt, g_row, red[w], lane, xx, zz, ar, ai, br, bi, cr, ci, gbr, gbi, M);
-        } else {
-#pragma unroll
-            for (int t = 0; t < kBlk; ++t)
-                if (t >= nt || !cok) xx[t] = zz[t] = 0.f;
-            adjoint_block<MW, CONJ_W, true>(nt, g_row, red[w], lane, xx, zz, ar, ai, br, bi, cr, ci, gbr, gbi, M);
+        int64_t i0 = N > kBlk ? N - kBlk : 0;
+        int nt = static_cast<int>(N - i0);
+        Stage nx = stage_fetch<true, X_IO, BF16>(p, b, h, row0, i0, nt, group, wv, x, zsrc);
+        while (true) {
+            stage_store<true, XB>(nx, nt, M, group, d, w_blk, x_blk, z_blk);
+            __syncthreads();
+            const int64_t j0 = i0 > kBlk ? i0 - kBlk : 0;  // the previous block, loaded while this one runs
+            const int jnt = static_cast<int>(i0 - j0);
+            if (jnt > 0) nx = stage_fetch<true, X_IO, BF16>(p, b, h, row0, j0, jnt, group, wv, x, zsrc);
+            if (nt == kBlk)
+                adjoint_block<MW, CONJ_W, false>(nt, g_row, x_blk + lane, z_blk + lane, red[w], lane, ar, ai, br, bi,
+                                                 cr, ci, gbr, gbi, M);
+            else
+                adjoint_block<MW, CONJ_W, true>(nt, g_row, x_blk + lane, z_blk + lane, red[w], lane, ar, ai, br, bi,
+                                                cr, ci, gbr, gbi, M);
+            __syncthreads();
+            reduce_block(red, nt, group, d, g_z + (row0 + i0) * d);
+            if (jnt == 0) break;
+            i0 = j0;
+            nt = jnt;
         }
-        __syncthreads();
-        for (int e = threadIdx.x; e < nt * kWave; e += kVW * 64) {
-            const int t = e / kWave, l = e % kWave;
-            const int cc = static_cast<int>(blockIdx.y) * kWave + l;
-            if (cc < d) {
-                float part[kVW];
-#pragma unroll
-                for (int i = 0; i < kVW; ++i) part[i] = red[i][t][l];
-                g_z[(row0 + i0 + t) * d + cc] = tree_sum(part);
-            }
-        }
-        __syncthreads();
     }
     if (grad_state_in != nullptr && cok) {
 #pragma unroll
@@ -851,8 +899,24 @@ __device__ inline void phi_z(double zr, double zi, double& pr, double& pi) {
     pi = (ni * z2r - nr * z2i) / den;
 }
 
-// One block per head: the gain, bias and conv gradients summed over batch
-// rows and runs in a fixed order, and the ZOH chain rule from g_abar,
+// acc += src[0], src[stride], ..., src[(runs - 1) stride] in that order, with
+// sixteen loads in flight.
+__device__ __forceinline__ void sum_runs(const float* src, int64_t stride, int64_t runs, double& acc) {
+    int64_t r = 0;
+    for (; r + 16 <= runs; r += 16) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = src[(r + i) * stride];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc += v[i];
+    }
+    for (; r < runs; ++r) acc += src[r * stride];
+}
+
+// Grid (H, slices): blocks y < slices - 1 take kRedThreads of the head's
+// 4 d + 2 d W gain, bias and conv gradient elements each, summed over batch
+// rows and runs in a fixed order; block y = slices - 1 applies the ZOH
+// chain rule from g_abar,
 // g_bbar (summed over batch rows and channel groups) to lambda, B and
 // log_dt:
 //   g_lambda = conj(Delta abar) g_abar + conj(B Delta^2 phi(Delta lambda)) g_bbar
@@ -869,20 +933,23 @@ __global__ __launch_bounds__(kRedThreads) void bwd_param_kernel(Problem p, idatt
     __shared__ double ldt[kRedThreads];
     const int64_t h = blockIdx.x, H = p.H, B = p.B, M = p.M;
     const int d = static_cast<int>(p.d), W = static_cast<int>(p.W);
-    for (int e = threadIdx.x; e < 4 * d; e += kRedThreads) {
-        double acc = 0.0;
-        for (int64_t b = 0; b < B; ++b)
-            for (int64_t r = 0; r < runs; ++r) acc += part_f[((b * H + h) * runs + r) * 4 * d + e];
-        const int half = e / d, c = e % d;  // gain key, gain value, bias key, bias value
-        float* dst = half < 2 ? out.gain : out.bias;
-        dst[h * 2 * d + (half & 1) * d + c] = static_cast<float>(acc);
-    }
-    for (int e = threadIdx.x; e < 2 * d * W; e += kRedThreads) {
-        double acc = 0.0;
-        for (int64_t b = 0; b < B; ++b)
-            for (int64_t r = 0; r < runs; ++r) acc += part_c[((b * H + h) * runs + r) * 2 * d * W + e];
-        const int sel = e / (d * W), rest = e % (d * W);
-        (sel == 0 ? out.conv_q : out.conv_k)[h * d * W + rest] = static_cast<float>(acc);
+    if (blockIdx.y + 1 < gridDim.y) {
+        const int e = static_cast<int>(blockIdx.y) * kRedThreads + static_cast<int>(threadIdx.x);
+        if (e < 4 * d) {
+            double acc = 0.0;
+            for (int64_t b = 0; b < B; ++b) sum_runs(part_f + (b * H + h) * runs * 4 * d + e, 4 * d, runs, acc);
+            const int half = e / d, c = e % d;  // gain key, gain value, bias key, bias value
+            float* dst = half < 2 ? out.gain : out.bias;
+            dst[h * 2 * d + (half & 1) * d + c] = static_cast<float>(acc);
+        } else if (e < 4 * d + 2 * d * W) {
+            const int ec = e - 4 * d;
+            double acc = 0.0;
+            for (int64_t b = 0; b < B; ++b)
+                sum_runs(part_c + (b * H + h) * runs * 2 * d * W + ec, 2 * d * W, runs, acc);
+            const int sel = ec / (d * W), rest = ec % (d * W);
+            (sel == 0 ? out.conv_q : out.conv_k)[h * d * W + rest] = static_cast<float>(acc);
+        }
+        return;
     }
     double my_ldt = 0.0;
     for (int64_t m = threadIdx.x; m < M; m += kRedThreads) {
@@ -1049,7 +1116,8 @@ hipError_t launch_backward(const Problem& p, const idattn_params& prm, const voi
     }
 #undef IDATTN_BF
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    bwd_param_kernel<<<dim3(static_cast<unsigned>(p.H)), kRedThreads, 0, stream>>>(p, prm, part_f, part_c, ga, gbk, gbv,
+    const unsigned slices = static_cast<unsigned>((4 * p.d + 2 * p.d * p.W + kRedThreads - 1) / kRedThreads + 1);
+    bwd_param_kernel<<<dim3(static_cast<unsigned>(p.H), slices), kRedThreads, 0, stream>>>(p, prm, part_f, part_c, ga, gbk, gbv,
                                                                                    runs, groups, grads);
     return hipGetLastError();
 }
