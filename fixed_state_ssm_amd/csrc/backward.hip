@@ -35,7 +35,6 @@ constexpr int kTok = 8;    // tokens loaded ahead in the per-mode scans
 constexpr int kBlk = 16;   // tokens per LDS round of the per-channel scans
 constexpr int kVW = 16;    // waves per per-channel scan block
 constexpr int kRun = 64;   // tokens per wave in the feature and conv kernels
-constexpr int kWMax = 8;   // largest conv width
 
 __device__ __forceinline__ Zoh zoh_of(const idattn_params& prm, int64_t h, int64_t M, int64_t m) {
     return zoh_mode(prm.log_dt[h], prm.A[(h * M + m) * 2], prm.A[(h * M + m) * 2 + 1], prm.Bc[(h * M + m) * 2],
@@ -626,7 +625,9 @@ __global__ __launch_bounds__(kStage) void bwd_adjoint_kernel(Problem p, idattn_p
 // g_c of queries and keys overwrite g_xi and g_z_k in place (same token, same
 // lanes); the run's sums for the gain and bias gradients go to
 // part [B H][runs][4 d]: gain key half, gain value half, bias key, bias value.
-template <bool BF16, int DJ>
+// WT: the conv width when it is fixed at compile time (4), else 0 (any W,
+// with kConvMax taps of which the first W are used).
+template <bool BF16, int DJ, int WT>
 __global__ __launch_bounds__(256) void bwd_feature_kernel(Problem p, idattn_params prm, const void* __restrict__ q,
                                                           const void* __restrict__ k, const void* __restrict__ v,
                                                           const void* __restrict__ tail_in,
@@ -634,15 +635,27 @@ __global__ __launch_bounds__(256) void bwd_feature_kernel(Problem p, idattn_para
                                                           const float* __restrict__ g_zv, int64_t zs,
                                                           void* __restrict__ grad_v,
                                                           float* __restrict__ part, int64_t runs) {
+    constexpr int NT = WT > 0 ? WT : kConvMax;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     const int64_t H = p.H, N = p.N;
-    const int d = static_cast<int>(p.d), W = static_cast<int>(p.W);
+    const int d = static_cast<int>(p.d), W = WT > 0 ? WT : static_cast<int>(p.W);
     if (wid >= p.B * H * runs) return;  // whole wave; no barriers below
     const int64_t bh = wid / runs, run = wid % runs;
     const int64_t b = bh / H, h = bh % H;
     const int64_t t0 = run * kRun, t1 = t0 + kRun < N ? t0 + kRun : N;
     const int64_t row0 = h * p.T + b * N;
+    int cl[DJ];  // the lane's channels, clamped below d
+    float wq[NT][DJ], wk[NT][DJ];
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+        cl[j] = min(lane + kWave * j, d - 1);
+#pragma unroll
+        for (int j2 = 0; j2 < NT; ++j2) {
+            wq[j2][j] = prm.conv_q[(h * d + cl[j]) * W + min(j2, W - 1)];
+            wk[j2][j] = prm.conv_k[(h * d + cl[j]) * W + min(j2, W - 1)];
+        }
+    }
     float gk[DJ], bk[DJ], gv[DJ], bv[DJ];  // this head's gain and bias
     float agk[DJ], abk[DJ], agv[DJ], abv[DJ];
 #pragma unroll
@@ -659,34 +672,48 @@ __global__ __launch_bounds__(256) void bwd_feature_kernel(Problem p, idattn_para
     (void)bv;
     const float inv_d = 1.f / static_cast<float>(d);
     for (int64_t t = t0; t < t1; ++t) {
+        // every load of the token first (channels clamped below d, missing rows
+        // masked): the conv taps of q and k, v, and the scans' gradients
+        uint32_t xq_raw[NT][DJ], xk_raw[NT][DJ], v_raw[DJ];
+        bool tap_ok[NT];
+#pragma unroll
+        for (int j2 = 0; j2 < NT; ++j2) {
+            const ConvRow r = conv_row(q, k, tail_in, b * N, t - (W - 1) + j2, b * N + t, b, h, H, d, W, j2 < W);
+            tap_ok[j2] = r.ok;
+#pragma unroll
+            for (int j = 0; j < DJ; ++j) {
+                xq_raw[j2][j] = load_raw<BF16>(r.bq, r.rq + cl[j]);
+                xk_raw[j2][j] = load_raw<BF16>(r.bk, r.rk + cl[j]);
+            }
+        }
+        float gzk[DJ], gzv[DJ], gxq[DJ];
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            v_raw[j] = load_raw<BF16>(v, ((b * N + t) * H + h) * d + cl[j]);
+            // the scans' partial sums over the two mode splits, added in a fixed
+            // order (zs = 0: one split)
+            const int64_t o = (row0 + t) * d + cl[j];
+            const float zk0 = g_zk[o], zk1 = g_zk[o + zs];
+            const float zv0 = g_zv[o], zv1 = g_zv[o + zs];
+            const float xq0 = g_xi[o], xq1 = g_xi[o + zs];
+            gzk[j] = zs ? zk0 + zk1 : zk0;
+            gzv[j] = zs ? zv0 + zv1 : zv0;
+            gxq[j] = zs ? xq0 + xq1 : xq0;
+        }
         float cq[DJ], ck[DJ], vv[DJ];
 #pragma unroll
         for (int j = 0; j < DJ; ++j) {
-            const int c = lane + kWave * j;
-            float aq = 0.f, ak = 0.f, xv = 0.f;
-            if (c < d) {
-                const float* wq = prm.conv_q + (h * d + c) * W;
-                const float* wk = prm.conv_k + (h * d + c) * W;
-                for (int j2 = 0; j2 < W; ++j2) {
-                    const int64_t pos = t - (W - 1) + j2;
-                    float xq = 0.f, xk = 0.f;
-                    if (pos >= 0) {
-                        const int64_t idx = ((b * N + pos) * H + h) * d + c;
-                        xq = load_io<BF16>(q, idx);
-                        xk = load_io<BF16>(k, idx);
-                    } else if (tail_in != nullptr) {
-                        const int64_t tq = ((b * H + h) * 2 * (W - 1) + (W - 1 + pos)) * d + c;
-                        xq = load_io<BF16>(tail_in, tq);
-                        xk = load_io<BF16>(tail_in, tq + static_cast<int64_t>(W - 1) * d);
-                    }
-                    aq = fmaf(wq[j2], xq, aq);
-                    ak = fmaf(wk[j2], xk, ak);
-                }
-                xv = load_io<BF16>(v, ((b * N + t) * H + h) * d + c);
+            const bool in = lane + kWave * j < d;  // lanes past d hold zeros
+            float aq = 0.f, ak = 0.f;
+#pragma unroll
+            for (int j2 = 0; j2 < NT; ++j2) {
+                aq = fmaf(wq[j2][j], tap_ok[j2] ? widen<BF16>(xq_raw[j2][j]) : 0.f, aq);
+                ak = fmaf(wk[j2][j], tap_ok[j2] ? widen<BF16>(xk_raw[j2][j]) : 0.f, ak);
             }
-            cq[j] = aq;
-            ck[j] = ak;
-            vv[j] = xv;
+            cq[j] = in ? aq : 0.f;
+            ck[j] = in ? ak : 0.f;
+            vv[j] = in ? widen<BF16>(v_raw[j]) : 0.f;
+            if (!in) gzk[j] = gzv[j] = gxq[j] = 0.f;
         }
         // forward quantities: y = SiLU(c) with its sigmoid, norms
         float sq[DJ], sk[DJ], yq[DJ], yk[DJ];
@@ -707,20 +734,12 @@ __global__ __launch_bounds__(256) void bwd_feature_kernel(Problem p, idattn_para
         const float Dq = p.unit_feat ? sqrtf(nq + p.eps_feat) : nq + p.eps_feat;
         const float Dk = p.unit_feat ? sqrtf(nk + p.eps_feat) : nk + p.eps_feat;
         const float iDk = 1.f / Dk;
-        float xk[DJ], gzk[DJ], gzv[DJ], gxq[DJ];
+        float xk[DJ];
         float nxk = 0.f;
 #pragma unroll
         for (int j = 0; j < DJ; ++j) {
-            const int c = lane + kWave * j;
-            const bool in = c < d;
             xk[j] = yk[j] * iDk;
             nxk = fmaf(xk[j], xk[j], nxk);
-            // the scans' partial sums over the two mode splits, added in a fixed order
-            // (zs = 0: one split)
-            const int64_t o = (row0 + t) * d + c;
-            gzk[j] = in ? (zs ? g_zk[o] + g_zk[o + zs] : g_zk[o]) : 0.f;
-            gzv[j] = in ? (zs ? g_zv[o] + g_zv[o + zs] : g_zv[o]) : 0.f;
-            gxq[j] = in ? (zs ? g_xi[o] + g_xi[o + zs] : g_xi[o]) : 0.f;
         }
         nxk = wave_total(nxk);
         const float rk = 1.f / sqrtf(nxk * inv_d + p.eps_norm);
@@ -787,67 +806,81 @@ __global__ __launch_bounds__(256) void bwd_feature_kernel(Problem p, idattn_para
 //   g_w[c][j] += g_c(t)_c x(t - W + 1 + j)_c         (x before position 0 from the tail)
 // for queries (g_c in g_cq) and keys (g_ck); partial weight gradients to
 // part [B H][runs][2][d][W].
-template <bool BF16, int DJ>
+// WT as for the feature kernel.
+template <bool BF16, int DJ, int WT>
 __global__ __launch_bounds__(256) void bwd_conv_kernel(Problem p, idattn_params prm, const void* __restrict__ q,
                                                        const void* __restrict__ k, const void* __restrict__ tail_in,
                                                        const float* __restrict__ g_cq, const float* __restrict__ g_ck,
                                                        void* __restrict__ grad_q, void* __restrict__ grad_k,
                                                        float* __restrict__ part, int64_t runs) {
+    constexpr int NT = WT > 0 ? WT : kConvMax;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     const int64_t H = p.H, N = p.N;
-    const int d = static_cast<int>(p.d), W = static_cast<int>(p.W);
+    const int d = static_cast<int>(p.d), W = WT > 0 ? WT : static_cast<int>(p.W);
     if (wid >= p.B * H * runs) return;  // whole wave; no barriers below
     const int64_t bh = wid / runs, run = wid % runs;
     const int64_t b = bh / H, h = bh % H;
     const int64_t t0 = run * kRun, t1 = t0 + kRun < N ? t0 + kRun : N;
     const int64_t row0 = h * p.T + b * N;
-    float wq[DJ][kWMax], wk[DJ][kWMax], aq[DJ][kWMax], ak[DJ][kWMax];
+    int cl[DJ];  // the lane's channels, clamped below d
+    float wq[NT][DJ], wk[NT][DJ], aq[NT][DJ], ak[NT][DJ];
 #pragma unroll
     for (int j = 0; j < DJ; ++j) {
-        const int c = lane + kWave * j;
+        cl[j] = min(lane + kWave * j, d - 1);
 #pragma unroll
-        for (int e = 0; e < kWMax; ++e) {
-            const bool ok = c < d && e < W;
-            wq[j][e] = ok ? prm.conv_q[(h * d + c) * W + e] : 0.f;
-            wk[j][e] = ok ? prm.conv_k[(h * d + c) * W + e] : 0.f;
-            aq[j][e] = ak[j][e] = 0.f;
+        for (int e = 0; e < NT; ++e) {
+            wq[e][j] = prm.conv_q[(h * d + cl[j]) * W + min(e, W - 1)];
+            wk[e][j] = prm.conv_k[(h * d + cl[j]) * W + min(e, W - 1)];
+            aq[e][j] = ak[e][j] = 0.f;
         }
     }
     for (int64_t t = t0; t < t1; ++t) {
+        // every load of the token first (indices clamped, missing taps masked):
+        // g_c at t + W - 1 - e (tap e of the later tokens that read x(t)), the
+        // conv inputs x(t - W + 1 + e) that tap e of token t reads, g_c(t)
+        float gq[NT][DJ], gk[NT][DJ];
+        uint32_t xq_raw[NT][DJ], xk_raw[NT][DJ];
+        bool g_ok[NT], x_ok[NT];
+#pragma unroll
+        for (int e = 0; e < NT; ++e) {
+            const int64_t tt = t + W - 1 - e;
+            g_ok[e] = e < W && tt < N;
+            const int64_t gr = (row0 + max(min(tt, N - 1), int64_t{0})) * d;
+            const ConvRow r = conv_row(q, k, tail_in, b * N, t - (W - 1) + e, b * N + t, b, h, H, d, W, e < W);
+            x_ok[e] = r.ok;
+#pragma unroll
+            for (int j = 0; j < DJ; ++j) {
+                gq[e][j] = g_cq[gr + cl[j]];
+                gk[e][j] = g_ck[gr + cl[j]];
+                xq_raw[e][j] = load_raw<BF16>(r.bq, r.rq + cl[j]);
+                xk_raw[e][j] = load_raw<BF16>(r.bk, r.rk + cl[j]);
+            }
+        }
+        float gq_t[DJ], gk_t[DJ];
 #pragma unroll
         for (int j = 0; j < DJ; ++j) {
-            const int c = lane + kWave * j;
-            if (c >= d) continue;
-            const float gq_t = g_cq[(row0 + t) * d + c], gk_t = g_ck[(row0 + t) * d + c];
+            gq_t[j] = g_cq[(row0 + t) * d + cl[j]];
+            gk_t[j] = g_ck[(row0 + t) * d + cl[j]];
+        }
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
             float sq = 0.f, sk = 0.f;
 #pragma unroll
-            for (int e = 0; e < kWMax; ++e) {
-                if (e >= W) break;
+            for (int e = 0; e < NT; ++e) {
                 // g_x(t) takes g_c(t + W - 1 - e) through tap e
-                const int64_t tt = t + W - 1 - e;
-                if (tt < N) {
-                    sq = fmaf(wq[j][e], g_cq[(row0 + tt) * d + c], sq);
-                    sk = fmaf(wk[j][e], g_ck[(row0 + tt) * d + c], sk);
-                }
+                sq = fmaf(wq[e][j], g_ok[e] ? gq[e][j] : 0.f, sq);
+                sk = fmaf(wk[e][j], g_ok[e] ? gk[e][j] : 0.f, sk);
                 // tap e of token t reads x(t - W + 1 + e)
-                const int64_t pos = t - (W - 1) + e;
-                float xq = 0.f, xk = 0.f;
-                if (pos >= 0) {
-                    const int64_t idx = ((b * N + pos) * H + h) * d + c;
-                    xq = load_io<BF16>(q, idx);
-                    xk = load_io<BF16>(k, idx);
-                } else if (tail_in != nullptr) {
-                    const int64_t tq = ((b * H + h) * 2 * (W - 1) + (W - 1 + pos)) * d + c;
-                    xq = load_io<BF16>(tail_in, tq);
-                    xk = load_io<BF16>(tail_in, tq + static_cast<int64_t>(W - 1) * d);
-                }
-                aq[j][e] = fmaf(gq_t, xq, aq[j][e]);
-                ak[j][e] = fmaf(gk_t, xk, ak[j][e]);
+                aq[e][j] = fmaf(gq_t[j], x_ok[e] ? widen<BF16>(xq_raw[e][j]) : 0.f, aq[e][j]);
+                ak[e][j] = fmaf(gk_t[j], x_ok[e] ? widen<BF16>(xk_raw[e][j]) : 0.f, ak[e][j]);
             }
-            const int64_t o = ((b * N + t) * H + h) * d + c;
-            store_io<BF16>(grad_q, o, sq);
-            store_io<BF16>(grad_k, o, sk);
+            const int c = lane + kWave * j;
+            if (c < d) {
+                const int64_t o = ((b * N + t) * H + h) * d + c;
+                store_io<BF16>(grad_q, o, sq);
+                store_io<BF16>(grad_k, o, sk);
+            }
         }
     }
     float* pp = part + wid * 2 * d * W;
@@ -856,10 +889,10 @@ __global__ __launch_bounds__(256) void bwd_conv_kernel(Problem p, idattn_params 
         const int c = lane + kWave * j;
         if (c >= d) continue;
 #pragma unroll
-        for (int e = 0; e < kWMax; ++e) {
+        for (int e = 0; e < NT; ++e) {
             if (e >= W) break;
-            pp[c * W + e] = aq[j][e];
-            pp[d * W + c * W + e] = ak[j][e];
+            pp[c * W + e] = aq[e][j];
+            pp[d * W + c * W + e] = ak[e][j];
         }
     }
 }
@@ -1103,10 +1136,16 @@ hipError_t launch_backward(const Problem& p, const idattn_params& prm, const voi
 #undef IDATTN_BA
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 gr(static_cast<unsigned>((bh * runs + 3) / 4));
-#define IDATTN_BF(BF, DJ)                                                                                            \
-    bwd_feature_kernel<BF, DJ><<<gr, 256, 0, stream>>>(p, prm, q, k, v, tail_in, g_xi, g_zk, g_zv, zs, grad_v, part_f, \
-                                                       runs);                                                        \
-    bwd_conv_kernel<BF, DJ><<<gr, 256, 0, stream>>>(p, prm, q, k, tail_in, g_xi, g_zk, grad_q, grad_k, part_c, runs)
+#define IDATTN_BFW(BF, DJ, WT)                                                                                    \
+    bwd_feature_kernel<BF, DJ, WT><<<gr, 256, 0, stream>>>(p, prm, q, k, v, tail_in, g_xi, g_zk, g_zv, zs, grad_v,   \
+                                                           part_f, runs);                                            \
+    bwd_conv_kernel<BF, DJ, WT><<<gr, 256, 0, stream>>>(p, prm, q, k, tail_in, g_xi, g_zk, grad_q, grad_k, part_c, runs)
+#define IDATTN_BF(BF, DJ)          \
+    if (p.W == 4) {                \
+        IDATTN_BFW(BF, DJ, 4);     \
+    } else {                       \
+        IDATTN_BFW(BF, DJ, 0);     \
+    }
     if (p.d > 64) {
         if (p.bf16) { IDATTN_BF(true, 2); }
         else { IDATTN_BF(false, 2); }
@@ -1115,6 +1154,7 @@ hipError_t launch_backward(const Problem& p, const idattn_params& prm, const voi
         else { IDATTN_BF(false, 1); }
     }
 #undef IDATTN_BF
+#undef IDATTN_BFW
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const unsigned slices = static_cast<unsigned>((4 * p.d + 2 * p.d * p.W + kRedThreads - 1) / kRedThreads + 1);
     bwd_param_kernel<<<dim3(static_cast<unsigned>(p.H), slices), kRedThreads, 0, stream>>>(p, prm, part_f, part_c, ga, gbk, gbv,

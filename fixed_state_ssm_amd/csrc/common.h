@@ -27,6 +27,58 @@ __device__ __forceinline__ float load_io(const void* base, int64_t idx) {
     else return static_cast<const float*>(base)[idx];
 }
 
+// An element of an I/O tensor as loaded (bf16 bits in the low half, or fp32
+// bits), widened where it is used, so that a batch of loads can all be issued
+// before the first wait.
+template <bool BF16>
+__device__ __forceinline__ uint32_t load_raw(const void* base, int64_t idx) {
+    if constexpr (BF16) return static_cast<const uint16_t*>(base)[idx];
+    else return static_cast<const uint32_t*>(base)[idx];
+}
+template <bool BF16>
+__device__ __forceinline__ float widen(uint32_t raw) {
+    return __uint_as_float(BF16 ? raw << 16 : raw);
+}
+
+// ------------------------------------------------------------------ conv rows
+constexpr int kConvMax = 8;  // largest conv width W
+
+// Where a conv tap of head h reads its input row: sequence position pos >= 0
+// is token tok0 + pos of q and k ([T][H][d]); the W - 1 positions before the
+// sequence come from its conv tail ([B H][2][W - 1][d], q rows then k rows)
+// when one is given.  A tap that reads nothing (real false, or no row) gets
+// the row of token fallback_tok, so that its loads stay in bounds and can be
+// issued unconditionally, and ok false, so that the caller zeroes them.  All
+// arguments are uniform over the wave, and so is the result.
+struct ConvRow {
+    const void* bq;
+    const void* bk;
+    int64_t rq, rk;  // element offsets of the rows in bq, bk
+    bool ok;
+};
+__device__ __forceinline__ ConvRow conv_row(const void* q, const void* k, const void* tail, int64_t tok0,
+                                            int64_t pos, int64_t fallback_tok, int64_t b, int64_t h, int64_t H,
+                                            int d, int W, bool real) {
+    ConvRow r;
+    if (real && pos >= 0) {
+        r.bq = q;
+        r.bk = k;
+        r.rq = r.rk = ((tok0 + pos) * H + h) * d;
+        r.ok = true;
+    } else if (real && tail != nullptr && pos >= -(W - 1)) {
+        r.bq = r.bk = tail;
+        r.rq = ((b * H + h) * 2 * (W - 1) + (W - 1 + pos)) * d;
+        r.rk = r.rq + static_cast<int64_t>(W - 1) * d;
+        r.ok = true;
+    } else {
+        r.bq = q;
+        r.bk = k;
+        r.rq = r.rk = (fallback_tok * H + h) * d;
+        r.ok = false;
+    }
+    return r;
+}
+
 template <bool BF16>
 __device__ __forceinline__ void store_io(void* base, int64_t idx, float x) {
     if constexpr (BF16) static_cast<uint16_t*>(base)[idx] = f32_to_bf16(x);

@@ -17,15 +17,18 @@ namespace idattn {
 
 namespace {
 
-template <bool BF16, int DJ>
+// WT: the conv width when it is fixed at compile time (4), else 0 (any W,
+// with kConvMax taps of which the first W are used).
+template <bool BF16, int DJ, int WT>
 __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
     Problem p, idattn_params prm, const void* __restrict__ q, const void* __restrict__ k,
     const void* __restrict__ v, const void* __restrict__ tail_in, float* __restrict__ xi_q,
     float* __restrict__ z_k, float* __restrict__ z_v) {
+    constexpr int NT = WT > 0 ? WT : kConvMax;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t th = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     const int64_t H = p.H, T = p.T;
-    const int d = static_cast<int>(p.d), W = static_cast<int>(p.W);
+    const int d = static_cast<int>(p.d), W = WT > 0 ? WT : static_cast<int>(p.W);
     if (th >= T * H) return;  // whole wave exits; no barriers below
     const int64_t h = th % H;
     const int64_t t = th / H;  // token on the [T] axis
@@ -34,36 +37,44 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
     seq_range(p.cu, p.N, T, b, start, len);
     const int64_t n = t >= start ? t - start : 0;  // position in its sequence (0 <= n <= t)
 
+    // every load first (channels clamped below d, missing rows masked below):
+    // the conv taps of q and k, their weights, v
+    int cl[DJ];
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) cl[j] = min(lane + kWave * j, d - 1);
+    uint32_t xq_raw[NT][DJ], xk_raw[NT][DJ], v_raw[DJ];
+    float wq[NT][DJ], wk[NT][DJ];
+    bool tap_ok[NT];
+#pragma unroll
+    for (int j2 = 0; j2 < NT; ++j2) {
+        const ConvRow r = conv_row(q, k, tail_in, t - n, n - (W - 1) + j2, t, b, h, H, d, W, j2 < W);
+        tap_ok[j2] = r.ok;
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            xq_raw[j2][j] = load_raw<BF16>(r.bq, r.rq + cl[j]);
+            xk_raw[j2][j] = load_raw<BF16>(r.bk, r.rk + cl[j]);
+            wq[j2][j] = prm.conv_q[(h * d + cl[j]) * W + min(j2, W - 1)];
+            wk[j2][j] = prm.conv_k[(h * d + cl[j]) * W + min(j2, W - 1)];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) v_raw[j] = load_raw<BF16>(v, (t * H + h) * d + cl[j]);
+
     float cqv[DJ], ckv[DJ], yq[DJ], yk[DJ], xv[DJ];
     float sv = 0.f;
 #pragma unroll
     for (int j = 0; j < DJ; ++j) {
-        const int c = lane + kWave * j;
-        float cq = 0.f, ck = 0.f, vv = 0.f;
-        if (c < d) {
-            const float* wq = prm.conv_q + (h * d + c) * W;
-            const float* wk = prm.conv_k + (h * d + c) * W;
-            for (int j2 = 0; j2 < W; ++j2) {
-                const int64_t pos = n - (W - 1) + j2;
-                float xq = 0.f, xk = 0.f;
-                if (pos >= 0) {
-                    const int64_t idx = ((t - (W - 1) + j2) * H + h) * d + c;  // token t - n + pos
-                    xq = load_io<BF16>(q, idx);
-                    xk = load_io<BF16>(k, idx);
-                } else if (tail_in != nullptr) {
-                    const int64_t tq = ((b * H + h) * 2 * (W - 1) + (W - 1 + pos)) * d + c;
-                    xq = load_io<BF16>(tail_in, tq);
-                    xk = load_io<BF16>(tail_in, tq + static_cast<int64_t>(W - 1) * d);
-                }
-                cq = fmaf(wq[j2], xq, cq);
-                ck = fmaf(wk[j2], xk, ck);
-            }
-            vv = load_io<BF16>(v, (t * H + h) * d + c);
+        float cq = 0.f, ck = 0.f;
+#pragma unroll
+        for (int j2 = 0; j2 < NT; ++j2) {
+            cq = fmaf(wq[j2][j], tap_ok[j2] ? widen<BF16>(xq_raw[j2][j]) : 0.f, cq);
+            ck = fmaf(wk[j2][j], tap_ok[j2] ? widen<BF16>(xk_raw[j2][j]) : 0.f, ck);
         }
-        cqv[j] = cq;
-        ckv[j] = ck;
-        xv[j] = vv;
-        sv = fmaf(vv, vv, sv);
+        const bool in = lane + kWave * j < d;  // lanes past d hold zeros
+        cqv[j] = in ? cq : 0.f;
+        ckv[j] = in ? ck : 0.f;
+        xv[j] = in ? widen<BF16>(v_raw[j]) : 0.f;
+        sv = fmaf(xv[j], xv[j], sv);
     }
     sv = wave_total(sv);
     // xi = y * inv with y = SiLU(c) = c / (1 + exp(-c)); lanes past d hold c = 0 -> y = 0.
@@ -255,17 +266,23 @@ hipError_t launch_featmap_conv_norm(const Problem& p, const idattn_params& prm, 
     }
     const int64_t th = p.T * p.H;
     const dim3 grid(static_cast<unsigned>((th + 3) / 4));
+#define IDATTN_FM(BF, DJ, WT) featmap_conv_norm_kernel<BF, DJ, WT><<<grid, 256, 0, stream>>>(p, prm, q, k, v, tail_in, xi_q, z_k, z_v)
+#define IDATTN_FMW(BF, DJ) \
+    do {                   \
+        if (p.W == 4)      \
+            IDATTN_FM(BF, DJ, 4); \
+        else               \
+            IDATTN_FM(BF, DJ, 0); \
+    } while (0)
     if (p.d > 64) {
-        if (p.bf16)
-            featmap_conv_norm_kernel<true, 2><<<grid, 256, 0, stream>>>(p, prm, q, k, v, tail_in, xi_q, z_k, z_v);
-        else
-            featmap_conv_norm_kernel<false, 2><<<grid, 256, 0, stream>>>(p, prm, q, k, v, tail_in, xi_q, z_k, z_v);
+        if (p.bf16) IDATTN_FMW(true, 2);
+        else IDATTN_FMW(false, 2);
     } else {
-        if (p.bf16)
-            featmap_conv_norm_kernel<true, 1><<<grid, 256, 0, stream>>>(p, prm, q, k, v, tail_in, xi_q, z_k, z_v);
-        else
-            featmap_conv_norm_kernel<false, 1><<<grid, 256, 0, stream>>>(p, prm, q, k, v, tail_in, xi_q, z_k, z_v);
+        if (p.bf16) IDATTN_FMW(true, 1);
+        else IDATTN_FMW(false, 1);
     }
+#undef IDATTN_FMW
+#undef IDATTN_FM
     return hipGetLastError();
 }
 
