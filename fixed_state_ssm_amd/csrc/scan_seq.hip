@@ -3,8 +3,9 @@
 // recurrence) and the reference the chunked path is compared with.
 //
 // ssm_key_scan_seq: one wave per (b, h, mode m); lane l owns channels l, l+64
-// of U_m.  Each step updates U_m(i) = abar U_m(i-1) + bbar z_k(i) and reduces
-// s_m(i) = xi_q(i) . U_m(i) over the R channels with a wave butterfly.  With
+// of U_m.  Each step updates U_m(i) = abar U_m(i-1) + bbar z_k(i); the lanes'
+// shares of s_m(i) = xi_q(i) . U_m(i) over the R channels are reduced eight
+// tokens at a time with one reduce-scatter per quantity.  With
 // the normalised readout (ETA) the wave also carries the mode's normaliser
 // eta_m(i) = abar eta_m(i-1) + bbar and writes Re(s_m(i) eta_m(i)), the mode's
 // share of the denominator; it alone reads and writes eta_m, so eta may be
@@ -24,7 +25,43 @@ namespace idattn {
 
 namespace {
 
-constexpr int kTok = 8;  // tokens whose inputs are loaded ahead of the key recurrence
+constexpr int kTok = 8;  // tokens per batch of the key recurrence
+
+// One batch of the key recurrence: the lane's shares of s for each token and,
+// with ETA, the normaliser stepped along (the same in every lane); lane l keeps
+// eta after token slot8(l) in etr, eti.  A ragged batch steps only its first
+// nt tokens.
+template <int RJ, bool ETA, bool RAGGED>
+__device__ __forceinline__ void key_seq_batch(int nt, int ts, float (&ur)[RJ], float (&ui)[RJ],
+                                              const float (&xv)[kTok][RJ], const float (&zv)[kTok][RJ], float ar,
+                                              float ai, float br, float bi, float (&spr)[kTok], float (&spi)[kTok],
+                                              float& er, float& ei, float& etr, float& eti) {
+#pragma unroll
+    for (int t = 0; t < kTok; ++t) {
+        float pr = 0.f, pi = 0.f;
+        if (!RAGGED || t < nt) {
+#pragma unroll
+            for (int j = 0; j < RJ; ++j) {
+                const float nr = fmaf(ar, ur[j], fmaf(-ai, ui[j], br * zv[t][j]));
+                const float ni = fmaf(ar, ui[j], fmaf(ai, ur[j], bi * zv[t][j]));
+                ur[j] = nr;
+                ui[j] = ni;
+                pr = fmaf(xv[t][j], nr, pr);
+                pi = fmaf(xv[t][j], ni, pi);
+            }
+            if constexpr (ETA) {
+                const float nr = fmaf(ar, er, fmaf(-ai, ei, br));
+                const float ni = fmaf(ar, ei, fmaf(ai, er, bi));
+                er = nr;
+                ei = ni;
+                etr = t == ts ? nr : etr;
+                eti = t == ts ? ni : eti;
+            }
+        }
+        spr[t] = pr;
+        spi[t] = pi;
+    }
+}
 
 template <int RJ, bool ETA>
 __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_params prm,
@@ -60,48 +97,50 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
         }
     }
     const int64_t row0 = h * p.T + start;  // workspace rows [H][T]
-    const float* xq = xi_q + row0 * d;
-    const float* zk = z_k + row0 * d;
     float2* srow = s + row0 * M + m;
     float er = 0.f, ei = 0.f;  // eta_m, the same in every lane
     if (ETA && eta_in != nullptr) {
         er = eta_in[(bh * M + m) * 2];
         ei = eta_in[(bh * M + m) * 2 + 1];
     }
+    const bool dfull = d == kWave * RJ;
+    const int ts = slot8(lane);  // the token whose totals this lane ends with
+    uint32_t off[RJ];            // the lane's channels (clamped below d)
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) off[j] = static_cast<uint32_t>(min(lane + kWave * j, d - 1));
     for (int64_t i0 = 0; i0 < N; i0 += kTok) {
+        // every load at a token and channel clamped into range, all issued
+        // before the first use; a ragged batch zeroes what lies out of range
+        const int nt = static_cast<int>(min(N - i0, static_cast<int64_t>(kTok)));
         float xv[kTok][RJ], zv[kTok][RJ];
 #pragma unroll
-        for (int t = 0; t < kTok; ++t)
-#pragma unroll
-            for (int j = 0; j < RJ; ++j) {
-                const int r = lane + kWave * j;
-                const bool ok = (i0 + t < N) && (r < d);
-                xv[t][j] = ok ? xq[(i0 + t) * d + r] : 0.f;
-                zv[t][j] = ok ? zk[(i0 + t) * d + r] : 0.f;
-            }
-#pragma unroll
         for (int t = 0; t < kTok; ++t) {
-            if (i0 + t >= N) break;
-            float pr = 0.f, pi = 0.f;
+            const int64_t row = (row0 + i0 + min(t, nt - 1)) * d;  // uniform
+            const float* xr = xi_q + row;
+            const float* zr = z_k + row;
 #pragma unroll
             for (int j = 0; j < RJ; ++j) {
-                const float nr = fmaf(ar, ur[j], fmaf(-ai, ui[j], br * zv[t][j]));
-                const float ni = fmaf(ar, ui[j], fmaf(ai, ur[j], bi * zv[t][j]));
-                ur[j] = nr;
-                ui[j] = ni;
-                pr = fmaf(xv[t][j], nr, pr);
-                pi = fmaf(xv[t][j], ni, pi);
+                xv[t][j] = xr[off[j]];
+                zv[t][j] = zr[off[j]];
             }
-            pr = wave_total(pr);
-            pi = wave_total(pi);
-            if (lane == 0) srow[(i0 + t) * M] = make_float2(pr, pi);
-            if constexpr (ETA) {
-                const float nr = fmaf(ar, er, fmaf(-ai, ei, br));
-                const float ni = fmaf(ar, ei, fmaf(ai, er, bi));
-                er = nr;
-                ei = ni;
-                if (lane == 0) pden[(row0 + i0 + t) * M + m] = fmaf(pr, nr, -pi * ni);
-            }
+        }
+        float spr[kTok], spi[kTok];
+        float etr = 0.f, eti = 0.f;
+        if (nt == kTok && dfull) {
+            key_seq_batch<RJ, ETA, false>(nt, ts, ur, ui, xv, zv, ar, ai, br, bi, spr, spi, er, ei, etr, eti);
+        } else {
+#pragma unroll
+            for (int t = 0; t < kTok; ++t)
+#pragma unroll
+                for (int j = 0; j < RJ; ++j)
+                    if (t >= nt || lane + kWave * j >= d) xv[t][j] = zv[t][j] = 0.f;
+            key_seq_batch<RJ, ETA, true>(nt, ts, ur, ui, xv, zv, ar, ai, br, bi, spr, spi, er, ei, etr, eti);
+        }
+        static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
+        const float pr = wave_reduce_scatter8(spr, lane), pi = wave_reduce_scatter8(spi, lane);
+        if (lane < kTok && ts < nt) {
+            srow[(i0 + ts) * M] = make_float2(pr, pi);
+            if constexpr (ETA) pden[(row0 + i0 + ts) * M + m] = fmaf(pr, etr, -pi * eti);
         }
     }
     if (state_out != nullptr) {
@@ -133,25 +172,89 @@ __device__ __forceinline__ float tree_sum(float (&x)[K]) {
     return x[0];
 }
 
+// The value scan's inputs of one block of tokens go through LDS, one element
+// of each per thread: s and, with ETA, the per-mode denominator shares
+// (kBlk x M), and z_v (kBlk x 64 channels).  The next block's elements are
+// loaded into registers while this block's tokens are stepped; two barriers
+// per block.
+constexpr int kStage = kVW * kWave;  // threads per block = staged elements per input
+static_assert(kBlk * kWave == kStage, "one z_v element per thread");
+static_assert(kBlk * 64 <= kStage, "one s element per thread for M <= 64");
+
+struct SeqStage {
+    float2 s;
+    float z, pd;
+};
+
+// Thread e's elements of the block [i0, i0 + nt): s and pden of (token e / M,
+// mode e % M), z_v of (token e / 64, channel 64 group + e % 64), at indices
+// clamped into the block and below d.
+template <bool ETA>
+__device__ __forceinline__ SeqStage seq_fetch(int64_t row0, int64_t i0, int nt, int M, int d, int group,
+                                              const float2* __restrict__ s, const float* __restrict__ z_v,
+                                              const float* __restrict__ pden) {
+    const int e = static_cast<int>(threadIdx.x);
+    SeqStage r;
+    const int64_t im = (row0 + i0 + min(e / M, nt - 1)) * M + e % M;
+    r.s = s[im];
+    r.pd = ETA ? pden[im] : 0.f;
+    r.z = z_v[(row0 + i0 + min(e / kWave, nt - 1)) * d + min(group * kWave + e % kWave, d - 1)];
+    return r;
+}
+
+// One block of kBlk tokens for the wave's MW modes: Gamma steps forward, the
+// wave's share of o goes to red and, with ETA, its share of the denominator to
+// den.  A ragged block steps only its first nt tokens.
+template <int MW, bool ETA, bool RAGGED>
+__device__ __forceinline__ void value_seq_block(int nt, const float2* s_row, const float* p_row, const float* z_col,
+                                                float (*red_t)[kWave], float* den_t, int lane, const float (&ar)[MW],
+                                                const float (&ai)[MW], const float (&br)[MW], const float (&bi)[MW],
+                                                float (&gr)[MW], float (&gi)[MW], int M) {
+#pragma unroll
+    for (int t = 0; t < kBlk; ++t) {
+        if (RAGGED && t >= nt) continue;
+        const float zz = z_col[t * kWave];
+        float acc = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < MW; ++mm) {
+            const float2 sv = s_row[t * M + mm];
+            const float nr = fmaf(ar[mm], gr[mm], fmaf(-ai[mm], gi[mm], br[mm] * zz));
+            const float ni = fmaf(ar[mm], gi[mm], fmaf(ai[mm], gr[mm], bi[mm] * zz));
+            gr[mm] = nr;
+            gi[mm] = ni;
+            acc = fmaf(sv.x, nr, fmaf(-sv.y, ni, acc));
+        }
+        red_t[t][lane] = acc;
+        if constexpr (ETA) {
+            float dn = 0.f;
+#pragma unroll
+            for (int mm = 0; mm < MW; ++mm) dn += p_row[t * M + mm];
+            if (lane == 0) den_t[t] = dn;
+        }
+    }
+}
+
 // ETA: o = numerator / denominator, the denominator summed over the modes
 // from the key scan's per-mode shares pden [H][T][M].
 template <bool BF16, int MW, bool ETA>
-__global__ __launch_bounds__(kVW * 64) void value_scan_seq_kernel(Problem p, idattn_params prm,
-                                                             const float2* __restrict__ s,
-                                                             const float* __restrict__ z_v,
-                                                             const float* state_in, void* __restrict__ o,
-                                                             float* state_out, const float* __restrict__ pden) {
-    __shared__ float2 s_blk[kBlk * 64];
+__global__ __launch_bounds__(kStage) void value_scan_seq_kernel(Problem p, idattn_params prm,
+                                                                const float2* __restrict__ s,
+                                                                const float* __restrict__ z_v,
+                                                                const float* state_in, void* __restrict__ o,
+                                                                float* state_out, const float* __restrict__ pden) {
+    __shared__ float2 s_blk[kStage];
+    __shared__ float z_blk[kStage];
+    __shared__ float p_blk[ETA ? kStage : 1];
     __shared__ float red[kVW][kBlk][kWave];
-    __shared__ float p_blk[ETA ? kBlk * 64 : 1];
     __shared__ float den_s[kVW][kBlk];
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x >> 6;
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / p.H, h = bh % p.H;
-    const int64_t M = p.M, H = p.H;
-    const int d = static_cast<int>(p.d);
-    const int c = static_cast<int>(blockIdx.y) * kWave + lane;
+    const int64_t H = p.H;
+    const int M = static_cast<int>(p.M), d = static_cast<int>(p.d);
+    const int group = static_cast<int>(blockIdx.y);
+    const int c = group * kWave + lane;
     int64_t start, N;  // this sequence's tokens on the [T] axis
     seq_range(p.cu, p.N, p.T, b, start, N);
     const int64_t row0 = h * p.T + start;  // workspace rows [H][T]
@@ -174,57 +277,51 @@ __global__ __launch_bounds__(kVW * 64) void value_scan_seq_kernel(Problem p, ida
             gi[mm] = state_in[idx + 1];
         }
     }
-    const float* zv = z_v + row0 * d;
-    for (int64_t i0 = 0; i0 < N; i0 += kBlk) {
-        const int nt = static_cast<int>(N - i0 < kBlk ? N - i0 : kBlk);
-        for (int e = threadIdx.x; e < nt * M; e += kVW * 64) s_blk[e] = s[(row0 + i0) * M + e];
-        if constexpr (ETA)
-            for (int e = threadIdx.x; e < nt * M; e += kVW * 64) p_blk[e] = pden[(row0 + i0) * M + e];
-        float zz[kBlk];
+    if (N > 0) {  // uniform over the block
+        const float2* s_row = s_blk + w * MW;
+        const float* p_row = p_blk + (ETA ? w * MW : 0);
+        int64_t i0 = 0;
+        int nt = static_cast<int>(min(N, static_cast<int64_t>(kBlk)));
+        SeqStage nx = seq_fetch<ETA>(row0, i0, nt, M, d, group, s, z_v, pden);
+        while (i0 < N) {
+            {
+                const int e = static_cast<int>(threadIdx.x);
+                const bool mok = e < nt * M;
+                s_blk[e] = mok ? nx.s : make_float2(0.f, 0.f);
+                if constexpr (ETA) p_blk[e] = mok ? nx.pd : 0.f;
+                z_blk[e] = (e / kWave < nt && group * kWave + e % kWave < d) ? nx.z : 0.f;
+            }
+            __syncthreads();
+            const int64_t j0 = i0 + kBlk;  // the next block, loaded while this one runs
+            const int jnt = static_cast<int>(min(N - j0, static_cast<int64_t>(kBlk)));
+            if (j0 < N) nx = seq_fetch<ETA>(row0, j0, jnt, M, d, group, s, z_v, pden);
+            if (nt == kBlk)
+                value_seq_block<MW, ETA, false>(nt, s_row, p_row, z_blk + lane, red[w], den_s[w], lane, ar, ai, br,
+                                                bi, gr, gi, M);
+            else
+                value_seq_block<MW, ETA, true>(nt, s_row, p_row, z_blk + lane, red[w], den_s[w], lane, ar, ai, br,
+                                               bi, gr, gi, M);
+            __syncthreads();
+            for (int e = threadIdx.x; e < nt * kWave; e += kStage) {
+                const int t = e / kWave, l = e % kWave;
+                const int cc = group * kWave + l;
+                if (cc < d) {
+                    // fixed pairwise order over the waves' partial sums
+                    float part[kVW];
 #pragma unroll
-        for (int t = 0; t < kBlk; ++t) zz[t] = (t < nt && cok) ? zv[(i0 + t) * d + c] : 0.f;
-        __syncthreads();
+                    for (int i = 0; i < kVW; ++i) part[i] = red[i][t][l];
+                    float sum = tree_sum(part);
+                    if constexpr (ETA) {
 #pragma unroll
-        for (int t = 0; t < kBlk; ++t) {
-            if (t < nt) {
-                float acc = 0.f;
-#pragma unroll
-                for (int mm = 0; mm < MW; ++mm) {
-                    const float2 sv = s_blk[t * M + w * MW + mm];
-                    const float nr = fmaf(ar[mm], gr[mm], fmaf(-ai[mm], gi[mm], br[mm] * zz[t]));
-                    const float ni = fmaf(ar[mm], gi[mm], fmaf(ai[mm], gr[mm], bi[mm] * zz[t]));
-                    gr[mm] = nr;
-                    gi[mm] = ni;
-                    acc = fmaf(sv.x, nr, fmaf(-sv.y, ni, acc));
-                }
-                red[w][t][lane] = acc;
-                if constexpr (ETA) {
-                    float dn = 0.f;
-#pragma unroll
-                    for (int mm = 0; mm < MW; ++mm) dn += p_blk[t * M + w * MW + mm];
-                    if (lane == 0) den_s[w][t] = dn;
+                        for (int i = 0; i < kVW; ++i) part[i] = den_s[i][t];
+                        sum /= tree_sum(part);
+                    }
+                    store_io<BF16>(o, ((start + i0 + t) * H + h) * d + cc, sum);
                 }
             }
+            i0 = j0;
+            nt = jnt;
         }
-        __syncthreads();
-        for (int e = threadIdx.x; e < nt * kWave; e += kVW * 64) {
-            const int t = e / kWave, l = e % kWave;
-            const int cc = static_cast<int>(blockIdx.y) * kWave + l;
-            if (cc < d) {
-                // fixed pairwise order over the waves' partial sums
-                float part[kVW];
-#pragma unroll
-                for (int i = 0; i < kVW; ++i) part[i] = red[i][t][l];
-                float sum = tree_sum(part);
-                if constexpr (ETA) {
-#pragma unroll
-                    for (int i = 0; i < kVW; ++i) part[i] = den_s[i][t];
-                    sum /= tree_sum(part);
-                }
-                store_io<BF16>(o, ((start + i0 + t) * H + h) * d + cc, sum);
-            }
-        }
-        __syncthreads();
     }
     if (state_out != nullptr && cok) {
 #pragma unroll
@@ -266,9 +363,9 @@ hipError_t launch_ssm_value_scan_readout_seq(const Problem& p, const idattn_para
 #define IDATTN_VSCAN_E(MW, ETA)                                                                  \
     do {                                                                                         \
         if (p.bf16)                                                                              \
-            value_scan_seq_kernel<true, MW, ETA><<<grid, kVW * 64, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out, pden); \
+            value_scan_seq_kernel<true, MW, ETA><<<grid, kStage, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out, pden); \
         else                                                                                     \
-            value_scan_seq_kernel<false, MW, ETA><<<grid, kVW * 64, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out, pden); \
+            value_scan_seq_kernel<false, MW, ETA><<<grid, kStage, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out, pden); \
     } while (0)
 #define IDATTN_VSCAN(MW)                          \
     do {                                          \
