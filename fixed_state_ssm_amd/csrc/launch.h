@@ -38,10 +38,15 @@ hipError_t launch_ssm_key_scan_seq(const Problem& p, const idattn_params& prm,
                                    const float* eta_in, float* eta_out, float* pden,
                                    hipStream_t stream);
 
+// With M >= 32 the modes are split over two blocks whose partial numerators
+// go to num0 and num1 ([H][T][d] fp32 each; the feature buffers xi_q and z_k,
+// free once the key scan has run) and, with pden, whose partial denominators
+// go to dpart ([2][H][T] fp32); a combine kernel forms o.
 hipError_t launch_ssm_value_scan_readout_seq(const Problem& p, const idattn_params& prm,
                                              const float* s, const float* z_v,
                                              const float* state_in, void* o,
-                                             float* state_out, const float* pden, hipStream_t stream);
+                                             float* state_out, const float* pden, float* num0, float* num1,
+                                             float* dpart, hipStream_t stream);
 
 // ---- chunked MFMA path (bf16 I/O; wave-specialised kernels for d = R in
 // {64, 128}, M = 64, W <= 4, the SiLU feature maps)

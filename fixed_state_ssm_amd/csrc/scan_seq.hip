@@ -18,6 +18,8 @@
 // tokens.  Sixteen waves (four per SIMD): there are only B H d/64 blocks,
 // fewer than compute units at the model shapes, so each one needs the latency
 // hiding.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -236,12 +238,17 @@ __device__ __forceinline__ void value_seq_block(int nt, const float2* s_row, con
 
 // ETA: o = numerator / denominator, the denominator summed over the modes
 // from the key scan's per-mode shares pden [H][T][M].
-template <bool BF16, int MW, bool ETA>
+// SPLIT: the modes are split over two blocks (blockIdx.z); split z writes its
+// partial numerator to num0 or num1 ([H][T][d] fp32) and, with ETA, its
+// partial denominator to dpart[z] ([2][H][T]); combine_seq_kernel forms o.
+template <bool BF16, int MW, bool ETA, bool SPLIT>
 __global__ __launch_bounds__(kStage) void value_scan_seq_kernel(Problem p, idattn_params prm,
                                                                 const float2* __restrict__ s,
                                                                 const float* __restrict__ z_v,
                                                                 const float* state_in, void* __restrict__ o,
-                                                                float* state_out, const float* __restrict__ pden) {
+                                                                float* state_out, const float* __restrict__ pden,
+                                                                float* __restrict__ num0, float* __restrict__ num1,
+                                                                float* __restrict__ dpart) {
     __shared__ float2 s_blk[kStage];
     __shared__ float z_blk[kStage];
     __shared__ float p_blk[ETA ? kStage : 1];
@@ -259,11 +266,13 @@ __global__ __launch_bounds__(kStage) void value_scan_seq_kernel(Problem p, idatt
     seq_range(p.cu, p.N, p.T, b, start, N);
     const int64_t row0 = h * p.T + start;  // workspace rows [H][T]
     const bool cok = c < d;
+    const int moff = SPLIT ? static_cast<int>(blockIdx.z) * kVW * MW : 0;  // the split's first mode
+    float* num = blockIdx.z == 0 ? num0 : num1;
 
     float ar[MW], ai[MW], br[MW], bi[MW], gr[MW], gi[MW];
 #pragma unroll
     for (int mm = 0; mm < MW; ++mm) {
-        const int64_t m = w * MW + mm;
+        const int64_t m = moff + w * MW + mm;
         const Zoh z = zoh_mode(prm.log_dt[h], prm.A[(h * M + m) * 2], prm.A[(h * M + m) * 2 + 1],
                                prm.Bc[(h * M + m) * 2], prm.Bc[(h * M + m) * 2 + 1]);
         ar[mm] = static_cast<float>(z.ar);
@@ -278,8 +287,8 @@ __global__ __launch_bounds__(kStage) void value_scan_seq_kernel(Problem p, idatt
         }
     }
     if (N > 0) {  // uniform over the block
-        const float2* s_row = s_blk + w * MW;
-        const float* p_row = p_blk + (ETA ? w * MW : 0);
+        const float2* s_row = s_blk + moff + w * MW;
+        const float* p_row = p_blk + (ETA ? moff + w * MW : 0);
         int64_t i0 = 0;
         int nt = static_cast<int>(min(N, static_cast<int64_t>(kBlk)));
         SeqStage nx = seq_fetch<ETA>(row0, i0, nt, M, d, group, s, z_v, pden);
@@ -311,12 +320,21 @@ __global__ __launch_bounds__(kStage) void value_scan_seq_kernel(Problem p, idatt
 #pragma unroll
                     for (int i = 0; i < kVW; ++i) part[i] = red[i][t][l];
                     float sum = tree_sum(part);
-                    if constexpr (ETA) {
+                    if constexpr (SPLIT) {
+                        num[(row0 + i0 + t) * d + cc] = sum;
+                        if (ETA && l == 0 && group == 0) {
 #pragma unroll
-                        for (int i = 0; i < kVW; ++i) part[i] = den_s[i][t];
-                        sum /= tree_sum(part);
+                            for (int i = 0; i < kVW; ++i) part[i] = den_s[i][t];
+                            dpart[blockIdx.z * H * p.T + row0 + i0 + t] = tree_sum(part);
+                        }
+                    } else {
+                        if constexpr (ETA) {
+#pragma unroll
+                            for (int i = 0; i < kVW; ++i) part[i] = den_s[i][t];
+                            sum /= tree_sum(part);
+                        }
+                        store_io<BF16>(o, ((start + i0 + t) * H + h) * d + cc, sum);
                     }
-                    store_io<BF16>(o, ((start + i0 + t) * H + h) * d + cc, sum);
                 }
             }
             i0 = j0;
@@ -326,10 +344,29 @@ __global__ __launch_bounds__(kStage) void value_scan_seq_kernel(Problem p, idatt
     if (state_out != nullptr && cok) {
 #pragma unroll
         for (int mm = 0; mm < MW; ++mm) {
-            const int64_t idx = ((bh * M + w * MW + mm) * 2 * d + d + c) * 2;
+            const int64_t idx = ((bh * M + moff + w * MW + mm) * 2 * d + d + c) * 2;
             state_out[idx] = gr[mm];
             state_out[idx + 1] = gi[mm];
         }
+    }
+}
+
+// o [T][H][d] from the two splits' partial numerators (and denominators):
+// o = num0 + num1, or (num0 + num1) / (den0 + den1) with ETA.
+template <bool BF16, bool ETA>
+__global__ __launch_bounds__(256) void combine_seq_kernel(Problem p, const float* __restrict__ num0,
+                                                          const float* __restrict__ num1,
+                                                          const float* __restrict__ dpart, void* __restrict__ o) {
+    const int64_t H = p.H, T = p.T, d = p.d;
+    const int64_t n = T * H * d;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
+         e += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t c = e % d, th = e / d;  // o is [T][H][d]
+        const int64_t h = th % H, t = th / H;
+        const int64_t w = (h * T + t) * d + c;  // the partials are [H][T][d]
+        float x = num0[w] + num1[w];
+        if constexpr (ETA) x /= dpart[h * T + t] + dpart[H * T + h * T + t];
+        store_io<BF16>(o, e, x);
     }
 }
 
@@ -357,29 +394,50 @@ hipError_t launch_ssm_key_scan_seq(const Problem& p, const idattn_params& prm, c
 hipError_t launch_ssm_value_scan_readout_seq(const Problem& p, const idattn_params& prm,
                                              const float* s, const float* z_v,
                                              const float* state_in, void* o, float* state_out,
-                                             const float* pden, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(p.B * p.H), static_cast<unsigned>((p.d + kWave - 1) / kWave));
+                                             const float* pden, float* num0, float* num1, float* dpart,
+                                             hipStream_t stream) {
+    // two mode splits when each still gets at least one mode per wave
+    const int splits = p.M >= 2 * kVW ? 2 : 1;
+    const dim3 grid(static_cast<unsigned>(p.B * p.H), static_cast<unsigned>((p.d + kWave - 1) / kWave),
+                    static_cast<unsigned>(splits));
     const float2* s2 = reinterpret_cast<const float2*>(s);
-#define IDATTN_VSCAN_E(MW, ETA)                                                                  \
-    do {                                                                                         \
-        if (p.bf16)                                                                              \
-            value_scan_seq_kernel<true, MW, ETA><<<grid, kStage, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out, pden); \
-        else                                                                                     \
-            value_scan_seq_kernel<false, MW, ETA><<<grid, kStage, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out, pden); \
+#define IDATTN_VSCAN_K(BF, MW, ETA, SPLIT) \
+    value_scan_seq_kernel<BF, MW, ETA, SPLIT><<<grid, kStage, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out, pden, num0, num1, dpart)
+#define IDATTN_VSCAN_E(MW, ETA, SPLIT)                  \
+    do {                                                \
+        if (p.bf16) IDATTN_VSCAN_K(true, MW, ETA, SPLIT); \
+        else IDATTN_VSCAN_K(false, MW, ETA, SPLIT);       \
     } while (0)
-#define IDATTN_VSCAN(MW)                          \
-    do {                                          \
-        if (pden != nullptr) IDATTN_VSCAN_E(MW, true); \
-        else IDATTN_VSCAN_E(MW, false);           \
+#define IDATTN_VSCAN(MW, SPLIT)                                \
+    do {                                                       \
+        if (pden != nullptr) IDATTN_VSCAN_E(MW, true, SPLIT);  \
+        else IDATTN_VSCAN_E(MW, false, SPLIT);                 \
     } while (0)
-    switch (p.M / kVW) {
-        case 1: IDATTN_VSCAN(1); break;
-        case 2: IDATTN_VSCAN(2); break;
-        case 4: IDATTN_VSCAN(4); break;
+    switch (p.M / (kVW * splits)) {
+        case 1:
+            if (splits == 2) IDATTN_VSCAN(1, true);
+            else IDATTN_VSCAN(1, false);
+            break;
+        case 2: IDATTN_VSCAN(2, true); break;
         default: return hipErrorInvalidValue;
     }
 #undef IDATTN_VSCAN
 #undef IDATTN_VSCAN_E
+#undef IDATTN_VSCAN_K
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    const int64_t n = p.T * p.H * p.d;
+    const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 4096));
+    if (n == 0) return hipSuccess;
+#define IDATTN_COMB(BF, ETA) combine_seq_kernel<BF, ETA><<<blocks, 256, 0, stream>>>(p, num0, num1, dpart, o)
+    if (p.bf16) {
+        if (pden != nullptr) IDATTN_COMB(true, true);
+        else IDATTN_COMB(true, false);
+    } else {
+        if (pden != nullptr) IDATTN_COMB(false, true);
+        else IDATTN_COMB(false, false);
+    }
+#undef IDATTN_COMB
     return hipGetLastError();
 }
 
