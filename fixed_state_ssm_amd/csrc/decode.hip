@@ -21,6 +21,17 @@ namespace idattn {
 
 namespace {
 
+// State rows are read and written once per call: non-temporal accesses.
+typedef float f4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream(const float4* p) {
+    const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(const float4& x, float4* p) {
+    const f4v v = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<f4v*>(p));
+}
+
 // ZOH coefficients of one mode, abar = exp(Delta lambda) and
 // bbar = (exp(Delta lambda) - 1) / lambda * B (Delta B when lambda = 0), with
 // Delta and the phase Delta Im(lambda) formed and reduced modulo 2 pi in fp64 and
@@ -283,7 +294,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
             const int f = lane + kWave * j;
-            row[j] = f < nf ? st4[m * nf + f] : make_float4(0.f, 0.f, 0.f, 0.f);
+            row[j] = f < nf ? load_stream(&st4[m * nf + f]) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         const float4 cf = coef_s[m];
         float er = 0.f, ei = 0.f;  // eta_m, the same in every lane
@@ -339,7 +350,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
             const int f = lane + kWave * j;
-            if (f < nf) st4[m * nf + f] = row[j];
+            if (f < nf) store_stream(row[j], &st4[m * nf + f]);
         }
         if (ETA && lane == 0) {
             eta[(bh * M + m) * 2] = er;
