@@ -287,14 +287,25 @@ __global__ __launch_bounds__(256) void decode_step_kernel(Problem p, idattn_para
 #pragma unroll
         for (int j = 0; j < FJ; ++j) acc[t][j][0] = acc[t][j][1] = 0.f;
     }
+    // the next row is loaded while this one is updated
+    float4 nxt[FJ];
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) {
+        const int f = lane + kWave * j;
+        nxt[j] = f < nf ? load_stream(&st4[(w * RPW) * nf + f]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll 1
     for (int rr = 0; rr < RPW; ++rr) {
         const int m = w * RPW + rr;
         float4 row[FJ];
 #pragma unroll
-        for (int j = 0; j < FJ; ++j) {
-            const int f = lane + kWave * j;
-            row[j] = f < nf ? load_stream(&st4[m * nf + f]) : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < FJ; ++j) row[j] = nxt[j];
+        if (rr + 1 < RPW) {
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) {
+                const int f = lane + kWave * j;
+                if (f < nf) nxt[j] = load_stream(&st4[(m + 1) * nf + f]);
+            }
         }
         const float4 cf = coef_s[m];
         float er = 0.f, ei = 0.f;  // eta_m, the same in every lane
