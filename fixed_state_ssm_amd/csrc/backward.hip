@@ -42,8 +42,34 @@ __device__ __forceinline__ Zoh zoh_of(const idattn_params& prm, int64_t h, int64
 }
 
 // ------------------------------------------------------------------ per-mode scans
-// One wave per (b, h, m); lane l owns channels l and l + 64 (RJ of them).
+// One wave per (b, h, m); lane l owns the RJ adjacent channels RJ l .. RJ l +
+// RJ - 1, so that each token's inputs are one load per lane and tensor.
 //
+// RJ adjacent floats (one 4- or 8-byte load), and RJ adjacent elements of an
+// I/O tensor (a bf16 pair in one 4-byte load, or fp32).
+template <int RJ>
+__device__ __forceinline__ void load_pair(float (&x)[RJ], const float* p) {
+    if constexpr (RJ == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(p);
+        x[0] = v.x;
+        x[1] = v.y;
+    } else {
+        x[0] = *p;
+    }
+}
+template <int RJ, bool BF16>
+__device__ __forceinline__ void load_io_pair(float (&x)[RJ], const void* base, int64_t idx) {
+    if constexpr (BF16 && RJ == 2) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + idx);
+        x[0] = __uint_as_float(v << 16);
+        x[1] = __uint_as_float(v & 0xffff0000u);
+    } else if constexpr (RJ == 2) {
+        load_pair<2>(x, static_cast<const float*>(base) + idx);
+    } else {
+        x[0] = load_io<BF16>(base, idx);
+    }
+}
+
 // Each scan takes kTok tokens at a time.  All their loads are issued first,
 // at token and channel indices clamped into range (addressed from a uniform
 // base with 32-bit lane offsets); a ragged batch (fewer than kTok tokens left,
@@ -142,7 +168,7 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
     float ur[RJ], ui[RJ], vr[RJ], vi[RJ];
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
-        const int r = lane + kWave * j;
+        const int r = RJ * lane + j;
         ur[j] = ui[j] = vr[j] = vi[j] = 0.f;
         if (state_in != nullptr && r < d) {
             ur[j] = state_in[st_row + 2 * r];
@@ -151,9 +177,7 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
     }
     const int64_t row0 = h * p.T + (bh / p.H) * N;
     const bool dfull = d == kWave * RJ;
-    uint32_t off[RJ];  // the lane's channels (clamped below d)
-#pragma unroll
-    for (int j = 0; j < RJ; ++j) off[j] = static_cast<uint32_t>(min(lane + kWave * j, d - 1));
+    const uint32_t off = static_cast<uint32_t>(min(RJ * lane, d - RJ));  // the lane's first channel (clamped)
     for (int64_t i0 = 0; i0 < N; i0 += kTok) {
         const int nt = static_cast<int>(min(N - i0, static_cast<int64_t>(kTok)));
         float xv[kTok][RJ], zv[kTok][RJ];
@@ -162,11 +186,8 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
             const int64_t row = (row0 + i0 + min(t, nt - 1)) * d;  // uniform
             const float* xr = xi_q + row;
             const float* zr = z_k + row;
-#pragma unroll
-            for (int j = 0; j < RJ; ++j) {
-                xv[t][j] = xr[off[j]];
-                zv[t][j] = zr[off[j]];
-            }
+            load_pair<RJ>(xv[t], xr + off);
+            load_pair<RJ>(zv[t], zr + off);
         }
         // the lane's shares of s and s_a of the kTok tokens, then one reduce-scatter
         // per quantity (lane t < 8 ends with token slot8(t)'s totals)
@@ -178,7 +199,7 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
             for (int t = 0; t < kTok; ++t)
 #pragma unroll
                 for (int j = 0; j < RJ; ++j)
-                    if (t >= nt || lane + kWave * j >= d) xv[t][j] = zv[t][j] = 0.f;
+                    if (t >= nt || RJ * lane + j >= d) xv[t][j] = zv[t][j] = 0.f;
             key_batch<RJ, true>(nt, ur, ui, vr, vi, xv, zv, ar, ai, br, bi, spr, spi, sqr, sqi);
         }
         static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
@@ -194,7 +215,7 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
         float gr = 0.f, gi = 0.f;  // sum_r g_S[r] conj(V_r)
 #pragma unroll
         for (int j = 0; j < RJ; ++j) {
-            const int r = lane + kWave * j;
+            const int r = RJ * lane + j;
             if (r < d) {
                 const float sr = grad_state[st_row + 2 * r], si = grad_state[st_row + 2 * r + 1];
                 gr = fmaf(sr, vr[j], fmaf(si, vi[j], gr));
@@ -233,7 +254,7 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
     float gmr[RJ], gmi[RJ], wr[RJ], wi[RJ];
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
-        const int c = lane + kWave * j;
+        const int c = RJ * lane + j;
         gmr[j] = gmi[j] = wr[j] = wi[j] = 0.f;
         if (state_in != nullptr && c < d) {
             gmr[j] = state_in[st_row + 2 * (d + c)];
@@ -245,9 +266,7 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
     double accr = 0.0, acci = 0.0;  // g_abar share of this mode
     const bool dfull = d == kWave * RJ;
     const int ts = slot8(lane);  // the token whose totals this lane ends with
-    uint32_t coff[RJ];           // the lane's channels (clamped below d)
-#pragma unroll
-    for (int j = 0; j < RJ; ++j) coff[j] = static_cast<uint32_t>(min(lane + kWave * j, d - 1));
+    const uint32_t coff = static_cast<uint32_t>(min(RJ * lane, d - RJ));  // the lane's first channel (clamped)
     for (int64_t i0 = 0; i0 < N; i0 += kTok) {
         const int nt = static_cast<int>(min(N - i0, static_cast<int64_t>(kTok)));
         float zz[kTok][RJ], go[kTok][RJ];
@@ -256,12 +275,8 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
             const int64_t ti = i0 + min(t, nt - 1);
             const float* zr = zvp + ti * d;  // uniform
             const int64_t gr = ((b * N + ti) * H + h) * d;
-#pragma unroll
-            for (int j = 0; j < RJ; ++j) {
-                zz[t][j] = zr[coff[j]];
-                go[t][j] = BF16 ? bf16_to_f32((static_cast<const uint16_t*>(grad_o) + gr)[coff[j]])
-                                : (static_cast<const float*>(grad_o) + gr)[coff[j]];
-            }
+            load_pair<RJ>(zz[t], zr + coff);
+            load_io_pair<RJ, BF16>(go[t], grad_o, gr + coff);
         }
         const int64_t sidx = (row0 + i0 + min(ts, nt - 1)) * M + m;
         const float2 sv = s[sidx], sa = s_a[sidx];  // used after the reduce-scatter
@@ -275,7 +290,7 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
             for (int t = 0; t < kTok; ++t)
 #pragma unroll
                 for (int j = 0; j < RJ; ++j)
-                    if (t >= nt || lane + kWave * j >= d) zz[t][j] = go[t][j] = 0.f;
+                    if (t >= nt || RJ * lane + j >= d) zz[t][j] = go[t][j] = 0.f;
             value_batch<RJ, true>(nt, gmr, gmi, wr, wi, zz, go, ar, ai, br, bi, spr, spi, sqr, sqi);
         }
         static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
@@ -298,7 +313,7 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
         float gr = 0.f, gi = 0.f;  // sum_c g_S[c] conj(W_c)
 #pragma unroll
         for (int j = 0; j < RJ; ++j) {
-            const int c = lane + kWave * j;
+            const int c = RJ * lane + j;
             if (c < d) {
                 const float sr = grad_state[st_row + 2 * (d + c)], si = grad_state[st_row + 2 * (d + c) + 1];
                 gr = fmaf(sr, wr[j], fmaf(si, wi[j], gr));
