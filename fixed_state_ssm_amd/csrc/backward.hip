@@ -42,34 +42,12 @@ __device__ __forceinline__ Zoh zoh_of(const idattn_params& prm, int64_t h, int64
 }
 
 // ------------------------------------------------------------------ per-mode scans
-// One wave per (b, h, m); lane l owns the RJ adjacent channels RJ l .. RJ l +
-// RJ - 1, so that each token's inputs are one load per lane and tensor.
+// One wave per (b, h, m).  In the key scan lane l owns channels l and l + 64
+// (RJ of them); in the value scan the RJ adjacent channels RJ l .. RJ l + RJ - 1,
+// so that a token's bf16 g_o pair is one 4-byte load (measured: adjacent fp32
+// pairs as 8-byte loads made the key scans slower, the bf16 pairs made the
+// value scan faster).
 //
-// RJ adjacent floats (one 4- or 8-byte load), and RJ adjacent elements of an
-// I/O tensor (a bf16 pair in one 4-byte load, or fp32).
-template <int RJ>
-__device__ __forceinline__ void load_pair(float (&x)[RJ], const float* p) {
-    if constexpr (RJ == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(p);
-        x[0] = v.x;
-        x[1] = v.y;
-    } else {
-        x[0] = *p;
-    }
-}
-template <int RJ, bool BF16>
-__device__ __forceinline__ void load_io_pair(float (&x)[RJ], const void* base, int64_t idx) {
-    if constexpr (BF16 && RJ == 2) {
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + idx);
-        x[0] = __uint_as_float(v << 16);
-        x[1] = __uint_as_float(v & 0xffff0000u);
-    } else if constexpr (RJ == 2) {
-        load_pair<2>(x, static_cast<const float*>(base) + idx);
-    } else {
-        x[0] = load_io<BF16>(base, idx);
-    }
-}
-
 // Each scan takes kTok tokens at a time.  All their loads are issued first,
 // at token and channel indices clamped into range (addressed from a uniform
 // base with 32-bit lane offsets); a ragged batch (fewer than kTok tokens left,
@@ -168,7 +146,7 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
     float ur[RJ], ui[RJ], vr[RJ], vi[RJ];
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
-        const int r = RJ * lane + j;
+        const int r = lane + kWave * j;
         ur[j] = ui[j] = vr[j] = vi[j] = 0.f;
         if (state_in != nullptr && r < d) {
             ur[j] = state_in[st_row + 2 * r];
@@ -177,7 +155,9 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
     }
     const int64_t row0 = h * p.T + (bh / p.H) * N;
     const bool dfull = d == kWave * RJ;
-    const uint32_t off = static_cast<uint32_t>(min(RJ * lane, d - RJ));  // the lane's first channel (clamped)
+    uint32_t off[RJ];  // the lane's channels (clamped below d)
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) off[j] = static_cast<uint32_t>(min(lane + kWave * j, d - 1));
     for (int64_t i0 = 0; i0 < N; i0 += kTok) {
         const int nt = static_cast<int>(min(N - i0, static_cast<int64_t>(kTok)));
         float xv[kTok][RJ], zv[kTok][RJ];
@@ -186,8 +166,11 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
             const int64_t row = (row0 + i0 + min(t, nt - 1)) * d;  // uniform
             const float* xr = xi_q + row;
             const float* zr = z_k + row;
-            load_pair<RJ>(xv[t], xr + off);
-            load_pair<RJ>(zv[t], zr + off);
+#pragma unroll
+            for (int j = 0; j < RJ; ++j) {
+                xv[t][j] = xr[off[j]];
+                zv[t][j] = zr[off[j]];
+            }
         }
         // the lane's shares of s and s_a of the kTok tokens, then one reduce-scatter
         // per quantity (lane t < 8 ends with token slot8(t)'s totals)
@@ -199,7 +182,7 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
             for (int t = 0; t < kTok; ++t)
 #pragma unroll
                 for (int j = 0; j < RJ; ++j)
-                    if (t >= nt || RJ * lane + j >= d) xv[t][j] = zv[t][j] = 0.f;
+                    if (t >= nt || lane + kWave * j >= d) xv[t][j] = zv[t][j] = 0.f;
             key_batch<RJ, true>(nt, ur, ui, vr, vi, xv, zv, ar, ai, br, bi, spr, spi, sqr, sqi);
         }
         static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
@@ -215,7 +198,7 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
         float gr = 0.f, gi = 0.f;  // sum_r g_S[r] conj(V_r)
 #pragma unroll
         for (int j = 0; j < RJ; ++j) {
-            const int r = RJ * lane + j;
+            const int r = lane + kWave * j;
             if (r < d) {
                 const float sr = grad_state[st_row + 2 * r], si = grad_state[st_row + 2 * r + 1];
                 gr = fmaf(sr, vr[j], fmaf(si, vi[j], gr));

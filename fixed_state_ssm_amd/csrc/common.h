@@ -40,6 +40,31 @@ __device__ __forceinline__ float widen(uint32_t raw) {
     return __uint_as_float(BF16 ? raw << 16 : raw);
 }
 
+// RJ adjacent floats (one 4- or 8-byte load), and RJ adjacent elements of an
+// I/O tensor (a bf16 pair in one 4-byte load, or fp32).
+template <int RJ>
+__device__ __forceinline__ void load_pair(float (&x)[RJ], const float* p) {
+    if constexpr (RJ == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(p);
+        x[0] = v.x;
+        x[1] = v.y;
+    } else {
+        x[0] = *p;
+    }
+}
+template <int RJ, bool BF16>
+__device__ __forceinline__ void load_io_pair(float (&x)[RJ], const void* base, int64_t idx) {
+    if constexpr (BF16 && RJ == 2) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + idx);
+        x[0] = __uint_as_float(v << 16);
+        x[1] = __uint_as_float(v & 0xffff0000u);
+    } else if constexpr (RJ == 2) {
+        load_pair<2>(x, static_cast<const float*>(base) + idx);
+    } else {
+        x[0] = load_io<BF16>(base, idx);
+    }
+}
+
 // ------------------------------------------------------------------ conv rows
 constexpr int kConvMax = 8;  // largest conv width W
 
