@@ -31,7 +31,7 @@ namespace idattn {
 
 namespace {
 
-constexpr int kTok = 8;    // tokens loaded ahead in the per-mode scans
+constexpr int kTok = 8;    // tokens per batch of the per-mode scans
 constexpr int kBlk = 16;   // tokens per LDS round of the per-channel scans
 constexpr int kVW = 16;    // waves per per-channel scan block
 constexpr int kRun = 64;   // tokens per wave in the feature and conv kernels

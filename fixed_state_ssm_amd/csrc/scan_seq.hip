@@ -11,13 +11,13 @@
 // share of the denominator; it alone reads and writes eta_m, so eta may be
 // updated in place.
 //
-// ssm_value_scan_readout_seq: one block per (b, h, 64-channel group); wave w
-// owns a contiguous sixteenth of the modes, lane l one channel, so
-// Gamma_{m,c} stays in registers and o_i,c = Re sum_m s_m(i) Gamma_{m,c}(i)
-// needs only a 16-way cross-wave sum through LDS, done once per block of 16
-// tokens.  Sixteen waves (four per SIMD): there are only B H d/64 blocks,
-// fewer than compute units at the model shapes, so each one needs the latency
-// hiding.
+// ssm_value_scan_readout_seq: one block of sixteen waves per (b, h, 64-channel
+// group) and, with M >= 32, per half of the modes; wave w owns a contiguous
+// sixteenth of the block's modes, lane l one channel, so Gamma_{m,c} stays in
+// registers and o_i,c = Re sum_m s_m(i) Gamma_{m,c}(i) needs only a 16-way
+// cross-wave sum through LDS, done once per block of 16 tokens.  The two
+// halves' partial sums are added by a small combine kernel: B H d/64 alone
+// is fewer blocks than compute units at the model shapes.
 #include <algorithm>
 
 #include "common.h"
