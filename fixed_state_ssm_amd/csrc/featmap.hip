@@ -5,9 +5,10 @@
 // random Fourier features, Chinese rendering, section 3.1, eq. 6).  Also the
 // conv-tail update and a copy kernel.
 //
-// One wave per token-head; lane l owns channels l and l + 64.  Token-heads are
-// numbered in [T][H] order (T tokens of the dense [B][N] or of a packed
-// batch) so that neighbouring waves read neighbouring rows of q, k, v.
+// One wave per four consecutive tokens of one head; lane l owns channels l and
+// l + 64.  Waves are numbered in [T / 4][H] order (T tokens of the dense
+// [B][N] or of a packed batch) so that neighbouring waves read neighbouring
+// rows of q, k, v.
 // Outputs go to the workspace in [H][T][d] float32 order, where each (b, h)
 // sequence is a contiguous run that the sequential scans read in turn.
 #include "common.h"
@@ -18,8 +19,12 @@ namespace idattn {
 namespace {
 
 // WT: the conv width when it is fixed at compile time (4), else 0 (any W,
-// with kConvMax taps of which the first W are used).
-template <bool BF16, int DJ, int WT>
+// with kConvMax taps of which the first W are used).  TPW consecutive tokens
+// of one head per wave (waves numbered [T / TPW][H]): their chains of loads,
+// conv and norm reductions are independent, so the wave interleaves them, and
+// the head's conv weights, gain and bias are loaded once.  A token past T (in
+// the last group) computes on a copy of token T - 1 and stores nothing.
+template <bool BF16, int DJ, int WT, int TPW>
 __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
     Problem p, idattn_params prm, const void* __restrict__ q, const void* __restrict__ k,
     const void* __restrict__ v, const void* __restrict__ tail_in, float* __restrict__ xi_q,
@@ -29,87 +34,104 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
     const int64_t th = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     const int64_t H = p.H, T = p.T;
     const int d = static_cast<int>(p.d), W = WT > 0 ? WT : static_cast<int>(p.W);
-    if (th >= T * H) return;  // whole wave exits; no barriers below
+    if (th >= (T + TPW - 1) / TPW * H) return;  // whole wave exits; no barriers below
     const int64_t h = th % H;
-    const int64_t t = th / H;  // token on the [T] axis
-    const int64_t b = seq_of_token(p.cu, p.N, p.B, t);
-    int64_t start, len;
-    seq_range(p.cu, p.N, T, b, start, len);
-    const int64_t n = t >= start ? t - start : 0;  // position in its sequence (0 <= n <= t)
+    const int64_t tg = (th / H) * TPW;  // the group's first token on the [T] axis
 
-    // every load first (channels clamped below d, missing rows masked below):
-    // the conv taps of q and k, their weights, v
+    // the head's conv weights, gain and bias (channels clamped below d)
     int cl[DJ];
+    float wq[NT][DJ], wk[NT][DJ], gk[DJ], bk[DJ], gv[DJ], bv[DJ];
 #pragma unroll
-    for (int j = 0; j < DJ; ++j) cl[j] = min(lane + kWave * j, d - 1);
-    uint32_t xq_raw[NT][DJ], xk_raw[NT][DJ], v_raw[DJ];
-    float wq[NT][DJ], wk[NT][DJ];
-    bool tap_ok[NT];
+    for (int j = 0; j < DJ; ++j) {
+        cl[j] = min(lane + kWave * j, d - 1);
 #pragma unroll
-    for (int j2 = 0; j2 < NT; ++j2) {
-        const ConvRow r = conv_row(q, k, tail_in, t - n, n - (W - 1) + j2, t, b, h, H, d, W, j2 < W);
-        tap_ok[j2] = r.ok;
-#pragma unroll
-        for (int j = 0; j < DJ; ++j) {
-            xq_raw[j2][j] = load_raw<BF16>(r.bq, r.rq + cl[j]);
-            xk_raw[j2][j] = load_raw<BF16>(r.bk, r.rk + cl[j]);
+        for (int j2 = 0; j2 < NT; ++j2) {
             wq[j2][j] = prm.conv_q[(h * d + cl[j]) * W + min(j2, W - 1)];
             wk[j2][j] = prm.conv_k[(h * d + cl[j]) * W + min(j2, W - 1)];
         }
+        gk[j] = prm.gain[h * 2 * d + cl[j]];
+        bk[j] = prm.bias[h * 2 * d + cl[j]];
+        gv[j] = prm.gain[h * 2 * d + d + cl[j]];
+        bv[j] = prm.bias[h * 2 * d + d + cl[j]];
     }
 #pragma unroll
-    for (int j = 0; j < DJ; ++j) v_raw[j] = load_raw<BF16>(v, (t * H + h) * d + cl[j]);
+    for (int u = 0; u < TPW; ++u) {
+        const int64_t t = min(tg + u, T - 1);  // token on the [T] axis
+        const int64_t b = seq_of_token(p.cu, p.N, p.B, t);
+        int64_t start, len;
+        seq_range(p.cu, p.N, T, b, start, len);
+        const int64_t n = t >= start ? t - start : 0;  // position in its sequence (0 <= n <= t)
 
-    float cqv[DJ], ckv[DJ], yq[DJ], yk[DJ], xv[DJ];
-    float sv = 0.f;
-#pragma unroll
-    for (int j = 0; j < DJ; ++j) {
-        float cq = 0.f, ck = 0.f;
+        // every load of the token first (missing rows masked below): the conv
+        // taps of q and k, v
+        uint32_t xq_raw[NT][DJ], xk_raw[NT][DJ], v_raw[DJ];
+        bool tap_ok[NT];
 #pragma unroll
         for (int j2 = 0; j2 < NT; ++j2) {
-            cq = fmaf(wq[j2][j], tap_ok[j2] ? widen<BF16>(xq_raw[j2][j]) : 0.f, cq);
-            ck = fmaf(wk[j2][j], tap_ok[j2] ? widen<BF16>(xk_raw[j2][j]) : 0.f, ck);
+            const ConvRow r = conv_row(q, k, tail_in, t - n, n - (W - 1) + j2, t, b, h, H, d, W, j2 < W);
+            tap_ok[j2] = r.ok;
+#pragma unroll
+            for (int j = 0; j < DJ; ++j) {
+                xq_raw[j2][j] = load_raw<BF16>(r.bq, r.rq + cl[j]);
+                xk_raw[j2][j] = load_raw<BF16>(r.bk, r.rk + cl[j]);
+            }
         }
-        const bool in = lane + kWave * j < d;  // lanes past d hold zeros
-        cqv[j] = in ? cq : 0.f;
-        ckv[j] = in ? ck : 0.f;
-        xv[j] = in ? widen<BF16>(v_raw[j]) : 0.f;
-        sv = fmaf(xv[j], xv[j], sv);
-    }
-    sv = wave_total(sv);
-    // xi = y * inv with y = SiLU(c) = c / (1 + exp(-c)); lanes past d hold c = 0 -> y = 0.
-    // (The RFF map has its own kernel below.)
-    float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int j = 0; j < DJ; ++j) {
-        yq[j] = cqv[j] / (1.f + expf(-cqv[j]));
-        yk[j] = ckv[j] / (1.f + expf(-ckv[j]));
-        sq = fmaf(yq[j], yq[j], sq);
-        sk = fmaf(yk[j], yk[j], sk);
-    }
-    sq = wave_total(sq);
-    sk = wave_total(sk);
-    // squared norm, or its square root for the unit-norm map
-    const float inv_q = p.unit_feat ? 1.f / sqrtf(sq + p.eps_feat) : 1.f / (sq + p.eps_feat);
-    const float inv_k = p.unit_feat ? 1.f / sqrtf(sk + p.eps_feat) : 1.f / (sk + p.eps_feat);
-    float xk2 = 0.f;
-    float xik[DJ];
+        for (int j = 0; j < DJ; ++j) v_raw[j] = load_raw<BF16>(v, (t * H + h) * d + cl[j]);
+
+        float cqv[DJ], ckv[DJ], yq[DJ], yk[DJ], xv[DJ];
+        float sv = 0.f;
 #pragma unroll
-    for (int j = 0; j < DJ; ++j) {
-        xik[j] = yk[j] * inv_k;
-        xk2 = fmaf(xik[j], xik[j], xk2);
-    }
-    xk2 = wave_total(xk2);
-    const float rk = 1.f / sqrtf(xk2 / d + p.eps_norm);
-    const float rv = 1.f / sqrtf(sv / d + p.eps_norm);
-    const int64_t orow = (h * T + t) * d;
+        for (int j = 0; j < DJ; ++j) {
+            float cq = 0.f, ck = 0.f;
 #pragma unroll
-    for (int j = 0; j < DJ; ++j) {
-        const int c = lane + kWave * j;
-        if (c < d) {
-            xi_q[orow + c] = yq[j] * inv_q;
-            z_k[orow + c] = fmaf(prm.gain[h * 2 * d + c] * xik[j], rk, prm.bias[h * 2 * d + c]);
-            z_v[orow + c] = fmaf(prm.gain[h * 2 * d + d + c] * xv[j], rv, prm.bias[h * 2 * d + d + c]);
+            for (int j2 = 0; j2 < NT; ++j2) {
+                cq = fmaf(wq[j2][j], tap_ok[j2] ? widen<BF16>(xq_raw[j2][j]) : 0.f, cq);
+                ck = fmaf(wk[j2][j], tap_ok[j2] ? widen<BF16>(xk_raw[j2][j]) : 0.f, ck);
+            }
+            const bool in = lane + kWave * j < d;  // lanes past d hold zeros
+            cqv[j] = in ? cq : 0.f;
+            ckv[j] = in ? ck : 0.f;
+            xv[j] = in ? widen<BF16>(v_raw[j]) : 0.f;
+            sv = fmaf(xv[j], xv[j], sv);
+        }
+        sv = wave_total(sv);
+        // xi = y * inv with y = SiLU(c) = c / (1 + exp(-c)); lanes past d hold c = 0 -> y = 0.
+        // (The RFF map has its own kernel below.)
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            yq[j] = cqv[j] / (1.f + expf(-cqv[j]));
+            yk[j] = ckv[j] / (1.f + expf(-ckv[j]));
+            sq = fmaf(yq[j], yq[j], sq);
+            sk = fmaf(yk[j], yk[j], sk);
+        }
+        sq = wave_total(sq);
+        sk = wave_total(sk);
+        // squared norm, or its square root for the unit-norm map
+        const float inv_q = p.unit_feat ? 1.f / sqrtf(sq + p.eps_feat) : 1.f / (sq + p.eps_feat);
+        const float inv_k = p.unit_feat ? 1.f / sqrtf(sk + p.eps_feat) : 1.f / (sk + p.eps_feat);
+        float xk2 = 0.f;
+        float xik[DJ];
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            xik[j] = yk[j] * inv_k;
+            xk2 = fmaf(xik[j], xik[j], xk2);
+        }
+        xk2 = wave_total(xk2);
+        const float rk = 1.f / sqrtf(xk2 / d + p.eps_norm);
+        const float rv = 1.f / sqrtf(sv / d + p.eps_norm);
+        if (tg + u < T) {  // uniform over the wave
+            const int64_t orow = (h * T + t) * d;
+#pragma unroll
+            for (int j = 0; j < DJ; ++j) {
+                const int c = lane + kWave * j;
+                if (c < d) {
+                    xi_q[orow + c] = yq[j] * inv_q;
+                    z_k[orow + c] = fmaf(gk[j] * xik[j], rk, bk[j]);
+                    z_v[orow + c] = fmaf(gv[j] * xv[j], rv, bv[j]);
+                }
+            }
         }
     }
 }
@@ -264,9 +286,11 @@ hipError_t launch_featmap_conv_norm(const Problem& p, const idattn_params& prm, 
 #undef IDATTN_RFF
         return hipGetLastError();
     }
-    const int64_t th = p.T * p.H;
+    constexpr int kFmTPW = 4;  // tokens per wave
+    const int64_t th = (p.T + kFmTPW - 1) / kFmTPW * p.H;
     const dim3 grid(static_cast<unsigned>((th + 3) / 4));
-#define IDATTN_FM(BF, DJ, WT) featmap_conv_norm_kernel<BF, DJ, WT><<<grid, 256, 0, stream>>>(p, prm, q, k, v, tail_in, xi_q, z_k, z_v)
+#define IDATTN_FM(BF, DJ, WT) \
+    featmap_conv_norm_kernel<BF, DJ, WT, kFmTPW><<<grid, 256, 0, stream>>>(p, prm, q, k, v, tail_in, xi_q, z_k, z_v)
 #define IDATTN_FMW(BF, DJ) \
     do {                   \
         if (p.W == 4)      \
