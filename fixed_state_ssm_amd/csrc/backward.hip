@@ -34,7 +34,7 @@ namespace {
 constexpr int kTok = 8;    // tokens per batch of the per-mode scans
 constexpr int kBlk = 16;   // tokens per LDS round of the per-channel scans
 constexpr int kVW = 16;    // waves per per-channel scan block
-constexpr int kRun = 64;   // tokens per wave in the feature and conv kernels
+constexpr int kRun = 32;   // tokens per wave in the feature and conv kernels
 
 __device__ __forceinline__ Zoh zoh_of(const idattn_params& prm, int64_t h, int64_t M, int64_t m) {
     return zoh_mode(prm.log_dt[h], prm.A[(h * M + m) * 2], prm.A[(h * M + m) * 2 + 1], prm.Bc[(h * M + m) * 2],
