@@ -257,50 +257,6 @@ __device__ __forceinline__ void rff_features(const float (&cq)[DJ], const float 
     }
 }
 
-// The same for TPW tokens of one head held by one wave (token u in slot u):
-// every row of Omega is loaded once and serves all TPW tokens.
-template <int DJ, int TPW>
-__device__ __forceinline__ void rff_features_multi(const float (&cq)[TPW][DJ], const float (&ck)[TPW][DJ],
-                                                   const float* __restrict__ om, int d, float (&yq)[TPW][DJ],
-                                                   float (&yk)[TPW][DJ]) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int D = d >> 1;
-    const int f = lane & (D - 1);
-    float pq[TPW], pk[TPW];
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) pq[u] = pk[u] = 0.f;
-#pragma unroll
-    for (int j = 0; j < DJ; ++j) {
-        const int n = min(d - kWave * j, kWave);  // inputs held in slot j: 0, 16, 32 or 64
-        for (int l0 = 0; l0 < n; l0 += 16) {
-            float w[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) w[e] = om[(kWave * j + l0 + e) * D + f];
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-#pragma unroll
-                for (int u = 0; u < TPW; ++u) {
-                    pq[u] = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(cq[u][j]), l0 + e)), w[e], pq[u]);
-                    pk[u] = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ck[u][j]), l0 + e)), w[e], pk[u]);
-                }
-        }
-    }
-    const float sc = 1.f / sqrtf(static_cast<float>(D));
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        float sq, cs_q, sk, cs_k;
-        sincosf(pq[u], &sq, &cs_q);
-        sincosf(pk[u], &sk, &cs_k);
-#pragma unroll
-        for (int j = 0; j < DJ; ++j) {
-            const int c = lane + kWave * j;
-            const bool in = c < d, sn = c >= D;
-            yq[u][j] = in ? (sn ? sq : cs_q) * sc : 0.f;
-            yk[u][j] = in ? (sn ? sk : cs_k) * sc : 0.f;
-        }
-    }
-}
-
 // ------------------------------------------------------------------ ZOH
 // Zero-order hold of u' = lambda u + B z over a step Delta = exp(log_dt),
 // evaluated in fp64:  abar = exp(Delta lambda),

@@ -136,67 +136,149 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
     }
 }
 
+// Random Fourier features of TPW tokens held by one wave (Chinese rendering of
+// the paper, section 3.1, eq. 6), as rff_features computes them for one
+// token, with the conv outputs broadcast through the wave's slice of shared
+// memory (cs: [2][TPW][d] floats, queries then keys) instead of one readlane
+// per input: lane l forms the phases of frequency l mod D, reading four
+// inputs of a token per 16-byte broadcast load, and every row of Omega it
+// loads serves all TPW tokens.  The products are summed in the same order
+// (input 0 to d - 1), so the features are the same bits.
+template <int DJ, int TPW>
+__device__ __forceinline__ void rff_features_lds(const float (&cq)[TPW][DJ], const float (&ck)[TPW][DJ],
+                                                 const float* __restrict__ om, int d, float* cs,
+                                                 float (&yq)[TPW][DJ], float (&yk)[TPW][DJ]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int D = d >> 1;  // a power of two, at most 64
+    const int f = lane & (D - 1);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            const int c = lane + kWave * j;
+            if (c < d) {
+                cs[u * d + c] = cq[u][j];
+                cs[(TPW + u) * d + c] = ck[u][j];
+            }
+        }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // the wave's writes before its reads
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float pq[TPW], pk[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) pq[u] = pk[u] = 0.f;
+    for (int r0 = 0; r0 < d; r0 += 16) {
+        float w[16];  // sixteen rows of Omega in flight at once
+#pragma unroll
+        for (int e = 0; e < 16; ++e) w[e] = om[(r0 + e) * D + f];
+#pragma unroll
+        for (int e4 = 0; e4 < 16; e4 += 4)
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) {
+                const float4 xq = *reinterpret_cast<const float4*>(&cs[u * d + r0 + e4]);
+                const float4 xk = *reinterpret_cast<const float4*>(&cs[(TPW + u) * d + r0 + e4]);
+                pq[u] = fmaf(xq.w, w[e4 + 3], fmaf(xq.z, w[e4 + 2], fmaf(xq.y, w[e4 + 1], fmaf(xq.x, w[e4], pq[u]))));
+                pk[u] = fmaf(xk.w, w[e4 + 3], fmaf(xk.z, w[e4 + 2], fmaf(xk.y, w[e4 + 1], fmaf(xk.x, w[e4], pk[u]))));
+            }
+    }
+    const float sc = 1.f / sqrtf(static_cast<float>(D));
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        float sq, cs_q, sk, cs_k;
+        sincosf(pq[u], &sq, &cs_q);
+        sincosf(pk[u], &sk, &cs_k);
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            const int c = lane + kWave * j;
+            const bool in = c < d, sn = c >= D;
+            yq[u][j] = in ? (sn ? sq : cs_q) * sc : 0.f;
+            yk[u][j] = in ? (sn ? sk : cs_k) * sc : 0.f;
+        }
+    }
+}
+
 // The RFF map: one wave per TPW consecutive tokens of one head (waves numbered
 // [T / TPW][H]), so that each row of the head's frequency table is loaded once
-// for TPW tokens; otherwise the same steps as featmap_conv_norm_kernel.
-template <bool BF16, int DJ, int TPW>
+// for TPW tokens; the conv taps and the input RMSNorm as in
+// featmap_conv_norm_kernel (every load of a token issued before its first use,
+// a token past T computing on a copy of token T - 1 and storing nothing).
+template <bool BF16, int DJ, int WT, int TPW>
 __global__ __launch_bounds__(256) void featmap_rff_kernel(
     Problem p, idattn_params prm, const void* __restrict__ q, const void* __restrict__ k,
     const void* __restrict__ v, const void* __restrict__ tail_in, float* __restrict__ xi_q,
     float* __restrict__ z_k, float* __restrict__ z_v) {
+    constexpr int NT = WT > 0 ? WT : kConvMax;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t th = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     const int64_t H = p.H, T = p.T;
-    const int d = static_cast<int>(p.d), W = static_cast<int>(p.W);
-    const int64_t groups = (T + TPW - 1) / TPW;
-    if (th >= groups * H) return;  // whole wave exits; no barriers below
+    const int d = static_cast<int>(p.d), W = WT > 0 ? WT : static_cast<int>(p.W);
+    __shared__ __align__(16) float cs_all[4][2 * TPW * (DJ * kWave)];  // per wave: conv outputs for the features
+    if (th >= (T + TPW - 1) / TPW * H) return;  // whole wave exits; no barriers below
     const int64_t h = th % H;
-    const int64_t t0 = (th / H) * TPW;
+    const int64_t tg = (th / H) * TPW;  // the group's first token on the [T] axis
+
+    int cl[DJ];
+    float wq[NT][DJ], wk[NT][DJ];
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+        cl[j] = min(lane + kWave * j, d - 1);
+#pragma unroll
+        for (int j2 = 0; j2 < NT; ++j2) {
+            wq[j2][j] = prm.conv_q[(h * d + cl[j]) * W + min(j2, W - 1)];
+            wk[j2][j] = prm.conv_k[(h * d + cl[j]) * W + min(j2, W - 1)];
+        }
+    }
     float cq[TPW][DJ], ck[TPW][DJ], xv[TPW][DJ], sv[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-        const int64_t t = t0 + u;  // tokens past T compute zeros and store nothing
-        const bool tok = t < T;
-        const int64_t b = tok ? seq_of_token(p.cu, p.N, p.B, t) : 0;
-        int64_t start = 0, len = 0;
-        if (tok) seq_range(p.cu, p.N, T, b, start, len);
+        const int64_t t = min(tg + u, T - 1);
+        const int64_t b = seq_of_token(p.cu, p.N, p.B, t);
+        int64_t start, len;
+        seq_range(p.cu, p.N, T, b, start, len);
         const int64_t n = t >= start ? t - start : 0;
+        uint32_t xq_raw[NT][DJ], xk_raw[NT][DJ], v_raw[DJ];
+        bool tap_ok[NT];
+#pragma unroll
+        for (int j2 = 0; j2 < NT; ++j2) {
+            const ConvRow r = conv_row(q, k, tail_in, t - n, n - (W - 1) + j2, t, b, h, H, d, W, j2 < W);
+            tap_ok[j2] = r.ok;
+#pragma unroll
+            for (int j = 0; j < DJ; ++j) {
+                xq_raw[j2][j] = load_raw<BF16>(r.bq, r.rq + cl[j]);
+                xk_raw[j2][j] = load_raw<BF16>(r.bk, r.rk + cl[j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) v_raw[j] = load_raw<BF16>(v, (t * H + h) * d + cl[j]);
         sv[u] = 0.f;
 #pragma unroll
         for (int j = 0; j < DJ; ++j) {
-            const int c = lane + kWave * j;
-            float a = 0.f, e = 0.f, vv = 0.f;
-            if (tok && c < d) {
-                const float* wq = prm.conv_q + (h * d + c) * W;
-                const float* wk = prm.conv_k + (h * d + c) * W;
-                for (int j2 = 0; j2 < W; ++j2) {
-                    const int64_t pos = n - (W - 1) + j2;
-                    float xq = 0.f, xk = 0.f;
-                    if (pos >= 0) {
-                        const int64_t idx = ((t - (W - 1) + j2) * H + h) * d + c;
-                        xq = load_io<BF16>(q, idx);
-                        xk = load_io<BF16>(k, idx);
-                    } else if (tail_in != nullptr) {
-                        const int64_t tq = ((b * H + h) * 2 * (W - 1) + (W - 1 + pos)) * d + c;
-                        xq = load_io<BF16>(tail_in, tq);
-                        xk = load_io<BF16>(tail_in, tq + static_cast<int64_t>(W - 1) * d);
-                    }
-                    a = fmaf(wq[j2], xq, a);
-                    e = fmaf(wk[j2], xk, e);
-                }
-                vv = load_io<BF16>(v, (t * H + h) * d + c);
+            float a = 0.f, e = 0.f;
+#pragma unroll
+            for (int j2 = 0; j2 < NT; ++j2) {
+                a = fmaf(wq[j2][j], tap_ok[j2] ? widen<BF16>(xq_raw[j2][j]) : 0.f, a);
+                e = fmaf(wk[j2][j], tap_ok[j2] ? widen<BF16>(xk_raw[j2][j]) : 0.f, e);
             }
-            cq[u][j] = a;
-            ck[u][j] = e;
-            xv[u][j] = vv;
-            sv[u] = fmaf(vv, vv, sv[u]);
+            const bool in = lane + kWave * j < d;  // lanes past d hold zeros
+            cq[u][j] = in ? a : 0.f;
+            ck[u][j] = in ? e : 0.f;
+            xv[u][j] = in ? widen<BF16>(v_raw[j]) : 0.f;
+            sv[u] = fmaf(xv[u][j], xv[u][j], sv[u]);
         }
     }
     float yq[TPW][DJ], yk[TPW][DJ];
-    rff_features_multi<DJ, TPW>(cq, ck, prm.rff_omega + h * d * (d / 2), d, yq, yk);
+    rff_features_lds<DJ, TPW>(cq, ck, prm.rff_omega + h * d * (d / 2), d, cs_all[threadIdx.x >> 6], yq, yk);
+    float gk[DJ], bk[DJ], gv[DJ], bv[DJ];
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+        gk[j] = prm.gain[h * 2 * d + cl[j]];
+        bk[j] = prm.bias[h * 2 * d + cl[j]];
+        gv[j] = prm.gain[h * 2 * d + d + cl[j]];
+        bv[j] = prm.bias[h * 2 * d + d + cl[j]];
+    }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-        const int64_t t = t0 + u;
+        const int64_t t = tg + u;
         float xk2 = 0.f;
 #pragma unroll
         for (int j = 0; j < DJ; ++j) xk2 = fmaf(yk[u][j], yk[u][j], xk2);
@@ -211,8 +293,8 @@ __global__ __launch_bounds__(256) void featmap_rff_kernel(
             const int c = lane + kWave * j;
             if (c < d) {
                 xi_q[orow + c] = yq[u][j];
-                z_k[orow + c] = fmaf(prm.gain[h * 2 * d + c] * yk[u][j], rk, prm.bias[h * 2 * d + c]);
-                z_v[orow + c] = fmaf(prm.gain[h * 2 * d + d + c] * xv[u][j], rv, prm.bias[h * 2 * d + d + c]);
+                z_k[orow + c] = fmaf(gk[j] * yk[u][j], rk, bk[j]);
+                z_v[orow + c] = fmaf(gv[j] * xv[u][j], rv, bv[j]);
             }
         }
     }
@@ -275,14 +357,23 @@ hipError_t launch_featmap_conv_norm(const Problem& p, const idattn_params& prm, 
         constexpr int kTPW = 4;
         const int64_t waves = (p.T + kTPW - 1) / kTPW * p.H;
         const dim3 g(static_cast<unsigned>((waves + 3) / 4));
-#define IDATTN_RFF(BF, DJ) featmap_rff_kernel<BF, DJ, kTPW><<<g, 256, 0, stream>>>(p, prm, q, k, v, tail_in, xi_q, z_k, z_v)
+#define IDATTN_RFF(BF, DJ, WT) \
+    featmap_rff_kernel<BF, DJ, WT, kTPW><<<g, 256, 0, stream>>>(p, prm, q, k, v, tail_in, xi_q, z_k, z_v)
+#define IDATTN_RFFW(BF, DJ)        \
+    do {                           \
+        if (p.W == 4)              \
+            IDATTN_RFF(BF, DJ, 4); \
+        else                       \
+            IDATTN_RFF(BF, DJ, 0); \
+    } while (0)
         if (p.d > 64) {
-            if (p.bf16) IDATTN_RFF(true, 2);
-            else IDATTN_RFF(false, 2);
+            if (p.bf16) IDATTN_RFFW(true, 2);
+            else IDATTN_RFFW(false, 2);
         } else {
-            if (p.bf16) IDATTN_RFF(true, 1);
-            else IDATTN_RFF(false, 1);
+            if (p.bf16) IDATTN_RFFW(true, 1);
+            else IDATTN_RFFW(false, 1);
         }
+#undef IDATTN_RFFW
 #undef IDATTN_RFF
         return hipGetLastError();
     }
