@@ -155,21 +155,22 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
     }
     const int64_t row0 = h * p.T + (bh / p.H) * N;
     const bool dfull = d == kWave * RJ;
-    uint32_t off[RJ];  // the lane's channels (clamped below d)
+    uint32_t off[RJ];  // byte offsets of the lane's channels (clamped below d)
 #pragma unroll
-    for (int j = 0; j < RJ; ++j) off[j] = static_cast<uint32_t>(min(lane + kWave * j, d - 1));
+    for (int j = 0; j < RJ; ++j) off[j] = 4u * static_cast<uint32_t>(min(lane + kWave * j, d - 1));
     for (int64_t i0 = 0; i0 < N; i0 += kTok) {
         const int nt = static_cast<int>(min(N - i0, static_cast<int64_t>(kTok)));
         float xv[kTok][RJ], zv[kTok][RJ];
+        const int64_t row = (row0 + i0) * d;  // the batch's rows, uniform
+        const uint32_t nb = static_cast<uint32_t>(nt * d * 4);
+        const __amdgpu_buffer_rsrc_t xr = rsrc_at(xi_q + row, nb), zr = rsrc_at(z_k + row, nb);
 #pragma unroll
         for (int t = 0; t < kTok; ++t) {
-            const int64_t row = (row0 + i0 + min(t, nt - 1)) * d;  // uniform
-            const float* xr = xi_q + row;
-            const float* zr = z_k + row;
+            const uint32_t tb = static_cast<uint32_t>(min(t, nt - 1) * d * 4);
 #pragma unroll
             for (int j = 0; j < RJ; ++j) {
-                xv[t][j] = xr[off[j]];
-                zv[t][j] = zr[off[j]];
+                xv[t][j] = buf_load(xr, off[j], tb);
+                zv[t][j] = buf_load(zr, off[j], tb);
             }
         }
         // the lane's shares of s and s_a of the kTok tokens, then one reduce-scatter
@@ -250,16 +251,19 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
     const bool dfull = d == kWave * RJ;
     const int ts = slot8(lane);  // the token whose totals this lane ends with
     const uint32_t coff = static_cast<uint32_t>(min(RJ * lane, d - RJ));  // the lane's first channel (clamped)
+    constexpr uint32_t kIoB = BF16 ? 2 : 4;  // bytes per element of grad_o
+    const uint32_t gstride = static_cast<uint32_t>(H * d) * kIoB;  // bytes per token of grad_o
     for (int64_t i0 = 0; i0 < N; i0 += kTok) {
         const int nt = static_cast<int>(min(N - i0, static_cast<int64_t>(kTok)));
         float zz[kTok][RJ], go[kTok][RJ];
+        const __amdgpu_buffer_rsrc_t zr = rsrc_at(zvp + i0 * d, static_cast<uint32_t>(nt * d * 4));
+        const __amdgpu_buffer_rsrc_t gr = rsrc_at(
+            static_cast<const char*>(grad_o) + ((b * N + i0) * H + h) * d * kIoB, static_cast<uint32_t>(nt) * gstride);
 #pragma unroll
         for (int t = 0; t < kTok; ++t) {
-            const int64_t ti = i0 + min(t, nt - 1);
-            const float* zr = zvp + ti * d;  // uniform
-            const int64_t gr = ((b * N + ti) * H + h) * d;
-            load_pair<RJ>(zz[t], zr + coff);
-            load_io_pair<RJ, BF16>(go[t], grad_o, gr + coff);
+            const uint32_t tt = static_cast<uint32_t>(min(t, nt - 1));
+            buf_load_pair<RJ>(zz[t], zr, 4u * coff, tt * static_cast<uint32_t>(d) * 4u);
+            buf_load_io_pair<RJ, BF16>(go[t], gr, kIoB * coff, tt * gstride);
         }
         const int64_t sidx = (row0 + i0 + min(ts, nt - 1)) * M + m;
         const float2 sv = s[sidx], sa = s_a[sidx];  // used after the reduce-scatter

@@ -40,6 +40,43 @@ __device__ __forceinline__ float widen(uint32_t raw) {
     return __uint_as_float(BF16 ? raw << 16 : raw);
 }
 
+// Buffer loads from a wave-uniform base: a buffer resource over n_bytes at
+// base, read at a per-lane byte offset voff plus a uniform byte offset soff, so
+// a lane needs no 64-bit address arithmetic.  The hardware checks voff against
+// n_bytes (a load past it returns zero); soff is not checked, so callers keep
+// voff + soff inside the buffer themselves.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const void* base, uint32_t n_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n_bytes), 0x00020000);
+}
+__device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+// RJ adjacent floats (one 4- or 8-byte buffer load), and RJ adjacent elements
+// of an I/O tensor (a bf16 pair in one 4-byte load, or fp32).
+template <int RJ>
+__device__ __forceinline__ void buf_load_pair(float (&x)[RJ], __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    if constexpr (RJ == 2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        x[0] = __uint_as_float(v[0]);
+        x[1] = __uint_as_float(v[1]);
+    } else {
+        x[0] = buf_load(r, voff, soff);
+    }
+}
+template <int RJ, bool BF16>
+__device__ __forceinline__ void buf_load_io_pair(float (&x)[RJ], __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 uint32_t soff) {
+    if constexpr (BF16 && RJ == 2) {
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+        x[0] = __uint_as_float(v << 16);
+        x[1] = __uint_as_float(v & 0xffff0000u);
+    } else if constexpr (BF16) {
+        x[0] = __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)) << 16);
+    } else {
+        buf_load_pair<RJ>(x, r, voff, soff);
+    }
+}
+
 // RJ adjacent floats (one 4- or 8-byte load), and RJ adjacent elements of an
 // I/O tensor (a bf16 pair in one 4-byte load, or fp32).
 template <int RJ>

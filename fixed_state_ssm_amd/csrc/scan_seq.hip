@@ -7,7 +7,8 @@
 // shares of s_m(i) = xi_q(i) . U_m(i) over the R channels are reduced eight
 // tokens at a time with one reduce-scatter per quantity.  With
 // the normalised readout (ETA) the wave also carries the mode's normaliser
-// eta_m(i) = abar eta_m(i-1) + bbar and writes Re(s_m(i) eta_m(i)), the mode's
+// eta_m(i) = abar eta_m(i-1) + bbar (over a full batch in closed form, from
+// powers of abar formed in fp64) and writes Re(s_m(i) eta_m(i)), the mode's
 // share of the denominator; it alone reads and writes eta_m, so eta may be
 // updated in place.
 //
@@ -30,9 +31,10 @@ namespace {
 constexpr int kTok = 8;  // tokens per batch of the key recurrence
 
 // One batch of the key recurrence: the lane's shares of s for each token and,
-// with ETA, the normaliser stepped along (the same in every lane); lane l keeps
-// eta after token slot8(l) in etr, eti.  A ragged batch steps only its first
-// nt tokens.
+// for a ragged batch with ETA, the normaliser stepped along (the same in every
+// lane); lane l keeps eta after token slot8(l) in etr, eti.  A ragged batch
+// steps only its first nt tokens.  A full batch leaves eta to the caller, which
+// jumps it over the eight tokens in closed form.
 template <int RJ, bool ETA, bool RAGGED>
 __device__ __forceinline__ void key_seq_batch(int nt, int ts, float (&ur)[RJ], float (&ui)[RJ],
                                               const float (&xv)[kTok][RJ], const float (&zv)[kTok][RJ], float ar,
@@ -51,7 +53,7 @@ __device__ __forceinline__ void key_seq_batch(int nt, int ts, float (&ur)[RJ], f
                 pr = fmaf(xv[t][j], nr, pr);
                 pi = fmaf(xv[t][j], ni, pi);
             }
-            if constexpr (ETA) {
+            if constexpr (ETA && RAGGED) {
                 const float nr = fmaf(ar, er, fmaf(-ai, ei, br));
                 const float ni = fmaf(ar, ei, fmaf(ai, er, bi));
                 er = nr;
@@ -107,6 +109,33 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
     }
     const bool dfull = d == kWave * RJ;
     const int ts = slot8(lane);  // the token whose totals this lane ends with
+    // eta over a full batch in closed form, eta(i0 + k) = abar^(k+1) eta(i0 - 1)
+    // + bbar sum_{j<=k} abar^j: (plr, pli), (qlr, qli) for k = ts (this lane's
+    // token), (a8r, a8i), (q8r, q8i) for k = 7 (the next batch's start), in fp64
+    float plr = 0.f, pli = 0.f, qlr = 0.f, qli = 0.f, a8r = 0.f, a8i = 0.f, q8r = 0.f, q8i = 0.f;
+    if constexpr (ETA) {
+        double pr = 1.0, pi = 0.0, sr = 0.0, si = 0.0;  // abar^k and sum_{j<k} abar^j
+        for (int k = 0; k < kTok; ++k) {
+            sr += pr;
+            si += pi;
+            const double nr = pr * z.ar - pi * z.ai, ni = pr * z.ai + pi * z.ar;
+            pr = nr;
+            pi = ni;
+            const float br_k = static_cast<float>(z.br * sr - z.bi * si), bi_k = static_cast<float>(z.br * si + z.bi * sr);
+            if (k == ts) {
+                plr = static_cast<float>(pr);
+                pli = static_cast<float>(pi);
+                qlr = br_k;
+                qli = bi_k;
+            }
+            if (k == kTok - 1) {
+                a8r = static_cast<float>(pr);
+                a8i = static_cast<float>(pi);
+                q8r = br_k;
+                q8i = bi_k;
+            }
+        }
+    }
     uint32_t off[RJ];            // the lane's channels (clamped below d)
 #pragma unroll
     for (int j = 0; j < RJ; ++j) off[j] = static_cast<uint32_t>(min(lane + kWave * j, d - 1));
@@ -130,6 +159,14 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
         float etr = 0.f, eti = 0.f;
         if (nt == kTok && dfull) {
             key_seq_batch<RJ, ETA, false>(nt, ts, ur, ui, xv, zv, ar, ai, br, bi, spr, spi, er, ei, etr, eti);
+            if constexpr (ETA) {
+                etr = fmaf(plr, er, fmaf(-pli, ei, qlr));
+                eti = fmaf(plr, ei, fmaf(pli, er, qli));
+                const float nr = fmaf(a8r, er, fmaf(-a8i, ei, q8r));
+                const float ni = fmaf(a8r, ei, fmaf(a8i, er, q8i));
+                er = nr;
+                ei = ni;
+            }
         } else {
 #pragma unroll
             for (int t = 0; t < kTok; ++t)
