@@ -134,7 +134,7 @@ def parse():
     ap.add_argument("--algo", default="auto", choices=["auto", "sequential", "chunked"])
     ap.add_argument("--feature-norm", default="squared", choices=["squared", "unit", "rff"],
                     help="feature map xi = y / (||y||^2 + eps) (squared), y / sqrt(||y||^2 + eps) (unit), or "
-                         "random Fourier features of the conv output (rff; sequential path only)")
+                         "random Fourier features of the conv output (rff; the chunked path then runs an RFF pre-pass)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU sample")
