@@ -639,7 +639,7 @@ __global__ __launch_bounds__(256) void bwd_feature_kernel(Problem p, idattn_para
                                                           float* __restrict__ part, int64_t runs) {
     constexpr int NT = WT > 0 ? WT : kConvMax;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + wave_id();
     const int64_t H = p.H, N = p.N;
     const int d = static_cast<int>(p.d), W = WT > 0 ? WT : static_cast<int>(p.W);
     if (wid >= p.B * H * runs) return;  // whole wave; no barriers below
@@ -648,10 +648,13 @@ __global__ __launch_bounds__(256) void bwd_feature_kernel(Problem p, idattn_para
     const int64_t t0 = run * kRun, t1 = t0 + kRun < N ? t0 + kRun : N;
     const int64_t row0 = h * p.T + b * N;
     int cl[DJ];  // the lane's channels, clamped below d
+    uint32_t lb[DJ], lf[DJ];  // their byte offsets in a row of q, k, v and in a float row
     float wq[NT][DJ], wk[NT][DJ];
 #pragma unroll
     for (int j = 0; j < DJ; ++j) {
         cl[j] = min(lane + kWave * j, d - 1);
+        lb[j] = static_cast<uint32_t>(cl[j]) * (BF16 ? 2u : 4u);
+        lf[j] = static_cast<uint32_t>(cl[j]) * 4u;
 #pragma unroll
         for (int j2 = 0; j2 < NT; ++j2) {
             wq[j2][j] = prm.conv_q[(h * d + cl[j]) * W + min(j2, W - 1)];
@@ -675,29 +678,36 @@ __global__ __launch_bounds__(256) void bwd_feature_kernel(Problem p, idattn_para
     const float inv_d = 1.f / static_cast<float>(d);
     for (int64_t t = t0; t < t1; ++t) {
         // every load of the token first (channels clamped below d, missing rows
-        // masked): the conv taps of q and k, v, and the scans' gradients
+        // masked): the conv taps of q and k, v, and the scans' gradients, each
+        // row a buffer resource at a uniform base
         uint32_t xq_raw[NT][DJ], xk_raw[NT][DJ], v_raw[DJ];
         bool tap_ok[NT];
 #pragma unroll
         for (int j2 = 0; j2 < NT; ++j2) {
             const ConvRow r = conv_row(q, k, tail_in, b * N, t - (W - 1) + j2, b * N + t, b, h, H, d, W, j2 < W);
             tap_ok[j2] = r.ok;
+            const __amdgpu_buffer_rsrc_t rq = io_rsrc<BF16>(r.bq, r.rq, d), rk = io_rsrc<BF16>(r.bk, r.rk, d);
 #pragma unroll
             for (int j = 0; j < DJ; ++j) {
-                xq_raw[j2][j] = load_raw<BF16>(r.bq, r.rq + cl[j]);
-                xk_raw[j2][j] = load_raw<BF16>(r.bk, r.rk + cl[j]);
+                xq_raw[j2][j] = buf_load_raw<BF16>(rq, lb[j]);
+                xk_raw[j2][j] = buf_load_raw<BF16>(rk, lb[j]);
             }
         }
+        const __amdgpu_buffer_rsrc_t vrow = io_rsrc<BF16>(v, ((b * N + t) * H + h) * d, d);
+        const int64_t o = (row0 + t) * d;
+        const uint32_t fb = static_cast<uint32_t>(d) * 4u;
+        const __amdgpu_buffer_rsrc_t rzk0 = rsrc_at(g_zk + o, fb), rzk1 = rsrc_at(g_zk + o + zs, fb);
+        const __amdgpu_buffer_rsrc_t rzv0 = rsrc_at(g_zv + o, fb), rzv1 = rsrc_at(g_zv + o + zs, fb);
+        const __amdgpu_buffer_rsrc_t rxq0 = rsrc_at(g_xi + o, fb), rxq1 = rsrc_at(g_xi + o + zs, fb);
         float gzk[DJ], gzv[DJ], gxq[DJ];
 #pragma unroll
         for (int j = 0; j < DJ; ++j) {
-            v_raw[j] = load_raw<BF16>(v, ((b * N + t) * H + h) * d + cl[j]);
+            v_raw[j] = buf_load_raw<BF16>(vrow, lb[j]);
             // the scans' partial sums over the two mode splits, added in a fixed
             // order (zs = 0: one split)
-            const int64_t o = (row0 + t) * d + cl[j];
-            const float zk0 = g_zk[o], zk1 = g_zk[o + zs];
-            const float zv0 = g_zv[o], zv1 = g_zv[o + zs];
-            const float xq0 = g_xi[o], xq1 = g_xi[o + zs];
+            const float zk0 = buf_load(rzk0, lf[j], 0), zk1 = buf_load(rzk1, lf[j], 0);
+            const float zv0 = buf_load(rzv0, lf[j], 0), zv1 = buf_load(rzv1, lf[j], 0);
+            const float xq0 = buf_load(rxq0, lf[j], 0), xq1 = buf_load(rxq1, lf[j], 0);
             gzk[j] = zs ? zk0 + zk1 : zk0;
             gzv[j] = zs ? zv0 + zv1 : zv0;
             gxq[j] = zs ? xq0 + xq1 : xq0;
@@ -817,7 +827,7 @@ __global__ __launch_bounds__(256) void bwd_conv_kernel(Problem p, idattn_params 
                                                        float* __restrict__ part, int64_t runs) {
     constexpr int NT = WT > 0 ? WT : kConvMax;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + wave_id();
     const int64_t H = p.H, N = p.N;
     const int d = static_cast<int>(p.d), W = WT > 0 ? WT : static_cast<int>(p.W);
     if (wid >= p.B * H * runs) return;  // whole wave; no barriers below
@@ -826,10 +836,13 @@ __global__ __launch_bounds__(256) void bwd_conv_kernel(Problem p, idattn_params 
     const int64_t t0 = run * kRun, t1 = t0 + kRun < N ? t0 + kRun : N;
     const int64_t row0 = h * p.T + b * N;
     int cl[DJ];  // the lane's channels, clamped below d
+    uint32_t lb[DJ], lf[DJ];  // their byte offsets in a row of q, k and in a float row
     float wq[NT][DJ], wk[NT][DJ], aq[NT][DJ], ak[NT][DJ];
 #pragma unroll
     for (int j = 0; j < DJ; ++j) {
         cl[j] = min(lane + kWave * j, d - 1);
+        lb[j] = static_cast<uint32_t>(cl[j]) * (BF16 ? 2u : 4u);
+        lf[j] = static_cast<uint32_t>(cl[j]) * 4u;
 #pragma unroll
         for (int e = 0; e < NT; ++e) {
             wq[e][j] = prm.conv_q[(h * d + cl[j]) * W + min(e, W - 1)];
@@ -851,19 +864,24 @@ __global__ __launch_bounds__(256) void bwd_conv_kernel(Problem p, idattn_params 
             const int64_t gr = (row0 + max(min(tt, N - 1), int64_t{0})) * d;
             const ConvRow r = conv_row(q, k, tail_in, b * N, t - (W - 1) + e, b * N + t, b, h, H, d, W, e < W);
             x_ok[e] = r.ok;
+            const uint32_t fb = static_cast<uint32_t>(d) * 4u;
+            const __amdgpu_buffer_rsrc_t rgq = rsrc_at(g_cq + gr, fb), rgk = rsrc_at(g_ck + gr, fb);
+            const __amdgpu_buffer_rsrc_t rq = io_rsrc<BF16>(r.bq, r.rq, d), rk = io_rsrc<BF16>(r.bk, r.rk, d);
 #pragma unroll
             for (int j = 0; j < DJ; ++j) {
-                gq[e][j] = g_cq[gr + cl[j]];
-                gk[e][j] = g_ck[gr + cl[j]];
-                xq_raw[e][j] = load_raw<BF16>(r.bq, r.rq + cl[j]);
-                xk_raw[e][j] = load_raw<BF16>(r.bk, r.rk + cl[j]);
+                gq[e][j] = buf_load(rgq, lf[j], 0);
+                gk[e][j] = buf_load(rgk, lf[j], 0);
+                xq_raw[e][j] = buf_load_raw<BF16>(rq, lb[j]);
+                xk_raw[e][j] = buf_load_raw<BF16>(rk, lb[j]);
             }
         }
         float gq_t[DJ], gk_t[DJ];
+        const __amdgpu_buffer_rsrc_t rgq_t = rsrc_at(g_cq + (row0 + t) * d, static_cast<uint32_t>(d) * 4u);
+        const __amdgpu_buffer_rsrc_t rgk_t = rsrc_at(g_ck + (row0 + t) * d, static_cast<uint32_t>(d) * 4u);
 #pragma unroll
         for (int j = 0; j < DJ; ++j) {
-            gq_t[j] = g_cq[(row0 + t) * d + cl[j]];
-            gk_t[j] = g_ck[(row0 + t) * d + cl[j]];
+            gq_t[j] = buf_load(rgq_t, lf[j], 0);
+            gk_t[j] = buf_load(rgk_t, lf[j], 0);
         }
 #pragma unroll
         for (int j = 0; j < DJ; ++j) {

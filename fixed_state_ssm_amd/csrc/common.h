@@ -51,6 +51,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const void* base, uint
 __device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
+// n elements of an I/O tensor from element offset off of base as a buffer
+// resource, and one element of it (as loaded, like load_raw) at a per-lane
+// byte offset.
+template <bool BF16>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t io_rsrc(const void* base, int64_t off, int n) {
+    constexpr int kEB = BF16 ? 2 : 4;
+    return rsrc_at(static_cast<const char*>(base) + off * kEB, static_cast<uint32_t>(n * kEB));
+}
+template <bool BF16>
+__device__ __forceinline__ uint32_t buf_load_raw(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    if constexpr (BF16) return __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+}
+
 // RJ adjacent floats (one 4- or 8-byte buffer load), and RJ adjacent elements
 // of an I/O tensor (a bf16 pair in one 4-byte load, or fp32).
 template <int RJ>
@@ -101,6 +115,10 @@ __device__ __forceinline__ void load_io_pair(float (&x)[RJ], const void* base, i
         x[0] = load_io<BF16>(base, idx);
     }
 }
+
+// The wave's index in its block, as a value the compiler knows to be uniform
+// over the wave (so that what is derived from it stays in scalar registers).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)); }
 
 // ------------------------------------------------------------------ conv rows
 constexpr int kConvMax = 8;  // largest conv width W

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
     float* __restrict__ z_k, float* __restrict__ z_v) {
     constexpr int NT = WT > 0 ? WT : kConvMax;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t th = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t th = static_cast<int64_t>(blockIdx.x) * 4 + wave_id();
     const int64_t H = p.H, T = p.T;
     const int d = static_cast<int>(p.d), W = WT > 0 ? WT : static_cast<int>(p.W);
     if (th >= (T + TPW - 1) / TPW * H) return;  // whole wave exits; no barriers below
@@ -40,10 +40,12 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
 
     // the head's conv weights, gain and bias (channels clamped below d)
     int cl[DJ];
+    uint32_t lb[DJ];  // byte offsets of the lane's channels in a row of q, k, v
     float wq[NT][DJ], wk[NT][DJ], gk[DJ], bk[DJ], gv[DJ], bv[DJ];
 #pragma unroll
     for (int j = 0; j < DJ; ++j) {
         cl[j] = min(lane + kWave * j, d - 1);
+        lb[j] = static_cast<uint32_t>(cl[j]) * (BF16 ? 2u : 4u);
 #pragma unroll
         for (int j2 = 0; j2 < NT; ++j2) {
             wq[j2][j] = prm.conv_q[(h * d + cl[j]) * W + min(j2, W - 1)];
@@ -63,21 +65,23 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
         const int64_t n = t >= start ? t - start : 0;  // position in its sequence (0 <= n <= t)
 
         // every load of the token first (missing rows masked below): the conv
-        // taps of q and k, v
+        // taps of q and k, v; each row is a buffer resource at a uniform base
         uint32_t xq_raw[NT][DJ], xk_raw[NT][DJ], v_raw[DJ];
         bool tap_ok[NT];
 #pragma unroll
         for (int j2 = 0; j2 < NT; ++j2) {
             const ConvRow r = conv_row(q, k, tail_in, t - n, n - (W - 1) + j2, t, b, h, H, d, W, j2 < W);
             tap_ok[j2] = r.ok;
+            const __amdgpu_buffer_rsrc_t rq = io_rsrc<BF16>(r.bq, r.rq, d), rk = io_rsrc<BF16>(r.bk, r.rk, d);
 #pragma unroll
             for (int j = 0; j < DJ; ++j) {
-                xq_raw[j2][j] = load_raw<BF16>(r.bq, r.rq + cl[j]);
-                xk_raw[j2][j] = load_raw<BF16>(r.bk, r.rk + cl[j]);
+                xq_raw[j2][j] = buf_load_raw<BF16>(rq, lb[j]);
+                xk_raw[j2][j] = buf_load_raw<BF16>(rk, lb[j]);
             }
         }
+        const __amdgpu_buffer_rsrc_t vrow = io_rsrc<BF16>(v, (t * H + h) * d, d);
 #pragma unroll
-        for (int j = 0; j < DJ; ++j) v_raw[j] = load_raw<BF16>(v, (t * H + h) * d + cl[j]);
+        for (int j = 0; j < DJ; ++j) v_raw[j] = buf_load_raw<BF16>(vrow, lb[j]);
 
         float cqv[DJ], ckv[DJ], yq[DJ], yk[DJ], xv[DJ];
         float sv = 0.f;
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(256) void featmap_rff_kernel(
     float* __restrict__ z_k, float* __restrict__ z_v) {
     constexpr int NT = WT > 0 ? WT : kConvMax;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t th = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t th = static_cast<int64_t>(blockIdx.x) * 4 + wave_id();
     const int64_t H = p.H, T = p.T;
     const int d = static_cast<int>(p.d), W = WT > 0 ? WT : static_cast<int>(p.W);
     __shared__ __align__(16) float cs_all[4][2 * TPW * (DJ * kWave)];  // per wave: conv outputs for the features
@@ -218,10 +222,12 @@ __global__ __launch_bounds__(256) void featmap_rff_kernel(
     const int64_t tg = (th / H) * TPW;  // the group's first token on the [T] axis
 
     int cl[DJ];
+    uint32_t lb[DJ];  // byte offsets of the lane's channels in a row of q, k, v
     float wq[NT][DJ], wk[NT][DJ];
 #pragma unroll
     for (int j = 0; j < DJ; ++j) {
         cl[j] = min(lane + kWave * j, d - 1);
+        lb[j] = static_cast<uint32_t>(cl[j]) * (BF16 ? 2u : 4u);
 #pragma unroll
         for (int j2 = 0; j2 < NT; ++j2) {
             wq[j2][j] = prm.conv_q[(h * d + cl[j]) * W + min(j2, W - 1)];
@@ -242,14 +248,16 @@ __global__ __launch_bounds__(256) void featmap_rff_kernel(
         for (int j2 = 0; j2 < NT; ++j2) {
             const ConvRow r = conv_row(q, k, tail_in, t - n, n - (W - 1) + j2, t, b, h, H, d, W, j2 < W);
             tap_ok[j2] = r.ok;
+            const __amdgpu_buffer_rsrc_t rq = io_rsrc<BF16>(r.bq, r.rq, d), rk = io_rsrc<BF16>(r.bk, r.rk, d);
 #pragma unroll
             for (int j = 0; j < DJ; ++j) {
-                xq_raw[j2][j] = load_raw<BF16>(r.bq, r.rq + cl[j]);
-                xk_raw[j2][j] = load_raw<BF16>(r.bk, r.rk + cl[j]);
+                xq_raw[j2][j] = buf_load_raw<BF16>(rq, lb[j]);
+                xk_raw[j2][j] = buf_load_raw<BF16>(rk, lb[j]);
             }
         }
+        const __amdgpu_buffer_rsrc_t vrow = io_rsrc<BF16>(v, (t * H + h) * d, d);
 #pragma unroll
-        for (int j = 0; j < DJ; ++j) v_raw[j] = load_raw<BF16>(v, (t * H + h) * d + cl[j]);
+        for (int j = 0; j < DJ; ++j) v_raw[j] = buf_load_raw<BF16>(vrow, lb[j]);
         sv[u] = 0.f;
 #pragma unroll
         for (int j = 0; j < DJ; ++j) {
@@ -267,7 +275,7 @@ __global__ __launch_bounds__(256) void featmap_rff_kernel(
         }
     }
     float yq[TPW][DJ], yk[TPW][DJ];
-    rff_features_lds<DJ, TPW>(cq, ck, prm.rff_omega + h * d * (d / 2), d, cs_all[threadIdx.x >> 6], yq, yk);
+    rff_features_lds<DJ, TPW>(cq, ck, prm.rff_omega + h * d * (d / 2), d, cs_all[wave_id()], yq, yk);
     float gk[DJ], bk[DJ], gv[DJ], bv[DJ];
 #pragma unroll
     for (int j = 0; j < DJ; ++j) {
