@@ -37,6 +37,7 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
     if (th >= (T + TPW - 1) / TPW * H) return;  // whole wave exits; no barriers below
     const int64_t h = th % H;
     const int64_t tg = (th / H) * TPW;  // the group's first token on the [T] axis
+    const float inv_d = 1.f / static_cast<float>(d);
 
     // the head's conv weights, gain and bias (channels clamped below d)
     int cl[DJ];
@@ -100,21 +101,22 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
             sv = fmaf(xv[j], xv[j], sv);
         }
         sv = wave_total(sv);
-        // xi = y * inv with y = SiLU(c) = c / (1 + exp(-c)); lanes past d hold c = 0 -> y = 0.
+        // xi = y * inv with y = SiLU(c) = c / (1 + exp(-c)) (the hardware exp and
+        // reciprocal, each within about an ulp); lanes past d hold c = 0 -> y = 0.
         // (The RFF map has its own kernel below.)
         float sq = 0.f, sk = 0.f;
 #pragma unroll
         for (int j = 0; j < DJ; ++j) {
-            yq[j] = cqv[j] / (1.f + expf(-cqv[j]));
-            yk[j] = ckv[j] / (1.f + expf(-ckv[j]));
+            yq[j] = cqv[j] * __builtin_amdgcn_rcpf(1.f + __expf(-cqv[j]));
+            yk[j] = ckv[j] * __builtin_amdgcn_rcpf(1.f + __expf(-ckv[j]));
             sq = fmaf(yq[j], yq[j], sq);
             sk = fmaf(yk[j], yk[j], sk);
         }
         sq = wave_total(sq);
         sk = wave_total(sk);
         // squared norm, or its square root for the unit-norm map
-        const float inv_q = p.unit_feat ? 1.f / sqrtf(sq + p.eps_feat) : 1.f / (sq + p.eps_feat);
-        const float inv_k = p.unit_feat ? 1.f / sqrtf(sk + p.eps_feat) : 1.f / (sk + p.eps_feat);
+        const float inv_q = p.unit_feat ? __builtin_amdgcn_rsqf(sq + p.eps_feat) : __builtin_amdgcn_rcpf(sq + p.eps_feat);
+        const float inv_k = p.unit_feat ? __builtin_amdgcn_rsqf(sk + p.eps_feat) : __builtin_amdgcn_rcpf(sk + p.eps_feat);
         float xk2 = 0.f;
         float xik[DJ];
 #pragma unroll
@@ -123,8 +125,8 @@ __global__ __launch_bounds__(256) void featmap_conv_norm_kernel(
             xk2 = fmaf(xik[j], xik[j], xk2);
         }
         xk2 = wave_total(xk2);
-        const float rk = 1.f / sqrtf(xk2 / d + p.eps_norm);
-        const float rv = 1.f / sqrtf(sv / d + p.eps_norm);
+        const float rk = __builtin_amdgcn_rsqf(fmaf(xk2, inv_d, p.eps_norm));
+        const float rv = __builtin_amdgcn_rsqf(fmaf(sv, inv_d, p.eps_norm));
         if (tg + u < T) {  // uniform over the wave
             const int64_t orow = (h * T + t) * d;
 #pragma unroll

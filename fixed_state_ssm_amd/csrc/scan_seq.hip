@@ -144,15 +144,21 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
         // before the first use; a ragged batch zeroes what lies out of range
         const int nt = static_cast<int>(min(N - i0, static_cast<int64_t>(kTok)));
         float xv[kTok][RJ], zv[kTok][RJ];
+        uint32_t boff[RJ];
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) {
+            boff[j] = 4u * off[j];
+            asm volatile("" : "+v"(boff[j]));  // formed here, so each load takes it as a 32-bit offset
+        }
 #pragma unroll
         for (int t = 0; t < kTok; ++t) {
             const int64_t row = (row0 + i0 + min(t, nt - 1)) * d;  // uniform
-            const float* xr = xi_q + row;
-            const float* zr = z_k + row;
+            const char* xr = reinterpret_cast<const char*>(xi_q + row);
+            const char* zr = reinterpret_cast<const char*>(z_k + row);
 #pragma unroll
             for (int j = 0; j < RJ; ++j) {
-                xv[t][j] = xr[off[j]];
-                zv[t][j] = zr[off[j]];
+                xv[t][j] = *reinterpret_cast<const float*>(xr + boff[j]);
+                zv[t][j] = *reinterpret_cast<const float*>(zr + boff[j]);
             }
         }
         float spr[kTok], spi[kTok];
