@@ -247,12 +247,12 @@ __device__ __forceinline__ SeqStage seq_fetch(int64_t row0, int64_t i0, int nt, 
     return r;
 }
 
-// One block of kBlk tokens for the wave's MW modes: Gamma steps forward, the
-// wave's share of o goes to red and, with ETA, its share of the denominator to
-// den.  A ragged block steps only its first nt tokens.
-template <int MW, bool ETA, bool RAGGED>
-__device__ __forceinline__ void value_seq_block(int nt, const float2* s_row, const float* p_row, const float* z_col,
-                                                float (*red_t)[kWave], float* den_t, int lane, const float (&ar)[MW],
+// One block of kBlk tokens for the wave's MW modes: Gamma steps forward and
+// the wave's share of o goes to red.  A ragged block steps only its first nt
+// tokens.
+template <int MW, bool RAGGED>
+__device__ __forceinline__ void value_seq_block(int nt, const float2* s_row, const float* z_col,
+                                                float (*red_t)[kWave], int lane, const float (&ar)[MW],
                                                 const float (&ai)[MW], const float (&br)[MW], const float (&bi)[MW],
                                                 float (&gr)[MW], float (&gi)[MW], int M) {
 #pragma unroll
@@ -270,12 +270,6 @@ __device__ __forceinline__ void value_seq_block(int nt, const float2* s_row, con
             acc = fmaf(sv.x, nr, fmaf(-sv.y, ni, acc));
         }
         red_t[t][lane] = acc;
-        if constexpr (ETA) {
-            float dn = 0.f;
-#pragma unroll
-            for (int mm = 0; mm < MW; ++mm) dn += p_row[t * M + mm];
-            if (lane == 0) den_t[t] = dn;
-        }
     }
 }
 
@@ -347,12 +341,18 @@ __global__ __launch_bounds__(kStage) void value_scan_seq_kernel(Problem p, idatt
             const int64_t j0 = i0 + kBlk;  // the next block, loaded while this one runs
             const int jnt = static_cast<int>(min(N - j0, static_cast<int64_t>(kBlk)));
             if (j0 < N) nx = seq_fetch<ETA>(row0, j0, jnt, M, d, group, s, z_v, pden);
+            if constexpr (ETA) {  // the wave's share of the denominator, lane t for token t
+                if (lane < nt) {
+                    float dn = 0.f;
+#pragma unroll
+                    for (int mm = 0; mm < MW; ++mm) dn += p_row[lane * M + mm];
+                    den_s[w][lane] = dn;
+                }
+            }
             if (nt == kBlk)
-                value_seq_block<MW, ETA, false>(nt, s_row, p_row, z_blk + lane, red[w], den_s[w], lane, ar, ai, br,
-                                                bi, gr, gi, M);
+                value_seq_block<MW, false>(nt, s_row, z_blk + lane, red[w], lane, ar, ai, br, bi, gr, gi, M);
             else
-                value_seq_block<MW, ETA, true>(nt, s_row, p_row, z_blk + lane, red[w], den_s[w], lane, ar, ai, br,
-                                               bi, gr, gi, M);
+                value_seq_block<MW, true>(nt, s_row, z_blk + lane, red[w], lane, ar, ai, br, bi, gr, gi, M);
             __syncthreads();
             for (int e = threadIdx.x; e < nt * kWave; e += kStage) {
                 const int t = e / kWave, l = e % kWave;
