@@ -28,13 +28,8 @@ __device__ __forceinline__ float load_io(const void* base, int64_t idx) {
 }
 
 // An element of an I/O tensor as loaded (bf16 bits in the low half, or fp32
-// bits), widened where it is used, so that a batch of loads can all be issued
-// before the first wait.
-template <bool BF16>
-__device__ __forceinline__ uint32_t load_raw(const void* base, int64_t idx) {
-    if constexpr (BF16) return static_cast<const uint16_t*>(base)[idx];
-    else return static_cast<const uint32_t*>(base)[idx];
-}
+// bits) is widened where it is used, so that a batch of loads can all be
+// issued before the first wait.
 template <bool BF16>
 __device__ __forceinline__ float widen(uint32_t raw) {
     return __uint_as_float(BF16 ? raw << 16 : raw);
@@ -52,8 +47,8 @@ __device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t r, uint32_t vof
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 // n elements of an I/O tensor from element offset off of base as a buffer
-// resource, and one element of it (as loaded, like load_raw) at a per-lane
-// byte offset.
+// resource, and one element of it, as loaded (see widen), at a per-lane byte
+// offset.
 template <bool BF16>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t io_rsrc(const void* base, int64_t off, int n) {
     constexpr int kEB = BF16 ? 2 : 4;
@@ -88,31 +83,6 @@ __device__ __forceinline__ void buf_load_io_pair(float (&x)[RJ], __amdgpu_buffer
         x[0] = __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)) << 16);
     } else {
         buf_load_pair<RJ>(x, r, voff, soff);
-    }
-}
-
-// RJ adjacent floats (one 4- or 8-byte load), and RJ adjacent elements of an
-// I/O tensor (a bf16 pair in one 4-byte load, or fp32).
-template <int RJ>
-__device__ __forceinline__ void load_pair(float (&x)[RJ], const float* p) {
-    if constexpr (RJ == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(p);
-        x[0] = v.x;
-        x[1] = v.y;
-    } else {
-        x[0] = *p;
-    }
-}
-template <int RJ, bool BF16>
-__device__ __forceinline__ void load_io_pair(float (&x)[RJ], const void* base, int64_t idx) {
-    if constexpr (BF16 && RJ == 2) {
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + idx);
-        x[0] = __uint_as_float(v << 16);
-        x[1] = __uint_as_float(v & 0xffff0000u);
-    } else if constexpr (RJ == 2) {
-        load_pair<2>(x, static_cast<const float*>(base) + idx);
-    } else {
-        x[0] = load_io<BF16>(base, idx);
     }
 }
 
@@ -210,17 +180,10 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ------------------------------------------------------------------ reductions
-// Butterfly sum over the 64 lanes of a wave; every lane gets the total.
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
-    return x;
-}
-
-// The same total with lower latency, for reductions on a serial path: lane
-// swaps by DPP within rows of 16 (xor 1, xor 2, rotate by 4 and 8), then
-// across rows with v_permlane16_swap and v_permlane32_swap, with no trip
-// through the LDS crossbar.
+// Sums over the 64 lanes of a wave with low latency, for reductions on a
+// serial path: lane swaps by DPP within rows of 16 (xor 1, xor 2, rotate by 4
+// and 8), then across rows with v_permlane16_swap and v_permlane32_swap, with
+// no trip through the LDS crossbar.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
@@ -254,6 +217,7 @@ __device__ __forceinline__ float wave_reduce_scatter8(const float (&v)[8], int l
     const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
+// The total over the 64 lanes; every lane gets it.
 __device__ __forceinline__ float wave_total(float x) {
     x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
     x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
