@@ -217,6 +217,26 @@ __device__ __forceinline__ float wave_reduce_scatter8(const float (&v)[8], int l
     const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
+// The same over each half of the wave (lanes 0..31 and 32..63 on their own):
+// lane l ends with its half's total of value slot8(l & 31).
+__device__ __forceinline__ float half_reduce_scatter8(const float (&v)[8], int lane) {
+    const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4;
+    float u[4], w[2];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float send = b0 ? v[k] : v[k + 4], keep = b0 ? v[k + 4] : v[k];
+        u[k] = keep + dpp_f<0xB1>(send);  // quad_perm [1,0,3,2]
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const float send = b1 ? u[k] : u[k + 2], keep = b1 ? u[k + 2] : u[k];
+        w[k] = keep + dpp_f<0x4E>(send);  // quad_perm [2,3,0,1]
+    }
+    float x = (b2 ? w[1] : w[0]) + dpp_f<0x124>(b2 ? w[0] : w[1]);  // row_ror:4
+    x += dpp_f<0x128>(x);                                           // row_ror:8
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
 // The total over the 64 lanes; every lane gets it.
 __device__ __forceinline__ float wave_total(float x) {
     x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]

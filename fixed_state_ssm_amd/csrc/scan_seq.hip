@@ -2,10 +2,11 @@
 // This is the all-fp32 path (it keeps the per-step rounding of a plain fp32
 // recurrence) and the reference the chunked path is compared with.
 //
-// ssm_key_scan_seq: one wave per (b, h, mode m); lane l owns channels l, l+64
-// of U_m.  Each step updates U_m(i) = abar U_m(i-1) + bbar z_k(i); the lanes'
-// shares of s_m(i) = xi_q(i) . U_m(i) over the R channels are reduced eight
-// tokens at a time with one reduce-scatter per quantity.  With
+// ssm_key_scan_seq: one half-wave per (b, h, mode m), two modes per wave; lane
+// l of a half owns channels l + 32 j of U_m.  Each step updates U_m(i) = abar
+// U_m(i-1) + bbar z_k(i); the lanes' shares of s_m(i) = xi_q(i) . U_m(i) over
+// the R channels are reduced eight tokens at a time with one reduce-scatter per
+// quantity over the half, which serves both modes of the wave at once.  With
 // the normalised readout (ETA) the wave also carries the mode's normaliser
 // eta_m(i) = abar eta_m(i-1) + bbar (over a full batch in closed form, from
 // powers of abar formed in fp64) and writes Re(s_m(i) eta_m(i)), the mode's
@@ -32,7 +33,7 @@ constexpr int kTok = 8;  // tokens per batch of the key recurrence
 
 // One batch of the key recurrence: the lane's shares of s for each token and,
 // for a ragged batch with ETA, the normaliser stepped along (the same in every
-// lane); lane l keeps eta after token slot8(l) in etr, eti.  A ragged batch
+// lane of a half); the lane keeps eta after its token ts in etr, eti.  A ragged batch
 // steps only its first nt tokens.  A full batch leaves eta to the caller, which
 // jumps it over the eight tokens in closed form.
 template <int RJ, bool ETA, bool RAGGED>
@@ -76,39 +77,43 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
                                                            const float* eta_in, float* eta_out,
                                                            float* __restrict__ pden) {
     const int lane = threadIdx.x & (kWave - 1);
+    const int li = lane & 31;  // the lane in its half
     const int64_t bh = blockIdx.x;
-    const int64_t m = static_cast<int64_t>(blockIdx.y) * 4 + (threadIdx.x >> 6);
+    const int64_t m0 = (static_cast<int64_t>(blockIdx.y) * 4 + (threadIdx.x >> 6)) * 2;  // the wave's first mode
+    const int64_t m = m0 + (lane >> 5);
     const int64_t M = p.M;
     const int d = static_cast<int>(p.d);
-    if (m >= M) return;  // whole wave; no barriers in this kernel
+    if (m0 >= M) return;  // whole wave; no barriers in this kernel
+    const bool mok = m < M;  // false for the second half of the last wave when M is odd
+    const int64_t mc = mok ? m : M - 1;
     const int64_t h = bh % p.H;
     int64_t start, N;  // this sequence's tokens on the [T] axis
     seq_range(p.cu, p.N, p.T, bh / p.H, start, N);
-    const Zoh z = zoh_mode(prm.log_dt[h], prm.A[(h * M + m) * 2], prm.A[(h * M + m) * 2 + 1],
-                           prm.Bc[(h * M + m) * 2], prm.Bc[(h * M + m) * 2 + 1]);
+    const Zoh z = zoh_mode(prm.log_dt[h], prm.A[(h * M + mc) * 2], prm.A[(h * M + mc) * 2 + 1],
+                           prm.Bc[(h * M + mc) * 2], prm.Bc[(h * M + mc) * 2 + 1]);
     const float ar = static_cast<float>(z.ar), ai = static_cast<float>(z.ai);
     const float br = static_cast<float>(z.br), bi = static_cast<float>(z.bi);
 
     float ur[RJ], ui[RJ];
-    const int64_t st_row = ((bh * M + m) * 2 * d) * 2;  // complex row m of [M][2d], U half first
+    const int64_t st_row = ((bh * M + mc) * 2 * d) * 2;  // complex row m of [M][2d], U half first
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
-        const int r = lane + kWave * j;
+        const int r = li + 32 * j;
         ur[j] = ui[j] = 0.f;
-        if (state_in != nullptr && r < d) {
+        if (state_in != nullptr && mok && r < d) {
             ur[j] = state_in[st_row + 2 * r];
             ui[j] = state_in[st_row + 2 * r + 1];
         }
     }
     const int64_t row0 = h * p.T + start;  // workspace rows [H][T]
-    float2* srow = s + row0 * M + m;
-    float er = 0.f, ei = 0.f;  // eta_m, the same in every lane
+    float2* srow = s + row0 * M + mc;
+    float er = 0.f, ei = 0.f;  // eta_m, the same in every lane of the half
     if (ETA && eta_in != nullptr) {
-        er = eta_in[(bh * M + m) * 2];
-        ei = eta_in[(bh * M + m) * 2 + 1];
+        er = eta_in[(bh * M + mc) * 2];
+        ei = eta_in[(bh * M + mc) * 2 + 1];
     }
-    const bool dfull = d == kWave * RJ;
-    const int ts = slot8(lane);  // the token whose totals this lane ends with
+    const bool dfull = d == 32 * RJ;
+    const int ts = slot8(li);  // the token whose totals this lane ends with
     // eta over a full batch in closed form, eta(i0 + k) = abar^(k+1) eta(i0 - 1)
     // + bbar sum_{j<=k} abar^j: (plr, pli), (qlr, qli) for k = ts (this lane's
     // token), (a8r, a8i), (q8r, q8i) for k = 7 (the next batch's start), in fp64
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
     }
     uint32_t off[RJ];            // the lane's channels (clamped below d)
 #pragma unroll
-    for (int j = 0; j < RJ; ++j) off[j] = static_cast<uint32_t>(min(lane + kWave * j, d - 1));
+    for (int j = 0; j < RJ; ++j) off[j] = static_cast<uint32_t>(min(li + 32 * j, d - 1));
     for (int64_t i0 = 0; i0 < N; i0 += kTok) {
         // every load at a token and channel clamped into range, all issued
         // before the first use; a ragged batch zeroes what lies out of range
@@ -178,27 +183,27 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
             for (int t = 0; t < kTok; ++t)
 #pragma unroll
                 for (int j = 0; j < RJ; ++j)
-                    if (t >= nt || lane + kWave * j >= d) xv[t][j] = zv[t][j] = 0.f;
+                    if (t >= nt || li + 32 * j >= d) xv[t][j] = zv[t][j] = 0.f;
             key_seq_batch<RJ, ETA, true>(nt, ts, ur, ui, xv, zv, ar, ai, br, bi, spr, spi, er, ei, etr, eti);
         }
         static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
-        const float pr = wave_reduce_scatter8(spr, lane), pi = wave_reduce_scatter8(spi, lane);
-        if (lane < kTok && ts < nt) {
+        const float pr = half_reduce_scatter8(spr, lane), pi = half_reduce_scatter8(spi, lane);
+        if (li < kTok && ts < nt && mok) {
             srow[(i0 + ts) * M] = make_float2(pr, pi);
             if constexpr (ETA) pden[(row0 + i0 + ts) * M + m] = fmaf(pr, etr, -pi * eti);
         }
     }
-    if (state_out != nullptr) {
+    if (state_out != nullptr && mok) {
 #pragma unroll
         for (int j = 0; j < RJ; ++j) {
-            const int r = lane + kWave * j;
+            const int r = li + 32 * j;
             if (r < d) {
                 state_out[st_row + 2 * r] = ur[j];
                 state_out[st_row + 2 * r + 1] = ui[j];
             }
         }
     }
-    if (ETA && eta_out != nullptr && lane == 0) {
+    if (ETA && eta_out != nullptr && li == 0 && mok) {
         eta_out[(bh * M + m) * 2] = er;
         eta_out[(bh * M + m) * 2 + 1] = ei;
     }
@@ -419,17 +424,20 @@ hipError_t launch_ssm_key_scan_seq(const Problem& p, const idattn_params& prm, c
                                    const float* z_k, const float* state_in, float* s,
                                    float* state_out, const float* eta_in, float* eta_out, float* pden,
                                    hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(p.B * p.H), static_cast<unsigned>((p.M + 3) / 4));
+    // two modes per wave, four waves per block
+    const dim3 grid(static_cast<unsigned>(p.B * p.H), static_cast<unsigned>((p.M + 7) / 8));
     float2* s2 = reinterpret_cast<float2*>(s);
 #define IDATTN_KSCAN(RJ, ETA) \
     key_scan_seq_kernel<RJ, ETA><<<grid, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, s2, state_out, eta_in, eta_out, pden)
-    if (pden != nullptr) {
-        if (p.d > 64) IDATTN_KSCAN(2, true);
-        else IDATTN_KSCAN(1, true);
-    } else {
-        if (p.d > 64) IDATTN_KSCAN(2, false);
-        else IDATTN_KSCAN(1, false);
-    }
+#define IDATTN_KSCAN_D(ETA)                     \
+    do {                                        \
+        if (p.d > 64) IDATTN_KSCAN(4, ETA);     \
+        else if (p.d > 32) IDATTN_KSCAN(2, ETA); \
+        else IDATTN_KSCAN(1, ETA);              \
+    } while (0)
+    if (pden != nullptr) IDATTN_KSCAN_D(true);
+    else IDATTN_KSCAN_D(false);
+#undef IDATTN_KSCAN_D
 #undef IDATTN_KSCAN
     return hipGetLastError();
 }
