@@ -42,16 +42,17 @@ __device__ __forceinline__ Zoh zoh_of(const idattn_params& prm, int64_t h, int64
 }
 
 // ------------------------------------------------------------------ per-mode scans
-// One wave per (b, h, m).  In the key scan lane l owns channels l and l + 64
-// (RJ of them); in the value scan the RJ adjacent channels RJ l .. RJ l + RJ - 1,
-// so that a token's bf16 g_o pair is one 4-byte load (measured: adjacent fp32
-// pairs as 8-byte loads made the key scans slower, the bf16 pairs made the
-// value scan faster).
+// One half-wave per (b, h, m), two modes per wave, so that each reduction
+// over the channels runs over 32 lanes and serves both modes at once.  In the
+// key scan lane l of a half owns channels l + 32 j (RJ of them); in the value
+// scan the RJ adjacent channels RJ l .. RJ l + RJ - 1, so that a token's bf16
+// g_o values are one load (measured: adjacent fp32 channels made the key
+// scans slower, adjacent bf16 ones made the value scan faster).
 //
 // Each scan takes kTok tokens at a time.  All their loads are issued first,
 // at token and channel indices clamped into range (addressed from a uniform
 // base with 32-bit lane offsets); a ragged batch (fewer than kTok tokens left,
-// or d below 64 RJ) then zeroes what lies out of range and steps only its
+// or d below 32 RJ) then zeroes what lies out of range and steps only its
 // tokens.  A full batch runs with no per-token condition.
 
 // One batch of the key-side recurrence: V(i) = abar V(i-1) + U(i-1), then
@@ -133,11 +134,14 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
                                                            const float* grad_state, float2* __restrict__ s,
                                                            float2* __restrict__ s_a, float2* __restrict__ ga_key) {
     const int lane = threadIdx.x & (kWave - 1);
+    const int li = lane & 31;  // the lane in its half
     const int64_t bh = blockIdx.x;
-    const int64_t m = static_cast<int64_t>(blockIdx.y) * 4 + (threadIdx.x >> 6);
+    const int64_t m0 = (static_cast<int64_t>(blockIdx.y) * 4 + (threadIdx.x >> 6)) * 2;  // the wave's first mode
     const int64_t M = p.M, N = p.N;
     const int d = static_cast<int>(p.d);
-    if (m >= M) return;  // whole wave; no barriers in this kernel
+    if (m0 >= M) return;  // whole wave; no barriers in this kernel
+    const bool mok = m0 + (lane >> 5) < M;  // false for the second half of the last wave when M is odd
+    const int64_t m = mok ? m0 + (lane >> 5) : M - 1;
     const int64_t h = bh % p.H;
     const Zoh z = zoh_of(prm, h, M, m);
     const float ar = static_cast<float>(z.ar), ai = static_cast<float>(z.ai);
@@ -146,18 +150,18 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
     float ur[RJ], ui[RJ], vr[RJ], vi[RJ];
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
-        const int r = lane + kWave * j;
+        const int r = li + 32 * j;
         ur[j] = ui[j] = vr[j] = vi[j] = 0.f;
-        if (state_in != nullptr && r < d) {
+        if (state_in != nullptr && mok && r < d) {
             ur[j] = state_in[st_row + 2 * r];
             ui[j] = state_in[st_row + 2 * r + 1];
         }
     }
     const int64_t row0 = h * p.T + (bh / p.H) * N;
-    const bool dfull = d == kWave * RJ;
+    const bool dfull = d == 32 * RJ;
     uint32_t off[RJ];  // byte offsets of the lane's channels (clamped below d)
 #pragma unroll
-    for (int j = 0; j < RJ; ++j) off[j] = 4u * static_cast<uint32_t>(min(lane + kWave * j, d - 1));
+    for (int j = 0; j < RJ; ++j) off[j] = 4u * static_cast<uint32_t>(min(li + 32 * j, d - 1));
     for (int64_t i0 = 0; i0 < N; i0 += kTok) {
         const int nt = static_cast<int>(min(N - i0, static_cast<int64_t>(kTok)));
         float xv[kTok][RJ], zv[kTok][RJ];
@@ -183,14 +187,14 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
             for (int t = 0; t < kTok; ++t)
 #pragma unroll
                 for (int j = 0; j < RJ; ++j)
-                    if (t >= nt || lane + kWave * j >= d) xv[t][j] = zv[t][j] = 0.f;
+                    if (t >= nt || li + 32 * j >= d) xv[t][j] = zv[t][j] = 0.f;
             key_batch<RJ, true>(nt, ur, ui, vr, vi, xv, zv, ar, ai, br, bi, spr, spi, sqr, sqi);
         }
         static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
-        const float tpr = wave_reduce_scatter8(spr, lane), tpi = wave_reduce_scatter8(spi, lane);
-        const float tqr = wave_reduce_scatter8(sqr, lane), tqi = wave_reduce_scatter8(sqi, lane);
-        const int t = slot8(lane);
-        if (lane < kTok && t < nt) {
+        const float tpr = half_reduce_scatter8(spr, lane), tpi = half_reduce_scatter8(spi, lane);
+        const float tqr = half_reduce_scatter8(sqr, lane), tqi = half_reduce_scatter8(sqi, lane);
+        const int t = slot8(li);
+        if (li < kTok && t < nt && mok) {
             s[(row0 + i0 + t) * M + m] = make_float2(tpr, tpi);
             s_a[(row0 + i0 + t) * M + m] = make_float2(tqr, tqi);
         }
@@ -199,16 +203,16 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
         float gr = 0.f, gi = 0.f;  // sum_r g_S[r] conj(V_r)
 #pragma unroll
         for (int j = 0; j < RJ; ++j) {
-            const int r = lane + kWave * j;
+            const int r = li + 32 * j;
             if (r < d) {
                 const float sr = grad_state[st_row + 2 * r], si = grad_state[st_row + 2 * r + 1];
                 gr = fmaf(sr, vr[j], fmaf(si, vi[j], gr));
                 gi = fmaf(si, vr[j], fmaf(-sr, vi[j], gi));
             }
         }
-        gr = wave_total(gr);
-        gi = wave_total(gi);
-        if (lane == 0) ga_key[bh * M + m] = make_float2(gr, gi);
+        gr = half_total(gr);
+        gi = half_total(gi);
+        if (li == 0 && mok) ga_key[bh * M + m] = make_float2(gr, gi);
     }
 }
 
@@ -225,11 +229,14 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
                                                              const float2* __restrict__ ga_key,
                                                              float2* __restrict__ gs, float2* __restrict__ ga) {
     const int lane = threadIdx.x & (kWave - 1);
+    const int li = lane & 31;  // the lane in its half
     const int64_t bh = blockIdx.x;
-    const int64_t m = static_cast<int64_t>(blockIdx.y) * 4 + (threadIdx.x >> 6);
+    const int64_t m0 = (static_cast<int64_t>(blockIdx.y) * 4 + (threadIdx.x >> 6)) * 2;  // the wave's first mode
     const int64_t M = p.M, N = p.N, H = p.H;
     const int d = static_cast<int>(p.d);
-    if (m >= M) return;
+    if (m0 >= M) return;  // whole wave; no barriers in this kernel
+    const bool mok = m0 + (lane >> 5) < M;  // false for the second half of the last wave when M is odd
+    const int64_t m = mok ? m0 + (lane >> 5) : M - 1;
     const int64_t b = bh / H, h = bh % H;
     const Zoh z = zoh_of(prm, h, M, m);
     const float ar = static_cast<float>(z.ar), ai = static_cast<float>(z.ai);
@@ -238,9 +245,9 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
     float gmr[RJ], gmi[RJ], wr[RJ], wi[RJ];
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
-        const int c = RJ * lane + j;
+        const int c = RJ * li + j;
         gmr[j] = gmi[j] = wr[j] = wi[j] = 0.f;
-        if (state_in != nullptr && c < d) {
+        if (state_in != nullptr && mok && c < d) {
             gmr[j] = state_in[st_row + 2 * (d + c)];
             gmi[j] = state_in[st_row + 2 * (d + c) + 1];
         }
@@ -248,9 +255,9 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
     const int64_t row0 = h * p.T + b * N;
     const float* zvp = z_v + row0 * d;
     double accr = 0.0, acci = 0.0;  // g_abar share of this mode
-    const bool dfull = d == kWave * RJ;
-    const int ts = slot8(lane);  // the token whose totals this lane ends with
-    const uint32_t coff = static_cast<uint32_t>(min(RJ * lane, d - RJ));  // the lane's first channel (clamped)
+    const bool dfull = d == 32 * RJ;
+    const int ts = slot8(li);  // the token whose totals this lane ends with
+    const uint32_t coff = static_cast<uint32_t>(min(RJ * li, d - RJ));  // the lane's first channel (clamped)
     constexpr uint32_t kIoB = BF16 ? 2 : 4;  // bytes per element of grad_o
     const uint32_t gstride = static_cast<uint32_t>(H * d) * kIoB;  // bytes per token of grad_o
     for (int64_t i0 = 0; i0 < N; i0 += kTok) {
@@ -262,8 +269,8 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
 #pragma unroll
         for (int t = 0; t < kTok; ++t) {
             const uint32_t tt = static_cast<uint32_t>(min(t, nt - 1));
-            buf_load_pair<RJ>(zz[t], zr, 4u * coff, tt * static_cast<uint32_t>(d) * 4u);
-            buf_load_io_pair<RJ, BF16>(go[t], gr, kIoB * coff, tt * gstride);
+            buf_load_run<RJ>(zz[t], zr, 4u * coff, tt * static_cast<uint32_t>(d) * 4u);
+            buf_load_io_run<RJ, BF16>(go[t], gr, kIoB * coff, tt * gstride);
         }
         const int64_t sidx = (row0 + i0 + min(ts, nt - 1)) * M + m;
         const float2 sv = s[sidx], sa = s_a[sidx];  // used after the reduce-scatter
@@ -277,20 +284,20 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
             for (int t = 0; t < kTok; ++t)
 #pragma unroll
                 for (int j = 0; j < RJ; ++j)
-                    if (t >= nt || RJ * lane + j >= d) zz[t][j] = go[t][j] = 0.f;
+                    if (t >= nt || RJ * li + j >= d) zz[t][j] = go[t][j] = 0.f;
             value_batch<RJ, true>(nt, gmr, gmi, wr, wi, zz, go, ar, ai, br, bi, spr, spi, sqr, sqi);
         }
         static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
-        const float pr = wave_reduce_scatter8(spr, lane), pi = wave_reduce_scatter8(spi, lane);
-        const float qr = wave_reduce_scatter8(sqr, lane), qi = wave_reduce_scatter8(sqi, lane);
-        if (lane < kTok && ts < nt) {
+        const float pr = half_reduce_scatter8(spr, lane), pi = half_reduce_scatter8(spi, lane);
+        const float qr = half_reduce_scatter8(sqr, lane), qi = half_reduce_scatter8(sqi, lane);
+        if (li < kTok && ts < nt && mok) {
             gs[sidx] = make_float2(pr, pi);
             // conj(s) gw + g_s conj(s_a), summed per lane (every eighth token) in fp64
             accr += static_cast<double>(sv.x * qr + sv.y * qi) + static_cast<double>(pr * sa.x + pi * sa.y);
             acci += static_cast<double>(sv.x * qi - sv.y * qr) + static_cast<double>(pi * sa.x - pr * sa.y);
         }
     }
-    // the eight lanes' sums in a fixed order (lanes >= 8 hold zeros)
+    // the eight lanes' sums of each half in a fixed order (the other lanes hold zeros)
 #pragma unroll
     for (int off = 4; off >= 1; off >>= 1) {
         accr += __shfl_xor(accr, off, kWave);
@@ -300,22 +307,22 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
         float gr = 0.f, gi = 0.f;  // sum_c g_S[c] conj(W_c)
 #pragma unroll
         for (int j = 0; j < RJ; ++j) {
-            const int c = RJ * lane + j;
+            const int c = RJ * li + j;
             if (c < d) {
                 const float sr = grad_state[st_row + 2 * (d + c)], si = grad_state[st_row + 2 * (d + c) + 1];
                 gr = fmaf(sr, wr[j], fmaf(si, wi[j], gr));
                 gi = fmaf(si, wr[j], fmaf(-sr, wi[j], gi));
             }
         }
-        gr = wave_total(gr);
-        gi = wave_total(gi);
-        if (lane == 0) {
+        gr = half_total(gr);
+        gi = half_total(gi);
+        if (li == 0) {
             const float2 k = ga_key[bh * M + m];
             accr += static_cast<double>(gr) + k.x;
             acci += static_cast<double>(gi) + k.y;
         }
     }
-    if (lane == 0) ga[bh * M + m] = make_float2(static_cast<float>(accr), static_cast<float>(acci));
+    if (li == 0 && mok) ga[bh * M + m] = make_float2(static_cast<float>(accr), static_cast<float>(acci));
 }
 
 // Sum of x[0..K) in a fixed pairwise order (deterministic).
@@ -1115,8 +1122,11 @@ hipError_t launch_backward(const Problem& p, const idattn_params& prm, const voi
 
     hipError_t e = launch_featmap_conv_norm(p, prm, q, k, v, tail_in, xi_q, z_k, z_v, stream);
     if (e != hipSuccess) return e;
-    const dim3 gm(static_cast<unsigned>(bh), static_cast<unsigned>((p.M + 3) / 4));
+    // the per-mode scans: two modes per wave (one per half), four waves per block
+    const dim3 gm(static_cast<unsigned>(bh), static_cast<unsigned>((p.M + 7) / 8));
     if (p.d > 64)
+        bwd_key_scan_kernel<4><<<gm, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, grad_state, s, s_a, ga_key);
+    else if (p.d > 32)
         bwd_key_scan_kernel<2><<<gm, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, grad_state, s, s_a, ga_key);
     else
         bwd_key_scan_kernel<1><<<gm, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, grad_state, s, s_a, ga_key);
@@ -1125,6 +1135,9 @@ hipError_t launch_backward(const Problem& p, const idattn_params& prm, const voi
     bwd_value_scan_kernel<RJ, BF><<<gm, 256, 0, stream>>>(p, prm, z_v, grad_o, state_in, grad_state, s, s_a, ga_key, \
                                                           gs, ga)
     if (p.d > 64) {
+        if (p.bf16) IDATTN_BV(4, true);
+        else IDATTN_BV(4, false);
+    } else if (p.d > 32) {
         if (p.bf16) IDATTN_BV(2, true);
         else IDATTN_BV(2, false);
     } else {

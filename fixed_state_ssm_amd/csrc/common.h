@@ -60,11 +60,16 @@ __device__ __forceinline__ uint32_t buf_load_raw(__amdgpu_buffer_rsrc_t r, uint3
     else return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
 }
 
-// RJ adjacent floats (one 4- or 8-byte buffer load), and RJ adjacent elements
-// of an I/O tensor (a bf16 pair in one 4-byte load, or fp32).
+// RJ (1, 2 or 4) adjacent floats in one buffer load, and RJ adjacent elements
+// of an I/O tensor (bf16 in one 2-, 4- or 8-byte load, or fp32).
 template <int RJ>
-__device__ __forceinline__ void buf_load_pair(float (&x)[RJ], __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    if constexpr (RJ == 2) {
+__device__ __forceinline__ void buf_load_run(float (&x)[RJ], __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    static_assert(RJ == 1 || RJ == 2 || RJ == 4, "1, 2 or 4 elements");
+    if constexpr (RJ == 4) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = __uint_as_float(v[j]);
+    } else if constexpr (RJ == 2) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
         x[0] = __uint_as_float(v[0]);
         x[1] = __uint_as_float(v[1]);
@@ -73,16 +78,23 @@ __device__ __forceinline__ void buf_load_pair(float (&x)[RJ], __amdgpu_buffer_rs
     }
 }
 template <int RJ, bool BF16>
-__device__ __forceinline__ void buf_load_io_pair(float (&x)[RJ], __amdgpu_buffer_rsrc_t r, uint32_t voff,
-                                                 uint32_t soff) {
-    if constexpr (BF16 && RJ == 2) {
+__device__ __forceinline__ void buf_load_io_run(float (&x)[RJ], __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                uint32_t soff) {
+    if constexpr (BF16 && RJ == 4) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            x[2 * j] = __uint_as_float(v[j] << 16);
+            x[2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+        }
+    } else if constexpr (BF16 && RJ == 2) {
         const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
         x[0] = __uint_as_float(v << 16);
         x[1] = __uint_as_float(v & 0xffff0000u);
     } else if constexpr (BF16) {
         x[0] = __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)) << 16);
     } else {
-        buf_load_pair<RJ>(x, r, voff, soff);
+        buf_load_run<RJ>(x, r, voff, soff);
     }
 }
 
@@ -234,6 +246,15 @@ __device__ __forceinline__ float half_reduce_scatter8(const float (&v)[8], int l
     }
     float x = (b2 ? w[1] : w[0]) + dpp_f<0x124>(b2 ? w[0] : w[1]);  // row_ror:4
     x += dpp_f<0x128>(x);                                           // row_ror:8
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+// The total over each half of the wave; every lane gets its half's.
+__device__ __forceinline__ float half_total(float x) {
+    x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_f<0x124>(x);  // row_ror:4
+    x += dpp_f<0x128>(x);  // row_ror:8
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
