@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
     float ur[RJ], ui[RJ], vr[RJ], vi[RJ];
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
-        const int r = li + 32 * j;
+        const int r = RJ * li + j;
         ur[j] = ui[j] = vr[j] = vi[j] = 0.f;
         if (state_in != nullptr && mok && r < d) {
             ur[j] = state_in[st_row + 2 * r];
@@ -159,36 +159,38 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
     }
     const int64_t row0 = h * p.T + (bh / p.H) * N;
     const bool dfull = d == 32 * RJ;
-    uint32_t off[RJ];  // byte offsets of the lane's channels (clamped below d)
-#pragma unroll
-    for (int j = 0; j < RJ; ++j) off[j] = 4u * static_cast<uint32_t>(min(li + 32 * j, d - 1));
-    for (int64_t i0 = 0; i0 < N; i0 += kTok) {
-        const int nt = static_cast<int>(min(N - i0, static_cast<int64_t>(kTok)));
-        float xv[kTok][RJ], zv[kTok][RJ];
-        const int64_t row = (row0 + i0) * d;  // the batch's rows, uniform
-        const uint32_t nb = static_cast<uint32_t>(nt * d * 4);
+    const uint32_t coff = 4u * static_cast<uint32_t>(min(RJ * li, d - RJ));  // byte offset of the lane's channels
+    // one batch's rows into x, z (tokens clamped below the batch's nt)
+    auto fetch = [&](int64_t j0, int jnt, float (&x)[kTok][RJ], float (&zq)[kTok][RJ]) {
+        const int64_t row = (row0 + j0) * d;  // uniform
+        const uint32_t nb = static_cast<uint32_t>(jnt * d * 4);
         const __amdgpu_buffer_rsrc_t xr = rsrc_at(xi_q + row, nb), zr = rsrc_at(z_k + row, nb);
 #pragma unroll
         for (int t = 0; t < kTok; ++t) {
-            const uint32_t tb = static_cast<uint32_t>(min(t, nt - 1) * d * 4);
-#pragma unroll
-            for (int j = 0; j < RJ; ++j) {
-                xv[t][j] = buf_load(xr, off[j], tb);
-                zv[t][j] = buf_load(zr, off[j], tb);
-            }
+            const uint32_t tb = static_cast<uint32_t>(min(t, jnt - 1) * d * 4);
+            buf_load_run<RJ>(x[t], xr, coff, tb);
+            buf_load_run<RJ>(zq[t], zr, coff, tb);
         }
+    };
+    // one batch from x, z while the batch at j0 is loaded into xn, zn (the last
+    // batch loads itself again), so that no batch waits on memory
+    auto step = [&](int64_t i0, float (&x)[kTok][RJ], float (&zq)[kTok][RJ], float (&xn)[kTok][RJ],
+                    float (&zn)[kTok][RJ]) {
+        const int nt = static_cast<int>(min(N - i0, static_cast<int64_t>(kTok)));
+        const int64_t j0 = i0 + kTok < N ? i0 + kTok : i0;
+        fetch(j0, static_cast<int>(min(N - j0, static_cast<int64_t>(kTok))), xn, zn);
         // the lane's shares of s and s_a of the kTok tokens, then one reduce-scatter
-        // per quantity (lane t < 8 ends with token slot8(t)'s totals)
+        // per quantity (lane t < 8 of a half ends with token slot8(t)'s totals)
         float spr[kTok], spi[kTok], sqr[kTok], sqi[kTok];
         if (nt == kTok && dfull) {
-            key_batch<RJ, false>(nt, ur, ui, vr, vi, xv, zv, ar, ai, br, bi, spr, spi, sqr, sqi);
+            key_batch<RJ, false>(nt, ur, ui, vr, vi, x, zq, ar, ai, br, bi, spr, spi, sqr, sqi);
         } else {
 #pragma unroll
             for (int t = 0; t < kTok; ++t)
 #pragma unroll
                 for (int j = 0; j < RJ; ++j)
-                    if (t >= nt || li + 32 * j >= d) xv[t][j] = zv[t][j] = 0.f;
-            key_batch<RJ, true>(nt, ur, ui, vr, vi, xv, zv, ar, ai, br, bi, spr, spi, sqr, sqi);
+                    if (t >= nt || RJ * li + j >= d) x[t][j] = zq[t][j] = 0.f;
+            key_batch<RJ, true>(nt, ur, ui, vr, vi, x, zq, ar, ai, br, bi, spr, spi, sqr, sqi);
         }
         static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
         const float tpr = half_reduce_scatter8(spr, lane), tpi = half_reduce_scatter8(spi, lane);
@@ -198,12 +200,19 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
             s[(row0 + i0 + t) * M + m] = make_float2(tpr, tpi);
             s_a[(row0 + i0 + t) * M + m] = make_float2(tqr, tqi);
         }
+    };
+    float xa[kTok][RJ], za[kTok][RJ], xb[kTok][RJ], zb[kTok][RJ];  // two batches' rows, in turn
+    if (N > 0) fetch(0, static_cast<int>(min(N, static_cast<int64_t>(kTok))), xa, za);
+    for (int64_t i0 = 0; i0 < N; i0 += 2 * kTok) {
+        step(i0, xa, za, xb, zb);
+        if (i0 + kTok >= N) break;
+        step(i0 + kTok, xb, zb, xa, za);
     }
     if (grad_state != nullptr) {
         float gr = 0.f, gi = 0.f;  // sum_r g_S[r] conj(V_r)
 #pragma unroll
         for (int j = 0; j < RJ; ++j) {
-            const int r = li + 32 * j;
+            const int r = RJ * li + j;
             if (r < d) {
                 const float sr = grad_state[st_row + 2 * r], si = grad_state[st_row + 2 * r + 1];
                 gr = fmaf(sr, vr[j], fmaf(si, vi[j], gr));
