@@ -3,10 +3,12 @@
 // recurrence) and the reference the chunked path is compared with.
 //
 // ssm_key_scan_seq: one half-wave per (b, h, mode m), two modes per wave; lane
-// l of a half owns channels l + 32 j of U_m.  Each step updates U_m(i) = abar
-// U_m(i-1) + bbar z_k(i); the lanes' shares of s_m(i) = xi_q(i) . U_m(i) over
-// the R channels are reduced eight tokens at a time with one reduce-scatter per
-// quantity over the half, which serves both modes of the wave at once.  With
+// l of a half owns the RJ adjacent channels RJ l .. RJ l + RJ - 1 of U_m.  Each
+// step updates U_m(i) = abar U_m(i-1) + bbar z_k(i); the lanes' shares of
+// s_m(i) = xi_q(i) . U_m(i) over the R channels are reduced eight tokens at a
+// time with one reduce-scatter per quantity over the half, which serves both
+// modes of the wave at once.  Each batch of eight tokens issues the next
+// batch's loads before it is stepped (two register sets in turn).  With
 // the normalised readout (ETA) the wave also carries the mode's normaliser
 // eta_m(i) = abar eta_m(i-1) + bbar (over a full batch in closed form, from
 // powers of abar formed in fp64) and writes Re(s_m(i) eta_m(i)), the mode's
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
     const int64_t st_row = ((bh * M + mc) * 2 * d) * 2;  // complex row m of [M][2d], U half first
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
-        const int r = li + 32 * j;
+        const int r = RJ * li + j;
         ur[j] = ui[j] = 0.f;
         if (state_in != nullptr && mok && r < d) {
             ur[j] = state_in[st_row + 2 * r];
@@ -141,31 +143,27 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
             }
         }
     }
-    uint32_t off[RJ];            // the lane's channels (clamped below d)
-#pragma unroll
-    for (int j = 0; j < RJ; ++j) off[j] = static_cast<uint32_t>(min(li + 32 * j, d - 1));
-    for (int64_t i0 = 0; i0 < N; i0 += kTok) {
-        // every load at a token and channel clamped into range, all issued
-        // before the first use; a ragged batch zeroes what lies out of range
-        const int nt = static_cast<int>(min(N - i0, static_cast<int64_t>(kTok)));
-        float xv[kTok][RJ], zv[kTok][RJ];
-        uint32_t boff[RJ];
-#pragma unroll
-        for (int j = 0; j < RJ; ++j) {
-            boff[j] = 4u * off[j];
-            asm volatile("" : "+v"(boff[j]));  // formed here, so each load takes it as a 32-bit offset
-        }
+    const uint32_t coff = 4u * static_cast<uint32_t>(min(RJ * li, d - RJ));  // byte offset of the lane's channels
+    // one batch's rows into x, z (tokens clamped below the batch's nt): the
+    // lane's RJ adjacent channels in one buffer load per row
+    auto fetch = [&](int64_t j0, int jnt, float (&x)[kTok][RJ], float (&zq)[kTok][RJ]) {
+        const int64_t row = (row0 + j0) * d;  // uniform
+        const uint32_t nb = static_cast<uint32_t>(jnt * d * 4);
+        const __amdgpu_buffer_rsrc_t xr = rsrc_at(xi_q + row, nb), zr = rsrc_at(z_k + row, nb);
 #pragma unroll
         for (int t = 0; t < kTok; ++t) {
-            const int64_t row = (row0 + i0 + min(t, nt - 1)) * d;  // uniform
-            const char* xr = reinterpret_cast<const char*>(xi_q + row);
-            const char* zr = reinterpret_cast<const char*>(z_k + row);
-#pragma unroll
-            for (int j = 0; j < RJ; ++j) {
-                xv[t][j] = *reinterpret_cast<const float*>(xr + boff[j]);
-                zv[t][j] = *reinterpret_cast<const float*>(zr + boff[j]);
-            }
+            const uint32_t tb = static_cast<uint32_t>(min(t, jnt - 1) * d * 4);
+            buf_load_run<RJ>(x[t], xr, coff, tb);
+            buf_load_run<RJ>(zq[t], zr, coff, tb);
         }
+    };
+    // one batch from x, z while the batch at j0 is loaded into xn, zn (the last
+    // batch loads itself again), so that no batch waits on memory
+    auto step = [&](int64_t i0, float (&xv)[kTok][RJ], float (&zv)[kTok][RJ], float (&xn)[kTok][RJ],
+                    float (&zn)[kTok][RJ]) {
+        const int nt = static_cast<int>(min(N - i0, static_cast<int64_t>(kTok)));
+        const int64_t j0 = i0 + kTok < N ? i0 + kTok : i0;
+        fetch(j0, static_cast<int>(min(N - j0, static_cast<int64_t>(kTok))), xn, zn);
         float spr[kTok], spi[kTok];
         float etr = 0.f, eti = 0.f;
         if (nt == kTok && dfull) {
@@ -178,12 +176,12 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
                 er = nr;
                 ei = ni;
             }
-        } else {
+        } else {  // a ragged batch zeroes what lies out of range
 #pragma unroll
             for (int t = 0; t < kTok; ++t)
 #pragma unroll
                 for (int j = 0; j < RJ; ++j)
-                    if (t >= nt || li + 32 * j >= d) xv[t][j] = zv[t][j] = 0.f;
+                    if (t >= nt || RJ * li + j >= d) xv[t][j] = zv[t][j] = 0.f;
             key_seq_batch<RJ, ETA, true>(nt, ts, ur, ui, xv, zv, ar, ai, br, bi, spr, spi, er, ei, etr, eti);
         }
         static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
@@ -192,11 +190,18 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
             srow[(i0 + ts) * M] = make_float2(pr, pi);
             if constexpr (ETA) pden[(row0 + i0 + ts) * M + m] = fmaf(pr, etr, -pi * eti);
         }
+    };
+    float xa[kTok][RJ], za[kTok][RJ], xb[kTok][RJ], zb[kTok][RJ];  // two batches' rows, in turn
+    if (N > 0) fetch(0, static_cast<int>(min(N, static_cast<int64_t>(kTok))), xa, za);
+    for (int64_t i0 = 0; i0 < N; i0 += 2 * kTok) {
+        step(i0, xa, za, xb, zb);
+        if (i0 + kTok >= N) break;
+        step(i0 + kTok, xb, zb, xa, za);
     }
     if (state_out != nullptr && mok) {
 #pragma unroll
         for (int j = 0; j < RJ; ++j) {
-            const int r = li + 32 * j;
+            const int r = RJ * li + j;
             if (r < d) {
                 state_out[st_row + 2 * r] = ur[j];
                 state_out[st_row + 2 * r + 1] = ui[j];
