@@ -405,21 +405,46 @@ __global__ __launch_bounds__(kStage) void value_scan_seq_kernel(Problem p, idatt
 }
 
 // o [T][H][d] from the two splits' partial numerators (and denominators):
-// o = num0 + num1, or (num0 + num1) / (den0 + den1) with ETA.
-template <bool BF16, bool ETA>
+// o = num0 + num1, or (num0 + num1) / (den0 + den1) with ETA.  A thread takes
+// four adjacent channels (d is 16, 32, 64 or 128: dq_shift = log2(d / 4)), and
+// the (token, head) of a row comes from 32-bit index arithmetic when T H fits
+// in 32 bits (TH32).
+template <bool BF16, bool ETA, bool TH32>
 __global__ __launch_bounds__(256) void combine_seq_kernel(Problem p, const float* __restrict__ num0,
                                                           const float* __restrict__ num1,
-                                                          const float* __restrict__ dpart, void* __restrict__ o) {
+                                                          const float* __restrict__ dpart, void* __restrict__ o,
+                                                          int dq_shift) {
     const int64_t H = p.H, T = p.T, d = p.d;
-    const int64_t n = T * H * d;
-    for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
-         e += static_cast<int64_t>(gridDim.x) * 256) {
-        const int64_t c = e % d, th = e / d;  // o is [T][H][d]
-        const int64_t h = th % H, t = th / H;
+    const int64_t nq = (T * H) << dq_shift;
+    for (int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; q < nq;
+         q += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t th = q >> dq_shift;  // o's row, t H + h
+        const int64_t c = (q & ((int64_t{1} << dq_shift) - 1)) * 4;
+        int64_t h, t;
+        if constexpr (TH32) {
+            const uint32_t th32 = static_cast<uint32_t>(th), H32 = static_cast<uint32_t>(H);
+            t = th32 / H32;
+            h = th32 - static_cast<uint32_t>(t) * H32;
+        } else {
+            t = th / H;
+            h = th - t * H;
+        }
         const int64_t w = (h * T + t) * d + c;  // the partials are [H][T][d]
-        float x = num0[w] + num1[w];
-        if constexpr (ETA) x /= dpart[h * T + t] + dpart[H * T + h * T + t];
-        store_io<BF16>(o, e, x);
+        const float4 a = *reinterpret_cast<const float4*>(num0 + w), b = *reinterpret_cast<const float4*>(num1 + w);
+        float x[4] = {a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w};
+        if constexpr (ETA) {
+            const float den = dpart[h * T + t] + dpart[H * T + h * T + t];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] /= den;
+        }
+        const int64_t e = th * d + c;
+        if constexpr (BF16) {
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(o) + e) =
+                make_uint2(f32_to_bf16(x[0]) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16),
+                           f32_to_bf16(x[2]) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16));
+        } else {
+            *reinterpret_cast<float4*>(static_cast<float*>(o) + e) = make_float4(x[0], x[1], x[2], x[3]);
+        }
     }
 }
 
@@ -482,10 +507,17 @@ hipError_t launch_ssm_value_scan_readout_seq(const Problem& p, const idattn_para
 #undef IDATTN_VSCAN_K
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
-    const int64_t n = p.T * p.H * p.d;
-    const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 4096));
-    if (n == 0) return hipSuccess;
-#define IDATTN_COMB(BF, ETA) combine_seq_kernel<BF, ETA><<<blocks, 256, 0, stream>>>(p, num0, num1, dpart, o)
+    const int64_t nq = p.T * p.H * (p.d / 4);  // d is 16, 32, 64 or 128
+    if (nq == 0) return hipSuccess;
+    if (p.d % 4 != 0 || (p.d & (p.d - 1)) != 0) return hipErrorInvalidValue;
+    const int dq_shift = __builtin_ctzll(static_cast<unsigned long long>(p.d / 4));
+    const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((nq + 255) / 256, 4096));
+    const bool th32 = p.T * p.H <= int64_t{0xffffffff};
+#define IDATTN_COMB(BF, ETA)                                                                                  \
+    do {                                                                                                      \
+        if (th32) combine_seq_kernel<BF, ETA, true><<<blocks, 256, 0, stream>>>(p, num0, num1, dpart, o, dq_shift); \
+        else combine_seq_kernel<BF, ETA, false><<<blocks, 256, 0, stream>>>(p, num0, num1, dpart, o, dq_shift);     \
+    } while (0)
     if (p.bf16) {
         if (pden != nullptr) IDATTN_COMB(true, true);
         else IDATTN_COMB(true, false);
