@@ -200,37 +200,16 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
 }
-// Reduce-scatter of 8 values over the 64 lanes of a wave: on return lane l
-// holds the wave total of value slot8(l) = 4 b0 + 2 b1 + b2 (b_k bit k of l),
-// so that lanes 0..7 hold all eight.  Each of the first three steps pairs
-// lanes that differ in one of bits 0..2, keeps the half of the values that
-// the lane's bit selects and adds what the partner sends of that half; the
-// last steps add the one remaining value across bit 3 (rotate by 8 in a row
-// of 16, whose rotation by 4 has already paired bit 2), across rows and
-// across halves.  About 26 instructions against 8 wave_total's 80.
+// Reduce-scatter of 8 values over each half of a wave (lanes 0..31 and
+// 32..63 on their own): on return lane l holds its half's total of value
+// slot8(l & 31) = 4 b0 + 2 b1 + b2 (b_k bit k of l), so that lanes 0..7 of
+// each half hold all eight.  Each of the first three steps pairs lanes that
+// differ in one of bits 0..2, keeps the half of the values that the lane's bit
+// selects and adds what the partner sends of that half; the last steps add the
+// one remaining value across bit 3 (rotate by 8 in a row of 16, whose rotation
+// by 4 has already paired bit 2) and across the two rows of the half.  About
+// 24 instructions against 8 half_total's 72.
 __device__ __forceinline__ int slot8(int lane) { return 4 * (lane & 1) + 2 * ((lane >> 1) & 1) + ((lane >> 2) & 1); }
-__device__ __forceinline__ float wave_reduce_scatter8(const float (&v)[8], int lane) {
-    const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4;
-    float u[4], w[2];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float send = b0 ? v[k] : v[k + 4], keep = b0 ? v[k + 4] : v[k];
-        u[k] = keep + dpp_f<0xB1>(send);  // quad_perm [1,0,3,2]
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const float send = b1 ? u[k] : u[k + 2], keep = b1 ? u[k + 2] : u[k];
-        w[k] = keep + dpp_f<0x4E>(send);  // quad_perm [2,3,0,1]
-    }
-    float x = (b2 ? w[1] : w[0]) + dpp_f<0x124>(b2 ? w[0] : w[1]);  // row_ror:4
-    x += dpp_f<0x128>(x);                                           // row_ror:8
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
-// The same over each half of the wave (lanes 0..31 and 32..63 on their own):
-// lane l ends with its half's total of value slot8(l & 31).
 __device__ __forceinline__ float half_reduce_scatter8(const float (&v)[8], int lane) {
     const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4;
     float u[4], w[2];
@@ -260,12 +239,7 @@ __device__ __forceinline__ float half_total(float x) {
 }
 // The total over the 64 lanes; every lane gets it.
 __device__ __forceinline__ float wave_total(float x) {
-    x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
-    x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
-    x += dpp_f<0x124>(x);  // row_ror:4
-    x += dpp_f<0x128>(x);  // row_ror:8
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    x = half_total(x);
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
