@@ -133,12 +133,11 @@ int resolve_algo(const idattn_dims& D) {
 // tokens on the [T] axis: B N for the dense entry points, N for the packed one
 size_t seq_workspace_bytes(const idattn_dims& D, int64_t T, bool eta = false) {
     // xi_q, z_k, z_v: float [H][T][d]; s: complex float [H][T][M]; with the
-    // normalised readout also the denominator shares, float [H][T][M], and the
-    // value scan's two partial denominators, float [2][H][T]
+    // normalised readout also the denominator shares, float [H][T][M]
     const size_t tok = static_cast<size_t>(D.H) * T;
     const size_t a = 3 * tok * D.d * sizeof(float);
     const size_t s = tok * D.M * 2 * sizeof(float);
-    const size_t e = eta ? (tok * D.M + 2 * tok) * sizeof(float) : 0;
+    const size_t e = eta ? tok * D.M * sizeof(float) : 0;
     return ((a + 255) / 256) * 256 + ((s + 255) / 256) * 256 + e;
 }
 
@@ -176,14 +175,12 @@ idattn_status run_sequential(const idattn::Problem& p, const idattn_params& prm,
     float* sbuf = reinterpret_cast<float*>(base + off_s);
     float* pden = eta ? reinterpret_cast<float*>(base + off_s + ((tok * p.M * 2 * sizeof(float) + 255) / 256) * 256)
                       : nullptr;
-    float* dpart = eta ? pden + tok * p.M : nullptr;  // [2][H][T]
     hipError_t e = idattn::launch_featmap_conv_norm(p, prm, q, k, v, tail_in, xi_q, z_k, z_v, s);
     if (e != hipSuccess) return hip_fail(e, "featmap_conv_norm");
     e = idattn::launch_ssm_key_scan_seq(p, prm, xi_q, z_k, state_in, sbuf, state_out, eta_in, eta_out, pden, s);
     if (e != hipSuccess) return hip_fail(e, "ssm_key_scan");
     // xi_q and z_k are dead once the key scan has run: they take the value scan's partial numerators
-    e = idattn::launch_ssm_value_scan_readout_seq(p, prm, sbuf, z_v, state_in, o, state_out, pden, xi_q, z_k, dpart,
-                                                  s);
+    e = idattn::launch_ssm_value_scan_readout_seq(p, prm, sbuf, z_v, state_in, o, state_out, pden, xi_q, z_k, s);
     if (e != hipSuccess) return hip_fail(e, "ssm_value_scan_readout");
     if (tail_out) {
         e = idattn::launch_tail_update(p, q, k, tail_in, tail_out, s);

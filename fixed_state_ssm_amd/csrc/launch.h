@@ -40,13 +40,13 @@ hipError_t launch_ssm_key_scan_seq(const Problem& p, const idattn_params& prm,
 
 // With M >= 32 the modes are split over two blocks whose partial numerators
 // go to num0 and num1 ([H][T][d] fp32 each; the feature buffers xi_q and z_k,
-// free once the key scan has run) and, with pden, whose partial denominators
-// go to dpart ([2][H][T] fp32); a combine kernel forms o.
+// free once the key scan has run); a combine kernel forms o, and with pden
+// (the normalised readout) sums the denominator from it.
 hipError_t launch_ssm_value_scan_readout_seq(const Problem& p, const idattn_params& prm,
                                              const float* s, const float* z_v,
                                              const float* state_in, void* o,
                                              float* state_out, const float* pden, float* num0, float* num1,
-                                             float* dpart, hipStream_t stream);
+                                             hipStream_t stream);
 
 // ---- chunked MFMA path (bf16 I/O; wave-specialised kernels for d = R in
 // {64, 128}, M = 64, W <= 4, the SiLU feature maps)

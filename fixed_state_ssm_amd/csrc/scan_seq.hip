@@ -286,16 +286,17 @@ __device__ __forceinline__ void value_seq_block(int nt, const float2* s_row, con
 // ETA: o = numerator / denominator, the denominator summed over the modes
 // from the key scan's per-mode shares pden [H][T][M].
 // SPLIT: the modes are split over two blocks (blockIdx.z); split z writes its
-// partial numerator to num0 or num1 ([H][T][d] fp32) and, with ETA, its
-// partial denominator to dpart[z] ([2][H][T]); combine_seq_kernel forms o.
+// partial numerator to num0 or num1 ([H][T][d] fp32), and combine_seq_kernel
+// forms o (and with the normalised readout sums the denominator itself, so a
+// split block runs without ETA).
 template <bool BF16, int MW, bool ETA, bool SPLIT>
 __global__ __launch_bounds__(kStage) void value_scan_seq_kernel(Problem p, idattn_params prm,
                                                                 const float2* __restrict__ s,
                                                                 const float* __restrict__ z_v,
                                                                 const float* state_in, void* __restrict__ o,
                                                                 float* state_out, const float* __restrict__ pden,
-                                                                float* __restrict__ num0, float* __restrict__ num1,
-                                                                float* __restrict__ dpart) {
+                                                                float* __restrict__ num0, float* __restrict__ num1) {
+    static_assert(!(ETA && SPLIT), "the combine kernel divides when the modes are split");
     __shared__ float2 s_blk[kStage];
     __shared__ float z_blk[kStage];
     __shared__ float p_blk[ETA ? kStage : 1];
@@ -375,11 +376,6 @@ __global__ __launch_bounds__(kStage) void value_scan_seq_kernel(Problem p, idatt
                     float sum = tree_sum(part);
                     if constexpr (SPLIT) {
                         num[(row0 + i0 + t) * d + cc] = sum;
-                        if (ETA && l == 0 && group == 0) {
-#pragma unroll
-                            for (int i = 0; i < kVW; ++i) part[i] = den_s[i][t];
-                            dpart[blockIdx.z * H * p.T + row0 + i0 + t] = tree_sum(part);
-                        }
                     } else {
                         if constexpr (ETA) {
 #pragma unroll
@@ -404,17 +400,20 @@ __global__ __launch_bounds__(kStage) void value_scan_seq_kernel(Problem p, idatt
     }
 }
 
-// o [T][H][d] from the two splits' partial numerators (and denominators):
-// o = num0 + num1, or (num0 + num1) / (den0 + den1) with ETA.  A thread takes
-// four adjacent channels (d is 16, 32, 64 or 128: dq_shift = log2(d / 4)), and
-// the (token, head) of a row comes from 32-bit index arithmetic when T H fits
-// in 32 bits (TH32).
+// o [T][H][d] from the two splits' partial numerators: o = num0 + num1, or
+// with ETA (num0 + num1) / den, den = sum_m pden[h][t][m].  A thread takes four
+// adjacent channels (d is 16, 32, 64 or 128: dq_shift = log2(d / 4)), and the
+// (token, head) of a row comes from 32-bit index arithmetic when T H fits in
+// 32 bits (TH32).  A row's d / 4 threads are adjacent lanes of one wave: each
+// sums every (d/4)-th mode share from its own, then the lanes add theirs in a
+// fixed butterfly order.
 template <bool BF16, bool ETA, bool TH32>
 __global__ __launch_bounds__(256) void combine_seq_kernel(Problem p, const float* __restrict__ num0,
                                                           const float* __restrict__ num1,
-                                                          const float* __restrict__ dpart, void* __restrict__ o,
+                                                          const float* __restrict__ pden, void* __restrict__ o,
                                                           int dq_shift) {
     const int64_t H = p.H, T = p.T, d = p.d;
+    const int M = static_cast<int>(p.M), dq = 1 << dq_shift;
     const int64_t nq = (T * H) << dq_shift;
     for (int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; q < nq;
          q += static_cast<int64_t>(gridDim.x) * 256) {
@@ -433,7 +432,10 @@ __global__ __launch_bounds__(256) void combine_seq_kernel(Problem p, const float
         const float4 a = *reinterpret_cast<const float4*>(num0 + w), b = *reinterpret_cast<const float4*>(num1 + w);
         float x[4] = {a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w};
         if constexpr (ETA) {
-            const float den = dpart[h * T + t] + dpart[H * T + h * T + t];
+            const float* pr = pden + (h * T + t) * M;
+            float den = 0.f;
+            for (int m = static_cast<int>(c >> 2); m < M; m += dq) den += pr[m];
+            for (int off = 1; off < dq; off <<= 1) den += __shfl_xor(den, off, kWave);
 #pragma unroll
             for (int j = 0; j < 4; ++j) x[j] /= den;
         }
@@ -475,7 +477,7 @@ hipError_t launch_ssm_key_scan_seq(const Problem& p, const idattn_params& prm, c
 hipError_t launch_ssm_value_scan_readout_seq(const Problem& p, const idattn_params& prm,
                                              const float* s, const float* z_v,
                                              const float* state_in, void* o, float* state_out,
-                                             const float* pden, float* num0, float* num1, float* dpart,
+                                             const float* pden, float* num0, float* num1,
                                              hipStream_t stream) {
     // two mode splits when each still gets at least one mode per wave
     const int splits = p.M >= 2 * kVW ? 2 : 1;
@@ -483,16 +485,17 @@ hipError_t launch_ssm_value_scan_readout_seq(const Problem& p, const idattn_para
                     static_cast<unsigned>(splits));
     const float2* s2 = reinterpret_cast<const float2*>(s);
 #define IDATTN_VSCAN_K(BF, MW, ETA, SPLIT) \
-    value_scan_seq_kernel<BF, MW, ETA, SPLIT><<<grid, kStage, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out, pden, num0, num1, dpart)
+    value_scan_seq_kernel<BF, MW, ETA, SPLIT><<<grid, kStage, 0, stream>>>(p, prm, s2, z_v, state_in, o, state_out, pden, num0, num1)
 #define IDATTN_VSCAN_E(MW, ETA, SPLIT)                  \
     do {                                                \
         if (p.bf16) IDATTN_VSCAN_K(true, MW, ETA, SPLIT); \
         else IDATTN_VSCAN_K(false, MW, ETA, SPLIT);       \
     } while (0)
-#define IDATTN_VSCAN(MW, SPLIT)                                \
-    do {                                                       \
-        if (pden != nullptr) IDATTN_VSCAN_E(MW, true, SPLIT);  \
-        else IDATTN_VSCAN_E(MW, false, SPLIT);                 \
+// split blocks leave the division to the combine kernel
+#define IDATTN_VSCAN(MW, SPLIT)                                     \
+    do {                                                            \
+        if (!(SPLIT) && pden != nullptr) IDATTN_VSCAN_E(MW, true, false); \
+        else IDATTN_VSCAN_E(MW, false, SPLIT);                      \
     } while (0)
     switch (p.M / (kVW * splits)) {
         case 1:
@@ -515,8 +518,8 @@ hipError_t launch_ssm_value_scan_readout_seq(const Problem& p, const idattn_para
     const bool th32 = p.T * p.H <= int64_t{0xffffffff};
 #define IDATTN_COMB(BF, ETA)                                                                                  \
     do {                                                                                                      \
-        if (th32) combine_seq_kernel<BF, ETA, true><<<blocks, 256, 0, stream>>>(p, num0, num1, dpart, o, dq_shift); \
-        else combine_seq_kernel<BF, ETA, false><<<blocks, 256, 0, stream>>>(p, num0, num1, dpart, o, dq_shift);     \
+        if (th32) combine_seq_kernel<BF, ETA, true><<<blocks, 256, 0, stream>>>(p, num0, num1, pden, o, dq_shift); \
+        else combine_seq_kernel<BF, ETA, false><<<blocks, 256, 0, stream>>>(p, num0, num1, pden, o, dq_shift);     \
     } while (0)
     if (p.bf16) {
         if (pden != nullptr) IDATTN_COMB(true, true);
