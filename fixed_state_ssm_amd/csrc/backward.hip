@@ -866,39 +866,35 @@ __global__ __launch_bounds__(256) void bwd_conv_kernel(Problem p, idattn_params 
             aq[e][j] = ak[e][j] = 0.f;
         }
     }
-    for (int64_t t = t0; t < t1; ++t) {
-        // every load of the token first (indices clamped, missing taps masked):
-        // g_c at t + W - 1 - e (tap e of the later tokens that read x(t)), the
-        // conv inputs x(t - W + 1 + e) that tap e of token t reads, g_c(t)
-        float gq[NT][DJ], gk[NT][DJ];
-        uint32_t xq_raw[NT][DJ], xk_raw[NT][DJ];
-        bool g_ok[NT], x_ok[NT];
-#pragma unroll
-        for (int e = 0; e < NT; ++e) {
-            const int64_t tt = t + W - 1 - e;
-            g_ok[e] = e < W && tt < N;
-            const int64_t gr = (row0 + max(min(tt, N - 1), int64_t{0})) * d;
-            const ConvRow r = conv_row(q, k, tail_in, b * N, t - (W - 1) + e, b * N + t, b, h, H, d, W, e < W);
-            x_ok[e] = r.ok;
-            const uint32_t fb = static_cast<uint32_t>(d) * 4u;
-            const __amdgpu_buffer_rsrc_t rgq = rsrc_at(g_cq + gr, fb), rgk = rsrc_at(g_ck + gr, fb);
-            const __amdgpu_buffer_rsrc_t rq = io_rsrc<BF16>(r.bq, r.rq, d), rk = io_rsrc<BF16>(r.bk, r.rk, d);
-#pragma unroll
-            for (int j = 0; j < DJ; ++j) {
-                gq[e][j] = buf_load(rgq, lf[j], 0);
-                gk[e][j] = buf_load(rgk, lf[j], 0);
-                xq_raw[e][j] = buf_load_raw<BF16>(rq, lb[j]);
-                xk_raw[e][j] = buf_load_raw<BF16>(rk, lb[j]);
-            }
-        }
-        float gq_t[DJ], gk_t[DJ];
-        const __amdgpu_buffer_rsrc_t rgq_t = rsrc_at(g_cq + (row0 + t) * d, static_cast<uint32_t>(d) * 4u);
-        const __amdgpu_buffer_rsrc_t rgk_t = rsrc_at(g_ck + (row0 + t) * d, static_cast<uint32_t>(d) * 4u);
+    // one row of g_cq, g_ck at sequence position tt (clamped), and the conv
+    // inputs of q, k at position pos (the tail before the sequence, a masked
+    // row where there is none)
+    auto load_g = [&](int64_t tt, float (&gq1)[DJ], float (&gk1)[DJ]) {
+        const int64_t gr = (row0 + max(min(tt, N - 1), int64_t{0})) * d;
+        const uint32_t fb = static_cast<uint32_t>(d) * 4u;
+        const __amdgpu_buffer_rsrc_t rgq = rsrc_at(g_cq + gr, fb), rgk = rsrc_at(g_ck + gr, fb);
 #pragma unroll
         for (int j = 0; j < DJ; ++j) {
-            gq_t[j] = buf_load(rgq_t, lf[j], 0);
-            gk_t[j] = buf_load(rgk_t, lf[j], 0);
+            gq1[j] = buf_load(rgq, lf[j], 0);
+            gk1[j] = buf_load(rgk, lf[j], 0);
         }
+    };
+    auto load_x = [&](int64_t pos, bool real, uint32_t (&xq1)[DJ], uint32_t (&xk1)[DJ]) -> bool {
+        const ConvRow r = conv_row(q, k, tail_in, b * N, pos, b * N + min(max(pos, int64_t{0}), N - 1), b, h, H, d,
+                                   W, real);
+        const __amdgpu_buffer_rsrc_t rq = io_rsrc<BF16>(r.bq, r.rq, d), rk = io_rsrc<BF16>(r.bk, r.rk, d);
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            xq1[j] = buf_load_raw<BF16>(rq, lb[j]);
+            xk1[j] = buf_load_raw<BF16>(rk, lb[j]);
+        }
+        return r.ok;
+    };
+    // token t's rows and the conv update of its outputs and of the weight sums:
+    //   g_x(t) = sum_e w[e] g_c(t + W - 1 - e),   g_w[e] += g_c(t) x(t - W + 1 + e)
+    auto token = [&](int64_t t, const float (&gq)[NT][DJ], const float (&gk)[NT][DJ], const bool (&g_ok)[NT],
+                     const uint32_t (&xq_raw)[NT][DJ], const uint32_t (&xk_raw)[NT][DJ], const bool (&x_ok)[NT],
+                     const float (&gq_t)[DJ], const float (&gk_t)[DJ]) {
 #pragma unroll
         for (int j = 0; j < DJ; ++j) {
             float sq = 0.f, sk = 0.f;
@@ -917,6 +913,72 @@ __global__ __launch_bounds__(256) void bwd_conv_kernel(Problem p, idattn_params 
                 store_io<BF16>(grad_q, o, sq);
                 store_io<BF16>(grad_k, o, sk);
             }
+        }
+    };
+    if constexpr (WT > 0) {
+        // W fixed: windows of W rows slide along the run, so each token loads
+        // one new row of g_c and of x (the next token's, ahead of its use):
+        // slot e of gw holds g_c(t + W - 1 - e), slot e of xw x(t - W + 1 + e)
+        float gqw[NT][DJ], gkw[NT][DJ];
+        uint32_t xqw[NT][DJ], xkw[NT][DJ];
+        bool g_ok[NT], x_ok[NT];
+#pragma unroll
+        for (int e = 0; e < NT; ++e) {
+            load_g(t0 + W - 1 - e, gqw[e], gkw[e]);
+            g_ok[e] = t0 + W - 1 - e < N;
+            x_ok[e] = load_x(t0 - (W - 1) + e, true, xqw[e], xkw[e]);
+        }
+        for (int64_t t = t0; t < t1; ++t) {
+            float gqn[DJ], gkn[DJ];
+            uint32_t xqn[DJ], xkn[DJ];
+            load_g(t + W, gqn, gkn);  // g_c(t + 1 + W - 1), clamped and masked past the end
+            // x(t + 1), clamped into the sequence (past its end it is never used)
+            const bool xn_ok = load_x(min(t + 1, N - 1), true, xqn, xkn);
+            token(t, gqw, gkw, g_ok, xqw, xkw, x_ok, gqw[W - 1], gkw[W - 1]);
+#pragma unroll
+            for (int e = NT - 1; e > 0; --e) {
+#pragma unroll
+                for (int j = 0; j < DJ; ++j) {
+                    gqw[e][j] = gqw[e - 1][j];
+                    gkw[e][j] = gkw[e - 1][j];
+                }
+                g_ok[e] = g_ok[e - 1];
+            }
+#pragma unroll
+            for (int e = 0; e + 1 < NT; ++e) {
+#pragma unroll
+                for (int j = 0; j < DJ; ++j) {
+                    xqw[e][j] = xqw[e + 1][j];
+                    xkw[e][j] = xkw[e + 1][j];
+                }
+                x_ok[e] = x_ok[e + 1];
+            }
+#pragma unroll
+            for (int j = 0; j < DJ; ++j) {
+                gqw[0][j] = gqn[j];
+                gkw[0][j] = gkn[j];
+                xqw[NT - 1][j] = xqn[j];
+                xkw[NT - 1][j] = xkn[j];
+            }
+            g_ok[0] = t + W < N;
+            x_ok[NT - 1] = xn_ok;
+        }
+    } else {
+        for (int64_t t = t0; t < t1; ++t) {
+            // every load of the token first (indices clamped, missing taps masked):
+            // g_c at t + W - 1 - e (tap e of the later tokens that read x(t)), the
+            // conv inputs x(t - W + 1 + e) that tap e of token t reads, g_c(t)
+            float gq[NT][DJ], gk[NT][DJ], gq_t[DJ], gk_t[DJ];
+            uint32_t xq_raw[NT][DJ], xk_raw[NT][DJ];
+            bool g_ok[NT], x_ok[NT];
+#pragma unroll
+            for (int e = 0; e < NT; ++e) {
+                load_g(t + W - 1 - e, gq[e], gk[e]);
+                g_ok[e] = e < W && t + W - 1 - e < N;
+                x_ok[e] = load_x(t - (W - 1) + e, e < W, xq_raw[e], xk_raw[e]);
+            }
+            load_g(t, gq_t, gk_t);
+            token(t, gq, gk, g_ok, xq_raw, xk_raw, x_ok, gq_t, gk_t);
         }
     }
     float* pp = part + wid * 2 * d * W;
