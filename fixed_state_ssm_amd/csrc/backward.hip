@@ -692,22 +692,51 @@ __global__ __launch_bounds__(256) void bwd_feature_kernel(Problem p, idattn_para
     (void)bk;
     (void)bv;
     const float inv_d = 1.f / static_cast<float>(d);
+    // the conv inputs of q, k at sequence position pos (the tail before the
+    // sequence, a masked row where there is none), as loaded
+    auto load_x = [&](int64_t pos, bool real, uint32_t (&xq1)[DJ], uint32_t (&xk1)[DJ]) -> bool {
+        const ConvRow r = conv_row(q, k, tail_in, b * N, pos, b * N + min(max(pos, int64_t{0}), N - 1), b, h, H, d,
+                                   W, real);
+        const __amdgpu_buffer_rsrc_t rq = io_rsrc<BF16>(r.bq, r.rq, d), rk = io_rsrc<BF16>(r.bk, r.rk, d);
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            xq1[j] = buf_load_raw<BF16>(rq, lb[j]);
+            xk1[j] = buf_load_raw<BF16>(rk, lb[j]);
+        }
+        return r.ok;
+    };
+    // W fixed: a window of the W conv inputs of the current token slides along
+    // the run (slot e holds x(t - W + 1 + e)), so each token loads one new row
+    uint32_t xqw[NT][DJ], xkw[NT][DJ];
+    bool okw[NT];
+    if constexpr (WT > 0) {
+#pragma unroll
+        for (int e = 0; e < NT; ++e) okw[e] = load_x(t0 - (W - 1) + e, true, xqw[e], xkw[e]);
+    }
     for (int64_t t = t0; t < t1; ++t) {
         // every load of the token first (channels clamped below d, missing rows
         // masked): the conv taps of q and k, v, and the scans' gradients, each
         // row a buffer resource at a uniform base
         uint32_t xq_raw[NT][DJ], xk_raw[NT][DJ], v_raw[DJ];
         bool tap_ok[NT];
+        uint32_t xqn[DJ], xkn[DJ];
+        bool okn = false;
+        if constexpr (WT > 0) {
 #pragma unroll
-        for (int j2 = 0; j2 < NT; ++j2) {
-            const ConvRow r = conv_row(q, k, tail_in, b * N, t - (W - 1) + j2, b * N + t, b, h, H, d, W, j2 < W);
-            tap_ok[j2] = r.ok;
-            const __amdgpu_buffer_rsrc_t rq = io_rsrc<BF16>(r.bq, r.rq, d), rk = io_rsrc<BF16>(r.bk, r.rk, d);
+            for (int e = 0; e < NT; ++e) {
+                tap_ok[e] = okw[e];
 #pragma unroll
-            for (int j = 0; j < DJ; ++j) {
-                xq_raw[j2][j] = buf_load_raw<BF16>(rq, lb[j]);
-                xk_raw[j2][j] = buf_load_raw<BF16>(rk, lb[j]);
+                for (int j = 0; j < DJ; ++j) {
+                    xq_raw[e][j] = xqw[e][j];
+                    xk_raw[e][j] = xkw[e][j];
+                }
             }
+            // the next token's newest tap, x(t + 1), clamped into the sequence
+            // (past its end it is never used)
+            okn = load_x(min(t + 1, N - 1), true, xqn, xkn);
+        } else {
+#pragma unroll
+            for (int j2 = 0; j2 < NT; ++j2) tap_ok[j2] = load_x(t - (W - 1) + j2, j2 < W, xq_raw[j2], xk_raw[j2]);
         }
         const __amdgpu_buffer_rsrc_t vrow = io_rsrc<BF16>(v, ((b * N + t) * H + h) * d, d);
         const int64_t o = (row0 + t) * d;
@@ -813,6 +842,23 @@ __global__ __launch_bounds__(256) void bwd_feature_kernel(Problem p, idattn_para
                 const float gyk = gxk[j] * iDk - fk * yk[j];
                 g_xi[(row0 + t) * d + c] = gyq * sq[j] * (1.f + cq[j] * (1.f - sq[j]));
                 g_zk[(row0 + t) * d + c] = gyk * sk[j] * (1.f + ck[j] * (1.f - sk[j]));
+            }
+        }
+        if constexpr (WT > 0) {  // slide the window by one token
+#pragma unroll
+            for (int e = 0; e + 1 < NT; ++e) {
+                okw[e] = okw[e + 1];
+#pragma unroll
+                for (int j = 0; j < DJ; ++j) {
+                    xqw[e][j] = xqw[e + 1][j];
+                    xkw[e][j] = xkw[e + 1][j];
+                }
+            }
+            okw[NT - 1] = okn;
+#pragma unroll
+            for (int j = 0; j < DJ; ++j) {
+                xqw[NT - 1][j] = xqn[j];
+                xkw[NT - 1][j] = xkn[j];
             }
         }
     }
