@@ -187,6 +187,24 @@ def measure_copy_gbps(torch, nbytes=2 << 30):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def measure_inplace_gbps(torch, nbytes=1090519040):
+    """Read + write rate of a plain in-place elementwise pass (torch's mul_)
+    over a buffer the size of the decode workload's state: the streaming
+    rate that a kernel updating its state in place can hope for."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    a.mul_(1.0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        a.mul_(1.0)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    del a
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def decode_bench(torch, fs, steps, warmup):
     """Decode workload: 256 sequences x 16 heads, d = R = 128, M = 64, prefilled
     by a 2048-token forward on N(0,1) inputs drawn on the device, then one
@@ -590,6 +608,7 @@ def main():
     out["measured_copy_gbps"] = measure_copy_gbps(torch)
     if not args.no_decode:
         out["decode"] = decode_bench(torch, fs, steps=20, warmup=20)
+        out["decode"]["measured_inplace_stream_gbps"] = measure_inplace_gbps(torch)
         out["varlen"] = varlen_bench(torch, fs, WL, mean_launch_ms if args.config == "1p3b" else None)
         out["normalized"] = normalized_bench(torch, fs, WL, args.config, mean_launch_ms)
         out["rff"] = rff_bench(torch, fs, WL, args.config, mean_launch_ms)
