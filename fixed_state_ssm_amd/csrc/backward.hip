@@ -57,8 +57,9 @@ __device__ __forceinline__ Zoh zoh_of(const idattn_params& prm, int64_t h, int64
 
 // One batch of the key-side recurrence: V(i) = abar V(i-1) + U(i-1), then
 // U(i) = abar U(i-1) + bbar z_k(i); the lane's shares of s = xi_q . U and
-// s_a = xi_q . V per token.
-template <int RJ, bool RAGGED>
+// s_a = xi_q . V per token.  SCALED: the lane carries U / bbar and V / bbar,
+// which take the input unscaled.
+template <int RJ, bool RAGGED, bool SCALED>
 __device__ __forceinline__ void key_batch(int nt, float (&ur)[RJ], float (&ui)[RJ], float (&vr)[RJ], float (&vi)[RJ],
                                           const float (&xv)[kTok][RJ], const float (&zv)[kTok][RJ], float ar, float ai,
                                           float br, float bi, float (&spr)[kTok], float (&spi)[kTok],
@@ -71,8 +72,8 @@ __device__ __forceinline__ void key_batch(int nt, float (&ur)[RJ], float (&ui)[R
             for (int j = 0; j < RJ; ++j) {
                 const float nvr = fmaf(ar, vr[j], fmaf(-ai, vi[j], ur[j]));
                 const float nvi = fmaf(ar, vi[j], fmaf(ai, vr[j], ui[j]));
-                const float nur = fmaf(ar, ur[j], fmaf(-ai, ui[j], br * zv[t][j]));
-                const float nui = fmaf(ar, ui[j], fmaf(ai, ur[j], bi * zv[t][j]));
+                const float nur = fmaf(ar, ur[j], fmaf(-ai, ui[j], SCALED ? zv[t][j] : br * zv[t][j]));
+                const float nui = SCALED ? fmaf(ar, ui[j], ai * ur[j]) : fmaf(ar, ui[j], fmaf(ai, ur[j], bi * zv[t][j]));
                 vr[j] = nvr;
                 vi[j] = nvi;
                 ur[j] = nur;
@@ -93,7 +94,9 @@ __device__ __forceinline__ void key_batch(int nt, float (&ur)[RJ], float (&ui)[R
 // One batch of the value-side recurrence: W(i) = abar W(i-1) + Gamma(i-1),
 // then Gamma(i) = abar Gamma(i-1) + bbar z_v(i); the lane's shares of
 // g_s = sum_c g_o[c] conj(Gamma_c) and gw = sum_c g_o[c] conj(W_c) per token.
-template <int RJ, bool RAGGED>
+// SCALED: the lane carries Gamma / bbar and W / bbar, which take the input
+// unscaled.
+template <int RJ, bool RAGGED, bool SCALED>
 __device__ __forceinline__ void value_batch(int nt, float (&gmr)[RJ], float (&gmi)[RJ], float (&wr)[RJ],
                                             float (&wi)[RJ], const float (&zz)[kTok][RJ], const float (&go)[kTok][RJ],
                                             float ar, float ai, float br, float bi, float (&spr)[kTok],
@@ -106,8 +109,8 @@ __device__ __forceinline__ void value_batch(int nt, float (&gmr)[RJ], float (&gm
             for (int j = 0; j < RJ; ++j) {
                 const float nwr = fmaf(ar, wr[j], fmaf(-ai, wi[j], gmr[j]));
                 const float nwi = fmaf(ar, wi[j], fmaf(ai, wr[j], gmi[j]));
-                const float ngr = fmaf(ar, gmr[j], fmaf(-ai, gmi[j], br * zz[t][j]));
-                const float ngi = fmaf(ar, gmi[j], fmaf(ai, gmr[j], bi * zz[t][j]));
+                const float ngr = fmaf(ar, gmr[j], fmaf(-ai, gmi[j], SCALED ? zz[t][j] : br * zz[t][j]));
+                const float ngi = SCALED ? fmaf(ar, gmi[j], ai * gmr[j]) : fmaf(ar, gmi[j], fmaf(ai, gmr[j], bi * zz[t][j]));
                 wr[j] = nwr;
                 wi[j] = nwi;
                 gmr[j] = ngr;
@@ -128,7 +131,9 @@ __device__ __forceinline__ void value_batch(int nt, float (&gmr)[RJ], float (&gm
 // Key side: U and V = dU/dabar; writes s = xi_q . U and s_a = xi_q . V
 // [H][T][M] and, when the state_out gradient is given, the mode's share
 // sum_r g_S,U[r] conj(V_r(N-1)) of g_abar to ga_key [B H][M].
-template <int RJ>
+// SCALED (no state enters): U and V are carried divided by bbar, which then
+// multiplies each token's reduced s and s_a and the state-gradient sum.
+template <int RJ, bool SCALED>
 __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_params prm, const float* __restrict__ xi_q,
                                                            const float* __restrict__ z_k, const float* state_in,
                                                            const float* grad_state, float2* __restrict__ s,
@@ -183,18 +188,25 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
         // per quantity (lane t < 8 of a half ends with token slot8(t)'s totals)
         float spr[kTok], spi[kTok], sqr[kTok], sqi[kTok];
         if (nt == kTok && dfull) {
-            key_batch<RJ, false>(nt, ur, ui, vr, vi, x, zq, ar, ai, br, bi, spr, spi, sqr, sqi);
+            key_batch<RJ, false, SCALED>(nt, ur, ui, vr, vi, x, zq, ar, ai, br, bi, spr, spi, sqr, sqi);
         } else {
 #pragma unroll
             for (int t = 0; t < kTok; ++t)
 #pragma unroll
                 for (int j = 0; j < RJ; ++j)
                     if (t >= nt || RJ * li + j >= d) x[t][j] = zq[t][j] = 0.f;
-            key_batch<RJ, true>(nt, ur, ui, vr, vi, x, zq, ar, ai, br, bi, spr, spi, sqr, sqi);
+            key_batch<RJ, true, SCALED>(nt, ur, ui, vr, vi, x, zq, ar, ai, br, bi, spr, spi, sqr, sqi);
         }
         static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
-        const float tpr = half_reduce_scatter8(spr, lane), tpi = half_reduce_scatter8(spi, lane);
-        const float tqr = half_reduce_scatter8(sqr, lane), tqi = half_reduce_scatter8(sqi, lane);
+        float tpr = half_reduce_scatter8(spr, lane), tpi = half_reduce_scatter8(spi, lane);
+        float tqr = half_reduce_scatter8(sqr, lane), tqi = half_reduce_scatter8(sqi, lane);
+        if constexpr (SCALED) {  // times bbar
+            const float a = br * tpr - bi * tpi, c = br * tqr - bi * tqi;
+            tpi = fmaf(br, tpi, bi * tpr);
+            tqi = fmaf(br, tqi, bi * tqr);
+            tpr = a;
+            tqr = c;
+        }
         const int t = slot8(li);
         if (li < kTok && t < nt && mok) {
             s[(row0 + i0 + t) * M + m] = make_float2(tpr, tpi);
@@ -221,6 +233,11 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
         }
         gr = half_total(gr);
         gi = half_total(gi);
+        if constexpr (SCALED) {  // times conj(bbar)
+            const float a = fmaf(br, gr, bi * gi);
+            gi = br * gi - bi * gr;
+            gr = a;
+        }
         if (li == 0 && mok) ga_key[bh * M + m] = make_float2(gr, gi);
     }
 }
@@ -229,8 +246,10 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
 // g_s = sum_c g_o[c] conj(Gamma_c) (to gs [H][T][M]) and
 // gw = sum_c g_o[c] conj(W_c); the mode's g_abar partial
 // sum_i [conj(s) gw + g_s conj(s_a)] plus the state_out terms goes to
-// ga [B H][M].
-template <int RJ, bool BF16>
+// ga [B H][M].  SCALED (no state enters): Gamma and W are carried divided by
+// bbar, and conj(bbar) multiplies each token's reduced g_s and gw and the
+// state-gradient sum.
+template <int RJ, bool BF16, bool SCALED>
 __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_params prm, const float* __restrict__ z_v,
                                                              const void* __restrict__ grad_o, const float* state_in,
                                                              const float* grad_state, const float2* __restrict__ s,
@@ -287,18 +306,25 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
         // per quantity (lane t < 8 ends with token slot8(t)'s totals)
         float spr[kTok], spi[kTok], sqr[kTok], sqi[kTok];
         if (nt == kTok && dfull) {
-            value_batch<RJ, false>(nt, gmr, gmi, wr, wi, zz, go, ar, ai, br, bi, spr, spi, sqr, sqi);
+            value_batch<RJ, false, SCALED>(nt, gmr, gmi, wr, wi, zz, go, ar, ai, br, bi, spr, spi, sqr, sqi);
         } else {
 #pragma unroll
             for (int t = 0; t < kTok; ++t)
 #pragma unroll
                 for (int j = 0; j < RJ; ++j)
                     if (t >= nt || RJ * li + j >= d) zz[t][j] = go[t][j] = 0.f;
-            value_batch<RJ, true>(nt, gmr, gmi, wr, wi, zz, go, ar, ai, br, bi, spr, spi, sqr, sqi);
+            value_batch<RJ, true, SCALED>(nt, gmr, gmi, wr, wi, zz, go, ar, ai, br, bi, spr, spi, sqr, sqi);
         }
         static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
-        const float pr = half_reduce_scatter8(spr, lane), pi = half_reduce_scatter8(spi, lane);
-        const float qr = half_reduce_scatter8(sqr, lane), qi = half_reduce_scatter8(sqi, lane);
+        float pr = half_reduce_scatter8(spr, lane), pi = half_reduce_scatter8(spi, lane);
+        float qr = half_reduce_scatter8(sqr, lane), qi = half_reduce_scatter8(sqi, lane);
+        if constexpr (SCALED) {  // times conj(bbar)
+            const float a = fmaf(br, pr, bi * pi), c = fmaf(br, qr, bi * qi);
+            pi = br * pi - bi * pr;
+            qi = br * qi - bi * qr;
+            pr = a;
+            qr = c;
+        }
         if (li < kTok && ts < nt && mok) {
             gs[sidx] = make_float2(pr, pi);
             // conj(s) gw + g_s conj(s_a), summed per lane (every eighth token) in fp64
@@ -325,6 +351,11 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
         }
         gr = half_total(gr);
         gi = half_total(gi);
+        if constexpr (SCALED) {  // times conj(bbar)
+            const float a = fmaf(br, gr, bi * gi);
+            gi = br * gi - bi * gr;
+            gr = a;
+        }
         if (li == 0) {
             const float2 k = ga_key[bh * M + m];
             accr += static_cast<double>(gr) + k.x;
@@ -1241,16 +1272,30 @@ hipError_t launch_backward(const Problem& p, const idattn_params& prm, const voi
     if (e != hipSuccess) return e;
     // the per-mode scans: two modes per wave (one per half), four waves per block
     const dim3 gm(static_cast<unsigned>(bh), static_cast<unsigned>((p.M + 7) / 8));
-    if (p.d > 64)
-        bwd_key_scan_kernel<4><<<gm, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, grad_state, s, s_a, ga_key);
-    else if (p.d > 32)
-        bwd_key_scan_kernel<2><<<gm, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, grad_state, s, s_a, ga_key);
-    else
-        bwd_key_scan_kernel<1><<<gm, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, grad_state, s, s_a, ga_key);
+    // without a state entering, the per-mode scans carry their states divided by bbar
+#define IDATTN_BK(RJ)                                                                                              \
+    do {                                                                                                           \
+        if (state_in == nullptr)                                                                                   \
+            bwd_key_scan_kernel<RJ, true><<<gm, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, grad_state, s, s_a, \
+                                                                  ga_key);                                         \
+        else                                                                                                       \
+            bwd_key_scan_kernel<RJ, false><<<gm, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, grad_state, s, s_a, \
+                                                                   ga_key);                                        \
+    } while (0)
+    if (p.d > 64) IDATTN_BK(4);
+    else if (p.d > 32) IDATTN_BK(2);
+    else IDATTN_BK(1);
+#undef IDATTN_BK
     if ((e = hipGetLastError()) != hipSuccess) return e;
-#define IDATTN_BV(RJ, BF)                                                                                         \
-    bwd_value_scan_kernel<RJ, BF><<<gm, 256, 0, stream>>>(p, prm, z_v, grad_o, state_in, grad_state, s, s_a, ga_key, \
-                                                          gs, ga)
+#define IDATTN_BV(RJ, BF)                                                                                      \
+    do {                                                                                                       \
+        if (state_in == nullptr)                                                                               \
+            bwd_value_scan_kernel<RJ, BF, true><<<gm, 256, 0, stream>>>(p, prm, z_v, grad_o, state_in, grad_state, \
+                                                                        s, s_a, ga_key, gs, ga);               \
+        else                                                                                                   \
+            bwd_value_scan_kernel<RJ, BF, false><<<gm, 256, 0, stream>>>(p, prm, z_v, grad_o, state_in,            \
+                                                                         grad_state, s, s_a, ga_key, gs, ga);  \
+    } while (0)
     if (p.d > 64) {
         if (p.bf16) IDATTN_BV(4, true);
         else IDATTN_BV(4, false);
