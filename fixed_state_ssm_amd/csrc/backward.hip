@@ -460,8 +460,10 @@ __device__ __forceinline__ void reduce_block(const float (*red)[kBlk][kWave], in
 // state_in; the result goes to g_xi [H][T][d].
 // One block of kBlk tokens of the xi scan for the wave's MW modes: U steps
 // forward and the wave's share sum_m Re(g_s conj(U_m)) of each token goes to
-// red.  A ragged block steps only its first nt tokens.
-template <int MW, bool RAGGED>
+// red.  A ragged block steps only its first nt tokens.  SCALED: the lane
+// carries U / bbar, which takes the input unscaled, and the staged g_s carry
+// the factor conj(bbar) instead.
+template <int MW, bool RAGGED, bool SCALED>
 __device__ __forceinline__ void xi_block(int nt, const float2* g_row, const float* z_col, float (*red_t)[kWave],
                                          int lane, const float (&ar)[MW], const float (&ai)[MW],
                                          const float (&br)[MW], const float (&bi)[MW], float (&ur)[MW],
@@ -474,8 +476,9 @@ __device__ __forceinline__ void xi_block(int nt, const float2* g_row, const floa
 #pragma unroll
         for (int mm = 0; mm < MW; ++mm) {
             const float2 g = g_row[t * M + mm];
-            const float nr = fmaf(ar[mm], ur[mm], fmaf(-ai[mm], ui[mm], br[mm] * zz));
-            const float ni = fmaf(ar[mm], ui[mm], fmaf(ai[mm], ur[mm], bi[mm] * zz));
+            const float nr = fmaf(ar[mm], ur[mm], fmaf(-ai[mm], ui[mm], SCALED ? zz : br[mm] * zz));
+            const float ni = SCALED ? fmaf(ar[mm], ui[mm], ai[mm] * ur[mm])
+                                    : fmaf(ar[mm], ui[mm], fmaf(ai[mm], ur[mm], bi[mm] * zz));
             ur[mm] = nr;
             ui[mm] = ni;
             acc = fmaf(g.x, nr, fmaf(g.y, ni, acc));  // Re(g conj(U))
@@ -484,7 +487,9 @@ __device__ __forceinline__ void xi_block(int nt, const float2* g_row, const floa
     }
 }
 
-template <int MW>
+// SCALED (no state enters): U is carried as U / bbar and each staged g_s
+// element is multiplied by conj(bbar) of its mode.
+template <int MW, bool SCALED>
 __global__ __launch_bounds__(kStage) void bwd_xi_scan_kernel(Problem p, idattn_params prm,
                                                              const float* __restrict__ z_k, const float* state_in,
                                                              const float2* __restrict__ gs,
@@ -492,6 +497,7 @@ __global__ __launch_bounds__(kStage) void bwd_xi_scan_kernel(Problem p, idattn_p
     __shared__ float2 w_blk[kStage];
     __shared__ float z_blk[kStage];
     __shared__ float red[kVW][kBlk][kWave];
+    __shared__ float2 cb_s[SCALED ? 64 : 1];  // conj(bbar) of every mode (M <= 64)
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x >> 6;
     const int64_t bh = blockIdx.x;
@@ -521,20 +527,31 @@ __global__ __launch_bounds__(kStage) void bwd_xi_scan_kernel(Problem p, idattn_p
             ui[mm] = state_in[idx + 1];
         }
     }
+    float2 cbe = make_float2(1.f, 0.f);  // conj(bbar) of the mode this thread stages
+    if constexpr (SCALED) {
+        if (threadIdx.x < M) {
+            const Zoh zm = zoh_of(prm, h, M, threadIdx.x);
+            cb_s[threadIdx.x] = make_float2(static_cast<float>(zm.br), -static_cast<float>(zm.bi));
+        }
+        __syncthreads();
+        cbe = cb_s[threadIdx.x % M];
+    }
     const float2* g_row = w_blk + moff + w * MW;
     int64_t i0 = 0;
     int nt = static_cast<int>(min(N, static_cast<int64_t>(kBlk)));
     Stage nx = stage_fetch<false, false, false>(p, b, h, row0, i0, nt, group, gs, nullptr, z_k);
     while (i0 < N) {
+        if constexpr (SCALED)
+            nx.w = make_float2(nx.w.x * cbe.x - nx.w.y * cbe.y, fmaf(nx.w.x, cbe.y, nx.w.y * cbe.x));
         stage_store<false, false>(nx, nt, M, group, d, w_blk, nullptr, z_blk);
         __syncthreads();
         const int64_t j0 = i0 + kBlk;  // the next block, loaded while this one runs
         const int jnt = static_cast<int>(min(N - j0, static_cast<int64_t>(kBlk)));
         if (j0 < N) nx = stage_fetch<false, false, false>(p, b, h, row0, j0, jnt, group, gs, nullptr, z_k);
         if (nt == kBlk)
-            xi_block<MW, false>(nt, g_row, z_blk + lane, red[w], lane, ar, ai, br, bi, ur, ui, M);
+            xi_block<MW, false, SCALED>(nt, g_row, z_blk + lane, red[w], lane, ar, ai, br, bi, ur, ui, M);
         else
-            xi_block<MW, true>(nt, g_row, z_blk + lane, red[w], lane, ar, ai, br, bi, ur, ui, M);
+            xi_block<MW, true, SCALED>(nt, g_row, z_blk + lane, red[w], lane, ar, ai, br, bi, ur, ui, M);
         __syncthreads();
         reduce_block(red, nt, group, d, g_xi + (row0 + i0) * d);
         i0 = j0;
@@ -1309,7 +1326,13 @@ hipError_t launch_backward(const Problem& p, const idattn_params& prm, const voi
 #undef IDATTN_BV
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 gc(static_cast<unsigned>(bh), static_cast<unsigned>(groups), static_cast<unsigned>(splits));
-#define IDATTN_BX(MW) bwd_xi_scan_kernel<MW><<<gc, kVW * 64, 0, stream>>>(p, prm, z_k, state_in, gs, g_xi, zs)
+#define IDATTN_BX(MW)                                                                                     \
+    do {                                                                                                  \
+        if (state_in == nullptr)                                                                          \
+            bwd_xi_scan_kernel<MW, true><<<gc, kVW * 64, 0, stream>>>(p, prm, z_k, state_in, gs, g_xi, zs);  \
+        else                                                                                              \
+            bwd_xi_scan_kernel<MW, false><<<gc, kVW * 64, 0, stream>>>(p, prm, z_k, state_in, gs, g_xi, zs); \
+    } while (0)
 #define IDATTN_BA(MW)                                                                                          \
     do {                                                                                                       \
         bwd_adjoint_kernel<MW, false, false, false><<<gc, kVW * 64, 0, stream>>>(p, prm, xi_q, gs, z_k, grad_state, \
