@@ -43,11 +43,9 @@ __device__ __forceinline__ Zoh zoh_of(const idattn_params& prm, int64_t h, int64
 
 // ------------------------------------------------------------------ per-mode scans
 // One half-wave per (b, h, m), two modes per wave, so that each reduction
-// over the channels runs over 32 lanes and serves both modes at once.  In the
-// key scan lane l of a half owns channels l + 32 j (RJ of them); in the value
-// scan the RJ adjacent channels RJ l .. RJ l + RJ - 1, so that a token's bf16
-// g_o values are one load (measured: adjacent fp32 channels made the key
-// scans slower, adjacent bf16 ones made the value scan faster).
+// over the channels runs over 32 lanes and serves both modes at once.  Lane l
+// of a half owns the RJ adjacent channels RJ l .. RJ l + RJ - 1, so that a
+// token's values of them are one load.
 //
 // Each scan takes kTok tokens at a time.  All their loads are issued first,
 // at token and channel indices clamped into range (addressed from a uniform
@@ -132,12 +130,15 @@ __device__ __forceinline__ void value_batch(int nt, float (&gmr)[RJ], float (&gm
 // [H][T][M] and, when the state_out gradient is given, the mode's share
 // sum_r g_S,U[r] conj(V_r(N-1)) of g_abar to ga_key [B H][M].
 // SCALED (no state enters): U and V are carried divided by bbar, which then
-// multiplies each token's reduced s and s_a and the state-gradient sum.
+// multiplies each token's reduced s and s_a and the state-gradient sum; the
+// key side's state_out share of the g_bbar sum, sum_r g_S,U[r] conj(U_r(N-1)
+// / bbar), goes to gb_key [B H][M] (zero without a state_out gradient).
 template <int RJ, bool SCALED>
 __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_params prm, const float* __restrict__ xi_q,
                                                            const float* __restrict__ z_k, const float* state_in,
                                                            const float* grad_state, float2* __restrict__ s,
-                                                           float2* __restrict__ s_a, float2* __restrict__ ga_key) {
+                                                           float2* __restrict__ s_a, float2* __restrict__ ga_key,
+                                                           float2* __restrict__ gb_key) {
     const int lane = threadIdx.x & (kWave - 1);
     const int li = lane & 31;  // the lane in its half
     const int64_t bh = blockIdx.x;
@@ -220,6 +221,7 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
         if (i0 + kTok >= N) break;
         step(i0 + kTok, xb, zb, xa, za);
     }
+    float ur_ = 0.f, ui_ = 0.f;  // SCALED: sum_r g_S[r] conj(U_r / bbar)
     if (grad_state != nullptr) {
         float gr = 0.f, gi = 0.f;  // sum_r g_S[r] conj(V_r)
 #pragma unroll
@@ -229,6 +231,10 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
                 const float sr = grad_state[st_row + 2 * r], si = grad_state[st_row + 2 * r + 1];
                 gr = fmaf(sr, vr[j], fmaf(si, vi[j], gr));
                 gi = fmaf(si, vr[j], fmaf(-sr, vi[j], gi));
+                if constexpr (SCALED) {
+                    ur_ = fmaf(sr, ur[j], fmaf(si, ui[j], ur_));
+                    ui_ = fmaf(si, ur[j], fmaf(-sr, ui[j], ui_));
+                }
             }
         }
         gr = half_total(gr);
@@ -237,9 +243,13 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
             const float a = fmaf(br, gr, bi * gi);
             gi = br * gi - bi * gr;
             gr = a;
+            ur_ = half_total(ur_);
+            ui_ = half_total(ui_);
         }
         if (li == 0 && mok) ga_key[bh * M + m] = make_float2(gr, gi);
     }
+    if constexpr (SCALED)
+        if (li == 0 && mok) gb_key[bh * M + m] = make_float2(ur_, ui_);
 }
 
 // Value side: Gamma and W = dGamma/dabar, driven by z_v; per token
@@ -248,14 +258,20 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
 // sum_i [conj(s) gw + g_s conj(s_a)] plus the state_out terms goes to
 // ga [B H][M].  SCALED (no state enters): Gamma and W are carried divided by
 // bbar, and conj(bbar) multiplies each token's reduced g_s and gw and the
-// state-gradient sum.
+// state-gradient sum.  Then the g_bbar sums of both adjoints also follow from
+// per-token totals: with G = sum_c g_o[c] conj(Gamma_c / bbar) (g_s before
+// its conj(bbar)), each adjoint's sum_i sum_c A(i)_c z(i)_c is
+// sum_i G(i) conj(s(i)) plus its state_out share; the value scan writes
+// 2 sum_i G conj(s) + sum_c g_S,Gamma[c] conj(Gamma_c(N-1) / bbar) to
+// gb_val [B H][M] and the key scan its own share to gb_key.
 template <int RJ, bool BF16, bool SCALED>
 __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_params prm, const float* __restrict__ z_v,
                                                              const void* __restrict__ grad_o, const float* state_in,
                                                              const float* grad_state, const float2* __restrict__ s,
                                                              const float2* __restrict__ s_a,
                                                              const float2* __restrict__ ga_key,
-                                                             float2* __restrict__ gs, float2* __restrict__ ga) {
+                                                             float2* __restrict__ gs, float2* __restrict__ ga,
+                                                             float2* __restrict__ gb_val) {
     const int lane = threadIdx.x & (kWave - 1);
     const int li = lane & 31;  // the lane in its half
     const int64_t bh = blockIdx.x;
@@ -283,6 +299,7 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
     const int64_t row0 = h * p.T + b * N;
     const float* zvp = z_v + row0 * d;
     double accr = 0.0, acci = 0.0;  // g_abar share of this mode
+    double bcr = 0.0, bci = 0.0;    // SCALED: sum_i G conj(s)
     const bool dfull = d == 32 * RJ;
     const int ts = slot8(li);  // the token whose totals this lane ends with
     const uint32_t coff = static_cast<uint32_t>(min(RJ * li, d - RJ));  // the lane's first channel (clamped)
@@ -318,6 +335,7 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
         static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
         float pr = half_reduce_scatter8(spr, lane), pi = half_reduce_scatter8(spi, lane);
         float qr = half_reduce_scatter8(sqr, lane), qi = half_reduce_scatter8(sqi, lane);
+        const float g0r = pr, g0i = pi;  // G before its conj(bbar)
         if constexpr (SCALED) {  // times conj(bbar)
             const float a = fmaf(br, pr, bi * pi), c = fmaf(br, qr, bi * qi);
             pi = br * pi - bi * pr;
@@ -327,6 +345,10 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
         }
         if (li < kTok && ts < nt && mok) {
             gs[sidx] = make_float2(pr, pi);
+            if constexpr (SCALED) {  // G conj(s)
+                bcr += static_cast<double>(g0r) * sv.x + static_cast<double>(g0i) * sv.y;
+                bci += static_cast<double>(g0i) * sv.x - static_cast<double>(g0r) * sv.y;
+            }
             // conj(s) gw + g_s conj(s_a), summed per lane (every eighth token) in fp64
             accr += static_cast<double>(sv.x * qr + sv.y * qi) + static_cast<double>(pr * sa.x + pi * sa.y);
             acci += static_cast<double>(sv.x * qi - sv.y * qr) + static_cast<double>(pi * sa.x - pr * sa.y);
@@ -337,9 +359,16 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
     for (int off = 4; off >= 1; off >>= 1) {
         accr += __shfl_xor(accr, off, kWave);
         acci += __shfl_xor(acci, off, kWave);
+        if constexpr (SCALED) {
+            bcr += __shfl_xor(bcr, off, kWave);
+            bci += __shfl_xor(bci, off, kWave);
+        }
     }
+    bcr *= 2.0;  // the key and the value adjoint
+    bci *= 2.0;
     if (grad_state != nullptr) {
         float gr = 0.f, gi = 0.f;  // sum_c g_S[c] conj(W_c)
+        float tr = 0.f, ti = 0.f;  // SCALED: sum_c g_S[c] conj(Gamma_c / bbar)
 #pragma unroll
         for (int j = 0; j < RJ; ++j) {
             const int c = RJ * li + j;
@@ -347,6 +376,10 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
                 const float sr = grad_state[st_row + 2 * (d + c)], si = grad_state[st_row + 2 * (d + c) + 1];
                 gr = fmaf(sr, wr[j], fmaf(si, wi[j], gr));
                 gi = fmaf(si, wr[j], fmaf(-sr, wi[j], gi));
+                if constexpr (SCALED) {
+                    tr = fmaf(sr, gmr[j], fmaf(si, gmi[j], tr));
+                    ti = fmaf(si, gmr[j], fmaf(-sr, gmi[j], ti));
+                }
             }
         }
         gr = half_total(gr);
@@ -355,6 +388,10 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
             const float a = fmaf(br, gr, bi * gi);
             gi = br * gi - bi * gr;
             gr = a;
+            tr = half_total(tr);
+            ti = half_total(ti);
+            bcr += tr;
+            bci += ti;
         }
         if (li == 0) {
             const float2 k = ga_key[bh * M + m];
@@ -362,7 +399,10 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
             acci += static_cast<double>(gi) + k.y;
         }
     }
-    if (li == 0 && mok) ga[bh * M + m] = make_float2(static_cast<float>(accr), static_cast<float>(acci));
+    if (li == 0 && mok) {
+        ga[bh * M + m] = make_float2(static_cast<float>(accr), static_cast<float>(acci));
+        if constexpr (SCALED) gb_val[bh * M + m] = make_float2(static_cast<float>(bcr), static_cast<float>(bci));
+    }
 }
 
 // Sum of x[0..K) in a fixed pairwise order (deterministic).
@@ -563,6 +603,7 @@ __global__ __launch_bounds__(kStage) void bwd_xi_scan_kernel(Problem p, idattn_p
 //   A_m(i) = x(i) w_m(i) + conj(abar_m) A_m(i+1),   A_m(N-1) = x w + g_S,
 //   y(i) = Re sum_m conj(bbar_m) A_m(i)           -> g_z [H][T][d]
 //   g_bbar_m partial = sum_i sum_c A_m,c(i) z(i)_c  -> gb [B H][channel groups][M]
+//     (only when a state enters: else the per-mode scans form it)
 //   g_state_in = conj(abar) A(0)                    (columns off .. off + d - 1)
 // Key side: x = xi_q, w = g_s, z = z_k, off = 0.  Value side: x = g_o (io
 // dtype, [B][N][H][d]), w = conj(s), z = z_v, off = d.
@@ -570,8 +611,9 @@ __global__ __launch_bounds__(kStage) void bwd_xi_scan_kernel(Problem p, idattn_p
 // reverse token order: the adjoint A = x g + carry, the wave's share
 // sum_m Re(conj(bbar_m) A_m) of each token to red, the g_bbar sums, and the
 // carry conj(abar) A into the previous token.  A ragged block steps only its
-// first nt tokens.
-template <int MW, bool CONJ_W, bool RAGGED>
+// first nt tokens.  GB: whether it forms the g_bbar sums (without a state
+// entering the per-mode scans form them from per-token totals instead).
+template <int MW, bool CONJ_W, bool RAGGED, bool GB>
 __device__ __forceinline__ void adjoint_block(int nt, const float2* g_row, const float* x_col, const float* z_col,
                                               float (*red_t)[kWave], int lane, const float (&ar)[MW],
                                               const float (&ai)[MW], const float (&br)[MW], const float (&bi)[MW],
@@ -589,8 +631,10 @@ __device__ __forceinline__ void adjoint_block(int nt, const float2* g_row, const
             const float nr = fmaf(xx, g.x, cr[mm]);
             const float ni = fmaf(xx, g.y, ci[mm]);
             acc = fmaf(br[mm], nr, fmaf(bi[mm], ni, acc));  // Re(conj(bbar) A)
-            gbr[mm] = fmaf(nr, zz, gbr[mm]);
-            gbi[mm] = fmaf(ni, zz, gbi[mm]);
+            if constexpr (GB) {
+                gbr[mm] = fmaf(nr, zz, gbr[mm]);
+                gbi[mm] = fmaf(ni, zz, gbi[mm]);
+            }
             // carry into the previous token: conj(abar) A
             cr[mm] = fmaf(ar[mm], nr, ai[mm] * ni);
             ci[mm] = fmaf(ar[mm], ni, -ai[mm] * nr);
@@ -599,7 +643,7 @@ __device__ __forceinline__ void adjoint_block(int nt, const float2* g_row, const
     }
 }
 
-template <int MW, bool X_IO, bool BF16, bool CONJ_W>
+template <int MW, bool X_IO, bool BF16, bool CONJ_W, bool GB>
 __global__ __launch_bounds__(kStage) void bwd_adjoint_kernel(Problem p, idattn_params prm,
                                                              const void* __restrict__ x,
                                                              const float2* __restrict__ wv,
@@ -652,11 +696,11 @@ __global__ __launch_bounds__(kStage) void bwd_adjoint_kernel(Problem p, idattn_p
             const int jnt = static_cast<int>(i0 - j0);
             if (jnt > 0) nx = stage_fetch<true, X_IO, BF16>(p, b, h, row0, j0, jnt, group, wv, x, zsrc);
             if (nt == kBlk)
-                adjoint_block<MW, CONJ_W, false>(nt, g_row, x_blk + lane, z_blk + lane, red[w], lane, ar, ai, br, bi,
-                                                 cr, ci, gbr, gbi, M);
+                adjoint_block<MW, CONJ_W, false, GB>(nt, g_row, x_blk + lane, z_blk + lane, red[w], lane, ar, ai, br,
+                                                     bi, cr, ci, gbr, gbi, M);
             else
-                adjoint_block<MW, CONJ_W, true>(nt, g_row, x_blk + lane, z_blk + lane, red[w], lane, ar, ai, br, bi,
-                                                cr, ci, gbr, gbi, M);
+                adjoint_block<MW, CONJ_W, true, GB>(nt, g_row, x_blk + lane, z_blk + lane, red[w], lane, ar, ai, br,
+                                                    bi, cr, ci, gbr, gbi, M);
             __syncthreads();
             reduce_block(red, nt, group, d, g_z + (row0 + i0) * d);
             if (jnt == 0) break;
@@ -673,10 +717,12 @@ __global__ __launch_bounds__(kStage) void bwd_adjoint_kernel(Problem p, idattn_p
         }
     }
     // g_bbar: sum over the wave's channels, one value per (mode, channel group)
+    if constexpr (GB) {
 #pragma unroll
-    for (int mm = 0; mm < MW; ++mm) {
-        const float sr = wave_total(gbr[mm]), si = wave_total(gbi[mm]);
-        if (lane == 0) gb[(bh * gridDim.y + blockIdx.y) * M + moff + w * MW + mm] = make_float2(sr, si);
+        for (int mm = 0; mm < MW; ++mm) {
+            const float sr = wave_total(gbr[mm]), si = wave_total(gbi[mm]);
+            if (lane == 0) gb[(bh * gridDim.y + blockIdx.y) * M + moff + w * MW + mm] = make_float2(sr, si);
+        }
     }
 }
 
@@ -1294,10 +1340,10 @@ hipError_t launch_backward(const Problem& p, const idattn_params& prm, const voi
     do {                                                                                                           \
         if (state_in == nullptr)                                                                                   \
             bwd_key_scan_kernel<RJ, true><<<gm, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, grad_state, s, s_a, \
-                                                                  ga_key);                                         \
+                                                                  ga_key, gbk);                                    \
         else                                                                                                       \
             bwd_key_scan_kernel<RJ, false><<<gm, 256, 0, stream>>>(p, prm, xi_q, z_k, state_in, grad_state, s, s_a, \
-                                                                   ga_key);                                        \
+                                                                   ga_key, gbk);                                   \
     } while (0)
     if (p.d > 64) IDATTN_BK(4);
     else if (p.d > 32) IDATTN_BK(2);
@@ -1308,10 +1354,10 @@ hipError_t launch_backward(const Problem& p, const idattn_params& prm, const voi
     do {                                                                                                       \
         if (state_in == nullptr)                                                                               \
             bwd_value_scan_kernel<RJ, BF, true><<<gm, 256, 0, stream>>>(p, prm, z_v, grad_o, state_in, grad_state, \
-                                                                        s, s_a, ga_key, gs, ga);               \
+                                                                        s, s_a, ga_key, gs, ga, gbv);          \
         else                                                                                                   \
             bwd_value_scan_kernel<RJ, BF, false><<<gm, 256, 0, stream>>>(p, prm, z_v, grad_o, state_in,            \
-                                                                         grad_state, s, s_a, ga_key, gs, ga);  \
+                                                                         grad_state, s, s_a, ga_key, gs, ga, gbv); \
     } while (0)
     if (p.d > 64) {
         if (p.bf16) IDATTN_BV(4, true);
@@ -1333,16 +1379,24 @@ hipError_t launch_backward(const Problem& p, const idattn_params& prm, const voi
         else                                                                                              \
             bwd_xi_scan_kernel<MW, false><<<gc, kVW * 64, 0, stream>>>(p, prm, z_k, state_in, gs, g_xi, zs); \
     } while (0)
-#define IDATTN_BA(MW)                                                                                          \
-    do {                                                                                                       \
-        bwd_adjoint_kernel<MW, false, false, false><<<gc, kVW * 64, 0, stream>>>(p, prm, xi_q, gs, z_k, grad_state, \
-                                                                                 0, g_zk, grad_state_in, gbk, zs); \
-        if (p.bf16)                                                                                            \
-            bwd_adjoint_kernel<MW, true, true, true><<<gc, kVW * 64, 0, stream>>>(                              \
-                p, prm, grad_o, s, z_v, grad_state, static_cast<int>(p.d), g_zv, grad_state_in, gbv, zs);      \
-        else                                                                                                   \
-            bwd_adjoint_kernel<MW, true, false, true><<<gc, kVW * 64, 0, stream>>>(                             \
-                p, prm, grad_o, s, z_v, grad_state, static_cast<int>(p.d), g_zv, grad_state_in, gbv, zs);      \
+#define IDATTN_BAG(MW, GB)                                                                                    \
+    do {                                                                                                      \
+        bwd_adjoint_kernel<MW, false, false, false, GB><<<gc, kVW * 64, 0, stream>>>(                          \
+            p, prm, xi_q, gs, z_k, grad_state, 0, g_zk, grad_state_in, gbk, zs);                               \
+        if (p.bf16)                                                                                           \
+            bwd_adjoint_kernel<MW, true, true, true, GB><<<gc, kVW * 64, 0, stream>>>(                         \
+                p, prm, grad_o, s, z_v, grad_state, static_cast<int>(p.d), g_zv, grad_state_in, gbv, zs);     \
+        else                                                                                                  \
+            bwd_adjoint_kernel<MW, true, false, true, GB><<<gc, kVW * 64, 0, stream>>>(                        \
+                p, prm, grad_o, s, z_v, grad_state, static_cast<int>(p.d), g_zv, grad_state_in, gbv, zs);     \
+    } while (0)
+    // without a state entering, the per-mode scans have formed the g_bbar sums
+#define IDATTN_BA(MW)              \
+    do {                           \
+        if (state_in == nullptr)   \
+            IDATTN_BAG(MW, false); \
+        else                       \
+            IDATTN_BAG(MW, true);  \
     } while (0)
     switch (p.M / (kVW * splits)) {
         case 1: IDATTN_BX(1); IDATTN_BA(1); break;
@@ -1352,6 +1406,7 @@ hipError_t launch_backward(const Problem& p, const idattn_params& prm, const voi
     }
 #undef IDATTN_BX
 #undef IDATTN_BA
+#undef IDATTN_BAG
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 gr(static_cast<unsigned>((bh * runs + 3) / 4));
 #define IDATTN_BFW(BF, DJ, WT)                                                                                    \
@@ -1375,8 +1430,11 @@ hipError_t launch_backward(const Problem& p, const idattn_params& prm, const voi
 #undef IDATTN_BFW
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const unsigned slices = static_cast<unsigned>((4 * p.d + 2 * p.d * p.W + kRedThreads - 1) / kRedThreads + 1);
+    // the g_bbar partials: one per (b, h, mode) from the per-mode scans without
+    // a state entering, else one per channel group from the adjoints
+    const int gb_groups = state_in == nullptr ? 1 : groups;
     bwd_param_kernel<<<dim3(static_cast<unsigned>(p.H), slices), kRedThreads, 0, stream>>>(p, prm, part_f, part_c, ga, gbk, gbv,
-                                                                                   runs, groups, grads);
+                                                                                   runs, gb_groups, grads);
     return hipGetLastError();
 }
 
