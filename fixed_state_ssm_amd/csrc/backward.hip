@@ -607,16 +607,36 @@ __global__ __launch_bounds__(kStage) void bwd_xi_scan_kernel(Problem p, idattn_p
 //   g_state_in = conj(abar) A(0)                    (columns off .. off + d - 1)
 // Key side: x = xi_q, w = g_s, z = z_k, off = 0.  Value side: x = g_o (io
 // dtype, [B][N][H][d]), w = conj(s), z = z_v, off = d.
+// The scans carry beta_m A_m instead of A_m, beta = conj(bbar) wherever
+// |bbar|^2 >= kMinB2 (else 1): the staged mode input w is multiplied by beta
+// once per block, each token's share Re(conj(bbar) A) is then just
+// Re(beta A), and the g_bbar sums and g_state_in are divided by beta once at
+// the end.  The bound keeps beta A far above the fp32 subnormal range.
+constexpr double kMinB2 = 0x1p-80;
+__device__ __forceinline__ bool adj_scaled(const Zoh& z) { return z.br * z.br + z.bi * z.bi >= kMinB2; }
+__device__ __forceinline__ float2 adj_beta(const Zoh& z) {
+    return adj_scaled(z) ? make_float2(static_cast<float>(z.br), -static_cast<float>(z.bi)) : make_float2(1.f, 0.f);
+}
+// 1 / beta
+__device__ __forceinline__ float2 adj_beta_inv(const Zoh& z) {
+    if (!adj_scaled(z)) return make_float2(1.f, 0.f);
+    const double n = z.br * z.br + z.bi * z.bi;
+    return make_float2(static_cast<float>(z.br / n), static_cast<float>(z.bi / n));
+}
+
 // One block of kBlk tokens of an adjoint scan for the wave's MW modes, in
-// reverse token order: the adjoint A = x g + carry, the wave's share
-// sum_m Re(conj(bbar_m) A_m) of each token to red, the g_bbar sums, and the
-// carry conj(abar) A into the previous token.  A ragged block steps only its
-// first nt tokens.  GB: whether it forms the g_bbar sums (without a state
-// entering the per-mode scans form them from per-token totals instead).
-template <int MW, bool CONJ_W, bool RAGGED, bool GB>
+// reverse token order: the carried adjoint beta A = x (beta w) + carry, the
+// wave's share sum_m Re(conj(bbar_m) A_m) of each token to red, the g_bbar
+// sums, and the carry conj(abar) beta A into the previous token.  The share
+// weighs mode m's carried value by (yr, yi): (1, 0) where beta = conj(bbar),
+// else bbar; FAST: every mode of the wave is of the first kind.  A ragged
+// block steps only its first nt tokens.  GB: whether it forms the g_bbar sums
+// (without a state entering the per-mode scans form them from per-token
+// totals instead).
+template <int MW, bool CONJ_W, bool RAGGED, bool GB, bool FAST>
 __device__ __forceinline__ void adjoint_block(int nt, const float2* g_row, const float* x_col, const float* z_col,
                                               float (*red_t)[kWave], int lane, const float (&ar)[MW],
-                                              const float (&ai)[MW], const float (&br)[MW], const float (&bi)[MW],
+                                              const float (&ai)[MW], const float (&yr)[MW], const float (&yi)[MW],
                                               float (&cr)[MW], float (&ci)[MW], float (&gbr)[MW], float (&gbi)[MW],
                                               int M) {
 #pragma unroll
@@ -630,7 +650,10 @@ __device__ __forceinline__ void adjoint_block(int nt, const float2* g_row, const
             if constexpr (CONJ_W) g.y = -g.y;
             const float nr = fmaf(xx, g.x, cr[mm]);
             const float ni = fmaf(xx, g.y, ci[mm]);
-            acc = fmaf(br[mm], nr, fmaf(bi[mm], ni, acc));  // Re(conj(bbar) A)
+            if constexpr (FAST)
+                acc = mm == 0 ? nr : acc + nr;  // Re(beta A)
+            else
+                acc = fmaf(yr[mm], nr, fmaf(yi[mm], ni, acc));  // Re(conj(bbar) A)
             if constexpr (GB) {
                 gbr[mm] = fmaf(nr, zz, gbr[mm]);
                 gbi[mm] = fmaf(ni, zz, gbi[mm]);
@@ -655,6 +678,7 @@ __global__ __launch_bounds__(kStage) void bwd_adjoint_kernel(Problem p, idattn_p
     __shared__ float x_blk[kStage];
     __shared__ float z_blk[kStage];
     __shared__ float red[kVW][kBlk][kWave];
+    __shared__ float2 beta_s[kStage / kBlk];  // beta of every mode (M <= 64)
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x >> 6;
     const int64_t bh = blockIdx.x;
@@ -667,22 +691,35 @@ __global__ __launch_bounds__(kStage) void bwd_adjoint_kernel(Problem p, idattn_p
     const int64_t row0 = h * p.T + b * N;
     const int moff = static_cast<int>(blockIdx.z) * kVW * MW;  // the split's first mode
     g_z += blockIdx.z * zs;
-    float ar[MW], ai[MW], br[MW], bi[MW], cr[MW], ci[MW], gbr[MW], gbi[MW];
+    if (threadIdx.x < M) beta_s[threadIdx.x] = adj_beta(zoh_of(prm, h, M, threadIdx.x));
+    float ar[MW], ai[MW], yr[MW], yi[MW], cr[MW], ci[MW], gbr[MW], gbi[MW];
+    float2 rho[MW];  // 1 / beta
+    bool fast = true;
 #pragma unroll
     for (int mm = 0; mm < MW; ++mm) {
         const int64_t m = moff + w * MW + mm;
         const Zoh zz = zoh_of(prm, h, M, m);
         ar[mm] = static_cast<float>(zz.ar);
         ai[mm] = static_cast<float>(zz.ai);
-        br[mm] = static_cast<float>(zz.br);
-        bi[mm] = static_cast<float>(zz.bi);
+        const bool sc = adj_scaled(zz);
+        fast = fast && sc;
+        yr[mm] = sc ? 1.f : static_cast<float>(zz.br);
+        yi[mm] = sc ? 0.f : static_cast<float>(zz.bi);
+        rho[mm] = adj_beta_inv(zz);
         cr[mm] = ci[mm] = gbr[mm] = gbi[mm] = 0.f;
-        if (grad_state != nullptr && cok) {  // the carry into the last token: g_S
+        if (grad_state != nullptr && cok) {  // the carry into the last token: beta g_S
             const int64_t idx = ((bh * M + m) * 2 * d + off + c) * 2;
-            cr[mm] = grad_state[idx];
-            ci[mm] = grad_state[idx + 1];
+            const float2 be = adj_beta(zz);
+            const float gr = grad_state[idx], gi = grad_state[idx + 1];
+            cr[mm] = be.x * gr - be.y * gi;
+            ci[mm] = fmaf(be.x, gi, be.y * gr);
         }
     }
+    __syncthreads();
+    // beta of the mode this thread stages (conjugated where the scan reads the
+    // staged value conjugated)
+    float2 bst = beta_s[threadIdx.x % M];
+    if constexpr (CONJ_W) bst.y = -bst.y;
     if (N > 0) {  // uniform over the block
         constexpr bool XB = X_IO && BF16;
         const float2* g_row = w_blk + moff + w * MW;
@@ -690,17 +727,27 @@ __global__ __launch_bounds__(kStage) void bwd_adjoint_kernel(Problem p, idattn_p
         int nt = static_cast<int>(N - i0);
         Stage nx = stage_fetch<true, X_IO, BF16>(p, b, h, row0, i0, nt, group, wv, x, zsrc);
         while (true) {
+            nx.w = make_float2(bst.x * nx.w.x - bst.y * nx.w.y, fmaf(bst.x, nx.w.y, bst.y * nx.w.x));
             stage_store<true, XB>(nx, nt, M, group, d, w_blk, x_blk, z_blk);
             __syncthreads();
             const int64_t j0 = i0 > kBlk ? i0 - kBlk : 0;  // the previous block, loaded while this one runs
             const int jnt = static_cast<int>(i0 - j0);
             if (jnt > 0) nx = stage_fetch<true, X_IO, BF16>(p, b, h, row0, j0, jnt, group, wv, x, zsrc);
-            if (nt == kBlk)
-                adjoint_block<MW, CONJ_W, false, GB>(nt, g_row, x_blk + lane, z_blk + lane, red[w], lane, ar, ai, br,
-                                                     bi, cr, ci, gbr, gbi, M);
-            else
-                adjoint_block<MW, CONJ_W, true, GB>(nt, g_row, x_blk + lane, z_blk + lane, red[w], lane, ar, ai, br,
-                                                    bi, cr, ci, gbr, gbi, M);
+            if (nt == kBlk) {
+                if (fast)
+                    adjoint_block<MW, CONJ_W, false, GB, true>(nt, g_row, x_blk + lane, z_blk + lane, red[w], lane, ar,
+                                                               ai, yr, yi, cr, ci, gbr, gbi, M);
+                else
+                    adjoint_block<MW, CONJ_W, false, GB, false>(nt, g_row, x_blk + lane, z_blk + lane, red[w], lane,
+                                                                ar, ai, yr, yi, cr, ci, gbr, gbi, M);
+            } else {
+                if (fast)
+                    adjoint_block<MW, CONJ_W, true, GB, true>(nt, g_row, x_blk + lane, z_blk + lane, red[w], lane, ar,
+                                                              ai, yr, yi, cr, ci, gbr, gbi, M);
+                else
+                    adjoint_block<MW, CONJ_W, true, GB, false>(nt, g_row, x_blk + lane, z_blk + lane, red[w], lane, ar,
+                                                               ai, yr, yi, cr, ci, gbr, gbi, M);
+            }
             __syncthreads();
             reduce_block(red, nt, group, d, g_z + (row0 + i0) * d);
             if (jnt == 0) break;
@@ -708,12 +755,12 @@ __global__ __launch_bounds__(kStage) void bwd_adjoint_kernel(Problem p, idattn_p
             nt = jnt;
         }
     }
-    if (grad_state_in != nullptr && cok) {
+    if (grad_state_in != nullptr && cok) {  // conj(abar) A(0) = the carry / beta
 #pragma unroll
         for (int mm = 0; mm < MW; ++mm) {
             const int64_t idx = ((bh * M + moff + w * MW + mm) * 2 * d + off + c) * 2;
-            grad_state_in[idx] = cr[mm];
-            grad_state_in[idx + 1] = ci[mm];
+            grad_state_in[idx] = rho[mm].x * cr[mm] - rho[mm].y * ci[mm];
+            grad_state_in[idx + 1] = fmaf(rho[mm].x, ci[mm], rho[mm].y * cr[mm]);
         }
     }
     // g_bbar: sum over the wave's channels, one value per (mode, channel group)
@@ -721,7 +768,9 @@ __global__ __launch_bounds__(kStage) void bwd_adjoint_kernel(Problem p, idattn_p
 #pragma unroll
         for (int mm = 0; mm < MW; ++mm) {
             const float sr = wave_total(gbr[mm]), si = wave_total(gbi[mm]);
-            if (lane == 0) gb[(bh * gridDim.y + blockIdx.y) * M + moff + w * MW + mm] = make_float2(sr, si);
+            if (lane == 0)
+                gb[(bh * gridDim.y + blockIdx.y) * M + moff + w * MW + mm] =
+                    make_float2(rho[mm].x * sr - rho[mm].y * si, fmaf(rho[mm].x, si, rho[mm].y * sr));
         }
     }
 }

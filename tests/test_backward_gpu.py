@@ -138,6 +138,35 @@ def test_backward_small(fs, name, mode):
     _compare(f"{name} {mode}", got, want, io, c.params)
 
 
+@pytest.mark.parametrize("mode", ["no_state", "grad_state_only", "state_and_grad_state"])
+def test_backward_zero_and_tiny_bbar(fs, mode):
+    """Modes with B = 0 (bbar = 0 exactly) and with B so small that |bbar|
+    falls below the bound under which the adjoint scans carry A itself
+    rather than conj(bbar) A, next to ordinary modes of the same waves."""
+    from oracle import idattn_backward as OB
+    base, over, tag, fn = BWD["d64_w8_f32"]
+    c = WL.make_case(base, seed=3, tag=tag, **over)
+    s = c.spec
+    c.params["Bc"][:, 0::5] = 0.0
+    c.params["Bc"][:, 2::7] *= 1e-14
+    go, gS = _grad_inputs(s, seed=tag + 50)
+    with_state = mode == "state_and_grad_state"
+    g_S = None if mode == "no_state" else gS
+    st0 = tl0 = None
+    if with_state:
+        st0, tl0 = WL.make_decode_state(s, seed=4)
+    zero = np.zeros((s["B"], s["H"], s["M"], 2 * s["d"]), np.complex128)
+    want = OB.backward(c.q, c.k, c.v, c.params, go, state_in=zero if st0 is None else st0, tail_in=tl0,
+                       grad_state=g_S, feature_norm=fn)
+    p = fs.params_to_device(c.params)
+    got = fs.backward(up(c.q, "f32"), up(c.k, "f32"), up(c.v, "f32"), p, up(go, "f32"),
+                      state_in=None if st0 is None else state_dev(st0), tail_in=None if tl0 is None else up(tl0, "f32"),
+                      grad_state=None if g_S is None else state_dev(g_S), feature_norm=fn)
+    _sync()
+    print(f"backward zero/tiny bbar {mode}", flush=True)
+    _compare(f"zero/tiny bbar {mode}", got, want, "f32", c.params)
+
+
 def test_backward_deterministic_and_zero_tokens(fs):
     """Repeated calls give the same bits; N = 0 gives zero parameter
     gradients and passes grad_state through to grad_state_in."""
