@@ -195,11 +195,13 @@ def test_backward_deterministic_and_zero_tokens(fs):
         assert not grads[key].any(), key
 
 
-def test_backward_full_1p3b_one_head(fs):
+@pytest.mark.parametrize("with_state", [True, False], ids=["state_and_grad_state", "no_state"])
+def test_backward_full_1p3b_one_head(fs, with_state):
     """The 1.3B workload (B=4 H=16 N=4096 d=128 M=64, bf16) on the GPU; the
     oracle differentiates head 5 over all four batch rows: the input
-    gradients of those pairs, that head's parameter gradients and its state
-    gradient."""
+    gradients of those pairs, that head's parameter gradients and, with a
+    state, its state gradient.  no_state is the call the benchmark times (no
+    state, tail or state_out gradient)."""
     from oracle import idattn_backward as OB
     import torch
     s = WL.spec("1p3b", tag=110)
@@ -207,19 +209,24 @@ def test_backward_full_1p3b_one_head(fs):
     params = WL.make_params(s)
     go, gS = _grad_inputs(s, seed=111)
     st0, tl0 = WL.make_decode_state(s, seed=112)
+    if not with_state:
+        st0 = tl0 = gS = None
     p = fs.params_to_device(params)
-    print("backward 1.3B: GPU", flush=True)
-    got = fs.backward(up(q, "bf16"), up(k, "bf16"), up(v, "bf16"), p, up(go, "bf16"), state_in=state_dev(st0),
-                      tail_in=up(tl0, "bf16"), grad_state=state_dev(gS))
+    print(f"backward 1.3B with_state={with_state}: GPU", flush=True)
+    got = fs.backward(up(q, "bf16"), up(k, "bf16"), up(v, "bf16"), p, up(go, "bf16"),
+                      state_in=None if st0 is None else state_dev(st0), tail_in=None if tl0 is None else up(tl0, "bf16"),
+                      grad_state=None if gS is None else state_dev(gS))
     _sync()
     h = 5
     hs = slice(h, h + 1)
     print("backward 1.3B: oracle, head 5", flush=True)
     want = OB.backward(q[:, :, hs], k[:, :, hs], v[:, :, hs], {key: val[hs] for key, val in params.items()},
-                       go[:, :, hs], state_in=st0[:, hs], tail_in=tl0[:, hs], grad_state=gS[:, hs])
+                       go[:, :, hs], state_in=None if st0 is None else st0[:, hs],
+                       tail_in=None if tl0 is None else tl0[:, hs], grad_state=None if gS is None else gS[:, hs])
     sub = {key: got[key][:, :, hs] for key in ("q", "k", "v")}
     sub.update({key: got[key][hs] for key in PARAM_KEYS})
-    sub["state"] = got["state"][:, hs]
-    _compare("1.3B head 5", sub, want, "bf16", {key: val[hs] for key, val in params.items()})
+    if with_state:
+        sub["state"] = got["state"][:, hs]
+    _compare(f"1.3B head 5 with_state={with_state}", sub, want, "bf16", {key: val[hs] for key, val in params.items()})
     del got
     torch.cuda.empty_cache()
