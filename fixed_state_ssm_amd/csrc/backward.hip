@@ -53,6 +53,32 @@ __device__ __forceinline__ Zoh zoh_of(const idattn_params& prm, int64_t h, int64
 // or d below 32 RJ) then zeroes what lies out of range and steps only its
 // tokens.  A full batch runs with no per-token condition.
 
+// The scans multiply by abar_f = fl32(abar), which differs from abar by up to
+// about 2^-24 relative; a state that is multiplied by it n times carries that
+// error n-fold, some 1e-5 in the far terms of a mode with |abar| = 0.998 (a
+// memory of about 500 tokens) and more in the n abar^(n-1) weights of the
+// abar derivatives.  So every K tokens the scans multiply their states by
+// (abar / abar_f)^K, as x + dk x with dk = (abar / abar_f)^K - 1 formed in
+// fp64: no term then holds more than K roundings of abar.  K: a power of two.
+constexpr int kFixTok = 32;  // per-mode scans: every fourth batch
+__device__ __forceinline__ float2 decay_fix(const Zoh& z, int K) {
+    const double fr = static_cast<float>(z.ar), fi = static_cast<float>(z.ai);
+    const double n = fr * fr + fi * fi;
+    double rr = (z.ar * fr + z.ai * fi) / n, ri = (z.ai * fr - z.ar * fi) / n;  // abar / abar_f
+    for (int k = 1; k < K; k <<= 1) {
+        const double t = rr * rr - ri * ri;
+        ri = 2.0 * rr * ri;
+        rr = t;
+    }
+    return make_float2(static_cast<float>(rr - 1.0), static_cast<float>(ri));
+}
+// (1 + d) x for complex x = (xr, xi)
+__device__ __forceinline__ void apply_fix(float2 d, float& xr, float& xi) {
+    const float r = fmaf(d.x, xr, fmaf(-d.y, xi, xr));
+    xi = fmaf(d.x, xi, fmaf(d.y, xr, xi));
+    xr = r;
+}
+
 // One batch of the key-side recurrence: V(i) = abar V(i-1) + U(i-1), then
 // U(i) = abar U(i-1) + bbar z_k(i); the lane's shares of s = xi_q . U and
 // s_a = xi_q . V per token.  SCALED: the lane carries U / bbar and V / bbar,
@@ -153,6 +179,7 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
     const float ar = static_cast<float>(z.ar), ai = static_cast<float>(z.ai);
     const float br = static_cast<float>(z.br), bi = static_cast<float>(z.bi);
     const int64_t st_row = ((bh * M + m) * 2 * d) * 2;
+    const float2 fix = decay_fix(z, kFixTok);
     float ur[RJ], ui[RJ], vr[RJ], vi[RJ];
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
@@ -197,6 +224,14 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
                 for (int j = 0; j < RJ; ++j)
                     if (t >= nt || RJ * li + j >= d) x[t][j] = zq[t][j] = 0.f;
             key_batch<RJ, true, SCALED>(nt, ur, ui, vr, vi, x, zq, ar, ai, br, bi, spr, spi, sqr, sqi);
+        }
+        static_assert(kFixTok % kTok == 0, "the decay fix at a batch's end");
+        if (i0 % kFixTok == kFixTok - kTok) {  // uniform
+#pragma unroll
+            for (int j = 0; j < RJ; ++j) {
+                apply_fix(fix, ur[j], ui[j]);
+                apply_fix(fix, vr[j], vi[j]);
+            }
         }
         static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
         float tpr = half_reduce_scatter8(spr, lane), tpi = half_reduce_scatter8(spi, lane);
@@ -286,6 +321,7 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
     const float ar = static_cast<float>(z.ar), ai = static_cast<float>(z.ai);
     const float br = static_cast<float>(z.br), bi = static_cast<float>(z.bi);
     const int64_t st_row = ((bh * M + m) * 2 * d) * 2;
+    const float2 fix = decay_fix(z, kFixTok);
     float gmr[RJ], gmi[RJ], wr[RJ], wi[RJ];
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
@@ -331,6 +367,13 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
                 for (int j = 0; j < RJ; ++j)
                     if (t >= nt || RJ * li + j >= d) zz[t][j] = go[t][j] = 0.f;
             value_batch<RJ, true, SCALED>(nt, gmr, gmi, wr, wi, zz, go, ar, ai, br, bi, spr, spi, sqr, sqi);
+        }
+        if (i0 % kFixTok == kFixTok - kTok) {  // uniform
+#pragma unroll
+            for (int j = 0; j < RJ; ++j) {
+                apply_fix(fix, gmr[j], gmi[j]);
+                apply_fix(fix, wr[j], wi[j]);
+            }
         }
         static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
         float pr = half_reduce_scatter8(spr, lane), pi = half_reduce_scatter8(spi, lane);
@@ -552,6 +595,7 @@ __global__ __launch_bounds__(kStage) void bwd_xi_scan_kernel(Problem p, idattn_p
     if (N <= 0) return;  // whole block
     g_xi += blockIdx.z * zs;
     float ar[MW], ai[MW], br[MW], bi[MW], ur[MW], ui[MW];
+    float2 fix[MW];  // the decay fix of a full block (kBlk steps by abar_f)
 #pragma unroll
     for (int mm = 0; mm < MW; ++mm) {
         const int64_t m = moff + w * MW + mm;
@@ -560,6 +604,7 @@ __global__ __launch_bounds__(kStage) void bwd_xi_scan_kernel(Problem p, idattn_p
         ai[mm] = static_cast<float>(zz.ai);
         br[mm] = static_cast<float>(zz.br);
         bi[mm] = static_cast<float>(zz.bi);
+        fix[mm] = decay_fix(zz, kBlk);
         ur[mm] = ui[mm] = 0.f;
         if (state_in != nullptr && cok) {
             const int64_t idx = ((bh * M + m) * 2 * d + c) * 2;
@@ -588,9 +633,11 @@ __global__ __launch_bounds__(kStage) void bwd_xi_scan_kernel(Problem p, idattn_p
         const int64_t j0 = i0 + kBlk;  // the next block, loaded while this one runs
         const int jnt = static_cast<int>(min(N - j0, static_cast<int64_t>(kBlk)));
         if (j0 < N) nx = stage_fetch<false, false, false>(p, b, h, row0, j0, jnt, group, gs, nullptr, z_k);
-        if (nt == kBlk)
+        if (nt == kBlk) {
             xi_block<MW, false, SCALED>(nt, g_row, z_blk + lane, red[w], lane, ar, ai, br, bi, ur, ui, M);
-        else
+#pragma unroll
+            for (int mm = 0; mm < MW; ++mm) apply_fix(fix[mm], ur[mm], ui[mm]);
+        } else
             xi_block<MW, true, SCALED>(nt, g_row, z_blk + lane, red[w], lane, ar, ai, br, bi, ur, ui, M);
         __syncthreads();
         reduce_block(red, nt, group, d, g_xi + (row0 + i0) * d);
@@ -694,6 +741,7 @@ __global__ __launch_bounds__(kStage) void bwd_adjoint_kernel(Problem p, idattn_p
     if (threadIdx.x < M) beta_s[threadIdx.x] = adj_beta(zoh_of(prm, h, M, threadIdx.x));
     float ar[MW], ai[MW], yr[MW], yi[MW], cr[MW], ci[MW], gbr[MW], gbi[MW];
     float2 rho[MW];  // 1 / beta
+    float2 fix[MW];  // the decay fix of a full block (kBlk carries by conj(abar_f))
     bool fast = true;
 #pragma unroll
     for (int mm = 0; mm < MW; ++mm) {
@@ -706,6 +754,8 @@ __global__ __launch_bounds__(kStage) void bwd_adjoint_kernel(Problem p, idattn_p
         yr[mm] = sc ? 1.f : static_cast<float>(zz.br);
         yi[mm] = sc ? 0.f : static_cast<float>(zz.bi);
         rho[mm] = adj_beta_inv(zz);
+        const float2 f = decay_fix(zz, kBlk);
+        fix[mm] = make_float2(f.x, -f.y);  // (conj(abar) / conj(abar_f))^kBlk - 1
         cr[mm] = ci[mm] = gbr[mm] = gbi[mm] = 0.f;
         if (grad_state != nullptr && cok) {  // the carry into the last token: beta g_S
             const int64_t idx = ((bh * M + m) * 2 * d + off + c) * 2;
@@ -740,6 +790,8 @@ __global__ __launch_bounds__(kStage) void bwd_adjoint_kernel(Problem p, idattn_p
                 else
                     adjoint_block<MW, CONJ_W, false, GB, false>(nt, g_row, x_blk + lane, z_blk + lane, red[w], lane,
                                                                 ar, ai, yr, yi, cr, ci, gbr, gbi, M);
+#pragma unroll
+                for (int mm = 0; mm < MW; ++mm) apply_fix(fix[mm], cr[mm], ci[mm]);
             } else {
                 if (fast)
                     adjoint_block<MW, CONJ_W, true, GB, true>(nt, g_row, x_blk + lane, z_blk + lane, red[w], lane, ar,
