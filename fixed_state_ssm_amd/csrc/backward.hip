@@ -53,32 +53,6 @@ __device__ __forceinline__ Zoh zoh_of(const idattn_params& prm, int64_t h, int64
 // or d below 32 RJ) then zeroes what lies out of range and steps only its
 // tokens.  A full batch runs with no per-token condition.
 
-// The scans multiply by abar_f = fl32(abar), which differs from abar by up to
-// about 2^-24 relative; a state that is multiplied by it n times carries that
-// error n-fold, some 1e-5 in the far terms of a mode with |abar| = 0.998 (a
-// memory of about 500 tokens) and more in the n abar^(n-1) weights of the
-// abar derivatives.  So every K tokens the scans multiply their states by
-// (abar / abar_f)^K, as x + dk x with dk = (abar / abar_f)^K - 1 formed in
-// fp64: no term then holds more than K roundings of abar.  K: a power of two.
-constexpr int kFixTok = 32;  // per-mode scans: every fourth batch
-__device__ __forceinline__ float2 decay_fix(const Zoh& z, int K) {
-    const double fr = static_cast<float>(z.ar), fi = static_cast<float>(z.ai);
-    const double n = fr * fr + fi * fi;
-    double rr = (z.ar * fr + z.ai * fi) / n, ri = (z.ai * fr - z.ar * fi) / n;  // abar / abar_f
-    for (int k = 1; k < K; k <<= 1) {
-        const double t = rr * rr - ri * ri;
-        ri = 2.0 * rr * ri;
-        rr = t;
-    }
-    return make_float2(static_cast<float>(rr - 1.0), static_cast<float>(ri));
-}
-// (1 + d) x for complex x = (xr, xi)
-__device__ __forceinline__ void apply_fix(float2 d, float& xr, float& xi) {
-    const float r = fmaf(d.x, xr, fmaf(-d.y, xi, xr));
-    xi = fmaf(d.x, xi, fmaf(d.y, xr, xi));
-    xr = r;
-}
-
 // One batch of the key-side recurrence: V(i) = abar V(i-1) + U(i-1), then
 // U(i) = abar U(i-1) + bbar z_k(i); the lane's shares of s = xi_q . U and
 // s_a = xi_q . V per token.  SCALED: the lane carries U / bbar and V / bbar,
@@ -226,7 +200,7 @@ __global__ __launch_bounds__(256) void bwd_key_scan_kernel(Problem p, idattn_par
             key_batch<RJ, true, SCALED>(nt, ur, ui, vr, vi, x, zq, ar, ai, br, bi, spr, spi, sqr, sqi);
         }
         static_assert(kFixTok % kTok == 0, "the decay fix at a batch's end");
-        if (i0 % kFixTok == kFixTok - kTok) {  // uniform
+        if (nt == kTok && i0 % kFixTok == kFixTok - kTok) {  // uniform
 #pragma unroll
             for (int j = 0; j < RJ; ++j) {
                 apply_fix(fix, ur[j], ui[j]);
@@ -368,7 +342,7 @@ __global__ __launch_bounds__(256) void bwd_value_scan_kernel(Problem p, idattn_p
                     if (t >= nt || RJ * li + j >= d) zz[t][j] = go[t][j] = 0.f;
             value_batch<RJ, true, SCALED>(nt, gmr, gmi, wr, wi, zz, go, ar, ai, br, bi, spr, spi, sqr, sqi);
         }
-        if (i0 % kFixTok == kFixTok - kTok) {  // uniform
+        if (nt == kTok && i0 % kFixTok == kFixTok - kTok) {  // uniform
 #pragma unroll
             for (int j = 0; j < RJ; ++j) {
                 apply_fix(fix, gmr[j], gmi[j]);

@@ -327,4 +327,30 @@ __device__ inline Zoh zoh_mode(float log_dt, float lre, float lim, float bre, fl
     return z;
 }
 
+// The sequential scans multiply by abar_f = fl32(abar), which differs from abar by up to
+// about 2^-24 relative; a state that is multiplied by it n times carries that
+// error n-fold, some 1e-5 in the far terms of a mode with |abar| = 0.998 (a
+// memory of about 500 tokens) and more in the n abar^(n-1) weights of the
+// abar derivatives.  So every K tokens the scans multiply their states by
+// (abar / abar_f)^K, as x + dk x with dk = (abar / abar_f)^K - 1 formed in
+// fp64: no term then holds more than K roundings of abar.  K: a power of two.
+constexpr int kFixTok = 32;  // the per-mode scans' K: every fourth batch of eight tokens
+__device__ __forceinline__ float2 decay_fix(const Zoh& z, int K) {
+    const double fr = static_cast<float>(z.ar), fi = static_cast<float>(z.ai);
+    const double n = fr * fr + fi * fi;
+    double rr = (z.ar * fr + z.ai * fi) / n, ri = (z.ai * fr - z.ar * fi) / n;  // abar / abar_f
+    for (int k = 1; k < K; k <<= 1) {
+        const double t = rr * rr - ri * ri;
+        ri = 2.0 * rr * ri;
+        rr = t;
+    }
+    return make_float2(static_cast<float>(rr - 1.0), static_cast<float>(ri));
+}
+// (1 + d) x for complex x = (xr, xi)
+__device__ __forceinline__ void apply_fix(float2 d, float& xr, float& xi) {
+    const float r = fmaf(d.x, xr, fmaf(-d.y, xi, xr));
+    xi = fmaf(d.x, xi, fmaf(d.y, xr, xi));
+    xr = r;
+}
+
 }  // namespace idattn

@@ -95,6 +95,7 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
                            prm.Bc[(h * M + mc) * 2], prm.Bc[(h * M + mc) * 2 + 1]);
     const float ar = static_cast<float>(z.ar), ai = static_cast<float>(z.ai);
     const float br = static_cast<float>(z.br), bi = static_cast<float>(z.bi);
+    const float2 fix = decay_fix(z, kFixTok);
 
     float ur[RJ], ui[RJ];
     const int64_t st_row = ((bh * M + mc) * 2 * d) * 2;  // complex row m of [M][2d], U half first
@@ -183,6 +184,11 @@ __global__ __launch_bounds__(256) void key_scan_seq_kernel(Problem p, idattn_par
                 for (int j = 0; j < RJ; ++j)
                     if (t >= nt || RJ * li + j >= d) xv[t][j] = zv[t][j] = 0.f;
             key_seq_batch<RJ, ETA, true>(nt, ts, ur, ui, xv, zv, ar, ai, br, bi, spr, spi, er, ei, etr, eti);
+        }
+        static_assert(kFixTok % kTok == 0, "the decay fix at a batch's end");
+        if (nt == kTok && i0 % kFixTok == kFixTok - kTok) {  // uniform
+#pragma unroll
+            for (int j = 0; j < RJ; ++j) apply_fix(fix, ur[j], ui[j]);
         }
         static_assert(kTok == 8, "one reduce-scatter per kTok tokens");
         const float pr = half_reduce_scatter8(spr, lane), pi = half_reduce_scatter8(spi, lane);
@@ -318,11 +324,13 @@ __global__ __launch_bounds__(kStage) void value_scan_seq_kernel(Problem p, idatt
     float* num = blockIdx.z == 0 ? num0 : num1;
 
     float ar[MW], ai[MW], br[MW], bi[MW], gr[MW], gi[MW];
+    float2 fix[MW];  // the decay fix of a full block (kBlk steps by abar_f)
 #pragma unroll
     for (int mm = 0; mm < MW; ++mm) {
         const int64_t m = moff + w * MW + mm;
         const Zoh z = zoh_mode(prm.log_dt[h], prm.A[(h * M + m) * 2], prm.A[(h * M + m) * 2 + 1],
                                prm.Bc[(h * M + m) * 2], prm.Bc[(h * M + m) * 2 + 1]);
+        fix[mm] = decay_fix(z, kBlk);
         ar[mm] = static_cast<float>(z.ar);
         ai[mm] = static_cast<float>(z.ai);
         br[mm] = static_cast<float>(z.br);
@@ -360,9 +368,11 @@ __global__ __launch_bounds__(kStage) void value_scan_seq_kernel(Problem p, idatt
                     den_s[w][lane] = dn;
                 }
             }
-            if (nt == kBlk)
+            if (nt == kBlk) {
                 value_seq_block<MW, false>(nt, s_row, z_blk + lane, red[w], lane, ar, ai, br, bi, gr, gi, M);
-            else
+#pragma unroll
+                for (int mm = 0; mm < MW; ++mm) apply_fix(fix[mm], gr[mm], gi[mm]);
+            } else
                 value_seq_block<MW, true>(nt, s_row, z_blk + lane, red[w], lane, ar, ai, br, bi, gr, gi, M);
             __syncthreads();
             for (int e = threadIdx.x; e < nt * kWave; e += kStage) {
